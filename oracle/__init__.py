@@ -1,0 +1,16 @@
+"""CPU oracle for the PRISM rank-L gated delta-rule forward.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the package smoke check and the
+benchmark's CPU-baseline leg may import this package.  The product path (the
+HIP library and its Python binding) never calls it, and it shares no code
+with that path.
+
+The oracle is plain float64 numpy that steps the recurrence token by token
+and runs the residual chain one refinement step at a time.  See
+``oracle.prism`` for the definitions and the passages each one follows.
+"""
+from .prism import (shortconv_anchor, residual_chain, token_step, forward,
+                    forward_pairs)
+
+__all__ = ["shortconv_anchor", "residual_chain", "token_step", "forward",
+           "forward_pairs"]
