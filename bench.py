@@ -1,0 +1,259 @@
+"""Benchmark of the PRISM rank-L gated delta-rule forward on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload rec16k_bf16] [--no-cpu-baseline]
+
+One step = one prism_fwd call (segment sweep + segment scan + output
+correction) over one batch of synthetic inputs already resident in HBM.  Input
+sets are rotated so the working set exceeds the 256 MB Infinity Cache.  Prints
+one JSON line with whole-job tokens/s, the dominant kernel's achieved HBM
+bandwidth against the 8 TB/s peak (HIP events on the launch stream), and the
+float64 oracle timed on the host cores on a bounded sample.
+
+    python bench.py --calibrate-copy MB
+runs a plain device-to-device copy of MB megabytes (for scaling the
+FETCH_SIZE / WRITE_SIZE counters of rocprofv3) and exits.
+"""
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MALL_BYTES = 256 << 20
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def algorithmic_bytes(w):
+    """Bytes the method must move per token-head (inputs once, output once) and
+    the share read by the segment-sweep kernel (all inputs)."""
+    E = 2 if w.dtype == "bf16" else 4
+    rank = (w.L - 1) * (w.dk + w.dv) * E + (4 * w.L if w.L > 1 else 0)
+    inputs = (2 * w.dk + w.dv) * E + rank + 8
+    return inputs, inputs + w.dv * E
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "delta_rule_sequence_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload_name):
+    """HBM bytes per launch of the segment-sweep kernel from the committed
+    rocprofv3 counter summary, or None if the kernels changed since."""
+    path = os.path.join(PROFILES, "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    ent = rec.get(workload_name)
+    if not ent or ent.get("kernel_source_sha") != kernel_source_hash():
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+class Hip:
+    """Minimal ctypes access to HIP events (the library records them on the
+    stream its kernels run on)."""
+
+    def __init__(self):
+        self.lib = None
+        for name in ["libamdhip64.so", "/opt/rocm/lib/libamdhip64.so"]:
+            try:
+                self.lib = ctypes.CDLL(name)
+                break
+            except OSError:
+                continue
+        if self.lib is None:
+            raise RuntimeError("libamdhip64.so not found")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def events(self, n):
+        out = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            if self.lib.hipEventCreate(ctypes.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            out.append(e)
+        return out
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        if self.lib.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def destroy(self, evs):
+        for e in evs:
+            self.lib.hipEventDestroy(e)
+
+
+def cpu_baseline(w, x, budget_s=10.0):
+    """The float64 oracle on the host, single-threaded, on whole sequences of
+    the workload's first input set (repeated until `budget_s` has elapsed)."""
+    import numpy as np  # noqa: F401
+    import oracle
+    try:
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(limits=1)
+    except Exception:  # pragma: no cover
+        limiter = None
+    tokens = 0
+    runs = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.forward(x["q"], x["k"], x["v"], x["g"], x["beta"], x["u"], x["alpha"], x["gamma"],
+                       x["conv_w"], w.L)
+        tokens += w.B * w.T
+        runs += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    if limiter is not None:
+        limiter.unregister() if hasattr(limiter, "unregister") else None
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{runs} full pass(es) of {w.name} (B={w.B}, H={w.H}, T={w.T}), all heads, "
+                      f"float64 numpy, one thread, {dt:.1f} s"}
+
+
+def calibrate_copy(mb):
+    import torch
+    n = mb * (1 << 20) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": n * 4, "launches": 3}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="rec16k_bf16")
+    ap.add_argument("--sets", type=int, default=0, help="input sets rotated (0: enough to exceed the MALL)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MB")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the forward has no multi-GPU path "
+              "(pairs and sequence segments would shard with no exchange but a small operator "
+              "all-gather; see DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
+
+    import numpy as np
+    import torch
+
+    import delta_rule_sequence_amd as prism
+    import workloads
+
+    w = workloads.workload(args.workload)
+    lib = prism.load_library()
+    dt = prism.PRISM_BF16 if w.dtype == "bf16" else prism.PRISM_F32
+    in_bytes, path_bytes = algorithmic_bytes(w)
+    set_bytes = w.pairs * w.T * in_bytes
+    nsets = args.sets or max(1, -(-2 * MALL_BYTES // set_bytes))
+    print(f"[bench] {w.name}: {nsets} input set(s) of {set_bytes / 1e6:.1f} MB", file=sys.stderr, flush=True)
+
+    host_sets, dev_sets = [], []
+    for i in range(nsets):
+        x = workloads.generate(w, seed=w.seed + 1000 * i)
+        if i == 0:
+            host_sets.append(x)
+        dev_sets.append(workloads.to_torch(x, w.dtype, "cuda"))
+    vt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    o = torch.empty((w.B, w.H, w.T, w.dv), dtype=vt, device="cuda")
+    S = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device="cuda")
+    need = lib.prism_fwd_workspace_bytes(w.B, w.H, w.T, w.dk, w.dv, w.L, w.chunk, dt)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    sh = ctypes.c_void_p(stream.cuda_stream)
+
+    def argv(d):
+        p = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())  # noqa: E731
+        return [p(d["q"]), p(d["k"]), p(d["v"]), p(d["g"]), p(d["beta"]), p(d["u"]), p(d["alpha"]),
+                p(d["gamma"]), p(d["conv_w"]), w.B, w.H, w.T, w.dk, w.dv, w.L, w.chunk, dt,
+                ctypes.c_void_p(o.data_ptr()), ctypes.c_void_p(S.data_ptr()),
+                ctypes.c_void_p(ws.data_ptr()), ctypes.c_size_t(need)]
+
+    calls = [argv(d) for d in dev_sets]
+    for i in range(args.warmup):
+        st = lib.prism_fwd(*calls[i % nsets], sh)
+        if st != 0:
+            raise RuntimeError(prism.status_string(st))
+    torch.cuda.synchronize()
+
+    hip = Hip()
+    evs = hip.events(4 * args.steps)
+    ev_arrays = [(ctypes.c_void_p * 4)(*evs[4 * i:4 * i + 4]) for i in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        st = lib.prism_fwd_timed(*calls[i % nsets], ev_arrays[i], sh)
+        if st != 0:
+            raise RuntimeError(prism.status_string(st))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = np.array([[hip.elapsed_ms(evs[4 * i + j], evs[4 * i + j + 1]) for j in range(3)]
+                    for i in range(args.steps)])
+    span_ms = hip.elapsed_ms(evs[0], evs[4 * args.steps - 1])
+    hip.destroy(evs)
+
+    ms_per_step = 1e3 * wall / args.steps
+    tokens = w.B * w.T
+    sweep_ms = float(per[:, 0].mean())
+    sweep_bytes = w.pairs * w.T * in_bytes + w.H * 4 * w.dv * 4
+    achieved = sweep_bytes / (sweep_ms * 1e-3) / 1e9
+    traffic = load_traffic(w.name)
+
+    out = {
+        "metric": "fwd tokens/sec at T=16K,H=4,d=64,L=4 bf16; % of HBM/MFMA roofline",
+        "value": tokens / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded generator; random inputs of the workload's shapes and distributions)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "dk": w.dk, "dv": w.dv, "L": w.L,
+                   "chunk": w.chunk, "input_sets": nsets},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "seg_local_kernel", "algorithmic_bytes_per_launch": sweep_bytes},
+        "path": {"algorithmic_bytes_per_step": w.pairs * w.T * path_bytes,
+                 "hbm_roofline_tokens_per_s": tokens * HBM_PEAK_GBS * 1e9 / (w.pairs * w.T * path_bytes),
+                 "kernel_ms": {"seg_local": sweep_ms, "seg_scan": float(per[:, 1].mean()),
+                               "seg_fixup": float(per[:, 2].mean())},
+                 "event_span_ms_per_step": span_ms / args.steps},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(w, host_sets[0])
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

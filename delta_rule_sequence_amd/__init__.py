@@ -1,0 +1,148 @@
+"""Python binding of libprism: the PRISM rank-L gated delta-rule forward on MI355X.
+
+Argument marshalling only.  Every step of the forward (ShortConv anchor,
+residual chain, chunked UT/WY delta rule, segment scan, output correction) runs
+in the HIP kernels of libprism.so; PyTorch supplies device memory and the
+stream.  There is no CPU path: without the built library every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional, Tuple
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libprism.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "prism.h")
+
+PRISM_F32, PRISM_BF16 = 0, 1
+_lib = None
+
+
+class PrismError(RuntimeError):
+    pass
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libprism.so (built by delta_rule_sequence_amd.build); raise if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise PrismError(f"{LIB_PATH} is missing: build it with `python -m delta_rule_sequence_amd.build` "
+                         "(or __graft_entry__.build())")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, fp, i, sz = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    fwd_args = [vp, vp, vp, fp, fp, vp, fp, vp, fp, i, i, i, i, i, i, i, i, vp, fp, vp, sz]
+    lib.prism_fwd.argtypes = fwd_args + [vp]
+    lib.prism_fwd.restype = ctypes.c_int
+    lib.prism_fwd_seg.argtypes = fwd_args + [i, vp]
+    lib.prism_fwd_seg.restype = ctypes.c_int
+    lib.prism_fwd_timed.argtypes = fwd_args + [vp, vp]
+    lib.prism_fwd_timed.restype = ctypes.c_int
+    lib.prism_fwd_workspace_bytes.argtypes = [i] * 8
+    lib.prism_fwd_workspace_bytes.restype = sz
+    lib.prism_fwd_seg_workspace_bytes.argtypes = [i] * 9
+    lib.prism_fwd_seg_workspace_bytes.restype = sz
+    lib.prism_status_string.argtypes = [ctypes.c_int]
+    lib.prism_status_string.restype = ctypes.c_char_p
+    lib.prism_version.argtypes = []
+    lib.prism_version.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def header_functions() -> list:
+    """Names of the functions include/prism.h declares."""
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(prism_[a-z_]+)\s*\(", text)))
+
+
+def status_string(code: int) -> str:
+    return load_library().prism_status_string(code).decode()
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return PRISM_BF16
+    if t.dtype == torch.float32:
+        return PRISM_F32
+    raise PrismError(f"unsupported dtype {t.dtype}: q, k, v, u, gamma must be bfloat16 or float32")
+
+
+def workspace_bytes(B: int, H: int, T: int, dk: int, dv: int, L: int, chunk: int, dtype_code: int,
+                    seg_chunks: Optional[int] = None) -> int:
+    lib = load_library()
+    if seg_chunks is None:
+        return int(lib.prism_fwd_workspace_bytes(B, H, T, dk, dv, L, chunk, dtype_code))
+    return int(lib.prism_fwd_seg_workspace_bytes(B, H, T, dk, dv, L, chunk, dtype_code, seg_chunks))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def fwd(q, k, v, g, beta, u=None, alpha=None, gamma=None, conv_w=None, L: int = 1, chunk: int = 64,
+        seg_chunks: Optional[int] = None, out: Optional[Tuple] = None, workspace=None, stream=None):
+    """o, S_final = fwd(q, k, v, g, beta, u, alpha, gamma, conv_w, L, chunk).
+
+    q, k [B,H,T,dk]; v [B,H,T,dv]; u [B,H,T,L-1,dk]; gamma [B,H,T,L-1,dv] in
+    bfloat16 or float32 (one dtype); g, beta [B,H,T], alpha [B,H,T,L], conv_w
+    [H,4,dv] float32.  All on one GPU, contiguous.  Returns o [B,H,T,dv] (input
+    dtype) and S_final [B,H,dk,dv] (float32, the transposed final state).
+    """
+    import torch
+    lib = load_library()
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    dt = _dtype_code(q)
+    dev = q.device
+    if dev.type != "cuda":
+        raise PrismError("inputs must be on a GPU")
+    vec = [("q", q), ("k", k), ("v", v)] + ([("u", u), ("gamma", gamma)] if L > 1 else [])
+    flt = [("g", g), ("beta", beta)] + ([("alpha", alpha), ("conv_w", conv_w)] if L > 1 else [])
+    for name, t in vec + flt:
+        if t is None:
+            raise PrismError(f"{name} is required when L = {L}")
+        if t.device != dev or not t.is_contiguous():
+            raise PrismError(f"{name} must be a contiguous tensor on {dev}")
+    for name, t in vec:
+        if t.dtype != q.dtype:
+            raise PrismError(f"{name} must have dtype {q.dtype}")
+    for name, t in flt:
+        if t.dtype != torch.float32:
+            raise PrismError(f"{name} must be float32")
+    shapes = {"k": (B, H, T, dk), "v": (B, H, T, dv), "g": (B, H, T), "beta": (B, H, T)}
+    if L > 1:
+        shapes.update({"u": (B, H, T, L - 1, dk), "gamma": (B, H, T, L - 1, dv),
+                       "alpha": (B, H, T, L), "conv_w": (H, 4, dv)})
+    for name, t in vec + flt:
+        if name in shapes and tuple(t.shape) != shapes[name]:
+            raise PrismError(f"{name} has shape {tuple(t.shape)}, expected {shapes[name]}")
+    if out is None:
+        o = torch.empty((B, H, T, dv), dtype=q.dtype, device=dev)
+        S = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    else:
+        o, S = out
+    need = workspace_bytes(B, H, T, dk, dv, L, chunk, dt, seg_chunks)
+    if need == 0:
+        # let the library report which argument is wrong
+        need = 1
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    s = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
+    args = [_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+            _ptr(u) if L > 1 else None, _ptr(alpha) if L > 1 else None,
+            _ptr(gamma) if L > 1 else None, _ptr(conv_w) if L > 1 else None,
+            B, H, T, dk, dv, L, chunk, dt, _ptr(o), _ptr(S),
+            ctypes.c_void_p(workspace.data_ptr()), workspace.numel()]
+    if seg_chunks is None:
+        st = lib.prism_fwd(*args, ctypes.c_void_p(s))
+    else:
+        st = lib.prism_fwd_seg(*args, seg_chunks, ctypes.c_void_p(s))
+    if st != 0:
+        raise PrismError(f"prism_fwd failed: {status_string(st)}")
+    return o, S

@@ -1,0 +1,215 @@
+// prism_api.hip - C ABI of the PRISM rank-L gated delta-rule forward (see include/prism.h).
+//
+// Host side only: argument validation, workspace layout, segment sizing and the
+// three kernel launches.  Every check runs before anything is enqueued.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "prism.h"
+#include "prism_kernels.h"
+
+namespace {
+
+using prism::bf16_t;
+using prism::FwdArgs;
+
+constexpr size_t kAlign = 256;
+constexpr int kTargetWorkgroups = 512;  // about two per CU on a 256-CU MI355X
+
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// a * b with overflow detection (returns false on overflow)
+inline bool mul_ok(size_t a, size_t b, size_t* out) {
+  if (a != 0 && b > SIZE_MAX / a) return false;
+  *out = a * b;
+  return true;
+}
+
+struct Plan {
+  int P, nch, seg_chunks, nseg;
+  size_t off_oloc, off_qhat, off_aagg, off_bagg, off_hin, total;
+};
+
+bool valid_dim(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+
+template <class E, int D, int C>
+constexpr bool fits() { return prism::SegLds<E, D, D, C>::fits; }
+
+bool lds_fits(prism_dtype dt, int d, int C) {
+#define PRISM_FITS(E) \
+  switch (d) { \
+    case 16: return C == 16 ? fits<E, 16, 16>() : C == 32 ? fits<E, 16, 32>() : fits<E, 16, 64>(); \
+    case 32: return C == 16 ? fits<E, 32, 16>() : C == 32 ? fits<E, 32, 32>() : fits<E, 32, 64>(); \
+    case 64: return C == 16 ? fits<E, 64, 16>() : C == 32 ? fits<E, 64, 32>() : fits<E, 64, 64>(); \
+    default: return C == 16 ? fits<E, 128, 16>() : C == 32 ? fits<E, 128, 32>() : fits<E, 128, 64>(); \
+  }
+  if (dt == PRISM_BF16) { PRISM_FITS(bf16_t) }
+  PRISM_FITS(float)
+#undef PRISM_FITS
+}
+
+// Shape checks shared by the size query and the forward call.
+prism_status check_shape(int B, int H, int T, int dk, int dv, int L, int chunk, prism_dtype dt) {
+  if (B <= 0 || H <= 0 || T <= 0) return PRISM_ERR_INVALID_ARG;
+  if (dt != PRISM_F32 && dt != PRISM_BF16) return PRISM_ERR_INVALID_ARG;
+  if (L < 1 || L > 8) return PRISM_ERR_UNSUPPORTED;
+  if (!valid_dim(dk) || !valid_dim(dv)) return PRISM_ERR_UNSUPPORTED;
+  if (dk != dv) return PRISM_ERR_UNSUPPORTED;
+  if (chunk != 16 && chunk != 32 && chunk != 64) return PRISM_ERR_UNSUPPORTED;
+  if (!lds_fits(dt, dk, chunk)) return PRISM_ERR_UNSUPPORTED;
+  return PRISM_OK;
+}
+
+prism_status make_plan(int B, int H, int T, int dk, int dv, int L, int chunk, prism_dtype dt,
+                       int seg_chunks, Plan* pl) {
+  prism_status st = check_shape(B, H, T, dk, dv, L, chunk, dt);
+  if (st != PRISM_OK) return st;
+  if (seg_chunks < 0) return PRISM_ERR_INVALID_ARG;
+  size_t P;
+  if (!mul_ok((size_t)B, (size_t)H, &P) || P > (size_t)INT32_MAX / 2) return PRISM_ERR_INVALID_ARG;
+  if (P > 65535) return PRISM_ERR_UNSUPPORTED;  // (b, h) pairs map to grid.y
+  const size_t nch = ((size_t)T + chunk - 1) / chunk;
+  if (seg_chunks == 0) {
+    size_t nseg_target = ((size_t)kTargetWorkgroups + P - 1) / P;
+    if (nseg_target < 1) nseg_target = 1;
+    seg_chunks = (int)((nch + nseg_target - 1) / nseg_target);
+    if (seg_chunks < 1) seg_chunks = 1;
+  }
+  const size_t nseg = (nch + seg_chunks - 1) / seg_chunks;
+  size_t Tpad = nch * (size_t)chunk, a, b, c;
+  size_t sz_oloc, sz_qhat, sz_agg_a, sz_agg_b;
+  if (!mul_ok(P, Tpad, &a) || !mul_ok(a, (size_t)dv * 4, &sz_oloc)) return PRISM_ERR_INVALID_ARG;
+  if (!mul_ok(a, (size_t)dk * 4, &sz_qhat)) return PRISM_ERR_INVALID_ARG;
+  if (!mul_ok(P, nseg, &b) || !mul_ok(b, (size_t)dk * dk * 4, &sz_agg_a)) return PRISM_ERR_INVALID_ARG;
+  if (!mul_ok(b, (size_t)dk * dv * 4, &sz_agg_b)) return PRISM_ERR_INVALID_ARG;
+  // inputs must be addressable too: P*T*(L-1)*max(dk,dv) elements
+  if (!mul_ok(P, (size_t)T, &c) || !mul_ok(c, (size_t)L * (dk > dv ? dk : dv) * 4, &c))
+    return PRISM_ERR_INVALID_ARG;
+  pl->P = (int)P;
+  pl->nch = (int)nch;
+  pl->seg_chunks = seg_chunks;
+  pl->nseg = (int)nseg;
+  pl->off_oloc = 0;
+  pl->off_qhat = align_up(pl->off_oloc + sz_oloc);
+  pl->off_aagg = align_up(pl->off_qhat + sz_qhat);
+  pl->off_bagg = align_up(pl->off_aagg + sz_agg_a);
+  pl->off_hin = align_up(pl->off_bagg + sz_agg_b);
+  pl->total = align_up(pl->off_hin + sz_agg_b);
+  if (pl->total < sz_oloc) return PRISM_ERR_INVALID_ARG;
+  return PRISM_OK;
+}
+
+inline bool record(hipEvent_t* ev, int i, hipStream_t stream) {
+  return ev == nullptr || hipEventRecord(ev[i], stream) == hipSuccess;
+}
+
+template <class E, int D, int C>
+prism_status launch(const FwdArgs& a, const Plan& pl, hipEvent_t* ev, hipStream_t stream) {
+  if constexpr (!prism::SegLds<E, D, D, C>::fits) {
+    return PRISM_ERR_UNSUPPORTED;
+  } else {
+    if (!record(ev, 0, stream)) return PRISM_ERR_HIP;
+    hipLaunchKernelGGL((prism::seg_local_kernel<E, D, D, C>), dim3(pl.nseg, pl.P), dim3(256), 0, stream, a);
+    if (hipGetLastError() != hipSuccess || !record(ev, 1, stream)) return PRISM_ERR_HIP;
+    hipLaunchKernelGGL((prism::seg_scan_kernel<D, D>), dim3(pl.P, D / 16), dim3(256), 0, stream, a);
+    if (hipGetLastError() != hipSuccess || !record(ev, 2, stream)) return PRISM_ERR_HIP;
+    hipLaunchKernelGGL((prism::seg_fixup_kernel<E, D, D, C>), dim3(pl.nch, pl.P), dim3(256), 0, stream, a);
+    if (hipGetLastError() != hipSuccess || !record(ev, 3, stream)) return PRISM_ERR_HIP;
+    return PRISM_OK;
+  }
+}
+
+template <class E>
+prism_status dispatch(int d, int C, const FwdArgs& a, const Plan& pl, hipEvent_t* ev, hipStream_t s) {
+  switch (d) {
+    case 16: return C == 16 ? launch<E, 16, 16>(a, pl, ev, s) : C == 32 ? launch<E, 16, 32>(a, pl, ev, s) : launch<E, 16, 64>(a, pl, ev, s);
+    case 32: return C == 16 ? launch<E, 32, 16>(a, pl, ev, s) : C == 32 ? launch<E, 32, 32>(a, pl, ev, s) : launch<E, 32, 64>(a, pl, ev, s);
+    case 64: return C == 16 ? launch<E, 64, 16>(a, pl, ev, s) : C == 32 ? launch<E, 64, 32>(a, pl, ev, s) : launch<E, 64, 64>(a, pl, ev, s);
+    default: return C == 16 ? launch<E, 128, 16>(a, pl, ev, s) : C == 32 ? launch<E, 128, 32>(a, pl, ev, s) : launch<E, 128, 64>(a, pl, ev, s);
+  }
+}
+
+prism_status fwd_impl(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                      const void* u, const float* alpha, const void* gamma, const float* conv_w,
+                      int B, int H, int T, int dk, int dv, int L, int chunk, prism_dtype dt,
+                      void* o, float* S_final, void* workspace, size_t workspace_bytes,
+                      int seg_chunks, hipEvent_t* ev, hipStream_t stream) {
+  Plan pl;
+  prism_status st = make_plan(B, H, T, dk, dv, L, chunk, dt, seg_chunks, &pl);
+  if (st != PRISM_OK) return st;
+  if (!q || !k || !v || !g || !beta || !o || !S_final) return PRISM_ERR_INVALID_ARG;
+  if (L > 1 && (!u || !alpha || !gamma || !conv_w)) return PRISM_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < pl.total) return PRISM_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  FwdArgs a;
+  a.q = q; a.k = k; a.v = v; a.u = u; a.gamma = gamma;
+  a.g = g; a.beta = beta; a.alpha = alpha; a.conv_w = conv_w;
+  a.o = o; a.S_final = S_final;
+  a.Oloc = reinterpret_cast<float*>(ws + pl.off_oloc);
+  a.Qhat = reinterpret_cast<float*>(ws + pl.off_qhat);
+  a.Aagg = reinterpret_cast<float*>(ws + pl.off_aagg);
+  a.Bagg = reinterpret_cast<float*>(ws + pl.off_bagg);
+  a.Hin = reinterpret_cast<float*>(ws + pl.off_hin);
+  a.B = B; a.H = H; a.T = T; a.L = L;
+  a.nch = pl.nch; a.seg_chunks = pl.seg_chunks; a.nseg = pl.nseg;
+  return dt == PRISM_BF16 ? dispatch<bf16_t>(dk, chunk, a, pl, ev, stream)
+                          : dispatch<float>(dk, chunk, a, pl, ev, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t prism_fwd_workspace_bytes(int B, int H, int T, int dk, int dv, int L, int chunk, prism_dtype dt) {
+  Plan pl;
+  return make_plan(B, H, T, dk, dv, L, chunk, dt, 0, &pl) == PRISM_OK ? pl.total : 0;
+}
+
+size_t prism_fwd_seg_workspace_bytes(int B, int H, int T, int dk, int dv, int L, int chunk, prism_dtype dt,
+                                     int seg_chunks) {
+  Plan pl;
+  return make_plan(B, H, T, dk, dv, L, chunk, dt, seg_chunks, &pl) == PRISM_OK ? pl.total : 0;
+}
+
+prism_status prism_fwd(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                       const void* u, const float* alpha, const void* gamma, const float* conv_w,
+                       int B, int H, int T, int dk, int dv, int L, int chunk, prism_dtype dt,
+                       void* o, float* S_final, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return fwd_impl(q, k, v, g, beta, u, alpha, gamma, conv_w, B, H, T, dk, dv, L, chunk, dt, o, S_final,
+                  workspace, workspace_bytes, 0, nullptr, stream);
+}
+
+prism_status prism_fwd_timed(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                             const void* u, const float* alpha, const void* gamma, const float* conv_w,
+                             int B, int H, int T, int dk, int dv, int L, int chunk, prism_dtype dt,
+                             void* o, float* S_final, void* workspace, size_t workspace_bytes,
+                             hipEvent_t* events, hipStream_t stream) {
+  if (!events) return PRISM_ERR_INVALID_ARG;
+  return fwd_impl(q, k, v, g, beta, u, alpha, gamma, conv_w, B, H, T, dk, dv, L, chunk, dt, o, S_final,
+                  workspace, workspace_bytes, 0, events, stream);
+}
+
+prism_status prism_fwd_seg(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                           const void* u, const float* alpha, const void* gamma, const float* conv_w,
+                           int B, int H, int T, int dk, int dv, int L, int chunk, prism_dtype dt,
+                           void* o, float* S_final, void* workspace, size_t workspace_bytes,
+                           int seg_chunks, hipStream_t stream) {
+  if (seg_chunks <= 0) return PRISM_ERR_INVALID_ARG;
+  return fwd_impl(q, k, v, g, beta, u, alpha, gamma, conv_w, B, H, T, dk, dv, L, chunk, dt, o, S_final,
+                  workspace, workspace_bytes, seg_chunks, nullptr, stream);
+}
+
+const char* prism_status_string(prism_status s) {
+  switch (s) {
+    case PRISM_OK: return "PRISM_OK";
+    case PRISM_ERR_INVALID_ARG: return "PRISM_ERR_INVALID_ARG: null pointer, non-positive size or size overflow";
+    case PRISM_ERR_UNSUPPORTED: return "PRISM_ERR_UNSUPPORTED: no kernel for this shape / dtype / L / chunk";
+    case PRISM_ERR_WORKSPACE: return "PRISM_ERR_WORKSPACE: workspace missing or too small";
+    case PRISM_ERR_HIP: return "PRISM_ERR_HIP: a HIP launch failed";
+  }
+  return "PRISM_ERR_UNKNOWN";
+}
+
+const char* prism_version(void) { return "0.1.0"; }
+
+}  // extern "C"

@@ -1,0 +1,570 @@
+// prism_kernels.h - HIP kernels of the PRISM rank-L gated delta-rule forward (gfx950).
+//
+// Three launches per forward:
+//   seg_local  : one workgroup per (segment, pair).  Sweeps the segment's chunks
+//                from a zero state with the chunked UT/WY form of the delta rule,
+//                fusing the ShortConv anchor and the residual chain (prologue),
+//                and writes the zero-start outputs O_loc, the output-correction
+//                rows Qhat and the segment operator (A_seg, B_seg).
+//   seg_scan   : one workgroup per (pair, 16 state columns).  Runs the short
+//                sequential recurrence H_in(s+1) = A_s H_in(s) + B_s over the
+//                segments (float32) and writes the final state.
+//   seg_fixup  : one workgroup per (chunk, pair).  o = O_loc + Qhat H_in(seg).
+//
+// Math (state H = S^T, dk x dv; per chunk of C tokens, start state H):
+//   b = cumsum(log g), G = exp(b), D_j = exp(b_last - b_j), Gam_ij = exp(b_i - b_j), j <= i
+//   M  = I + strict(diag(beta) (Gam * K K^T))                (unit lower triangular)
+//   V' = V - sum_l strict(Gam * K U_l^T) R_l
+//   Uc = M^-1 diag(beta) V',   Wc = M^-1 diag(beta G) K
+//   E  = Uc - Wc H
+//   O  = diag(G) Q H + lower(Gam * Q K^T) E + sum_l lower(Gam * Q U_l^T) R_l
+//   H' = G_last H + K^T diag(D) E + sum_l U_l^T diag(D) R_l
+// The forgetting operator is the Gated DeltaNet one and the write is the rank-L
+// injection of the PRISM reading notes (liuzhao09.github.io, "PRISM", sections
+// 2.2-2.3); associativity of S_t = S_{t-1} A_t + B_t (notes section 2.1, Tencent
+// Ads article section 01-二) is what lets segments start from zero and be
+// corrected afterwards:  H_chunk_start = H_loc + A_acc H_in,
+//   O = O_loc + Qhat H_in,  Qhat = (diag(G) Q - lower(Gam * Q K^T) Wc) A_acc.
+#pragma once
+#include "prism_tile.h"
+
+namespace prism {
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* u;
+  const void* gamma;
+  const float* g;
+  const float* beta;
+  const float* alpha;
+  const float* conv_w;
+  void* o;
+  float* S_final;
+  float* Oloc;   // [P][Tpad][dv]
+  float* Qhat;   // [P][Tpad][dk]
+  float* Aagg;   // [P][nseg][dk][dk]
+  float* Bagg;   // [P][nseg][dk][dv]
+  float* Hin;    // [P][nseg][dk][dv]
+  int B, H, T, L;
+  int nch;          // chunks per sequence
+  int seg_chunks;   // chunks per segment
+  int nseg;         // segments per sequence
+};
+
+// LDS plan of seg_local (bytes).  Row strides are padded by 16 bytes.
+template <class E, int DK, int DV, int C>
+struct SegLds {
+  static constexpr int PADE = 16 / (int)sizeof(E);
+  static constexpr int LDK = DK + PADE, LDC = C + PADE;
+  static constexpr int SROWS = DV > DK ? DV : DK;
+  static constexpr int LDF = C + 1;  // float32 solve arrays
+  static constexpr size_t oQ = 0;
+  static constexpr size_t oK = oQ + (size_t)C * LDK * sizeof(E);
+  static constexpr size_t oP = oK + (size_t)C * LDK * sizeof(E);
+  static constexpr size_t oT = oP + (size_t)C * LDC * sizeof(E);
+  static constexpr size_t oW = oT + (size_t)C * LDC * sizeof(E);
+  static constexpr size_t oS = oW + (size_t)C * LDK * sizeof(E);
+  static constexpr size_t oGate = oS + (size_t)SROWS * LDK * sizeof(E);
+  static constexpr size_t nGate = 5 * C + 8 * C;  // b, G, D, beta, beta*G, alpha[C][8]
+  static constexpr size_t oX = oGate + nGate * sizeof(float);
+  static constexpr size_t xLoop = (size_t)C * LDK * sizeof(E) + 2 * (size_t)C * LDC * sizeof(E);
+  static constexpr size_t xSolve = 2 * (size_t)C * LDF * sizeof(float) + 3 * 16 * 17 * sizeof(float);
+  static constexpr size_t xQt = (size_t)C * LDK * sizeof(E);
+  static constexpr size_t xSize = xLoop > xSolve ? (xLoop > xQt ? xLoop : xQt) : (xSolve > xQt ? xSolve : xQt);
+  static constexpr size_t total = oX + xSize;
+  static constexpr bool fits = total <= 160 * 1024;
+};
+
+template <class E, int DK, int DV, int C>
+__global__ __launch_bounds__(256, 1) void seg_local_kernel(FwdArgs a) {
+  using Ly = SegLds<E, DK, DV, C>;
+  constexpr int LDK = Ly::LDK, LDC = Ly::LDC, LDF = Ly::LDF;
+  constexpr int MT = C / 16, KT = DK / 16, VT = DV / 16;
+  constexpr int NVW = (VT + 3) / 4;  // value column blocks per wave
+  constexpr int NKW = (KT + 3) / 4;  // key column blocks per wave
+  __shared__ __align__(16) unsigned char smem[Ly::total];
+  E* sQ = reinterpret_cast<E*>(smem + Ly::oQ);
+  E* sK = reinterpret_cast<E*>(smem + Ly::oK);
+  E* sP = reinterpret_cast<E*>(smem + Ly::oP);
+  E* sT = reinterpret_cast<E*>(smem + Ly::oT);
+  E* sW = reinterpret_cast<E*>(smem + Ly::oW);
+  E* sS = reinterpret_cast<E*>(smem + Ly::oS);
+  float* sB = reinterpret_cast<float*>(smem + Ly::oGate);
+  float* sG = sB + C;
+  float* sD = sG + C;
+  float* sBeta = sD + C;
+  float* sBG = sBeta + C;
+  float* sAlpha = sBG + C;  // [C][8]
+  unsigned char* X = smem + Ly::oX;
+  E* sU = reinterpret_cast<E*>(X);
+  E* sX1 = reinterpret_cast<E*>(X + (size_t)C * LDK * sizeof(E));
+  E* sX2 = sX1 + C * LDC;
+  float* sMf = reinterpret_cast<float*>(X);
+  float* sTf = sMf + C * LDF;
+  float* sTmp = sTf + C * LDF;  // [3][16][17]
+  E* sQt = reinterpret_cast<E*>(X);
+
+  const int tid = threadIdx.x, w = wave_id(), l = lane_id(), g4 = (l >> 4) * 4, li = l & 15;
+  const int seg = blockIdx.x, pr = blockIdx.y;
+  const int hd = pr % a.H;
+  const int T = a.T, L = a.L, Lm1 = L - 1;
+  const int c_begin = seg * a.seg_chunks;
+  const int c_end = min(a.nch, c_begin + a.seg_chunks);
+  const int Tpad = a.nch * C;
+  const E* q = reinterpret_cast<const E*>(a.q) + (size_t)pr * T * DK;
+  const E* k = reinterpret_cast<const E*>(a.k) + (size_t)pr * T * DK;
+  const E* v = reinterpret_cast<const E*>(a.v) + (size_t)pr * T * DV;
+  const E* u = L > 1 ? reinterpret_cast<const E*>(a.u) + (size_t)pr * T * Lm1 * DK : nullptr;
+  const E* gam = L > 1 ? reinterpret_cast<const E*>(a.gamma) + (size_t)pr * T * Lm1 * DV : nullptr;
+  const float* gg = a.g + (size_t)pr * T;
+  const float* bb = a.beta + (size_t)pr * T;
+  const float* al = L > 1 ? a.alpha + (size_t)pr * T * L : nullptr;
+  const float* cw = L > 1 ? a.conv_w + (size_t)hd * 4 * DV : nullptr;
+
+  // State tiles owned by this wave: value column blocks vt = w + 4*jv, key
+  // column blocks kt' = w + 4*jk.
+  f32x4 Hs[NVW][KT];   // H(kt, vt)
+  f32x4 As[NKW][KT];   // A_acc(kt, kt')
+#pragma unroll
+  for (int jv = 0; jv < NVW; ++jv)
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) Hs[jv][kt] = zero4();
+#pragma unroll
+  for (int jk = 0; jk < NKW; ++jk)
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) {
+      const int kc = w + 4 * jk;
+      f32x4 t = zero4();
+      if (kc == kt) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) t[r] = (g4 + r == li) ? 1.f : 0.f;
+      }
+      As[jk][kt] = t;
+    }
+
+  for (int c = c_begin; c < c_end; ++c) {
+    const int t0 = c * C;
+    const int nvalid = min(C, T - t0);
+
+    // ---- stage 0: state operand (H^T) into LDS, Q / K rows, gates --------------
+#pragma unroll
+    for (int jv = 0; jv < NVW; ++jv) {
+      const int vt = w + 4 * jv;
+      if (vt < VT) {
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            sS[(16 * vt + li) * LDK + 16 * kt + g4 + r] = from_f<E>(Hs[jv][kt][r]);
+      }
+    }
+    {
+      constexpr int VEC = 16 / sizeof(E);
+      constexpr int PER_ROW = DK / VEC;
+      for (int idx = tid; idx < C * PER_ROW; idx += 256) {
+        const int row = idx / PER_ROW, cv = (idx % PER_ROW) * VEC;
+        uint4 qv = make_uint4(0, 0, 0, 0), kv = make_uint4(0, 0, 0, 0);
+        if (row < nvalid) {
+          qv = *reinterpret_cast<const uint4*>(q + (size_t)(t0 + row) * DK + cv);
+          kv = *reinterpret_cast<const uint4*>(k + (size_t)(t0 + row) * DK + cv);
+        }
+        *reinterpret_cast<uint4*>(sQ + row * LDK + cv) = qv;
+        *reinterpret_cast<uint4*>(sK + row * LDK + cv) = kv;
+      }
+    }
+    if (w == 0) {
+      const bool ok = l < nvalid;
+      float lam = (ok && l < C) ? __logf(gg[t0 + l]) : 0.f;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        float y = __shfl_up(lam, off);
+        if (l >= off) lam += y;
+      }
+      const float blast = __shfl(lam, C - 1);
+      if (l < C) {
+        const float be = ok ? bb[t0 + l] : 0.f;
+        const float G = __expf(lam);
+        sB[l] = lam;
+        sG[l] = G;
+        sD[l] = __expf(blast - lam);
+        sBeta[l] = be;
+        sBG[l] = be * G;
+        for (int j = 0; j < L; ++j) sAlpha[l * 8 + j] = (ok && L > 1) ? al[(size_t)(t0 + l) * L + j] : 0.f;
+      }
+    }
+    __syncthreads();
+
+    // ---- prologue: V' init, anchor and initial residual, in tile layout ------
+    f32x4 Vp[NVW][MT], Oc[NVW][MT], Rr[NVW][MT], HB[NVW][KT];
+#pragma unroll
+    for (int jv = 0; jv < NVW; ++jv) {
+      const int vt = w + 4 * jv;
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) HB[jv][kt] = zero4();
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        Oc[jv][mt] = zero4();
+        f32x4 vv = zero4(), rr = zero4();
+        if (vt < VT) {
+          const int col = 16 * vt + li;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int t = 16 * mt + g4 + r;
+            if (t < nvalid) {
+              const int tg = t0 + t;
+              const float x = to_f(v[(size_t)tg * DV + col]);
+              vv[r] = x;
+              if (L > 1) {
+                float anc = 0.f;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                  const int ts = tg - 3 + j;
+                  if (ts >= 0) anc += cw[j * DV + col] * to_f(v[(size_t)ts * DV + col]);
+                }
+                rr[r] = x - anc;
+              }
+            }
+          }
+        }
+        Vp[jv][mt] = vv;
+        Rr[jv][mt] = rr;
+      }
+    }
+
+    // ---- P = lower(Gam * Q K^T) -----------------------------------------------
+    for (int tI = w; tI < MT * MT; tI += 4) {
+      const int mt = tI / MT, jt = tI % MT;
+      f32x4 acc = zero4();
+      if (jt <= mt) mm_ll<E>(acc, sQ, LDK, 16 * mt, sK, LDK, 16 * jt, DK);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * mt + g4 + r, j = 16 * jt + li;
+        const float val = (j <= i) ? __expf(sB[i] - sB[j]) * acc[r] : 0.f;
+        sP[i * LDC + j] = from_f<E>(val);
+      }
+    }
+
+    // ---- rank-L terms, one refinement step at a time ---------------------------
+    for (int lr = 1; lr < L; ++lr) {
+      {  // U_l rows into LDS
+        constexpr int VEC = 16 / sizeof(E);
+        constexpr int PER_ROW = DK / VEC;
+        for (int idx = tid; idx < C * PER_ROW; idx += 256) {
+          const int row = idx / PER_ROW, cv = (idx % PER_ROW) * VEC;
+          uint4 uv = make_uint4(0, 0, 0, 0);
+          if (row < nvalid)
+            uv = *reinterpret_cast<const uint4*>(u + ((size_t)(t0 + row) * Lm1 + (lr - 1)) * DK + cv);
+          *reinterpret_cast<uint4*>(sU + row * LDK + cv) = uv;
+        }
+      }
+      // residual step and written values R_l = alpha_l r_l (tile layout)
+      f32x4 R[NVW][MT];
+#pragma unroll
+      for (int jv = 0; jv < NVW; ++jv) {
+        const int vt = w + 4 * jv;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          f32x4 rv = zero4();
+          if (vt < VT) {
+            const int col = 16 * vt + li;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int t = 16 * mt + g4 + r;
+              if (t < nvalid) {
+                const float gm = to_f(gam[((size_t)(t0 + t) * Lm1 + (lr - 1)) * DV + col]);
+                const float x = Rr[jv][mt][r] * (1.f - sAlpha[t * 8 + lr - 1] * gm);
+                Rr[jv][mt][r] = x;
+                rv[r] = sAlpha[t * 8 + lr] * x;
+              }
+            }
+          }
+          R[jv][mt] = rv;
+        }
+      }
+      __syncthreads();
+      // X1 = -strict(Gam * K U^T), X2 = lower(Gam * Q U^T)
+      for (int tI = w; tI < 2 * MT * MT; tI += 4) {
+        const int which = tI / (MT * MT), t2 = tI % (MT * MT);
+        const int mt = t2 / MT, jt = t2 % MT;
+        f32x4 acc = zero4();
+        if (jt <= mt) mm_ll<E>(acc, which ? sQ : sK, LDK, 16 * mt, sU, LDK, 16 * jt, DK);
+        E* dst = which ? sX2 : sX1;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = 16 * mt + g4 + r, j = 16 * jt + li;
+          float val = 0.f;
+          if (which ? (j <= i) : (j < i)) val = __expf(sB[i] - sB[j]) * acc[r];
+          dst[i * LDC + j] = from_f<E>(which ? val : -val);
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int jv = 0; jv < NVW; ++jv) {
+        if (w + 4 * jv < VT) {
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) {
+            mm_lt<E, MT>(Vp[jv][mt], sX1, LDC, 16 * mt, R[jv], nullptr, C);
+            mm_lt<E, MT>(Oc[jv][mt], sX2, LDC, 16 * mt, R[jv], nullptr, C);
+          }
+#pragma unroll
+          for (int kt = 0; kt < KT; ++kt) mm_tt<E, MT>(HB[jv][kt], sU, LDK, 16 * kt, sD, R[jv], C);
+        }
+      }
+      __syncthreads();
+    }
+
+    // ---- UT transform: T = (I + strict(diag(beta) Gam * K K^T))^-1 -------------
+    for (int tI = w; tI < MT * MT; tI += 4) {
+      const int mt = tI / MT, jt = tI % MT;
+      f32x4 acc = zero4();
+      if (jt <= mt) mm_ll<E>(acc, sK, LDK, 16 * mt, sK, LDK, 16 * jt, DK);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * mt + g4 + r, j = 16 * jt + li;
+        sMf[i * LDF + j] = (j < i) ? sBeta[i] * __expf(sB[i] - sB[j]) * acc[r] : 0.f;
+      }
+    }
+    __syncthreads();
+    if (w < MT && l < 16) {  // diagonal 16x16 blocks by forward substitution, one column per lane
+      const int base = 16 * w, cc = l;
+      float x[16];
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) {
+        float s = (rr == cc) ? 1.f : 0.f;
+        if (rr > cc) {
+#pragma unroll
+          for (int kk = 0; kk < rr; ++kk)
+            if (kk >= cc) s -= sMf[(base + rr) * LDF + base + kk] * x[kk];
+        }
+        x[rr] = s;
+      }
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) sTf[(base + rr) * LDF + base + cc] = x[rr];
+    }
+    __syncthreads();
+    for (int d = 1; d < MT; ++d) {  // off-diagonal blocks, T_ij = -T_ii sum_k M_ik T_kj
+      const int r = tid >> 4, cc = tid & 15;
+      for (int bi = d; bi < MT; ++bi) {
+        const int bj = bi - d;
+        float s = 0.f;
+        for (int kk = 16 * bj; kk < 16 * bi; ++kk) s += sMf[(16 * bi + r) * LDF + kk] * sTf[kk * LDF + 16 * bj + cc];
+        sTmp[(bi - d) * 272 + r * 17 + cc] = s;
+      }
+      __syncthreads();
+      for (int bi = d; bi < MT; ++bi) {
+        const int bj = bi - d;
+        float s = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < 16; ++kk) s += sTf[(16 * bi + r) * LDF + 16 * bi + kk] * sTmp[(bi - d) * 272 + kk * 17 + cc];
+        sTf[(16 * bi + r) * LDF + 16 * bj + cc] = -s;
+      }
+      __syncthreads();
+    }
+    for (int idx = tid; idx < C * C; idx += 256) {
+      const int i = idx / C, j = idx % C;
+      sT[i * LDC + j] = from_f<E>(j <= i ? sTf[i * LDF + j] : 0.f);
+    }
+    __syncthreads();
+
+    // ---- Uc = T diag(beta) V',  Wc = T diag(beta G) K ---------------------------
+    f32x4 Wc[NKW][MT];
+#pragma unroll
+    for (int jv = 0; jv < NVW; ++jv) {
+      f32x4 Uc[MT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        Uc[mt] = zero4();
+        if (w + 4 * jv < VT) mm_lt<E, MT>(Uc[mt], sT, LDC, 16 * mt, Vp[jv], sBeta, C);
+      }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) Vp[jv][mt] = Uc[mt];
+    }
+#pragma unroll
+    for (int jk = 0; jk < NKW; ++jk) {
+      const int kc = w + 4 * jk;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        f32x4 acc = zero4();
+        if (kc < KT) {
+          mm_ls<E>(acc, sT, LDC, 16 * mt, sK, LDK, 16 * kc, sBG, C);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sW[(16 * mt + g4 + r) * LDK + 16 * kc + li] = from_f<E>(acc[r]);
+        }
+        Wc[jk][mt] = acc;
+      }
+    }
+    __syncthreads();
+
+    // ---- E = Uc - Wc H;  O_loc;  H update ---------------------------------------
+    float* oloc = a.Oloc + ((size_t)pr * Tpad + t0) * DV;
+#pragma unroll
+    for (int jv = 0; jv < NVW; ++jv) {
+      const int vt = w + 4 * jv;
+      if (vt >= VT) continue;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        f32x4 wh = zero4(), qh = zero4();
+        mm_ll<E>(wh, sW, LDK, 16 * mt, sS, LDK, 16 * vt, DK);
+        mm_ll<E>(qh, sQ, LDK, 16 * mt, sS, LDK, 16 * vt, DK);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          Vp[jv][mt][r] -= wh[r];                       // E
+          Oc[jv][mt][r] += sG[16 * mt + g4 + r] * qh[r];  // diag(G) Q H
+        }
+      }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        mm_lt<E, MT>(Oc[jv][mt], sP, LDC, 16 * mt, Vp[jv], nullptr, C);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) oloc[(size_t)(16 * mt + g4 + r) * DV + 16 * vt + li] = Oc[jv][mt][r];
+      }
+      const float GC = sG[C - 1];
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) {
+        f32x4 acc = HB[jv][kt];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[r] += GC * Hs[jv][kt][r];
+        mm_tt<E, MT>(acc, sK, LDK, 16 * kt, sD, Vp[jv], C);
+        Hs[jv][kt] = acc;
+      }
+    }
+    __syncthreads();
+    // A_acc^T into the state-operand buffer
+#pragma unroll
+    for (int jk = 0; jk < NKW; ++jk) {
+      const int kc = w + 4 * jk;
+      if (kc < KT) {
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            sS[(16 * kc + li) * LDK + 16 * kt + g4 + r] = from_f<E>(As[jk][kt][r]);
+      }
+    }
+    __syncthreads();
+
+    // ---- Qtilde = diag(G) Q - P Wc;  A_acc update ------------------------------
+    {
+      const float GC = sG[C - 1];
+#pragma unroll
+      for (int jk = 0; jk < NKW; ++jk) {
+        const int kc = w + 4 * jk;
+        if (kc >= KT) continue;
+        f32x4 WA[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          f32x4 pw = zero4();
+          mm_lt<E, MT>(pw, sP, LDC, 16 * mt, Wc[jk], nullptr, C);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int i = 16 * mt + g4 + r;
+            sQt[i * LDK + 16 * kc + li] = from_f<E>(sG[i] * to_f(sQ[i * LDK + 16 * kc + li]) - pw[r]);
+          }
+          WA[mt] = zero4();
+          mm_ll<E>(WA[mt], sW, LDK, 16 * mt, sS, LDK, 16 * kc, DK);
+        }
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt) {
+          f32x4 acc = zero4();
+          mm_tt<E, MT>(acc, sK, LDK, 16 * kt, sD, WA, C);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) As[jk][kt][r] = GC * As[jk][kt][r] - acc[r];
+        }
+      }
+    }
+    __syncthreads();
+    // ---- Qhat = Qtilde A_acc (A_acc before this chunk) --------------------------
+    {
+      float* qhat = a.Qhat + ((size_t)pr * Tpad + t0) * DK;
+      for (int tI = w; tI < MT * KT; tI += 4) {
+        const int mt = tI / KT, kc = tI % KT;
+        f32x4 acc = zero4();
+        mm_ll<E>(acc, sQt, LDK, 16 * mt, sS, LDK, 16 * kc, DK);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) qhat[(size_t)(16 * mt + g4 + r) * DK + 16 * kc + li] = acc[r];
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- segment operator ---------------------------------------------------------
+  float* Ag = a.Aagg + ((size_t)pr * a.nseg + seg) * DK * DK;
+  float* Bg = a.Bagg + ((size_t)pr * a.nseg + seg) * DK * DV;
+#pragma unroll
+  for (int jk = 0; jk < NKW; ++jk) {
+    const int kc = w + 4 * jk;
+    if (kc >= KT) continue;
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Ag[(16 * kt + g4 + r) * DK + 16 * kc + li] = As[jk][kt][r];
+  }
+#pragma unroll
+  for (int jv = 0; jv < NVW; ++jv) {
+    const int vt = w + 4 * jv;
+    if (vt >= VT) continue;
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Bg[(16 * kt + g4 + r) * DV + 16 * vt + li] = Hs[jv][kt][r];
+  }
+}
+
+// Inter-segment recurrence for 16 state columns of one pair (float32 VALU).
+template <int DK, int DV>
+__global__ __launch_bounds__(256) void seg_scan_kernel(FwdArgs a) {
+  __shared__ float sA[DK * DK];
+  __shared__ float sH[2][DK * 16];
+  const int tid = threadIdx.x, pr = blockIdx.x, c0 = 16 * blockIdx.y;
+  const int j = tid & 15;
+  for (int idx = tid; idx < DK * 16; idx += 256) sH[0][idx] = 0.f;
+  __syncthreads();
+  int cur = 0;
+  for (int s = 0; s < a.nseg; ++s) {
+    const float* As = a.Aagg + ((size_t)pr * a.nseg + s) * DK * DK;
+    const float* Bs = a.Bagg + ((size_t)pr * a.nseg + s) * DK * DV;
+    float* Hi = a.Hin + ((size_t)pr * a.nseg + s) * DK * DV;
+    for (int idx = tid; idx < DK * 16; idx += 256) Hi[(idx >> 4) * DV + c0 + (idx & 15)] = sH[cur][idx];
+    for (int idx = tid; idx < DK * DK / 4; idx += 256)
+      reinterpret_cast<float4*>(sA)[idx] = reinterpret_cast<const float4*>(As)[idx];
+    __syncthreads();
+    for (int i = tid >> 4; i < DK; i += 16) {
+      float acc = Bs[i * DV + c0 + j];
+      for (int kk = 0; kk < DK; ++kk) acc += sA[i * DK + kk] * sH[cur][kk * 16 + j];
+      sH[cur ^ 1][i * 16 + j] = acc;
+    }
+    __syncthreads();
+    cur ^= 1;
+  }
+  float* Sf = a.S_final + (size_t)pr * DK * DV;
+  for (int idx = tid; idx < DK * 16; idx += 256) Sf[(idx >> 4) * DV + c0 + (idx & 15)] = sH[cur][idx];
+}
+
+// o = O_loc + Qhat H_in(segment) for one chunk of one pair (float32 VALU).
+template <class E, int DK, int DV, int C>
+__global__ __launch_bounds__(256) void seg_fixup_kernel(FwdArgs a) {
+  __shared__ float sH[DK * DV];
+  __shared__ float sQh[C * (DK + 1)];
+  const int tid = threadIdx.x, c = blockIdx.x, pr = blockIdx.y;
+  const int seg = c / a.seg_chunks;
+  const int t0 = c * C, nvalid = min(C, a.T - t0);
+  const int Tpad = a.nch * C;
+  const float* Hi = a.Hin + ((size_t)pr * a.nseg + seg) * DK * DV;
+  const float* qh = a.Qhat + ((size_t)pr * Tpad + t0) * DK;
+  const float* ol = a.Oloc + ((size_t)pr * Tpad + t0) * DV;
+  E* o = reinterpret_cast<E*>(a.o) + ((size_t)pr * a.T + t0) * DV;
+  for (int idx = tid; idx < DK * DV / 4; idx += 256)
+    reinterpret_cast<float4*>(sH)[idx] = reinterpret_cast<const float4*>(Hi)[idx];
+  for (int idx = tid; idx < C * DK; idx += 256) sQh[(idx / DK) * (DK + 1) + idx % DK] = qh[idx];
+  __syncthreads();
+  for (int idx = tid; idx < nvalid * DV; idx += 256) {
+    const int t = idx / DV, jj = idx % DV;
+    float acc = ol[(size_t)t * DV + jj];
+    for (int kk = 0; kk < DK; ++kk) acc += sQh[t * (DK + 1) + kk] * sH[kk * DV + jj];
+    o[(size_t)t * DV + jj] = from_f<E>(acc);
+  }
+}
+
+}  // namespace prism

@@ -1,0 +1,131 @@
+/*
+ * prism.h - C ABI of the PRISM rank-L gated delta-rule forward on MI355X (gfx950).
+ *
+ * What is computed (per batch b and head h, state S_0 = 0, S is dv x dk):
+ *
+ *   anchor_t = sum_{j=0..3} conv_w[h, j, :] * v_{t-3+j}        (rows before t = 0 are 0)
+ *   r_{t,0}  = v_t - anchor_t
+ *   r_{t,l}  = r_{t,l-1} * (1 - alpha_{t,l-1} * gamma_{t,l-1})  (element-wise), l = 1..L-1
+ *   A_t      = g_t (I - beta_t k_t k_t^T)
+ *   B_t      = beta_t v_t k_t^T + sum_{l=1}^{L-1} (alpha_{t,l} r_{t,l}) u_{t,l}^T
+ *   S_t      = S_{t-1} A_t + B_t
+ *   o_t      = S_t q_t
+ *
+ * Sources: the linear recurrence S_t = S_{t-1} A_t + B_t with input-only A_t, B_t
+ * ("PRISM" reading notes, liuzhao09.github.io, section 2.1; Tencent Ads article,
+ * section 01-二); the GDN forgetting operator (notes section 2.2; article
+ * section 01-四); rank accumulation of the write (notes section 2.2; ai-engineering
+ * summary "ICML 2026 | PRISM", section "PRISM 设计"); the ShortConv anchor and the
+ * residual chain (notes section 2.3; article section 03-三, where the GELU is absorbed
+ * into a fixed preconditioner so the chain is element-wise linear).  The pages outline
+ * this form without printing the equations; the concrete form above is the one this
+ * library implements and its oracle checks.
+ *
+ * Layout: every tensor is dense, row-major (C order), head-major [B, H, T, ...].
+ *   q, k   [B, H, T, dk]         dtype dt
+ *   v      [B, H, T, dv]         dtype dt
+ *   g      [B, H, T]             float32, 0 < g <= 1 (decay gate)
+ *   beta   [B, H, T]             float32 (GDN write / erase strength)
+ *   u      [B, H, T, L-1, dk]    dtype dt;  u[..., j, :] = u_{t, j+1}
+ *   alpha  [B, H, T, L]          float32;   alpha[..., l] = alpha_{t, l}
+ *   gamma  [B, H, T, L-1, dv]    dtype dt;  gamma[..., j, :] = gamma_{t, j}
+ *   conv_w [H, 4, dv]            float32;   tap j multiplies v_{t-3+j}
+ *   o      [B, H, T, dv]         dtype dt   (output, fully overwritten)
+ *   S_final[B, H, dk, dv]        float32    (output: the transpose of S_T)
+ * u, alpha and gamma are not read when L == 1 (they may be NULL then); conv_w is
+ * not read when L == 1 either.
+ *
+ * Pointers are device pointers (hipMalloc'd or equivalent).  The caller owns every
+ * buffer, the workspace included.  The library allocates nothing, keeps no state
+ * between calls, never synchronises, and enqueues all work on `stream`
+ * (NULL = the null stream).  Outputs must not alias inputs or the workspace.
+ *
+ * Precision: dt = PRISM_BF16 rounds MFMA operands to bfloat16 and accumulates in
+ * float32; the state stays float32.  dt = PRISM_F32 computes in float32 throughout.
+ *
+ * Errors: argument checks happen on the host before anything is enqueued; a
+ * failed check returns an error code and enqueues nothing.  A launch failure
+ * returns PRISM_ERR_HIP.  Faults inside kernels surface at the caller's next
+ * synchronisation.  Not checked: g > 0, finiteness of inputs.
+ */
+#ifndef PRISM_H_
+#define PRISM_H_
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+struct ihipStream_t;
+typedef struct ihipStream_t* hipStream_t;
+struct ihipEvent_t;
+typedef struct ihipEvent_t* hipEvent_t;
+
+typedef enum {
+  PRISM_OK = 0,
+  PRISM_ERR_INVALID_ARG = -1,   /* NULL pointer, non-positive size, size overflow */
+  PRISM_ERR_UNSUPPORTED = -2,   /* a shape / dtype combination with no kernel */
+  PRISM_ERR_WORKSPACE = -3,     /* workspace NULL or smaller than required */
+  PRISM_ERR_HIP = -4            /* a HIP launch or runtime call failed */
+} prism_status;
+
+typedef enum { PRISM_F32 = 0, PRISM_BF16 = 1 } prism_dtype;
+
+/* Bytes of device workspace prism_fwd needs for these sizes; 0 when the
+ * arguments are invalid or unsupported (prism_fwd then reports which).
+ * Supported: B, H, T >= 1; dk == dv in {16, 32, 64, 128}; chunk in {16, 32, 64};
+ * 1 <= L <= 8; with PRISM_F32 the chunk tiles must fit the 160 KB of LDS per CU
+ * (dk = dv = 128 needs chunk <= 32, dk = dv = 64 needs chunk <= 64). */
+size_t prism_fwd_workspace_bytes(int B, int H, int T, int dk, int dv, int L, int chunk,
+                                 prism_dtype dt);
+
+/* The forward pass.  `chunk` is the token count of the intra-chunk UT/WY block
+ * (results agree across chunk sizes up to rounding).  Returns PRISM_OK or an
+ * error code; see the header comment for layout, ownership and errors. */
+prism_status prism_fwd(const void* q, const void* k, const void* v,
+                       const float* g, const float* beta,
+                       const void* u, const float* alpha, const void* gamma,
+                       const float* conv_w,
+                       int B, int H, int T, int dk, int dv, int L, int chunk, prism_dtype dt,
+                       void* o, float* S_final,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Same as prism_fwd with an explicit segment length (in chunks, >= 1) for the
+ * sequence-parallel split; results agree across segment lengths up to rounding.
+ * prism_fwd picks the segment length itself.  Used to test that independence. */
+size_t prism_fwd_seg_workspace_bytes(int B, int H, int T, int dk, int dv, int L, int chunk,
+                                     prism_dtype dt, int seg_chunks);
+prism_status prism_fwd_seg(const void* q, const void* k, const void* v,
+                           const float* g, const float* beta,
+                           const void* u, const float* alpha, const void* gamma,
+                           const float* conv_w,
+                           int B, int H, int T, int dk, int dv, int L, int chunk, prism_dtype dt,
+                           void* o, float* S_final,
+                           void* workspace, size_t workspace_bytes, int seg_chunks,
+                           hipStream_t stream);
+
+/* Same as prism_fwd, and records four caller-created events on `stream` around
+ * the launches: events[0] before the segment sweep kernel, events[1] after it,
+ * events[2] after the inter-segment scan, events[3] after the output correction.
+ * For per-kernel timing with hipEventElapsedTime.  events must not be NULL. */
+prism_status prism_fwd_timed(const void* q, const void* k, const void* v,
+                             const float* g, const float* beta,
+                             const void* u, const float* alpha, const void* gamma,
+                             const float* conv_w,
+                             int B, int H, int T, int dk, int dv, int L, int chunk, prism_dtype dt,
+                             void* o, float* S_final,
+                             void* workspace, size_t workspace_bytes,
+                             hipEvent_t* events, hipStream_t stream);
+
+/* A static, human-readable name of a status code. */
+const char* prism_status_string(prism_status s);
+
+/* Library version string ("major.minor.patch"). */
+const char* prism_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PRISM_H_ */

@@ -1,0 +1,105 @@
+"""The C ABI of libprism on the host: exported symbols and argument checks.
+
+No kernel runs here: every call below fails validation on the host, before
+anything is enqueued, so these tests need no GPU.
+"""
+import ctypes
+import os
+
+import pytest
+
+import delta_rule_sequence_amd as prism
+
+OK, INVALID, UNSUPPORTED, WORKSPACE, HIP = 0, -1, -2, -3, -4
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(prism.LIB_PATH):
+        pytest.fail("libprism.so is not built (run __graft_entry__.build())")
+    return prism.load_library()
+
+
+def test_exports_every_header_symbol(lib):
+    names = prism.header_functions()
+    assert {"prism_fwd", "prism_fwd_workspace_bytes", "prism_status_string"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for code in [OK, INVALID, UNSUPPORTED, WORKSPACE, HIP]:
+        s = lib.prism_status_string(code).decode()
+        assert s.startswith("PRISM_")
+    assert lib.prism_version().decode().count(".") == 2
+
+
+def test_workspace_bytes_valid_and_invalid(lib):
+    f = lib.prism_fwd_workspace_bytes
+    assert f(2, 4, 16384, 64, 64, 4, 64, 1) > 0
+    assert f(1, 1, 64, 16, 16, 1, 16, 0) > 0
+    assert f(1, 1, 1, 16, 16, 1, 16, 0) > 0           # a single token
+    assert f(0, 1, 64, 16, 16, 1, 16, 0) == 0          # B <= 0
+    assert f(1, 1, 0, 16, 16, 1, 16, 0) == 0           # T <= 0
+    assert f(1, 1, 64, 48, 48, 1, 16, 0) == 0          # unsupported head dim
+    assert f(1, 1, 64, 64, 32, 1, 16, 0) == 0          # dk != dv
+    assert f(1, 1, 64, 16, 16, 1, 8, 0) == 0           # chunk not in {16, 32, 64}
+    assert f(1, 1, 64, 16, 16, 9, 16, 0) == 0          # L > 8
+    assert f(1, 1, 64, 16, 16, 0, 16, 0) == 0          # L < 1
+    assert f(1, 1, 64, 16, 16, 1, 16, 7) == 0          # unknown dtype
+    assert f(1, 1, 64, 128, 128, 2, 64, 0) == 0        # fp32 tiles exceed LDS
+    assert f(1 << 20, 1 << 12, 1 << 20, 128, 128, 8, 64, 1) == 0   # size overflow
+
+
+def test_workspace_grows_with_segments(lib):
+    f = lib.prism_fwd_seg_workspace_bytes
+    assert f(1, 2, 1024, 64, 64, 4, 64, 1, 1) > f(1, 2, 1024, 64, 64, 4, 64, 1, 16) > 0
+    assert f(1, 2, 1024, 64, 64, 4, 64, 1, -1) == 0
+
+
+def _call(lib, B=1, H=1, T=64, d=16, L=2, chunk=16, dt=1, ptr=1, null=(), ws_bytes=1 << 30, seg=None):
+    p = ctypes.c_void_p(ptr)
+    args = {n: p for n in ["q", "k", "v", "g", "beta", "u", "alpha", "gamma", "conv_w", "o", "S", "ws"]}
+    for n in null:
+        args[n] = None
+    vals = [args["q"], args["k"], args["v"], args["g"], args["beta"], args["u"], args["alpha"],
+            args["gamma"], args["conv_w"], B, H, T, d, d, L, chunk, dt, args["o"], args["S"], args["ws"], ws_bytes]
+    if seg is None:
+        return lib.prism_fwd(*vals, None)
+    return lib.prism_fwd_seg(*vals, seg, None)
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "g", "beta", "o", "S"])
+def test_null_required_pointer(lib, name):
+    assert _call(lib, null=(name,)) == INVALID
+
+
+@pytest.mark.parametrize("name", ["u", "alpha", "gamma", "conv_w"])
+def test_null_rank_pointer_when_L_gt_1(lib, name):
+    assert _call(lib, L=3, null=(name,)) == INVALID
+
+
+def test_bad_shapes(lib):
+    assert _call(lib, B=0) == INVALID
+    assert _call(lib, H=-1) == INVALID
+    assert _call(lib, T=0) == INVALID
+    assert _call(lib, d=24) == UNSUPPORTED
+    assert _call(lib, chunk=128) == UNSUPPORTED
+    assert _call(lib, L=0) == UNSUPPORTED
+    assert _call(lib, L=9) == UNSUPPORTED
+    assert _call(lib, dt=5) == INVALID
+
+
+def test_workspace_checks(lib):
+    assert _call(lib, null=("ws",)) == WORKSPACE
+    need = lib.prism_fwd_workspace_bytes(1, 1, 64, 16, 16, 2, 16, 1)
+    assert _call(lib, ws_bytes=need - 1) == WORKSPACE
+    assert _call(lib, seg=0) == INVALID
+    assert _call(lib, seg=2, ws_bytes=lib.prism_fwd_seg_workspace_bytes(1, 1, 64, 16, 16, 2, 16, 1, 2) - 1) == WORKSPACE
+
+
+def test_python_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(prism, "_lib", None)
+    monkeypatch.setattr(prism, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(prism.PrismError):
+        prism.load_library()

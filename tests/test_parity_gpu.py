@@ -1,0 +1,153 @@
+"""Parity of the HIP forward (through the C ABI) with the float64 oracle.
+
+Tolerance (max-abs error relative to max |reference|, for o and for S_final):
+1e-4 for float32 I/O, 2e-2 for bfloat16 I/O.  The bf16 path rounds MFMA operands
+to bfloat16 (relative step 2^-8) while the state stays float32; the measured
+errors sit one to two orders of magnitude under the bound.
+"""
+import sys
+import time
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from tests.conftest import gpu_available
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def prism():
+    if not gpu_available():
+        pytest.skip("no GPU")
+    import delta_rule_sequence_amd as m
+    m.load_library()
+    return m
+
+
+def rel_err(a, b):
+    return float(np.max(np.abs(np.asarray(a, np.float64) - b)) / max(1e-30, float(np.max(np.abs(b)))))
+
+
+def run_gpu(prism, w, x, chunk=None, seg=None):
+    import torch
+    d = workloads.to_torch(x, w.dtype)
+    o, S = prism.fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["u"], d["alpha"], d["gamma"], d["conv_w"],
+                     L=w.L, chunk=chunk or w.chunk, seg_chunks=seg)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy().astype(np.float64), S.cpu().numpy().astype(np.float64)
+
+
+def run_oracle(w, x, heads=None):
+    return oracle.forward(x["q"], x["k"], x["v"], x["g"], x["beta"], x["u"], x["alpha"], x["gamma"],
+                          x["conv_w"], w.L, heads=heads)
+
+
+def check(w, got, ref, tag=""):
+    eo, es = rel_err(got[0], ref[0]), rel_err(got[1], ref[1])
+    log(f"  {w.name}{tag}: rel err o {eo:.3e}  S_final {es:.3e}  (tol {TOL[w.dtype]:.0e})")
+    assert np.all(np.isfinite(got[0])) and np.all(np.isfinite(got[1]))
+    assert eo <= TOL[w.dtype], f"o error {eo}"
+    assert es <= TOL[w.dtype], f"S_final error {es}"
+
+
+@pytest.mark.parametrize("name", workloads.ORDER)
+def test_parity_full_size(prism, name):
+    """Every workload at its full size; the 64K workload checks 2 of its 8 heads
+    against the oracle (heads are independent) and all heads for finiteness."""
+    w = workloads.workload(name)
+    log(f"[parity] {name}: generating")
+    x = workloads.generate(w)
+    log(f"[parity] {name}: gpu")
+    got = run_gpu(prism, w, x)
+    heads = [0, 5] if name == "long64k_bf16" else None
+    log(f"[parity] {name}: oracle heads={heads}")
+    t = time.time()
+    ref = run_oracle(w, x, heads)
+    log(f"[parity] {name}: oracle took {time.time() - t:.1f}s")
+    if heads is not None:
+        assert np.all(np.isfinite(got[0])) and np.all(np.isfinite(got[1]))
+        got = (got[0][:, heads], got[1][:, heads])
+    check(w, got, ref)
+
+
+SMALL = {
+    "f32": workloads.Workload("small_f32", "f32", B=1, H=2, T=203, dk=32, dv=32, L=3, chunk=32, seed=11),
+    "bf16": workloads.Workload("small_bf16", "bf16", B=2, H=1, T=331, dk=64, dv=64, L=4, chunk=64, seed=12),
+    "bf16_128": workloads.Workload("small_bf16_128", "bf16", B=1, H=2, T=150, dk=128, dv=128, L=8, chunk=64, seed=13),
+    "f32_64": workloads.Workload("small_f32_64", "f32", B=1, H=1, T=300, dk=64, dv=64, L=2, chunk=64, seed=14),
+}
+
+
+@pytest.mark.parametrize("key", list(SMALL))
+def test_ragged_tail(prism, key):
+    w = SMALL[key]
+    x = workloads.generate(w)
+    check(w, run_gpu(prism, w, x), run_oracle(w, x), " ragged")
+
+
+@pytest.mark.parametrize("T", [1, 2, 3, 5, 17])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_short_sequences(prism, T, dtype):
+    w = workloads.Workload("short", dtype, B=2, H=1, T=T, dk=32, dv=32, L=3, chunk=16, seed=20 + T)
+    x = workloads.generate(w)
+    check(w, run_gpu(prism, w, x), run_oracle(w, x), f" T={T}")
+
+
+@pytest.mark.parametrize("chunk", [16, 32, 64])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_chunk_size_independent(prism, chunk, dtype):
+    w = workloads.Workload("chunks", dtype, B=1, H=2, T=256, dk=32, dv=32, L=4, chunk=chunk, seed=30)
+    x = workloads.generate(w)
+    check(w, run_gpu(prism, w, x), run_oracle(w, x), f" chunk={chunk}")
+
+
+@pytest.mark.parametrize("seg", [1, 2, 3, 100])
+def test_segment_size_independent(prism, seg):
+    w = workloads.Workload("segs", "bf16", B=1, H=2, T=700, dk=64, dv=64, L=4, chunk=64, seed=40)
+    x = workloads.generate(w)
+    check(w, run_gpu(prism, w, x, seg=seg), run_oracle(w, x), f" seg={seg}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_L1_with_null_rank_pointers(prism, dtype):
+    w = workloads.Workload("gdn", dtype, B=2, H=2, T=200, dk=64, dv=64, L=1, chunk=32, seed=50)
+    x = workloads.generate(w)
+    assert x["u"] is None and x["alpha"] is None and x["gamma"] is None
+    check(w, run_gpu(prism, w, x), run_oracle(w, x), " L=1")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_correlated_keys(prism, dtype):
+    w = workloads.Workload("corr", dtype, B=1, H=2, T=256, dk=64 if dtype == "bf16" else 32,
+                           dv=64 if dtype == "bf16" else 32, L=3, chunk=64 if dtype == "bf16" else 32, seed=60)
+    x = workloads.generate(w, keys="correlated")
+    check(w, run_gpu(prism, w, x), run_oracle(w, x), " correlated keys")
+
+
+def test_run_to_run_deterministic(prism):
+    w = workloads.workload("rec16k_bf16").replace(T=2048)
+    x = workloads.generate(w)
+    a = run_gpu(prism, w, x)
+    b = run_gpu(prism, w, x)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_linear_in_v_on_device(prism):
+    w = workloads.Workload("lin", "f32", B=1, H=2, T=300, dk=32, dv=32, L=3, chunk=32, seed=70)
+    x1 = workloads.generate(w)
+    x2 = dict(x1, v=workloads.generate(w, seed=71)["v"])
+    x3 = dict(x1, v=(x1["v"] + 2.0 * x2["v"]).astype(np.float32))
+    o1, _ = run_gpu(prism, w, x1)
+    o2, _ = run_gpu(prism, w, x2)
+    o3, _ = run_gpu(prism, w, x3)
+    assert rel_err(o3, o1 + 2.0 * o2) < 1e-4

@@ -4,22 +4,24 @@ This module is shared by the tests, the benchmark and the smoke check.  It
 holds the workload shapes and the input recipe only: no step of the method
 (anchor, residual chain, recurrence, readout) is computed here.
 
-Input recipe (one ``numpy.random.default_rng(seed)`` stream, drawn in this
-order, then L2-normalisation and the cast to the I/O dtype):
+Input recipe (seed = the workload's seed):
 
-1. q, k, v ~ N(0, 1), each [B, H, T, d]                (drawn q, then k, then v)
-2. x ~ U(lo, hi) [B, H, T];  g = exp(-x)                (the scalar decay gate)
-3. beta = sigmoid(N(0, 1)) [B, H, T]
-4. conv_w ~ N(0, 0.5) [H, 4, dv]  (0.5 is the standard deviation)
-5. if L > 1:  u ~ N(0, 1) [B, H, T, L-1, dk];
-              alpha = 0.5 * sigmoid(N(0, 1)) [B, H, T, L];
-              z ~ N(0, 1) [B, H, T, L-1, dv];  gamma = GELU'(z) (exact erf GELU)
-
-q and k are normalised over dk per (b, h, t), u over dk per (b, h, t, l), in
-float64, before the cast.  Vectors (q, k, v, u, gamma) are cast to the I/O
-dtype: float32 (round to nearest even from float64), or bfloat16 taken as
-RNE(float32 RNE(x)).  The scalars g, beta, alpha and the conv weights are
-float32 in both paths.
+* Large vector tensors are filled block by block (BLOCK_ROWS rows of the last
+  axis per block).  Block j of tensor i (q=0, k=1, v=2, u=3, z=4) is drawn from
+  its own generator numpy.random.Generator(PCG64(SeedSequence([seed, i, j]))) as
+  float32 standard normals.  Blocks are independent, so they are filled in
+  parallel threads and the result does not depend on the thread count.
+* Small tensors come from one numpy.random.default_rng(seed) stream, in order:
+  x ~ U(lo, hi) [B, H, T] with g = exp(-x) (the scalar decay gate);
+  beta = sigmoid(N(0, 1)) [B, H, T]; conv_w ~ N(0, 0.5) [H, 4, dv] (0.5 is the
+  standard deviation); and, if L > 1, alpha = 0.5 * sigmoid(N(0, 1)) [B, H, T, L].
+* q, k ~ N(0, 1) [B, H, T, dk] and u ~ N(0, 1) [B, H, T, L-1, dk] are
+  L2-normalised over dk per row; v ~ N(0, 1) [B, H, T, dv];
+  gamma = GELU'(z) = Phi(z) + z phi(z) with z ~ N(0, 1) [B, H, T, L-1, dv]
+  (derivative of the exact erf GELU).
+* Vectors (q, k, v, u, gamma) are stored in the I/O dtype: float32, or
+  bfloat16 values (round to nearest even of the float32 value).  The scalars g,
+  beta, alpha and the conv weights are float32 in both paths.
 
 The shapes and value ranges stand in for the pages' workloads: the 16K-long
 behaviour sequences of the sequential-recommendation throughput table
@@ -30,6 +32,8 @@ from __future__ import annotations
 
 import dataclasses
 import hashlib
+import os
+from concurrent.futures import ThreadPoolExecutor
 from typing import Dict, Optional
 
 import numpy as np
@@ -98,8 +102,8 @@ def to_bf16_values(x: np.ndarray) -> np.ndarray:
     return rounded.view(np.float32)
 
 
-def _cast_vec(x64: np.ndarray, dtype: str) -> np.ndarray:
-    x32 = x64.astype(np.float32)
+def _cast_vec(x: np.ndarray, dtype: str) -> np.ndarray:
+    x32 = np.asarray(x, dtype=np.float32)
     if dtype == "f32":
         return x32
     if dtype == "bf16":
@@ -108,7 +112,8 @@ def _cast_vec(x64: np.ndarray, dtype: str) -> np.ndarray:
 
 
 def _l2_normalise(x: np.ndarray) -> np.ndarray:
-    return x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True))
+    x64 = np.asarray(x, dtype=np.float64)
+    return x64 / np.sqrt(np.sum(x64 * x64, axis=-1, keepdims=True))
 
 
 def _sigmoid(x: np.ndarray) -> np.ndarray:
@@ -117,16 +122,36 @@ def _sigmoid(x: np.ndarray) -> np.ndarray:
 
 def _gelu_prime(z: np.ndarray) -> np.ndarray:
     # derivative of the exact GELU z * Phi(z):  Phi(z) + z * phi(z)
-    return ndtr(z) + z * np.exp(-0.5 * z * z) / np.sqrt(2.0 * np.pi)
+    return ndtr(z) + z * np.exp(-0.5 * z * z) * np.float32(1.0 / np.sqrt(2.0 * np.pi))
 
 
-def _normal_block(rng, shape, block_axis0_rows: int = 1 << 22):
-    """Standard normals of `shape` drawn as one stream (identical to one call)."""
-    n = int(np.prod(shape))
-    out = np.empty(n, dtype=np.float64)
-    for s in range(0, n, block_axis0_rows):
-        e = min(n, s + block_axis0_rows)
-        out[s:e] = rng.standard_normal(e - s)
+BLOCK_ROWS = 8192
+_THREADS = max(1, min(16, os.cpu_count() or 1))
+
+
+def _fill_rows(seed: int, tensor_id: int, shape, dtype: str, post) -> np.ndarray:
+    """Fill a [..., d] tensor block by block: float32 normals from a generator
+    keyed by (seed, tensor_id, block), then `post` (per-row transform), then the
+    cast to the I/O dtype."""
+    d = shape[-1]
+    rows = int(np.prod(shape[:-1]))
+    out = np.empty((rows, d), dtype=np.float32)
+
+    def work(j):
+        r0 = j * BLOCK_ROWS
+        r1 = min(rows, r0 + BLOCK_ROWS)
+        gen = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, tensor_id, j])))
+        x = gen.standard_normal((r1 - r0, d), dtype=np.float32)
+        if post is not None:
+            x = post(x)
+        out[r0:r1] = _cast_vec(x, dtype)
+
+    nblk = (rows + BLOCK_ROWS - 1) // BLOCK_ROWS
+    if nblk == 1:
+        work(0)
+    else:
+        with ThreadPoolExecutor(_THREADS) as ex:
+            list(ex.map(work, range(nblk)))
     return out.reshape(shape)
 
 
@@ -139,42 +164,38 @@ def generate(w: Workload, seed: Optional[int] = None, keys: str = "iid") -> Dict
     (None for L == 1).
 
     keys="correlated" replaces k by one of 8 base directions per token plus
-    small noise (a stress case for the intra-chunk triangular solve; it is drawn
-    after everything else so the other tensors are unchanged).
+    small noise (a stress case for the intra-chunk triangular solve); the other
+    tensors are unchanged.
     """
-    rng = np.random.default_rng(w.seed if seed is None else seed)
+    seed = w.seed if seed is None else seed
     B, H, T, dk, dv, L = w.B, w.H, w.T, w.dk, w.dv, w.L
-    q = _normal_block(rng, (B, H, T, dk))
-    k = _normal_block(rng, (B, H, T, dk))
-    v = _normal_block(rng, (B, H, T, dv))
+    rng = np.random.default_rng(seed)
     x = rng.uniform(w.x_lo, w.x_hi, size=(B, H, T))
     g = np.exp(-x)
     beta = _sigmoid(rng.standard_normal((B, H, T)))
     conv_w = rng.normal(0.0, 0.5, size=(H, 4, dv))
-    u = alpha = gamma = None
-    if L > 1:
-        u = _normal_block(rng, (B, H, T, L - 1, dk))
-        alpha = 0.5 * _sigmoid(rng.standard_normal((B, H, T, L)))
-        z = _normal_block(rng, (B, H, T, L - 1, dv))
-        gamma = _gelu_prime(z)
-        del z
-    if keys == "correlated":
-        base = rng.standard_normal((8, dk))
-        idx = rng.integers(0, 8, size=(B, H, T))
-        k = base[idx] + 0.05 * rng.standard_normal((B, H, T, dk))
-    elif keys != "iid":
-        raise ValueError(keys)
+    alpha = 0.5 * _sigmoid(rng.standard_normal((B, H, T, L))) if L > 1 else None
     out = {
-        "q": _cast_vec(_l2_normalise(q), w.dtype),
-        "k": _cast_vec(_l2_normalise(k), w.dtype),
-        "v": _cast_vec(v, w.dtype),
+        "q": _fill_rows(seed, 0, (B, H, T, dk), w.dtype, _l2_normalise),
+        "k": _fill_rows(seed, 1, (B, H, T, dk), w.dtype, _l2_normalise),
+        "v": _fill_rows(seed, 2, (B, H, T, dv), w.dtype, None),
         "g": g.astype(np.float32),
         "beta": beta.astype(np.float32),
         "conv_w": conv_w.astype(np.float32),
-        "u": None if u is None else _cast_vec(_l2_normalise(u), w.dtype),
-        "alpha": None if alpha is None else alpha.astype(np.float32),
-        "gamma": None if gamma is None else _cast_vec(gamma, w.dtype),
+        "u": None, "alpha": None, "gamma": None,
     }
+    if L > 1:
+        out["u"] = _fill_rows(seed, 3, (B, H, T, L - 1, dk), w.dtype, _l2_normalise)
+        out["alpha"] = alpha.astype(np.float32)
+        out["gamma"] = _fill_rows(seed, 4, (B, H, T, L - 1, dv), w.dtype, _gelu_prime)
+    if keys == "correlated":
+        crng = np.random.default_rng([seed, 99])
+        base = crng.standard_normal((8, dk))
+        idx = crng.integers(0, 8, size=(B, H, T))
+        kk = base[idx] + 0.05 * crng.standard_normal((B, H, T, dk))
+        out["k"] = _cast_vec(_l2_normalise(kk), w.dtype)
+    elif keys != "iid":
+        raise ValueError(keys)
     return out
 
 
@@ -182,3 +203,22 @@ def manifest(inputs: Dict[str, np.ndarray]) -> Dict[str, str]:
     """SHA-256 of every tensor's bytes (generator determinism check)."""
     return {k: hashlib.sha256(np.ascontiguousarray(v).tobytes()).hexdigest()
             for k, v in sorted(inputs.items()) if v is not None}
+
+
+def to_torch(inputs: Dict[str, np.ndarray], dtype: str, device="cuda"):
+    """Copy generated inputs to `device`: vectors in the I/O dtype (exact, the
+    values are already representable), scalars and conv weights in float32."""
+    import torch
+    vt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    out = {}
+    for key, val in inputs.items():
+        if val is None:
+            out[key] = None
+            continue
+        t = torch.from_numpy(np.ascontiguousarray(val))
+        if key in ("q", "k", "v", "u", "gamma"):
+            t = t.to(device=device).to(vt)
+        else:
+            t = t.to(device=device, dtype=torch.float32)
+        out[key] = t.contiguous()
+    return out
