@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include "prism.h"
+#include "prism_fast.h"
 #include "prism_kernels.h"
 
 namespace {
@@ -14,7 +15,8 @@ using prism::bf16_t;
 using prism::FwdArgs;
 
 constexpr size_t kAlign = 256;
-constexpr int kTargetWorkgroups = 512;  // about two per CU on a 256-CU MI355X
+constexpr int kTargetWorkgroups = 512;      // generic sweep: about two per CU on a 256-CU MI355X
+constexpr int kTargetWorkgroupsFast = 256;  // fast sweep: one segment per CU (its LDS fills a CU)
 
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -26,11 +28,17 @@ inline bool mul_ok(size_t a, size_t b, size_t* out) {
 }
 
 struct Plan {
+  bool fast;
   int P, nch, seg_chunks, nseg;
   size_t off_oloc, off_qhat, off_aagg, off_bagg, off_hin, total;
 };
 
 bool valid_dim(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+
+// The specialised sweep (prism_fast.h): bfloat16, head dim 64, chunk 64.
+bool use_fast(int dk, int dv, int chunk, prism_dtype dt) {
+  return dt == PRISM_BF16 && dk == 64 && dv == 64 && chunk == 64 && prism::FastLds<64, 64>::fits;
+}
 
 template <class E, int D, int C>
 constexpr bool fits() { return prism::SegLds<E, D, D, C>::fits; }
@@ -69,8 +77,10 @@ prism_status make_plan(int B, int H, int T, int dk, int dv, int L, int chunk, pr
   if (!mul_ok((size_t)B, (size_t)H, &P) || P > (size_t)INT32_MAX / 2) return PRISM_ERR_INVALID_ARG;
   if (P > 65535) return PRISM_ERR_UNSUPPORTED;  // (b, h) pairs map to grid.y
   const size_t nch = ((size_t)T + chunk - 1) / chunk;
+  const bool fast = use_fast(dk, dv, chunk, dt);
   if (seg_chunks == 0) {
-    size_t nseg_target = ((size_t)kTargetWorkgroups + P - 1) / P;
+    const size_t target = fast ? kTargetWorkgroupsFast : kTargetWorkgroups;
+    size_t nseg_target = fast ? target / P : (target + P - 1) / P;
     if (nseg_target < 1) nseg_target = 1;
     seg_chunks = (int)((nch + nseg_target - 1) / nseg_target);
     if (seg_chunks < 1) seg_chunks = 1;
@@ -85,6 +95,7 @@ prism_status make_plan(int B, int H, int T, int dk, int dv, int L, int chunk, pr
   // inputs must be addressable too: P*T*(L-1)*max(dk,dv) elements
   if (!mul_ok(P, (size_t)T, &c) || !mul_ok(c, (size_t)L * (dk > dv ? dk : dv) * 4, &c))
     return PRISM_ERR_INVALID_ARG;
+  pl->fast = fast;
   pl->P = (int)P;
   pl->nch = (int)nch;
   pl->seg_chunks = seg_chunks;
@@ -119,8 +130,20 @@ prism_status launch(const FwdArgs& a, const Plan& pl, hipEvent_t* ev, hipStream_
   }
 }
 
+prism_status launch_fast(const FwdArgs& a, const Plan& pl, hipEvent_t* ev, hipStream_t stream) {
+  if (!record(ev, 0, stream)) return PRISM_ERR_HIP;
+  hipLaunchKernelGGL((prism::seg_fast_kernel<64, 64>), dim3(pl.nseg, pl.P), dim3(256), 0, stream, a);
+  if (hipGetLastError() != hipSuccess || !record(ev, 1, stream)) return PRISM_ERR_HIP;
+  hipLaunchKernelGGL((prism::seg_scan_fast_kernel<64, 64>), dim3(pl.P, 64 / 4), dim3(256), 0, stream, a);
+  if (hipGetLastError() != hipSuccess || !record(ev, 2, stream)) return PRISM_ERR_HIP;
+  hipLaunchKernelGGL((prism::seg_fixup_fast_kernel<64, 64>), dim3(pl.nch, pl.P), dim3(256), 0, stream, a);
+  if (hipGetLastError() != hipSuccess || !record(ev, 3, stream)) return PRISM_ERR_HIP;
+  return PRISM_OK;
+}
+
 template <class E>
 prism_status dispatch(int d, int C, const FwdArgs& a, const Plan& pl, hipEvent_t* ev, hipStream_t s) {
+  if (pl.fast) return launch_fast(a, pl, ev, s);
   switch (d) {
     case 16: return C == 16 ? launch<E, 16, 16>(a, pl, ev, s) : C == 32 ? launch<E, 16, 32>(a, pl, ev, s) : launch<E, 16, 64>(a, pl, ev, s);
     case 32: return C == 16 ? launch<E, 32, 16>(a, pl, ev, s) : C == 32 ? launch<E, 32, 32>(a, pl, ev, s) : launch<E, 32, 64>(a, pl, ev, s);

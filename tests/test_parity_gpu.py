@@ -151,3 +151,26 @@ def test_linear_in_v_on_device(prism):
     o2, _ = run_gpu(prism, w, x2)
     o3, _ = run_gpu(prism, w, x3)
     assert rel_err(o3, o1 + 2.0 * o2) < 1e-4
+
+
+@pytest.mark.parametrize("L", [1, 2, 3, 5, 8])
+def test_bf16_d64_c64_all_L(prism, L):
+    """The specialised bf16 / d=64 / chunk=64 sweep streams the rank inputs one
+    refinement step at a time; every L uses the two LDS slots differently."""
+    w = workloads.Workload("fastL", "bf16", B=1, H=2, T=450, dk=64, dv=64, L=L, chunk=64, seed=80 + L)
+    x = workloads.generate(w)
+    check(w, run_gpu(prism, w, x), run_oracle(w, x), f" L={L}")
+
+
+@pytest.mark.parametrize("T", [1, 3, 64, 65, 130])
+def test_bf16_d64_c64_short(prism, T):
+    w = workloads.Workload("fastT", "bf16", B=2, H=1, T=T, dk=64, dv=64, L=4, chunk=64, seed=90 + T)
+    x = workloads.generate(w)
+    check(w, run_gpu(prism, w, x), run_oracle(w, x), f" T={T}")
+
+
+def test_bf16_d64_generic_chunk32_matches(prism):
+    """chunk=32 at d=64 runs the generic sweep; both must meet the oracle."""
+    w = workloads.Workload("gen32", "bf16", B=1, H=2, T=300, dk=64, dv=64, L=4, chunk=32, seed=95)
+    x = workloads.generate(w)
+    check(w, run_gpu(prism, w, x), run_oracle(w, x), " generic chunk=32")
