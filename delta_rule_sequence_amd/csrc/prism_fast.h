@@ -70,49 +70,132 @@ struct FastLds {
   static constexpr size_t oAt = oHt + szDD;
   static constexpr size_t oM = oAt + szDD;
   static constexpr size_t oTd = oM + (size_t)C * LDC * 2;
+  // V^T with a 4-token halo: element (c, t) at [c][t + 4], t = -4 .. C-1
   static constexpr size_t oV = oTd + (size_t)(C / 16) * 16 * LDT * 2;
-  static constexpr size_t oGate = oV + (size_t)(C + 3) * LD * 2;
-  static constexpr size_t nGate = 5 * C + 8 * C;
-  // two slots of (U_l [C][LD], gamma_l [C][LD], R_l^T [D][LDC]); after the
-  // refinement loop the region holds V'^T, Wc, Wc^T and E^T.
+  static constexpr size_t oGate = oV + szDT;
+  // b, G, D, beta, beta*G [C]; alpha^T [8][C]; conv taps [4][D]
+  static constexpr size_t nGate = 5 * C + 8 * C + 4 * D;
+  // two slots of (U_l [C][LD], gamma_{l-1}^T [D][LDC], R_l^T [D][LDC], U_l^T [D][LDC]);
+  // after the refinement loop the region holds V'^T, Wc, Wc^T and E^T.
   static constexpr size_t oSlot = oGate + nGate * 4;
-  static constexpr size_t szSlot = 2 * szTD + szDT;
+  static constexpr size_t szSlot = szTD + 3 * szDT;
   static constexpr size_t total = oSlot + 2 * szSlot;
   static_assert(szTD + 2 * szDT <= szSlot, "Wc, Wc^T and E^T must fit one slot");
+  static_assert(C + 4 <= LDC, "V^T needs C + 4 token positions");
   static constexpr bool fits = total <= 160 * 1024;
 };
 
-// Row-major [ROWS][D] bf16 tile load from global (16-byte pieces) into LDS with
-// row stride LD.  Tile row r is global row row0 + r of `src` (row stride
-// `row_stride` elements); rows outside [0, hi) read as zero.  Optionally also
-// writes the transposed copy dstT[c][r] (row stride LDC).
-template <int D, int ROWS, int LD, int LDC>
-__device__ __forceinline__ void load_rows(bf16_t* dst, bf16_t* dstT, const bf16_t* src, size_t row_stride,
-                                          int row0, int hi) {
-  constexpr int PER_ROW = D / 8;
-  constexpr int NP = ROWS * PER_ROW;
-  constexpr int NIT = (NP + 255) / 256;
-  uint4 buf[NIT];
+// Row-major [ROWS][D] bf16 tiles move global -> registers -> LDS in 16-byte
+// pieces: fetch_rows issues the loads (tile row r is global row row0 + r of
+// `src`, row stride `row_stride` elements; rows outside [0, hi) read as zero)
+// and store_rows writes them to LDS (row stride LD), optionally also as the
+// transposed copy dstT[c][r] (row stride LDC).  Splitting the two lets a load be
+// issued a whole phase before its data is needed.
+template <int D, int ROWS>
+struct RowRegs {
+  static constexpr int PER_ROW = D / 8;
+  static constexpr int NP = ROWS * PER_ROW;
+  static constexpr int NIT = (NP + 255) / 256;
+  uint4 x[NIT];
+  int row0, hi;  // validity window, applied when the registers are stored
+};
+
+// Issues the loads only: the registers are not read until store_rows, so the
+// loads stay in flight across the caller's compute.  Out-of-range rows load
+// row 0 of `src` (always valid) and are zeroed at store time.
+template <int D, int ROWS>
+__device__ __forceinline__ void fetch_rows(RowRegs<D, ROWS>& R, const bf16_t* src, size_t row_stride, int row0,
+                                           int hi) {
+  using RR = RowRegs<D, ROWS>;
+  R.row0 = row0;
+  R.hi = hi;
 #pragma unroll
-  for (int it = 0; it < NIT; ++it) {
+  for (int it = 0; it < RR::NIT; ++it) {
     const int idx = threadIdx.x + 256 * it;
-    const int row = idx / PER_ROW, cv = (idx % PER_ROW) * 8;
+    const int row = idx / RR::PER_ROW, cv = (idx % RR::PER_ROW) * 8;
     const int gr = row0 + row;
-    const bool ok = idx < NP && gr >= 0 && gr < hi;
+    const bool ok = idx < RR::NP && gr >= 0 && gr < hi;
     const size_t rc = ok ? (size_t)gr : 0;
-    uint4 x = *reinterpret_cast<const uint4*>(src + rc * row_stride + cv);
-    buf[it] = ok ? x : make_uint4(0, 0, 0, 0);
+    R.x[it] = *reinterpret_cast<const uint4*>(src + rc * row_stride + cv);
   }
+}
+
+template <int D, int ROWS, int LD, int LDC>
+__device__ __forceinline__ void store_rows(const RowRegs<D, ROWS>& R, bf16_t* dst, bf16_t* dstT) {
+  using RR = RowRegs<D, ROWS>;
 #pragma unroll
-  for (int it = 0; it < NIT; ++it) {
+  for (int it = 0; it < RR::NIT; ++it) {
     const int idx = threadIdx.x + 256 * it;
-    if (idx >= NP) break;
-    const int row = idx / PER_ROW, cv = (idx % PER_ROW) * 8;
-    *reinterpret_cast<uint4*>(dst + row * LD + cv) = buf[it];
+    if (idx >= RR::NP) break;
+    const int row = idx / RR::PER_ROW, cv = (idx % RR::PER_ROW) * 8;
+    const int gr = R.row0 + row;
+    const uint4 x = (gr >= 0 && gr < R.hi) ? R.x[it] : make_uint4(0, 0, 0, 0);
+    if (dst != nullptr) *reinterpret_cast<uint4*>(dst + row * LD + cv) = x;
     if (dstT != nullptr) {
-      const bf16_t* e = reinterpret_cast<const bf16_t*>(&buf[it]);
+      const bf16_t* e = reinterpret_cast<const bf16_t*>(&x);
 #pragma unroll
       for (int j = 0; j < 8; ++j) dstT[(cv + j) * LDC + row] = e[j];
+    }
+  }
+}
+
+// Tiles that also need a transposed LDS copy move in 4-row x 4-column blocks:
+// each thread loads four 8-byte row pieces and writes the transposed copy as
+// four 8-byte writes (4 consecutive tokens of one column) instead of sixteen
+// 2-byte ones.  Blocks are numbered column-quad fastest so that the global loads
+// of 16 lanes cover one 128-byte row.
+template <int D, int ROWS>
+struct QuadRegs {
+  static_assert(ROWS % 4 == 0, "rows come in quads");
+  static constexpr int CQ = D / 4;
+  static constexpr int NB = (ROWS / 4) * CQ;
+  static constexpr int NIT = (NB + 255) / 256;
+  uint2 x[NIT][4];
+  int row0, hi;
+};
+
+template <int D, int ROWS>
+__device__ __forceinline__ void fetch_quads(QuadRegs<D, ROWS>& R, const bf16_t* src, size_t row_stride, int row0,
+                                            int hi) {
+  using RR = QuadRegs<D, ROWS>;
+  R.row0 = row0;
+  R.hi = hi;
+#pragma unroll
+  for (int it = 0; it < RR::NIT; ++it) {
+    const int b = threadIdx.x + 256 * it;
+    const int rq = b / RR::CQ, c4 = (b % RR::CQ) * 4;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int gr = row0 + 4 * rq + r;
+      const bool ok = b < RR::NB && gr >= 0 && gr < hi;
+      const size_t rc = ok ? (size_t)gr : 0;
+      R.x[it][r] = *reinterpret_cast<const uint2*>(src + rc * row_stride + c4);
+    }
+  }
+}
+
+template <int D, int ROWS, int LD, int LDC>
+__device__ __forceinline__ void store_quads(const QuadRegs<D, ROWS>& R, bf16_t* dst, bf16_t* dstT) {
+  using RR = QuadRegs<D, ROWS>;
+#pragma unroll
+  for (int it = 0; it < RR::NIT; ++it) {
+    const int b = threadIdx.x + 256 * it;
+    if (b >= RR::NB) break;
+    const int rq = b / RR::CQ, c4 = (b % RR::CQ) * 4;
+    bf16x4 rows[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int gr = R.row0 + 4 * rq + r;
+      const uint2 x = (gr >= 0 && gr < R.hi) ? R.x[it][r] : make_uint2(0, 0);
+      rows[r] = __builtin_bit_cast(bf16x4, x);
+      if (dst != nullptr) *reinterpret_cast<uint2*>(dst + (4 * rq + r) * LD + c4) = x;
+    }
+    if (dstT != nullptr) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        bf16x4 col = {rows[0][c], rows[1][c], rows[2][c], rows[3][c]};
+        *reinterpret_cast<bf16x4*>(dstT + (c4 + c) * LDC + 4 * rq) = col;
+      }
     }
   }
 }
@@ -139,13 +222,14 @@ __global__ __launch_bounds__(256, 1) void seg_fast_kernel(FwdArgs a) {
   bf16_t* sAt = reinterpret_cast<bf16_t*>(smem + Ly::oAt);
   bf16_t* sM = reinterpret_cast<bf16_t*>(smem + Ly::oM);
   bf16_t* sTd = reinterpret_cast<bf16_t*>(smem + Ly::oTd);
-  bf16_t* sV = reinterpret_cast<bf16_t*>(smem + Ly::oV);  // rows t0-3 .. t0+C-1
+  bf16_t* sVt0 = reinterpret_cast<bf16_t*>(smem + Ly::oV);  // V^T, token t at position t + 4
   float* sB = reinterpret_cast<float*>(smem + Ly::oGate);
   float* sG = sB + C;
   float* sD = sG + C;
   float* sBeta = sD + C;
   float* sBG = sBeta + C;
-  float* sAlpha = sBG + C;  // [C][8]
+  float* sAlphaT = sBG + C;     // [8][C]
+  float* sTaps = sAlphaT + 8 * C;  // [4][D]
   unsigned char* slot0 = smem + Ly::oSlot;
 
   const int w = wave_id(), l = lane_id(), g = l >> 4, g4 = g * 4, li = l & 15;
@@ -166,12 +250,8 @@ __global__ __launch_bounds__(256, 1) void seg_fast_kernel(FwdArgs a) {
   const float* cw = L > 1 ? a.conv_w + (size_t)hd * 4 * D : nullptr;
   bf16_t* qhat_out = reinterpret_cast<bf16_t*>(a.Qhat);
 
-  // conv taps for this lane's value columns (column block vt, lane column li)
-  float taps[KT][4];
-#pragma unroll
-  for (int vt = 0; vt < KT; ++vt)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) taps[vt][j] = L > 1 ? cw[j * D + 16 * vt + li] : 0.f;
+  // conv taps [4][D] (zero when there is no rank injection)
+  for (int idx = threadIdx.x; idx < 4 * D; idx += 256) sTaps[idx] = L > 1 ? cw[idx] : 0.f;
 
   // column-owned state: H(:, w) and A_acc(:, w), tiles over row blocks kt
   f32x4 Hs[KT], As[KT];
@@ -192,34 +272,71 @@ __global__ __launch_bounds__(256, 1) void seg_fast_kernel(FwdArgs a) {
     sAt[r * LD + c] = (bf16_t)(r == c ? 1.f : 0.f);
   }
 
-  for (int c = c_begin; c < c_end; ++c) {
-    const int t0 = c * C;
-    const int nvalid = min(C, T - t0);
-    // ---- loads: Q, K (+K^T), V with a 3-row halo, gates ------------------------------
-    const int hi = t0 + nvalid;
-    load_rows<D, C, LD, LDC>(sQ, nullptr, q, D, t0, hi);
-    load_rows<D, C, LD, LDC>(sK, sKt, k, D, t0, hi);
-    load_rows<D, C + 3, LD, LDC>(sV, nullptr, v, D, t0 - 3, hi);
-    if (w == 0) {
-      const bool ok = l < nvalid;
-      float lam = ok ? __logf(gg[t0 + min(l, nvalid - 1)]) : 0.f;
+  // Everything one chunk reads from HBM, held in registers between its fetch (one
+  // chunk ahead) and its store into LDS.
+  struct ChunkRegs {
+    RowRegs<D, C> q;
+    QuadRegs<D, C> k, u1, g1;
+    QuadRegs<D, C + 4> v;
+    float lg, be, al[8];
+    bool ok;  // this lane's token of the gates is inside the sequence
+  };
+  auto fetch_chunk = [&](ChunkRegs& R, int c) {
+    const int t0 = c * C, hi = min(T, t0 + C);
+    fetch_rows<D, C>(R.q, q, D, t0, hi);
+    fetch_quads<D, C>(R.k, k, D, t0, hi);
+    fetch_quads<D, C + 4>(R.v, v, D, t0 - 4, hi);
+    if (L > 1) {
+      fetch_quads<D, C>(R.u1, u, (size_t)Lm1 * D, t0, hi);
+      fetch_quads<D, C>(R.g1, gam, (size_t)Lm1 * D, t0, hi);
+    }
+    if (w == 0) {  // raw loads; padding values are substituted at store time
+      R.ok = t0 + l < hi;
+      const int tl = R.ok ? t0 + l : 0;
+      R.lg = gg[tl];
+      R.be = bb[tl];
+      if (L > 1) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) R.al[j] = al[(size_t)tl * L + (j < L ? j : 0)];
+      }
+    }
+  };
+  auto store_chunk = [&](const ChunkRegs& R) {
+    store_rows<D, C, LD, LDC>(R.q, sQ, nullptr);
+    store_quads<D, C, LD, LDC>(R.k, sK, sKt);
+    store_quads<D, C + 4, LD, LDC>(R.v, nullptr, sVt0);
+    if (L > 1) {
+      store_quads<D, C, LD, LDC>(R.u1, reinterpret_cast<bf16_t*>(slot0),
+                                 reinterpret_cast<bf16_t*>(slot0 + Ly::szTD + 2 * Ly::szDT));
+      store_quads<D, C, LD, LDC>(R.g1, nullptr, reinterpret_cast<bf16_t*>(slot0 + Ly::szTD));
+    }
+    if (w == 0) {  // gates: b = cumsum(log g) over the chunk, G = exp(b), D = exp(b_last - b)
+      float lam = R.ok ? __logf(R.lg) : 0.f;
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
-        float y = __shfl_up(lam, off);
+        const float y = __shfl_up(lam, off);
         if (l >= off) lam += y;
       }
       const float blast = __shfl(lam, C - 1);
-      const float be = ok ? bb[t0 + min(l, nvalid - 1)] : 0.f;
       const float G = __expf(lam);
       sB[l] = lam;
       sG[l] = G;
       sD[l] = __expf(blast - lam);
+      const float be = R.ok ? R.be : 0.f;
       sBeta[l] = be;
       sBG[l] = be * G;
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        sAlpha[l * 8 + j] = (ok && j < L && L > 1) ? al[(size_t)(t0 + min(l, nvalid - 1)) * L + j] : 0.f;
+      for (int j = 0; j < 8; ++j) sAlphaT[j * C + l] = (R.ok && L > 1 && j < L) ? R.al[j] : 0.f;
     }
+  };
+
+  ChunkRegs pre;
+  if (c_begin < c_end) {
+    fetch_chunk(pre, c_begin);
+    store_chunk(pre);
+  }
+  for (int c = c_begin; c < c_end; ++c) {
+    const int t0 = c * C;
     __syncthreads();
 
     // ---- row-owned prologue: V' = V, residual r0 = V - anchor (tiles: rows 16w.., cols 16vt..)
@@ -228,16 +345,17 @@ __global__ __launch_bounds__(256, 1) void seg_fast_kernel(FwdArgs a) {
 #pragma unroll
     for (int vt = 0; vt < KT; ++vt) {
       const int col = 16 * vt + li;
-      float vv[7];
+      // tokens i0 + g4 - 4 .. i0 + g4 + 3 of column col (positions i0 + g4 .. +7)
+      const bf16x4 va = *reinterpret_cast<const bf16x4*>(sVt0 + col * LDC + i0 + g4);
+      const bf16x4 vb = *reinterpret_cast<const bf16x4*>(sVt0 + col * LDC + i0 + g4 + 4);
+      const float vv[8] = {(float)va[0], (float)va[1], (float)va[2], (float)va[3],
+                           (float)vb[0], (float)vb[1], (float)vb[2], (float)vb[3]};
+      const float w0 = sTaps[col], w1 = sTaps[D + col], w2 = sTaps[2 * D + col], w3 = sTaps[3 * D + col];
 #pragma unroll
-      for (int j = 0; j < 7; ++j) vv[j] = to_f(sV[(i0 + g4 + j) * LD + col]);  // rows t-3..t+3 (+3 halo offset)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float x = vv[r + 3];
+      for (int r = 0; r < 4; ++r) {  // token i0 + g4 + r is vv[r + 4]; tap j multiplies token - 3 + j
+        const float x = vv[r + 4];
         Vp[vt][r] = x;
-        const float anc = taps[vt][0] * vv[r] + taps[vt][1] * vv[r + 1] + taps[vt][2] * vv[r + 2] +
-                          taps[vt][3] * vv[r + 3];
-        Rr[vt][r] = x - anc;
+        Rr[vt][r] = x - (w0 * vv[r + 1] + w1 * vv[r + 2] + w2 * vv[r + 3] + w3 * vv[r + 4]);
       }
       Oc[vt] = zero4();
     }
@@ -249,10 +367,9 @@ __global__ __launch_bounds__(256, 1) void seg_fast_kernel(FwdArgs a) {
       for (int jt = 0; jt < MT; ++jt) {
         praw[jt] = zero4();
         mraw[jt] = zero4();
-        if (jt <= w) {
-          mm_ll<bf16_t>(praw[jt], sK, LD, 16 * jt, sQ, LD, i0, D);   // (K_j Q_w^T): [j][i]
-          mm_ll<bf16_t>(mraw[jt], sK, LD, i0, sK, LD, 16 * jt, D);   // (K_w K_j^T): [i][j]
-        }
+        // all four tiles, masked below: branch-free, and wave 3 needs all four anyway
+        mm_ll<bf16_t>(praw[jt], sK, LD, 16 * jt, sQ, LD, i0, D);   // (K_j Q_w^T): [j][i]
+        mm_ll<bf16_t>(mraw[jt], sK, LD, 16 * jt, sK, LD, i0, D);   // (K_j K_w^T): [j][i]
       }
       const float bi_lane = sB[i0 + li];
 #pragma unroll
@@ -260,34 +377,46 @@ __global__ __launch_bounds__(256, 1) void seg_fast_kernel(FwdArgs a) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const int jt = 2 * kb + h;
+          const float4 bj = *reinterpret_cast<const float4*>(sB + 16 * jt + g4);
+          const float bjr[4] = {bj.x, bj.y, bj.z, bj.w};
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int jj = 16 * jt + g4 + r, ii = i0 + li;
-            const float val = (jt <= w && jj <= ii) ? __expf(bi_lane - sB[jj]) * praw[jt][r] : 0.f;
+            const float val = (jj <= ii) ? __expf(bi_lane - bjr[r]) * praw[jt][r] : 0.f;
             Pa[kb][4 * h + r] = (bf16_t)val;
           }
         }
       }
       // M tiles (row-major [i][j], strict lower, beta_i Gam_ij K_i.K_j)
+      const float4 bi4 = *reinterpret_cast<const float4*>(sB + i0 + g4);
+      const float4 be4 = *reinterpret_cast<const float4*>(sBeta + i0 + g4);
+      const float bir[4] = {bi4.x, bi4.y, bi4.z, bi4.w};
+      const float ber[4] = {be4.x, be4.y, be4.z, be4.w};
+      {  // lane holds M[i0 + li][16 jt + g4 + r]: four consecutive columns of one row
+        const float bil = sB[i0 + li], beil = sBeta[i0 + li];
 #pragma unroll
-      for (int jt = 0; jt < MT; ++jt) {
-        if (jt <= w) {
+        for (int jt = 0; jt < MT; ++jt) {
+          if (jt < w) {
+            const float4 bj = *reinterpret_cast<const float4*>(sB + 16 * jt + g4);
+            const float bjr[4] = {bj.x, bj.y, bj.z, bj.w};
+            bf16x4 mv;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int ii = i0 + g4 + r, jj = 16 * jt + li;
-            const float val = (jj < ii) ? sBeta[ii] * __expf(sB[ii] - sB[jj]) * mraw[jt][r] : 0.f;
-            sM[ii * LDC + jj] = (bf16_t)val;
+            for (int r = 0; r < 4; ++r) mv[r] = (bf16_t)(beil * __expf(bil - bjr[r]) * mraw[jt][r]);
+            *reinterpret_cast<bf16x4*>(sM + (i0 + li) * LDC + 16 * jt + g4) = mv;
           }
         }
       }
       // diagonal block inverse: Y = -M_ww (and Y^T, from the symmetric raw Gram tile)
       f32x4 Y, Yt;
+      {
+        const float bl = sB[i0 + li], bel = sBeta[i0 + li];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int ii = i0 + g4 + r, jj = i0 + li;
-        const float raw = mraw[w][r];
-        Y[r] = (jj < ii) ? -sBeta[ii] * __expf(sB[ii] - sB[jj]) * raw : 0.f;
-        Yt[r] = (ii < jj) ? -sBeta[jj] * __expf(sB[jj] - sB[ii]) * raw : 0.f;
+        for (int r = 0; r < 4; ++r) {
+          const int ii = i0 + g4 + r, jj = i0 + li;
+          const float raw = mraw[w][r];
+          Y[r] = (jj < ii) ? -ber[r] * __expf(bir[r] - bl) * raw : 0.f;
+          Yt[r] = (ii < jj) ? -bel * __expf(bl - bir[r]) * raw : 0.f;
+        }
       }
       const f32x4 Y2 = mm16_f32(Yt, Y), Y2t = mm16_f32(Y, Yt);
       const f32x4 Y4 = mm16_f32(Y2t, Y2), Y4t = mm16_f32(Y2, Y2t);
@@ -305,28 +434,39 @@ __global__ __launch_bounds__(256, 1) void seg_fast_kernel(FwdArgs a) {
     f32x4 HB[KT];
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt) HB[kt] = zero4();
+    QuadRegs<D, C> preU, preG;
     for (int lr = 1; lr < L; ++lr) {
       unsigned char* slot = slot0 + (size_t)((lr - 1) & 1) * Ly::szSlot;
       bf16_t* sU = reinterpret_cast<bf16_t*>(slot);
-      bf16_t* sGm = reinterpret_cast<bf16_t*>(slot + Ly::szTD);
-      bf16_t* sRt = reinterpret_cast<bf16_t*>(slot + 2 * Ly::szTD);
-      load_rows<D, C, LD, LDC>(sU, nullptr, u + (size_t)(lr - 1) * D, (size_t)Lm1 * D, t0, hi);
-      load_rows<D, C, LD, LDC>(sGm, nullptr, gam + (size_t)(lr - 1) * D, (size_t)Lm1 * D, t0, hi);
-      __syncthreads();
+      bf16_t* sGt = reinterpret_cast<bf16_t*>(slot + Ly::szTD);                  // gamma_{l-1}^T
+      bf16_t* sRt = reinterpret_cast<bf16_t*>(slot + Ly::szTD + Ly::szDT);       // R_l^T
+      bf16_t* sUt = reinterpret_cast<bf16_t*>(slot + Ly::szTD + 2 * Ly::szDT);   // U_l^T
+      __syncthreads();  // U_l, gamma_{l-1} of this step are in the slot
+      if (lr + 1 < L) {
+        const int hi = min(T, t0 + C);
+        fetch_quads<D, C>(preU, u + (size_t)lr * D, (size_t)Lm1 * D, t0, hi);
+        fetch_quads<D, C>(preG, gam + (size_t)lr * D, (size_t)Lm1 * D, t0, hi);
+      }
       // residual step and R_l = alpha_l r_l for rows 16w.., written transposed
+      {
+        const float4 ap4 = *reinterpret_cast<const float4*>(sAlphaT + (lr - 1) * C + i0 + g4);
+        const float4 al4 = *reinterpret_cast<const float4*>(sAlphaT + lr * C + i0 + g4);
+        const float ap[4] = {ap4.x, ap4.y, ap4.z, ap4.w}, aw[4] = {al4.x, al4.y, al4.z, al4.w};
+        bf16x4 gv[KT];
 #pragma unroll
-      for (int vt = 0; vt < KT; ++vt) {
-        const int col = 16 * vt + li;
-        bf16x4 rv;
+        for (int vt = 0; vt < KT; ++vt)
+          gv[vt] = *reinterpret_cast<const bf16x4*>(sGt + (16 * vt + li) * LDC + i0 + g4);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int t = i0 + g4 + r;
-          const float gm = to_f(sGm[t * LD + col]);
-          const float x = Rr[vt][r] * (1.f - sAlpha[t * 8 + lr - 1] * gm);
-          Rr[vt][r] = x;
-          rv[r] = (bf16_t)(sAlpha[t * 8 + lr] * x);
+        for (int vt = 0; vt < KT; ++vt) {
+          bf16x4 rv;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float x = Rr[vt][r] * (1.f - ap[r] * (float)gv[vt][r]);
+            Rr[vt][r] = x;
+            rv[r] = (bf16_t)(aw[r] * x);
+          }
+          *reinterpret_cast<bf16x4*>(sRt + (16 * vt + li) * LDC + i0 + g4) = rv;
         }
-        *reinterpret_cast<bf16x4*>(sRt + col * LDC + i0 + g4) = rv;
       }
       __syncthreads();
       // row-owned: X1 = -strict(Gam * K U^T), X2 = lower(Gam * Q U^T) as A fragments
@@ -336,10 +476,8 @@ __global__ __launch_bounds__(256, 1) void seg_fast_kernel(FwdArgs a) {
         for (int jt = 0; jt < MT; ++jt) {
           x1raw[jt] = zero4();
           x2raw[jt] = zero4();
-          if (jt <= w) {
-            mm_ll<bf16_t>(x1raw[jt], sU, LD, 16 * jt, sK, LD, i0, D);  // (U_j K_w^T): [j][i]
-            mm_ll<bf16_t>(x2raw[jt], sU, LD, 16 * jt, sQ, LD, i0, D);  // (U_j Q_w^T): [j][i]
-          }
+          mm_ll<bf16_t>(x1raw[jt], sU, LD, 16 * jt, sK, LD, i0, D);  // (U_j K_w^T): [j][i]
+          mm_ll<bf16_t>(x2raw[jt], sU, LD, 16 * jt, sQ, LD, i0, D);  // (U_j Q_w^T): [j][i]
         }
         const float bi_lane = sB[i0 + li];
         bf16x8 X1a[2], X2a[2];
@@ -348,43 +486,58 @@ __global__ __launch_bounds__(256, 1) void seg_fast_kernel(FwdArgs a) {
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
             const int jt = 2 * kb + h;
+            const float4 bj = *reinterpret_cast<const float4*>(sB + 16 * jt + g4);
+            const float bjr[4] = {bj.x, bj.y, bj.z, bj.w};
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
               const int jj = 16 * jt + g4 + r, ii = i0 + li;
-              const float gm = (jt <= w && jj <= ii) ? __expf(bi_lane - sB[jj]) : 0.f;
+              const float gm = (jj <= ii) ? __expf(bi_lane - bjr[r]) : 0.f;
               X1a[kb][4 * h + r] = (bf16_t)((jj < ii) ? -gm * x1raw[jt][r] : 0.f);
               X2a[kb][4 * h + r] = (bf16_t)(gm * x2raw[jt][r]);
             }
           }
-        const int nkb = (w + 2) / 2;
 #pragma unroll
         for (int vt = 0; vt < KT; ++vt) {
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb) {
-            if (kb < nkb) {
-              const bf16x8 rb = cat8(ldsT_b4(sRt, LDC, 16 * vt, 32 * kb), ldsT_b4(sRt, LDC, 16 * vt, 32 * kb + 16));
-              Vp[vt] = mfma(X1a[kb], rb, Vp[vt]);
-              Oc[vt] = mfma(X2a[kb], rb, Oc[vt]);
-            }
+          for (int kb = 0; kb < 2; ++kb) {  // fragments above the diagonal are zero
+            const bf16x8 rb = cat8(ldsT_b4(sRt, LDC, 16 * vt, 32 * kb), ldsT_b4(sRt, LDC, 16 * vt, 32 * kb + 16));
+            Vp[vt] = mfma(X1a[kb], rb, Vp[vt]);
+            Oc[vt] = mfma(X2a[kb], rb, Oc[vt]);
           }
         }
       }
-      // column-owned: HB(:, w) += U^T diag(D) R(:, w)
-#pragma unroll
-      for (int kt = 0; kt < KT; ++kt) {
+      // column-owned: HB(:, w) += U^T diag(D) R(:, w)  (A from U^T, scaled by D in registers)
+      {
+        bf16x8 rb[2];  // D (.) R(:, w), the B operand
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-          bf16x8 ua;
+          const float4 d0 = *reinterpret_cast<const float4*>(sD + 32 * kb + g4);
+          const float4 d1 = *reinterpret_cast<const float4*>(sD + 32 * kb + 16 + g4);
+          const float dv8[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+          const bf16x8 r8 = cat8(ldsT_b4(sRt, LDC, 16 * w, 32 * kb), ldsT_b4(sRt, LDC, 16 * w, 32 * kb + 16));
 #pragma unroll
-          for (int p = 0; p < 8; ++p) {
-            const int tk = 32 * kb + ((p >> 2) << 4) + g4 + (p & 3);
-            ua[p] = (bf16_t)(sD[tk] * to_f(sU[tk * LD + 16 * kt + li]));
+          for (int p = 0; p < 8; ++p) rb[kb][p] = (bf16_t)(dv8[p] * (float)r8[p]);
+        }
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt) {
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) {
+            const bf16x8 ua = cat8(ldsT_b4(sUt, LDC, 16 * kt, 32 * kb), ldsT_b4(sUt, LDC, 16 * kt, 32 * kb + 16));
+            HB[kt] = mfma(ua, rb[kb], HB[kt]);
           }
-          const bf16x8 rb = cat8(ldsT_b4(sRt, LDC, 16 * w, 32 * kb), ldsT_b4(sRt, LDC, 16 * w, 32 * kb + 16));
-          HB[kt] = mfma(ua, rb, HB[kt]);
         }
       }
+      if (lr + 1 < L) {  // the other slot was last read before this step's first barrier
+        unsigned char* nslot = slot0 + (size_t)(lr & 1) * Ly::szSlot;
+        store_quads<D, C, LD, LDC>(preU, reinterpret_cast<bf16_t*>(nslot),
+                                   reinterpret_cast<bf16_t*>(nslot + Ly::szTD + 2 * Ly::szDT));
+        store_quads<D, C, LD, LDC>(preG, nullptr, reinterpret_cast<bf16_t*>(nslot + Ly::szTD));
+      }
     }
+
+    // next chunk's inputs: issued here so their registers are live only through the
+    // remaining phases, which still cover the load latency
+    if (c + 1 < c_end) fetch_chunk(pre, c + 1);
 
     // ---- exchange beta * V' (transposed) for the column-owned solve -------------------
     // After the refinement loop: slot F (not used by the last step, so free while other
@@ -532,15 +685,12 @@ __global__ __launch_bounds__(256, 1) void seg_fast_kernel(FwdArgs a) {
     // ---- row-owned: O += P E, write O_loc ---------------------------------------------------
     {
       float* oloc = a.Oloc + ((size_t)pr * Tpad + t0 + i0) * D;
-      const int nkb = (w + 2) / 2;
 #pragma unroll
       for (int vt = 0; vt < KT; ++vt) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-          if (kb < nkb) {
-            const bf16x8 eb = cat8(ldsT_b4(sEt, LDC, 16 * vt, 32 * kb), ldsT_b4(sEt, LDC, 16 * vt, 32 * kb + 16));
-            Oc[vt] = mfma(Pa[kb], eb, Oc[vt]);
-          }
+          const bf16x8 eb = cat8(ldsT_b4(sEt, LDC, 16 * vt, 32 * kb), ldsT_b4(sEt, LDC, 16 * vt, 32 * kb + 16));
+          Oc[vt] = mfma(Pa[kb], eb, Oc[vt]);
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) oloc[(size_t)(g4 + r) * D + 16 * vt + li] = Oc[vt][r];
@@ -549,26 +699,26 @@ __global__ __launch_bounds__(256, 1) void seg_fast_kernel(FwdArgs a) {
     // ---- column-owned: H(:, w) = G_C H + K^T D E + HB;  A_acc(:, w) = G_C A_acc - K^T D WA
     {
       const float GC = sG[C - 1];
-      bf16x8 eb[2], wb[2];
+      bf16x8 eb[2], wb[2];  // D (.) E(:, w) and D (.) WA(:, w), the B operands
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        eb[kb] = cat8(to_bf16x4(E[2 * kb]), to_bf16x4(E[2 * kb + 1]));
-        wb[kb] = cat8(to_bf16x4(WA[2 * kb]), to_bf16x4(WA[2 * kb + 1]));
+        const float4 d0 = *reinterpret_cast<const float4*>(sD + 32 * kb + g4);
+        const float4 d1 = *reinterpret_cast<const float4*>(sD + 32 * kb + 16 + g4);
+        const float dv8[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          eb[kb][r] = (bf16_t)(dv8[r] * E[2 * kb][r]);
+          eb[kb][4 + r] = (bf16_t)(dv8[4 + r] * E[2 * kb + 1][r]);
+          wb[kb][r] = (bf16_t)(dv8[r] * WA[2 * kb][r]);
+          wb[kb][4 + r] = (bf16_t)(dv8[4 + r] * WA[2 * kb + 1][r]);
+        }
       }
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt) {
         f32x4 he = zero4(), aw = zero4();
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-          bf16x8 kd;
-          const bf16_t* ar = sKt + (16 * kt + li) * LDC + 32 * kb + g4;
-          const bf16x4 k0 = *reinterpret_cast<const bf16x4*>(ar);
-          const bf16x4 k1 = *reinterpret_cast<const bf16x4*>(ar + 16);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            kd[r] = (bf16_t)(sD[32 * kb + g4 + r] * (float)k0[r]);
-            kd[4 + r] = (bf16_t)(sD[32 * kb + 16 + g4 + r] * (float)k1[r]);
-          }
+          const bf16x8 kd = cat8(ldsT_b4(sKt, LDC, 16 * kt, 32 * kb), ldsT_b4(sKt, LDC, 16 * kt, 32 * kb + 16));
           he = mfma(kd, eb[kb], he);
           aw = mfma(kd, wb[kb], aw);
         }
@@ -580,12 +730,13 @@ __global__ __launch_bounds__(256, 1) void seg_fast_kernel(FwdArgs a) {
       }
     }
     __syncthreads();
-    // new H^T and A_acc^T into LDS for the next chunk
+    // new H^T and A_acc^T into LDS for the next chunk, then the prefetched inputs
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt) {
       *reinterpret_cast<bf16x4*>(sHt + (16 * w + li) * LD + 16 * kt + g4) = to_bf16x4(Hs[kt]);
       *reinterpret_cast<bf16x4*>(sAt + (16 * w + li) * LD + 16 * kt + g4) = to_bf16x4(As[kt]);
     }
+    if (c + 1 < c_end) store_chunk(pre);
   }
 
   // ---- segment operator (float32) ---------------------------------------------------------
@@ -600,46 +751,86 @@ __global__ __launch_bounds__(256, 1) void seg_fast_kernel(FwdArgs a) {
     }
 }
 
-// Inter-segment recurrence H_in(s+1) = A_s H_in(s) + B_s (float32), JW state
-// columns per workgroup; each thread owns one (row, column) and prefetches the
-// next segment's operator row while the current step runs.
+// Inter-segment recurrence H_in(s+1) = A_s H_in(s) + B_s (float32) for JW state
+// columns per workgroup; thread (i, j) owns row i, column c0 + j.  The step is
+// latency-bound (each needs a fresh 64x64 A_s), so the operators are prefetched
+// DEPTH steps ahead into a register ring (each thread holds 1/256 of every
+// in-flight A_s) and shared through LDS one step at a time.
 template <int DK, int DV>
 __global__ __launch_bounds__(256) void seg_scan_fast_kernel(FwdArgs a) {
   constexpr int JW = 256 / DK;
+  constexpr int DEPTH = 8;
+  constexpr int LDA = DK + 4;                  // padded row stride of the staged operator
+  constexpr int PIECES = DK * DK / 4 / 256;    // float4 pieces of A_s per thread
+  static_assert(PIECES >= 1, "operator must cover the workgroup");
+  __shared__ __align__(16) float sA[DK * LDA];
   __shared__ __align__(16) float sH[2][JW][DK];
+  __shared__ __align__(16) float sBs[DK * 4];
+  static_assert(JW == 4, "the B_s slice is staged as one float4 per row");
   const int tid = threadIdx.x, pr = blockIdx.x, c0 = JW * blockIdx.y;
   const int i = tid / JW, j = tid % JW;
-  sH[0][j][i] = 0.f;
-  float4 arow[DK / 4], nrow[DK / 4];
-  const float* A0 = a.Aagg + (size_t)pr * a.nseg * DK * DK;
-  const float* B0 = a.Bagg + (size_t)pr * a.nseg * DK * DV;
-#pragma unroll
-  for (int q = 0; q < DK / 4; ++q) arow[q] = reinterpret_cast<const float4*>(A0 + (size_t)i * DK)[q];
-  float bcur = B0[(size_t)i * DV + c0 + j];
-  __syncthreads();
-  int cur = 0;
-  for (int s = 0; s < a.nseg; ++s) {
-    float* Hi = a.Hin + ((size_t)pr * a.nseg + s) * DK * DV;
-    Hi[(size_t)i * DV + c0 + j] = sH[cur][j][i];
-    const int sn = s + 1 < a.nseg ? s + 1 : s;
-    const float* An = A0 + (size_t)sn * DK * DK;
-#pragma unroll
-    for (int q = 0; q < DK / 4; ++q) nrow[q] = reinterpret_cast<const float4*>(An + (size_t)i * DK)[q];
-    const float bnext = B0[(size_t)sn * DK * DV + (size_t)i * DV + c0 + j];
-    float acc = bcur;
-    const float4* hcol = reinterpret_cast<const float4*>(&sH[cur][j][0]);
-#pragma unroll
-    for (int q = 0; q < DK / 4; ++q) {
-      const float4 hv = hcol[q];
-      acc += arow[q].x * hv.x + arow[q].y * hv.y + arow[q].z * hv.z + arow[q].w * hv.w;
-    }
-    sH[cur ^ 1][j][i] = acc;
-    __syncthreads();
-    cur ^= 1;
-#pragma unroll
-    for (int q = 0; q < DK / 4; ++q) arow[q] = nrow[q];
-    bcur = bnext;
+  const int nseg = a.nseg;
+  const float* A0 = a.Aagg + (size_t)pr * nseg * DK * DK;
+  const float* B0 = a.Bagg + (size_t)pr * nseg * DK * DV;
+  float* H0 = a.Hin + (size_t)pr * nseg * DK * DV;
+  // Ring slot d (d = 0..7) holds the operator of the next step s with s % 8 == d,
+  // in named registers R<d>_<p>: four float4 pieces of A_s and one float4 of the
+  // B_s slice (rows tid % DK, columns c0..c0+3) per thread; the
+  // loop is unrolled eight times so each slot is read eight steps after its
+  // loads were issued.
+  static_assert(PIECES == 4, "the register ring is written for 4 pieces per thread");
+#define PRISM_FETCH(D, S)                                                                     \
+  {                                                                                           \
+    const int sn_ = (S) < nseg ? (S) : nseg - 1;                                              \
+    const float4* src_ = reinterpret_cast<const float4*>(A0 + (size_t)sn_ * DK * DK) + tid;   \
+    R##D##_0 = src_[0];                                                                       \
+    R##D##_1 = src_[256];                                                                     \
+    R##D##_2 = src_[512];                                                                     \
+    R##D##_3 = src_[768];                                                                     \
+    R##D##_4 = reinterpret_cast<const float4*>(B0 + (size_t)sn_ * DK * DV +                  \
+                                               (size_t)(tid % DK) * DV + c0)[0];              \
   }
+#define PRISM_DECL(D) float4 R##D##_0, R##D##_1, R##D##_2, R##D##_3, R##D##_4;
+  PRISM_DECL(0) PRISM_DECL(1) PRISM_DECL(2) PRISM_DECL(3)
+  PRISM_DECL(4) PRISM_DECL(5) PRISM_DECL(6) PRISM_DECL(7)
+  PRISM_FETCH(0, 0) PRISM_FETCH(1, 1) PRISM_FETCH(2, 2) PRISM_FETCH(3, 3)
+  PRISM_FETCH(4, 4) PRISM_FETCH(5, 5) PRISM_FETCH(6, 6) PRISM_FETCH(7, 7)
+  sH[0][j][i] = 0.f;
+  int cur = 0;
+  const int e0 = 4 * tid;  // element index of piece 0; piece p adds 1024 p
+#define PRISM_SCAN_STEP(D)                                                                    \
+  if (s0 + (D) < nseg) {                                                                      \
+    const int s = s0 + (D);                                                                   \
+    *reinterpret_cast<float4*>(&sA[((e0) / DK) * LDA + (e0) % DK]) = R##D##_0;                \
+    *reinterpret_cast<float4*>(&sA[((e0 + 1024) / DK) * LDA + (e0) % DK]) = R##D##_1;         \
+    *reinterpret_cast<float4*>(&sA[((e0 + 2048) / DK) * LDA + (e0) % DK]) = R##D##_2;         \
+    *reinterpret_cast<float4*>(&sA[((e0 + 3072) / DK) * LDA + (e0) % DK]) = R##D##_3;         \
+    if (tid < DK) *reinterpret_cast<float4*>(&sBs[tid * 4]) = R##D##_4;                       \
+    PRISM_FETCH(D, s + 8)                                                                     \
+    __syncthreads();                                                                          \
+    H0[(size_t)s * DK * DV + (size_t)i * DV + c0 + j] = sH[cur][j][i];                        \
+    float acc0 = sBs[i * 4 + j], acc1 = 0.f, acc2 = 0.f, acc3 = 0.f;                          \
+    const float4* arow = reinterpret_cast<const float4*>(&sA[i * LDA]);                       \
+    const float4* hcol = reinterpret_cast<const float4*>(&sH[cur][j][0]);                     \
+    _Pragma("unroll") for (int q = 0; q < DK / 4; ++q) {                                      \
+      const float4 av = arow[q], hv = hcol[q];                                                \
+      acc0 += av.x * hv.x;                                                                    \
+      acc1 += av.y * hv.y;                                                                    \
+      acc2 += av.z * hv.z;                                                                    \
+      acc3 += av.w * hv.w;                                                                    \
+    }                                                                                         \
+    sH[cur ^ 1][j][i] = (acc0 + acc1) + (acc2 + acc3);                                        \
+    cur ^= 1;                                                                                 \
+    __syncthreads();                                                                          \
+  }
+  static_assert(DEPTH == 8, "the step list below has eight ring slots");
+  for (int s0 = 0; s0 < nseg; s0 += DEPTH) {
+    PRISM_SCAN_STEP(0) PRISM_SCAN_STEP(1) PRISM_SCAN_STEP(2) PRISM_SCAN_STEP(3)
+    PRISM_SCAN_STEP(4) PRISM_SCAN_STEP(5) PRISM_SCAN_STEP(6) PRISM_SCAN_STEP(7)
+  }
+#undef PRISM_SCAN_STEP
+#undef PRISM_FETCH
+#undef PRISM_DECL
   a.S_final[(size_t)pr * DK * DV + (size_t)i * DV + c0 + j] = sH[cur][j][i];
 }
 
