@@ -57,9 +57,11 @@ __device__ __forceinline__ bf16x8 cat8(const bf16x4& a, const bf16x4& b) {
 // LDS plan of the fast sweep (bytes).
 template <int D, int C>
 struct FastLds {
-  static constexpr int LD = D + 8;    // row stride of [token][d] arrays (bf16)
-  static constexpr int LDC = C + 8;   // row stride of [d][token] arrays (bf16)
-  static constexpr int LDT = 16 + 8;  // row stride of a 16x16 diagonal inverse block
+  // Row strides of 34 / 10 dwords: the 16 rows an MFMA fragment read touches (and
+  // the 16 lanes of a 4x4-block store) land in distinct bank pairs.
+  static constexpr int LD = D + 4;    // row stride of [token][d] arrays (bf16)
+  static constexpr int LDC = C + 4;   // row stride of [d][token] arrays (bf16)
+  static constexpr int LDT = 16 + 4;  // row stride of a 16x16 diagonal inverse block
   static constexpr size_t szTD = (size_t)C * LD * 2;   // [C][LD]
   static constexpr size_t szDT = (size_t)D * LDC * 2;  // [D][LDC]
   static constexpr size_t szDD = (size_t)D * LD * 2;   // [D][LD]
@@ -82,76 +84,33 @@ struct FastLds {
   static constexpr size_t total = oSlot + 2 * szSlot;
   static_assert(szTD + 2 * szDT <= szSlot, "Wc, Wc^T and E^T must fit one slot");
   static_assert(C + 4 <= LDC, "V^T needs C + 4 token positions");
+  static_assert(LD % 4 == 0 && LDC % 4 == 0 && LDT % 4 == 0, "8-byte aligned rows");
   static constexpr bool fits = total <= 160 * 1024;
 };
 
-// Row-major [ROWS][D] bf16 tiles move global -> registers -> LDS in 16-byte
-// pieces: fetch_rows issues the loads (tile row r is global row row0 + r of
-// `src`, row stride `row_stride` elements; rows outside [0, hi) read as zero)
-// and store_rows writes them to LDS (row stride LD), optionally also as the
-// transposed copy dstT[c][r] (row stride LDC).  Splitting the two lets a load be
-// issued a whole phase before its data is needed.
-template <int D, int ROWS>
-struct RowRegs {
-  static constexpr int PER_ROW = D / 8;
-  static constexpr int NP = ROWS * PER_ROW;
-  static constexpr int NIT = (NP + 255) / 256;
-  uint4 x[NIT];
-  int row0, hi;  // validity window, applied when the registers are stored
-};
-
-// Issues the loads only: the registers are not read until store_rows, so the
-// loads stay in flight across the caller's compute.  Out-of-range rows load
-// row 0 of `src` (always valid) and are zeroed at store time.
-template <int D, int ROWS>
-__device__ __forceinline__ void fetch_rows(RowRegs<D, ROWS>& R, const bf16_t* src, size_t row_stride, int row0,
-                                           int hi) {
-  using RR = RowRegs<D, ROWS>;
-  R.row0 = row0;
-  R.hi = hi;
-#pragma unroll
-  for (int it = 0; it < RR::NIT; ++it) {
-    const int idx = threadIdx.x + 256 * it;
-    const int row = idx / RR::PER_ROW, cv = (idx % RR::PER_ROW) * 8;
-    const int gr = row0 + row;
-    const bool ok = idx < RR::NP && gr >= 0 && gr < hi;
-    const size_t rc = ok ? (size_t)gr : 0;
-    R.x[it] = *reinterpret_cast<const uint4*>(src + rc * row_stride + cv);
-  }
-}
-
-template <int D, int ROWS, int LD, int LDC>
-__device__ __forceinline__ void store_rows(const RowRegs<D, ROWS>& R, bf16_t* dst, bf16_t* dstT) {
-  using RR = RowRegs<D, ROWS>;
-#pragma unroll
-  for (int it = 0; it < RR::NIT; ++it) {
-    const int idx = threadIdx.x + 256 * it;
-    if (idx >= RR::NP) break;
-    const int row = idx / RR::PER_ROW, cv = (idx % RR::PER_ROW) * 8;
-    const int gr = R.row0 + row;
-    const uint4 x = (gr >= 0 && gr < R.hi) ? R.x[it] : make_uint4(0, 0, 0, 0);
-    if (dst != nullptr) *reinterpret_cast<uint4*>(dst + row * LD + cv) = x;
-    if (dstT != nullptr) {
-      const bf16_t* e = reinterpret_cast<const bf16_t*>(&x);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) dstT[(cv + j) * LDC + row] = e[j];
-    }
-  }
-}
-
-// Tiles that also need a transposed LDS copy move in 4-row x 4-column blocks:
-// each thread loads four 8-byte row pieces and writes the transposed copy as
-// four 8-byte writes (4 consecutive tokens of one column) instead of sixteen
-// 2-byte ones.  Blocks are numbered column-quad fastest so that the global loads
-// of 16 lanes cover one 128-byte row.
+// Input tiles move global -> registers -> LDS in 4-row x 4-column blocks:
+// fetch_quads issues the loads (tile row r is global row row0 + r of `src`,
+// rows outside [0, hi) read as zero at store time) and store_quads writes them
+// to LDS, row-major and / or as the transposed copy; the transposed copy is four
+// 8-byte writes (4 consecutive tokens of one column).  Splitting fetch and
+// store lets a load be issued a whole phase before its data is needed.
 template <int D, int ROWS>
 struct QuadRegs {
   static_assert(ROWS % 4 == 0, "rows come in quads");
-  static constexpr int CQ = D / 4;
-  static constexpr int NB = (ROWS / 4) * CQ;
+  static_assert(D == 64, "the block map below assumes 16 column quads");
+  static constexpr int RQ = ROWS / 4;
+  static constexpr int NB = RQ * 16;
   static constexpr int NIT = (NB + 255) / 256;
   uint2 x[NIT][4];
   int row0, hi;
+  // Block b: a wave covers 4 row quads x 16 column quads; each 16-lane group holds a
+  // 4 x 4 patch of blocks, so its row-major and its transposed 8-byte stores both hit
+  // 32 distinct banks, and a wave's load of one row offset reads 4 whole rows.
+  static __device__ __forceinline__ void map(int b, int& rq, int& c4) {
+    const int l = b & 63;
+    rq = 4 * (b >> 6) + (l & 3);
+    c4 = 4 * (4 * (l >> 4) + ((l >> 2) & 3));
+  }
 };
 
 template <int D, int ROWS>
@@ -163,11 +122,12 @@ __device__ __forceinline__ void fetch_quads(QuadRegs<D, ROWS>& R, const bf16_t* 
 #pragma unroll
   for (int it = 0; it < RR::NIT; ++it) {
     const int b = threadIdx.x + 256 * it;
-    const int rq = b / RR::CQ, c4 = (b % RR::CQ) * 4;
+    int rq, c4;
+    RR::map(b, rq, c4);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int gr = row0 + 4 * rq + r;
-      const bool ok = b < RR::NB && gr >= 0 && gr < hi;
+      const bool ok = rq < RR::RQ && gr >= 0 && gr < hi;
       const size_t rc = ok ? (size_t)gr : 0;
       R.x[it][r] = *reinterpret_cast<const uint2*>(src + rc * row_stride + c4);
     }
@@ -180,8 +140,9 @@ __device__ __forceinline__ void store_quads(const QuadRegs<D, ROWS>& R, bf16_t* 
 #pragma unroll
   for (int it = 0; it < RR::NIT; ++it) {
     const int b = threadIdx.x + 256 * it;
-    if (b >= RR::NB) break;
-    const int rq = b / RR::CQ, c4 = (b % RR::CQ) * 4;
+    int rq, c4;
+    RR::map(b, rq, c4);
+    if (rq >= RR::RQ) continue;
     bf16x4 rows[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -275,15 +236,14 @@ __global__ __launch_bounds__(256, 1) void seg_fast_kernel(FwdArgs a) {
   // Everything one chunk reads from HBM, held in registers between its fetch (one
   // chunk ahead) and its store into LDS.
   struct ChunkRegs {
-    RowRegs<D, C> q;
-    QuadRegs<D, C> k, u1, g1;
+    QuadRegs<D, C> q, k, u1, g1;
     QuadRegs<D, C + 4> v;
     float lg, be, al[8];
     bool ok;  // this lane's token of the gates is inside the sequence
   };
   auto fetch_chunk = [&](ChunkRegs& R, int c) {
     const int t0 = c * C, hi = min(T, t0 + C);
-    fetch_rows<D, C>(R.q, q, D, t0, hi);
+    fetch_quads<D, C>(R.q, q, D, t0, hi);
     fetch_quads<D, C>(R.k, k, D, t0, hi);
     fetch_quads<D, C + 4>(R.v, v, D, t0 - 4, hi);
     if (L > 1) {
@@ -302,7 +262,7 @@ __global__ __launch_bounds__(256, 1) void seg_fast_kernel(FwdArgs a) {
     }
   };
   auto store_chunk = [&](const ChunkRegs& R) {
-    store_rows<D, C, LD, LDC>(R.q, sQ, nullptr);
+    store_quads<D, C, LD, LDC>(R.q, sQ, nullptr);
     store_quads<D, C, LD, LDC>(R.k, sK, sKt);
     store_quads<D, C + 4, LD, LDC>(R.v, nullptr, sVt0);
     if (L > 1) {
@@ -361,6 +321,7 @@ __global__ __launch_bounds__(256, 1) void seg_fast_kernel(FwdArgs a) {
     }
     // ---- P(w, j) = lower(Gam * Q K^T) as chained A fragments; M(w, j) -> LDS -------------
     bf16x8 Pa[2];
+    float dec[MT][4];
     {
       f32x4 praw[MT], mraw[MT];
 #pragma unroll
@@ -371,37 +332,38 @@ __global__ __launch_bounds__(256, 1) void seg_fast_kernel(FwdArgs a) {
         mm_ll<bf16_t>(praw[jt], sK, LD, 16 * jt, sQ, LD, i0, D);   // (K_j Q_w^T): [j][i]
         mm_ll<bf16_t>(mraw[jt], sK, LD, 16 * jt, sK, LD, i0, D);   // (K_j K_w^T): [j][i]
       }
-      const float bi_lane = sB[i0 + li];
+      // decay factors Gam(i0 + li, 16 jt + g4 + r), zero above the diagonal; every
+      // masked Gram tile of this chunk (P, M, X1, X2) uses this lane layout
+      {
+        const float bi_lane = sB[i0 + li];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int jt = 2 * kb + h;
+        for (int jt = 0; jt < MT; ++jt) {
           const float4 bj = *reinterpret_cast<const float4*>(sB + 16 * jt + g4);
           const float bjr[4] = {bj.x, bj.y, bj.z, bj.w};
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int jj = 16 * jt + g4 + r, ii = i0 + li;
-            const float val = (jj <= ii) ? __expf(bi_lane - bjr[r]) * praw[jt][r] : 0.f;
-            Pa[kb][4 * h + r] = (bf16_t)val;
-          }
+          for (int r = 0; r < 4; ++r)
+            dec[jt][r] = (16 * jt + g4 + r <= i0 + li) ? __expf(bi_lane - bjr[r]) : 0.f;
         }
       }
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) Pa[kb][4 * h + r] = (bf16_t)(dec[2 * kb + h][r] * praw[2 * kb + h][r]);
       // M tiles (row-major [i][j], strict lower, beta_i Gam_ij K_i.K_j)
       const float4 bi4 = *reinterpret_cast<const float4*>(sB + i0 + g4);
       const float4 be4 = *reinterpret_cast<const float4*>(sBeta + i0 + g4);
       const float bir[4] = {bi4.x, bi4.y, bi4.z, bi4.w};
       const float ber[4] = {be4.x, be4.y, be4.z, be4.w};
+      const float beil = sBeta[i0 + li];
       {  // lane holds M[i0 + li][16 jt + g4 + r]: four consecutive columns of one row
-        const float bil = sB[i0 + li], beil = sBeta[i0 + li];
 #pragma unroll
         for (int jt = 0; jt < MT; ++jt) {
           if (jt < w) {
-            const float4 bj = *reinterpret_cast<const float4*>(sB + 16 * jt + g4);
-            const float bjr[4] = {bj.x, bj.y, bj.z, bj.w};
             bf16x4 mv;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) mv[r] = (bf16_t)(beil * __expf(bil - bjr[r]) * mraw[jt][r]);
+            for (int r = 0; r < 4; ++r) mv[r] = (bf16_t)(beil * dec[jt][r] * mraw[jt][r]);
             *reinterpret_cast<bf16x4*>(sM + (i0 + li) * LDC + 16 * jt + g4) = mv;
           }
         }
@@ -409,13 +371,12 @@ __global__ __launch_bounds__(256, 1) void seg_fast_kernel(FwdArgs a) {
       // diagonal block inverse: Y = -M_ww (and Y^T, from the symmetric raw Gram tile)
       f32x4 Y, Yt;
       {
-        const float bl = sB[i0 + li], bel = sBeta[i0 + li];
+        const float bl = sB[i0 + li];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int ii = i0 + g4 + r, jj = i0 + li;
           const float raw = mraw[w][r];
-          Y[r] = (jj < ii) ? -ber[r] * __expf(bir[r] - bl) * raw : 0.f;
-          Yt[r] = (ii < jj) ? -bel * __expf(bl - bir[r]) * raw : 0.f;
+          Y[r] = (li < g4 + r) ? -ber[r] * __expf(bir[r] - bl) * raw : 0.f;
+          Yt[r] = (g4 + r < li) ? -beil * dec[w][r] * raw : 0.f;
         }
       }
       const f32x4 Y2 = mm16_f32(Yt, Y), Y2t = mm16_f32(Y, Yt);
@@ -479,20 +440,16 @@ __global__ __launch_bounds__(256, 1) void seg_fast_kernel(FwdArgs a) {
           mm_ll<bf16_t>(x1raw[jt], sU, LD, 16 * jt, sK, LD, i0, D);  // (U_j K_w^T): [j][i]
           mm_ll<bf16_t>(x2raw[jt], sU, LD, 16 * jt, sQ, LD, i0, D);  // (U_j Q_w^T): [j][i]
         }
-        const float bi_lane = sB[i0 + li];
         bf16x8 X1a[2], X2a[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
             const int jt = 2 * kb + h;
-            const float4 bj = *reinterpret_cast<const float4*>(sB + 16 * jt + g4);
-            const float bjr[4] = {bj.x, bj.y, bj.z, bj.w};
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-              const int jj = 16 * jt + g4 + r, ii = i0 + li;
-              const float gm = (jj <= ii) ? __expf(bi_lane - bjr[r]) : 0.f;
-              X1a[kb][4 * h + r] = (bf16_t)((jj < ii) ? -gm * x1raw[jt][r] : 0.f);
+              const float gm = dec[jt][r];
+              X1a[kb][4 * h + r] = (bf16_t)((16 * jt + g4 + r < i0 + li) ? -gm * x1raw[jt][r] : 0.f);
               X2a[kb][4 * h + r] = (bf16_t)(gm * x2raw[jt][r]);
             }
           }
@@ -764,7 +721,8 @@ __global__ __launch_bounds__(256) void seg_scan_fast_kernel(FwdArgs a) {
   constexpr int PIECES = DK * DK / 4 / 256;    // float4 pieces of A_s per thread
   static_assert(PIECES >= 1, "operator must cover the workgroup");
   __shared__ __align__(16) float sA[DK * LDA];
-  __shared__ __align__(16) float sH[2][JW][DK];
+  // column j of H at row stride DK + 4: the JW columns read together fall in different banks
+  __shared__ __align__(16) float sH[2][JW][DK + 4];
   __shared__ __align__(16) float sBs[DK * 4];
   static_assert(JW == 4, "the B_s slice is staged as one float4 per row");
   const int tid = threadIdx.x, pr = blockIdx.x, c0 = JW * blockIdx.y;
