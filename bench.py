@@ -247,8 +247,8 @@ def main():
                      "kernel": sweep_name, "algorithmic_bytes_per_launch": sweep_bytes},
         "path": {"algorithmic_bytes_per_step": w.pairs * w.T * path_bytes,
                  "hbm_roofline_tokens_per_s": tokens * HBM_PEAK_GBS * 1e9 / (w.pairs * w.T * path_bytes),
-                 "kernel_ms": {"seg_local": sweep_ms, "seg_scan": float(per[:, 1].mean()),
-                               "seg_fixup": float(per[:, 2].mean())},
+                 "kernel_ms": {"sweep": sweep_ms, "scan": float(per[:, 1].mean()),
+                               "fixup": float(per[:, 2].mean())},
                  "event_span_ms_per_step": span_ms / args.steps},
         "cpu_baseline": None,
     }
