@@ -8,6 +8,7 @@
 #include "prism.h"
 #include "prism_fast.h"
 #include "prism_kernels.h"
+#include "prism_sweep8.h"
 
 namespace {
 
@@ -35,9 +36,11 @@ struct Plan {
 
 bool valid_dim(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 
-// The specialised sweep (prism_fast.h): bfloat16, head dim 64, chunk 64.
-bool use_fast(int dk, int dv, int chunk, prism_dtype dt) {
-  return dt == PRISM_BF16 && dk == 64 && dv == 64 && chunk == 64 && prism::FastLds<64, 64>::fits;
+// The specialised sweep (prism_sweep8.h): bfloat16, head dim 64, chunk 64.
+// Its loads address one (b, h) pair's slice of u / gamma with 32-bit byte offsets.
+bool use_fast(int T, int dk, int dv, int L, int chunk, prism_dtype dt) {
+  const size_t slice = (size_t)T * (size_t)(L > 1 ? L - 1 : 1) * 64 * 2;
+  return dt == PRISM_BF16 && dk == 64 && dv == 64 && chunk == 64 && slice < ((size_t)1 << 31);
 }
 
 template <class E, int D, int C>
@@ -77,7 +80,7 @@ prism_status make_plan(int B, int H, int T, int dk, int dv, int L, int chunk, pr
   if (!mul_ok((size_t)B, (size_t)H, &P) || P > (size_t)INT32_MAX / 2) return PRISM_ERR_INVALID_ARG;
   if (P > 65535) return PRISM_ERR_UNSUPPORTED;  // (b, h) pairs map to grid.y
   const size_t nch = ((size_t)T + chunk - 1) / chunk;
-  const bool fast = use_fast(dk, dv, chunk, dt);
+  const bool fast = use_fast(T, dk, dv, L, chunk, dt);
   if (seg_chunks == 0) {
     const size_t target = fast ? kTargetWorkgroupsFast : kTargetWorkgroups;
     size_t nseg_target = fast ? target / P : (target + P - 1) / P;
@@ -132,7 +135,7 @@ prism_status launch(const FwdArgs& a, const Plan& pl, hipEvent_t* ev, hipStream_
 
 prism_status launch_fast(const FwdArgs& a, const Plan& pl, hipEvent_t* ev, hipStream_t stream) {
   if (!record(ev, 0, stream)) return PRISM_ERR_HIP;
-  hipLaunchKernelGGL((prism::seg_fast_kernel<64, 64>), dim3(pl.nseg, pl.P), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((prism::seg_sweep8_kernel<64, 64>), dim3(pl.nseg, pl.P), dim3(512), 0, stream, a);
   if (hipGetLastError() != hipSuccess || !record(ev, 1, stream)) return PRISM_ERR_HIP;
   hipLaunchKernelGGL((prism::seg_scan_fast_kernel<64, 64>), dim3(pl.P, 64 / 4), dim3(256), 0, stream, a);
   if (hipGetLastError() != hipSuccess || !record(ev, 2, stream)) return PRISM_ERR_HIP;
