@@ -135,7 +135,10 @@ prism_status launch(const FwdArgs& a, const Plan& pl, hipEvent_t* ev, hipStream_
 
 prism_status launch_fast(const FwdArgs& a, const Plan& pl, hipEvent_t* ev, hipStream_t stream) {
   if (!record(ev, 0, stream)) return PRISM_ERR_HIP;
-  hipLaunchKernelGGL((prism::seg_sweep8_kernel<64, 64>), dim3(pl.nseg, pl.P), dim3(512), 0, stream, a);
+  if (a.L == 4)  // the rank-4 sweep with its steps unrolled
+    hipLaunchKernelGGL((prism::seg_sweep8_kernel<64, 64, 3>), dim3(pl.nseg, pl.P), dim3(512), 0, stream, a);
+  else
+    hipLaunchKernelGGL((prism::seg_sweep8_kernel<64, 64, -1>), dim3(pl.nseg, pl.P), dim3(512), 0, stream, a);
   if (hipGetLastError() != hipSuccess || !record(ev, 1, stream)) return PRISM_ERR_HIP;
   hipLaunchKernelGGL((prism::seg_scan_fast_kernel<64, 64>), dim3(pl.P, 64 / 4), dim3(256), 0, stream, a);
   if (hipGetLastError() != hipSuccess || !record(ev, 2, stream)) return PRISM_ERR_HIP;

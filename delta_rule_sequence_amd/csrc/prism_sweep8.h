@@ -160,7 +160,7 @@ struct Sweep8Ctx {
   rsrc_t rq_, rk_, rv_, ru_, rg_;  // buffers over the pair's q, k, v, u, gamma
   const float *gg, *bb, *al;       // the pair's g, beta, alpha
   float *oloc, *qhat_base, *agg;   // outputs of this pair / segment
-  int T, L, Lm1, NL, c_begin, c_end, Tpad, pr;
+  int T, L, Lm1, c_begin, c_end, Tpad, pr;
   int ubytes;                      // bytes per token row of u / gamma
 };
 
@@ -239,6 +239,7 @@ __device__ __forceinline__ void gram_rows(bf16x8 (&fa)[2], const bf16_t* sY, con
 }
 
 // ---- the K waves ------------------------------------------------------------------------
+template <int LM1S>
 __device__ __forceinline__ void sweep8_kwave(const Sweep8Ctx& x, int wq) {
   constexpr int LD = Sweep8Lds::LD, LDT = Sweep8Lds::LDT, C = 64;
   const Sweep8View V(x.smem);
@@ -246,7 +247,10 @@ __device__ __forceinline__ void sweep8_kwave(const Sweep8Ctx& x, int wq) {
   const int rb = 3 - wq, cb = wq;
   int rq, c4;
   quad_map(threadIdx.x & 255, rq, c4);
-  const int Lm1 = x.Lm1, NL = x.NL, L = x.L;
+  // LM1S >= 0 fixes L - 1 at compile time: the rank-L steps are then unrolled, so the
+  // wait for each prefetched operand counts only the loads issued before it.
+  const int Lm1 = LM1S >= 0 ? LM1S : x.Lm1;
+  const int NL = Lm1 > 3 ? Lm1 : 3, L = Lm1 + 1;
 
   f32x4 H[4], Vp[4], HB[4], WH[4];
   float dec[4][4];
@@ -362,7 +366,7 @@ __device__ __forceinline__ void sweep8_kwave(const Sweep8Ctx& x, int wq) {
     __syncthreads();  // B1: M, diagonal inverse blocks, R_1
 
     // ---- P1 .. P_NL: rank-L steps ---------------------------------------------------------
-    for (int lv = 1; lv <= NL; ++lv) {
+    auto level_phase = [&](const int lv) {
       const int s = (lv - 1) & 1;
       if (lv <= Lm1) {
         const bf16_t* sU = V.slotU(s);
@@ -397,7 +401,9 @@ __device__ __forceinline__ void sweep8_kwave(const Sweep8Ctx& x, int wq) {
         if (lv + 2 <= Lm1)
           quad_fetch<4>(lpf, x.ru_, (t0 + 4 * rq) * x.ubytes + (lv + 1) * 128 + 2 * c4, x.ubytes);
       }
-      if (lv == 1 && c + 1 < x.c_end) fetch_chunk(c + 1);
+      // next chunk's inputs, issued once this chunk's last rank-L prefetch is consumed (the
+      // wait for a prefetched operand may cover every load issued before it)
+      if (lv == (Lm1 >= 2 ? Lm1 - 1 : 1) && c + 1 < x.c_end) fetch_chunk(c + 1);
       if (lv == NL) {  // (beta V')^T rows rb for the per-column solve
         const float4 be = *reinterpret_cast<const float4*>(V.sBeta + 16 * rb + g4);
 #pragma unroll
@@ -408,6 +414,12 @@ __device__ __forceinline__ void sweep8_kwave(const Sweep8Ctx& x, int wq) {
         }
       }
       __syncthreads();
+    };
+    if constexpr (LM1S >= 0) {
+#pragma unroll
+      for (int lv = 1; lv <= (LM1S > 3 ? LM1S : 3); ++lv) level_phase(lv);
+    } else {
+      for (int lv = 1; lv <= NL; ++lv) level_phase(lv);
     }
 
     // ---- P_S: Uc = M^-1 (beta V')(:, cb), E = Uc - WH, H(:, cb) update -------------------------
@@ -447,6 +459,7 @@ __device__ __forceinline__ void sweep8_kwave(const Sweep8Ctx& x, int wq) {
 }
 
 // ---- the Q waves ------------------------------------------------------------------------
+template <int LM1S>
 __device__ __forceinline__ void sweep8_qwave(const Sweep8Ctx& x, int wq) {
   constexpr int LD = Sweep8Lds::LD, LDT = Sweep8Lds::LDT, C = 64;
   const Sweep8View V(x.smem);
@@ -454,7 +467,10 @@ __device__ __forceinline__ void sweep8_qwave(const Sweep8Ctx& x, int wq) {
   const int rb = wq, cb = wq;
   int rq, c4;
   quad_map(threadIdx.x & 255, rq, c4);
-  const int Lm1 = x.Lm1, NL = x.NL, L = x.L;
+  // LM1S >= 0 fixes L - 1 at compile time: the rank-L steps are then unrolled, so the
+  // wait for each prefetched operand counts only the loads issued before it.
+  const int Lm1 = LM1S >= 0 ? LM1S : x.Lm1;
+  const int NL = Lm1 > 3 ? Lm1 : 3, L = Lm1 + 1;
 
   f32x4 A[4], O[4], WA[4];
   float rr[4][4];  // residual r_l of this lane's 4x4 block [row][col]
@@ -550,7 +566,7 @@ __device__ __forceinline__ void sweep8_qwave(const Sweep8Ctx& x, int wq) {
     __syncthreads();  // B1
 
     // ---- P1 .. P_NL: rank-L steps; M^-1 (P1), Wc (P2), WA and Qhat (P3) -------------------------
-    for (int lv = 1; lv <= NL; ++lv) {
+    auto level_phase = [&](const int lv) {
       const int s = (lv - 1) & 1;
       if (lv <= Lm1) {  // O += lower(Gam * Q U_l^T) R_l
         const bf16_t* sU = V.slotU(s);
@@ -642,8 +658,16 @@ __device__ __forceinline__ void sweep8_qwave(const Sweep8Ctx& x, int wq) {
         if (lv + 2 <= Lm1)
           quad_fetch<4>(lpf, x.rg_, (t0 + 4 * rq) * x.ubytes + (lv + 1) * 128 + 2 * c4, x.ubytes);
       }
-      if (lv == 1 && c + 1 < x.c_end) fetch_chunk(c + 1);
+      // next chunk's inputs, issued once this chunk's last rank-L prefetch is consumed (the
+      // wait for a prefetched operand may cover every load issued before it)
+      if (lv == (Lm1 >= 2 ? Lm1 - 1 : 1) && c + 1 < x.c_end) fetch_chunk(c + 1);
       __syncthreads();
+    };
+    if constexpr (LM1S >= 0) {
+#pragma unroll
+      for (int lv = 1; lv <= (LM1S > 3 ? LM1S : 3); ++lv) level_phase(lv);
+    } else {
+      for (int lv = 1; lv <= NL; ++lv) level_phase(lv);
     }
 
     // ---- P_S: O += diag(G) Q H;  A_acc(:, cb) = G_C A_acc - K^T D WA ---------------------------
@@ -689,7 +713,7 @@ __device__ __forceinline__ void sweep8_qwave(const Sweep8Ctx& x, int wq) {
     for (int r = 0; r < 4; ++r) x.agg[(16 * kt + g4 + r) * 64 + 16 * cb + li] = A[kt][r];
 }
 
-template <int D, int C>
+template <int D, int C, int LM1S>
 __global__ __launch_bounds__(512, 1) void seg_sweep8_kernel(FwdArgs a) {
   static_assert(D == 64 && C == 64, "the two-wave sweep is written for head dim 64 and 64-token chunks");
   __shared__ __align__(16) unsigned char smem[Sweep8Lds::total];
@@ -705,7 +729,6 @@ __global__ __launch_bounds__(512, 1) void seg_sweep8_kernel(FwdArgs a) {
   x.T = T;
   x.L = L;
   x.Lm1 = Lm1;
-  x.NL = Lm1 > 3 ? Lm1 : 3;  // phases between the Gram phase and the state phase
   x.c_begin = seg * a.seg_chunks;
   x.c_end = min(a.nch, x.c_begin + a.seg_chunks);
   x.Tpad = a.nch * C;
@@ -738,8 +761,8 @@ __global__ __launch_bounds__(512, 1) void seg_sweep8_kernel(FwdArgs a) {
   __syncthreads();
   // Both roles pass the same barriers in the same order: B0, B1, one per phase
   // P1 .. P_NL and one after the state phase, for every chunk of the segment.
-  if (w < 4) sweep8_kwave(x, w);
-  else sweep8_qwave(x, w - 4);
+  if (w < 4) sweep8_kwave<LM1S>(x, w);
+  else sweep8_qwave<LM1S>(x, w - 4);
 }
 
 }  // namespace prism
