@@ -54,6 +54,15 @@ __device__ __forceinline__ bf16x8 cat8(const bf16x4& a, const bf16x4& b) {
   return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// 8 bf16 of a 32-deep MFMA operand from row (r0 + lane%16) of a row-major array (LDS or global):
+// slots 0-3 are k0 + 4g .. +3 and slots 4-7 are k0 + 16 + 4g .. +3 (g = lane/16).  The
+// same read is the A operand (rows = output rows) and the B operand of a [n][k] array.
+__device__ __forceinline__ bf16x8 frag8(const bf16_t* X, int ld, int r0, int k0) {
+  const int l = lane_id();
+  const bf16_t* p = X + (r0 + (l & 15)) * ld + k0 + 4 * (l >> 4);
+  return cat8(*reinterpret_cast<const bf16x4*>(p), *reinterpret_cast<const bf16x4*>(p + 16));
+}
+
 // LDS plan of the fast sweep (bytes).
 template <int D, int C>
 struct FastLds {
@@ -708,136 +717,183 @@ __global__ __launch_bounds__(256, 1) void seg_fast_kernel(FwdArgs a) {
     }
 }
 
-// Inter-segment recurrence H_in(s+1) = A_s H_in(s) + B_s (float32) for JW state
-// columns per workgroup; thread (i, j) owns row i, column c0 + j.  The step is
-// latency-bound (each needs a fresh 64x64 A_s), so the operators are prefetched
-// DEPTH steps ahead into a register ring (each thread holds 1/256 of every
-// in-flight A_s) and shared through LDS one step at a time.
+// Cross-lane moves within 8-lane groups (DPP): lane l reads lane 7 - l of its group of 8,
+// 3 - l of its quad, or l ^ 1.
+__device__ __forceinline__ float dpp_half_mirror(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x141, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float dpp_quad_rev(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x1B, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float dpp_quad_swap(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
+}
+
+// Inter-segment recurrence H_in(s+1) = A_s H_in(s) + B_s (float32); one workgroup per
+// (pair, 4 state columns c0 ..).  Thread t takes state rows i0 = 2 (t / 8), i0 + 1 and the
+// contraction slice k = 8 q .. 8 q + 7 (q = t % 8): it keeps those 16 entries of A_s in
+// registers (loaded DEPTH steps ahead, so a step never waits on memory), reads rows
+// 8 q .. 8 q + 7 of the four H_in(s) columns from LDS (skewed so the eight slices of a
+// wave hit distinct banks) and forms 2 x 4 partial sums; three DPP exchange rounds within
+// the 8 lanes of the row pair leave lane q with H_in(s+1)[i0 + q / 4][c0 + q % 4].  One
+// barrier per step.
 template <int DK, int DV>
 __global__ __launch_bounds__(256) void seg_scan_fast_kernel(FwdArgs a) {
-  constexpr int JW = 256 / DK;
+  static_assert(DK == 64, "the row-pair / k-slice split assumes 64 state rows");
   constexpr int DEPTH = 8;
-  constexpr int LDA = DK + 4;                  // padded row stride of the staged operator
-  constexpr int PIECES = DK * DK / 4 / 256;    // float4 pieces of A_s per thread
-  static_assert(PIECES >= 1, "operator must cover the workgroup");
-  __shared__ __align__(16) float sA[DK * LDA];
-  // column j of H at row stride DK + 4: the JW columns read together fall in different banks
-  __shared__ __align__(16) float sH[2][JW][DK + 4];
-  __shared__ __align__(16) float sBs[DK * 4];
-  static_assert(JW == 4, "the B_s slice is staged as one float4 per row");
-  const int tid = threadIdx.x, pr = blockIdx.x, c0 = JW * blockIdx.y;
-  const int i = tid / JW, j = tid % JW;
+  constexpr int HS = DK + DK / 8;  // H rows with a one-row skew every 8 rows
+  __shared__ __align__(16) float4 sH[2][HS];
+  const int tid = threadIdx.x, i0 = 2 * (tid >> 3), q = tid & 7;
+  const int pr = blockIdx.x, c0 = 4 * blockIdx.y;
   const int nseg = a.nseg;
-  const float* A0 = a.Aagg + (size_t)pr * nseg * DK * DK;
-  const float* B0 = a.Bagg + (size_t)pr * nseg * DK * DV;
-  float* H0 = a.Hin + (size_t)pr * nseg * DK * DV;
-  // Ring slot d (d = 0..7) holds the operator of the next step s with s % 8 == d,
-  // in named registers R<d>_<p>: four float4 pieces of A_s and one float4 of the
-  // B_s slice (rows tid % DK, columns c0..c0+3) per thread; the
-  // loop is unrolled eight times so each slot is read eight steps after its
-  // loads were issued.
-  static_assert(PIECES == 4, "the register ring is written for 4 pieces per thread");
+  const int orow = i0 + (q >> 2), ocol = c0 + (q & 3);  // the output this lane ends with
+  const float* A0 = a.Aagg + (size_t)pr * nseg * DK * DK + (size_t)i0 * DK + 8 * q;
+  const float* B0 = a.Bagg + (size_t)pr * nseg * DK * DV + (size_t)orow * DV + ocol;
+  // H_in(s) for the output correction: bfloat16, transposed ([column][row], the layout
+  // of its MFMA B operand)
+  bf16_t* H0 = reinterpret_cast<bf16_t*>(a.Hin) + (size_t)pr * nseg * DK * DV + (size_t)ocol * DK + orow;
+  auto hrow = [](int r) { return r + (r >> 3); };
+  // ring slot D: the operands of the next step s with s % DEPTH == D (rows i0, i0 + 1 of
+  // A_s over the slice, and this lane's entry of B_s)
+#define PRISM_DECL(D) float4 R##D##_0, R##D##_1, R##D##_2, R##D##_3; float R##D##_b;
 #define PRISM_FETCH(D, S)                                                                     \
   {                                                                                           \
-    const int sn_ = (S) < nseg ? (S) : nseg - 1;                                              \
-    const float4* src_ = reinterpret_cast<const float4*>(A0 + (size_t)sn_ * DK * DK) + tid;   \
+    const size_t sn_ = (size_t)((S) < nseg ? (S) : nseg - 1);                                 \
+    const float4* src_ = reinterpret_cast<const float4*>(A0 + sn_ * DK * DK);                \
     R##D##_0 = src_[0];                                                                       \
-    R##D##_1 = src_[256];                                                                     \
-    R##D##_2 = src_[512];                                                                     \
-    R##D##_3 = src_[768];                                                                     \
-    R##D##_4 = reinterpret_cast<const float4*>(B0 + (size_t)sn_ * DK * DV +                  \
-                                               (size_t)(tid % DK) * DV + c0)[0];              \
+    R##D##_1 = src_[1];                                                                       \
+    R##D##_2 = src_[DK / 4];                                                                  \
+    R##D##_3 = src_[DK / 4 + 1];                                                              \
+    R##D##_b = B0[sn_ * DK * DV];                                                             \
   }
-#define PRISM_DECL(D) float4 R##D##_0, R##D##_1, R##D##_2, R##D##_3, R##D##_4;
   PRISM_DECL(0) PRISM_DECL(1) PRISM_DECL(2) PRISM_DECL(3)
   PRISM_DECL(4) PRISM_DECL(5) PRISM_DECL(6) PRISM_DECL(7)
   PRISM_FETCH(0, 0) PRISM_FETCH(1, 1) PRISM_FETCH(2, 2) PRISM_FETCH(3, 3)
   PRISM_FETCH(4, 4) PRISM_FETCH(5, 5) PRISM_FETCH(6, 6) PRISM_FETCH(7, 7)
-  sH[0][j][i] = 0.f;
+  float h = 0.f;  // H_in(s)[orow][ocol]
+  if (tid < DK) sH[0][hrow(tid)] = make_float4(0.f, 0.f, 0.f, 0.f);
+  __syncthreads();
+  const bool lo4 = q < 4, lo2 = (q & 2) == 0, lo1 = (q & 1) == 0;
   int cur = 0;
-  const int e0 = 4 * tid;  // element index of piece 0; piece p adds 1024 p
-#define PRISM_SCAN_STEP(D)                                                                    \
-  if (s0 + (D) < nseg) {                                                                      \
+#define PRISM_SCAN_STEP(D, PREFETCH)                                                          \
+  {                                                                                           \
     const int s = s0 + (D);                                                                   \
-    *reinterpret_cast<float4*>(&sA[((e0) / DK) * LDA + (e0) % DK]) = R##D##_0;                \
-    *reinterpret_cast<float4*>(&sA[((e0 + 1024) / DK) * LDA + (e0) % DK]) = R##D##_1;         \
-    *reinterpret_cast<float4*>(&sA[((e0 + 2048) / DK) * LDA + (e0) % DK]) = R##D##_2;         \
-    *reinterpret_cast<float4*>(&sA[((e0 + 3072) / DK) * LDA + (e0) % DK]) = R##D##_3;         \
-    if (tid < DK) *reinterpret_cast<float4*>(&sBs[tid * 4]) = R##D##_4;                       \
-    PRISM_FETCH(D, s + 8)                                                                     \
-    __syncthreads();                                                                          \
-    H0[(size_t)s * DK * DV + (size_t)i * DV + c0 + j] = sH[cur][j][i];                        \
-    float acc0 = sBs[i * 4 + j], acc1 = 0.f, acc2 = 0.f, acc3 = 0.f;                          \
-    const float4* arow = reinterpret_cast<const float4*>(&sA[i * LDA]);                       \
-    const float4* hcol = reinterpret_cast<const float4*>(&sH[cur][j][0]);                     \
-    _Pragma("unroll") for (int q = 0; q < DK / 4; ++q) {                                      \
-      const float4 av = arow[q], hv = hcol[q];                                                \
-      acc0 += av.x * hv.x;                                                                    \
-      acc1 += av.y * hv.y;                                                                    \
-      acc2 += av.z * hv.z;                                                                    \
-      acc3 += av.w * hv.w;                                                                    \
+    H0[(size_t)s * DK * DV] = (bf16_t)h;                                                      \
+    const float ar0[8] = {R##D##_0.x, R##D##_0.y, R##D##_0.z, R##D##_0.w,                     \
+                          R##D##_1.x, R##D##_1.y, R##D##_1.z, R##D##_1.w};                    \
+    const float ar1[8] = {R##D##_2.x, R##D##_2.y, R##D##_2.z, R##D##_2.w,                     \
+                          R##D##_3.x, R##D##_3.y, R##D##_3.z, R##D##_3.w};                    \
+    const float bv = R##D##_b;                                                                \
+    if (PREFETCH) PRISM_FETCH(D, s + DEPTH)                                                   \
+    float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}; /* [row][col] */                   \
+    _Pragma("unroll") for (int m = 0; m < 8; ++m) {                                           \
+      const float4 hv = sH[cur][hrow(8 * q + m)];                                             \
+      v[0] += ar0[m] * hv.x;                                                                  \
+      v[1] += ar0[m] * hv.y;                                                                  \
+      v[2] += ar0[m] * hv.z;                                                                  \
+      v[3] += ar0[m] * hv.w;                                                                  \
+      v[4] += ar1[m] * hv.x;                                                                  \
+      v[5] += ar1[m] * hv.y;                                                                  \
+      v[6] += ar1[m] * hv.z;                                                                  \
+      v[7] += ar1[m] * hv.w;                                                                  \
     }                                                                                         \
-    sH[cur ^ 1][j][i] = (acc0 + acc1) + (acc2 + acc3);                                        \
+    /* keep row q / 4, then columns (q & 2) .., then column q & 3 */                          \
+    float n4[4], n2[2];                                                                       \
+    _Pragma("unroll") for (int j = 0; j < 4; ++j)                                             \
+      n4[j] = (lo4 ? v[j] : v[4 + j]) + dpp_half_mirror(lo4 ? v[4 + j] : v[j]);               \
+    _Pragma("unroll") for (int j = 0; j < 2; ++j)                                             \
+      n2[j] = (lo2 ? n4[j] : n4[2 + j]) + dpp_quad_rev(lo2 ? n4[2 + j] : n4[j]);              \
+    h = (lo1 ? n2[0] : n2[1]) + dpp_quad_swap(lo1 ? n2[1] : n2[0]) + bv;                       \
+    reinterpret_cast<float*>(&sH[cur ^ 1][hrow(orow)])[q & 3] = h;                            \
     cur ^= 1;                                                                                 \
     __syncthreads();                                                                          \
   }
-  static_assert(DEPTH == 8, "the step list below has eight ring slots");
-  for (int s0 = 0; s0 < nseg; s0 += DEPTH) {
-    PRISM_SCAN_STEP(0) PRISM_SCAN_STEP(1) PRISM_SCAN_STEP(2) PRISM_SCAN_STEP(3)
-    PRISM_SCAN_STEP(4) PRISM_SCAN_STEP(5) PRISM_SCAN_STEP(6) PRISM_SCAN_STEP(7)
+  // full blocks of DEPTH steps: every step consumes its ring slot and refills it
+  // unconditionally, so each slot is loaded straight into its own registers
+  int s0 = 0;
+  for (; s0 + DEPTH <= nseg; s0 += DEPTH) {
+    PRISM_SCAN_STEP(0, true) PRISM_SCAN_STEP(1, true) PRISM_SCAN_STEP(2, true) PRISM_SCAN_STEP(3, true)
+    PRISM_SCAN_STEP(4, true) PRISM_SCAN_STEP(5, true) PRISM_SCAN_STEP(6, true) PRISM_SCAN_STEP(7, true)
   }
+  // the last nseg % DEPTH steps: their operands are already in the ring
+  if (s0 + 0 < nseg) PRISM_SCAN_STEP(0, false)
+  if (s0 + 1 < nseg) PRISM_SCAN_STEP(1, false)
+  if (s0 + 2 < nseg) PRISM_SCAN_STEP(2, false)
+  if (s0 + 3 < nseg) PRISM_SCAN_STEP(3, false)
+  if (s0 + 4 < nseg) PRISM_SCAN_STEP(4, false)
+  if (s0 + 5 < nseg) PRISM_SCAN_STEP(5, false)
+  if (s0 + 6 < nseg) PRISM_SCAN_STEP(6, false)
 #undef PRISM_SCAN_STEP
 #undef PRISM_FETCH
 #undef PRISM_DECL
-  a.S_final[(size_t)pr * DK * DV + (size_t)i * DV + c0 + j] = sH[cur][j][i];
+  a.S_final[(size_t)pr * DK * DV + (size_t)orow * DV + ocol] = h;
 }
 
-// o = O_loc + Qhat H_in(segment) with MFMA; one workgroup per chunk, wave w owns
-// token rows 16w.., output staged in LDS for 16-byte stores.
+// Output correction o = O_loc + Qhat H_in(segment) with MFMA; one workgroup per segment
+// (4 waves), wave w takes token rows 16 w .. of every chunk of the segment.  Each wave
+// holds its B operand, H_in(segment) transposed in bfloat16, in registers for the whole
+// segment and streams the chunks: O_loc and Qhat come in the sweep's fragment order (one
+// contiguous 8- or 16-byte load per lane and tile), the next chunk's fragments are loaded
+// while the current one is finished, and the 16 x 64 output block is staged in the
+// wave's own LDS rows for 16-byte row stores (no workgroup barrier).
 template <int D, int C>
 __global__ __launch_bounds__(256) void seg_fixup_fast_kernel(FwdArgs a) {
+  static_assert(D == 64 && C == 64, "fragment order written for 64 x 64 chunks");
   constexpr int LD = D + 8;
-  __shared__ __align__(16) bf16_t sHt[D * LD];
-  __shared__ __align__(16) bf16_t sO[C * LD];
-  const int tid = threadIdx.x, w = wave_id(), l = lane_id(), g4 = (l >> 4) * 4, li = l & 15;
-  const int c = blockIdx.x, pr = blockIdx.y;
-  const int seg = c / a.seg_chunks;
-  const int t0 = c * C, nvalid = min(C, a.T - t0);
-  const int Tpad = a.nch * C;
-  const float* Hi = a.Hin + ((size_t)pr * a.nseg + seg) * D * D;
-  for (int idx = tid; idx < D * D; idx += 256) {
-    const int kk = idx / D, jj = idx % D;
-    sHt[jj * LD + kk] = (bf16_t)Hi[idx];
-  }
-  __syncthreads();
-  const bf16_t* qh = reinterpret_cast<const bf16_t*>(a.Qhat) + ((size_t)pr * Tpad + t0 + 16 * w) * D;
-  const float* ol = a.Oloc + ((size_t)pr * Tpad + t0 + 16 * w) * D;
-  bf16x8 af[D / 32];
+  __shared__ __align__(16) bf16_t sO[4][16 * LD];
+  const int w = wave_id(), l = lane_id(), g4 = (l >> 4) * 4, li = l & 15;
+  const int seg = blockIdx.x, pr = blockIdx.y;
+  const int c_begin = seg * a.seg_chunks, c_end = min(a.nch, c_begin + a.seg_chunks);
+  const bf16_t* hin = reinterpret_cast<const bf16_t*>(a.Hin) + ((size_t)pr * a.nseg + seg) * D * D;
+  bf16x8 hb[4][2];
 #pragma unroll
-  for (int kb = 0; kb < D / 32; ++kb) {
-    const bf16_t* ar = qh + (size_t)li * D + 32 * kb + g4;
-    af[kb] = cat8(*reinterpret_cast<const bf16x4*>(ar), *reinterpret_cast<const bf16x4*>(ar + 16));
-  }
+  for (int vt = 0; vt < 4; ++vt)
 #pragma unroll
-  for (int vt = 0; vt < D / 16; ++vt) {
-    f32x4 acc;
+    for (int kb = 0; kb < 2; ++kb) hb[vt][kb] = frag8(hin, D, 16 * vt, 32 * kb);
+  const size_t gc0 = (size_t)pr * a.nch;
+  const bf16_t* qbase = reinterpret_cast<const bf16_t*>(a.Qhat) + (size_t)w * 1024 + l * 8;
+  const bf16_t* obase = reinterpret_cast<const bf16_t*>(a.Oloc) + (size_t)w * 1024 + l * 4;
+  bf16_t* so = sO[w];
+  const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
+      reinterpret_cast<bf16_t*>(a.o) + (size_t)pr * a.T * D, (short)0, a.T * D * 2, 0x00020000);
+  bf16x8 qf[2];
+  bf16x4 of[4];
+  auto fetch = [&](int c) {
+    const size_t off = (gc0 + c) * 4096;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) acc[r] = ol[(size_t)(g4 + r) * D + 16 * vt + li];
+    for (int kb = 0; kb < 2; ++kb) qf[kb] = *reinterpret_cast<const bf16x8*>(qbase + off + kb * 512);
 #pragma unroll
-    for (int kb = 0; kb < D / 32; ++kb) {
-      const bf16_t* br = sHt + (16 * vt + li) * LD + 32 * kb + g4;
-      const bf16x8 bf = cat8(*reinterpret_cast<const bf16x4*>(br), *reinterpret_cast<const bf16x4*>(br + 16));
-      acc = mfma(af[kb], bf, acc);
+    for (int vt = 0; vt < 4; ++vt) of[vt] = *reinterpret_cast<const bf16x4*>(obase + off + vt * 256);
+  };
+  if (c_begin < c_end) fetch(c_begin);
+  for (int c = c_begin; c < c_end; ++c) {
+    f32x4 acc[4];
+    bf16x8 qa[2] = {qf[0], qf[1]};
+#pragma unroll
+    for (int vt = 0; vt < 4; ++vt) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[vt][r] = (float)of[vt][r];
     }
+    fetch(c + 1 < c_end ? c + 1 : c);  // unconditional: the wait for it stays exact
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sO[(16 * w + g4 + r) * LD + 16 * vt + li] = (bf16_t)acc[r];
-  }
-  __syncthreads();
-  bf16_t* o = reinterpret_cast<bf16_t*>(a.o) + ((size_t)pr * a.T + t0) * D;
-  constexpr int PER_ROW = D / 8;
-  for (int idx = tid; idx < nvalid * PER_ROW; idx += 256) {
-    const int row = idx / PER_ROW, cv = (idx % PER_ROW) * 8;
-    *reinterpret_cast<uint4*>(o + (size_t)row * D + cv) = *reinterpret_cast<const uint4*>(sO + row * LD + cv);
+    for (int vt = 0; vt < 4; ++vt) {
+      acc[vt] = mfma(qa[0], hb[vt][0], acc[vt]);
+      acc[vt] = mfma(qa[1], hb[vt][1], acc[vt]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) so[(g4 + r) * LD + 16 * vt + li] = (bf16_t)acc[vt][r];
+    }
+    __builtin_amdgcn_wave_barrier();  // the wave's LDS writes land before its reads (in order)
+    // rows t0 + 16 w .. of the output, 8 lanes per 128-byte row; rows past the sequence
+    // end fall outside the pair's buffer and are dropped by the store
+    const int t0 = c * C + 16 * w;
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int row = 8 * it + (l >> 3), cv = (l & 7) * 8;
+      const uint4 x = *reinterpret_cast<const uint4*>(so + row * LD + cv);
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned, x), orsrc,
+                                            ((t0 + row) * D + cv) * 2, 0, 0);
+    }
+    __builtin_amdgcn_wave_barrier();  // reads done before the next chunk's writes
   }
 }
 

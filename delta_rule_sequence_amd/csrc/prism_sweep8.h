@@ -58,15 +58,6 @@ struct Sweep8Lds {
   static_assert(total <= 160 * 1024, "LDS plan exceeds the 160 KB of a CU");
 };
 
-// 8 bf16 of a 32-deep MFMA operand from row (r0 + lane%16) of a row-major LDS array:
-// slots 0-3 are k0 + 4g .. +3 and slots 4-7 are k0 + 16 + 4g .. +3 (g = lane/16).  The
-// same read is the A operand (rows = output rows) and the B operand of a [n][k] array.
-__device__ __forceinline__ bf16x8 frag8(const bf16_t* X, int ld, int r0, int k0) {
-  const int l = lane_id();
-  const bf16_t* p = X + (r0 + (l & 15)) * ld + k0 + 4 * (l >> 4);
-  return cat8(*reinterpret_cast<const bf16x4*>(p), *reinterpret_cast<const bf16x4*>(p + 16));
-}
-
 // Two accumulator tiles (rows k0.. and k0+16.. of the contraction) as a 32-deep B
 // operand, each element scaled by s[k].
 __device__ __forceinline__ bf16x8 scaled_pair(const f32x4& t0, const f32x4& t1, const float* s, int k0) {
@@ -160,7 +151,7 @@ struct Sweep8Ctx {
   rsrc_t rq_, rk_, rv_, ru_, rg_;  // buffers over the pair's q, k, v, u, gamma
   const float *gg, *bb, *al;       // the pair's g, beta, alpha
   float *oloc, *qhat_base, *agg;   // outputs of this pair / segment
-  int T, L, Lm1, c_begin, c_end, Tpad, pr;
+  int T, L, Lm1, c_begin, c_end, Tpad, pr, nch;
   int ubytes;                      // bytes per token row of u / gamma
 };
 
@@ -645,12 +636,16 @@ __device__ __forceinline__ void sweep8_qwave(const Sweep8Ctx& x, int wq) {
           for (int r = 0; r < 4; ++r) Qt[kt][r] = Gi * (float)qv[r] - pw[r];
         }
         const bf16x8 q0 = pair8(Qt[0], Qt[1]), q1 = pair8(Qt[2], Qt[3]);
-        bf16_t* qh = reinterpret_cast<bf16_t*>(x.qhat_base) + (size_t)(t0 + 16 * rb + li) * 64;
+        // lane (li, g) holds Qhat[16 rb + li][16 kt + 4 g + r]: tiles 2 kb and 2 kb + 1 are
+        // exactly its 32-deep A operand for k block kb
+        bf16_t* qf = reinterpret_cast<bf16_t*>(x.qhat_base) + ((size_t)c * 4 + rb) * 1024 + l * 8;
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-          f32x4 acc = mfma(frag8(V.sAt, LD, 16 * kt, 0), q0, zero4());
-          acc = mfma(frag8(V.sAt, LD, 16 * kt, 32), q1, acc);
-          *reinterpret_cast<bf16x4*>(qh + 16 * kt + g4) = to_bf16x4(acc);
+        for (int kb = 0; kb < 2; ++kb) {
+          f32x4 e0 = mfma(frag8(V.sAt, LD, 32 * kb, 0), q0, zero4());
+          e0 = mfma(frag8(V.sAt, LD, 32 * kb, 32), q1, e0);
+          f32x4 e1 = mfma(frag8(V.sAt, LD, 32 * kb + 16, 0), q0, zero4());
+          e1 = mfma(frag8(V.sAt, LD, 32 * kb + 16, 32), q1, e1);
+          *reinterpret_cast<bf16x8*>(qf + kb * 512) = pair8(e0, e1);
         }
       }
       if (lv + 1 <= Lm1) {  // R_{lv+1} into the other slot, then fetch gamma_{lv+1}
@@ -696,13 +691,12 @@ __device__ __forceinline__ void sweep8_qwave(const Sweep8Ctx& x, int wq) {
 
     // ---- P_O: O += P E, write O_loc; next chunk's V^T and residual ------------------------------
     {
-      float* oloc = x.oloc + (size_t)(t0 + 16 * rb) * 64;
+      bf16_t* of = reinterpret_cast<bf16_t*>(x.oloc) + ((size_t)c * 4 + rb) * 1024 + l * 4;
 #pragma unroll
       for (int vt = 0; vt < 4; ++vt) {
         O[vt] = mfma(Pa[0], frag8(V.sEt, LD, 16 * vt, 0), O[vt]);
         if (rb >= 2) O[vt] = mfma(Pa[1], frag8(V.sEt, LD, 16 * vt, 32), O[vt]);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) oloc[(size_t)(g4 + r) * 64 + 16 * vt + li] = O[vt][r];
+        *reinterpret_cast<bf16x4*>(of + vt * 256) = to_bf16x4(O[vt]);
       }
     }
     if (c + 1 < x.c_end) store_chunk();
@@ -733,6 +727,7 @@ __global__ __launch_bounds__(512, 1) void seg_sweep8_kernel(FwdArgs a) {
   x.c_end = min(a.nch, x.c_begin + a.seg_chunks);
   x.Tpad = a.nch * C;
   x.pr = pr;
+  x.nch = a.nch;
   x.ubytes = (L > 1 ? Lm1 : 1) * D * 2;
   const size_t pair_rows = (size_t)pr * T;
   const unsigned vbytes = (unsigned)T * D * 2;
@@ -746,8 +741,11 @@ __global__ __launch_bounds__(512, 1) void seg_sweep8_kernel(FwdArgs a) {
   x.gg = a.g + pair_rows;
   x.bb = a.beta + pair_rows;
   x.al = L > 1 ? a.alpha + pair_rows * L : nullptr;
-  x.oloc = a.Oloc + (size_t)pr * x.Tpad * D;
-  x.qhat_base = reinterpret_cast<float*>(reinterpret_cast<bf16_t*>(a.Qhat) + (size_t)pr * x.Tpad * D);
+  // O_loc and Qhat in fragment order: per chunk and token row block, the lanes' MFMA
+  // tiles back to back (O_loc: 4 value tiles of 64 lanes x 4; Qhat: 2 k blocks of
+  // 64 lanes x 8), bfloat16
+  x.oloc = reinterpret_cast<float*>(reinterpret_cast<bf16_t*>(a.Oloc) + (size_t)pr * a.nch * 4096);
+  x.qhat_base = reinterpret_cast<float*>(reinterpret_cast<bf16_t*>(a.Qhat) + (size_t)pr * a.nch * 4096);
   x.agg = (w < 4 ? a.Bagg : a.Aagg) + ((size_t)pr * a.nseg + seg) * D * D;
 
   // conv taps, H^T = 0, A_acc^T = I
