@@ -10,11 +10,11 @@
 //     runs two waves and one wave's MFMA / LDS latency hides behind the other;
 //   * waves 0-3 ("K waves") own the key side of the chunk: the masked Gram
 //     tiles K K^T and K U_l^T of token rows 16 (3 - w)..; the corrected values
-//     V'; the per-column work Uc = M^-1 beta V', E = Uc - Wc H and the state
+//     V'; the per-column work Wc = M^-1 diag(beta G) K, Uc = M^-1 beta V', E = Uc - Wc H and the state
 //     update of H (columns 16 w..); the rank-L state term sum_l U_l^T D R_l;
 //   * waves 4-7 ("Q waves") own the query side: the masked Gram tiles Q K^T and
 //     Q U_l^T of token rows 16 (w - 4)..; the chunk output; the inverse M^-1
-//     (column block w - 4), Wc = M^-1 diag(beta G) K, the segment operator
+//     (column block w - 4), the segment operator
 //     A_acc and Qhat; they also run the residual chain of the rank-L values;
 //   * a K wave and a Q wave on one SIMD take row blocks r and 3 - r, so the
 //     triangular Gram work is the same on every SIMD;
@@ -379,7 +379,22 @@ __device__ __forceinline__ void sweep8_kwave(const Sweep8Ctx& x, int wq) {
           HB[kt] = mfma(frag8(sUt, LD, 16 * kt, 32), rd1, HB[kt]);
         }
       }
-      if (lv == 3) {  // WH = Wc H(:, cb), Wc from the Q waves' phase 2
+      if (lv == 2) {
+        // Wc(:, cb) = (I + M)^-1 diag(beta G) K(:, cb), row-major and transposed (the
+        // inverse's column blocks come from the Q waves' phase 1)
+        const bf16x8 k0 = scaled_frag8(V.sKt, LD, 16 * cb, 0, V.sBG);
+        const bf16x8 k1 = scaled_frag8(V.sKt, LD, 16 * cb, 32, V.sBG);
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+          f32x4 acc = mfma(frag8(V.sMinv, LD, 16 * it, 0), k0, zero4());
+          if (it >= 2) acc = mfma(frag8(V.sMinv, LD, 16 * it, 32), k1, acc);
+          const bf16x4 xv = to_bf16x4(acc);  // Wc[16 it + g4 + r][16 cb + li]
+          *reinterpret_cast<bf16x4*>(V.sWct + (16 * cb + li) * LD + 16 * it + g4) = xv;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) V.sWc[(16 * it + g4 + r) * LD + 16 * cb + li] = xv[r];
+        }
+      }
+      if (lv == 3) {  // WH = Wc H(:, cb), Wc from phase 2
         const bf16x8 h0 = pair8(H[0], H[1]), h1 = pair8(H[2], H[3]);
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
@@ -556,7 +571,7 @@ __device__ __forceinline__ void sweep8_qwave(const Sweep8Ctx& x, int wq) {
     if (Lm1 >= 2) quad_fetch<4>(lpf, x.rg_, (t0 + 4 * rq) * x.ubytes + 128 + 2 * c4, x.ubytes);  // gamma_1
     __syncthreads();  // B1
 
-    // ---- P1 .. P_NL: rank-L steps; M^-1 (P1), Wc (P2), WA and Qhat (P3) -------------------------
+    // ---- P1 .. P_NL: rank-L steps; M^-1 (P1), WA and Qhat (P3) -------------------------------
     auto level_phase = [&](const int lv) {
       const int s = (lv - 1) & 1;
       if (lv <= Lm1) {  // O += lower(Gam * Q U_l^T) R_l
@@ -602,19 +617,6 @@ __device__ __forceinline__ void sweep8_qwave(const Sweep8Ctx& x, int wq) {
           const bf16x4 xv = to_bf16x4(X[i]);
 #pragma unroll
           for (int r = 0; r < 4; ++r) V.sMinv[(16 * i + g4 + r) * LD + 16 * cb + li] = xv[r];
-        }
-      } else if (lv == 2) {
-        // Wc(:, cb) = (I + M)^-1 diag(beta G) K(:, cb), row-major and transposed
-        const bf16x8 k0 = scaled_frag8(V.sKt, LD, 16 * cb, 0, V.sBG);
-        const bf16x8 k1 = scaled_frag8(V.sKt, LD, 16 * cb, 32, V.sBG);
-#pragma unroll
-        for (int it = 0; it < 4; ++it) {
-          f32x4 acc = mfma(frag8(V.sMinv, LD, 16 * it, 0), k0, zero4());
-          if (it >= 2) acc = mfma(frag8(V.sMinv, LD, 16 * it, 32), k1, acc);
-          const bf16x4 xv = to_bf16x4(acc);  // Wc[16 it + g4 + r][16 cb + li]
-          *reinterpret_cast<bf16x4*>(V.sWct + (16 * cb + li) * LD + 16 * it + g4) = xv;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) V.sWc[(16 * it + g4 + r) * LD + 16 * cb + li] = xv[r];
         }
       } else if (lv == 3) {
         // WA = Wc A_acc(:, cb)
