@@ -118,7 +118,6 @@ __global__ __launch_bounds__(256) void seg_scan_fast_kernel(FwdArgs a) {
     const float ar1[8] = {R##D##_2.x, R##D##_2.y, R##D##_2.z, R##D##_2.w,                     \
                           R##D##_3.x, R##D##_3.y, R##D##_3.z, R##D##_3.w};                    \
     const float bv = R##D##_b;                                                                \
-    if (PREFETCH) PRISM_FETCH(D, s + DEPTH)                                                   \
     float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}; /* [row][col] */                   \
     _Pragma("unroll") for (int m = 0; m < 8; ++m) {                                           \
       const float4 hv = sH[cur][hrow(8 * q + m)];                                             \
@@ -131,6 +130,8 @@ __global__ __launch_bounds__(256) void seg_scan_fast_kernel(FwdArgs a) {
       v[6] += ar1[m] * hv.z;                                                                  \
       v[7] += ar1[m] * hv.w;                                                                  \
     }                                                                                         \
+    /* refill the slot after the products: the loads queue while the exchanges run */         \
+    if (PREFETCH) PRISM_FETCH(D, s + DEPTH)                                                   \
     /* keep row q / 4, then columns (q & 2) .., then column q & 3 */                          \
     float n4[4], n2[2];                                                                       \
     _Pragma("unroll") for (int j = 0; j < 4; ++j)                                             \
