@@ -190,6 +190,21 @@ struct Sweep8View {
   __device__ __forceinline__ bf16_t* slotRt(int s) const { return slotU(s) + 2 * 64 * Sweep8Lds::LD; }
 };
 
+// Inclusive prefix sum over the 64 lanes of a wave: shifts by 1, 2, 4, 8 within each row
+// of 16 lanes, then row 15's total into the next row and row 31's into rows 2 and 3 (DPP).
+__device__ __forceinline__ float wave_inclusive_sum(float x) {
+#define PRISM_ADD_DPP(CTRL, ROWS)                                                              \
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, ROWS, 0xF, true));
+  PRISM_ADD_DPP(0x111, 0xF)  // row_shr:1
+  PRISM_ADD_DPP(0x112, 0xF)  // row_shr:2
+  PRISM_ADD_DPP(0x114, 0xF)  // row_shr:4
+  PRISM_ADD_DPP(0x118, 0xF)  // row_shr:8
+  PRISM_ADD_DPP(0x142, 0xA)  // row_bcast:15 into rows 1 and 3
+  PRISM_ADD_DPP(0x143, 0xC)  // row_bcast:31 into rows 2 and 3
+#undef PRISM_ADD_DPP
+  return x;
+}
+
 // Decay factors of the Gram tiles of token row block rb: lane (li, g) of tile jt holds
 // Gam(i, j) = exp(b_i - b_j) for i = 16 rb + li, j = 16 jt + 4g + r, zero where j > i
 // (or j >= i when strict) and for tiles above the diagonal.
@@ -246,7 +261,7 @@ __device__ __forceinline__ void sweep8_kwave(const Sweep8Ctx& x, int wq) {
   f32x4 H[4], Vp[4], HB[4], WH[4];
   float dec[4][4];
   uint2 pf[12], lpf[4];
-  float glg = 0.f, gbe = 0.f, gal[8];
+  float glg = 1.f, gbe = 0.f, gal[8];  // wave 0: next chunk's gates for token t0 + lane
 #pragma unroll
   for (int kt = 0; kt < 4; ++kt) H[kt] = zero4();
 #pragma unroll
@@ -258,7 +273,7 @@ __device__ __forceinline__ void sweep8_kwave(const Sweep8Ctx& x, int wq) {
     quad_fetch<4>(pf + 0, x.rq_, o, 128);
     quad_fetch<4>(pf + 4, x.rk_, o, 128);
     if (L > 1) quad_fetch<4>(pf + 8, x.ru_, (t0 + 4 * rq) * x.ubytes + 2 * c4, x.ubytes);
-    if (wq == 0) {  // gates of token t0 + lane
+    if (wq == 0) {
       const int hi = min(x.T, t0 + C);
       const int tl = t0 + l < hi ? t0 + l : 0;
       glg = x.gg[tl];
@@ -275,14 +290,9 @@ __device__ __forceinline__ void sweep8_kwave(const Sweep8Ctx& x, int wq) {
     if (L > 1) quad_store(pf + 8, V.slotU(0), V.slotUt(0), rq, c4);
     if (wq == 0) {  // b = cumsum(log g) over the chunk, G = exp(b), D = exp(b_last - b)
       const int t0 = c * C, hi = min(x.T, t0 + C);
-      const bool ok = t0 + l < hi;
-      float lam = ok ? __logf(glg) : 0.f;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const float y = __shfl_up(lam, off);
-        if (l >= off) lam += y;
-      }
-      const float blast = __shfl(lam, C - 1);
+      const bool ok = t0 + l < hi;  // tokens past the end: g = 1, beta = alpha = 0
+      const float lam = wave_inclusive_sum(ok ? __logf(glg) : 0.f);
+      const float blast = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lam), C - 1));
       const float G = __expf(lam);
       V.sB[l] = lam;
       V.sG[l] = G;
@@ -304,6 +314,8 @@ __device__ __forceinline__ void sweep8_kwave(const Sweep8Ctx& x, int wq) {
     __syncthreads();  // B0: the chunk's inputs, gates and H^T are in LDS
 
     // ---- P0: M[i][j] = beta_i Gam_ij K_i.K_j (j < i) rows rb; diagonal inverse block --
+    const int cn = c + 1 < x.c_end ? c + 1 : c;  // next chunk (this one again at the end:
+                                                  // unconditional loads keep waits exact)
     decay_factors(dec, V.sB, rb, true);
     {
       f32x4 mraw[4];
@@ -409,7 +421,7 @@ __device__ __forceinline__ void sweep8_kwave(const Sweep8Ctx& x, int wq) {
       }
       // next chunk's inputs, issued once this chunk's last rank-L prefetch is consumed (the
       // wait for a prefetched operand may cover every load issued before it)
-      if (lv == (Lm1 >= 2 ? Lm1 - 1 : 1) && c + 1 < x.c_end) fetch_chunk(c + 1);
+      if (lv == (Lm1 >= 2 ? Lm1 - 1 : 1)) fetch_chunk(cn);
       if (lv == NL) {  // (beta V')^T rows rb for the per-column solve
         const float4 be = *reinterpret_cast<const float4*>(V.sBeta + 16 * rb + g4);
 #pragma unroll
@@ -501,20 +513,23 @@ __device__ __forceinline__ void sweep8_qwave(const Sweep8Ctx& x, int wq) {
     quad_fetch<4>(pf + 4, x.rv_, (t0 + 4 * rq) * 128 + 2 * c4, 128);
     if (L > 1) quad_fetch<4>(pf + 8, x.rg_, (t0 + 4 * rq) * x.ubytes + 2 * c4, x.ubytes);  // gamma_0
   };
-  // V^T into LDS and the residual r_0 = v - anchor of the block (anchor_t = sum_j w_j v_{t-3+j})
+  // V^T into LDS (the v rows stay in registers for the anchor)
   auto store_chunk = [&]() {
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
+      const bf16x4 col = {__builtin_bit_cast(bf16x4, pf[4])[cc], __builtin_bit_cast(bf16x4, pf[5])[cc],
+                          __builtin_bit_cast(bf16x4, pf[6])[cc], __builtin_bit_cast(bf16x4, pf[7])[cc]};
+      *reinterpret_cast<bf16x4*>(V.sVt + (c4 + cc) * LD + 4 * rq) = col;
+    }
+  };
+  // the residual r_0 = v - anchor of the block (anchor_t = sum_j w_j v_{t-3+j})
+  auto anchor = [&]() {
     float vv[8][4];
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
       const bf16x4 b4 = __builtin_bit_cast(bf16x4, pf[r]);
 #pragma unroll
       for (int cc = 0; cc < 4; ++cc) vv[r][cc] = (float)b4[cc];
-    }
-#pragma unroll
-    for (int cc = 0; cc < 4; ++cc) {
-      const bf16x4 col = {__builtin_bit_cast(bf16x4, pf[4])[cc], __builtin_bit_cast(bf16x4, pf[5])[cc],
-                          __builtin_bit_cast(bf16x4, pf[6])[cc], __builtin_bit_cast(bf16x4, pf[7])[cc]};
-      *reinterpret_cast<bf16x4*>(V.sVt + (c4 + cc) * LD + 4 * rq) = col;
     }
     const float4 w0 = *reinterpret_cast<const float4*>(V.sTaps + c4);
     const float4 w1 = *reinterpret_cast<const float4*>(V.sTaps + 64 + c4);
@@ -560,9 +575,11 @@ __device__ __forceinline__ void sweep8_qwave(const Sweep8Ctx& x, int wq) {
   }
   for (int c = x.c_begin; c < x.c_end; ++c) {
     const int t0 = c * C;
+    const int cn = c + 1 < x.c_end ? c + 1 : c;  // next chunk (unconditional loads)
     __syncthreads();  // B0
 
-    // ---- P0: P = lower(Gam * Q K^T) rows rb (registers); R_1 ---------------------------------
+    // ---- P0: P = lower(Gam * Q K^T) rows rb (registers); r_0 and R_1 ------------------------
+    if (L > 1) anchor();
     decay_factors(dec, V.sB, rb, false);
     gram_rows(Pa, V.sK, V.sQ, rb, dec, 1.f);
 #pragma unroll
@@ -657,7 +674,7 @@ __device__ __forceinline__ void sweep8_qwave(const Sweep8Ctx& x, int wq) {
       }
       // next chunk's inputs, issued once this chunk's last rank-L prefetch is consumed (the
       // wait for a prefetched operand may cover every load issued before it)
-      if (lv == (Lm1 >= 2 ? Lm1 - 1 : 1) && c + 1 < x.c_end) fetch_chunk(c + 1);
+      if (lv == (Lm1 >= 2 ? Lm1 - 1 : 1)) fetch_chunk(cn);
       __syncthreads();
     };
     if constexpr (LM1S >= 0) {
