@@ -32,6 +32,9 @@ def build(verbose: bool = False) -> str:
            "-I", INCLUDE, "-I", CSRC,
            # packed fp32 VALU ops are kept out of every kernel
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           # the latency-bound kernels (scan, sweep phases) gain from the ILP-first
+           # machine scheduler (measured: scan 19.0 -> 17.1 us at the 16K workload)
+           "-mllvm", "-amdgpu-sched-strategy=max-ilp",
            *sources, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
