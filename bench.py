@@ -129,6 +129,70 @@ def cpu_baseline(w, x, budget_s=10.0):
                       f"float64 numpy, one thread, {dt:.1f} s"}
 
 
+_PAIR_DATA = None  # per-pair oracle inputs, inherited by the forked workers
+
+
+def _oracle_pair(p):
+    """Pair p through the oracle in a single-threaded worker process."""
+    import oracle
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=1):
+        oracle.forward_pairs(*_PAIR_DATA[p])
+    return p
+
+
+def cpu_baseline_parallel(w, x, budget_s=5.0):
+    """The oracle with one single-threaded worker per (b, h) pair (P = min(pairs,
+    usable cores, 16) processes), whole passes of the first input set until
+    `budget_s` has elapsed.  Runs before the GPU is touched (workers are forked and
+    inherit the inputs)."""
+    import multiprocessing as mp
+    import numpy as np
+    global _PAIR_DATA
+    usable = len(os.sched_getaffinity(0))
+    procs = max(1, min(w.pairs, usable, 16))
+    P = w.pairs
+
+    def pick(a):
+        return None if a is None else np.asarray(a).reshape((P,) + a.shape[2:])
+
+    conv = np.broadcast_to(np.asarray(x["conv_w"])[None], (w.B, w.H, 4, w.dv)).reshape(P, 4, w.dv)
+    cols = [pick(x["q"]), pick(x["k"]), pick(x["v"]), pick(x["g"]), pick(x["beta"]),
+            pick(x["u"]), pick(x["alpha"]), pick(x["gamma"]), conv]
+    _PAIR_DATA = [tuple(None if a is None else a[p_:p_ + 1] for a in cols) + (w.L,) for p_ in range(P)]
+    tokens, runs = 0, 0
+    with mp.get_context("fork").Pool(procs) as pool:
+        t0 = time.perf_counter()
+        while True:
+            pool.map(_oracle_pair, range(P))
+            tokens += w.B * w.T
+            runs += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        dt = time.perf_counter() - t0
+    _PAIR_DATA = None
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": procs, "kind": "oracle",
+            "cpu_count": os.cpu_count(), "usable_cores": usable,
+            "sample": f"{runs} full pass(es) of {w.name}, one single-threaded process per (b, h) "
+                      f"pair over {procs} processes, {dt:.1f} s"}
+
+
+def copy_bandwidth(torch, mb=1024, reps=10):
+    """Measured device-to-device copy rate (read + write bytes per second)."""
+    n = mb * (1 << 20) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    del a, b
+    return {"value": 2 * n * 4 * reps / dt / 1e9, "unit": "GB/s", "bytes_per_copy": 2 * n * 4}
+
+
 def calibrate_copy(mb):
     import torch
     n = mb * (1 << 20) // 4
@@ -176,10 +240,14 @@ def main():
     print(f"[bench] {w.name}: {nsets} input set(s) of {set_bytes / 1e6:.1f} MB", file=sys.stderr, flush=True)
 
     host_sets, dev_sets = [], []
+    x0 = workloads.generate(w, seed=w.seed)
+    host_sets.append(x0)
+    cpu_par = None
+    if not args.no_cpu_baseline:  # forked workers: before anything touches the GPU
+        print("[bench] timing the oracle on the host (one process per pair)", file=sys.stderr, flush=True)
+        cpu_par = cpu_baseline_parallel(w, x0)
     for i in range(nsets):
-        x = workloads.generate(w, seed=w.seed + 1000 * i)
-        if i == 0:
-            host_sets.append(x)
+        x = x0 if i == 0 else workloads.generate(w, seed=w.seed + 1000 * i)
         dev_sets.append(workloads.to_torch(x, w.dtype, "cuda"))
     vt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     o = torch.empty((w.B, w.H, w.T, w.dv), dtype=vt, device="cuda")
@@ -263,9 +331,11 @@ def main():
                  "instrumented_ms_per_step": span_ms / args.steps},
         "cpu_baseline": None,
     }
+    out["roofline"]["measured_copy"] = copy_bandwidth(torch)
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(w, host_sets[0])
+        out["cpu_baseline_parallel"] = cpu_par
     print(json.dumps(out))
 
 
