@@ -205,49 +205,24 @@ def calibrate_copy(mb):
     print(json.dumps({"calibrate_copy_bytes": n * 4, "launches": 3}))
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="rec16k_bf16")
-    ap.add_argument("--sets", type=int, default=0, help="input sets rotated (0: enough to exceed the MALL)")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MB")
-    args = ap.parse_args()
-
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: the forward has no multi-GPU path "
-              "(pairs and sequence segments would shard with no exchange but a small operator "
-              "all-gather; see DESIGN.md). Run with --gpus 1.", file=sys.stderr)
-        sys.exit(2)
-    if args.calibrate_copy:
-        calibrate_copy(args.calibrate_copy)
-        return
-
+def time_workload(w, steps, warmup, sets, x0=None):
+    """Rotated input sets of workload w in HBM, warm-up, then the two timed regions
+    (plain, and with per-kernel HIP events).  Returns the timings."""
     import numpy as np
     import torch
 
     import delta_rule_sequence_amd as prism
     import workloads
 
-    w = workloads.workload(args.workload)
     lib = prism.load_library()
     dt = prism.PRISM_BF16 if w.dtype == "bf16" else prism.PRISM_F32
-    in_bytes, path_bytes = algorithmic_bytes(w)
+    in_bytes, _ = algorithmic_bytes(w)
     set_bytes = w.pairs * w.T * in_bytes
-    nsets = args.sets or max(1, -(-2 * MALL_BYTES // set_bytes))
+    nsets = sets or max(1, -(-2 * MALL_BYTES // set_bytes))
     print(f"[bench] {w.name}: {nsets} input set(s) of {set_bytes / 1e6:.1f} MB", file=sys.stderr, flush=True)
-
-    host_sets, dev_sets = [], []
-    x0 = workloads.generate(w, seed=w.seed)
-    host_sets.append(x0)
-    cpu_par = None
-    if not args.no_cpu_baseline:  # forked workers: before anything touches the GPU
-        print("[bench] timing the oracle on the host (one process per pair)", file=sys.stderr, flush=True)
-        cpu_par = cpu_baseline_parallel(w, x0)
+    dev_sets = []
     for i in range(nsets):
-        x = x0 if i == 0 else workloads.generate(w, seed=w.seed + 1000 * i)
+        x = x0 if (i == 0 and x0 is not None) else workloads.generate(w, seed=w.seed + 1000 * i)
         dev_sets.append(workloads.to_torch(x, w.dtype, "cuda"))
     vt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     o = torch.empty((w.B, w.H, w.T, w.dv), dtype=vt, device="cuda")
@@ -265,7 +240,7 @@ def main():
                 ctypes.c_void_p(ws.data_ptr()), ctypes.c_size_t(need)]
 
     calls = [argv(d) for d in dev_sets]
-    for i in range(args.warmup):
+    for i in range(warmup):
         st = lib.prism_fwd(*calls[i % nsets], sh)
         if st != 0:
             raise RuntimeError(prism.status_string(st))
@@ -274,7 +249,7 @@ def main():
     # timed region 1 (the reported throughput): K forwards back to back, no instrumentation
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(steps):
         st = lib.prism_fwd(*calls[i % nsets], sh)
         if st != 0:
             raise RuntimeError(prism.status_string(st))
@@ -284,20 +259,81 @@ def main():
     # timed region 2: the same K forwards with HIP events recorded on the launch stream
     # around each of the three kernels (the per-kernel durations of the roofline)
     hip = Hip()
-    evs = hip.events(4 * args.steps)
-    ev_arrays = [(ctypes.c_void_p * 4)(*evs[4 * i:4 * i + 4]) for i in range(args.steps)]
+    evs = hip.events(4 * steps)
+    ev_arrays = [(ctypes.c_void_p * 4)(*evs[4 * i:4 * i + 4]) for i in range(steps)]
     torch.cuda.synchronize()
-    for i in range(args.steps):
+    for i in range(steps):
         st = lib.prism_fwd_timed(*calls[i % nsets], ev_arrays[i], sh)
         if st != 0:
             raise RuntimeError(prism.status_string(st))
     torch.cuda.synchronize()
     per = np.array([[hip.elapsed_ms(evs[4 * i + j], evs[4 * i + j + 1]) for j in range(3)]
-                    for i in range(args.steps)])
-    span_ms = hip.elapsed_ms(evs[0], evs[4 * args.steps - 1])
+                    for i in range(steps)])
+    span_ms = hip.elapsed_ms(evs[0], evs[4 * steps - 1])
     hip.destroy(evs)
+    del dev_sets, o, S, ws
+    return {"ms_per_step": 1e3 * wall / steps, "per": per, "span_ms": span_ms, "nsets": nsets}
 
-    ms_per_step = 1e3 * wall / args.steps
+
+def l_sweep(steps, warmup):
+    """The 16K bf16 shape at L = 1 (the plain gated delta rule), 2, 4 and 8: one JSON
+    line per L with whole-forward tokens/s and the sweep's HBM roofline fraction."""
+    import workloads
+    base = workloads.workload("rec16k_bf16")
+    for L in (1, 2, 4, 8):
+        w = base.replace(L=L, name=f"rec16k_bf16_L{L}")
+        t = time_workload(w, steps, warmup, 0)
+        in_bytes, path_bytes = algorithmic_bytes(w)
+        sweep_ms = float(t["per"][:, 0].mean())
+        sweep_bytes = w.pairs * w.T * in_bytes
+        print(json.dumps({"workload": w.name, "L": L, "tokens_per_s": w.B * w.T / (t["ms_per_step"] * 1e-3),
+                          "ms_per_step": t["ms_per_step"],
+                          "kernel_ms": {"sweep": sweep_ms, "scan": float(t["per"][:, 1].mean()),
+                                        "fixup": float(t["per"][:, 2].mean())},
+                          "input_bytes_per_token_head": in_bytes,
+                          "sweep_hbm_frac": sweep_bytes / (sweep_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                          "path_hbm_roofline_tokens_per_s":
+                              w.B * w.T * HBM_PEAK_GBS * 1e9 / (w.pairs * w.T * path_bytes)}), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="rec16k_bf16")
+    ap.add_argument("--sets", type=int, default=0, help="input sets rotated (0: enough to exceed the MALL)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MB")
+    ap.add_argument("--l-sweep", action="store_true",
+                    help="time the 16K shape at L = 1, 2, 4, 8 (one JSON line each) instead")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the forward has no multi-GPU path "
+              "(pairs and sequence segments would shard with no exchange but a small operator "
+              "all-gather; see DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
+    if args.l_sweep:
+        l_sweep(args.steps, args.warmup)
+        return
+
+    import workloads
+
+    w = workloads.workload(args.workload)
+    x0 = workloads.generate(w, seed=w.seed)
+    cpu_par = None
+    if not args.no_cpu_baseline:  # forked workers: before anything touches the GPU
+        print("[bench] timing the oracle on the host (one process per pair)", file=sys.stderr, flush=True)
+        cpu_par = cpu_baseline_parallel(w, x0)
+    t = time_workload(w, args.steps, args.warmup, args.sets, x0)
+    import torch
+
+    in_bytes, path_bytes = algorithmic_bytes(w)
+    ms_per_step, per, span_ms, nsets = t["ms_per_step"], t["per"], t["span_ms"], t["nsets"]
     tokens = w.B * w.T
     sweep_ms = float(per[:, 0].mean())
     sweep_bytes = w.pairs * w.T * in_bytes + w.H * 4 * w.dv * 4
@@ -334,7 +370,7 @@ def main():
     out["roofline"]["measured_copy"] = copy_bandwidth(torch)
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(w, host_sets[0])
+        out["cpu_baseline"] = cpu_baseline(w, x0)
         out["cpu_baseline_parallel"] = cpu_par
     print(json.dumps(out))
 

@@ -135,10 +135,15 @@ prism_status launch(const FwdArgs& a, const Plan& pl, hipEvent_t* ev, hipStream_
 
 prism_status launch_fast(const FwdArgs& a, const Plan& pl, hipEvent_t* ev, hipStream_t stream) {
   if (!record(ev, 0, stream)) return PRISM_ERR_HIP;
-  if (a.L == 4)  // the rank-4 sweep with its steps unrolled
-    hipLaunchKernelGGL((prism::seg_sweep8_kernel<64, 64, 3>), dim3(pl.nseg, pl.P), dim3(512), 0, stream, a);
-  else
-    hipLaunchKernelGGL((prism::seg_sweep8_kernel<64, 64, -1>), dim3(pl.nseg, pl.P), dim3(512), 0, stream, a);
+  // L = 1, 2, 4, 8 with the rank-L steps unrolled; other L through the runtime step loop
+  const dim3 grid(pl.nseg, pl.P), block(512);
+  switch (a.L) {
+    case 1: hipLaunchKernelGGL((prism::seg_sweep8_kernel<64, 64, 0>), grid, block, 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((prism::seg_sweep8_kernel<64, 64, 1>), grid, block, 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((prism::seg_sweep8_kernel<64, 64, 3>), grid, block, 0, stream, a); break;
+    case 8: hipLaunchKernelGGL((prism::seg_sweep8_kernel<64, 64, 7>), grid, block, 0, stream, a); break;
+    default: hipLaunchKernelGGL((prism::seg_sweep8_kernel<64, 64, -1>), grid, block, 0, stream, a); break;
+  }
   if (hipGetLastError() != hipSuccess || !record(ev, 1, stream)) return PRISM_ERR_HIP;
   hipLaunchKernelGGL((prism::seg_scan_fast_kernel<64, 64>), dim3(pl.P, 64 / 4), dim3(256), 0, stream, a);
   if (hipGetLastError() != hipSuccess || !record(ev, 2, stream)) return PRISM_ERR_HIP;
