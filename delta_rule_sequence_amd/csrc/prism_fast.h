@@ -16,14 +16,6 @@ __device__ __forceinline__ f32x4 mfma16(const bf16x4& a, const bf16x4& b, const 
                                                    0, 0, 0);
 }
 
-// Z = A * B for 16x16 float32 tiles, A given by the tile of A^T, B by its tile.
-__device__ __forceinline__ f32x4 mm16_f32(const f32x4& At, const f32x4& Bt) {
-  f32x4 acc = zero4();
-#pragma unroll
-  for (int r = 0; r < 4; ++r) acc = mfma(At[r], Bt[r], acc);
-  return acc;
-}
-
 __device__ __forceinline__ f32x4 plus_identity(f32x4 x) {
   const int l = lane_id(), g4 = (l >> 4) * 4, li = l & 15;
 #pragma unroll
@@ -36,6 +28,12 @@ __device__ __forceinline__ bf16x4 to_bf16x4(const f32x4& x) {
 #pragma unroll
   for (int r = 0; r < 4; ++r) y[r] = (bf16_t)x[r];
   return y;
+}
+
+// Z = A * B for 16x16 tiles held as MFMA accumulators, A given by the tile of A^T and B
+// by its own tile: one 16x16x16 MFMA on the bfloat16-rounded operands, float32 sums.
+__device__ __forceinline__ f32x4 mm16_bf16(const f32x4& At, const f32x4& Bt) {
+  return mfma16(to_bf16x4(At), to_bf16x4(Bt), zero4());
 }
 
 __device__ __forceinline__ bf16x8 cat8(const bf16x4& a, const bf16x4& b) {

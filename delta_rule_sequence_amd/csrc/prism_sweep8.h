@@ -19,7 +19,8 @@
 //   * a K wave and a Q wave on one SIMD take row blocks r and 3 - r, so the
 //     triangular Gram work is the same on every SIMD;
 //   * (I + M)^-1 is built explicitly: the 16x16 diagonal blocks by the product
-//     (I + Y)(I + Y^2)(I + Y^4)(I + Y^8) (Y = -M_ii is nilpotent) in float32, the
+//     (I + Y)(I + Y^2)(I + Y^4)(I + Y^8) (Y = -M_ii is nilpotent; bfloat16 products
+//     with float32 accumulation, the factors rounded as the stored inverse is), the
 //     rest by block forward substitution on identity columns, overlapped with
 //     the rank-L steps, so the solve that depends on V' is one product;
 //   * one barrier per rank-L step plus four per chunk (L + 3 for L >= 4); the
@@ -231,10 +232,14 @@ __device__ __forceinline__ void gram_rows(bf16x8 (&fa)[2], const bf16_t* sY, con
                                           const float (&dec)[4][4], float sign) {
   constexpr int LD = Sweep8Lds::LD;
   f32x4 raw[4];
+  const bf16x8 x0 = frag8(sX, LD, 16 * rb, 0), x1 = frag8(sX, LD, 16 * rb, 32);
 #pragma unroll
   for (int jt = 0; jt < 4; ++jt) {
     raw[jt] = zero4();
-    if (jt <= rb) mm_ll<bf16_t>(raw[jt], sY, LD, 16 * jt, sX, LD, 16 * rb, 64);
+    if (jt <= rb) {
+      raw[jt] = mfma(frag8(sY, LD, 16 * jt, 0), x0, raw[jt]);
+      raw[jt] = mfma(frag8(sY, LD, 16 * jt, 32), x1, raw[jt]);
+    }
   }
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
@@ -316,15 +321,21 @@ __device__ __forceinline__ void sweep8_kwave(const Sweep8Ctx& x, int wq) {
     // ---- P0: M[i][j] = beta_i Gam_ij K_i.K_j (j < i) rows rb; diagonal inverse block --
     const int cn = c + 1 < x.c_end ? c + 1 : c;  // next chunk (this one again at the end:
                                                   // unconditional loads keep waits exact)
-    decay_factors(dec, V.sB, rb, true);
     {
+      // the diagonal tile first (its operands are the row block's own fragments): the
+      // inverse of the diagonal block is the longest chain of the phase
+      const bf16x8 k0 = frag8(V.sK, LD, 16 * rb, 0), k1 = frag8(V.sK, LD, 16 * rb, 32);
+      f32x4 draw = mfma(k0, k0, zero4());
+      draw = mfma(k1, k1, draw);
+      decay_factors(dec, V.sB, rb, true);
       f32x4 mraw[4];
-      f32x4 draw = zero4();
 #pragma unroll
-      for (int jt = 0; jt < 4; ++jt) {
+      for (int jt = 0; jt < 3; ++jt) {
         mraw[jt] = zero4();
-        if (jt <= rb) mm_ll<bf16_t>(mraw[jt], V.sK, LD, 16 * jt, V.sK, LD, 16 * rb, 64);
-        if (jt == rb) draw = mraw[jt];
+        if (jt < rb) {
+          mraw[jt] = mfma(frag8(V.sK, LD, 16 * jt, 0), k0, mraw[jt]);
+          mraw[jt] = mfma(frag8(V.sK, LD, 16 * jt, 32), k1, mraw[jt]);
+        }
       }
       const float beil = V.sBeta[16 * rb + li];
 #pragma unroll
@@ -349,13 +360,13 @@ __device__ __forceinline__ void sweep8_kwave(const Sweep8Ctx& x, int wq) {
         Y[r] = (li < g4 + r) ? -ber[r] * __expf(bir[r] - bl) * draw[r] : 0.f;  // Y[g4 + r][li]
         Yt[r] = -beil * dd * draw[r];                                        // Y[li][g4 + r]
       }
-      const f32x4 Y2 = mm16_f32(Yt, Y), Y2t = mm16_f32(Y, Yt);
-      const f32x4 Y4 = mm16_f32(Y2t, Y2), Y4t = mm16_f32(Y2, Y2t);
-      const f32x4 Y8 = mm16_f32(Y4t, Y4);
+      const f32x4 Y2 = mm16_bf16(Yt, Y), Y2t = mm16_bf16(Y, Yt);
+      const f32x4 Y4 = mm16_bf16(Y2t, Y2), Y4t = mm16_bf16(Y2, Y2t);
+      const f32x4 Y8 = mm16_bf16(Y4t, Y4);
       f32x4 Pt = plus_identity(Yt);
-      Pt = mm16_f32(plus_identity(Y2), Pt);
-      Pt = mm16_f32(plus_identity(Y4), Pt);
-      Pt = mm16_f32(plus_identity(Y8), Pt);  // Pt = T^T: T[li][g4 + r] = Pt[r]
+      Pt = mm16_bf16(plus_identity(Y2), Pt);
+      Pt = mm16_bf16(plus_identity(Y4), Pt);
+      Pt = mm16_bf16(plus_identity(Y8), Pt);  // Pt = T^T: T[li][g4 + r] = Pt[r]
       *reinterpret_cast<bf16x4*>(V.sTd + (16 * rb + li) * LDT + g4) = to_bf16x4(Pt);
     }
 #pragma unroll
@@ -689,10 +700,11 @@ __device__ __forceinline__ void sweep8_qwave(const Sweep8Ctx& x, int wq) {
       const float GC = V.sG[C - 1];
       const float4 G4 = *reinterpret_cast<const float4*>(V.sG + 16 * rb + g4);
       const float Gr[4] = {G4.x, G4.y, G4.z, G4.w};
+      const bf16x8 q0 = frag8(V.sQ, LD, 16 * rb, 0), q1 = frag8(V.sQ, LD, 16 * rb, 32);
 #pragma unroll
       for (int vt = 0; vt < 4; ++vt) {
-        f32x4 qh = zero4();
-        mm_ll<bf16_t>(qh, V.sQ, LD, 16 * rb, V.sHt, LD, 16 * vt, 64);
+        f32x4 qh = mfma(q0, frag8(V.sHt, LD, 16 * vt, 0), zero4());
+        qh = mfma(q1, frag8(V.sHt, LD, 16 * vt, 32), qh);
 #pragma unroll
         for (int r = 0; r < 4; ++r) O[vt][r] += Gr[r] * qh[r];
       }
