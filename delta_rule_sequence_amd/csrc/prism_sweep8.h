@@ -30,12 +30,14 @@
 
 namespace prism {
 
-// LDS plan (bytes); every [64][64] bf16 array has row stride 68 (34 dwords): the 16
-// rows an MFMA fragment read touches and the 16 lanes of a 4x4-block store land in
-// distinct bank pairs.
+// LDS plan (bytes).  Every [64][64] bf16 array has row stride 72 (36 dwords) and its
+// columns permuted inside each 32-column block (pcol below), so that a lane's MFMA operand
+// (8 values of one row) is 16 contiguous bytes: one ds_read_b128, which on gfx950 moves
+// twice the bytes per clock of the 8-byte reads.  With the 36-dword stride the 16 lanes of
+// an operand read, and the 16 lanes of a 4x4-block store, touch distinct banks.
 struct Sweep8Lds {
   static constexpr int D = 64, C = 64;
-  static constexpr int LD = 68;
+  static constexpr int LD = 72;
   static constexpr int LDT = 20;                     // row stride of a 16x16 inverse block
   static constexpr size_t szA = (size_t)64 * LD * 2;  // one array
   static constexpr size_t oQ = 0;                    // Q [token][d]
@@ -79,10 +81,23 @@ __device__ __forceinline__ bf16x8 scaled_pair(const f32x4& t0, const f32x4& t1, 
 
 __device__ __forceinline__ bf16x8 pair8(const f32x4& t0, const f32x4& t1) { return cat8(to_bf16x4(t0), to_bf16x4(t1)); }
 
-// A [n][k] LDS operand scaled by s[k] (k = k0 + slot order of frag8).
-__device__ __forceinline__ bf16x8 scaled_frag8(const bf16_t* X, int ld, int r0, int k0, const float* s) {
+// Stored position of logical column c of an LDS array: inside each 32-column block,
+// column 16 h + 4 g + e (h < 2, g < 4, e < 4) sits at 8 g + 4 h + e, so the two 4-column
+// halves of lane group g's 32-deep operand (columns 4 g .. and 16 + 4 g ..) are adjacent.
+// Four consecutive columns starting at a multiple of 4 stay consecutive.
+__device__ __forceinline__ constexpr int pcol(int c) { return (c & ~31) | ((c & 12) << 1) | ((c & 16) >> 2) | (c & 3); }
+
+// 8 bf16 of a 32-deep MFMA operand from row r0 + lane%16 of a column-permuted LDS array, in
+// the k order of frag8 (k0 + 4g .. +3, then k0 + 16 + 4g .. +3; k0 = 0 or 32): one 16-byte read.
+__device__ __forceinline__ bf16x8 lfrag(const bf16_t* X, int r0, int k0) {
+  const int l = lane_id();
+  return *reinterpret_cast<const bf16x8*>(X + (r0 + (l & 15)) * Sweep8Lds::LD + k0 + 8 * (l >> 4));
+}
+
+// The same operand scaled by s[k] (k in the logical column order).
+__device__ __forceinline__ bf16x8 lscaled(const bf16_t* X, int r0, int k0, const float* s) {
   const int g4 = 4 * (lane_id() >> 4);
-  const bf16x8 x = frag8(X, ld, r0, k0);
+  const bf16x8 x = lfrag(X, r0, k0);
   const float4 a = *reinterpret_cast<const float4*>(s + k0 + g4);
   const float4 b = *reinterpret_cast<const float4*>(s + k0 + 16 + g4);
   bf16x8 r;
@@ -135,13 +150,13 @@ __device__ __forceinline__ void quad_store(const uint2* x, bf16_t* dst, bf16_t* 
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     rows[r] = __builtin_bit_cast(bf16x4, x[r]);
-    if (dst != nullptr) *reinterpret_cast<uint2*>(dst + (4 * rq + r) * LD + c4) = x[r];
+    if (dst != nullptr) *reinterpret_cast<uint2*>(dst + (4 * rq + r) * LD + pcol(c4)) = x[r];
   }
   if (dstT != nullptr) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const bf16x4 col = {rows[0][c], rows[1][c], rows[2][c], rows[3][c]};
-      *reinterpret_cast<bf16x4*>(dstT + (c4 + c) * LD + 4 * rq) = col;
+      *reinterpret_cast<bf16x4*>(dstT + (c4 + c) * LD + pcol(4 * rq)) = col;
     }
   }
 }
@@ -232,13 +247,13 @@ __device__ __forceinline__ void gram_rows(bf16x8 (&fa)[2], const bf16_t* sY, con
                                           const float (&dec)[4][4], float sign) {
   constexpr int LD = Sweep8Lds::LD;
   f32x4 raw[4];
-  const bf16x8 x0 = frag8(sX, LD, 16 * rb, 0), x1 = frag8(sX, LD, 16 * rb, 32);
+  const bf16x8 x0 = lfrag(sX, 16 * rb, 0), x1 = lfrag(sX, 16 * rb, 32);
 #pragma unroll
   for (int jt = 0; jt < 4; ++jt) {
     raw[jt] = zero4();
     if (jt <= rb) {
-      raw[jt] = mfma(frag8(sY, LD, 16 * jt, 0), x0, raw[jt]);
-      raw[jt] = mfma(frag8(sY, LD, 16 * jt, 32), x1, raw[jt]);
+      raw[jt] = mfma(lfrag(sY, 16 * jt, 0), x0, raw[jt]);
+      raw[jt] = mfma(lfrag(sY, 16 * jt, 32), x1, raw[jt]);
     }
   }
 #pragma unroll
@@ -324,7 +339,7 @@ __device__ __forceinline__ void sweep8_kwave(const Sweep8Ctx& x, int wq) {
     {
       // the diagonal tile first (its operands are the row block's own fragments): the
       // inverse of the diagonal block is the longest chain of the phase
-      const bf16x8 k0 = frag8(V.sK, LD, 16 * rb, 0), k1 = frag8(V.sK, LD, 16 * rb, 32);
+      const bf16x8 k0 = lfrag(V.sK, 16 * rb, 0), k1 = lfrag(V.sK, 16 * rb, 32);
       f32x4 draw = mfma(k0, k0, zero4());
       draw = mfma(k1, k1, draw);
       decay_factors(dec, V.sB, rb, true);
@@ -333,8 +348,8 @@ __device__ __forceinline__ void sweep8_kwave(const Sweep8Ctx& x, int wq) {
       for (int jt = 0; jt < 3; ++jt) {
         mraw[jt] = zero4();
         if (jt < rb) {
-          mraw[jt] = mfma(frag8(V.sK, LD, 16 * jt, 0), k0, mraw[jt]);
-          mraw[jt] = mfma(frag8(V.sK, LD, 16 * jt, 32), k1, mraw[jt]);
+          mraw[jt] = mfma(lfrag(V.sK, 16 * jt, 0), k0, mraw[jt]);
+          mraw[jt] = mfma(lfrag(V.sK, 16 * jt, 32), k1, mraw[jt]);
         }
       }
       const float beil = V.sBeta[16 * rb + li];
@@ -344,7 +359,7 @@ __device__ __forceinline__ void sweep8_kwave(const Sweep8Ctx& x, int wq) {
           bf16x4 mv;
 #pragma unroll
           for (int r = 0; r < 4; ++r) mv[r] = (bf16_t)(beil * dec[jt][r] * mraw[jt][r]);
-          *reinterpret_cast<bf16x4*>(V.sM + (16 * rb + li) * LD + 16 * jt + g4) = mv;
+          *reinterpret_cast<bf16x4*>(V.sM + (16 * rb + li) * LD + pcol(16 * jt + g4)) = mv;
         }
       }
       // T_rb = (I + M_rb,rb)^-1 = (I + Y)(I + Y^2)(I + Y^4)(I + Y^8), Y = -M_rb,rb
@@ -371,7 +386,7 @@ __device__ __forceinline__ void sweep8_kwave(const Sweep8Ctx& x, int wq) {
     }
 #pragma unroll
     for (int vt = 0; vt < 4; ++vt) {  // V' starts as V (rows rb); the rank-L state term at zero
-      const bf16x4 xv = *reinterpret_cast<const bf16x4*>(V.sVt + (16 * vt + li) * LD + 16 * rb + g4);
+      const bf16x4 xv = *reinterpret_cast<const bf16x4*>(V.sVt + (16 * vt + li) * LD + pcol(16 * rb + g4));
 #pragma unroll
       for (int r = 0; r < 4; ++r) Vp[vt][r] = (float)xv[r];
       HB[vt] = zero4();
@@ -390,39 +405,39 @@ __device__ __forceinline__ void sweep8_kwave(const Sweep8Ctx& x, int wq) {
         gram_rows(xa, sU, V.sK, rb, dec, -1.f);
 #pragma unroll
         for (int vt = 0; vt < 4; ++vt) {  // V' += X1 R_l
-          Vp[vt] = mfma(xa[0], frag8(sRt, LD, 16 * vt, 0), Vp[vt]);
-          if (rb >= 2) Vp[vt] = mfma(xa[1], frag8(sRt, LD, 16 * vt, 32), Vp[vt]);
+          Vp[vt] = mfma(xa[0], lfrag(sRt, 16 * vt, 0), Vp[vt]);
+          if (rb >= 2) Vp[vt] = mfma(xa[1], lfrag(sRt, 16 * vt, 32), Vp[vt]);
         }
         // HB(:, cb) += U_l^T diag(D) R_l(:, cb)
-        const bf16x8 rd0 = scaled_frag8(sRt, LD, 16 * cb, 0, V.sD);
-        const bf16x8 rd1 = scaled_frag8(sRt, LD, 16 * cb, 32, V.sD);
+        const bf16x8 rd0 = lscaled(sRt, 16 * cb, 0, V.sD);
+        const bf16x8 rd1 = lscaled(sRt, 16 * cb, 32, V.sD);
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) {
-          HB[kt] = mfma(frag8(sUt, LD, 16 * kt, 0), rd0, HB[kt]);
-          HB[kt] = mfma(frag8(sUt, LD, 16 * kt, 32), rd1, HB[kt]);
+          HB[kt] = mfma(lfrag(sUt, 16 * kt, 0), rd0, HB[kt]);
+          HB[kt] = mfma(lfrag(sUt, 16 * kt, 32), rd1, HB[kt]);
         }
       }
       if (lv == 2) {
         // Wc(:, cb) = (I + M)^-1 diag(beta G) K(:, cb), row-major and transposed (the
         // inverse's column blocks come from the Q waves' phase 1)
-        const bf16x8 k0 = scaled_frag8(V.sKt, LD, 16 * cb, 0, V.sBG);
-        const bf16x8 k1 = scaled_frag8(V.sKt, LD, 16 * cb, 32, V.sBG);
+        const bf16x8 k0 = lscaled(V.sKt, 16 * cb, 0, V.sBG);
+        const bf16x8 k1 = lscaled(V.sKt, 16 * cb, 32, V.sBG);
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
-          f32x4 acc = mfma(frag8(V.sMinv, LD, 16 * it, 0), k0, zero4());
-          if (it >= 2) acc = mfma(frag8(V.sMinv, LD, 16 * it, 32), k1, acc);
+          f32x4 acc = mfma(lfrag(V.sMinv, 16 * it, 0), k0, zero4());
+          if (it >= 2) acc = mfma(lfrag(V.sMinv, 16 * it, 32), k1, acc);
           const bf16x4 xv = to_bf16x4(acc);  // Wc[16 it + g4 + r][16 cb + li]
-          *reinterpret_cast<bf16x4*>(V.sWct + (16 * cb + li) * LD + 16 * it + g4) = xv;
+          *reinterpret_cast<bf16x4*>(V.sWct + (16 * cb + li) * LD + pcol(16 * it + g4)) = xv;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) V.sWc[(16 * it + g4 + r) * LD + 16 * cb + li] = xv[r];
+          for (int r = 0; r < 4; ++r) V.sWc[(16 * it + g4 + r) * LD + pcol(16 * cb + li)] = xv[r];
         }
       }
       if (lv == 3) {  // WH = Wc H(:, cb), Wc from phase 2
         const bf16x8 h0 = pair8(H[0], H[1]), h1 = pair8(H[2], H[3]);
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
-          const f32x4 acc = mfma(frag8(V.sWc, LD, 16 * it, 0), h0, zero4());
-          WH[it] = mfma(frag8(V.sWc, LD, 16 * it, 32), h1, acc);
+          const f32x4 acc = mfma(lfrag(V.sWc, 16 * it, 0), h0, zero4());
+          WH[it] = mfma(lfrag(V.sWc, 16 * it, 32), h1, acc);
         }
       }
       if (lv + 1 <= Lm1) {  // U_{lv+1} into the other slot, then fetch U_{lv+2}
@@ -439,7 +454,7 @@ __device__ __forceinline__ void sweep8_kwave(const Sweep8Ctx& x, int wq) {
         for (int vt = 0; vt < 4; ++vt) {
           const bf16x4 xv = {(bf16_t)(be.x * Vp[vt][0]), (bf16_t)(be.y * Vp[vt][1]), (bf16_t)(be.z * Vp[vt][2]),
                              (bf16_t)(be.w * Vp[vt][3])};
-          *reinterpret_cast<bf16x4*>(V.sVt + (16 * vt + li) * LD + 16 * rb + g4) = xv;
+          *reinterpret_cast<bf16x4*>(V.sVt + (16 * vt + li) * LD + pcol(16 * rb + g4)) = xv;
         }
       }
       __syncthreads();
@@ -454,21 +469,21 @@ __device__ __forceinline__ void sweep8_kwave(const Sweep8Ctx& x, int wq) {
     // ---- P_S: Uc = M^-1 (beta V')(:, cb), E = Uc - WH, H(:, cb) update -------------------------
     {
       const float GC = V.sG[C - 1];
-      const bf16x8 v0 = frag8(V.sVt, LD, 16 * cb, 0), v1 = frag8(V.sVt, LD, 16 * cb, 32);
+      const bf16x8 v0 = lfrag(V.sVt, 16 * cb, 0), v1 = lfrag(V.sVt, 16 * cb, 32);
       f32x4 E[4];
 #pragma unroll
       for (int it = 0; it < 4; ++it) {
-        f32x4 acc = mfma(frag8(V.sMinv, LD, 16 * it, 0), v0, zero4());
-        if (it >= 2) acc = mfma(frag8(V.sMinv, LD, 16 * it, 32), v1, acc);
+        f32x4 acc = mfma(lfrag(V.sMinv, 16 * it, 0), v0, zero4());
+        if (it >= 2) acc = mfma(lfrag(V.sMinv, 16 * it, 32), v1, acc);
 #pragma unroll
         for (int r = 0; r < 4; ++r) E[it][r] = acc[r] - WH[it][r];
-        *reinterpret_cast<bf16x4*>(V.sEt + (16 * cb + li) * LD + 16 * it + g4) = to_bf16x4(E[it]);
+        *reinterpret_cast<bf16x4*>(V.sEt + (16 * cb + li) * LD + pcol(16 * it + g4)) = to_bf16x4(E[it]);
       }
       const bf16x8 e0 = scaled_pair(E[0], E[1], V.sD, 0), e1 = scaled_pair(E[2], E[3], V.sD, 32);
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
-        f32x4 he = mfma(frag8(V.sKt, LD, 16 * kt, 0), e0, zero4());
-        he = mfma(frag8(V.sKt, LD, 16 * kt, 32), e1, he);
+        f32x4 he = mfma(lfrag(V.sKt, 16 * kt, 0), e0, zero4());
+        he = mfma(lfrag(V.sKt, 16 * kt, 32), e1, he);
 #pragma unroll
         for (int r = 0; r < 4; ++r) H[kt][r] = GC * H[kt][r] + he[r] + HB[kt][r];
       }
@@ -478,7 +493,7 @@ __device__ __forceinline__ void sweep8_kwave(const Sweep8Ctx& x, int wq) {
     // ---- P_O: new H^T; next chunk into LDS ---------------------------------------------------
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
-      *reinterpret_cast<bf16x4*>(V.sHt + (16 * cb + li) * LD + 16 * kt + g4) = to_bf16x4(H[kt]);
+      *reinterpret_cast<bf16x4*>(V.sHt + (16 * cb + li) * LD + pcol(16 * kt + g4)) = to_bf16x4(H[kt]);
     if (c + 1 < x.c_end) store_chunk(c + 1);
   }
 #pragma unroll
@@ -530,7 +545,7 @@ __device__ __forceinline__ void sweep8_qwave(const Sweep8Ctx& x, int wq) {
     for (int cc = 0; cc < 4; ++cc) {
       const bf16x4 col = {__builtin_bit_cast(bf16x4, pf[4])[cc], __builtin_bit_cast(bf16x4, pf[5])[cc],
                           __builtin_bit_cast(bf16x4, pf[6])[cc], __builtin_bit_cast(bf16x4, pf[7])[cc]};
-      *reinterpret_cast<bf16x4*>(V.sVt + (c4 + cc) * LD + 4 * rq) = col;
+      *reinterpret_cast<bf16x4*>(V.sVt + (c4 + cc) * LD + pcol(4 * rq)) = col;
     }
   };
   // the residual r_0 = v - anchor of the block (anchor_t = sum_j w_j v_{t-3+j})
@@ -576,7 +591,7 @@ __device__ __forceinline__ void sweep8_qwave(const Sweep8Ctx& x, int wq) {
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc) {
       const bf16x4 col = {(bf16_t)R[0][cc], (bf16_t)R[1][cc], (bf16_t)R[2][cc], (bf16_t)R[3][cc]};
-      *reinterpret_cast<bf16x4*>(dst + (c4 + cc) * LD + 4 * rq) = col;
+      *reinterpret_cast<bf16x4*>(dst + (c4 + cc) * LD + pcol(4 * rq)) = col;
     }
   };
 
@@ -609,8 +624,8 @@ __device__ __forceinline__ void sweep8_qwave(const Sweep8Ctx& x, int wq) {
         gram_rows(xa, sU, V.sQ, rb, dec, 1.f);
 #pragma unroll
         for (int vt = 0; vt < 4; ++vt) {
-          O[vt] = mfma(xa[0], frag8(sRt, LD, 16 * vt, 0), O[vt]);
-          if (rb >= 2) O[vt] = mfma(xa[1], frag8(sRt, LD, 16 * vt, 32), O[vt]);
+          O[vt] = mfma(xa[0], lfrag(sRt, 16 * vt, 0), O[vt]);
+          if (rb >= 2) O[vt] = mfma(xa[1], lfrag(sRt, 16 * vt, 32), O[vt]);
         }
       }
       if (lv == 1) {
@@ -630,7 +645,7 @@ __device__ __forceinline__ void sweep8_qwave(const Sweep8Ctx& x, int wq) {
 #pragma unroll
             for (int kk = 0; kk < i; ++kk) {
               if (kk >= cb) {
-                const bf16x4 am = *reinterpret_cast<const bf16x4*>(V.sM + (16 * i + li) * LD + 16 * kk + g4);
+                const bf16x4 am = *reinterpret_cast<const bf16x4*>(V.sM + (16 * i + li) * LD + pcol(16 * kk + g4));
                 sacc = mfma16(am, to_bf16x4(X[kk]), sacc);
               }
             }
@@ -644,24 +659,24 @@ __device__ __forceinline__ void sweep8_qwave(const Sweep8Ctx& x, int wq) {
         for (int i = 0; i < 4; ++i) {  // zero above the diagonal blocks
           const bf16x4 xv = to_bf16x4(X[i]);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) V.sMinv[(16 * i + g4 + r) * LD + 16 * cb + li] = xv[r];
+          for (int r = 0; r < 4; ++r) V.sMinv[(16 * i + g4 + r) * LD + pcol(16 * cb + li)] = xv[r];
         }
       } else if (lv == 3) {
         // WA = Wc A_acc(:, cb)
         const bf16x8 a0 = pair8(A[0], A[1]), a1 = pair8(A[2], A[3]);
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
-          const f32x4 acc = mfma(frag8(V.sWc, LD, 16 * it, 0), a0, zero4());
-          WA[it] = mfma(frag8(V.sWc, LD, 16 * it, 32), a1, acc);
+          const f32x4 acc = mfma(lfrag(V.sWc, 16 * it, 0), a0, zero4());
+          WA[it] = mfma(lfrag(V.sWc, 16 * it, 32), a1, acc);
         }
         // Qtilde^T = (diag(G) Q)^T - Wc^T P^T (dk rows kt, tokens rb); Qhat^T = A_acc^T Qtilde^T
         const float Gi = V.sG[16 * rb + li];
         f32x4 Qt[4];
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) {
-          const bf16x4 qv = *reinterpret_cast<const bf16x4*>(V.sQ + (16 * rb + li) * LD + 16 * kt + g4);
-          f32x4 pw = mfma(frag8(V.sWct, LD, 16 * kt, 0), Pa[0], zero4());
-          if (rb >= 2) pw = mfma(frag8(V.sWct, LD, 16 * kt, 32), Pa[1], pw);
+          const bf16x4 qv = *reinterpret_cast<const bf16x4*>(V.sQ + (16 * rb + li) * LD + pcol(16 * kt + g4));
+          f32x4 pw = mfma(lfrag(V.sWct, 16 * kt, 0), Pa[0], zero4());
+          if (rb >= 2) pw = mfma(lfrag(V.sWct, 16 * kt, 32), Pa[1], pw);
 #pragma unroll
           for (int r = 0; r < 4; ++r) Qt[kt][r] = Gi * (float)qv[r] - pw[r];
         }
@@ -671,10 +686,10 @@ __device__ __forceinline__ void sweep8_qwave(const Sweep8Ctx& x, int wq) {
         bf16_t* qf = reinterpret_cast<bf16_t*>(x.qhat_base) + ((size_t)c * 4 + rb) * 1024 + l * 8;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-          f32x4 e0 = mfma(frag8(V.sAt, LD, 32 * kb, 0), q0, zero4());
-          e0 = mfma(frag8(V.sAt, LD, 32 * kb, 32), q1, e0);
-          f32x4 e1 = mfma(frag8(V.sAt, LD, 32 * kb + 16, 0), q0, zero4());
-          e1 = mfma(frag8(V.sAt, LD, 32 * kb + 16, 32), q1, e1);
+          f32x4 e0 = mfma(lfrag(V.sAt, 32 * kb, 0), q0, zero4());
+          e0 = mfma(lfrag(V.sAt, 32 * kb, 32), q1, e0);
+          f32x4 e1 = mfma(lfrag(V.sAt, 32 * kb + 16, 0), q0, zero4());
+          e1 = mfma(lfrag(V.sAt, 32 * kb + 16, 32), q1, e1);
           *reinterpret_cast<bf16x8*>(qf + kb * 512) = pair8(e0, e1);
         }
       }
@@ -700,22 +715,22 @@ __device__ __forceinline__ void sweep8_qwave(const Sweep8Ctx& x, int wq) {
       const float GC = V.sG[C - 1];
       const float4 G4 = *reinterpret_cast<const float4*>(V.sG + 16 * rb + g4);
       const float Gr[4] = {G4.x, G4.y, G4.z, G4.w};
-      const bf16x8 q0 = frag8(V.sQ, LD, 16 * rb, 0), q1 = frag8(V.sQ, LD, 16 * rb, 32);
+      const bf16x8 q0 = lfrag(V.sQ, 16 * rb, 0), q1 = lfrag(V.sQ, 16 * rb, 32);
 #pragma unroll
       for (int vt = 0; vt < 4; ++vt) {
-        f32x4 qh = mfma(q0, frag8(V.sHt, LD, 16 * vt, 0), zero4());
-        qh = mfma(q1, frag8(V.sHt, LD, 16 * vt, 32), qh);
+        f32x4 qh = mfma(q0, lfrag(V.sHt, 16 * vt, 0), zero4());
+        qh = mfma(q1, lfrag(V.sHt, 16 * vt, 32), qh);
 #pragma unroll
         for (int r = 0; r < 4; ++r) O[vt][r] += Gr[r] * qh[r];
       }
       const bf16x8 w0 = scaled_pair(WA[0], WA[1], V.sD, 0), w1 = scaled_pair(WA[2], WA[3], V.sD, 32);
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
-        f32x4 aw = mfma(frag8(V.sKt, LD, 16 * kt, 0), w0, zero4());
-        aw = mfma(frag8(V.sKt, LD, 16 * kt, 32), w1, aw);
+        f32x4 aw = mfma(lfrag(V.sKt, 16 * kt, 0), w0, zero4());
+        aw = mfma(lfrag(V.sKt, 16 * kt, 32), w1, aw);
 #pragma unroll
         for (int r = 0; r < 4; ++r) A[kt][r] = GC * A[kt][r] - aw[r];
-        *reinterpret_cast<bf16x4*>(V.sAt + (16 * cb + li) * LD + 16 * kt + g4) = to_bf16x4(A[kt]);
+        *reinterpret_cast<bf16x4*>(V.sAt + (16 * cb + li) * LD + pcol(16 * kt + g4)) = to_bf16x4(A[kt]);
       }
     }
     __syncthreads();  // E^T in LDS
@@ -725,8 +740,8 @@ __device__ __forceinline__ void sweep8_qwave(const Sweep8Ctx& x, int wq) {
       bf16_t* of = reinterpret_cast<bf16_t*>(x.oloc) + ((size_t)c * 4 + rb) * 1024 + l * 4;
 #pragma unroll
       for (int vt = 0; vt < 4; ++vt) {
-        O[vt] = mfma(Pa[0], frag8(V.sEt, LD, 16 * vt, 0), O[vt]);
-        if (rb >= 2) O[vt] = mfma(Pa[1], frag8(V.sEt, LD, 16 * vt, 32), O[vt]);
+        O[vt] = mfma(Pa[0], lfrag(V.sEt, 16 * vt, 0), O[vt]);
+        if (rb >= 2) O[vt] = mfma(Pa[1], lfrag(V.sEt, 16 * vt, 32), O[vt]);
         *reinterpret_cast<bf16x4*>(of + vt * 256) = to_bf16x4(O[vt]);
       }
     }
@@ -784,8 +799,8 @@ __global__ __launch_bounds__(512, 1) void seg_sweep8_kernel(FwdArgs a) {
   for (int i = tid; i < 4 * D; i += 512) V.sTaps[i] = L > 1 ? cw[i] : 0.f;
   for (int i = tid; i < D * D; i += 512) {
     const int r = i / D, c = i % D;
-    V.sHt[r * Sweep8Lds::LD + c] = (bf16_t)0.f;
-    V.sAt[r * Sweep8Lds::LD + c] = (bf16_t)(r == c ? 1.f : 0.f);
+    V.sHt[r * Sweep8Lds::LD + pcol(c)] = (bf16_t)0.f;
+    V.sAt[r * Sweep8Lds::LD + pcol(c)] = (bf16_t)(r == c ? 1.f : 0.f);
   }
   __syncthreads();
   // Both roles pass the same barriers in the same order: B0, B1, one per phase
