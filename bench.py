@@ -26,6 +26,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = 2500.0  # dense bf16
 MALL_BYTES = 256 << 20
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -191,6 +192,23 @@ def copy_bandwidth(torch, mb=1024, reps=10):
     dt = time.perf_counter() - t0
     del a, b
     return {"value": 2 * n * 4 * reps / dt / 1e9, "unit": "GB/s", "bytes_per_copy": 2 * n * 4}
+
+
+def mfma_rate(torch, n=8192, reps=10):
+    """Measured dense bf16 matrix rate: a vendor GEMM (torch.mm on contiguous n x n bfloat16
+    operands, float32 accumulation inside) as the achievable MFMA ceiling beside the peak."""
+    a = torch.randn(n, n, device="cuda").to(torch.bfloat16)
+    b = torch.randn(n, n, device="cuda").to(torch.bfloat16)
+    c = torch.mm(a, b)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        c = torch.mm(a, b)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    del a, b, c
+    return {"value": 2.0 * n ** 3 * reps / dt / 1e12, "unit": "TFLOP/s", "shape": [n, n, n], "dtype": "bf16",
+            "via": "torch.mm"}
 
 
 def calibrate_copy(mb):
@@ -367,7 +385,16 @@ def main():
                  "instrumented_ms_per_step": span_ms / args.steps},
         "cpu_baseline": None,
     }
+    # secondary figure: the chunked form's MFMA work in the sweep against the dense bf16 peak
+    C = w.chunk
+    chunk_flop = 2 * (2 * w.L * C * w.dk + (w.L - 1) * C * w.dv + C * w.dv + C * w.dk + 2 * w.dk * w.dv
+                      + w.L * C * w.dv + w.L * w.dk * w.dv)
+    mfma_achieved = w.pairs * w.T * chunk_flop / (sweep_ms * 1e-3) / 1e12
+    out["roofline"]["mfma_secondary"] = {"achieved": mfma_achieved, "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                         "frac": mfma_achieved / MFMA_PEAK_TFLOPS,
+                                         "flop_per_token_head": chunk_flop}
     out["roofline"]["measured_copy"] = copy_bandwidth(torch)
+    out["roofline"]["measured_mfma"] = mfma_rate(torch)
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(w, x0)

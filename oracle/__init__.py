@@ -10,7 +10,7 @@ and runs the residual chain one refinement step at a time.  See
 ``oracle.prism`` for the definitions and the passages each one follows.
 """
 from .prism import (shortconv_anchor, residual_chain, token_step, forward,
-                    forward_pairs)
+                    forward_pairs, conv_tail, decode_step)
 
 __all__ = ["shortconv_anchor", "residual_chain", "token_step", "forward",
-           "forward_pairs"]
+           "forward_pairs", "conv_tail", "decode_step"]
