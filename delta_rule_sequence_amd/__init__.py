@@ -41,6 +41,10 @@ def load_library() -> ctypes.CDLL:
     lib.prism_fwd_seg.restype = ctypes.c_int
     lib.prism_fwd_timed.argtypes = fwd_args + [vp, vp]
     lib.prism_fwd_timed.restype = ctypes.c_int
+    lib.prism_fwd_state.argtypes = fwd_args[:17] + [fp, vp, vp, fp, vp, vp, sz, vp]
+    lib.prism_fwd_state.restype = ctypes.c_int
+    lib.prism_decode_step.argtypes = [vp, vp, vp, fp, fp, vp, fp, vp, fp, i, i, i, i, i, i, fp, vp, vp, vp]
+    lib.prism_decode_step.restype = ctypes.c_int
     lib.prism_fwd_workspace_bytes.argtypes = [i] * 8
     lib.prism_fwd_workspace_bytes.restype = sz
     lib.prism_fwd_seg_workspace_bytes.argtypes = [i] * 9
@@ -83,6 +87,100 @@ def workspace_bytes(B: int, H: int, T: int, dk: int, dv: int, L: int, chunk: int
 
 def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(named_vec, named_flt, shapes, dtype, dev):
+    """Device, contiguity, dtype and shape checks of the tensor arguments."""
+    import torch
+    for name, t in named_vec + named_flt:
+        if t is None:
+            raise PrismError(f"{name} is required")
+        if t.device != dev or not t.is_contiguous():
+            raise PrismError(f"{name} must be a contiguous tensor on {dev}")
+        if name in shapes and tuple(t.shape) != shapes[name]:
+            raise PrismError(f"{name} has shape {tuple(t.shape)}, expected {shapes[name]}")
+    for name, t in named_vec:
+        if t.dtype != dtype:
+            raise PrismError(f"{name} must have dtype {dtype}")
+    for name, t in named_flt:
+        if t.dtype != torch.float32:
+            raise PrismError(f"{name} must be float32")
+
+
+def fwd_state(q, k, v, g, beta, u=None, alpha=None, gamma=None, conv_w=None, L: int = 1, chunk: int = 64,
+              S0=None, conv_in=None, want_conv: bool = True, workspace=None, stream=None):
+    """o, S_final, conv_out = fwd_state(..., S0, conv_in): the forward continued from a state.
+
+    S0 [B,H,dk,dv] float32 (the S_final layout) and conv_in [B,H,3,dv] (the input dtype;
+    values of the three tokens before the first) are optional (zero when None).  conv_out
+    holds the values of the last three tokens of [conv_in; v] (None if want_conv is False);
+    (S_final, conv_out) continue the sequence in the next call.
+    """
+    import torch
+    lib = load_library()
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    dt = _dtype_code(q)
+    dev = q.device
+    if dev.type != "cuda":
+        raise PrismError("inputs must be on a GPU")
+    vec = [("q", q), ("k", k), ("v", v)] + ([("u", u), ("gamma", gamma)] if L > 1 else [])
+    flt = [("g", g), ("beta", beta)] + ([("alpha", alpha), ("conv_w", conv_w)] if L > 1 else [])
+    shapes = {"k": (B, H, T, dk), "v": (B, H, T, dv), "g": (B, H, T), "beta": (B, H, T),
+              "u": (B, H, T, L - 1, dk), "gamma": (B, H, T, L - 1, dv), "alpha": (B, H, T, L),
+              "conv_w": (H, 4, dv), "S0": (B, H, dk, dv), "conv_in": (B, H, 3, dv)}
+    _check(vec + ([("conv_in", conv_in)] if conv_in is not None else []),
+           flt + ([("S0", S0)] if S0 is not None else []), shapes, q.dtype, dev)
+    o = torch.empty((B, H, T, dv), dtype=q.dtype, device=dev)
+    S = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    conv_out = torch.empty((B, H, 3, dv), dtype=q.dtype, device=dev) if want_conv else None
+    need = max(1, workspace_bytes(B, H, T, dk, dv, L, chunk, dt))
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    s = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
+    st = lib.prism_fwd_state(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                             _ptr(u) if L > 1 else None, _ptr(alpha) if L > 1 else None,
+                             _ptr(gamma) if L > 1 else None, _ptr(conv_w) if L > 1 else None,
+                             B, H, T, dk, dv, L, chunk, dt, _ptr(S0), _ptr(conv_in),
+                             _ptr(o), _ptr(S), _ptr(conv_out),
+                             ctypes.c_void_p(workspace.data_ptr()), workspace.numel(), ctypes.c_void_p(s))
+    if st != 0:
+        raise PrismError(f"prism_fwd_state failed: {status_string(st)}")
+    return o, S, conv_out
+
+
+def decode_step(S, conv_state, q, k, v, g, beta, u=None, alpha=None, gamma=None, conv_w=None, L: int = 1,
+                stream=None):
+    """o = decode_step(S, conv_state, q, k, v, g, beta, u, alpha, gamma, conv_w, L).
+
+    One token for every (b, h) pair; S [B,H,dk,dv] float32 and conv_state [B,H,3,dv]
+    (input dtype) are updated in place.  q, k [B,H,dk]; v [B,H,dv]; g, beta [B,H];
+    u [B,H,L-1,dk]; alpha [B,H,L]; gamma [B,H,L-1,dv]; conv_w [H,4,dv].  Returns o [B,H,dv].
+    """
+    import torch
+    lib = load_library()
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = _dtype_code(q)
+    dev = q.device
+    if dev.type != "cuda":
+        raise PrismError("inputs must be on a GPU")
+    vec = [("q", q), ("k", k), ("v", v)] + ([("u", u), ("gamma", gamma), ("conv_state", conv_state)]
+                                            if L > 1 else ([("conv_state", conv_state)] if conv_state is not None else []))
+    flt = [("g", g), ("beta", beta), ("S", S)] + ([("alpha", alpha), ("conv_w", conv_w)] if L > 1 else [])
+    shapes = {"k": (B, H, dk), "v": (B, H, dv), "g": (B, H), "beta": (B, H), "u": (B, H, L - 1, dk),
+              "gamma": (B, H, L - 1, dv), "alpha": (B, H, L), "conv_w": (H, 4, dv), "S": (B, H, dk, dv),
+              "conv_state": (B, H, 3, dv)}
+    _check(vec, flt, shapes, q.dtype, dev)
+    o = torch.empty((B, H, dv), dtype=q.dtype, device=dev)
+    s = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
+    st = lib.prism_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                               _ptr(u) if L > 1 else None, _ptr(alpha) if L > 1 else None,
+                               _ptr(gamma) if L > 1 else None, _ptr(conv_w) if L > 1 else None,
+                               B, H, dk, dv, L, dt, _ptr(S), _ptr(conv_state), _ptr(o), ctypes.c_void_p(s))
+    if st != 0:
+        raise PrismError(f"prism_decode_step failed: {status_string(st)}")
+    return o
 
 
 def fwd(q, k, v, g, beta, u=None, alpha=None, gamma=None, conv_w=None, L: int = 1, chunk: int = 64,

@@ -9,6 +9,7 @@
 #include "prism_fast.h"
 #include "prism_kernels.h"
 #include "prism_sweep8.h"
+#include "prism_decode.h"
 
 namespace {
 
@@ -167,7 +168,8 @@ prism_status fwd_impl(const void* q, const void* k, const void* v, const float* 
                       const void* u, const float* alpha, const void* gamma, const float* conv_w,
                       int B, int H, int T, int dk, int dv, int L, int chunk, prism_dtype dt,
                       void* o, float* S_final, void* workspace, size_t workspace_bytes,
-                      int seg_chunks, hipEvent_t* ev, hipStream_t stream) {
+                      int seg_chunks, hipEvent_t* ev, hipStream_t stream,
+                      const float* S0 = nullptr, const void* conv_in = nullptr, void* conv_out = nullptr) {
   Plan pl;
   prism_status st = make_plan(B, H, T, dk, dv, L, chunk, dt, seg_chunks, &pl);
   if (st != PRISM_OK) return st;
@@ -179,6 +181,7 @@ prism_status fwd_impl(const void* q, const void* k, const void* v, const float* 
   a.q = q; a.k = k; a.v = v; a.u = u; a.gamma = gamma;
   a.g = g; a.beta = beta; a.alpha = alpha; a.conv_w = conv_w;
   a.o = o; a.S_final = S_final;
+  a.S0 = S0; a.conv_in = conv_in; a.conv_out = conv_out;
   a.Oloc = reinterpret_cast<float*>(ws + pl.off_oloc);
   a.Qhat = reinterpret_cast<float*>(ws + pl.off_qhat);
   a.Aagg = reinterpret_cast<float*>(ws + pl.off_aagg);
@@ -186,8 +189,26 @@ prism_status fwd_impl(const void* q, const void* k, const void* v, const float* 
   a.Hin = reinterpret_cast<float*>(ws + pl.off_hin);
   a.B = B; a.H = H; a.T = T; a.L = L;
   a.nch = pl.nch; a.seg_chunks = pl.seg_chunks; a.nseg = pl.nseg;
-  return dt == PRISM_BF16 ? dispatch<bf16_t>(dk, chunk, a, pl, ev, stream)
-                          : dispatch<float>(dk, chunk, a, pl, ev, stream);
+  st = dt == PRISM_BF16 ? dispatch<bf16_t>(dk, chunk, a, pl, ev, stream)
+                        : dispatch<float>(dk, chunk, a, pl, ev, stream);
+  if (st != PRISM_OK || conv_out == nullptr) return st;
+  // after the sweep, the only reader of conv_in, so conv_out may alias it
+  if (dt == PRISM_BF16)
+    hipLaunchKernelGGL((prism::conv_tail_kernel<bf16_t>), dim3(pl.P), dim3(128), 0, stream, a, dv);
+  else
+    hipLaunchKernelGGL((prism::conv_tail_kernel<float>), dim3(pl.P), dim3(128), 0, stream, a, dv);
+  return hipGetLastError() == hipSuccess ? PRISM_OK : PRISM_ERR_HIP;
+}
+
+template <class E>
+prism_status decode_dispatch(int d, const prism::DecodeArgs& a, int P, hipStream_t stream) {
+  switch (d) {
+    case 16: hipLaunchKernelGGL((prism::decode_kernel<E, 16>), dim3(P), dim3(256), 0, stream, a); break;
+    case 32: hipLaunchKernelGGL((prism::decode_kernel<E, 32>), dim3(P), dim3(256), 0, stream, a); break;
+    case 64: hipLaunchKernelGGL((prism::decode_kernel<E, 64>), dim3(P), dim3(256), 0, stream, a); break;
+    default: hipLaunchKernelGGL((prism::decode_kernel<E, 128>), dim3(P), dim3(256), 0, stream, a); break;
+  }
+  return hipGetLastError() == hipSuccess ? PRISM_OK : PRISM_ERR_HIP;
 }
 
 }  // namespace
@@ -221,6 +242,36 @@ prism_status prism_fwd_timed(const void* q, const void* k, const void* v, const 
   if (!events) return PRISM_ERR_INVALID_ARG;
   return fwd_impl(q, k, v, g, beta, u, alpha, gamma, conv_w, B, H, T, dk, dv, L, chunk, dt, o, S_final,
                   workspace, workspace_bytes, 0, events, stream);
+}
+
+prism_status prism_fwd_state(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                             const void* u, const float* alpha, const void* gamma, const float* conv_w,
+                             int B, int H, int T, int dk, int dv, int L, int chunk, prism_dtype dt,
+                             const float* S0, const void* conv_in,
+                             void* o, float* S_final, void* conv_out,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return fwd_impl(q, k, v, g, beta, u, alpha, gamma, conv_w, B, H, T, dk, dv, L, chunk, dt, o, S_final,
+                  workspace, workspace_bytes, 0, nullptr, stream, S0, conv_in, conv_out);
+}
+
+prism_status prism_decode_step(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                               const void* u, const float* alpha, const void* gamma, const float* conv_w,
+                               int B, int H, int dk, int dv, int L, prism_dtype dt,
+                               float* S, void* conv_state, void* o, hipStream_t stream) {
+  if (B <= 0 || H <= 0) return PRISM_ERR_INVALID_ARG;
+  if (!(dk == dv && (dk == 16 || dk == 32 || dk == 64 || dk == 128))) return PRISM_ERR_UNSUPPORTED;
+  if (L < 1 || L > 8 || (dt != PRISM_F32 && dt != PRISM_BF16)) return PRISM_ERR_UNSUPPORTED;
+  if (!q || !k || !v || !g || !beta || !S || !o) return PRISM_ERR_INVALID_ARG;
+  if (L > 1 && (!u || !alpha || !gamma || !conv_w || !conv_state)) return PRISM_ERR_INVALID_ARG;
+  size_t P;
+  if (!mul_ok((size_t)B, (size_t)H, &P) || P > 0x7fffffff) return PRISM_ERR_INVALID_ARG;
+  prism::DecodeArgs a;
+  a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
+  a.u = u; a.alpha = alpha; a.gamma = gamma; a.conv_w = conv_w;
+  a.S = S; a.conv_state = conv_state; a.o = o;
+  a.H = H; a.L = L;
+  return dt == PRISM_BF16 ? decode_dispatch<bf16_t>(dk, a, (int)P, stream)
+                          : decode_dispatch<float>(dk, a, (int)P, stream);
 }
 
 prism_status prism_fwd_seg(const void* q, const void* k, const void* v, const float* g, const float* beta,

@@ -102,8 +102,13 @@ __global__ __launch_bounds__(256) void seg_scan_fast_kernel(FwdArgs a) {
   PRISM_DECL(4) PRISM_DECL(5) PRISM_DECL(6) PRISM_DECL(7)
   PRISM_FETCH(0, 0) PRISM_FETCH(1, 1) PRISM_FETCH(2, 2) PRISM_FETCH(3, 3)
   PRISM_FETCH(4, 4) PRISM_FETCH(5, 5) PRISM_FETCH(6, 6) PRISM_FETCH(7, 7)
-  float h = 0.f;  // H_in(s)[orow][ocol]
-  if (tid < DK) sH[0][hrow(tid)] = make_float4(0.f, 0.f, 0.f, 0.f);
+  // H_in(s)[orow][ocol], from the starting state (zero unless given)
+  float h = a.S0 != nullptr ? a.S0[(size_t)pr * DK * DV + (size_t)orow * DV + ocol] : 0.f;
+  // the LDS copy of the four columns the products read: row tid of H_in(0)
+  if (tid < DK)
+    sH[0][hrow(tid)] = a.S0 != nullptr
+                           ? *reinterpret_cast<const float4*>(a.S0 + (size_t)pr * DK * DV + (size_t)tid * DV + c0)
+                           : make_float4(0.f, 0.f, 0.f, 0.f);
   __syncthreads();
   const bool lo4 = q < 4, lo2 = (q & 2) == 0, lo1 = (q & 1) == 0;
   int cur = 0;

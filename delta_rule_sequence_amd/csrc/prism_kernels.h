@@ -42,6 +42,9 @@ struct FwdArgs {
   const float* conv_w;
   void* o;
   float* S_final;
+  const float* S0;       // [P][dk][dv] starting state (the S_final layout), or null for zero
+  const void* conv_in;   // [P][3][dv] values of the 3 tokens before the sequence, or null
+  void* conv_out;        // [P][3][dv] values of the last 3 tokens of [conv_in; v], or null
   float* Oloc;   // [P][Tpad][dv]
   float* Qhat;   // [P][Tpad][dk]
   float* Aagg;   // [P][nseg][dk][dk]
@@ -209,6 +212,7 @@ __global__ __launch_bounds__(256, 1) void seg_local_kernel(FwdArgs a) {
         f32x4 vv = zero4(), rr = zero4();
         if (vt < VT) {
           const int col = 16 * vt + li;
+          const E* hist = a.conv_in != nullptr ? reinterpret_cast<const E*>(a.conv_in) + (size_t)pr * 3 * DV : nullptr;
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int t = 16 * mt + g4 + r;
@@ -222,6 +226,7 @@ __global__ __launch_bounds__(256, 1) void seg_local_kernel(FwdArgs a) {
                 for (int j = 0; j < 4; ++j) {
                   const int ts = tg - 3 + j;
                   if (ts >= 0) anc += cw[j * DV + col] * to_f(v[(size_t)ts * DV + col]);
+                  else if (hist != nullptr) anc += cw[j * DV + col] * to_f(hist[(ts + 3) * DV + col]);
                 }
                 rr[r] = x - anc;
               }
@@ -519,7 +524,9 @@ __global__ __launch_bounds__(256) void seg_scan_kernel(FwdArgs a) {
   __shared__ float sH[2][DK * 16];
   const int tid = threadIdx.x, pr = blockIdx.x, c0 = 16 * blockIdx.y;
   const int j = tid & 15;
-  for (int idx = tid; idx < DK * 16; idx += 256) sH[0][idx] = 0.f;
+  const float* S0 = a.S0 != nullptr ? a.S0 + (size_t)pr * DK * DV : nullptr;
+  for (int idx = tid; idx < DK * 16; idx += 256)
+    sH[0][idx] = S0 != nullptr ? S0[(idx >> 4) * DV + c0 + (idx & 15)] : 0.f;
   __syncthreads();
   int cur = 0;
   for (int s = 0; s < a.nseg; ++s) {

@@ -165,6 +165,8 @@ __device__ __forceinline__ void quad_store(const uint2* x, bf16_t* dst, bf16_t* 
 struct Sweep8Ctx {
   unsigned char* smem;
   rsrc_t rq_, rk_, rv_, ru_, rg_;  // buffers over the pair's q, k, v, u, gamma
+  rsrc_t rh_;                      // buffer over the pair's 3 value rows before the sequence
+  bool hist;                       // those rows are given (else they are zero)
   const float *gg, *bb, *al;       // the pair's g, beta, alpha
   float *oloc, *qhat_base, *agg;   // outputs of this pair / segment
   int T, L, Lm1, c_begin, c_end, Tpad, pr, nch;
@@ -597,6 +599,18 @@ __device__ __forceinline__ void sweep8_qwave(const Sweep8Ctx& x, int wq) {
 
   if (x.c_begin < x.c_end) {
     fetch_chunk(x.c_begin);
+    if (x.c_begin == 0 && x.hist) {
+      // the first chunk of the sequence: tokens -3 .. -1 of the anchor window come from the
+      // given history (block row rq = 0 holds tokens -4 .. -1; the other lanes read past
+      // the buffer, which returns zero, and keep their rows)
+      const int base = rq == 0 ? 2 * c4 : 4096;
+#pragma unroll
+      for (int j = 0; j < 3; ++j) {
+        const uint2 hv = bload8(x.rh_, base + j * 128);
+        pf[1 + j].x |= hv.x;
+        pf[1 + j].y |= hv.y;
+      }
+    }
     store_chunk();
   }
   for (int c = x.c_begin; c < x.c_end; ++c) {
@@ -784,6 +798,9 @@ __global__ __launch_bounds__(512, 1) void seg_sweep8_kernel(FwdArgs a) {
   x.ru_ = make_rsrc(L > 1 ? reinterpret_cast<const bf16_t*>(a.u) + pair_rows * Lm1 * D : a.q, L > 1 ? ubytes_all : 0u);
   x.rg_ = make_rsrc(L > 1 ? reinterpret_cast<const bf16_t*>(a.gamma) + pair_rows * Lm1 * D : a.q,
                     L > 1 ? ubytes_all : 0u);
+  x.hist = a.conv_in != nullptr;
+  x.rh_ = make_rsrc(x.hist ? reinterpret_cast<const bf16_t*>(a.conv_in) + (size_t)pr * 3 * D : a.q,
+                    x.hist ? 3u * D * 2u : 0u);
   x.gg = a.g + pair_rows;
   x.bb = a.beta + pair_rows;
   x.al = L > 1 ? a.alpha + pair_rows * L : nullptr;

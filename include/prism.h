@@ -1,9 +1,10 @@
 /*
  * prism.h - C ABI of the PRISM rank-L gated delta-rule forward on MI355X (gfx950).
  *
- * What is computed (per batch b and head h, state S_0 = 0, S is dv x dk):
+ * What is computed (per batch b and head h, state S_0 = 0 unless given, S is dv x dk):
  *
- *   anchor_t = sum_{j=0..3} conv_w[h, j, :] * v_{t-3+j}        (rows before t = 0 are 0)
+ *   anchor_t = sum_{j=0..3} conv_w[h, j, :] * v_{t-3+j}        (rows before t = 0 are 0,
+ *                                                               or given: prism_fwd_state)
  *   r_{t,0}  = v_t - anchor_t
  *   r_{t,l}  = r_{t,l-1} * (1 - alpha_{t,l-1} * gamma_{t,l-1})  (element-wise), l = 1..L-1
  *   A_t      = g_t (I - beta_t k_t k_t^T)
@@ -90,6 +91,47 @@ prism_status prism_fwd(const void* q, const void* k, const void* v,
                        int B, int H, int T, int dk, int dv, int L, int chunk, prism_dtype dt,
                        void* o, float* S_final,
                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* The forward pass continued from a given state, for streaming a long sequence in pieces
+ * (the fixed-size state is all the linear recurrence carries forward: Tencent Ads article,
+ * section 01-二; the ShortConv anchor looks three tokens back: "PRISM" reading notes,
+ * section 2.3).  Arguments as prism_fwd, plus:
+ *   S0       [B, H, dk, dv] float32: the state before the first token, in the S_final
+ *            layout (S_0^T); NULL = zero.  May be the same buffer as S_final.
+ *   conv_in  [B, H, 3, dv] dtype dt: the values of the three tokens before the first one
+ *            (oldest first), read by the anchor; NULL = zero (a sequence start).
+ *   conv_out [B, H, 3, dv] dtype dt, output: the values of the last three tokens of
+ *            [conv_in; v] (rows of conv_in when T < 3); NULL = not written.  May be the
+ *            same buffer as conv_in.
+ * Running T1 tokens and then T2 more from (S_final, conv_out) gives the same o and S_final
+ * as one call over T1 + T2 tokens, up to rounding.  Workspace: prism_fwd_workspace_bytes. */
+prism_status prism_fwd_state(const void* q, const void* k, const void* v,
+                             const float* g, const float* beta,
+                             const void* u, const float* alpha, const void* gamma,
+                             const float* conv_w,
+                             int B, int H, int T, int dk, int dv, int L, int chunk, prism_dtype dt,
+                             const float* S0, const void* conv_in,
+                             void* o, float* S_final, void* conv_out,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* One token for every (b, h) pair, in place: the token-at-a-time form of prism_fwd_state
+ * for generation and serving.  Layout (dense, row-major):
+ *   q, k  [B, H, dk]  dtype dt;   v [B, H, dv] dtype dt
+ *   g, beta [B, H] float32;       alpha [B, H, L] float32
+ *   u     [B, H, L-1, dk] dtype dt;   gamma [B, H, L-1, dv] dtype dt;   conv_w [H, 4, dv] float32
+ *   S           [B, H, dk, dv] float32, in / out: the state (the S_final layout)
+ *   conv_state  [B, H, 3, dv] dtype dt, in / out: values of the previous three tokens,
+ *               oldest first; the token's v is appended and the oldest row dropped.
+ *               Required when L > 1; may be NULL when L == 1 (the anchor is unused).
+ *   o     [B, H, dv] dtype dt, output.
+ * u, alpha, gamma, conv_w may be NULL when L == 1.  Supported: dk == dv in {16, 32, 64,
+ * 128}, 1 <= L <= 8.  No workspace.  Errors as prism_fwd (checked before any launch). */
+prism_status prism_decode_step(const void* q, const void* k, const void* v,
+                               const float* g, const float* beta,
+                               const void* u, const float* alpha, const void* gamma,
+                               const float* conv_w,
+                               int B, int H, int dk, int dv, int L, prism_dtype dt,
+                               float* S, void* conv_state, void* o, hipStream_t stream);
 
 /* Same as prism_fwd with an explicit segment length (in chunks, >= 1) for the
  * sequence-parallel split; results agree across segment lengths up to rounding.

@@ -199,6 +199,17 @@ def generate(w: Workload, seed: Optional[int] = None, keys: str = "iid") -> Dict
     return out
 
 
+def generate_state(w: Workload, seed: Optional[int] = None) -> Dict[str, np.ndarray]:
+    """A starting point for a continued sequence of workload `w`: S0 [B,H,dk,dv] float32
+    with N(0, 0.3^2) entries (the S_final layout) and conv_in [B,H,3,dv], values of the
+    three earlier tokens drawn like v (N(0,1), representable in the I/O dtype)."""
+    seed = (w.seed if seed is None else seed) + 1000
+    rng = np.random.default_rng(seed)
+    S0 = (0.3 * rng.standard_normal((w.B, w.H, w.dk, w.dv))).astype(np.float32)
+    conv_in = _cast_vec(rng.standard_normal((w.B, w.H, 3, w.dv)), w.dtype)
+    return {"S0": S0, "conv_in": conv_in}
+
+
 def manifest(inputs: Dict[str, np.ndarray]) -> Dict[str, str]:
     """SHA-256 of every tensor's bytes (generator determinism check)."""
     return {k: hashlib.sha256(np.ascontiguousarray(v).tobytes()).hexdigest()
@@ -216,7 +227,7 @@ def to_torch(inputs: Dict[str, np.ndarray], dtype: str, device="cuda"):
             out[key] = None
             continue
         t = torch.from_numpy(np.ascontiguousarray(val))
-        if key in ("q", "k", "v", "u", "gamma"):
+        if key in ("q", "k", "v", "u", "gamma", "conv_in"):
             t = t.to(device=device).to(vt)
         else:
             t = t.to(device=device, dtype=torch.float32)
