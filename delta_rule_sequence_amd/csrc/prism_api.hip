@@ -146,7 +146,7 @@ prism_status launch_fast(const FwdArgs& a, const Plan& pl, hipEvent_t* ev, hipSt
     default: hipLaunchKernelGGL((prism::seg_sweep8_kernel<64, 64, -1>), grid, block, 0, stream, a); break;
   }
   if (hipGetLastError() != hipSuccess || !record(ev, 1, stream)) return PRISM_ERR_HIP;
-  hipLaunchKernelGGL((prism::seg_scan_fast_kernel<64, 64>), dim3(pl.P, 64 / 4), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((prism::seg_scan_fast_kernel<64, 64>), dim3(pl.P, 64 / 2), dim3(256), 0, stream, a);
   if (hipGetLastError() != hipSuccess || !record(ev, 2, stream)) return PRISM_ERR_HIP;
   hipLaunchKernelGGL((prism::seg_fixup_fast_kernel<64, 64>), dim3(pl.nseg, pl.P), dim3(256), 0, stream, a);
   if (hipGetLastError() != hipSuccess || !record(ev, 3, stream)) return PRISM_ERR_HIP;

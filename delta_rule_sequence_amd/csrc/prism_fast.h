@@ -62,23 +62,23 @@ __device__ __forceinline__ float dpp_quad_swap(float x) {
 }
 
 // Inter-segment recurrence H_in(s+1) = A_s H_in(s) + B_s (float32); one workgroup per
-// (pair, 4 state columns c0 ..).  Thread t takes state rows i0 = 2 (t / 8), i0 + 1 and the
-// contraction slice k = 8 q .. 8 q + 7 (q = t % 8): it keeps those 16 entries of A_s in
-// registers (loaded DEPTH steps ahead, so a step never waits on memory), reads rows
-// 8 q .. 8 q + 7 of the four H_in(s) columns from LDS (skewed so the eight slices of a
-// wave hit distinct banks) and forms 2 x 4 partial sums; three DPP exchange rounds within
-// the 8 lanes of the row pair leave lane q with H_in(s+1)[i0 + q / 4][c0 + q % 4].  One
-// barrier per step.
+// (pair, 2 state columns c0 ..), 256 workgroups at 8 pairs.  Thread t takes state rows
+// i0 = 2 (t / 8), i0 + 1 and the contraction slice k = 8 q .. 8 q + 7 (q = t % 8): it keeps
+// those 16 entries of A_s in registers (loaded DEPTH steps ahead, so a step never waits on
+// memory), reads rows 8 q .. 8 q + 7 of the two H_in(s) columns from LDS (skewed so the
+// eight slices of a wave hit distinct banks) and forms 2 x 2 partial sums; three DPP
+// exchange rounds within the 8 lanes of the row pair leave lanes q and q ^ 1 with
+// H_in(s+1)[i0 + q / 4][c0 + (q / 2) % 2].  One barrier per step.
 template <int DK, int DV>
 __global__ __launch_bounds__(256) void seg_scan_fast_kernel(FwdArgs a) {
   static_assert(DK == 64, "the row-pair / k-slice split assumes 64 state rows");
   constexpr int DEPTH = 8;
   constexpr int HS = DK + DK / 8;  // H rows with a one-row skew every 8 rows
-  __shared__ __align__(16) float4 sH[2][HS];
+  __shared__ __align__(16) float2 sH[2][HS];
   const int tid = threadIdx.x, i0 = 2 * (tid >> 3), q = tid & 7;
-  const int pr = blockIdx.x, c0 = 4 * blockIdx.y;
+  const int pr = blockIdx.x, c0 = 2 * blockIdx.y;
   const int nseg = a.nseg;
-  const int orow = i0 + (q >> 2), ocol = c0 + (q & 3);  // the output this lane ends with
+  const int orow = i0 + (q >> 2), ocol = c0 + ((q >> 1) & 1);  // the output this lane ends with (lanes q, q ^ 1)
   const float* A0 = a.Aagg + (size_t)pr * nseg * DK * DK + (size_t)i0 * DK + 8 * q;
   const float* B0 = a.Bagg + (size_t)pr * nseg * DK * DV + (size_t)orow * DV + ocol;
   // H_in(s) for the output correction: bfloat16, transposed ([column][row], the layout
@@ -107,10 +107,10 @@ __global__ __launch_bounds__(256) void seg_scan_fast_kernel(FwdArgs a) {
   // the LDS copy of the four columns the products read: row tid of H_in(0)
   if (tid < DK)
     sH[0][hrow(tid)] = a.S0 != nullptr
-                           ? *reinterpret_cast<const float4*>(a.S0 + (size_t)pr * DK * DV + (size_t)tid * DV + c0)
-                           : make_float4(0.f, 0.f, 0.f, 0.f);
+                           ? *reinterpret_cast<const float2*>(a.S0 + (size_t)pr * DK * DV + (size_t)tid * DV + c0)
+                           : make_float2(0.f, 0.f);
   __syncthreads();
-  const bool lo4 = q < 4, lo2 = (q & 2) == 0, lo1 = (q & 1) == 0;
+  const bool lo4 = q < 4, lo2 = (q & 2) == 0;
   int cur = 0;
 #define PRISM_SCAN_STEP(D, PREFETCH)                                                          \
   {                                                                                           \
@@ -121,28 +121,23 @@ __global__ __launch_bounds__(256) void seg_scan_fast_kernel(FwdArgs a) {
     const float ar1[8] = {R##D##_2.x, R##D##_2.y, R##D##_2.z, R##D##_2.w,                     \
                           R##D##_3.x, R##D##_3.y, R##D##_3.z, R##D##_3.w};                    \
     const float bv = R##D##_b;                                                                \
-    float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}; /* [row][col] */                   \
+    float v[4] = {0.f, 0.f, 0.f, 0.f}; /* [row][col] */                                       \
     _Pragma("unroll") for (int m = 0; m < 8; ++m) {                                           \
-      const float4 hv = sH[cur][hrow(8 * q + m)];                                             \
+      const float2 hv = sH[cur][hrow(8 * q + m)];                                             \
       v[0] += ar0[m] * hv.x;                                                                  \
       v[1] += ar0[m] * hv.y;                                                                  \
-      v[2] += ar0[m] * hv.z;                                                                  \
-      v[3] += ar0[m] * hv.w;                                                                  \
-      v[4] += ar1[m] * hv.x;                                                                  \
-      v[5] += ar1[m] * hv.y;                                                                  \
-      v[6] += ar1[m] * hv.z;                                                                  \
-      v[7] += ar1[m] * hv.w;                                                                  \
+      v[2] += ar1[m] * hv.x;                                                                  \
+      v[3] += ar1[m] * hv.y;                                                                  \
     }                                                                                         \
     /* refill the slot after the products: the loads queue while the exchanges run */         \
     if (PREFETCH) PRISM_FETCH(D, s + DEPTH)                                                   \
     /* keep row q / 4, then columns (q & 2) .., then column q & 3 */                          \
-    float n4[4], n2[2];                                                                       \
-    _Pragma("unroll") for (int j = 0; j < 4; ++j)                                             \
-      n4[j] = (lo4 ? v[j] : v[4 + j]) + dpp_half_mirror(lo4 ? v[4 + j] : v[j]);               \
+    float n2[2];                                                                              \
     _Pragma("unroll") for (int j = 0; j < 2; ++j)                                             \
-      n2[j] = (lo2 ? n4[j] : n4[2 + j]) + dpp_quad_rev(lo2 ? n4[2 + j] : n4[j]);              \
-    h = (lo1 ? n2[0] : n2[1]) + dpp_quad_swap(lo1 ? n2[1] : n2[0]) + bv;                       \
-    reinterpret_cast<float*>(&sH[cur ^ 1][hrow(orow)])[q & 3] = h;                            \
+      n2[j] = (lo4 ? v[j] : v[2 + j]) + dpp_half_mirror(lo4 ? v[2 + j] : v[j]);               \
+    const float n1 = (lo2 ? n2[0] : n2[1]) + dpp_quad_rev(lo2 ? n2[1] : n2[0]);               \
+    h = n1 + dpp_quad_swap(n1) + bv;                                                          \
+    reinterpret_cast<float*>(&sH[cur ^ 1][hrow(orow)])[(q >> 1) & 1] = h;                     \
     cur ^= 1;                                                                                 \
     __syncthreads();                                                                          \
   }
