@@ -314,6 +314,52 @@ def l_sweep(steps, warmup):
                               w.B * w.T * HBM_PEAK_GBS * 1e9 / (w.pairs * w.T * path_bytes)}), flush=True)
 
 
+def decode_bench(steps, warmup, batch):
+    """One-token decode steps (prism_decode_step) at the 16K workload's head shape (H = 4,
+    d = 64, L = 4, bf16) for `batch` sequences: the float32 state (batch x 4 x 16 KB) is
+    read and written once per step, so the step is HBM-bound once the state exceeds the
+    256 MB Infinity Cache.  One JSON line: tokens/s (one token per sequence per step) and
+    the step's algorithmic bytes against the HBM peak."""
+    import torch
+    import workloads
+    import delta_rule_sequence_amd as prism
+    base = workloads.workload("rec16k_bf16")
+    w = base.replace(B=batch, T=steps + warmup, name=f"decode_b{batch}")
+    x = workloads.to_torch(workloads.generate(w, seed=w.seed), w.dtype)
+    st = workloads.to_torch(workloads.generate_state(w), w.dtype)
+    S, conv = st["S0"], st["conv_in"]
+    per_step = []
+    for t in range(w.T):
+        per_step.append({k: (x[k][:, :, t].contiguous() if x[k] is not None and k != "conv_w" else x[k])
+                         for k in ("q", "k", "v", "g", "beta", "u", "alpha", "gamma")})
+    del x["q"], x["k"], x["v"], x["u"], x["gamma"]
+
+    def step(t):
+        d = per_step[t]
+        prism.decode_step(S, conv, d["q"], d["k"], d["v"], d["g"], d["beta"], d["u"], d["alpha"], d["gamma"],
+                          x["conv_w"], L=w.L)
+
+    for t in range(warmup):
+        step(t)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for t in range(warmup, warmup + steps):
+        step(t)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    P, d, L, E = w.B * w.H, w.dk, w.L, 2
+    step_bytes = P * (2 * d * d * 4                          # state read + write
+                      + 2 * 3 * d * E                        # window read + write
+                      + (3 * d + 2 * (L - 1) * d) * E        # q, k, v, u, gamma
+                      + (2 + L) * 4                          # g, beta, alpha
+                      + d * E)                               # o
+    print(json.dumps({"metric": "decode tokens/sec (prism_decode_step), H=4, d=64, L=4, bf16",
+                      "batch": w.B, "steps": steps, "warmup": warmup, "ms_per_step": dt * 1e3,
+                      "tokens_per_s": w.B / dt, "state_bytes": P * d * d * 4,
+                      "achieved_GBs": step_bytes / dt / 1e9, "peak_GBs": HBM_PEAK_GBS,
+                      "frac": step_bytes / dt / 1e9 / HBM_PEAK_GBS}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -325,6 +371,8 @@ def main():
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MB")
     ap.add_argument("--l-sweep", action="store_true",
                     help="time the 16K shape at L = 1, 2, 4, 8 (one JSON line each) instead")
+    ap.add_argument("--decode", type=int, default=0, metavar="BATCH",
+                    help="time one-token decode steps for BATCH sequences instead")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -337,6 +385,9 @@ def main():
         return
     if args.l_sweep:
         l_sweep(args.steps, args.warmup)
+        return
+    if args.decode:
+        decode_bench(args.steps, args.warmup, args.decode)
         return
 
     import workloads
