@@ -103,3 +103,57 @@ def test_python_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(prism, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(prism.PrismError):
         prism.load_library()
+
+
+def _call_state(lib, B=1, H=1, T=64, d=16, L=2, chunk=16, dt=1, null=(), ws_bytes=1 << 30):
+    p = ctypes.c_void_p(1)
+    args = {n: p for n in ["q", "k", "v", "g", "beta", "u", "alpha", "gamma", "conv_w", "S0", "cin",
+                           "o", "S", "cout", "ws"]}
+    for n in null:
+        args[n] = None
+    return lib.prism_fwd_state(args["q"], args["k"], args["v"], args["g"], args["beta"], args["u"],
+                               args["alpha"], args["gamma"], args["conv_w"], B, H, T, d, d, L, chunk, dt,
+                               args["S0"], args["cin"], args["o"], args["S"], args["cout"], args["ws"],
+                               ws_bytes, None)
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "g", "beta", "o", "S"])
+def test_fwd_state_null_required_pointer(lib, name):
+    assert _call_state(lib, null=(name,)) == INVALID
+
+
+def test_fwd_state_argument_checks(lib):
+    assert _call_state(lib, T=0) == INVALID
+    assert _call_state(lib, d=48) == UNSUPPORTED
+    assert _call_state(lib, L=9) == UNSUPPORTED
+    assert _call_state(lib, L=3, null=("conv_w",)) == INVALID
+    assert _call_state(lib, ws_bytes=16) == WORKSPACE
+
+
+def _call_decode(lib, B=1, H=1, dk=16, dv=16, L=2, dt=1, null=()):
+    p = ctypes.c_void_p(1)
+    args = {n: p for n in ["q", "k", "v", "g", "beta", "u", "alpha", "gamma", "conv_w", "S", "cs", "o"]}
+    for n in null:
+        args[n] = None
+    return lib.prism_decode_step(args["q"], args["k"], args["v"], args["g"], args["beta"], args["u"],
+                                 args["alpha"], args["gamma"], args["conv_w"], B, H, dk, dv, L, dt,
+                                 args["S"], args["cs"], args["o"], None)
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "g", "beta", "S", "o"])
+def test_decode_null_required_pointer(lib, name):
+    assert _call_decode(lib, null=(name,)) == INVALID
+
+
+@pytest.mark.parametrize("name", ["u", "alpha", "gamma", "conv_w", "cs"])
+def test_decode_null_rank_pointer_when_L_gt_1(lib, name):
+    assert _call_decode(lib, L=3, null=(name,)) == INVALID
+
+
+def test_decode_argument_checks(lib):
+    assert _call_decode(lib, B=0) == INVALID
+    assert _call_decode(lib, dk=32, dv=16) == UNSUPPORTED
+    assert _call_decode(lib, dk=48, dv=48) == UNSUPPORTED
+    assert _call_decode(lib, L=0) == UNSUPPORTED
+    assert _call_decode(lib, L=9) == UNSUPPORTED
+    assert _call_decode(lib, dt=7) == UNSUPPORTED
