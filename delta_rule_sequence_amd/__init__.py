@@ -45,6 +45,10 @@ def load_library() -> ctypes.CDLL:
     lib.prism_fwd_state.restype = ctypes.c_int
     lib.prism_decode_step.argtypes = [vp, vp, vp, fp, fp, vp, fp, vp, fp, i, i, i, i, i, i, fp, vp, vp, vp]
     lib.prism_decode_step.restype = ctypes.c_int
+    lib.prism_bwd.argtypes = fwd_args[:9] + [i] * 7 + [vp, fp] + [fp] * 9 + [vp, sz, vp]
+    lib.prism_bwd.restype = ctypes.c_int
+    lib.prism_bwd_workspace_bytes.argtypes = [i] * 7
+    lib.prism_bwd_workspace_bytes.restype = sz
     lib.prism_fwd_workspace_bytes.argtypes = [i] * 8
     lib.prism_fwd_workspace_bytes.restype = sz
     lib.prism_fwd_seg_workspace_bytes.argtypes = [i] * 9
@@ -244,3 +248,52 @@ def fwd(q, k, v, g, beta, u=None, alpha=None, gamma=None, conv_w=None, L: int = 
     if st != 0:
         raise PrismError(f"prism_fwd failed: {status_string(st)}")
     return o, S
+
+
+def bwd(q, k, v, g, beta, u=None, alpha=None, gamma=None, conv_w=None, L: int = 1, d_o=None,
+        dS_final=None, workspace=None, stream=None):
+    """Gradients of sum <d_o, o> + <dS_final, S_final> for fwd(q, ..., conv_w, L) (zero start).
+
+    Inputs as fwd(); d_o [B,H,T,dv] in the input dtype; dS_final [B,H,dk,dv] float32 or None.
+    Returns a dict of float32 tensors dq, dk, dv, dg, dbeta and, when L > 1, du, dalpha,
+    dgamma, dconv_w (the shapes of the corresponding inputs; dconv_w summed over the batch).
+    """
+    import torch
+    lib = load_library()
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    dt = _dtype_code(q)
+    dev = q.device
+    if dev.type != "cuda":
+        raise PrismError("inputs must be on a GPU")
+    if d_o is None:
+        raise PrismError("d_o is required")
+    vec = [("q", q), ("k", k), ("v", v), ("d_o", d_o)] + ([("u", u), ("gamma", gamma)] if L > 1 else [])
+    flt = [("g", g), ("beta", beta)] + ([("alpha", alpha), ("conv_w", conv_w)] if L > 1 else []) + \
+        ([("dS_final", dS_final)] if dS_final is not None else [])
+    shapes = {"k": (B, H, T, dk), "v": (B, H, T, dv), "d_o": (B, H, T, dv), "g": (B, H, T), "beta": (B, H, T),
+              "u": (B, H, T, L - 1, dk), "gamma": (B, H, T, L - 1, dv), "alpha": (B, H, T, L),
+              "conv_w": (H, 4, dv), "dS_final": (B, H, dk, dv)}
+    _check(vec, flt, shapes, q.dtype, dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    out = {"dq": torch.empty((B, H, T, dk), **f32), "dk": torch.empty((B, H, T, dk), **f32),
+           "dv": torch.empty((B, H, T, dv), **f32), "dg": torch.empty((B, H, T), **f32),
+           "dbeta": torch.empty((B, H, T), **f32)}
+    if L > 1:
+        out.update({"du": torch.empty((B, H, T, L - 1, dk), **f32), "dalpha": torch.empty((B, H, T, L), **f32),
+                    "dgamma": torch.empty((B, H, T, L - 1, dv), **f32), "dconv_w": torch.empty((H, 4, dv), **f32)})
+    need = lib.prism_bwd_workspace_bytes(B, H, T, dk, dv, L, dt) or 1
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    s = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
+    st = lib.prism_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                       _ptr(u) if L > 1 else None, _ptr(alpha) if L > 1 else None,
+                       _ptr(gamma) if L > 1 else None, _ptr(conv_w) if L > 1 else None,
+                       B, H, T, dk, dv, L, dt, _ptr(d_o), _ptr(dS_final),
+                       _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]), _ptr(out["dbeta"]),
+                       _ptr(out.get("du")), _ptr(out.get("dalpha")), _ptr(out.get("dgamma")),
+                       _ptr(out.get("dconv_w")),
+                       ctypes.c_void_p(workspace.data_ptr()), workspace.numel(), ctypes.c_void_p(s))
+    if st != 0:
+        raise PrismError(f"prism_bwd failed: {status_string(st)}")
+    return out

@@ -10,6 +10,7 @@
 #include "prism_kernels.h"
 #include "prism_sweep8.h"
 #include "prism_decode.h"
+#include "prism_bwd.h"
 
 namespace {
 
@@ -211,9 +212,89 @@ prism_status decode_dispatch(int d, const prism::DecodeArgs& a, int P, hipStream
   return hipGetLastError() == hipSuccess ? PRISM_OK : PRISM_ERR_HIP;
 }
 
+// Workspace of the backward: checkpoints [P][nblk][D*D], block states [P][64][D*D] and
+// per-pair dconv_w shares [P][4][D], all float32, 256-byte aligned regions.
+struct BwdPlan {
+  int P, nblk;
+  size_t off_ckpt, off_scr, off_part, total;
+};
+
+prism_status make_bwd_plan(int B, int H, int T, int dk, int dv, int L, prism_dtype dt, BwdPlan* pl) {
+  if (B <= 0 || H <= 0 || T <= 0) return PRISM_ERR_INVALID_ARG;
+  if (dt != PRISM_F32 && dt != PRISM_BF16) return PRISM_ERR_INVALID_ARG;
+  if (L < 1 || L > 8) return PRISM_ERR_UNSUPPORTED;
+  if (!valid_dim(dk) || dk != dv) return PRISM_ERR_UNSUPPORTED;
+  size_t P, a, b, c, sz_ckpt, sz_scr, sz_part;
+  if (!mul_ok((size_t)B, (size_t)H, &P) || P > (size_t)INT32_MAX) return PRISM_ERR_INVALID_ARG;
+  const size_t nblk = ((size_t)T + prism::kBwdBlock - 1) / prism::kBwdBlock;
+  const size_t dd = (size_t)dk * dk * 4;
+  if (!mul_ok(P, nblk, &a) || !mul_ok(a, dd, &sz_ckpt)) return PRISM_ERR_INVALID_ARG;
+  if (!mul_ok(P, (size_t)prism::kBwdBlock, &b) || !mul_ok(b, dd, &sz_scr)) return PRISM_ERR_INVALID_ARG;
+  if (!mul_ok(P, (size_t)4 * dk * 4, &sz_part)) return PRISM_ERR_INVALID_ARG;
+  // inputs must be addressable: P*T*(L-1)*dk elements
+  if (!mul_ok(P, (size_t)T, &c) || !mul_ok(c, (size_t)L * dk * 4, &c)) return PRISM_ERR_INVALID_ARG;
+  pl->P = (int)P;
+  pl->nblk = (int)nblk;
+  pl->off_ckpt = 0;
+  pl->off_scr = align_up(sz_ckpt);
+  pl->off_part = align_up(pl->off_scr + sz_scr);
+  pl->total = align_up(pl->off_part + sz_part);
+  if (pl->total < sz_ckpt) return PRISM_ERR_INVALID_ARG;
+  return PRISM_OK;
+}
+
+template <class E>
+prism_status bwd_dispatch(int d, const prism::BwdArgs& a, int P, hipStream_t stream) {
+  switch (d) {
+    case 16: hipLaunchKernelGGL((prism::bwd_pair_kernel<E, 16>), dim3(P), dim3(256), 0, stream, a); break;
+    case 32: hipLaunchKernelGGL((prism::bwd_pair_kernel<E, 32>), dim3(P), dim3(256), 0, stream, a); break;
+    case 64: hipLaunchKernelGGL((prism::bwd_pair_kernel<E, 64>), dim3(P), dim3(256), 0, stream, a); break;
+    default: hipLaunchKernelGGL((prism::bwd_pair_kernel<E, 128>), dim3(P), dim3(256), 0, stream, a); break;
+  }
+  return hipGetLastError() == hipSuccess ? PRISM_OK : PRISM_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t prism_bwd_workspace_bytes(int B, int H, int T, int dk, int dv, int L, prism_dtype dt) {
+  BwdPlan pl;
+  return make_bwd_plan(B, H, T, dk, dv, L, dt, &pl) == PRISM_OK ? pl.total : 0;
+}
+
+prism_status prism_bwd(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                       const void* u, const float* alpha, const void* gamma, const float* conv_w,
+                       int B, int H, int T, int dk, int dv, int L, prism_dtype dt,
+                       const void* d_o, const float* dS_final,
+                       float* dq, float* dk_out, float* dv_out, float* dg, float* dbeta,
+                       float* du, float* dalpha, float* dgamma, float* dconv_w,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  BwdPlan pl;
+  prism_status st = make_bwd_plan(B, H, T, dk, dv, L, dt, &pl);
+  if (st != PRISM_OK) return st;
+  if (!q || !k || !v || !g || !beta || !d_o || !dq || !dk_out || !dv_out || !dg || !dbeta)
+    return PRISM_ERR_INVALID_ARG;
+  if (L > 1 && (!u || !alpha || !gamma || !conv_w || !du || !dalpha || !dgamma || !dconv_w))
+    return PRISM_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < pl.total) return PRISM_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  prism::BwdArgs a;
+  a.q = q; a.k = k; a.v = v; a.u = u; a.gamma = gamma; a.d_o = d_o;
+  a.g = g; a.beta = beta; a.alpha = alpha; a.conv_w = conv_w; a.dS_final = dS_final;
+  a.dq = dq; a.dk = dk_out; a.dv = dv_out; a.dg = dg; a.dbeta = dbeta;
+  a.du = du; a.dalpha = dalpha; a.dgamma = dgamma;
+  a.ckpt = reinterpret_cast<float*>(ws + pl.off_ckpt);
+  a.scratch = reinterpret_cast<float*>(ws + pl.off_scr);
+  a.dconv_part = reinterpret_cast<float*>(ws + pl.off_part);
+  a.H = H; a.T = T; a.L = L; a.nblk = pl.nblk;
+  st = dt == PRISM_BF16 ? bwd_dispatch<bf16_t>(dk, a, pl.P, stream) : bwd_dispatch<float>(dk, a, pl.P, stream);
+  if (st != PRISM_OK || L == 1) return st;
+  hipLaunchKernelGGL(prism::bwd_conv_reduce_kernel, dim3(H), dim3(256), 0, stream,
+                     static_cast<const float*>(a.dconv_part), dconv_w, B, H, dk);
+  return hipGetLastError() == hipSuccess ? PRISM_OK : PRISM_ERR_HIP;
+}
+
 
 size_t prism_fwd_workspace_bytes(int B, int H, int T, int dk, int dv, int L, int chunk, prism_dtype dt) {
   Plan pl;

@@ -1,0 +1,403 @@
+// prism_bwd.h - gradients of the PRISM rank-L gated delta-rule forward (gfx950).
+//
+// The forward, per (b, h) pair with S_0 = 0 (S is dv x dk):
+//   anchor_t = sum_j w_j v_{t-3+j};  r_{t,0} = v_t - anchor_t;
+//   r_{t,l} = r_{t,l-1} (1 - alpha_{t,l-1} gamma_{t,l-1});  W_{t,l} = alpha_{t,l} r_{t,l}
+//   S_t = g_t (S_{t-1} - beta_t (S_{t-1} k_t) k_t^T) + beta_t v_t k_t^T + sum_l W_{t,l} u_{t,l}^T
+//   o_t = S_t q_t
+// (PRISM reading notes, sections 2.1-2.3; Tencent / PKU article, sections 01-四 and 03-三).
+// The pages train the layer end to end (their throughput figures are training
+// throughput, reading notes section 3.3); this is the reverse-mode derivative of that
+// recurrence, token by token, in float32:
+//   dS_t += do_t q_t^T;  dq_t = S_t^T do_t;  p = S_{t-1} k_t;  e = dS_t k_t
+//   dk_t = dS_t^T (beta v_t - g beta p) - g beta S_{t-1}^T e
+//   dv_t = beta e + (1 - w_3) dr_0 + later tokens' anchor terms;  du_{t,l} = dS_t^T W_{t,l}
+//   dg_t = <dS_t, S_{t-1}> - beta p.e;  dbeta_t = e.(v_t - g p)
+//   dW_{t,l} = dS_t u_{t,l}, then back through the residual chain to alpha, gamma, v, w
+//   dS_{t-1} = g (dS_t - beta e k_t^T)
+//
+// One workgroup of 256 threads per pair; thread (rb, cb) = (tid / 16, tid % 16) owns the
+// R x R block (R = D / 16) of rows rb R .. and columns cb R .. of S and dS.  Sums over a row
+// run through the 16 lanes of the thread's row group (shuffles); sums over a column
+// through lanes 16 apart within the wave and then the four waves (one LDS exchange,
+// double-buffered, one barrier per token).  Pass 1 runs the forward and keeps the state
+// entering every block of kBwdBlock tokens; pass 2 walks the blocks backwards, re-runs
+// each block's forward into a per-pair scratch (every thread reads back only what it
+// wrote itself) and then the adjoint steps of the block in reverse order.
+#pragma once
+#include "prism_tile.h"
+
+namespace prism {
+
+constexpr int kBwdBlock = 64;  // tokens between state checkpoints
+constexpr int kBwdMaxRank = 7;  // L - 1 <= 7
+
+struct BwdArgs {
+  const void *q, *k, *v, *u, *gamma, *d_o;
+  const float *g, *beta, *alpha, *conv_w, *dS_final;
+  float *dq, *dk, *dv, *dg, *dbeta, *du, *dalpha, *dgamma;
+  float* dconv_part;  // [P][4][D] this pair's share of dconv_w
+  float* ckpt;        // [P][nblk][D * D] state entering each block (thread-block order)
+  float* scratch;     // [P][kBwdBlock][D * D] states S_t of the block being reversed
+  int H, T, L, nblk;
+};
+
+// One token's inputs as seen by thread (rb, cb): key-side entries of its columns,
+// value-side entries of its rows.
+template <int R>
+struct BwdTok {
+  float k[R], q[R], u[kBwdMaxRank][R];
+  float v[R], dO[R], gm[kBwdMaxRank][R], vh[3][R];  // vh: v_{t-3}, v_{t-2}, v_{t-1}
+  float g, beta, al[kBwdMaxRank + 1];
+};
+
+template <int R>
+__device__ __forceinline__ void sum_row_group(float (&x)[R]) {
+#pragma unroll
+  for (int a = 0; a < R; ++a) {
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) x[a] += __shfl_xor(x[a], m);
+  }
+}
+
+template <int R>
+__device__ __forceinline__ void store_block(float* dst, const float (&M)[R][R]) {
+  const int tid = threadIdx.x;
+  if constexpr ((R * R) % 4 == 0) {
+#pragma unroll
+    for (int e = 0; e < R * R; e += 4) {
+      const float4 x = make_float4(M[e / R][e % R], M[(e + 1) / R][(e + 1) % R], M[(e + 2) / R][(e + 2) % R],
+                                   M[(e + 3) / R][(e + 3) % R]);
+      *reinterpret_cast<float4*>(dst + (size_t)tid * R * R + e) = x;
+    }
+  } else {
+    dst[tid] = M[0][0];
+  }
+}
+
+template <int R>
+__device__ __forceinline__ void load_block(float (&M)[R][R], const float* src) {
+  const int tid = threadIdx.x;
+  if constexpr ((R * R) % 4 == 0) {
+#pragma unroll
+    for (int e = 0; e < R * R; e += 4) {
+      const float4 x = *reinterpret_cast<const float4*>(src + (size_t)tid * R * R + e);
+      M[e / R][e % R] = x.x;
+      M[(e + 1) / R][(e + 1) % R] = x.y;
+      M[(e + 2) / R][(e + 2) % R] = x.z;
+      M[(e + 3) / R][(e + 3) % R] = x.w;
+    }
+  } else {
+    M[0][0] = src[tid];
+  }
+}
+
+template <class E, int D>
+__global__ __launch_bounds__(256) void bwd_pair_kernel(BwdArgs a) {
+  constexpr int R = D / 16, CK = kBwdBlock, NR = kBwdMaxRank;
+  constexpr int NV = 2 + NR, NS = 2 + NR + 1;  // column vectors (dq, dk, du_l) and scalars (dg, dbeta, dalpha_l)
+  constexpr int RED = NV * D + NS;
+  __shared__ float red[2][4][RED];
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int rb = tid >> 4, cb = tid & 15;
+  const int pr = blockIdx.x, hd = pr % a.H;
+  const int T = a.T, L = a.L, Lm1 = L - 1;
+  const E* Q = reinterpret_cast<const E*>(a.q);
+  const E* K = reinterpret_cast<const E*>(a.k);
+  const E* V = reinterpret_cast<const E*>(a.v);
+  const E* U = reinterpret_cast<const E*>(a.u);
+  const E* GM = reinterpret_cast<const E*>(a.gamma);
+  const E* DO = reinterpret_cast<const E*>(a.d_o);
+  float* ckpt = a.ckpt + (size_t)pr * a.nblk * D * D;
+  float* scr = a.scratch + (size_t)pr * CK * D * D;
+
+  float tw[4][R];  // conv taps of this thread's rows
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int r = 0; r < R; ++r) tw[j][r] = L > 1 ? a.conv_w[((size_t)hd * 4 + j) * D + rb * R + r] : 0.f;
+
+  auto load_tok = [&](int t, BwdTok<R>& x) {
+    const size_t tr = (size_t)pr * T + t;
+#pragma unroll
+    for (int c = 0; c < R; ++c) {
+      x.k[c] = (float)K[tr * D + cb * R + c];
+      x.q[c] = (float)Q[tr * D + cb * R + c];
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      x.v[r] = (float)V[tr * D + rb * R + r];
+      x.dO[r] = (float)DO[tr * D + rb * R + r];
+#pragma unroll
+      for (int j = 0; j < 3; ++j) x.vh[j][r] = t - 3 + j >= 0 ? (float)V[(tr - 3 + j) * D + rb * R + r] : 0.f;
+    }
+    x.g = a.g[tr];
+    x.beta = a.beta[tr];
+#pragma unroll
+    for (int l = 0; l < NR; ++l) {
+      if (l < Lm1) {
+#pragma unroll
+        for (int c = 0; c < R; ++c) x.u[l][c] = (float)U[(tr * Lm1 + l) * D + cb * R + c];
+#pragma unroll
+        for (int r = 0; r < R; ++r) x.gm[l][r] = (float)GM[(tr * Lm1 + l) * D + rb * R + r];
+      }
+    }
+#pragma unroll
+    for (int l = 0; l <= NR; ++l) x.al[l] = (L > 1 && l < L) ? a.alpha[tr * L + l] : 0.f;
+  };
+  // residuals r_{t,0..L-1} and written values W_{t,1..L-1} of this thread's rows
+  auto chain = [&](const BwdTok<R>& x, float (&rr)[NR + 1][R], float (&W)[NR][R]) {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      rr[0][r] = x.v[r] - (tw[0][r] * x.vh[0][r] + tw[1][r] * x.vh[1][r] + tw[2][r] * x.vh[2][r] + tw[3][r] * x.v[r]);
+#pragma unroll
+    for (int l = 1; l <= NR; ++l) {
+      if (l <= Lm1) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          rr[l][r] = rr[l - 1][r] - x.al[l - 1] * x.gm[l - 1][r] * rr[l - 1][r];
+          W[l - 1][r] = x.al[l] * rr[l][r];
+        }
+      }
+    }
+  };
+  // S_t from S_{t-1} (in place)
+  auto fwd_step = [&](float (&M)[R][R], const BwdTok<R>& x) {
+    float rr[NR + 1][R], W[NR][R];
+    chain(x, rr, W);
+    float p[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      p[r] = 0.f;
+#pragma unroll
+      for (int c = 0; c < R; ++c) p[r] += M[r][c] * x.k[c];
+    }
+    sum_row_group(p);
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int c = 0; c < R; ++c) {
+        float s = x.g * (M[r][c] - x.beta * p[r] * x.k[c]) + x.beta * x.v[r] * x.k[c];
+#pragma unroll
+        for (int l = 0; l < NR; ++l)
+          if (l < Lm1) s += W[l][r] * x.u[l][c];
+        M[r][c] = s;
+      }
+  };
+
+  // ---- pass 1: the forward, keeping the state entering every block -------------------
+  float M[R][R];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int c = 0; c < R; ++c) M[r][c] = 0.f;
+  for (int t = 0; t < T; ++t) {
+    if (t % CK == 0) store_block(ckpt + (size_t)(t / CK) * D * D, M);
+    BwdTok<R> x;
+    load_tok(t, x);
+    fwd_step(M, x);
+  }
+
+  // ---- pass 2: blocks in reverse -------------------------------------------------------
+  float dS[R][R];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int c = 0; c < R; ++c)
+      dS[r][c] = a.dS_final != nullptr ? a.dS_final[(size_t)pr * D * D + (size_t)(cb * R + c) * D + rb * R + r] : 0.f;
+  float pend[3][R], dw[4][R];  // anchor terms owed to tokens t, t-1, t-2; dconv_w share
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+#pragma unroll
+    for (int j = 0; j < 3; ++j) pend[j][r] = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dw[j][r] = 0.f;
+  }
+  int buf = 0;
+  for (int blk = a.nblk - 1; blk >= 0; --blk) {
+    const int t0 = blk * CK, t1 = min(T, t0 + CK);
+    load_block(M, ckpt + (size_t)blk * D * D);
+    for (int t = t0; t < t1; ++t) {
+      BwdTok<R> x;
+      load_tok(t, x);
+      fwd_step(M, x);
+      store_block(scr + (size_t)(t - t0) * D * D, M);
+    }
+    float St[R][R];  // S_t
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int c = 0; c < R; ++c) St[r][c] = M[r][c];
+    for (int t = t1 - 1; t >= t0; --t) {
+      const size_t tr = (size_t)pr * T + t;
+      float Mp[R][R];  // S_{t-1}
+      load_block(Mp, t > t0 ? scr + (size_t)(t - 1 - t0) * D * D : ckpt + (size_t)blk * D * D);
+      BwdTok<R> x;
+      load_tok(t, x);
+      float rr[NR + 1][R], W[NR][R];
+      chain(x, rr, W);
+      // dS_t gains the readout's term
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int c = 0; c < R; ++c) dS[r][c] += x.dO[r] * x.q[c];
+      // row sums: p = S_{t-1} k, e = dS k, dW_l = dS u_l
+      float p[R], e[R], dW[NR][R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        p[r] = 0.f;
+        e[r] = 0.f;
+#pragma unroll
+        for (int c = 0; c < R; ++c) {
+          p[r] += Mp[r][c] * x.k[c];
+          e[r] += dS[r][c] * x.k[c];
+        }
+#pragma unroll
+        for (int l = 0; l < NR; ++l) {
+          dW[l][r] = 0.f;
+          if (l < Lm1) {
+#pragma unroll
+            for (int c = 0; c < R; ++c) dW[l][r] += dS[r][c] * x.u[l][c];
+          }
+        }
+      }
+      sum_row_group(p);
+      sum_row_group(e);
+#pragma unroll
+      for (int l = 0; l < NR; ++l)
+        if (l < Lm1) sum_row_group(dW[l]);
+      // this thread's share of the column sums and of the scalars
+      float y[NV][R], sc[NS];
+      const float gb = x.g * x.beta;
+#pragma unroll
+      for (int c = 0; c < R; ++c) {
+        float yq = 0.f, yk = 0.f;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          yq += St[r][c] * x.dO[r];
+          yk += dS[r][c] * (x.beta * x.v[r] - gb * p[r]) - gb * Mp[r][c] * e[r];
+        }
+        y[0][c] = yq;
+        y[1][c] = yk;
+#pragma unroll
+        for (int l = 0; l < NR; ++l) {
+          float yu = 0.f;
+          if (l < Lm1) {
+#pragma unroll
+            for (int r = 0; r < R; ++r) yu += dS[r][c] * W[l][r];
+          }
+          y[2 + l][c] = yu;
+        }
+      }
+      float sdg = 0.f;
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int c = 0; c < R; ++c) sdg += dS[r][c] * Mp[r][c];
+#pragma unroll
+      for (int s = 1; s < NS; ++s) sc[s] = 0.f;
+      if (cb == 0) {  // per-row terms, counted once per row
+        float dr[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          sdg -= x.beta * e[r] * p[r];
+          sc[1] += e[r] * (x.v[r] - x.g * p[r]);
+          dr[r] = 0.f;
+        }
+        // back through W_l = alpha_l r_l and r_l = r_{l-1} (1 - alpha_{l-1} gamma_{l-1})
+#pragma unroll
+        for (int l = NR; l >= 1; --l) {
+          if (l <= Lm1) {
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+              dr[r] += x.al[l] * dW[l - 1][r];
+              sc[2 + l] += dW[l - 1][r] * rr[l][r];
+              a.dgamma[(tr * Lm1 + (l - 1)) * D + rb * R + r] = -x.al[l - 1] * rr[l - 1][r] * dr[r];
+              sc[2 + l - 1] -= dr[r] * x.gm[l - 1][r] * rr[l - 1][r];
+              dr[r] *= 1.f - x.al[l - 1] * x.gm[l - 1][r];
+            }
+          }
+        }
+        // dr is now the gradient of r_0 = v_t - anchor_t
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          a.dv[tr * D + rb * R + r] = x.beta * e[r] + (1.f - tw[3][r]) * dr[r] + pend[0][r];
+          pend[0][r] = pend[1][r] - tw[2][r] * dr[r];
+          pend[1][r] = pend[2][r] - tw[1][r] * dr[r];
+          pend[2][r] = -tw[0][r] * dr[r];
+#pragma unroll
+          for (int j = 0; j < 3; ++j) dw[j][r] -= dr[r] * x.vh[j][r];
+          dw[3][r] -= dr[r] * x.v[r];
+        }
+      }
+      sc[0] = sdg;
+      // column sums: lanes 16 and 32 apart (rows of the wave), then the four waves
+#pragma unroll
+      for (int n = 0; n < NV; ++n)
+#pragma unroll
+        for (int c = 0; c < R; ++c) {
+          y[n][c] += __shfl_xor(y[n][c], 16);
+          y[n][c] += __shfl_xor(y[n][c], 32);
+        }
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int m = 1; m < 64; m <<= 1) sc[s] += __shfl_xor(sc[s], m);
+      if (lane < 16) {
+#pragma unroll
+        for (int n = 0; n < NV; ++n)
+#pragma unroll
+          for (int c = 0; c < R; ++c) red[buf][w][n * D + cb * R + c] = y[n][c];
+      }
+      if (lane == 0) {
+#pragma unroll
+        for (int s = 0; s < NS; ++s) red[buf][w][NV * D + s] = sc[s];
+      }
+      // dS_{t-1}
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int c = 0; c < R; ++c) dS[r][c] = x.g * (dS[r][c] - x.beta * e[r] * x.k[c]);
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int c = 0; c < R; ++c) St[r][c] = Mp[r][c];
+      __syncthreads();
+      for (int idx = tid; idx < RED; idx += 256) {
+        const float s = red[buf][0][idx] + red[buf][1][idx] + red[buf][2][idx] + red[buf][3][idx];
+        if (idx < D) {
+          a.dq[tr * D + idx] = s;
+        } else if (idx < 2 * D) {
+          a.dk[tr * D + idx - D] = s;
+        } else if (idx < NV * D) {
+          const int l = idx / D - 2, j = idx % D;
+          if (l < Lm1) a.du[(tr * Lm1 + l) * D + j] = s;
+        } else {
+          const int sidx = idx - NV * D;
+          if (sidx == 0) a.dg[tr] = s;
+          else if (sidx == 1) a.dbeta[tr] = s;
+          else if (sidx - 2 < L && L > 1) a.dalpha[tr * L + sidx - 2] = s;
+        }
+      }
+      buf ^= 1;
+    }
+  }
+  if (cb == 0 && L > 1) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < R; ++r) a.dconv_part[((size_t)pr * 4 + j) * D + rb * R + r] = dw[j][r];
+  }
+}
+
+// dconv_w[h] = sum over the batch of the pairs' shares (fixed order: deterministic).
+__global__ __launch_bounds__(256) void bwd_conv_reduce_kernel(const float* part, float* dconv_w, int B, int H, int D) {
+  const int h = blockIdx.x;
+  for (int i = threadIdx.x; i < 4 * D; i += 256) {
+    float s = 0.f;
+    for (int b = 0; b < B; ++b) s += part[((size_t)b * H + h) * 4 * D + i];
+    dconv_w[(size_t)h * 4 * D + i] = s;
+  }
+}
+
+}  // namespace prism

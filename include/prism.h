@@ -1,5 +1,6 @@
 /*
- * prism.h - C ABI of the PRISM rank-L gated delta-rule forward on MI355X (gfx950).
+ * prism.h - C ABI of the PRISM rank-L gated delta-rule forward (and its backward) on
+ * MI355X (gfx950).
  *
  * What is computed (per batch b and head h, state S_0 = 0 unless given, S is dv x dk):
  *
@@ -159,6 +160,35 @@ prism_status prism_fwd_timed(const void* q, const void* k, const void* v,
                              void* o, float* S_final,
                              void* workspace, size_t workspace_bytes,
                              hipEvent_t* events, hipStream_t stream);
+
+/* The backward pass: gradients of  sum_t <d_o_t, o_t> + <dS_final, S_final>  with respect
+ * to every input of prism_fwd (S_0 = 0, no ShortConv history), i.e. the reverse-mode
+ * derivative that end-to-end training of the layer needs (the pages quote training
+ * throughput: "PRISM" reading notes, section 3.3).  Token by token in float32, one
+ * workgroup per (b, h) pair: the forward is re-run with the state kept every 64 tokens,
+ * then each 64-token block is re-run and reversed.
+ *   inputs    q .. conv_w, B, H, T, dk, dv, L, dt exactly as prism_fwd
+ *   d_o       [B, H, T, dv] dtype dt: gradient of o
+ *   dS_final  [B, H, dk, dv] float32: gradient of S_final; NULL = zero
+ * outputs (float32, the layouts of the inputs, fully overwritten):
+ *   dq, dk [B, H, T, dk];  dv [B, H, T, dv];  dg, dbeta [B, H, T];
+ *   du [B, H, T, L-1, dk];  dalpha [B, H, T, L];  dgamma [B, H, T, L-1, dv];
+ *   dconv_w [H, 4, dv] (summed over the batch)
+ * The four rank-L gradients are not written when L == 1 (they may be NULL then) and
+ * are required otherwise.  Supported: dk == dv in {16, 32, 64, 128}, 1 <= L <= 8,
+ * B * H <= 2^31 - 1.  Workspace: prism_bwd_workspace_bytes (the checkpoints, a
+ * 64-token state buffer per pair and the per-pair dconv_w shares).  Ownership, stream
+ * and errors as prism_fwd. */
+size_t prism_bwd_workspace_bytes(int B, int H, int T, int dk, int dv, int L, prism_dtype dt);
+prism_status prism_bwd(const void* q, const void* k, const void* v,
+                       const float* g, const float* beta,
+                       const void* u, const float* alpha, const void* gamma,
+                       const float* conv_w,
+                       int B, int H, int T, int dk, int dv, int L, prism_dtype dt,
+                       const void* d_o, const float* dS_final,
+                       float* dq, float* dk_out, float* dv_out, float* dg, float* dbeta,
+                       float* du, float* dalpha, float* dgamma, float* dconv_w,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* A static, human-readable name of a status code. */
 const char* prism_status_string(prism_status s);

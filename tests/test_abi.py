@@ -157,3 +157,39 @@ def test_decode_argument_checks(lib):
     assert _call_decode(lib, L=0) == UNSUPPORTED
     assert _call_decode(lib, L=9) == UNSUPPORTED
     assert _call_decode(lib, dt=7) == UNSUPPORTED
+
+
+def _bwd_call(lib, B=1, H=1, T=64, d=16, L=2, dt=1, null=(), ws_bytes=1 << 30):
+    p = ctypes.c_void_p(1)
+    names = ["q", "k", "v", "g", "beta", "u", "alpha", "gamma", "conv_w", "d_o", "dS",
+             "dq", "dk", "dv", "dg", "dbeta", "du", "dalpha", "dgamma", "dconv_w", "ws"]
+    args = {n: (None if n in null else p) for n in names}
+    return lib.prism_bwd(args["q"], args["k"], args["v"], args["g"], args["beta"], args["u"], args["alpha"],
+                         args["gamma"], args["conv_w"], B, H, T, d, d, L, dt, args["d_o"], args["dS"],
+                         args["dq"], args["dk"], args["dv"], args["dg"], args["dbeta"], args["du"],
+                         args["dalpha"], args["dgamma"], args["dconv_w"], args["ws"], ws_bytes, None)
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "g", "beta", "d_o", "dq", "dk", "dv", "dg", "dbeta"])
+def test_bwd_null_required_pointer(lib, name):
+    assert _bwd_call(lib, null=(name,)) == INVALID
+
+
+@pytest.mark.parametrize("name", ["u", "alpha", "gamma", "conv_w", "du", "dalpha", "dgamma", "dconv_w"])
+def test_bwd_null_rank_pointer_when_L_gt_1(lib, name):
+    assert _bwd_call(lib, L=3, null=(name,)) == INVALID
+
+
+def test_bwd_argument_checks(lib):
+    assert _bwd_call(lib, B=0) == INVALID
+    assert _bwd_call(lib, T=-1) == INVALID
+    assert _bwd_call(lib, d=48) == UNSUPPORTED
+    assert _bwd_call(lib, L=9) == UNSUPPORTED
+    assert _bwd_call(lib, dt=3) == INVALID
+    assert _bwd_call(lib, null=("ws",)) == WORKSPACE
+    need = lib.prism_bwd_workspace_bytes(1, 1, 64, 16, 16, 2, 1)
+    assert need > 0
+    assert _bwd_call(lib, ws_bytes=need - 1) == WORKSPACE
+    assert lib.prism_bwd_workspace_bytes(1, 1, 64, 16, 32, 2, 1) == 0
+    # one 64-token checkpoint more per pair once T passes a multiple of 64
+    assert lib.prism_bwd_workspace_bytes(1, 1, 65, 16, 16, 2, 1) > need

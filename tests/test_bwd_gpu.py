@@ -1,0 +1,89 @@
+"""GPU parity of the backward pass (prism_bwd through the C ABI) against the float64
+gradient oracle (oracle/prism_grad.py: autograd through the token recurrence, pinned
+by finite differences of the numpy forward).
+
+Every gradient is compared as max |x - x_ref| / max |x_ref| <= 1e-4: the kernel
+computes in float32 from the same (bf16-rounded, for bf16 inputs) input values the
+oracle reads, so the float32 bar applies to both input dtypes.
+"""
+import numpy as np
+import pytest
+
+from tests.conftest import gpu_available
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-4
+CASES = [
+    # name, dtype, B, H, T, d, L, with dS_final
+    ("f32_d16_L1_T100", "f32", 1, 2, 100, 16, 1, True),
+    ("f32_d32_L3_T130", "f32", 2, 2, 130, 32, 3, False),
+    ("bf16_d64_L4_T200", "bf16", 1, 2, 200, 64, 4, True),
+    ("f32_d64_L8_T65", "f32", 1, 1, 65, 64, 8, True),
+    ("bf16_d128_L2_T70", "bf16", 1, 1, 70, 128, 2, True),
+    ("f32_d16_L3_T1", "f32", 1, 2, 1, 16, 3, True),
+    ("f32_d32_L2_T3", "f32", 2, 1, 3, 32, 2, False),
+    ("bf16_d64_L4_T128", "bf16", 1, 1, 128, 64, 4, False),
+]
+
+
+def _setup(dtype, B, H, T, d, L, with_dS, seed):
+    import workloads
+    w = workloads.Workload("bwd", dtype, B=B, H=H, T=T, dk=d, dv=d, L=L, chunk=64, seed=seed)
+    x = workloads.generate(w)
+    rng = np.random.default_rng(seed + 100)
+    d_o = rng.standard_normal((B, H, T, d)).astype(np.float32)
+    if dtype == "bf16":
+        d_o = workloads.to_bf16_values(d_o)
+    dS = rng.standard_normal((B, H, d, d)).astype(np.float32) if with_dS else None
+    return w, x, d_o, dS
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_bwd_matches_oracle(case):
+    if not gpu_available():
+        pytest.skip("no GPU")
+    import torch
+    import delta_rule_sequence_amd as prism
+    import workloads
+    from oracle import prism_grad
+    name, dtype, B, H, T, d, L, with_dS = case
+    print(f"[bwd] {name}", flush=True)
+    w, x, d_o, dS = _setup(dtype, B, H, T, d, L, with_dS, seed=len(name) + T)
+    dev = workloads.to_torch(x, dtype, "cuda")
+    vt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    got = prism.bwd(dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], dev["u"], dev["alpha"], dev["gamma"],
+                    dev["conv_w"], L=L, d_o=torch.tensor(d_o, device="cuda").to(vt),
+                    dS_final=None if dS is None else torch.tensor(dS, device="cuda"))
+    torch.cuda.synchronize()
+    ref = prism_grad.backward(x["q"], x["k"], x["v"], x["g"], x["beta"], x["u"], x["alpha"], x["gamma"],
+                              x["conv_w"], L, d_o, dS)
+    names = ["dq", "dk", "dv", "dg", "dbeta"] + (["du", "dalpha", "dgamma", "dconv_w"] if L > 1 else [])
+    errs = {}
+    for n in names:
+        g = got[n].cpu().numpy()
+        r = ref[n]
+        assert g.shape == r.shape, (n, g.shape, r.shape)
+        assert np.all(np.isfinite(g)), n
+        errs[n] = float(np.max(np.abs(g - r)) / max(1e-30, np.max(np.abs(r))))
+    print(f"[bwd] {name} rel errors " + " ".join(f"{n}={e:.1e}" for n, e in errs.items()), flush=True)
+    bad = {n: e for n, e in errs.items() if not e <= TOL}
+    assert not bad, bad
+
+
+def test_bwd_deterministic():
+    """Two calls on the same inputs give bit-identical gradients (fixed reduction order)."""
+    if not gpu_available():
+        pytest.skip("no GPU")
+    import torch
+    import delta_rule_sequence_amd as prism
+    import workloads
+    w, x, d_o, dS = _setup("bf16", 2, 2, 96, 32, 3, True, seed=5)
+    dev = workloads.to_torch(x, "bf16", "cuda")
+    args = (dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], dev["u"], dev["alpha"], dev["gamma"], dev["conv_w"])
+    kw = dict(L=3, d_o=torch.tensor(d_o, device="cuda").to(torch.bfloat16), dS_final=torch.tensor(dS, device="cuda"))
+    a = prism.bwd(*args, **kw)
+    b = prism.bwd(*args, **kw)
+    torch.cuda.synchronize()
+    for n in a:
+        assert torch.equal(a[n], b[n]), n
