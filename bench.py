@@ -10,6 +10,9 @@ the launch stream around each kernel (the dominant kernel's duration, hence its
 achieved HBM bandwidth against the 8 TB/s peak).  Prints one JSON line, with the
 float64 oracle timed on the host cores on a bounded sample.
 
+    python bench.py --bwd [--workload NAME] [--steps K]
+times the backward pass (prism_bwd) instead and prints its own JSON line.
+
     python bench.py --calibrate-copy MB
 runs a plain device-to-device copy of MB megabytes (for scaling the
 FETCH_SIZE / WRITE_SIZE counters of rocprofv3) and exits.
@@ -40,11 +43,17 @@ def algorithmic_bytes(w):
     return inputs, inputs + w.dv * E
 
 
+# the sources the segment-sweep kernel is compiled from, and the build flags
+SWEEP_SOURCES = ["delta_rule_sequence_amd/csrc/prism_sweep8.h", "delta_rule_sequence_amd/csrc/prism_fast.h",
+                 "delta_rule_sequence_amd/csrc/prism_kernels.h", "delta_rule_sequence_amd/csrc/prism_tile.h",
+                 "delta_rule_sequence_amd/build.py"]
+
+
 def kernel_source_hash():
+    """Hash of the sweep kernel's sources: counters taken with other sources are void."""
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "delta_rule_sequence_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, f), "rb") as fh:
+    for f in SWEEP_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
 
@@ -360,6 +369,71 @@ def decode_bench(steps, warmup, batch):
                       "frac": step_bytes / dt / 1e9 / HBM_PEAK_GBS}), flush=True)
 
 
+def bwd_bench(steps, warmup, workload_name, cpu=True):
+    """The backward (prism_bwd) on one workload: whole calls timed with HIP events on the
+    launch stream.  One JSON line: tokens/s and the call's algorithmic bytes (inputs and
+    d_o read once, every gradient written once in float32) against the HBM peak, beside
+    the float64 gradient oracle timed on a bounded sample (one pair, 512 tokens)."""
+    import numpy as np
+    import torch
+    import delta_rule_sequence_amd as prism
+    import workloads
+    w = workloads.workload(workload_name)
+    x = workloads.generate(w, seed=w.seed)
+    rng = np.random.default_rng(w.seed + 7)
+    d_o = rng.standard_normal((w.B, w.H, w.T, w.dv)).astype(np.float32)
+    if w.dtype == "bf16":
+        d_o = workloads.to_bf16_values(d_o)
+    cpu_out = None
+    if cpu:
+        from oracle import prism_grad
+        Ts = min(w.T, 512)
+        sl = lambda a: None if a is None else np.ascontiguousarray(a[:1, :1, :Ts])  # noqa: E731
+        t0 = time.perf_counter()
+        prism_grad.backward(sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(x["g"]), sl(x["beta"]), sl(x["u"]),
+                            sl(x["alpha"]), sl(x["gamma"]), x["conv_w"][:1], w.L, sl(d_o))
+        dt_cpu = time.perf_counter() - t0
+        cpu_out = {"value": Ts / dt_cpu, "unit": "tokens/s (per head)", "cores": torch.get_num_threads(),
+                   "kind": "oracle", "sample": f"one (b, h) pair, {Ts} tokens, float64 autograd, {dt_cpu:.1f} s"}
+    dev = workloads.to_torch(x, w.dtype, "cuda")
+    vt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    do_t = torch.tensor(d_o, device="cuda").to(vt)
+    args = (dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], dev["u"], dev["alpha"], dev["gamma"],
+            dev["conv_w"])
+    need = prism.load_library().prism_bwd_workspace_bytes(w.B, w.H, w.T, w.dk, w.dv, w.L,
+                                                          prism.PRISM_BF16 if w.dtype == "bf16" else prism.PRISM_F32)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    for _ in range(warmup):
+        prism.bwd(*args, L=w.L, d_o=do_t, workspace=ws)
+    torch.cuda.synchronize()
+    hip = Hip()
+    ev = hip.events(2)
+    stream = torch.cuda.current_stream()
+    rec = hip.lib.hipEventRecord
+    rec.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    rec(ev[0], ctypes.c_void_p(stream.cuda_stream))
+    for _ in range(steps):
+        prism.bwd(*args, L=w.L, d_o=do_t, workspace=ws)
+    rec(ev[1], ctypes.c_void_p(stream.cuda_stream))
+    torch.cuda.synchronize()
+    ms = hip.elapsed_ms(ev[0], ev[1]) / steps
+    hip.destroy(ev)
+    in_bytes, _ = algorithmic_bytes(w)
+    E = 2 if w.dtype == "bf16" else 4
+    grad_bytes = 4 * (2 * w.dk + w.dv + 2 + ((w.L - 1) * (w.dk + w.dv) + w.L if w.L > 1 else 0))
+    per_th = in_bytes + w.dv * E + grad_bytes
+    total = w.pairs * w.T * per_th
+    print(json.dumps({"metric": "bwd tokens/sec (prism_bwd)", "workload": w.name, "dtype": w.dtype,
+                      "config": {"B": w.B, "H": w.H, "T": w.T, "dk": w.dk, "dv": w.dv, "L": w.L},
+                      "steps": steps, "warmup": warmup, "ms_per_step": ms,
+                      "tokens_per_s": w.B * w.T / (ms * 1e-3),
+                      "roofline": {"bound": "hbm", "bytes_per_token_head": per_th, "bytes_per_call": total,
+                                   "achieved": total / (ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                   "frac": total / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                   "kernel": "bwd_pair_kernel"},
+                      "cpu_baseline": cpu_out}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -373,6 +447,8 @@ def main():
                     help="time the 16K shape at L = 1, 2, 4, 8 (one JSON line each) instead")
     ap.add_argument("--decode", type=int, default=0, metavar="BATCH",
                     help="time one-token decode steps for BATCH sequences instead")
+    ap.add_argument("--bwd", action="store_true",
+                    help="time the backward (prism_bwd) on --workload instead")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -388,6 +464,9 @@ def main():
         return
     if args.decode:
         decode_bench(args.steps, args.warmup, args.decode)
+        return
+    if args.bwd:
+        bwd_bench(args.steps, args.warmup, args.workload, cpu=not args.no_cpu_baseline)
         return
 
     import workloads
