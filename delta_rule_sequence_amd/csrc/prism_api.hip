@@ -243,14 +243,22 @@ prism_status make_bwd_plan(int B, int H, int T, int dk, int dv, int L, prism_dty
   return PRISM_OK;
 }
 
+template <class E, int NRK>
+void bwd_launch(int d, const prism::BwdArgs& a, int P, hipStream_t stream) {
+  switch (d) {
+    case 16: hipLaunchKernelGGL((prism::bwd_pair_kernel<E, 16, NRK>), dim3(P), dim3(256), 0, stream, a); break;
+    case 32: hipLaunchKernelGGL((prism::bwd_pair_kernel<E, 32, NRK>), dim3(P), dim3(256), 0, stream, a); break;
+    case 64: hipLaunchKernelGGL((prism::bwd_pair_kernel<E, 64, NRK>), dim3(P), dim3(256), 0, stream, a); break;
+    default: hipLaunchKernelGGL((prism::bwd_pair_kernel<E, 128, NRK>), dim3(P), dim3(256), 0, stream, a); break;
+  }
+}
+
+// rank slots compiled in: 0 for L = 1, 3 for L <= 4, 7 for L <= 8
 template <class E>
 prism_status bwd_dispatch(int d, const prism::BwdArgs& a, int P, hipStream_t stream) {
-  switch (d) {
-    case 16: hipLaunchKernelGGL((prism::bwd_pair_kernel<E, 16>), dim3(P), dim3(256), 0, stream, a); break;
-    case 32: hipLaunchKernelGGL((prism::bwd_pair_kernel<E, 32>), dim3(P), dim3(256), 0, stream, a); break;
-    case 64: hipLaunchKernelGGL((prism::bwd_pair_kernel<E, 64>), dim3(P), dim3(256), 0, stream, a); break;
-    default: hipLaunchKernelGGL((prism::bwd_pair_kernel<E, 128>), dim3(P), dim3(256), 0, stream, a); break;
-  }
+  if (a.L == 1) bwd_launch<E, 0>(d, a, P, stream);
+  else if (a.L <= 4) bwd_launch<E, 3>(d, a, P, stream);
+  else bwd_launch<E, 7>(d, a, P, stream);
   return hipGetLastError() == hipSuccess ? PRISM_OK : PRISM_ERR_HIP;
 }
 

@@ -18,9 +18,9 @@
 //
 // One workgroup of 256 threads per pair; thread (rb, cb) = (tid / 16, tid % 16) owns the
 // R x R block (R = D / 16) of rows rb R .. and columns cb R .. of S and dS.  Sums over a row
-// run through the 16 lanes of the thread's row group (shuffles); sums over a column
-// through lanes 16 apart within the wave and then the four waves (one LDS exchange,
-// double-buffered, one barrier per token).  Pass 1 runs the forward and keeps the state
+// run through the 16 lanes of the thread's row group (DPP butterfly); sums over a column
+// through one LDS table per token indexed by row block (double-buffered, one barrier per
+// token).  Pass 1 runs the forward and keeps the state
 // entering every block of kBwdBlock tokens; pass 2 walks the blocks backwards, re-runs
 // each block's forward into a per-pair scratch (every thread reads back only what it
 // wrote itself) and then the adjoint steps of the block in reverse order.
@@ -30,7 +30,6 @@
 namespace prism {
 
 constexpr int kBwdBlock = 64;  // tokens between state checkpoints
-constexpr int kBwdMaxRank = 7;  // L - 1 <= 7
 
 struct BwdArgs {
   const void *q, *k, *v, *u, *gamma, *d_o;
@@ -43,21 +42,30 @@ struct BwdArgs {
 };
 
 // One token's inputs as seen by thread (rb, cb): key-side entries of its columns,
-// value-side entries of its rows.
-template <int R>
+// value-side entries of its rows (NR rank slots).
+template <int R, int NR>
 struct BwdTok {
-  float k[R], q[R], u[kBwdMaxRank][R];
-  float v[R], dO[R], gm[kBwdMaxRank][R], vh[3][R];  // vh: v_{t-3}, v_{t-2}, v_{t-1}
-  float g, beta, al[kBwdMaxRank + 1];
+  float k[R], q[R], u[NR][R];
+  float v[R], dO[R], gm[NR][R], vh[3][R];  // vh: v_{t-3}, v_{t-2}, v_{t-1}
+  float g, beta, al[NR + 1];
 };
+
+// Sum over the 16 lanes of a row (DPP butterfly): swap neighbours, swap pairs, mirror
+// the halves of each 8 lanes, mirror the row; every lane ends with the row's total.
+__device__ __forceinline__ float row16_sum(float x) {
+#define PRISM_DPP_ADD(CTRL) x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+  PRISM_DPP_ADD(0xB1)   // quad_perm [1, 0, 3, 2]
+  PRISM_DPP_ADD(0x4E)   // quad_perm [2, 3, 0, 1]
+  PRISM_DPP_ADD(0x141)  // row_half_mirror
+  PRISM_DPP_ADD(0x140)  // row_mirror
+#undef PRISM_DPP_ADD
+  return x;
+}
 
 template <int R>
 __device__ __forceinline__ void sum_row_group(float (&x)[R]) {
 #pragma unroll
-  for (int a = 0; a < R; ++a) {
-#pragma unroll
-    for (int m = 1; m < 16; m <<= 1) x[a] += __shfl_xor(x[a], m);
-  }
+  for (int a = 0; a < R; ++a) x[a] = row16_sum(x[a]);
 }
 
 template <int R>
@@ -92,13 +100,18 @@ __device__ __forceinline__ void load_block(float (&M)[R][R], const float* src) {
   }
 }
 
-template <class E, int D>
+// NRK: rank slots compiled in (0 for L = 1, 3 for L <= 4, 7 for L <= 8).  Every loop
+// over the token sequence is software-pipelined: the next token's inputs (and, in the
+// adjoint, its previous state) are loaded while the current token is processed, into
+// the other of two register buffers.
+template <class E, int D, int NRK>
 __global__ __launch_bounds__(256) void bwd_pair_kernel(BwdArgs a) {
-  constexpr int R = D / 16, CK = kBwdBlock, NR = kBwdMaxRank;
-  constexpr int NV = 2 + NR, NS = 2 + NR + 1;  // column vectors (dq, dk, du_l) and scalars (dg, dbeta, dalpha_l)
+  constexpr int R = D / 16, CK = kBwdBlock, NR = NRK > 0 ? NRK : 1;
+  constexpr int NV = 2 + NR, NS = 3 + NR;  // column vectors (dq, dk, du_l) and scalars (dg, dbeta, dalpha_l)
   constexpr int RED = NV * D + NS;
-  __shared__ float red[2][4][RED];
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  using Tok = BwdTok<R, NR>;
+  __shared__ float red[2][16][RED];  // [token parity][row block][column sums, scalars]
+  const int tid = threadIdx.x;
   const int rb = tid >> 4, cb = tid & 15;
   const int pr = blockIdx.x, hd = pr % a.H;
   const int T = a.T, L = a.L, Lm1 = L - 1;
@@ -117,7 +130,7 @@ __global__ __launch_bounds__(256) void bwd_pair_kernel(BwdArgs a) {
 #pragma unroll
     for (int r = 0; r < R; ++r) tw[j][r] = L > 1 ? a.conv_w[((size_t)hd * 4 + j) * D + rb * R + r] : 0.f;
 
-  auto load_tok = [&](int t, BwdTok<R>& x) {
+  auto load_tok = [&](int t, Tok& x) {
     const size_t tr = (size_t)pr * T + t;
 #pragma unroll
     for (int c = 0; c < R; ++c) {
@@ -146,7 +159,7 @@ __global__ __launch_bounds__(256) void bwd_pair_kernel(BwdArgs a) {
     for (int l = 0; l <= NR; ++l) x.al[l] = (L > 1 && l < L) ? a.alpha[tr * L + l] : 0.f;
   };
   // residuals r_{t,0..L-1} and written values W_{t,1..L-1} of this thread's rows
-  auto chain = [&](const BwdTok<R>& x, float (&rr)[NR + 1][R], float (&W)[NR][R]) {
+  auto chain = [&](const Tok& x, float (&rr)[NR + 1][R], float (&W)[NR][R]) {
 #pragma unroll
     for (int r = 0; r < R; ++r)
       rr[0][r] = x.v[r] - (tw[0][r] * x.vh[0][r] + tw[1][r] * x.vh[1][r] + tw[2][r] * x.vh[2][r] + tw[3][r] * x.v[r]);
@@ -162,7 +175,7 @@ __global__ __launch_bounds__(256) void bwd_pair_kernel(BwdArgs a) {
     }
   };
   // S_t from S_{t-1} (in place)
-  auto fwd_step = [&](float (&M)[R][R], const BwdTok<R>& x) {
+  auto fwd_step = [&](float (&M)[R][R], const Tok& x) {
     float rr[NR + 1][R], W[NR][R];
     chain(x, rr, W);
     float p[R];
@@ -185,201 +198,220 @@ __global__ __launch_bounds__(256) void bwd_pair_kernel(BwdArgs a) {
       }
   };
 
+  float dS[R][R], St[R][R];                   // dL/dS_t (carried backwards), S_t
+  float pend[3][R], dw[4][R];                 // anchor terms owed to tokens t, t-1, t-2; dconv_w share
+  int buf = 0;
+  // one adjoint step at token t from its inputs x and the state before it, Mp = S_{t-1}
+  auto rev_step = [&](int t, const Tok& x, const float (&Mp)[R][R]) {
+    const size_t tr = (size_t)pr * T + t;
+    float rr[NR + 1][R], W[NR][R];
+    chain(x, rr, W);
+    // dS_t gains the readout's term
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int c = 0; c < R; ++c) dS[r][c] += x.dO[r] * x.q[c];
+    // row sums: p = S_{t-1} k, e = dS k, dW_l = dS u_l
+    float p[R], e[R], dW[NR][R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      p[r] = 0.f;
+      e[r] = 0.f;
+#pragma unroll
+      for (int c = 0; c < R; ++c) {
+        p[r] += Mp[r][c] * x.k[c];
+        e[r] += dS[r][c] * x.k[c];
+      }
+#pragma unroll
+      for (int l = 0; l < NR; ++l) {
+        dW[l][r] = 0.f;
+        if (l < Lm1) {
+#pragma unroll
+          for (int c = 0; c < R; ++c) dW[l][r] += dS[r][c] * x.u[l][c];
+        }
+      }
+    }
+    sum_row_group(p);
+    sum_row_group(e);
+#pragma unroll
+    for (int l = 0; l < NR; ++l)
+      if (l < Lm1) sum_row_group(dW[l]);
+    // this thread's share of the column sums and of the scalars
+    float y[NV][R], sc[NS];
+    const float gb = x.g * x.beta;
+#pragma unroll
+    for (int c = 0; c < R; ++c) {
+      float yq = 0.f, yk = 0.f;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        yq += St[r][c] * x.dO[r];
+        yk += dS[r][c] * (x.beta * x.v[r] - gb * p[r]) - gb * Mp[r][c] * e[r];
+      }
+      y[0][c] = yq;
+      y[1][c] = yk;
+#pragma unroll
+      for (int l = 0; l < NR; ++l) {
+        float yu = 0.f;
+        if (l < Lm1) {
+#pragma unroll
+          for (int r = 0; r < R; ++r) yu += dS[r][c] * W[l][r];
+        }
+        y[2 + l][c] = yu;
+      }
+    }
+    float sdg = 0.f;
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int c = 0; c < R; ++c) sdg += dS[r][c] * Mp[r][c];
+#pragma unroll
+    for (int s = 1; s < NS; ++s) sc[s] = 0.f;
+    if (cb == 0) {  // per-row terms, counted once per row
+      float dr[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        sdg -= x.beta * e[r] * p[r];
+        sc[1] += e[r] * (x.v[r] - x.g * p[r]);
+        dr[r] = 0.f;
+      }
+      // back through W_l = alpha_l r_l and r_l = r_{l-1} (1 - alpha_{l-1} gamma_{l-1})
+#pragma unroll
+      for (int l = NR; l >= 1; --l) {
+        if (l <= Lm1) {
+#pragma unroll
+          for (int r = 0; r < R; ++r) {
+            dr[r] += x.al[l] * dW[l - 1][r];
+            sc[2 + l] += dW[l - 1][r] * rr[l][r];
+            a.dgamma[(tr * Lm1 + (l - 1)) * D + rb * R + r] = -x.al[l - 1] * rr[l - 1][r] * dr[r];
+            sc[2 + l - 1] -= dr[r] * x.gm[l - 1][r] * rr[l - 1][r];
+            dr[r] *= 1.f - x.al[l - 1] * x.gm[l - 1][r];
+          }
+        }
+      }
+      // dr is now the gradient of r_0 = v_t - anchor_t
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        a.dv[tr * D + rb * R + r] = x.beta * e[r] + (1.f - tw[3][r]) * dr[r] + pend[0][r];
+        pend[0][r] = pend[1][r] - tw[2][r] * dr[r];
+        pend[1][r] = pend[2][r] - tw[1][r] * dr[r];
+        pend[2][r] = -tw[0][r] * dr[r];
+#pragma unroll
+        for (int j = 0; j < 3; ++j) dw[j][r] -= dr[r] * x.vh[j][r];
+        dw[3][r] -= dr[r] * x.v[r];
+      }
+    }
+    sc[0] = sdg;
+    // column sums and scalars: each row block's share into LDS, summed over the 16 row
+    // blocks after the barrier (the scalars first summed over the row's 16 lanes)
+#pragma unroll
+    for (int n = 0; n < NV; ++n)
+#pragma unroll
+      for (int c = 0; c < R; ++c) red[buf][rb][n * D + cb * R + c] = y[n][c];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) sc[s] = row16_sum(sc[s]);
+    if (cb == 0) {
+#pragma unroll
+      for (int s = 0; s < NS; ++s) red[buf][rb][NV * D + s] = sc[s];
+    }
+    // dS_{t-1}; S_{t-1} becomes the next step's S_t
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int c = 0; c < R; ++c) {
+        dS[r][c] = x.g * (dS[r][c] - x.beta * e[r] * x.k[c]);
+        St[r][c] = Mp[r][c];
+      }
+    __syncthreads();
+    for (int idx = tid; idx < RED; idx += 256) {
+      float s = 0.f;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) s += red[buf][j][idx];
+      if (idx < D) {
+        a.dq[tr * D + idx] = s;
+      } else if (idx < 2 * D) {
+        a.dk[tr * D + idx - D] = s;
+      } else if (idx < NV * D) {
+        const int l = idx / D - 2, j = idx % D;
+        if (l < Lm1) a.du[(tr * Lm1 + l) * D + j] = s;
+      } else {
+        const int sidx = idx - NV * D;
+        if (sidx == 0) a.dg[tr] = s;
+        else if (sidx == 1) a.dbeta[tr] = s;
+        else if (sidx - 2 < L && L > 1) a.dalpha[tr * L + sidx - 2] = s;
+      }
+    }
+    buf ^= 1;
+  };
+
   // ---- pass 1: the forward, keeping the state entering every block -------------------
   float M[R][R];
 #pragma unroll
   for (int r = 0; r < R; ++r)
 #pragma unroll
     for (int c = 0; c < R; ++c) M[r][c] = 0.f;
-  for (int t = 0; t < T; ++t) {
+  Tok xa, xb;
+  load_tok(0, xa);
+  for (int t = 0; t < T; t += 2) {  // tokens t (buffer a) and t + 1 (buffer b)
     if (t % CK == 0) store_block(ckpt + (size_t)(t / CK) * D * D, M);
-    BwdTok<R> x;
-    load_tok(t, x);
-    fwd_step(M, x);
+    if (t + 1 < T) load_tok(t + 1, xb);
+    fwd_step(M, xa);
+    if (t + 1 < T) {
+      if ((t + 1) % CK == 0) store_block(ckpt + (size_t)((t + 1) / CK) * D * D, M);
+      if (t + 2 < T) load_tok(t + 2, xa);
+      fwd_step(M, xb);
+    }
   }
 
   // ---- pass 2: blocks in reverse -------------------------------------------------------
-  float dS[R][R];
 #pragma unroll
-  for (int r = 0; r < R; ++r)
+  for (int r = 0; r < R; ++r) {
 #pragma unroll
     for (int c = 0; c < R; ++c)
       dS[r][c] = a.dS_final != nullptr ? a.dS_final[(size_t)pr * D * D + (size_t)(cb * R + c) * D + rb * R + r] : 0.f;
-  float pend[3][R], dw[4][R];  // anchor terms owed to tokens t, t-1, t-2; dconv_w share
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
 #pragma unroll
     for (int j = 0; j < 3; ++j) pend[j][r] = 0.f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) dw[j][r] = 0.f;
   }
-  int buf = 0;
+  float Ma[R][R], Mb[R][R];
   for (int blk = a.nblk - 1; blk >= 0; --blk) {
     const int t0 = blk * CK, t1 = min(T, t0 + CK);
-    load_block(M, ckpt + (size_t)blk * D * D);
-    for (int t = t0; t < t1; ++t) {
-      BwdTok<R> x;
-      load_tok(t, x);
-      fwd_step(M, x);
+    const float* cp = ckpt + (size_t)blk * D * D;
+    // the block's forward again, keeping every S_t
+    load_block(M, cp);
+    load_tok(t0, xa);
+    for (int t = t0; t < t1; t += 2) {
+      if (t + 1 < t1) load_tok(t + 1, xb);
+      fwd_step(M, xa);
       store_block(scr + (size_t)(t - t0) * D * D, M);
+      if (t + 1 < t1) {
+        if (t + 2 < t1) load_tok(t + 2, xa);
+        fwd_step(M, xb);
+        store_block(scr + (size_t)(t + 1 - t0) * D * D, M);
+      }
     }
-    float St[R][R];  // S_t
 #pragma unroll
     for (int r = 0; r < R; ++r)
 #pragma unroll
       for (int c = 0; c < R; ++c) St[r][c] = M[r][c];
-    for (int t = t1 - 1; t >= t0; --t) {
-      const size_t tr = (size_t)pr * T + t;
-      float Mp[R][R];  // S_{t-1}
-      load_block(Mp, t > t0 ? scr + (size_t)(t - 1 - t0) * D * D : ckpt + (size_t)blk * D * D);
-      BwdTok<R> x;
-      load_tok(t, x);
-      float rr[NR + 1][R], W[NR][R];
-      chain(x, rr, W);
-      // dS_t gains the readout's term
-#pragma unroll
-      for (int r = 0; r < R; ++r)
-#pragma unroll
-        for (int c = 0; c < R; ++c) dS[r][c] += x.dO[r] * x.q[c];
-      // row sums: p = S_{t-1} k, e = dS k, dW_l = dS u_l
-      float p[R], e[R], dW[NR][R];
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        p[r] = 0.f;
-        e[r] = 0.f;
-#pragma unroll
-        for (int c = 0; c < R; ++c) {
-          p[r] += Mp[r][c] * x.k[c];
-          e[r] += dS[r][c] * x.k[c];
-        }
-#pragma unroll
-        for (int l = 0; l < NR; ++l) {
-          dW[l][r] = 0.f;
-          if (l < Lm1) {
-#pragma unroll
-            for (int c = 0; c < R; ++c) dW[l][r] += dS[r][c] * x.u[l][c];
-          }
-        }
+    // the adjoint steps, last token first (S_{t-1} is the block state t - 1 - t0, or the
+    // checkpoint for the first token)
+    auto prev_state = [&](int t) { return t > t0 ? scr + (size_t)(t - 1 - t0) * D * D : cp; };
+    load_tok(t1 - 1, xa);
+    load_block(Ma, prev_state(t1 - 1));
+    for (int t = t1 - 1; t >= t0; t -= 2) {  // tokens t (buffers a) and t - 1 (buffers b)
+      if (t - 1 >= t0) {
+        load_tok(t - 1, xb);
+        load_block(Mb, prev_state(t - 1));
       }
-      sum_row_group(p);
-      sum_row_group(e);
-#pragma unroll
-      for (int l = 0; l < NR; ++l)
-        if (l < Lm1) sum_row_group(dW[l]);
-      // this thread's share of the column sums and of the scalars
-      float y[NV][R], sc[NS];
-      const float gb = x.g * x.beta;
-#pragma unroll
-      for (int c = 0; c < R; ++c) {
-        float yq = 0.f, yk = 0.f;
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-          yq += St[r][c] * x.dO[r];
-          yk += dS[r][c] * (x.beta * x.v[r] - gb * p[r]) - gb * Mp[r][c] * e[r];
+      rev_step(t, xa, Ma);
+      if (t - 1 >= t0) {
+        if (t - 2 >= t0) {
+          load_tok(t - 2, xa);
+          load_block(Ma, prev_state(t - 2));
         }
-        y[0][c] = yq;
-        y[1][c] = yk;
-#pragma unroll
-        for (int l = 0; l < NR; ++l) {
-          float yu = 0.f;
-          if (l < Lm1) {
-#pragma unroll
-            for (int r = 0; r < R; ++r) yu += dS[r][c] * W[l][r];
-          }
-          y[2 + l][c] = yu;
-        }
+        rev_step(t - 1, xb, Mb);
       }
-      float sdg = 0.f;
-#pragma unroll
-      for (int r = 0; r < R; ++r)
-#pragma unroll
-        for (int c = 0; c < R; ++c) sdg += dS[r][c] * Mp[r][c];
-#pragma unroll
-      for (int s = 1; s < NS; ++s) sc[s] = 0.f;
-      if (cb == 0) {  // per-row terms, counted once per row
-        float dr[R];
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-          sdg -= x.beta * e[r] * p[r];
-          sc[1] += e[r] * (x.v[r] - x.g * p[r]);
-          dr[r] = 0.f;
-        }
-        // back through W_l = alpha_l r_l and r_l = r_{l-1} (1 - alpha_{l-1} gamma_{l-1})
-#pragma unroll
-        for (int l = NR; l >= 1; --l) {
-          if (l <= Lm1) {
-#pragma unroll
-            for (int r = 0; r < R; ++r) {
-              dr[r] += x.al[l] * dW[l - 1][r];
-              sc[2 + l] += dW[l - 1][r] * rr[l][r];
-              a.dgamma[(tr * Lm1 + (l - 1)) * D + rb * R + r] = -x.al[l - 1] * rr[l - 1][r] * dr[r];
-              sc[2 + l - 1] -= dr[r] * x.gm[l - 1][r] * rr[l - 1][r];
-              dr[r] *= 1.f - x.al[l - 1] * x.gm[l - 1][r];
-            }
-          }
-        }
-        // dr is now the gradient of r_0 = v_t - anchor_t
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-          a.dv[tr * D + rb * R + r] = x.beta * e[r] + (1.f - tw[3][r]) * dr[r] + pend[0][r];
-          pend[0][r] = pend[1][r] - tw[2][r] * dr[r];
-          pend[1][r] = pend[2][r] - tw[1][r] * dr[r];
-          pend[2][r] = -tw[0][r] * dr[r];
-#pragma unroll
-          for (int j = 0; j < 3; ++j) dw[j][r] -= dr[r] * x.vh[j][r];
-          dw[3][r] -= dr[r] * x.v[r];
-        }
-      }
-      sc[0] = sdg;
-      // column sums: lanes 16 and 32 apart (rows of the wave), then the four waves
-#pragma unroll
-      for (int n = 0; n < NV; ++n)
-#pragma unroll
-        for (int c = 0; c < R; ++c) {
-          y[n][c] += __shfl_xor(y[n][c], 16);
-          y[n][c] += __shfl_xor(y[n][c], 32);
-        }
-#pragma unroll
-      for (int s = 0; s < NS; ++s)
-#pragma unroll
-        for (int m = 1; m < 64; m <<= 1) sc[s] += __shfl_xor(sc[s], m);
-      if (lane < 16) {
-#pragma unroll
-        for (int n = 0; n < NV; ++n)
-#pragma unroll
-          for (int c = 0; c < R; ++c) red[buf][w][n * D + cb * R + c] = y[n][c];
-      }
-      if (lane == 0) {
-#pragma unroll
-        for (int s = 0; s < NS; ++s) red[buf][w][NV * D + s] = sc[s];
-      }
-      // dS_{t-1}
-#pragma unroll
-      for (int r = 0; r < R; ++r)
-#pragma unroll
-        for (int c = 0; c < R; ++c) dS[r][c] = x.g * (dS[r][c] - x.beta * e[r] * x.k[c]);
-#pragma unroll
-      for (int r = 0; r < R; ++r)
-#pragma unroll
-        for (int c = 0; c < R; ++c) St[r][c] = Mp[r][c];
-      __syncthreads();
-      for (int idx = tid; idx < RED; idx += 256) {
-        const float s = red[buf][0][idx] + red[buf][1][idx] + red[buf][2][idx] + red[buf][3][idx];
-        if (idx < D) {
-          a.dq[tr * D + idx] = s;
-        } else if (idx < 2 * D) {
-          a.dk[tr * D + idx - D] = s;
-        } else if (idx < NV * D) {
-          const int l = idx / D - 2, j = idx % D;
-          if (l < Lm1) a.du[(tr * Lm1 + l) * D + j] = s;
-        } else {
-          const int sidx = idx - NV * D;
-          if (sidx == 0) a.dg[tr] = s;
-          else if (sidx == 1) a.dbeta[tr] = s;
-          else if (sidx - 2 < L && L > 1) a.dalpha[tr * L + sidx - 2] = s;
-        }
-      }
-      buf ^= 1;
     }
   }
   if (cb == 0 && L > 1) {
