@@ -100,6 +100,44 @@ __device__ __forceinline__ void load_block(float (&M)[R][R], const float* src) {
   }
 }
 
+// One input's run of a backward stage, in 16-byte units dealt round-robin to the 256
+// threads: unit un covers elements un * vec .. of the run, whose rows of row_elems
+// elements start at token tok0; rows outside [0, T) are zero and not read.
+template <int N, class E>
+__device__ __forceinline__ void stage_fetch_seg(uint4 (&dst)[N], const E* base, int nunits, int vec, int row_elems,
+                                                int tok0, int T) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const int un = threadIdx.x + 256 * i;
+    dst[i] = make_uint4(0u, 0u, 0u, 0u);
+    if (un < nunits) {
+      const int tok = tok0 + un * vec / row_elems;
+      if (tok >= 0 && tok < T) dst[i] = *reinterpret_cast<const uint4*>(base + (size_t)un * vec);
+    }
+  }
+}
+
+template <int N, class E>
+__device__ __forceinline__ void stage_commit_seg(E* lds, const uint4 (&src)[N], int nunits, int vec) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const int un = threadIdx.x + 256 * i;
+    if (un < nunits) *reinterpret_cast<uint4*>(lds + (size_t)un * vec) = src[i];
+  }
+}
+
+// Tokens per LDS stage of the backward's inputs: the largest of 16, 8, 4, 2 whose two
+// stage buffers fit beside the reduction table (0: inputs read straight from memory).
+template <class E, int D, int NR>
+constexpr int bwd_stage_tokens() {
+  const int red = 2 * 16 * ((2 + NR) * D + 3 + NR) * 4;
+  for (int nb = 16; nb >= 2; nb /= 2) {
+    const int stage = (4 * nb + 3 + 2 * nb * NR) * D * (int)sizeof(E) + nb * (3 + NR) * 4;
+    if (red + 2 * stage <= 156 * 1024) return nb;
+  }
+  return 0;
+}
+
 // NRK: rank slots compiled in (0 for L = 1, 3 for L <= 4, 7 for L <= 8).  Every loop
 // over the token sequence is software-pipelined: the next token's inputs (and, in the
 // adjoint, its previous state) are loaded while the current token is processed, into
@@ -121,6 +159,7 @@ __global__ __launch_bounds__(256) void bwd_pair_kernel(BwdArgs a) {
   const E* U = reinterpret_cast<const E*>(a.u);
   const E* GM = reinterpret_cast<const E*>(a.gamma);
   const E* DO = reinterpret_cast<const E*>(a.d_o);
+  const float *Gg = a.g, *Gb = a.beta, *Ga = a.alpha;
   float* ckpt = a.ckpt + (size_t)pr * a.nblk * D * D;
   float* scr = a.scratch + (size_t)pr * CK * D * D;
 
@@ -130,7 +169,7 @@ __global__ __launch_bounds__(256) void bwd_pair_kernel(BwdArgs a) {
 #pragma unroll
     for (int r = 0; r < R; ++r) tw[j][r] = L > 1 ? a.conv_w[((size_t)hd * 4 + j) * D + rb * R + r] : 0.f;
 
-  auto load_tok = [&](int t, Tok& x) {
+  auto load_tok = [&](int t, Tok& x) __attribute__((always_inline)) {
     const size_t tr = (size_t)pr * T + t;
 #pragma unroll
     for (int c = 0; c < R; ++c) {
@@ -159,7 +198,7 @@ __global__ __launch_bounds__(256) void bwd_pair_kernel(BwdArgs a) {
     for (int l = 0; l <= NR; ++l) x.al[l] = (L > 1 && l < L) ? a.alpha[tr * L + l] : 0.f;
   };
   // residuals r_{t,0..L-1} and written values W_{t,1..L-1} of this thread's rows
-  auto chain = [&](const Tok& x, float (&rr)[NR + 1][R], float (&W)[NR][R]) {
+  auto chain = [&](const Tok& x, float (&rr)[NR + 1][R], float (&W)[NR][R]) __attribute__((always_inline)) {
 #pragma unroll
     for (int r = 0; r < R; ++r)
       rr[0][r] = x.v[r] - (tw[0][r] * x.vh[0][r] + tw[1][r] * x.vh[1][r] + tw[2][r] * x.vh[2][r] + tw[3][r] * x.v[r]);
@@ -175,7 +214,7 @@ __global__ __launch_bounds__(256) void bwd_pair_kernel(BwdArgs a) {
     }
   };
   // S_t from S_{t-1} (in place)
-  auto fwd_step = [&](float (&M)[R][R], const Tok& x) {
+  auto fwd_step = [&](float (&M)[R][R], const Tok& x) __attribute__((always_inline)) {
     float rr[NR + 1][R], W[NR][R];
     chain(x, rr, W);
     float p[R];
@@ -202,7 +241,7 @@ __global__ __launch_bounds__(256) void bwd_pair_kernel(BwdArgs a) {
   float pend[3][R], dw[4][R];                 // anchor terms owed to tokens t, t-1, t-2; dconv_w share
   int buf = 0;
   // one adjoint step at token t from its inputs x and the state before it, Mp = S_{t-1}
-  auto rev_step = [&](int t, const Tok& x, const float (&Mp)[R][R]) {
+  auto rev_step = [&](int t, const Tok& x, const float (&Mp)[R][R]) __attribute__((always_inline)) {
     const size_t tr = (size_t)pr * T + t;
     float rr[NR + 1][R], W[NR][R];
     chain(x, rr, W);
@@ -343,74 +382,238 @@ __global__ __launch_bounds__(256) void bwd_pair_kernel(BwdArgs a) {
     buf ^= 1;
   };
 
-  // ---- pass 1: the forward, keeping the state entering every block -------------------
+  float Ma[R][R], Mb[R][R];
   float M[R][R];
-#pragma unroll
-  for (int r = 0; r < R; ++r)
-#pragma unroll
-    for (int c = 0; c < R; ++c) M[r][c] = 0.f;
-  Tok xa, xb;
-  load_tok(0, xa);
-  for (int t = 0; t < T; t += 2) {  // tokens t (buffer a) and t + 1 (buffer b)
-    if (t % CK == 0) store_block(ckpt + (size_t)(t / CK) * D * D, M);
-    if (t + 1 < T) load_tok(t + 1, xb);
-    fwd_step(M, xa);
-    if (t + 1 < T) {
-      if ((t + 1) % CK == 0) store_block(ckpt + (size_t)((t + 1) / CK) * D * D, M);
-      if (t + 2 < T) load_tok(t + 2, xa);
-      fwd_step(M, xb);
-    }
-  }
-
-  // ---- pass 2: blocks in reverse -------------------------------------------------------
 #pragma unroll
   for (int r = 0; r < R; ++r) {
 #pragma unroll
-    for (int c = 0; c < R; ++c)
+    for (int c = 0; c < R; ++c) {
+      M[r][c] = 0.f;
       dS[r][c] = a.dS_final != nullptr ? a.dS_final[(size_t)pr * D * D + (size_t)(cb * R + c) * D + rb * R + r] : 0.f;
+    }
 #pragma unroll
     for (int j = 0; j < 3; ++j) pend[j][r] = 0.f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) dw[j][r] = 0.f;
   }
-  float Ma[R][R], Mb[R][R];
-  for (int blk = a.nblk - 1; blk >= 0; --blk) {
-    const int t0 = blk * CK, t1 = min(T, t0 + CK);
-    const float* cp = ckpt + (size_t)blk * D * D;
-    // the block's forward again, keeping every S_t
-    load_block(M, cp);
-    load_tok(t0, xa);
-    for (int t = t0; t < t1; t += 2) {
-      if (t + 1 < t1) load_tok(t + 1, xb);
+  constexpr int NB = bwd_stage_tokens<E, D, NR>();
+  if constexpr (NB > 0) {
+    // ---- inputs staged through LDS, NB tokens at a time ---------------------------------
+    // A stage holds, for tokens s0 .. s0 + NB - 1, the rows of q, k, d_o, the value rows
+    // s0 - 3 .. s0 + NB - 1 (the anchor's window), the rank rows of u and gamma (the
+    // layouts of the inputs, so each is one contiguous run), and g, beta, alpha.  Both
+    // passes visit the stages in a fixed order; the next stage's loads are issued before
+    // the current stage is processed and land in the other buffer after it.
+    constexpr int VEC = 16 / (int)sizeof(E);
+    constexpr int SE = (4 * NB + 3 + 2 * NB * NR) * D;
+    constexpr int SS = NB * (3 + NR);
+    __shared__ __align__(16) E stv[2][SE];
+    __shared__ float sts[2][SS];
+    const int nq = NB * D / VEC, nv = (NB + 3) * D / VEC, nu = NB * Lm1 * D / VEC;
+    constexpr int UQ = (NB * D / VEC + 255) / 256, UV = ((NB + 3) * D / VEC + 255) / 256;
+    constexpr int UU = (NB * NR * D / VEC + 255) / 256;
+    uint4 pq[UQ], pk[UQ], po[UQ], pv[UV], pu[UU], pg[UU];  // the next stage, in flight
+    float pres = 0.f;
+    // one array per loop (no pointer is chosen at run time)
+    auto fetch = [&](int s0) __attribute__((always_inline)) {
+      const size_t row0 = (size_t)pr * T + s0;
+      stage_fetch_seg(pq, Q + row0 * D, nq, VEC, D, s0, T);
+      stage_fetch_seg(pk, K + row0 * D, nq, VEC, D, s0, T);
+      stage_fetch_seg(po, DO + row0 * D, nq, VEC, D, s0, T);
+      stage_fetch_seg(pv, V + row0 * D - 3 * D, nv, VEC, D, s0 - 3, T);
+      if (Lm1 > 0) {
+        stage_fetch_seg(pu, U + row0 * Lm1 * D, nu, VEC, Lm1 * D, s0, T);
+        stage_fetch_seg(pg, GM + row0 * Lm1 * D, nu, VEC, Lm1 * D, s0, T);
+      }
+      // scalars: g, beta (NB each), then alpha (NB x L)
+      pres = 0.f;
+      if (tid < NB * (2 + (L > 1 ? L : 0))) {
+        const int tl = tid < 2 * NB ? tid % NB : (tid - 2 * NB) / L;
+        const size_t tr = row0 + tl;
+        if (s0 + tl < T) {
+          if (tid < NB) pres = Gg[tr];
+          else if (tid < 2 * NB) pres = Gb[tr];
+          else pres = Ga[tr * L + (tid - 2 * NB) % L];
+        }
+      }
+    };
+    auto commit = [&](int bs) __attribute__((always_inline)) {
+      E* b = stv[bs];
+      stage_commit_seg(b, pq, nq, VEC);
+      stage_commit_seg(b + NB * D, pk, nq, VEC);
+      stage_commit_seg(b + 2 * NB * D, po, nq, VEC);
+      stage_commit_seg(b + 3 * NB * D, pv, nv, VEC);
+      if (Lm1 > 0) {
+        stage_commit_seg(b + (4 * NB + 3) * D, pu, nu, VEC);
+        stage_commit_seg(b + (4 * NB + 3) * D + NB * Lm1 * D, pg, nu, VEC);
+      }
+      if (tid < SS) sts[bs][tid] = pres;
+    };
+    const int oU = (4 * NB + 3) * D, oG = oU + NB * Lm1 * D;
+    auto load_tok_s = [&](int bs, int tl, Tok& x) __attribute__((always_inline)) {
+      const E* b = stv[bs];
+#pragma unroll
+      for (int c = 0; c < R; ++c) {
+        x.q[c] = (float)b[tl * D + cb * R + c];
+        x.k[c] = (float)b[(NB + tl) * D + cb * R + c];
+      }
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        x.dO[r] = (float)b[(2 * NB + tl) * D + rb * R + r];
+        x.v[r] = (float)b[(3 * NB + tl + 3) * D + rb * R + r];
+#pragma unroll
+        for (int j = 0; j < 3; ++j) x.vh[j][r] = (float)b[(3 * NB + tl + j) * D + rb * R + r];
+      }
+#pragma unroll
+      for (int l = 0; l < NR; ++l) {
+        if (l < Lm1) {
+#pragma unroll
+          for (int c = 0; c < R; ++c) x.u[l][c] = (float)b[oU + (tl * Lm1 + l) * D + cb * R + c];
+#pragma unroll
+          for (int r = 0; r < R; ++r) x.gm[l][r] = (float)b[oG + (tl * Lm1 + l) * D + rb * R + r];
+        }
+      }
+      x.g = sts[bs][tl];
+      x.beta = sts[bs][NB + tl];
+#pragma unroll
+      for (int l = 0; l <= NR; ++l) x.al[l] = (L > 1 && l < L) ? sts[bs][2 * NB + tl * L + l] : 0.f;
+    };
+
+    // ---- pass 1: the forward, keeping the state entering every block ---------------------
+    const int nst = (T + NB - 1) / NB;
+    int cur = 0;
+    fetch(0);
+    commit(0);
+    __syncthreads();
+    for (int st = 0; st < nst; ++st) {
+      const int s0 = st * NB;
+      if (st + 1 < nst) fetch(s0 + NB);
+      for (int t = s0; t < min(T, s0 + NB); ++t) {
+        if (t % CK == 0) store_block(ckpt + (size_t)(t / CK) * D * D, M);
+        Tok x;
+        load_tok_s(cur, t - s0, x);
+        fwd_step(M, x);
+      }
+      if (st + 1 < nst) commit(cur ^ 1);
+      __syncthreads();
+      cur ^= 1;
+    }
+
+    // ---- pass 2: per block (last first) its stages ascending (the block's forward again,
+    // keeping every S_t), then descending (the adjoint steps, last token first) -------------
+    int blk = a.nblk - 1, j = 0;
+    bool rev = false;
+    auto nstb = [&](int b) __attribute__((always_inline)) { return (min(T, b * CK + CK) - b * CK + NB - 1) / NB; };
+    fetch(blk * CK);
+    commit(cur);
+    __syncthreads();
+    while (blk >= 0) {
+      const int t0 = blk * CK, t1 = min(T, t0 + CK), s0 = t0 + j * NB, s1 = min(t1, s0 + NB);
+      // the visit after this one
+      int nb_ = blk, nj = j;
+      bool nrev = rev;
+      if (!rev) {
+        if (j + 1 < nstb(blk)) nj = j + 1;
+        else nrev = true;
+      } else {
+        if (j > 0) nj = j - 1;
+        else { nb_ = blk - 1; nj = 0; nrev = false; }
+      }
+      const bool more = nb_ >= 0;
+      if (more) fetch(nb_ * CK + nj * NB);
+      if (!rev) {
+        if (j == 0) load_block(M, ckpt + (size_t)blk * D * D);
+        for (int t = s0; t < s1; ++t) {
+          Tok x;
+          load_tok_s(cur, t - s0, x);
+          fwd_step(M, x);
+          store_block(scr + (size_t)(t - t0) * D * D, M);
+        }
+        if (s1 == t1) {
+#pragma unroll
+          for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int c = 0; c < R; ++c) St[r][c] = M[r][c];
+        }
+      } else {
+        const float* cp = ckpt + (size_t)blk * D * D;
+        auto prev_state = [&](int t) __attribute__((always_inline)) { return t > t0 ? scr + (size_t)(t - 1 - t0) * D * D : cp; };
+        load_block(Ma, prev_state(s1 - 1));
+        for (int t = s1 - 1; t >= s0; t -= 2) {  // tokens t (Ma) and t - 1 (Mb)
+          if (t - 1 >= s0) load_block(Mb, prev_state(t - 1));
+          Tok x;
+          load_tok_s(cur, t - s0, x);
+          rev_step(t, x, Ma);
+          if (t - 1 >= s0) {
+            if (t - 2 >= s0) load_block(Ma, prev_state(t - 2));
+            Tok y;
+            load_tok_s(cur, t - 1 - s0, y);
+            rev_step(t - 1, y, Mb);
+          }
+        }
+      }
+      if (more) commit(cur ^ 1);
+      __syncthreads();
+      cur ^= 1;
+      blk = nb_;
+      j = nj;
+      rev = nrev;
+    }
+  } else {
+    // ---- inputs read straight from memory (shapes whose stages do not fit in LDS) ------
+    // ---- pass 1: the forward, keeping the state entering every block -------------------
+    Tok xa, xb;
+    load_tok(0, xa);
+    for (int t = 0; t < T; t += 2) {  // tokens t (buffer a) and t + 1 (buffer b)
+      if (t % CK == 0) store_block(ckpt + (size_t)(t / CK) * D * D, M);
+      if (t + 1 < T) load_tok(t + 1, xb);
       fwd_step(M, xa);
-      store_block(scr + (size_t)(t - t0) * D * D, M);
-      if (t + 1 < t1) {
-        if (t + 2 < t1) load_tok(t + 2, xa);
+      if (t + 1 < T) {
+        if ((t + 1) % CK == 0) store_block(ckpt + (size_t)((t + 1) / CK) * D * D, M);
+        if (t + 2 < T) load_tok(t + 2, xa);
         fwd_step(M, xb);
-        store_block(scr + (size_t)(t + 1 - t0) * D * D, M);
       }
     }
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-      for (int c = 0; c < R; ++c) St[r][c] = M[r][c];
-    // the adjoint steps, last token first (S_{t-1} is the block state t - 1 - t0, or the
-    // checkpoint for the first token)
-    auto prev_state = [&](int t) { return t > t0 ? scr + (size_t)(t - 1 - t0) * D * D : cp; };
-    load_tok(t1 - 1, xa);
-    load_block(Ma, prev_state(t1 - 1));
-    for (int t = t1 - 1; t >= t0; t -= 2) {  // tokens t (buffers a) and t - 1 (buffers b)
-      if (t - 1 >= t0) {
-        load_tok(t - 1, xb);
-        load_block(Mb, prev_state(t - 1));
-      }
-      rev_step(t, xa, Ma);
-      if (t - 1 >= t0) {
-        if (t - 2 >= t0) {
-          load_tok(t - 2, xa);
-          load_block(Ma, prev_state(t - 2));
+
+    // ---- pass 2: blocks in reverse -------------------------------------------------------
+    for (int blk = a.nblk - 1; blk >= 0; --blk) {
+      const int t0 = blk * CK, t1 = min(T, t0 + CK);
+      const float* cp = ckpt + (size_t)blk * D * D;
+      // the block's forward again, keeping every S_t
+      load_block(M, cp);
+      load_tok(t0, xa);
+      for (int t = t0; t < t1; t += 2) {
+        if (t + 1 < t1) load_tok(t + 1, xb);
+        fwd_step(M, xa);
+        store_block(scr + (size_t)(t - t0) * D * D, M);
+        if (t + 1 < t1) {
+          if (t + 2 < t1) load_tok(t + 2, xa);
+          fwd_step(M, xb);
+          store_block(scr + (size_t)(t + 1 - t0) * D * D, M);
         }
-        rev_step(t - 1, xb, Mb);
+      }
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int c = 0; c < R; ++c) St[r][c] = M[r][c];
+      // the adjoint steps, last token first (S_{t-1} is the block state t - 1 - t0, or the
+      // checkpoint for the first token)
+      auto prev_state = [&](int t) __attribute__((always_inline)) { return t > t0 ? scr + (size_t)(t - 1 - t0) * D * D : cp; };
+      load_tok(t1 - 1, xa);
+      load_block(Ma, prev_state(t1 - 1));
+      for (int t = t1 - 1; t >= t0; t -= 2) {  // tokens t (buffers a) and t - 1 (buffers b)
+        if (t - 1 >= t0) {
+          load_tok(t - 1, xb);
+          load_block(Mb, prev_state(t - 1));
+        }
+        rev_step(t, xa, Ma);
+        if (t - 1 >= t0) {
+          if (t - 2 >= t0) {
+            load_tok(t - 2, xa);
+            load_block(Ma, prev_state(t - 2));
+          }
+          rev_step(t - 1, xb, Mb);
+        }
       }
     }
   }
