@@ -87,3 +87,49 @@ def test_bwd_deterministic():
     torch.cuda.synchronize()
     for n in a:
         assert torch.equal(a[n], b[n]), n
+
+
+@pytest.mark.parametrize("which", ["v", "q"])
+def test_bwd_full_size_linear_directions(which):
+    """At the full 16K bf16 workload (B=2, H=4, T=16384, d=64, L=4): o and S_final are linear
+    in v (A_t does not depend on v; B_t, the anchor and the residual chain are linear in it)
+    and o is linear in q (S does not depend on q), so for any direction e
+        <d_o, o(x := e)> + <dS_final, S_final(x := e)> = <dx, e>
+    with the forward kernel on the left and the backward kernel on the right (dx does not
+    depend on x).  Both sides carry bf16 rounding of their operands (a relative error of a
+    few 2^-9 per element, with random signs), so the bound is 2^-6 sqrt(sum (d_o o)^2):
+    about 23 here, against sums of a few hundred to a thousand that a wrong gradient would
+    miss by their own size."""
+    if not gpu_available():
+        pytest.skip("no GPU")
+    import torch
+    import delta_rule_sequence_amd as prism
+    import workloads
+    w = workloads.workload("rec16k_bf16")
+    print(f"[bwd] full-size linear direction {which} on {w.name}", flush=True)
+    x = workloads.generate(w)
+    dev = workloads.to_torch(x, w.dtype, "cuda")
+    gen = torch.Generator(device="cuda").manual_seed(17)
+    d_o = torch.randn((w.B, w.H, w.T, w.dv), device="cuda", generator=gen).to(torch.bfloat16)
+    dS = torch.randn((w.B, w.H, w.dk, w.dv), device="cuda", generator=gen)
+    e = torch.randn(dev[which].shape, device="cuda", generator=gen).to(torch.bfloat16)
+    if which == "q":
+        e = e / e.float().norm(dim=-1, keepdim=True).to(torch.bfloat16)
+    grads = prism.bwd(dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], dev["u"], dev["alpha"], dev["gamma"],
+                      dev["conv_w"], L=w.L, d_o=d_o, dS_final=dS)
+    args = dict(dev)
+    args[which] = e
+    o, S = prism.fwd(args["q"], args["k"], args["v"], args["g"], args["beta"], args["u"], args["alpha"],
+                     args["gamma"], args["conv_w"], L=w.L, chunk=w.chunk)
+    torch.cuda.synchronize()
+    prod = d_o.double() * o.double()
+    lhs = float(prod.sum())
+    sq = float((prod * prod).sum())
+    if which == "v":
+        prodS = dS.double() * S.double()
+        lhs += float(prodS.sum())
+        sq += float((prodS * prodS).sum())
+    rhs = float((grads["d" + which].double() * e.double()).sum())
+    bound = 2.0 ** -6 * sq ** 0.5
+    print(f"[bwd] <d_o, o(e)> = {lhs:.6e}, <d{which}, e> = {rhs:.6e}, bound {bound:.3e}", flush=True)
+    assert abs(lhs - rhs) <= bound, (lhs, rhs, bound)
