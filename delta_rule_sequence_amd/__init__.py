@@ -49,6 +49,10 @@ def load_library() -> ctypes.CDLL:
     lib.prism_bwd.restype = ctypes.c_int
     lib.prism_bwd_workspace_bytes.argtypes = [i] * 7
     lib.prism_bwd_workspace_bytes.restype = sz
+    lib.prism_bwd_lowmem.argtypes = lib.prism_bwd.argtypes
+    lib.prism_bwd_lowmem.restype = ctypes.c_int
+    lib.prism_bwd_lowmem_workspace_bytes.argtypes = [i] * 7
+    lib.prism_bwd_lowmem_workspace_bytes.restype = sz
     lib.prism_fwd_workspace_bytes.argtypes = [i] * 8
     lib.prism_fwd_workspace_bytes.restype = sz
     lib.prism_fwd_seg_workspace_bytes.argtypes = [i] * 9
@@ -251,10 +255,11 @@ def fwd(q, k, v, g, beta, u=None, alpha=None, gamma=None, conv_w=None, L: int = 
 
 
 def bwd(q, k, v, g, beta, u=None, alpha=None, gamma=None, conv_w=None, L: int = 1, d_o=None,
-        dS_final=None, workspace=None, stream=None):
+        dS_final=None, workspace=None, stream=None, low_memory: bool = False):
     """Gradients of sum <d_o, o> + <dS_final, S_final> for fwd(q, ..., conv_w, L) (zero start).
 
     Inputs as fwd(); d_o [B,H,T,dv] in the input dtype; dS_final [B,H,dk,dv] float32 or None.
+    low_memory: use prism_bwd_lowmem (states every 64 tokens only).
     Returns a dict of float32 tensors dq, dk, dv, dg, dbeta and, when L > 1, du, dalpha,
     dgamma, dconv_w (the shapes of the corresponding inputs; dconv_w summed over the batch).
     """
@@ -282,11 +287,13 @@ def bwd(q, k, v, g, beta, u=None, alpha=None, gamma=None, conv_w=None, L: int = 
     if L > 1:
         out.update({"du": torch.empty((B, H, T, L - 1, dk), **f32), "dalpha": torch.empty((B, H, T, L), **f32),
                     "dgamma": torch.empty((B, H, T, L - 1, dv), **f32), "dconv_w": torch.empty((H, 4, dv), **f32)})
-    need = lib.prism_bwd_workspace_bytes(B, H, T, dk, dv, L, dt) or 1
+    wsb = lib.prism_bwd_lowmem_workspace_bytes if low_memory else lib.prism_bwd_workspace_bytes
+    need = wsb(B, H, T, dk, dv, L, dt) or 1
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     s = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
-    st = lib.prism_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+    fn = lib.prism_bwd_lowmem if low_memory else lib.prism_bwd
+    st = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                        _ptr(u) if L > 1 else None, _ptr(alpha) if L > 1 else None,
                        _ptr(gamma) if L > 1 else None, _ptr(conv_w) if L > 1 else None,
                        B, H, T, dk, dv, L, dt, _ptr(d_o), _ptr(dS_final),
@@ -295,5 +302,5 @@ def bwd(q, k, v, g, beta, u=None, alpha=None, gamma=None, conv_w=None, L: int = 
                        _ptr(out.get("dconv_w")),
                        ctypes.c_void_p(workspace.data_ptr()), workspace.numel(), ctypes.c_void_p(s))
     if st != 0:
-        raise PrismError(f"prism_bwd failed: {status_string(st)}")
+        raise PrismError(f"{'prism_bwd_lowmem' if low_memory else 'prism_bwd'} failed: {status_string(st)}")
     return out

@@ -216,10 +216,27 @@ prism_status decode_dispatch(int d, const prism::DecodeArgs& a, int P, hipStream
 // per-pair dconv_w shares [P][4][D], all float32, 256-byte aligned regions.
 struct BwdPlan {
   int P, nblk;
+  bool all_states;
   size_t off_ckpt, off_scr, off_part, total;
 };
 
-prism_status make_bwd_plan(int B, int H, int T, int dk, int dv, int L, prism_dtype dt, BwdPlan* pl) {
+// Keep the state after every token (instead of one per 64 tokens and a re-run of each
+// block) when those states take at most this much memory and the kernel stages its inputs
+// through LDS: one sequential forward sweep fewer.
+constexpr size_t kBwdAllStatesMax = (size_t)4 << 30;
+
+template <class E>
+bool bwd_staged(int d, int L) {
+  const int nr = L == 1 ? 1 : L <= 4 ? 3 : 7;
+#define PRISM_NB(D) (nr == 1 ? prism::bwd_stage_tokens<E, D, 1>() : nr == 3 ? prism::bwd_stage_tokens<E, D, 3>() \
+                                                                          : prism::bwd_stage_tokens<E, D, 7>())
+  const int nb = d == 16 ? PRISM_NB(16) : d == 32 ? PRISM_NB(32) : d == 64 ? PRISM_NB(64) : PRISM_NB(128);
+#undef PRISM_NB
+  return nb > 0;
+}
+
+prism_status make_bwd_plan(int B, int H, int T, int dk, int dv, int L, prism_dtype dt, BwdPlan* pl,
+                           bool low_memory = false) {
   if (B <= 0 || H <= 0 || T <= 0) return PRISM_ERR_INVALID_ARG;
   if (dt != PRISM_F32 && dt != PRISM_BF16) return PRISM_ERR_INVALID_ARG;
   if (L < 1 || L > 8) return PRISM_ERR_UNSUPPORTED;
@@ -228,8 +245,17 @@ prism_status make_bwd_plan(int B, int H, int T, int dk, int dv, int L, prism_dty
   if (!mul_ok((size_t)B, (size_t)H, &P) || P > (size_t)INT32_MAX) return PRISM_ERR_INVALID_ARG;
   const size_t nblk = ((size_t)T + prism::kBwdBlock - 1) / prism::kBwdBlock;
   const size_t dd = (size_t)dk * dk * 4;
-  if (!mul_ok(P, nblk, &a) || !mul_ok(a, dd, &sz_ckpt)) return PRISM_ERR_INVALID_ARG;
-  if (!mul_ok(P, (size_t)prism::kBwdBlock, &b) || !mul_ok(b, dd, &sz_scr)) return PRISM_ERR_INVALID_ARG;
+  size_t sz_all;
+  const bool staged = dt == PRISM_BF16 ? bwd_staged<bf16_t>(dk, L) : bwd_staged<float>(dk, L);
+  pl->all_states = !low_memory && staged && mul_ok(P, (size_t)T, &a) && mul_ok(a, dd, &sz_all) &&
+                   sz_all <= kBwdAllStatesMax;
+  if (pl->all_states) {
+    sz_ckpt = sz_all;
+    sz_scr = 0;
+  } else {
+    if (!mul_ok(P, nblk, &a) || !mul_ok(a, dd, &sz_ckpt)) return PRISM_ERR_INVALID_ARG;
+    if (!mul_ok(P, (size_t)prism::kBwdBlock, &b) || !mul_ok(b, dd, &sz_scr)) return PRISM_ERR_INVALID_ARG;
+  }
   if (!mul_ok(P, (size_t)4 * dk * 4, &sz_part)) return PRISM_ERR_INVALID_ARG;
   // inputs must be addressable: P*T*(L-1)*dk elements
   if (!mul_ok(P, (size_t)T, &c) || !mul_ok(c, (size_t)L * dk * 4, &c)) return PRISM_ERR_INVALID_ARG;
@@ -271,15 +297,24 @@ size_t prism_bwd_workspace_bytes(int B, int H, int T, int dk, int dv, int L, pri
   return make_bwd_plan(B, H, T, dk, dv, L, dt, &pl) == PRISM_OK ? pl.total : 0;
 }
 
-prism_status prism_bwd(const void* q, const void* k, const void* v, const float* g, const float* beta,
-                       const void* u, const float* alpha, const void* gamma, const float* conv_w,
-                       int B, int H, int T, int dk, int dv, int L, prism_dtype dt,
-                       const void* d_o, const float* dS_final,
-                       float* dq, float* dk_out, float* dv_out, float* dg, float* dbeta,
-                       float* du, float* dalpha, float* dgamma, float* dconv_w,
-                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
+size_t prism_bwd_lowmem_workspace_bytes(int B, int H, int T, int dk, int dv, int L, prism_dtype dt) {
   BwdPlan pl;
-  prism_status st = make_bwd_plan(B, H, T, dk, dv, L, dt, &pl);
+  return make_bwd_plan(B, H, T, dk, dv, L, dt, &pl, true) == PRISM_OK ? pl.total : 0;
+}
+
+}  // extern "C"
+
+namespace {
+
+prism_status bwd_impl(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                      const void* u, const float* alpha, const void* gamma, const float* conv_w,
+                      int B, int H, int T, int dk, int dv, int L, prism_dtype dt,
+                      const void* d_o, const float* dS_final,
+                      float* dq, float* dk_out, float* dv_out, float* dg, float* dbeta,
+                      float* du, float* dalpha, float* dgamma, float* dconv_w,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream, bool low_memory) {
+  BwdPlan pl;
+  prism_status st = make_bwd_plan(B, H, T, dk, dv, L, dt, &pl, low_memory);
   if (st != PRISM_OK) return st;
   if (!q || !k || !v || !g || !beta || !d_o || !dq || !dk_out || !dv_out || !dg || !dbeta)
     return PRISM_ERR_INVALID_ARG;
@@ -295,12 +330,38 @@ prism_status prism_bwd(const void* q, const void* k, const void* v, const float*
   a.ckpt = reinterpret_cast<float*>(ws + pl.off_ckpt);
   a.scratch = reinterpret_cast<float*>(ws + pl.off_scr);
   a.dconv_part = reinterpret_cast<float*>(ws + pl.off_part);
-  a.H = H; a.T = T; a.L = L; a.nblk = pl.nblk;
+  a.H = H; a.T = T; a.L = L; a.nblk = pl.nblk; a.all_states = pl.all_states ? 1 : 0;
   st = dt == PRISM_BF16 ? bwd_dispatch<bf16_t>(dk, a, pl.P, stream) : bwd_dispatch<float>(dk, a, pl.P, stream);
   if (st != PRISM_OK || L == 1) return st;
   hipLaunchKernelGGL(prism::bwd_conv_reduce_kernel, dim3(H), dim3(256), 0, stream,
                      static_cast<const float*>(a.dconv_part), dconv_w, B, H, dk);
   return hipGetLastError() == hipSuccess ? PRISM_OK : PRISM_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+prism_status prism_bwd(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                       const void* u, const float* alpha, const void* gamma, const float* conv_w,
+                       int B, int H, int T, int dk, int dv, int L, prism_dtype dt,
+                       const void* d_o, const float* dS_final,
+                       float* dq, float* dk_out, float* dv_out, float* dg, float* dbeta,
+                       float* du, float* dalpha, float* dgamma, float* dconv_w,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return bwd_impl(q, k, v, g, beta, u, alpha, gamma, conv_w, B, H, T, dk, dv, L, dt, d_o, dS_final, dq, dk_out,
+                  dv_out, dg, dbeta, du, dalpha, dgamma, dconv_w, workspace, workspace_bytes, stream, false);
+}
+
+prism_status prism_bwd_lowmem(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                              const void* u, const float* alpha, const void* gamma, const float* conv_w,
+                              int B, int H, int T, int dk, int dv, int L, prism_dtype dt,
+                              const void* d_o, const float* dS_final,
+                              float* dq, float* dk_out, float* dv_out, float* dg, float* dbeta,
+                              float* du, float* dalpha, float* dgamma, float* dconv_w,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return bwd_impl(q, k, v, g, beta, u, alpha, gamma, conv_w, B, H, T, dk, dv, L, dt, d_o, dS_final, dq, dk_out,
+                  dv_out, dg, dbeta, du, dalpha, dgamma, dconv_w, workspace, workspace_bytes, stream, true);
 }
 
 

@@ -36,9 +36,11 @@ struct BwdArgs {
   const float *g, *beta, *alpha, *conv_w, *dS_final;
   float *dq, *dk, *dv, *dg, *dbeta, *du, *dalpha, *dgamma;
   float* dconv_part;  // [P][4][D] this pair's share of dconv_w
-  float* ckpt;        // [P][nblk][D * D] state entering each block (thread-block order)
+  float* ckpt;        // [P][nblk][D * D] state entering each block (thread-block order), or
+                      // with all_states: [P][T][D * D] the state after every token
   float* scratch;     // [P][kBwdBlock][D * D] states S_t of the block being reversed
   int H, T, L, nblk;
+  int all_states;  // 1: keep every S_t (one forward sweep fewer); only with LDS staging
 };
 
 // One token's inputs as seen by thread (rb, cb): key-side entries of its columns,
@@ -160,7 +162,7 @@ __global__ __launch_bounds__(256) void bwd_pair_kernel(BwdArgs a) {
   const E* GM = reinterpret_cast<const E*>(a.gamma);
   const E* DO = reinterpret_cast<const E*>(a.d_o);
   const float *Gg = a.g, *Gb = a.beta, *Ga = a.alpha;
-  float* ckpt = a.ckpt + (size_t)pr * a.nblk * D * D;
+  float* ckpt = a.ckpt + (size_t)pr * (a.all_states ? T : a.nblk) * D * D;
   float* scr = a.scratch + (size_t)pr * CK * D * D;
 
   float tw[4][R];  // conv taps of this thread's rows
@@ -479,8 +481,10 @@ __global__ __launch_bounds__(256) void bwd_pair_kernel(BwdArgs a) {
       for (int l = 0; l <= NR; ++l) x.al[l] = (L > 1 && l < L) ? sts[bs][2 * NB + tl * L + l] : 0.f;
     };
 
-    // ---- pass 1: the forward, keeping the state entering every block ---------------------
+    // ---- pass 1: the forward, keeping the state entering every block (or, with
+    // all_states, the state after every token) ----------------------------------------------
     const int nst = (T + NB - 1) / NB;
+    const bool all = a.all_states != 0;
     int cur = 0;
     fetch(0);
     commit(0);
@@ -489,15 +493,57 @@ __global__ __launch_bounds__(256) void bwd_pair_kernel(BwdArgs a) {
       const int s0 = st * NB;
       if (st + 1 < nst) fetch(s0 + NB);
       for (int t = s0; t < min(T, s0 + NB); ++t) {
-        if (t % CK == 0) store_block(ckpt + (size_t)(t / CK) * D * D, M);
+        if (!all && t % CK == 0) store_block(ckpt + (size_t)(t / CK) * D * D, M);
         Tok x;
         load_tok_s(cur, t - s0, x);
         fwd_step(M, x);
+        if (all) store_block(ckpt + (size_t)t * D * D, M);
       }
       if (st + 1 < nst) commit(cur ^ 1);
       __syncthreads();
       cur ^= 1;
     }
+    if (all) {
+      // ---- pass 2 with every S_t kept: the adjoint steps over the stages, last first -----
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int c = 0; c < R; ++c) St[r][c] = M[r][c];
+      // S_{t-1}: the kept state, zero before the first token
+      auto prev_state = [&](float (&Mx)[R][R], int t) __attribute__((always_inline)) {
+        if (t > 0) {
+          load_block(Mx, ckpt + (size_t)(t - 1) * D * D);
+        } else {
+#pragma unroll
+          for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int c = 0; c < R; ++c) Mx[r][c] = 0.f;
+        }
+      };
+      fetch((nst - 1) * NB);
+      commit(cur);
+      __syncthreads();
+      for (int st = nst - 1; st >= 0; --st) {
+        const int s0 = st * NB, s1 = min(T, s0 + NB);
+        if (st > 0) fetch(s0 - NB);
+        prev_state(Ma, s1 - 1);
+        for (int t = s1 - 1; t >= s0; t -= 2) {  // tokens t (Ma) and t - 1 (Mb)
+          if (t - 1 >= s0) prev_state(Mb, t - 1);
+          Tok x;
+          load_tok_s(cur, t - s0, x);
+          rev_step(t, x, Ma);
+          if (t - 1 >= s0) {
+            if (t - 2 >= s0) prev_state(Ma, t - 2);
+            Tok y;
+            load_tok_s(cur, t - 1 - s0, y);
+            rev_step(t - 1, y, Mb);
+          }
+        }
+        if (st > 0) commit(cur ^ 1);
+        __syncthreads();
+        cur ^= 1;
+      }
+    } else {
 
     // ---- pass 2: per block (last first) its stages ascending (the block's forward again,
     // keeping every S_t), then descending (the adjoint steps, last token first) -------------
@@ -558,6 +604,7 @@ __global__ __launch_bounds__(256) void bwd_pair_kernel(BwdArgs a) {
       blk = nb_;
       j = nj;
       rev = nrev;
+    }
     }
   } else {
     // ---- inputs read straight from memory (shapes whose stages do not fit in LDS) ------

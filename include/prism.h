@@ -176,9 +176,11 @@ prism_status prism_fwd_timed(const void* q, const void* k, const void* v,
  *   dconv_w [H, 4, dv] (summed over the batch)
  * The four rank-L gradients are not written when L == 1 (they may be NULL then) and
  * are required otherwise.  Supported: dk == dv in {16, 32, 64, 128}, 1 <= L <= 8,
- * B * H <= 2^31 - 1.  Workspace: prism_bwd_workspace_bytes (the checkpoints, a
- * 64-token state buffer per pair and the per-pair dconv_w shares).  Ownership, stream
- * and errors as prism_fwd. */
+ * B * H <= 2^31 - 1.  Workspace: prism_bwd_workspace_bytes.  When every per-token state
+ * fits in 4 GiB (B*H*T*dk*dv*4 bytes) the workspace keeps all of them and the forward is
+ * re-run once; otherwise it keeps the state every 64 tokens plus a 64-token buffer per pair
+ * and re-runs each 64-token block (one more forward sweep).  Ownership, stream and errors
+ * as prism_fwd. */
 size_t prism_bwd_workspace_bytes(int B, int H, int T, int dk, int dv, int L, prism_dtype dt);
 prism_status prism_bwd(const void* q, const void* k, const void* v,
                        const float* g, const float* beta,
@@ -189,6 +191,21 @@ prism_status prism_bwd(const void* q, const void* k, const void* v,
                        float* dq, float* dk_out, float* dv_out, float* dg, float* dbeta,
                        float* du, float* dalpha, float* dgamma, float* dconv_w,
                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* The same gradients with the low-memory workspace whatever the size: the state every 64
+ * tokens plus a 64-token buffer per pair (O(T / 64) states instead of O(T)), at the cost
+ * of one more sequential forward sweep.  For callers with little free device memory.
+ * Arguments, layouts and errors as prism_bwd; workspace: prism_bwd_lowmem_workspace_bytes. */
+size_t prism_bwd_lowmem_workspace_bytes(int B, int H, int T, int dk, int dv, int L, prism_dtype dt);
+prism_status prism_bwd_lowmem(const void* q, const void* k, const void* v,
+                              const float* g, const float* beta,
+                              const void* u, const float* alpha, const void* gamma,
+                              const float* conv_w,
+                              int B, int H, int T, int dk, int dv, int L, prism_dtype dt,
+                              const void* d_o, const float* dS_final,
+                              float* dq, float* dk_out, float* dv_out, float* dg, float* dbeta,
+                              float* du, float* dalpha, float* dgamma, float* dconv_w,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* A static, human-readable name of a status code. */
 const char* prism_status_string(prism_status s);

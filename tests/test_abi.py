@@ -191,5 +191,9 @@ def test_bwd_argument_checks(lib):
     assert need > 0
     assert _bwd_call(lib, ws_bytes=need - 1) == WORKSPACE
     assert lib.prism_bwd_workspace_bytes(1, 1, 64, 16, 32, 2, 1) == 0
-    # one 64-token checkpoint more per pair once T passes a multiple of 64
+    # the low-memory form keeps one state per 64 tokens: one more once T passes a multiple of 64
+    low = lib.prism_bwd_lowmem_workspace_bytes(1, 1, 64, 16, 16, 2, 1)
+    assert 0 < low and lib.prism_bwd_lowmem_workspace_bytes(1, 1, 65, 16, 16, 2, 1) > low
+    # the default keeps every per-token state while they fit: it grows with T
     assert lib.prism_bwd_workspace_bytes(1, 1, 65, 16, 16, 2, 1) > need
+    assert lib.prism_bwd_workspace_bytes(1, 1, 4096, 64, 64, 4, 1) > lib.prism_bwd_lowmem_workspace_bytes(1, 1, 4096, 64, 64, 4, 1)

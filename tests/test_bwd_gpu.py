@@ -39,8 +39,9 @@ def _setup(dtype, B, H, T, d, L, with_dS, seed):
     return w, x, d_o, dS
 
 
+@pytest.mark.parametrize("low_memory", [False, True], ids=["all_states", "lowmem"])
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
-def test_bwd_matches_oracle(case):
+def test_bwd_matches_oracle(case, low_memory):
     if not gpu_available():
         pytest.skip("no GPU")
     import torch
@@ -48,13 +49,13 @@ def test_bwd_matches_oracle(case):
     import workloads
     from oracle import prism_grad
     name, dtype, B, H, T, d, L, with_dS = case
-    print(f"[bwd] {name}", flush=True)
+    print(f"[bwd] {name} low_memory={low_memory}", flush=True)
     w, x, d_o, dS = _setup(dtype, B, H, T, d, L, with_dS, seed=len(name) + T)
     dev = workloads.to_torch(x, dtype, "cuda")
     vt = torch.bfloat16 if dtype == "bf16" else torch.float32
     got = prism.bwd(dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], dev["u"], dev["alpha"], dev["gamma"],
                     dev["conv_w"], L=L, d_o=torch.tensor(d_o, device="cuda").to(vt),
-                    dS_final=None if dS is None else torch.tensor(dS, device="cuda"))
+                    dS_final=None if dS is None else torch.tensor(dS, device="cuda"), low_memory=low_memory)
     torch.cuda.synchronize()
     ref = prism_grad.backward(x["q"], x["k"], x["v"], x["g"], x["beta"], x["u"], x["alpha"], x["gamma"],
                               x["conv_w"], L, d_o, dS)
