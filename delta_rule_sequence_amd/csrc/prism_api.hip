@@ -217,8 +217,11 @@ prism_status decode_dispatch(int d, const prism::DecodeArgs& a, int P, hipStream
 struct BwdPlan {
   int P, nblk;
   bool all_states;
-  size_t off_ckpt, off_scr, off_part, total;
+  size_t off_ckpt, off_scr, off_part, off_red, total;
 };
+
+// rank slots compiled in for L (0 for L = 1, 3 for L <= 4, 7 for L <= 8)
+inline int bwd_rank_slots(int L) { return L == 1 ? 0 : L <= 4 ? 3 : 7; }
 
 // Keep the state after every token (instead of one per 64 tokens and a re-run of each
 // block) when those states take at most this much memory and the kernel stages its inputs
@@ -257,6 +260,14 @@ prism_status make_bwd_plan(int B, int H, int T, int dk, int dv, int L, prism_dty
     if (!mul_ok(P, (size_t)prism::kBwdBlock, &b) || !mul_ok(b, dd, &sz_scr)) return PRISM_ERR_INVALID_ARG;
   }
   if (!mul_ok(P, (size_t)4 * dk * 4, &sz_part)) return PRISM_ERR_INVALID_ARG;
+  // per-workgroup column sums and scalars when a pair's rows span dk / 16 > 1 workgroups
+  size_t sz_red = 0;
+  const int nsp = dk / 16, nr = bwd_rank_slots(L) > 0 ? bwd_rank_slots(L) : 1;
+  if (nsp > 1) {
+    const size_t red = (size_t)(2 + nr) * dk + 3 + nr;
+    size_t x;
+    if (!mul_ok(P, (size_t)nsp * T, &x) || !mul_ok(x, red * 4, &sz_red)) return PRISM_ERR_INVALID_ARG;
+  }
   // inputs must be addressable: P*T*(L-1)*dk elements
   if (!mul_ok(P, (size_t)T, &c) || !mul_ok(c, (size_t)L * dk * 4, &c)) return PRISM_ERR_INVALID_ARG;
   pl->P = (int)P;
@@ -264,18 +275,31 @@ prism_status make_bwd_plan(int B, int H, int T, int dk, int dv, int L, prism_dty
   pl->off_ckpt = 0;
   pl->off_scr = align_up(sz_ckpt);
   pl->off_part = align_up(pl->off_scr + sz_scr);
-  pl->total = align_up(pl->off_part + sz_part);
+  pl->off_red = align_up(pl->off_part + sz_part);
+  pl->total = align_up(pl->off_red + sz_red);
   if (pl->total < sz_ckpt) return PRISM_ERR_INVALID_ARG;
   return PRISM_OK;
+}
+
+// D / 16 workgroups per pair (16 state rows each); then, when that is more than one, the
+// fixed-order sum of their per-token partials (8 tokens per workgroup, 1-D grid).
+template <class E, int D, int NRK>
+void bwd_launch_d(const prism::BwdArgs& a, int P, hipStream_t stream) {
+  constexpr int NSP = D / 16;
+  hipLaunchKernelGGL((prism::bwd_pair_kernel<E, D, NRK>), dim3((unsigned)P * NSP), dim3(256), 0, stream, a);
+  if constexpr (NSP > 1) {
+    const unsigned nt8 = (unsigned)((a.T + 7) / 8);
+    hipLaunchKernelGGL((prism::bwd_part_reduce_kernel<D, NRK>), dim3((unsigned)P * nt8), dim3(256), 0, stream, a);
+  }
 }
 
 template <class E, int NRK>
 void bwd_launch(int d, const prism::BwdArgs& a, int P, hipStream_t stream) {
   switch (d) {
-    case 16: hipLaunchKernelGGL((prism::bwd_pair_kernel<E, 16, NRK>), dim3(P), dim3(256), 0, stream, a); break;
-    case 32: hipLaunchKernelGGL((prism::bwd_pair_kernel<E, 32, NRK>), dim3(P), dim3(256), 0, stream, a); break;
-    case 64: hipLaunchKernelGGL((prism::bwd_pair_kernel<E, 64, NRK>), dim3(P), dim3(256), 0, stream, a); break;
-    default: hipLaunchKernelGGL((prism::bwd_pair_kernel<E, 128, NRK>), dim3(P), dim3(256), 0, stream, a); break;
+    case 16: bwd_launch_d<E, 16, NRK>(a, P, stream); break;
+    case 32: bwd_launch_d<E, 32, NRK>(a, P, stream); break;
+    case 64: bwd_launch_d<E, 64, NRK>(a, P, stream); break;
+    default: bwd_launch_d<E, 128, NRK>(a, P, stream); break;
   }
 }
 
@@ -330,6 +354,7 @@ prism_status bwd_impl(const void* q, const void* k, const void* v, const float* 
   a.ckpt = reinterpret_cast<float*>(ws + pl.off_ckpt);
   a.scratch = reinterpret_cast<float*>(ws + pl.off_scr);
   a.dconv_part = reinterpret_cast<float*>(ws + pl.off_part);
+  a.part = reinterpret_cast<float*>(ws + pl.off_red);
   a.H = H; a.T = T; a.L = L; a.nblk = pl.nblk; a.all_states = pl.all_states ? 1 : 0;
   st = dt == PRISM_BF16 ? bwd_dispatch<bf16_t>(dk, a, pl.P, stream) : bwd_dispatch<float>(dk, a, pl.P, stream);
   if (st != PRISM_OK || L == 1) return st;

@@ -16,11 +16,12 @@
 //   dW_{t,l} = dS_t u_{t,l}, then back through the residual chain to alpha, gamma, v, w
 //   dS_{t-1} = g (dS_t - beta e k_t^T)
 //
-// One workgroup of 256 threads per pair; thread (rb, cb) = (tid / 16, tid % 16) owns the
-// R x R block (R = D / 16) of rows rb R .. and columns cb R .. of S and dS.  Sums over a row
-// run through the 16 lanes of the thread's row group (DPP butterfly); sums over a column
-// through one LDS table per token indexed by row block (double-buffered, one barrier per
-// token).  Pass 1 runs the forward and keeps the state
+// The rows of S and dS evolve independently (the recurrence acts on the right), so a
+// pair's D rows are split over D / 16 workgroups of 256 threads; thread (rb, cb) =
+// (tid / 16, tid % 16) of workgroup sp owns row 16 sp + rb and columns cb R .. (R = D / 16).
+// Sums over a row run through the 16 lanes of the thread's row group (DPP butterfly); sums
+// over a column through one LDS table per token indexed by row block (double-buffered, one
+// barrier per token), then over the workgroups of the pair in bwd_part_reduce_kernel.  Pass 1 runs the forward and keeps the state
 // entering every block of kBwdBlock tokens; pass 2 walks the blocks backwards, re-runs
 // each block's forward into a per-pair scratch (every thread reads back only what it
 // wrote itself) and then the adjoint steps of the block in reverse order.
@@ -39,16 +40,17 @@ struct BwdArgs {
   float* ckpt;        // [P][nblk][D * D] state entering each block (thread-block order), or
                       // with all_states: [P][T][D * D] the state after every token
   float* scratch;     // [P][kBwdBlock][D * D] states S_t of the block being reversed
+  float* part;        // [P][NSP][T][RED] per-workgroup column sums and scalars (NSP > 1)
   int H, T, L, nblk;
   int all_states;  // 1: keep every S_t (one forward sweep fewer); only with LDS staging
 };
 
 // One token's inputs as seen by thread (rb, cb): key-side entries of its columns,
 // value-side entries of its rows (NR rank slots).
-template <int R, int NR>
+template <int R, int NR, int RW>
 struct BwdTok {
   float k[R], q[R], u[NR][R];
-  float v[R], dO[R], gm[NR][R], vh[3][R];  // vh: v_{t-3}, v_{t-2}, v_{t-1}
+  float v[RW], dO[RW], gm[NR][RW], vh[3][RW];  // vh: v_{t-3}, v_{t-2}, v_{t-1}
   float g, beta, al[NR + 1];
 };
 
@@ -70,35 +72,69 @@ __device__ __forceinline__ void sum_row_group(float (&x)[R]) {
   for (int a = 0; a < R; ++a) x[a] = row16_sum(x[a]);
 }
 
-template <int R>
-__device__ __forceinline__ void store_block(float* dst, const float (&M)[R][R]) {
+// A thread's RW x R block of a state, stored at RW * R consecutive floats of its own.
+template <int RW, int R>
+__device__ __forceinline__ void store_block(float* dst, const float (&M)[RW][R]) {
   const int tid = threadIdx.x;
-  if constexpr ((R * R) % 4 == 0) {
+  if constexpr ((RW * R) % 4 == 0) {
 #pragma unroll
-    for (int e = 0; e < R * R; e += 4) {
+    for (int e = 0; e < RW * R; e += 4) {
       const float4 x = make_float4(M[e / R][e % R], M[(e + 1) / R][(e + 1) % R], M[(e + 2) / R][(e + 2) % R],
                                    M[(e + 3) / R][(e + 3) % R]);
-      *reinterpret_cast<float4*>(dst + (size_t)tid * R * R + e) = x;
+      *reinterpret_cast<float4*>(dst + (size_t)tid * RW * R + e) = x;
     }
   } else {
-    dst[tid] = M[0][0];
+#pragma unroll
+    for (int e = 0; e < RW * R; ++e) dst[(size_t)tid * RW * R + e] = M[e / R][e % R];
   }
 }
 
-template <int R>
-__device__ __forceinline__ void load_block(float (&M)[R][R], const float* src) {
+template <int RW, int R>
+__device__ __forceinline__ void load_block(float (&M)[RW][R], const float* src) {
   const int tid = threadIdx.x;
-  if constexpr ((R * R) % 4 == 0) {
+  if constexpr ((RW * R) % 4 == 0) {
 #pragma unroll
-    for (int e = 0; e < R * R; e += 4) {
-      const float4 x = *reinterpret_cast<const float4*>(src + (size_t)tid * R * R + e);
+    for (int e = 0; e < RW * R; e += 4) {
+      const float4 x = *reinterpret_cast<const float4*>(src + (size_t)tid * RW * R + e);
       M[e / R][e % R] = x.x;
       M[(e + 1) / R][(e + 1) % R] = x.y;
       M[(e + 2) / R][(e + 2) % R] = x.z;
       M[(e + 3) / R][(e + 3) % R] = x.w;
     }
   } else {
-    M[0][0] = src[tid];
+#pragma unroll
+    for (int e = 0; e < RW * R; ++e) M[e / R][e % R] = src[(size_t)tid * RW * R + e];
+  }
+}
+
+// Sizes shared by the backward kernels: NR rank slots compiled in, NV column vectors
+// (dq, dk, du_l) and NS scalars (dg, dbeta, dalpha_l) per token; a pair's state rows are
+// split over NSP workgroups of 16 rows each.
+template <int D, int NRK>
+struct BwdShape {
+  static constexpr int NR = NRK > 0 ? NRK : 1;
+  static constexpr int NV = 2 + NR, NS = 3 + NR;
+  static constexpr int RED = NV * D + NS;
+  static constexpr int NSP = D / 16;
+};
+
+// Writes one of a token's summed column entries / scalars (idx < RED) to its gradient.
+template <int D, int NRK>
+__device__ __forceinline__ void bwd_write_out(const BwdArgs& a, size_t tr, int idx, float s) {
+  using Sh = BwdShape<D, NRK>;
+  const int L = a.L, Lm1 = L - 1;
+  if (idx < D) {
+    a.dq[tr * D + idx] = s;
+  } else if (idx < 2 * D) {
+    a.dk[tr * D + idx - D] = s;
+  } else if (idx < Sh::NV * D) {
+    const int l = idx / D - 2, j = idx % D;
+    if (l < Lm1) a.du[(tr * Lm1 + l) * D + j] = s;
+  } else {
+    const int sidx = idx - Sh::NV * D;
+    if (sidx == 0) a.dg[tr] = s;
+    else if (sidx == 1) a.dbeta[tr] = s;
+    else if (sidx - 2 < L && L > 1) a.dalpha[tr * L + sidx - 2] = s;
   }
 }
 
@@ -146,14 +182,15 @@ constexpr int bwd_stage_tokens() {
 // the other of two register buffers.
 template <class E, int D, int NRK>
 __global__ __launch_bounds__(256) void bwd_pair_kernel(BwdArgs a) {
-  constexpr int R = D / 16, CK = kBwdBlock, NR = NRK > 0 ? NRK : 1;
-  constexpr int NV = 2 + NR, NS = 3 + NR;  // column vectors (dq, dk, du_l) and scalars (dg, dbeta, dalpha_l)
-  constexpr int RED = NV * D + NS;
-  using Tok = BwdTok<R, NR>;
+  using Sh = BwdShape<D, NRK>;
+  constexpr int R = D / 16, RW = 1, CK = kBwdBlock, NR = Sh::NR, NV = Sh::NV, NS = Sh::NS, RED = Sh::RED;
+  constexpr int NSP = Sh::NSP, SD = D * D / NSP;  // workgroups per pair, floats of a state slice
+  using Tok = BwdTok<R, NR, RW>;
   __shared__ float red[2][16][RED];  // [token parity][row block][column sums, scalars]
   const int tid = threadIdx.x;
   const int rb = tid >> 4, cb = tid & 15;
-  const int pr = blockIdx.x, hd = pr % a.H;
+  const int pr = blockIdx.x / NSP, sp = blockIdx.x % NSP, hd = pr % a.H;
+  const int row0 = 16 * sp + rb;  // this thread's state row
   const int T = a.T, L = a.L, Lm1 = L - 1;
   const E* Q = reinterpret_cast<const E*>(a.q);
   const E* K = reinterpret_cast<const E*>(a.k);
@@ -162,14 +199,14 @@ __global__ __launch_bounds__(256) void bwd_pair_kernel(BwdArgs a) {
   const E* GM = reinterpret_cast<const E*>(a.gamma);
   const E* DO = reinterpret_cast<const E*>(a.d_o);
   const float *Gg = a.g, *Gb = a.beta, *Ga = a.alpha;
-  float* ckpt = a.ckpt + (size_t)pr * (a.all_states ? T : a.nblk) * D * D;
-  float* scr = a.scratch + (size_t)pr * CK * D * D;
+  float* ckpt = a.ckpt + ((size_t)pr * NSP + sp) * (a.all_states ? T : a.nblk) * SD;
+  float* scr = a.scratch + ((size_t)pr * NSP + sp) * CK * SD;
 
-  float tw[4][R];  // conv taps of this thread's rows
+  float tw[4][RW];  // conv taps of this thread's rows
 #pragma unroll
   for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int r = 0; r < R; ++r) tw[j][r] = L > 1 ? a.conv_w[((size_t)hd * 4 + j) * D + rb * R + r] : 0.f;
+    for (int r = 0; r < RW; ++r) tw[j][r] = L > 1 ? a.conv_w[((size_t)hd * 4 + j) * D + row0 + r] : 0.f;
 
   auto load_tok = [&](int t, Tok& x) __attribute__((always_inline)) {
     const size_t tr = (size_t)pr * T + t;
@@ -179,11 +216,11 @@ __global__ __launch_bounds__(256) void bwd_pair_kernel(BwdArgs a) {
       x.q[c] = (float)Q[tr * D + cb * R + c];
     }
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      x.v[r] = (float)V[tr * D + rb * R + r];
-      x.dO[r] = (float)DO[tr * D + rb * R + r];
+    for (int r = 0; r < RW; ++r) {
+      x.v[r] = (float)V[tr * D + row0 + r];
+      x.dO[r] = (float)DO[tr * D + row0 + r];
 #pragma unroll
-      for (int j = 0; j < 3; ++j) x.vh[j][r] = t - 3 + j >= 0 ? (float)V[(tr - 3 + j) * D + rb * R + r] : 0.f;
+      for (int j = 0; j < 3; ++j) x.vh[j][r] = t - 3 + j >= 0 ? (float)V[(tr - 3 + j) * D + row0 + r] : 0.f;
     }
     x.g = a.g[tr];
     x.beta = a.beta[tr];
@@ -193,22 +230,22 @@ __global__ __launch_bounds__(256) void bwd_pair_kernel(BwdArgs a) {
 #pragma unroll
         for (int c = 0; c < R; ++c) x.u[l][c] = (float)U[(tr * Lm1 + l) * D + cb * R + c];
 #pragma unroll
-        for (int r = 0; r < R; ++r) x.gm[l][r] = (float)GM[(tr * Lm1 + l) * D + rb * R + r];
+        for (int r = 0; r < RW; ++r) x.gm[l][r] = (float)GM[(tr * Lm1 + l) * D + row0 + r];
       }
     }
 #pragma unroll
     for (int l = 0; l <= NR; ++l) x.al[l] = (L > 1 && l < L) ? a.alpha[tr * L + l] : 0.f;
   };
   // residuals r_{t,0..L-1} and written values W_{t,1..L-1} of this thread's rows
-  auto chain = [&](const Tok& x, float (&rr)[NR + 1][R], float (&W)[NR][R]) __attribute__((always_inline)) {
+  auto chain = [&](const Tok& x, float (&rr)[NR + 1][RW], float (&W)[NR][RW]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int r = 0; r < R; ++r)
+    for (int r = 0; r < RW; ++r)
       rr[0][r] = x.v[r] - (tw[0][r] * x.vh[0][r] + tw[1][r] * x.vh[1][r] + tw[2][r] * x.vh[2][r] + tw[3][r] * x.v[r]);
 #pragma unroll
     for (int l = 1; l <= NR; ++l) {
       if (l <= Lm1) {
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
+        for (int r = 0; r < RW; ++r) {
           rr[l][r] = rr[l - 1][r] - x.al[l - 1] * x.gm[l - 1][r] * rr[l - 1][r];
           W[l - 1][r] = x.al[l] * rr[l][r];
         }
@@ -216,19 +253,19 @@ __global__ __launch_bounds__(256) void bwd_pair_kernel(BwdArgs a) {
     }
   };
   // S_t from S_{t-1} (in place)
-  auto fwd_step = [&](float (&M)[R][R], const Tok& x) __attribute__((always_inline)) {
-    float rr[NR + 1][R], W[NR][R];
+  auto fwd_step = [&](float (&M)[RW][R], const Tok& x) __attribute__((always_inline)) {
+    float rr[NR + 1][RW], W[NR][RW];
     chain(x, rr, W);
-    float p[R];
+    float p[RW];
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
+    for (int r = 0; r < RW; ++r) {
       p[r] = 0.f;
 #pragma unroll
       for (int c = 0; c < R; ++c) p[r] += M[r][c] * x.k[c];
     }
     sum_row_group(p);
 #pragma unroll
-    for (int r = 0; r < R; ++r)
+    for (int r = 0; r < RW; ++r)
 #pragma unroll
       for (int c = 0; c < R; ++c) {
         float s = x.g * (M[r][c] - x.beta * p[r] * x.k[c]) + x.beta * x.v[r] * x.k[c];
@@ -239,23 +276,23 @@ __global__ __launch_bounds__(256) void bwd_pair_kernel(BwdArgs a) {
       }
   };
 
-  float dS[R][R], St[R][R];                   // dL/dS_t (carried backwards), S_t
-  float pend[3][R], dw[4][R];                 // anchor terms owed to tokens t, t-1, t-2; dconv_w share
+  float dS[RW][R], St[RW][R];                   // dL/dS_t (carried backwards), S_t
+  float pend[3][RW], dw[4][RW];                 // anchor terms owed to tokens t, t-1, t-2; dconv_w share
   int buf = 0;
   // one adjoint step at token t from its inputs x and the state before it, Mp = S_{t-1}
-  auto rev_step = [&](int t, const Tok& x, const float (&Mp)[R][R]) __attribute__((always_inline)) {
+  auto rev_step = [&](int t, const Tok& x, const float (&Mp)[RW][R]) __attribute__((always_inline)) {
     const size_t tr = (size_t)pr * T + t;
-    float rr[NR + 1][R], W[NR][R];
+    float rr[NR + 1][RW], W[NR][RW];
     chain(x, rr, W);
     // dS_t gains the readout's term
 #pragma unroll
-    for (int r = 0; r < R; ++r)
+    for (int r = 0; r < RW; ++r)
 #pragma unroll
       for (int c = 0; c < R; ++c) dS[r][c] += x.dO[r] * x.q[c];
     // row sums: p = S_{t-1} k, e = dS k, dW_l = dS u_l
-    float p[R], e[R], dW[NR][R];
+    float p[RW], e[RW], dW[NR][RW];
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
+    for (int r = 0; r < RW; ++r) {
       p[r] = 0.f;
       e[r] = 0.f;
 #pragma unroll
@@ -284,7 +321,7 @@ __global__ __launch_bounds__(256) void bwd_pair_kernel(BwdArgs a) {
     for (int c = 0; c < R; ++c) {
       float yq = 0.f, yk = 0.f;
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
+      for (int r = 0; r < RW; ++r) {
         yq += St[r][c] * x.dO[r];
         yk += dS[r][c] * (x.beta * x.v[r] - gb * p[r]) - gb * Mp[r][c] * e[r];
       }
@@ -295,22 +332,22 @@ __global__ __launch_bounds__(256) void bwd_pair_kernel(BwdArgs a) {
         float yu = 0.f;
         if (l < Lm1) {
 #pragma unroll
-          for (int r = 0; r < R; ++r) yu += dS[r][c] * W[l][r];
+          for (int r = 0; r < RW; ++r) yu += dS[r][c] * W[l][r];
         }
         y[2 + l][c] = yu;
       }
     }
     float sdg = 0.f;
 #pragma unroll
-    for (int r = 0; r < R; ++r)
+    for (int r = 0; r < RW; ++r)
 #pragma unroll
       for (int c = 0; c < R; ++c) sdg += dS[r][c] * Mp[r][c];
 #pragma unroll
     for (int s = 1; s < NS; ++s) sc[s] = 0.f;
     if (cb == 0) {  // per-row terms, counted once per row
-      float dr[R];
+      float dr[RW];
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
+      for (int r = 0; r < RW; ++r) {
         sdg -= x.beta * e[r] * p[r];
         sc[1] += e[r] * (x.v[r] - x.g * p[r]);
         dr[r] = 0.f;
@@ -320,10 +357,10 @@ __global__ __launch_bounds__(256) void bwd_pair_kernel(BwdArgs a) {
       for (int l = NR; l >= 1; --l) {
         if (l <= Lm1) {
 #pragma unroll
-          for (int r = 0; r < R; ++r) {
+          for (int r = 0; r < RW; ++r) {
             dr[r] += x.al[l] * dW[l - 1][r];
             sc[2 + l] += dW[l - 1][r] * rr[l][r];
-            a.dgamma[(tr * Lm1 + (l - 1)) * D + rb * R + r] = -x.al[l - 1] * rr[l - 1][r] * dr[r];
+            a.dgamma[(tr * Lm1 + (l - 1)) * D + row0 + r] = -x.al[l - 1] * rr[l - 1][r] * dr[r];
             sc[2 + l - 1] -= dr[r] * x.gm[l - 1][r] * rr[l - 1][r];
             dr[r] *= 1.f - x.al[l - 1] * x.gm[l - 1][r];
           }
@@ -331,8 +368,8 @@ __global__ __launch_bounds__(256) void bwd_pair_kernel(BwdArgs a) {
       }
       // dr is now the gradient of r_0 = v_t - anchor_t
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        a.dv[tr * D + rb * R + r] = x.beta * e[r] + (1.f - tw[3][r]) * dr[r] + pend[0][r];
+      for (int r = 0; r < RW; ++r) {
+        a.dv[tr * D + row0 + r] = x.beta * e[r] + (1.f - tw[3][r]) * dr[r] + pend[0][r];
         pend[0][r] = pend[1][r] - tw[2][r] * dr[r];
         pend[1][r] = pend[2][r] - tw[1][r] * dr[r];
         pend[2][r] = -tw[0][r] * dr[r];
@@ -356,7 +393,7 @@ __global__ __launch_bounds__(256) void bwd_pair_kernel(BwdArgs a) {
     }
     // dS_{t-1}; S_{t-1} becomes the next step's S_t
 #pragma unroll
-    for (int r = 0; r < R; ++r)
+    for (int r = 0; r < RW; ++r)
 #pragma unroll
       for (int c = 0; c < R; ++c) {
         dS[r][c] = x.g * (dS[r][c] - x.beta * e[r] * x.k[c]);
@@ -367,31 +404,20 @@ __global__ __launch_bounds__(256) void bwd_pair_kernel(BwdArgs a) {
       float s = 0.f;
 #pragma unroll
       for (int j = 0; j < 16; ++j) s += red[buf][j][idx];
-      if (idx < D) {
-        a.dq[tr * D + idx] = s;
-      } else if (idx < 2 * D) {
-        a.dk[tr * D + idx - D] = s;
-      } else if (idx < NV * D) {
-        const int l = idx / D - 2, j = idx % D;
-        if (l < Lm1) a.du[(tr * Lm1 + l) * D + j] = s;
-      } else {
-        const int sidx = idx - NV * D;
-        if (sidx == 0) a.dg[tr] = s;
-        else if (sidx == 1) a.dbeta[tr] = s;
-        else if (sidx - 2 < L && L > 1) a.dalpha[tr * L + sidx - 2] = s;
-      }
+      if constexpr (NSP == 1) bwd_write_out<D, NRK>(a, tr, idx, s);
+      else a.part[(((size_t)pr * NSP + sp) * T + t) * RED + idx] = s;
     }
     buf ^= 1;
   };
 
-  float Ma[R][R], Mb[R][R];
-  float M[R][R];
+  float Ma[RW][R], Mb[RW][R];
+  float M[RW][R];
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
+  for (int r = 0; r < RW; ++r) {
 #pragma unroll
     for (int c = 0; c < R; ++c) {
       M[r][c] = 0.f;
-      dS[r][c] = a.dS_final != nullptr ? a.dS_final[(size_t)pr * D * D + (size_t)(cb * R + c) * D + rb * R + r] : 0.f;
+      dS[r][c] = a.dS_final != nullptr ? a.dS_final[(size_t)pr * D * D + (size_t)(cb * R + c) * D + row0 + r] : 0.f;
     }
 #pragma unroll
     for (int j = 0; j < 3; ++j) pend[j][r] = 0.f;
@@ -460,11 +486,11 @@ __global__ __launch_bounds__(256) void bwd_pair_kernel(BwdArgs a) {
         x.k[c] = (float)b[(NB + tl) * D + cb * R + c];
       }
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        x.dO[r] = (float)b[(2 * NB + tl) * D + rb * R + r];
-        x.v[r] = (float)b[(3 * NB + tl + 3) * D + rb * R + r];
+      for (int r = 0; r < RW; ++r) {
+        x.dO[r] = (float)b[(2 * NB + tl) * D + row0 + r];
+        x.v[r] = (float)b[(3 * NB + tl + 3) * D + row0 + r];
 #pragma unroll
-        for (int j = 0; j < 3; ++j) x.vh[j][r] = (float)b[(3 * NB + tl + j) * D + rb * R + r];
+        for (int j = 0; j < 3; ++j) x.vh[j][r] = (float)b[(3 * NB + tl + j) * D + row0 + r];
       }
 #pragma unroll
       for (int l = 0; l < NR; ++l) {
@@ -472,7 +498,7 @@ __global__ __launch_bounds__(256) void bwd_pair_kernel(BwdArgs a) {
 #pragma unroll
           for (int c = 0; c < R; ++c) x.u[l][c] = (float)b[oU + (tl * Lm1 + l) * D + cb * R + c];
 #pragma unroll
-          for (int r = 0; r < R; ++r) x.gm[l][r] = (float)b[oG + (tl * Lm1 + l) * D + rb * R + r];
+          for (int r = 0; r < RW; ++r) x.gm[l][r] = (float)b[oG + (tl * Lm1 + l) * D + row0 + r];
         }
       }
       x.g = sts[bs][tl];
@@ -493,11 +519,11 @@ __global__ __launch_bounds__(256) void bwd_pair_kernel(BwdArgs a) {
       const int s0 = st * NB;
       if (st + 1 < nst) fetch(s0 + NB);
       for (int t = s0; t < min(T, s0 + NB); ++t) {
-        if (!all && t % CK == 0) store_block(ckpt + (size_t)(t / CK) * D * D, M);
+        if (!all && t % CK == 0) store_block(ckpt + (size_t)(t / CK) * SD, M);
         Tok x;
         load_tok_s(cur, t - s0, x);
         fwd_step(M, x);
-        if (all) store_block(ckpt + (size_t)t * D * D, M);
+        if (all) store_block(ckpt + (size_t)t * SD, M);
       }
       if (st + 1 < nst) commit(cur ^ 1);
       __syncthreads();
@@ -506,16 +532,16 @@ __global__ __launch_bounds__(256) void bwd_pair_kernel(BwdArgs a) {
     if (all) {
       // ---- pass 2 with every S_t kept: the adjoint steps over the stages, last first -----
 #pragma unroll
-      for (int r = 0; r < R; ++r)
+      for (int r = 0; r < RW; ++r)
 #pragma unroll
         for (int c = 0; c < R; ++c) St[r][c] = M[r][c];
       // S_{t-1}: the kept state, zero before the first token
-      auto prev_state = [&](float (&Mx)[R][R], int t) __attribute__((always_inline)) {
+      auto prev_state = [&](float (&Mx)[RW][R], int t) __attribute__((always_inline)) {
         if (t > 0) {
-          load_block(Mx, ckpt + (size_t)(t - 1) * D * D);
+          load_block(Mx, ckpt + (size_t)(t - 1) * SD);
         } else {
 #pragma unroll
-          for (int r = 0; r < R; ++r)
+          for (int r = 0; r < RW; ++r)
 #pragma unroll
             for (int c = 0; c < R; ++c) Mx[r][c] = 0.f;
         }
@@ -568,22 +594,22 @@ __global__ __launch_bounds__(256) void bwd_pair_kernel(BwdArgs a) {
       const bool more = nb_ >= 0;
       if (more) fetch(nb_ * CK + nj * NB);
       if (!rev) {
-        if (j == 0) load_block(M, ckpt + (size_t)blk * D * D);
+        if (j == 0) load_block(M, ckpt + (size_t)blk * SD);
         for (int t = s0; t < s1; ++t) {
           Tok x;
           load_tok_s(cur, t - s0, x);
           fwd_step(M, x);
-          store_block(scr + (size_t)(t - t0) * D * D, M);
+          store_block(scr + (size_t)(t - t0) * SD, M);
         }
         if (s1 == t1) {
 #pragma unroll
-          for (int r = 0; r < R; ++r)
+          for (int r = 0; r < RW; ++r)
 #pragma unroll
             for (int c = 0; c < R; ++c) St[r][c] = M[r][c];
         }
       } else {
-        const float* cp = ckpt + (size_t)blk * D * D;
-        auto prev_state = [&](int t) __attribute__((always_inline)) { return t > t0 ? scr + (size_t)(t - 1 - t0) * D * D : cp; };
+        const float* cp = ckpt + (size_t)blk * SD;
+        auto prev_state = [&](int t) __attribute__((always_inline)) { return t > t0 ? scr + (size_t)(t - 1 - t0) * SD : cp; };
         load_block(Ma, prev_state(s1 - 1));
         for (int t = s1 - 1; t >= s0; t -= 2) {  // tokens t (Ma) and t - 1 (Mb)
           if (t - 1 >= s0) load_block(Mb, prev_state(t - 1));
@@ -612,11 +638,11 @@ __global__ __launch_bounds__(256) void bwd_pair_kernel(BwdArgs a) {
     Tok xa, xb;
     load_tok(0, xa);
     for (int t = 0; t < T; t += 2) {  // tokens t (buffer a) and t + 1 (buffer b)
-      if (t % CK == 0) store_block(ckpt + (size_t)(t / CK) * D * D, M);
+      if (t % CK == 0) store_block(ckpt + (size_t)(t / CK) * SD, M);
       if (t + 1 < T) load_tok(t + 1, xb);
       fwd_step(M, xa);
       if (t + 1 < T) {
-        if ((t + 1) % CK == 0) store_block(ckpt + (size_t)((t + 1) / CK) * D * D, M);
+        if ((t + 1) % CK == 0) store_block(ckpt + (size_t)((t + 1) / CK) * SD, M);
         if (t + 2 < T) load_tok(t + 2, xa);
         fwd_step(M, xb);
       }
@@ -625,27 +651,27 @@ __global__ __launch_bounds__(256) void bwd_pair_kernel(BwdArgs a) {
     // ---- pass 2: blocks in reverse -------------------------------------------------------
     for (int blk = a.nblk - 1; blk >= 0; --blk) {
       const int t0 = blk * CK, t1 = min(T, t0 + CK);
-      const float* cp = ckpt + (size_t)blk * D * D;
+      const float* cp = ckpt + (size_t)blk * SD;
       // the block's forward again, keeping every S_t
       load_block(M, cp);
       load_tok(t0, xa);
       for (int t = t0; t < t1; t += 2) {
         if (t + 1 < t1) load_tok(t + 1, xb);
         fwd_step(M, xa);
-        store_block(scr + (size_t)(t - t0) * D * D, M);
+        store_block(scr + (size_t)(t - t0) * SD, M);
         if (t + 1 < t1) {
           if (t + 2 < t1) load_tok(t + 2, xa);
           fwd_step(M, xb);
-          store_block(scr + (size_t)(t + 1 - t0) * D * D, M);
+          store_block(scr + (size_t)(t + 1 - t0) * SD, M);
         }
       }
 #pragma unroll
-      for (int r = 0; r < R; ++r)
+      for (int r = 0; r < RW; ++r)
 #pragma unroll
         for (int c = 0; c < R; ++c) St[r][c] = M[r][c];
       // the adjoint steps, last token first (S_{t-1} is the block state t - 1 - t0, or the
       // checkpoint for the first token)
-      auto prev_state = [&](int t) __attribute__((always_inline)) { return t > t0 ? scr + (size_t)(t - 1 - t0) * D * D : cp; };
+      auto prev_state = [&](int t) __attribute__((always_inline)) { return t > t0 ? scr + (size_t)(t - 1 - t0) * SD : cp; };
       load_tok(t1 - 1, xa);
       load_block(Ma, prev_state(t1 - 1));
       for (int t = t1 - 1; t >= t0; t -= 2) {  // tokens t (buffers a) and t - 1 (buffers b)
@@ -668,7 +694,25 @@ __global__ __launch_bounds__(256) void bwd_pair_kernel(BwdArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int r = 0; r < R; ++r) a.dconv_part[((size_t)pr * 4 + j) * D + rb * R + r] = dw[j][r];
+      for (int r = 0; r < RW; ++r) a.dconv_part[((size_t)pr * 4 + j) * D + row0 + r] = dw[j][r];
+  }
+}
+
+// Column sums and scalars of a pair whose rows were split over NSP workgroups: the
+// partials added in a fixed order (deterministic); 8 tokens per workgroup.
+template <int D, int NRK>
+__global__ __launch_bounds__(256) void bwd_part_reduce_kernel(BwdArgs a) {
+  using Sh = BwdShape<D, NRK>;
+  const int T = a.T, nt8 = (T + 7) / 8;
+  const int pr = blockIdx.x / nt8, t8 = blockIdx.x % nt8;
+  for (int tl = 0; tl < 8; ++tl) {
+    const int t = t8 * 8 + tl;
+    if (t >= T) break;
+    for (int idx = threadIdx.x; idx < Sh::RED; idx += 256) {
+      float s = 0.f;
+      for (int sp = 0; sp < Sh::NSP; ++sp) s += a.part[(((size_t)pr * Sh::NSP + sp) * T + t) * Sh::RED + idx];
+      bwd_write_out<D, NRK>(a, (size_t)pr * T + t, idx, s);
+    }
   }
 }
 

@@ -164,9 +164,9 @@ prism_status prism_fwd_timed(const void* q, const void* k, const void* v,
 /* The backward pass: gradients of  sum_t <d_o_t, o_t> + <dS_final, S_final>  with respect
  * to every input of prism_fwd (S_0 = 0, no ShortConv history), i.e. the reverse-mode
  * derivative that end-to-end training of the layer needs (the pages quote training
- * throughput: "PRISM" reading notes, section 3.3).  Token by token in float32, one
- * workgroup per (b, h) pair: the forward is re-run with the state kept every 64 tokens,
- * then each 64-token block is re-run and reversed.
+ * throughput: "PRISM" reading notes, section 3.3).  Token by token in float32, dk / 16
+ * workgroups per (b, h) pair (16 state rows each): the forward is re-run keeping its
+ * states, then the adjoint steps run last token first.
  *   inputs    q .. conv_w, B, H, T, dk, dv, L, dt exactly as prism_fwd
  *   d_o       [B, H, T, dv] dtype dt: gradient of o
  *   dS_final  [B, H, dk, dv] float32: gradient of S_final; NULL = zero
