@@ -18,7 +18,7 @@ using prism::bf16_t;
 using prism::FwdArgs;
 
 constexpr size_t kAlign = 256;
-constexpr int kTargetWorkgroups = 512;      // generic sweep: about two per CU on a 256-CU MI355X
+constexpr size_t kCUs = 256;                // compute units of an MI355X
 constexpr int kTargetWorkgroupsFast = 256;  // fast sweep: one segment per CU (its LDS fills a CU)
 
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -83,12 +83,26 @@ prism_status make_plan(int B, int H, int T, int dk, int dv, int L, int chunk, pr
   if (P > 65535) return PRISM_ERR_UNSUPPORTED;  // (b, h) pairs map to grid.y
   const size_t nch = ((size_t)T + chunk - 1) / chunk;
   const bool fast = use_fast(T, dk, dv, L, chunk, dt);
-  if (seg_chunks == 0) {
-    const size_t target = fast ? kTargetWorkgroupsFast : kTargetWorkgroups;
-    size_t nseg_target = fast ? target / P : (target + P - 1) / P;
+  if (seg_chunks == 0 && fast) {
+    size_t nseg_target = kTargetWorkgroupsFast / P;
     if (nseg_target < 1) nseg_target = 1;
     seg_chunks = (int)((nch + nseg_target - 1) / nseg_target);
     if (seg_chunks < 1) seg_chunks = 1;
+  } else if (seg_chunks == 0) {
+    // the generic sweep runs one workgroup per CU: the sweep takes about (rounds of
+    // kCUs workgroups) x (chunks per segment) chunk times, and every segment adds one
+    // step of the inter-segment scan (~0.1 of a chunk at d = 128, measured)
+    double best = 0.0;
+    const size_t smax = nch < 1024 ? nch : 1024;
+    for (size_t sc = 1; sc <= smax; ++sc) {
+      const size_t ns = (nch + sc - 1) / sc;
+      const size_t rounds = (P * ns + kCUs - 1) / kCUs;
+      const double cost = (double)rounds * (double)sc + 0.1 * (double)ns;
+      if (sc == 1 || cost < best) {
+        best = cost;
+        seg_chunks = (int)sc;
+      }
+    }
   }
   const size_t nseg = (nch + seg_chunks - 1) / seg_chunks;
   size_t Tpad = nch * (size_t)chunk, a, b, c;
