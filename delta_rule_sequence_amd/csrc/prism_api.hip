@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "prism.h"
 #include "prism_fast.h"
 #include "prism_kernels.h"
@@ -143,7 +145,10 @@ prism_status launch(const FwdArgs& a, const Plan& pl, hipEvent_t* ev, hipStream_
     if (hipGetLastError() != hipSuccess || !record(ev, 1, stream)) return PRISM_ERR_HIP;
     hipLaunchKernelGGL((prism::seg_scan_kernel<D, D>), dim3(pl.P, D / 16), dim3(256), 0, stream, a);
     if (hipGetLastError() != hipSuccess || !record(ev, 2, stream)) return PRISM_ERR_HIP;
-    hipLaunchKernelGGL((prism::seg_fixup_kernel<E, D, D, C>), dim3(pl.nch, pl.P), dim3(256), 0, stream, a);
+    if constexpr (std::is_same<E, bf16_t>::value && D == 128 && C == 64)
+      hipLaunchKernelGGL((prism::seg_fixup_mfma_kernel<D, C>), dim3(pl.nch, pl.P), dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((prism::seg_fixup_kernel<E, D, D, C>), dim3(pl.nch, pl.P), dim3(256), 0, stream, a);
     if (hipGetLastError() != hipSuccess || !record(ev, 3, stream)) return PRISM_ERR_HIP;
     return PRISM_OK;
   }

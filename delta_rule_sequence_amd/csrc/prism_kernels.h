@@ -574,4 +574,63 @@ __global__ __launch_bounds__(256) void seg_fixup_kernel(FwdArgs a) {
   }
 }
 
+// o = O_loc + Qhat H_in(segment) for one chunk of one pair on MFMA, for bfloat16 I/O at
+// d = 128 and 64-token chunks: bfloat16 operands (Qhat and H_in rounded once, as the
+// output itself is), float32 accumulation started from O_loc.  H_in^T of the chunk's
+// segment is staged in LDS with the contraction index permuted inside each 32-block
+// (k = 32 kb + 16 h + 4 q + e at 32 kb + 8 q + 4 h + e), so a lane's 8-value operand
+// (k0 + 4 q .. + 3 and k0 + 16 + 4 q .. + 3) is one 16-byte read; wave w takes token rows
+// 16 w .. 16 w + 15 and all 128 value columns.
+template <int D, int C>
+__global__ __launch_bounds__(256) void seg_fixup_mfma_kernel(FwdArgs a) {
+  static_assert(D == 128 && C == 64, "written for d = 128 and 64-token chunks");
+  constexpr int LH = D + 8;  // row stride of the staged H_in^T (bfloat16 elements)
+  __shared__ __align__(16) bf16_t sHt[D * LH];
+  const int tid = threadIdx.x, w = wave_id(), l = lane_id(), q = l >> 4, li = l & 15;
+  const int c = blockIdx.x, pr = blockIdx.y;
+  const int seg = c / a.seg_chunks;
+  const int t0 = c * C, nvalid = min(C, a.T - t0);
+  const int Tpad = a.nch * C;
+  const float* Hi = a.Hin + ((size_t)pr * a.nseg + seg) * D * D;  // [k][col]
+  for (int idx = tid; idx < D * D; idx += 256) {
+    const int k = idx / D, col = idx % D;
+    const int kp = (k & ~31) | ((k & 12) << 1) | ((k & 16) >> 2) | (k & 3);
+    sHt[col * LH + kp] = (bf16_t)Hi[idx];
+  }
+  // this wave's Qhat rows as A operands (4 blocks of 32 along k)
+  const int row = 16 * w + li;
+  const float* qh = a.Qhat + ((size_t)pr * Tpad + t0 + row) * D;
+  bf16x8 af[D / 32];
+#pragma unroll
+  for (int kb = 0; kb < D / 32; ++kb) {
+    const float4 x0 = *reinterpret_cast<const float4*>(qh + 32 * kb + 4 * q);
+    const float4 x1 = *reinterpret_cast<const float4*>(qh + 32 * kb + 16 + 4 * q);
+    const float v8[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) af[kb][e] = (bf16_t)v8[e];
+  }
+  // accumulators from O_loc: lane (li, q) of tile vt holds rows 16 w + 4 q + r, column 16 vt + li
+  const float* ol = a.Oloc + ((size_t)pr * Tpad + t0 + 16 * w + 4 * q) * D;
+  f32x4 acc[D / 16];
+#pragma unroll
+  for (int vt = 0; vt < D / 16; ++vt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[vt][r] = ol[(size_t)r * D + 16 * vt + li];
+  __syncthreads();
+#pragma unroll
+  for (int vt = 0; vt < D / 16; ++vt)
+#pragma unroll
+    for (int kb = 0; kb < D / 32; ++kb)
+      acc[vt] = mfma(af[kb], *reinterpret_cast<const bf16x8*>(&sHt[(16 * vt + li) * LH + 32 * kb + 8 * q]), acc[vt]);
+  bf16_t* o = reinterpret_cast<bf16_t*>(a.o) + ((size_t)pr * a.T + t0) * D;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int t = 16 * w + 4 * q + r;
+    if (t < nvalid) {
+#pragma unroll
+      for (int vt = 0; vt < D / 16; ++vt) o[(size_t)t * D + 16 * vt + li] = (bf16_t)acc[vt][r];
+    }
+  }
+}
+
 }  // namespace prism
