@@ -395,6 +395,21 @@ def bwd_bench(steps, warmup, workload_name, cpu=True):
         dt_cpu = time.perf_counter() - t0
         cpu_out = {"value": Ts / dt_cpu, "unit": "tokens/s (per head)", "cores": torch.get_num_threads(),
                    "kind": "oracle", "sample": f"one (b, h) pair, {Ts} tokens, float64 autograd, {dt_cpu:.1f} s"}
+    res = time_bwd(w, x, d_o, steps, warmup)
+    print(json.dumps({"metric": "bwd tokens/sec (prism_bwd)", "workload": w.name, "dtype": w.dtype,
+                      "config": {"B": w.B, "H": w.H, "T": w.T, "dk": w.dk, "dv": w.dv, "L": w.L},
+                      "steps": steps, "warmup": warmup, "ms_per_step": res["ms_per_step"],
+                      "tokens_per_s": res["tokens_per_s"], "roofline": res["roofline"],
+                      "cpu_baseline": cpu_out}), flush=True)
+
+
+def time_bwd(w, x, d_o, steps, warmup):
+    """prism_bwd on workload w (inputs x, output gradient d_o): whole calls timed with HIP
+    events on the launch stream; returns ms per call, tokens/s and the HBM roofline of the
+    call's algorithmic bytes."""
+    import torch
+    import delta_rule_sequence_amd as prism
+    import workloads
     dev = workloads.to_torch(x, w.dtype, "cuda")
     vt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     do_t = torch.tensor(d_o, device="cuda").to(vt)
@@ -423,15 +438,11 @@ def bwd_bench(steps, warmup, workload_name, cpu=True):
     grad_bytes = 4 * (2 * w.dk + w.dv + 2 + ((w.L - 1) * (w.dk + w.dv) + w.L if w.L > 1 else 0))
     per_th = in_bytes + w.dv * E + grad_bytes
     total = w.pairs * w.T * per_th
-    print(json.dumps({"metric": "bwd tokens/sec (prism_bwd)", "workload": w.name, "dtype": w.dtype,
-                      "config": {"B": w.B, "H": w.H, "T": w.T, "dk": w.dk, "dv": w.dv, "L": w.L},
-                      "steps": steps, "warmup": warmup, "ms_per_step": ms,
-                      "tokens_per_s": w.B * w.T / (ms * 1e-3),
-                      "roofline": {"bound": "hbm", "bytes_per_token_head": per_th, "bytes_per_call": total,
-                                   "achieved": total / (ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                   "frac": total / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                                   "kernel": "bwd_pair_kernel"},
-                      "cpu_baseline": cpu_out}), flush=True)
+    del dev, do_t, ws
+    return {"ms_per_step": ms, "tokens_per_s": w.B * w.T / (ms * 1e-3),
+            "roofline": {"bound": "hbm", "bytes_per_token_head": per_th, "bytes_per_call": total,
+                         "achieved": total / (ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": total / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "kernel": "bwd_pair_kernel"}}
 
 
 def main():
@@ -523,6 +534,13 @@ def main():
     out["roofline"]["mfma_secondary"] = {"achieved": mfma_achieved, "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                                          "frac": mfma_achieved / MFMA_PEAK_TFLOPS,
                                          "flop_per_token_head": chunk_flop}
+    # the backward on the same workload (one warm-up, two timed calls): reported beside the
+    # forward metric, not part of it
+    import numpy as np
+    d_o = np.random.default_rng(w.seed + 7).standard_normal((w.B, w.H, w.T, w.dv)).astype(np.float32)
+    if w.dtype == "bf16":
+        d_o = workloads.to_bf16_values(d_o)
+    out["bwd"] = dict(time_bwd(w, x0, d_o, 2, 1), steps=2, warmup=1)
     out["roofline"]["measured_copy"] = copy_bandwidth(torch)
     out["roofline"]["measured_mfma"] = mfma_rate(torch)
     if not args.no_cpu_baseline:
