@@ -179,8 +179,10 @@ prism_status prism_fwd_timed(const void* q, const void* k, const void* v,
  * B * H <= 2^31 - 1.  Workspace: prism_bwd_workspace_bytes.  When every per-token state
  * fits in 4 GiB (B*H*T*dk*dv*4 bytes) the workspace keeps all of them and the forward is
  * re-run once; otherwise it keeps the state every 64 tokens plus a 64-token buffer per pair
- * and re-runs each 64-token block (one more forward sweep).  Ownership, stream and errors
- * as prism_fwd. */
+ * and re-runs each 64-token block (one more forward sweep).  With dk > 16 it also holds
+ * each workgroup's per-token column sums, B*H * (dk/16) * T * ((2+R)*dk + 3 + R) floats
+ * (R = 1, 3 or 7 rank slots for L = 1, L <= 4, L <= 8), added in a fixed order by a second
+ * kernel.  Ownership, stream and errors as prism_fwd. */
 size_t prism_bwd_workspace_bytes(int B, int H, int T, int dk, int dv, int L, prism_dtype dt);
 prism_status prism_bwd(const void* q, const void* k, const void* v,
                        const float* g, const float* beta,
