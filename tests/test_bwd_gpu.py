@@ -24,6 +24,8 @@ CASES = [
     ("f32_d16_L3_T1", "f32", 1, 2, 1, 16, 3, True),
     ("f32_d32_L2_T3", "f32", 2, 1, 3, 32, 2, False),
     ("bf16_d64_L4_T128", "bf16", 1, 1, 128, 64, 4, False),
+    # d = 128 with L > 4: the inputs' LDS stages do not fit, so the kernel reads them from memory
+    ("bf16_d128_L8_T70", "bf16", 1, 2, 70, 128, 8, True),
 ]
 
 
