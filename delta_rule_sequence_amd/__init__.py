@@ -32,6 +32,10 @@ def load_library() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise PrismError(f"{LIB_PATH} is missing: build it with `python -m delta_rule_sequence_amd.build` "
                          "(or __graft_entry__.build())")
+    # torch first: the library then binds to the HIP runtime torch already loaded.  Opened
+    # before torch, it would pull in a second runtime, whose launches fail with
+    # hipErrorNoDevice once torch has brought up its own.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(LIB_PATH)
     vp, fp, i, sz = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
     fwd_args = [vp, vp, vp, fp, fp, vp, fp, vp, fp, i, i, i, i, i, i, i, i, vp, fp, vp, sz]
