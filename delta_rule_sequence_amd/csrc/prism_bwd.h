@@ -20,8 +20,9 @@
 // pair's D rows are split over D / 16 workgroups of 256 threads; thread (rb, cb) =
 // (tid / 16, tid % 16) of workgroup sp owns row 16 sp + rb and columns cb R .. (R = D / 16).
 // Sums over a row run through the 16 lanes of the thread's row group (DPP butterfly); sums
-// over a column through one LDS table per token indexed by row block (double-buffered, one
-// barrier per token), then over the workgroups of the pair in bwd_part_reduce_kernel.  Pass 1 runs the forward and keeps the state
+// over a column through an LDS table with one slot per token of a group of KR tokens,
+// indexed by row block and reduced once per group (two barriers per group), then over the
+// workgroups of the pair in bwd_part_reduce_kernel.  Pass 1 runs the forward and keeps the state
 // entering every block of kBwdBlock tokens; pass 2 walks the blocks backwards, re-runs
 // each block's forward into a per-pair scratch (every thread reads back only what it
 // wrote itself) and then the adjoint steps of the block in reverse order.
@@ -164,15 +165,26 @@ __device__ __forceinline__ void stage_commit_seg(E* lds, const uint4 (&src)[N], 
   }
 }
 
+// LDS of the backward: the reduction table holds KR tokens' column sums and scalars per
+// row block (reduced once per group of KR tokens), beside two stages of NB tokens' inputs.
+template <int D, int NR>
+constexpr int bwd_red_slot_bytes() { return 16 * ((2 + NR) * D + 3 + NR) * 4; }
+template <class E, int D, int NR>
+constexpr int bwd_stage_bytes(int nb) { return (4 * nb + 3 + 2 * nb * NR) * D * (int)sizeof(E) + nb * (3 + NR) * 4; }
+
+// Tokens per reduction group: 4 if that table fits beside two 8-token stages, else 2.
+template <class E, int D, int NR>
+constexpr int bwd_red_group() {
+  return 4 * bwd_red_slot_bytes<D, NR>() + 2 * bwd_stage_bytes<E, D, NR>(8) <= 156 * 1024 ? 4 : 2;
+}
+
 // Tokens per LDS stage of the backward's inputs: the largest of 16, 8, 4, 2 whose two
 // stage buffers fit beside the reduction table (0: inputs read straight from memory).
 template <class E, int D, int NR>
 constexpr int bwd_stage_tokens() {
-  const int red = 2 * 16 * ((2 + NR) * D + 3 + NR) * 4;
-  for (int nb = 16; nb >= 2; nb /= 2) {
-    const int stage = (4 * nb + 3 + 2 * nb * NR) * D * (int)sizeof(E) + nb * (3 + NR) * 4;
-    if (red + 2 * stage <= 156 * 1024) return nb;
-  }
+  const int red = bwd_red_group<E, D, NR>() * bwd_red_slot_bytes<D, NR>();
+  for (int nb = 16; nb >= 2; nb /= 2)
+    if (red + 2 * bwd_stage_bytes<E, D, NR>(nb) <= 156 * 1024) return nb;
   return 0;
 }
 
@@ -186,7 +198,8 @@ __global__ __launch_bounds__(256) void bwd_pair_kernel(BwdArgs a) {
   constexpr int R = D / 16, RW = 1, CK = kBwdBlock, NR = Sh::NR, NV = Sh::NV, NS = Sh::NS, RED = Sh::RED;
   constexpr int NSP = Sh::NSP, SD = D * D / NSP;  // workgroups per pair, floats of a state slice
   using Tok = BwdTok<R, NR, RW>;
-  __shared__ float red[2][16][RED];  // [token parity][row block][column sums, scalars]
+  constexpr int KR = bwd_red_group<E, D, NR>();
+  __shared__ float red[KR][16][RED];  // [token of the group][row block][column sums, scalars]
   const int tid = threadIdx.x;
   const int rb = tid >> 4, cb = tid & 15;
   const int pr = blockIdx.x / NSP, sp = blockIdx.x % NSP, hd = pr % a.H;
@@ -278,8 +291,23 @@ __global__ __launch_bounds__(256) void bwd_pair_kernel(BwdArgs a) {
 
   float dS[RW][R], St[RW][R];                   // dL/dS_t (carried backwards), S_t
   float pend[3][RW], dw[4][RW];                 // anchor terms owed to tokens t, t-1, t-2; dconv_w share
-  int buf = 0;
+  int ng = 0, gfirst = 0;  // tokens written into the reduction table, the group's first (last in time)
   // one adjoint step at token t from its inputs x and the state before it, Mp = S_{t-1}
+  // the group's column sums and scalars, summed over the row blocks (tokens gfirst,
+  // gfirst - 1, ..), to the gradients or, with several workgroups per pair, to the partials
+  auto flush = [&]() __attribute__((always_inline)) {
+    __syncthreads();
+    for (int idx = tid; idx < ng * RED; idx += 256) {
+      const int gi = idx / RED, e = idx - gi * RED, t = gfirst - gi;
+      float s = 0.f;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) s += red[gi][j][e];
+      if constexpr (NSP == 1) bwd_write_out<D, NRK>(a, (size_t)pr * T + t, e, s);
+      else a.part[(((size_t)pr * NSP + sp) * T + t) * RED + e] = s;
+    }
+    __syncthreads();
+    ng = 0;
+  };
   auto rev_step = [&](int t, const Tok& x, const float (&Mp)[RW][R]) __attribute__((always_inline)) {
     const size_t tr = (size_t)pr * T + t;
     float rr[NR + 1][RW], W[NR][RW];
@@ -379,17 +407,19 @@ __global__ __launch_bounds__(256) void bwd_pair_kernel(BwdArgs a) {
       }
     }
     sc[0] = sdg;
-    // column sums and scalars: each row block's share into LDS, summed over the 16 row
-    // blocks after the barrier (the scalars first summed over the row's 16 lanes)
+    // column sums and scalars: each row block's share into the group's LDS slot, summed
+    // over the 16 row blocks when the group is flushed (the scalars first summed over the
+    // row's 16 lanes)
+    if (ng == 0) gfirst = t;
 #pragma unroll
     for (int n = 0; n < NV; ++n)
 #pragma unroll
-      for (int c = 0; c < R; ++c) red[buf][rb][n * D + cb * R + c] = y[n][c];
+      for (int c = 0; c < R; ++c) red[ng][rb][n * D + cb * R + c] = y[n][c];
 #pragma unroll
     for (int s = 0; s < NS; ++s) sc[s] = row16_sum(sc[s]);
     if (cb == 0) {
 #pragma unroll
-      for (int s = 0; s < NS; ++s) red[buf][rb][NV * D + s] = sc[s];
+      for (int s = 0; s < NS; ++s) red[ng][rb][NV * D + s] = sc[s];
     }
     // dS_{t-1}; S_{t-1} becomes the next step's S_t
 #pragma unroll
@@ -399,15 +429,7 @@ __global__ __launch_bounds__(256) void bwd_pair_kernel(BwdArgs a) {
         dS[r][c] = x.g * (dS[r][c] - x.beta * e[r] * x.k[c]);
         St[r][c] = Mp[r][c];
       }
-    __syncthreads();
-    for (int idx = tid; idx < RED; idx += 256) {
-      float s = 0.f;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) s += red[buf][j][idx];
-      if constexpr (NSP == 1) bwd_write_out<D, NRK>(a, tr, idx, s);
-      else a.part[(((size_t)pr * NSP + sp) * T + t) * RED + idx] = s;
-    }
-    buf ^= 1;
+    if (++ng == KR) flush();
   };
 
   float Ma[RW][R], Mb[RW][R];
@@ -565,6 +587,7 @@ __global__ __launch_bounds__(256) void bwd_pair_kernel(BwdArgs a) {
             rev_step(t - 1, y, Mb);
           }
         }
+        if (ng > 0) flush();
         if (st > 0) commit(cur ^ 1);
         __syncthreads();
         cur ^= 1;
@@ -623,6 +646,7 @@ __global__ __launch_bounds__(256) void bwd_pair_kernel(BwdArgs a) {
             rev_step(t - 1, y, Mb);
           }
         }
+        if (ng > 0) flush();
       }
       if (more) commit(cur ^ 1);
       __syncthreads();
@@ -688,6 +712,7 @@ __global__ __launch_bounds__(256) void bwd_pair_kernel(BwdArgs a) {
           rev_step(t - 1, xb, Mb);
         }
       }
+      if (ng > 0) flush();
     }
   }
   if (cb == 0 && L > 1) {
