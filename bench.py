@@ -518,6 +518,8 @@ def main():
                    "chunk": w.chunk, "input_sets": nsets},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     # the counters' HBM bytes over the same duration (null with traffic)
+                     "traffic_GBs": None if traffic is None else traffic / (sweep_ms * 1e-3) / 1e9,
                      "kernel": sweep_name, "algorithmic_bytes_per_launch": sweep_bytes},
         "path": {"algorithmic_bytes_per_step": w.pairs * w.T * path_bytes,
                  "hbm_roofline_tokens_per_s": tokens * HBM_PEAK_GBS * 1e9 / (w.pairs * w.T * path_bytes),
