@@ -7,8 +7,10 @@ with that path.
 
 The oracle is plain float64 numpy that steps the recurrence token by token
 and runs the residual chain one refinement step at a time.  See
-``oracle.prism`` for the definitions and the passages each one follows, and
-``oracle.prism_grad`` for the float64 gradients of the same forward.
+``oracle.prism`` for the definitions and the passages each one follows,
+``oracle.prism_grad`` for the float64 gradients of the same forward, and
+``oracle.prism_nl`` for the nonlinear refinement variant (the GELU of the
+gain-modulated residual in the chain) and its absorbed per-channel factors.
 """
 from .prism import (shortconv_anchor, residual_chain, token_step, forward,
                     forward_pairs, conv_tail, decode_step)

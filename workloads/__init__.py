@@ -19,6 +19,10 @@ Input recipe (seed = the workload's seed):
   L2-normalised over dk per row; v ~ N(0, 1) [B, H, T, dv];
   gamma = GELU'(z) = Phi(z) + z phi(z) with z ~ N(0, 1) [B, H, T, L-1, dv]
   (derivative of the exact erf GELU).
+* For the nonlinear-refinement variant only (generate_gain): the gains
+  p ~ N(0, 1) [B, H, T, L-1, dv], tensor id 5, in the I/O dtype.  The pages give
+  no statistics for the predicted gains; unit normals put p * r across the
+  GELU's curved range.
 * Vectors (q, k, v, u, gamma) are stored in the I/O dtype: float32, or
   bfloat16 values (round to nearest even of the float32 value).  The scalars g,
   beta, alpha and the conv weights are float32 in both paths.
@@ -39,8 +43,8 @@ from typing import Dict, Optional
 import numpy as np
 from scipy.special import ndtr
 
-__all__ = ["Workload", "WORKLOADS", "workload", "generate", "to_bf16_values",
-           "manifest"]
+__all__ = ["Workload", "WORKLOADS", "workload", "generate", "generate_gain",
+           "generate_state", "to_bf16_values", "manifest"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -197,6 +201,14 @@ def generate(w: Workload, seed: Optional[int] = None, keys: str = "iid") -> Dict
     elif keys != "iid":
         raise ValueError(keys)
     return out
+
+
+def generate_gain(w: Workload, seed: Optional[int] = None) -> Optional[np.ndarray]:
+    """Gains p [B, H, T, L-1, dv] of the nonlinear refinement (None for L = 1)."""
+    if w.L == 1:
+        return None
+    seed = w.seed if seed is None else seed
+    return _fill_rows(seed, 5, (w.B, w.H, w.T, w.L - 1, w.dv), w.dtype, None)
 
 
 def generate_state(w: Workload, seed: Optional[int] = None) -> Dict[str, np.ndarray]:
