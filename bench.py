@@ -13,6 +13,9 @@ float64 oracle timed on the host cores on a bounded sample.
     python bench.py --bwd [--workload NAME] [--steps K]
 times the backward pass (prism_bwd) instead and prints its own JSON line.
 
+    python bench.py --nl [--workload NAME] [--steps K]
+times the forward with the nonlinear refinement (prism_fwd_nl) and its factor kernel.
+
     python bench.py --calibrate-copy MB
 runs a plain device-to-device copy of MB megabytes (for scaling the
 FETCH_SIZE / WRITE_SIZE counters of rocprofv3) and exits.
@@ -445,6 +448,67 @@ def time_bwd(w, x, d_o, steps, warmup):
                          "frac": total / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "kernel": "bwd_pair_kernel"}}
 
 
+def time_nl(w, steps, warmup, x0=None):
+    """The nonlinear-refinement forward (prism_fwd_nl: the chain-factor kernel, then the
+    forward) on workload w, gains drawn by workloads.generate_gain.  Two input sets are
+    rotated (with the gains they exceed the 256 MB Infinity Cache at the 16K shape).  Whole
+    calls, and the factor kernel alone (prism_nl_gain), timed with HIP events on the launch
+    stream; the factor kernel's roofline counts v, the gains and the step sizes read once
+    and the factors written once."""
+    import torch
+    import delta_rule_sequence_amd as prism
+    import workloads
+    sets = []
+    for s in range(2):
+        x = dict(x0) if (s == 0 and x0 is not None) else workloads.generate(w, seed=w.seed + 100 * s)
+        x.pop("gamma", None)
+        x["p"] = workloads.generate_gain(w, seed=w.seed + 100 * s)
+        sets.append(workloads.to_torch(x, w.dtype, "cuda"))
+    lib = prism.load_library()
+    dt = prism.PRISM_BF16 if w.dtype == "bf16" else prism.PRISM_F32
+    ws = torch.empty(lib.prism_fwd_nl_workspace_bytes(w.B, w.H, w.T, w.dk, w.dv, w.L, w.chunk, dt),
+                     dtype=torch.uint8, device="cuda")
+    vt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    o = torch.empty((w.B, w.H, w.T, w.dv), dtype=vt, device="cuda")
+    S = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device="cuda")
+
+    def fwd(d):
+        prism.fwd_nl(d["q"], d["k"], d["v"], d["g"], d["beta"], d["u"], d["alpha"], d["p"], d["conv_w"],
+                     L=w.L, chunk=w.chunk, out=(o, S), workspace=ws)
+
+    def gain(d):
+        prism.nl_gain(d["v"], d["alpha"], d["p"], d["conv_w"], w.L)
+
+    hip = Hip()
+    stream = torch.cuda.current_stream()
+    rec = hip.lib.hipEventRecord
+    rec.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    res = {}
+    for name, fn in (("fwd_nl", fwd), ("nl_gain", gain)):
+        for i in range(warmup):
+            fn(sets[i % 2])
+        torch.cuda.synchronize()
+        ev = hip.events(2)
+        rec(ev[0], ctypes.c_void_p(stream.cuda_stream))
+        for i in range(steps):
+            fn(sets[i % 2])
+        rec(ev[1], ctypes.c_void_p(stream.cuda_stream))
+        torch.cuda.synchronize()
+        res[name] = hip.elapsed_ms(ev[0], ev[1]) / steps
+        hip.destroy(ev)
+    E = 2 if w.dtype == "bf16" else 4
+    per_th = E * w.dv + 2 * E * (w.L - 1) * w.dv + 4 * w.L if w.L > 1 else 0
+    total = w.pairs * w.T * per_th
+    gb = total / (res["nl_gain"] * 1e-3) / 1e9 if w.L > 1 else None
+    del sets, ws
+    return {"ms_per_step": res["fwd_nl"], "tokens_per_s": w.B * w.T / (res["fwd_nl"] * 1e-3),
+            "gain_kernel_ms": res["nl_gain"],
+            "gain_roofline": {"bound": "hbm", "bytes_per_token_head": per_th, "bytes_per_launch": total,
+                              "achieved": gb, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                              "frac": None if gb is None else gb / HBM_PEAK_GBS, "kernel": "nl_gain_kernel"},
+            "steps": steps, "warmup": warmup, "input_sets": 2}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -460,6 +524,8 @@ def main():
                     help="time one-token decode steps for BATCH sequences instead")
     ap.add_argument("--bwd", action="store_true",
                     help="time the backward (prism_bwd) on --workload instead")
+    ap.add_argument("--nl", action="store_true",
+                    help="time the nonlinear-refinement forward (prism_fwd_nl) on --workload instead")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -478,6 +544,14 @@ def main():
         return
     if args.bwd:
         bwd_bench(args.steps, args.warmup, args.workload, cpu=not args.no_cpu_baseline)
+        return
+    if args.nl:
+        import workloads
+        w = workloads.workload(args.workload)
+        res = time_nl(w, args.steps, args.warmup)
+        print(json.dumps({"metric": "fwd tokens/sec, nonlinear refinement (prism_fwd_nl)", "workload": w.name,
+                          "dtype": w.dtype, "config": {"B": w.B, "H": w.H, "T": w.T, "dk": w.dk, "dv": w.dv,
+                                                       "L": w.L, "chunk": w.chunk}, **res}), flush=True)
         return
 
     import workloads
@@ -543,6 +617,8 @@ def main():
     if w.dtype == "bf16":
         d_o = workloads.to_bf16_values(d_o)
     out["bwd"] = dict(time_bwd(w, x0, d_o, 2, 1), steps=2, warmup=1)
+    # the nonlinear-refinement forward on the same shape (its own gains), reported beside it
+    out["nl"] = time_nl(w, 10, 2, x0)
     out["roofline"]["measured_copy"] = copy_bandwidth(torch)
     out["roofline"]["measured_mfma"] = mfma_rate(torch)
     if not args.no_cpu_baseline:

@@ -13,6 +13,7 @@
 #include "prism_sweep8.h"
 #include "prism_decode.h"
 #include "prism_bwd.h"
+#include "prism_nl.h"
 
 namespace {
 
@@ -476,6 +477,68 @@ prism_status prism_fwd_seg(const void* q, const void* k, const void* v, const fl
   if (seg_chunks <= 0) return PRISM_ERR_INVALID_ARG;
   return fwd_impl(q, k, v, g, beta, u, alpha, gamma, conv_w, B, H, T, dk, dv, L, chunk, dt, o, S_final,
                   workspace, workspace_bytes, seg_chunks, nullptr, stream);
+}
+
+// Bytes of the chain factors of the nonlinear refinement: B H T (L-1) dv elements of dt.
+static bool nl_gamma_bytes(int B, int H, int T, int dv, int L, prism_dtype dt, size_t* out) {
+  size_t P, pt;
+  if (!mul_ok((size_t)B, (size_t)H, &P) || !mul_ok(P, (size_t)T, &pt)) return false;
+  return mul_ok(pt, (size_t)(L - 1) * dv * (dt == PRISM_BF16 ? 2 : 4), out);
+}
+
+prism_status prism_nl_gain(const void* v, const float* alpha, const void* p, const float* conv_w,
+                           const void* conv_in, int B, int H, int T, int dv, int L, prism_dtype dt,
+                           void* gamma, hipStream_t stream) {
+  if (B <= 0 || H <= 0 || T <= 0) return PRISM_ERR_INVALID_ARG;
+  if (dt != PRISM_F32 && dt != PRISM_BF16) return PRISM_ERR_INVALID_ARG;
+  if (L < 1 || L > 8 || !valid_dim(dv)) return PRISM_ERR_UNSUPPORTED;
+  if (L == 1) return PRISM_OK;
+  if (!v || !alpha || !p || !conv_w || !gamma) return PRISM_ERR_INVALID_ARG;
+  size_t P, bytes;
+  if (!mul_ok((size_t)B, (size_t)H, &P) || !nl_gamma_bytes(B, H, T, dv, L, dt, &bytes)) return PRISM_ERR_INVALID_ARG;
+  if (P > 65535) return PRISM_ERR_UNSUPPORTED;  // (b, h) pairs map to grid.y, as in the forward
+  const int lognc = dv == 16 ? 2 : dv == 32 ? 3 : dv == 64 ? 4 : 5;
+  const size_t groups = (size_t)T << lognc;    // < 2^36: T < 2^31, dv / 4 <= 32
+  if (groups > (size_t)UINT32_MAX - 255) return PRISM_ERR_UNSUPPORTED;
+  const dim3 grid((unsigned)((groups + 255) / 256), (unsigned)P);
+  prism::NlArgs a;
+  a.v = v; a.alpha = alpha; a.p = p; a.conv_w = conv_w; a.conv_in = conv_in; a.gamma = gamma;
+  a.H = H; a.T = T; a.L = L; a.dv = dv; a.lognc = lognc;
+  if (dt == PRISM_BF16)
+    hipLaunchKernelGGL((prism::nl_gain_kernel<bf16_t>), grid, dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((prism::nl_gain_kernel<float>), grid, dim3(256), 0, stream, a);
+  return hipGetLastError() == hipSuccess ? PRISM_OK : PRISM_ERR_HIP;
+}
+
+size_t prism_fwd_nl_workspace_bytes(int B, int H, int T, int dk, int dv, int L, int chunk, prism_dtype dt) {
+  Plan pl;
+  size_t gb;
+  if (make_plan(B, H, T, dk, dv, L, chunk, dt, 0, &pl) != PRISM_OK || !nl_gamma_bytes(B, H, T, dv, L, dt, &gb))
+    return 0;
+  return align_up(gb) + pl.total;
+}
+
+prism_status prism_fwd_nl(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                          const void* u, const float* alpha, const void* p, const float* conv_w,
+                          int B, int H, int T, int dk, int dv, int L, int chunk, prism_dtype dt,
+                          void* o, float* S_final, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  // every check before the first launch
+  Plan pl;
+  prism_status st = make_plan(B, H, T, dk, dv, L, chunk, dt, 0, &pl);
+  if (st != PRISM_OK) return st;
+  if (!q || !k || !v || !g || !beta || !o || !S_final) return PRISM_ERR_INVALID_ARG;
+  if (L > 1 && (!u || !alpha || !p || !conv_w)) return PRISM_ERR_INVALID_ARG;
+  size_t gb;
+  if (!nl_gamma_bytes(B, H, T, dv, L, dt, &gb)) return PRISM_ERR_INVALID_ARG;
+  const size_t off = align_up(gb);
+  if (!workspace || workspace_bytes < off + pl.total) return PRISM_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  void* gamma = L > 1 ? ws : nullptr;
+  st = prism_nl_gain(v, alpha, p, conv_w, nullptr, B, H, T, dv, L, dt, gamma, stream);
+  if (st != PRISM_OK) return st;
+  return fwd_impl(q, k, v, g, beta, u, alpha, gamma, conv_w, B, H, T, dk, dv, L, chunk, dt, o, S_final,
+                  ws + off, workspace_bytes - off, 0, nullptr, stream);
 }
 
 const char* prism_status_string(prism_status s) {

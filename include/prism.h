@@ -209,6 +209,46 @@ prism_status prism_bwd_lowmem(const void* q, const void* k, const void* v,
                               float* du, float* dalpha, float* dgamma, float* dconv_w,
                               void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Nonlinear residual refinement.  PRISM's refinement layers subtract a GELU of the
+ * gain-modulated residual ("PRISM" reading notes, section 2.3: greedy residual
+ * subtraction, gains p from a predictor on the anchor):
+ *   r_{t,l} = r_{t,l-1} - alpha_{t,l-1} * GELU(p_{t,l-1} * r_{t,l-1})   (exact erf GELU)
+ * in place of the linear chain above; everything else is unchanged.  Because
+ * GELU(z) = z Phi(z), this is the linear chain with gamma_{t,l} = p_{t,l} Phi(p_{t,l} r_{t,l})
+ * evaluated on the chain's own residuals: the GELU folded into per-channel scaling factors
+ * (Tencent Ads article, section 03-三).
+ *
+ * prism_nl_gain writes those factors: gamma [B, H, T, L-1, dv] (dtype dt, the layout of the
+ * gamma argument above) from
+ *   v [B, H, T, dv] dt;  alpha [B, H, T, L] float32;  p [B, H, T, L-1, dv] dt (slot j holds
+ *   p_{t,j});  conv_w [H, 4, dv] float32;  conv_in [B, H, 3, dv] dt or NULL (as in
+ *   prism_fwd_state: the values of the three tokens before the first one).
+ * Each factor is rounded to dt before the chain continues with it, as the forward uses it.
+ * Phi is evaluated with the erfc approximation of Abramowitz and Stegun, formula 7.1.26
+ * (absolute error below 1.5e-7).
+ * Feeding the factors to prism_fwd, prism_fwd_state or prism_decode_step (with the same
+ * conv_in / conv_state) runs the nonlinear variant in every mode.  For L == 1 there are
+ * no factors: nothing is enqueued and the pointers may be NULL.  Supported dv in
+ * {16, 32, 64, 128} and B * H <= 65535 (as the forward); no workspace; gamma must not
+ * alias an input.  Errors as prism_fwd. */
+prism_status prism_nl_gain(const void* v, const float* alpha, const void* p, const float* conv_w,
+                           const void* conv_in, int B, int H, int T, int dv, int L, prism_dtype dt,
+                           void* gamma, hipStream_t stream);
+
+/* The nonlinear-refinement forward in one call: prism_nl_gain into the front of the
+ * workspace, then prism_fwd with those factors.  Arguments as prism_fwd with the gains p
+ * in place of gamma (p may be NULL when L == 1).  Workspace: prism_fwd_nl_workspace_bytes
+ * (the factors, 256-byte aligned, plus prism_fwd_workspace_bytes). */
+size_t prism_fwd_nl_workspace_bytes(int B, int H, int T, int dk, int dv, int L, int chunk,
+                                    prism_dtype dt);
+prism_status prism_fwd_nl(const void* q, const void* k, const void* v,
+                          const float* g, const float* beta,
+                          const void* u, const float* alpha, const void* p,
+                          const float* conv_w,
+                          int B, int H, int T, int dk, int dv, int L, int chunk, prism_dtype dt,
+                          void* o, float* S_final,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* A static, human-readable name of a status code. */
 const char* prism_status_string(prism_status s);
 

@@ -197,3 +197,52 @@ def test_bwd_argument_checks(lib):
     # the default keeps every per-token state while they fit: it grows with T
     assert lib.prism_bwd_workspace_bytes(1, 1, 65, 16, 16, 2, 1) > need
     assert lib.prism_bwd_workspace_bytes(1, 1, 4096, 64, 64, 4, 1) > lib.prism_bwd_lowmem_workspace_bytes(1, 1, 4096, 64, 64, 4, 1)
+
+
+def _nl_gain_call(lib, B=1, H=1, T=64, dv=16, L=3, dt=1, null=()):
+    p = ctypes.c_void_p(1)
+    args = {n: (None if n in null else p) for n in ["v", "alpha", "p", "conv_w", "gamma"]}
+    return lib.prism_nl_gain(args["v"], args["alpha"], args["p"], args["conv_w"], None, B, H, T, dv, L, dt,
+                             args["gamma"], None)
+
+
+@pytest.mark.parametrize("name", ["v", "alpha", "p", "conv_w", "gamma"])
+def test_nl_gain_null_pointer(lib, name):
+    assert _nl_gain_call(lib, null=(name,)) == INVALID
+
+
+def test_nl_gain_argument_checks(lib):
+    assert _nl_gain_call(lib, B=0) == INVALID
+    assert _nl_gain_call(lib, T=0) == INVALID
+    assert _nl_gain_call(lib, dv=24) == UNSUPPORTED
+    assert _nl_gain_call(lib, L=9) == UNSUPPORTED
+    assert _nl_gain_call(lib, dt=2) == INVALID
+    # L = 1 has no factors: nothing to check beyond the sizes, nothing enqueued
+    assert _nl_gain_call(lib, L=1, null=("v", "alpha", "p", "conv_w", "gamma")) == OK
+
+
+def _fwd_nl_call(lib, B=1, H=1, T=64, d=16, L=2, chunk=16, dt=1, null=(), ws_bytes=1 << 30):
+    p = ctypes.c_void_p(1)
+    names = ["q", "k", "v", "g", "beta", "u", "alpha", "p", "conv_w", "o", "S", "ws"]
+    a = {n: (None if n in null else p) for n in names}
+    return lib.prism_fwd_nl(a["q"], a["k"], a["v"], a["g"], a["beta"], a["u"], a["alpha"], a["p"], a["conv_w"],
+                            B, H, T, d, d, L, chunk, dt, a["o"], a["S"], a["ws"], ws_bytes, None)
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "g", "beta", "u", "alpha", "p", "conv_w", "o", "S"])
+def test_fwd_nl_null_pointer(lib, name):
+    assert _fwd_nl_call(lib, L=3, null=(name,)) == INVALID
+
+
+def test_fwd_nl_workspace(lib):
+    f = lib.prism_fwd_nl_workspace_bytes
+    base = lib.prism_fwd_workspace_bytes(1, 1, 64, 16, 16, 3, 16, 1)
+    # the factors (64 tokens x 2 slots x 16 channels of bf16) in front of the forward's workspace
+    assert f(1, 1, 64, 16, 16, 3, 16, 1) == 4096 + base
+    assert f(1, 1, 64, 16, 16, 1, 16, 1) == lib.prism_fwd_workspace_bytes(1, 1, 64, 16, 16, 1, 16, 1)
+    assert f(1, 1, 64, 16, 32, 3, 16, 1) == 0
+    need = f(1, 1, 64, 16, 16, 2, 16, 1)
+    assert _fwd_nl_call(lib, null=("ws",)) == WORKSPACE
+    assert _fwd_nl_call(lib, ws_bytes=need - 1) == WORKSPACE
+    assert _fwd_nl_call(lib, d=48) == UNSUPPORTED
+    assert _fwd_nl_call(lib, T=0) == INVALID

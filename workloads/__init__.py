@@ -239,7 +239,7 @@ def to_torch(inputs: Dict[str, np.ndarray], dtype: str, device="cuda"):
             out[key] = None
             continue
         t = torch.from_numpy(np.ascontiguousarray(val))
-        if key in ("q", "k", "v", "u", "gamma", "conv_in"):
+        if key in ("q", "k", "v", "u", "gamma", "conv_in", "p"):
             t = t.to(device=device).to(vt)
         else:
             t = t.to(device=device, dtype=torch.float32)
