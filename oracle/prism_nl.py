@@ -130,3 +130,25 @@ def preconditioner(v, alpha, p, conv_w, L: int, conv_in=None) -> np.ndarray:
             gam[:, :, t, l - 1] = np.where(r == 0.0, 0.5 * p[:, :, t, l - 1], z / safe)
             r = r - alpha[:, :, t, l - 1, None] * z
     return gam
+
+
+def predictor_gains(v, conv_w, W_p, L: int, conv_in=None) -> np.ndarray:
+    """Gains produced by a linear predictor on the anchor ([Notes §2.3]: parallel
+    predictors read the ShortConv anchor and emit each layer's gain vector):
+    p_{t,l} = W_p[h, l] anchor_t, with W_p [H, L-1, dv, dv] in the (out, in) layout.
+
+    v: [B, H, T, dv]; conv_w: [H, 4, dv]; conv_in: optional [B, H, 3, dv].
+    Returns p [B, H, T, L-1, dv], float64.
+    """
+    v = np.asarray(v, F64)
+    B, H, T, dv = v.shape
+    W = np.asarray(W_p, F64)
+    w = np.asarray(conv_w, F64)
+    hist = np.zeros((B, H, 3, dv), F64) if conv_in is None else np.asarray(conv_in, F64)
+    v_ext = np.concatenate([hist, v], axis=2)
+    p = np.zeros((B, H, T, max(L - 1, 0), dv), F64)
+    for t in range(T):
+        anchor = shortconv_anchor(v_ext, w[None], t + 3)          # [B, H, dv]
+        for l in range(L - 1):
+            p[:, :, t, l] = np.einsum("hoi,bhi->bho", W[:, l], anchor)
+    return p

@@ -115,3 +115,36 @@ def test_preconditioner_zero_residual_limit():
     cw[:, 3, :] = 1.0      # the anchor is the value itself: r_0 = 0
     gam = onl.preconditioner(x["v"], x["alpha"], x["p"], cw, 3)
     np.testing.assert_array_equal(gam, 0.5 * np.asarray(x["p"], np.float64))
+
+
+def test_predictor_gains_brute_force():
+    """p_{t,l}[o] = sum_i W[h, l, o, i] sum_j w[h, j, i] v[t - 3 + j, i], by plain loops."""
+    rng = np.random.default_rng(11)
+    B, H, T, dv, L = 1, 2, 6, 3, 3
+    v = rng.standard_normal((B, H, T, dv))
+    cw = rng.standard_normal((H, 4, dv))
+    W = rng.standard_normal((H, L - 1, dv, dv))
+    ci = rng.standard_normal((B, H, 3, dv))
+    p = onl.predictor_gains(v, cw, W, L, conv_in=ci)
+    for h in range(H):
+        for t in range(T):
+            for l in range(L - 1):
+                for o in range(dv):
+                    acc = 0.0
+                    for i in range(dv):
+                        a = 0.0
+                        for j in range(4):
+                            s = t - 3 + j
+                            x = v[0, h, s, i] if s >= 0 else ci[0, h, s + 3, i]
+                            a += cw[h, j, i] * x
+                        acc += W[h, l, o, i] * a
+                    assert abs(p[0, h, t, l, o] - acc) < 1e-12
+    # identity weights give the anchor itself; zero weights give zero gains
+    eye = np.broadcast_to(np.eye(dv), (H, L - 1, dv, dv))
+    pa = onl.predictor_gains(v, cw, eye, L)
+    pz = onl.predictor_gains(v, cw, np.zeros_like(W), L)
+    assert np.all(pz == 0)
+    np.testing.assert_allclose(pa[:, :, :, 0], pa[:, :, :, 1], rtol=0, atol=0)
+    for t in range(T):
+        np.testing.assert_allclose(pa[0, :, t, 0], orc.shortconv_anchor(
+            np.concatenate([np.zeros((H, 3, dv)), v[0]], axis=1), cw, t + 3), atol=1e-14)
