@@ -463,6 +463,7 @@ def time_nl(w, steps, warmup, x0=None):
         x = dict(x0) if (s == 0 and x0 is not None) else workloads.generate(w, seed=w.seed + 100 * s)
         x.pop("gamma", None)
         x["p"] = workloads.generate_gain(w, seed=w.seed + 100 * s)
+        x["W_p"] = workloads.generate_predictor(w, seed=w.seed + 100 * s)
         sets.append(workloads.to_torch(x, w.dtype, "cuda"))
     lib = prism.load_library()
     dt = prism.PRISM_BF16 if w.dtype == "bf16" else prism.PRISM_F32
@@ -479,12 +480,22 @@ def time_nl(w, steps, warmup, x0=None):
     def gain(d):
         prism.nl_gain(d["v"], d["alpha"], d["p"], d["conv_w"], w.L)
 
+    def fwd_pred(d):
+        prism.fwd_nl_pred(d["q"], d["k"], d["v"], d["g"], d["beta"], d["u"], d["alpha"], d["W_p"], d["conv_w"],
+                          L=w.L, chunk=w.chunk, out=(o, S), workspace=ws)
+
+    def gain_pred(d):
+        prism.nl_gain_pred(d["v"], d["alpha"], d["W_p"], d["conv_w"], w.L)
+
     hip = Hip()
     stream = torch.cuda.current_stream()
     rec = hip.lib.hipEventRecord
     rec.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
     res = {}
-    for name, fn in (("fwd_nl", fwd), ("nl_gain", gain)):
+    pred = w.dtype == "bf16" and w.dv in (32, 64, 128) and w.L > 1
+    fns = [("fwd_nl", fwd), ("nl_gain", gain)] + ([("fwd_nl_pred", fwd_pred), ("nl_gain_pred", gain_pred)]
+                                                  if pred else [])
+    for name, fn in fns:
         for i in range(warmup):
             fn(sets[i % 2])
         torch.cuda.synchronize()
@@ -500,13 +511,25 @@ def time_nl(w, steps, warmup, x0=None):
     per_th = E * w.dv + 2 * E * (w.L - 1) * w.dv + 4 * w.L if w.L > 1 else 0
     total = w.pairs * w.T * per_th
     gb = total / (res["nl_gain"] * 1e-3) / 1e9 if w.L > 1 else None
+    # predicted gains: v and the step sizes read, the factors written (the weights stay cached)
+    per_pred = E * w.dv + E * (w.L - 1) * w.dv + 4 * w.L
+    total_pred = w.pairs * w.T * per_pred
     del sets, ws
+    if pred:
+        gp = total_pred / (res["nl_gain_pred"] * 1e-3) / 1e9
+        pred_out = {"ms_per_step": res["fwd_nl_pred"], "tokens_per_s": w.B * w.T / (res["fwd_nl_pred"] * 1e-3),
+                    "gain_kernel_ms": res["nl_gain_pred"],
+                    "gain_roofline": {"bound": "hbm", "bytes_per_token_head": per_pred,
+                                      "bytes_per_launch": total_pred, "achieved": gp, "peak": HBM_PEAK_GBS,
+                                      "unit": "GB/s", "frac": gp / HBM_PEAK_GBS, "kernel": "nl_pred_gain_kernel"}}
+    else:
+        pred_out = None
     return {"ms_per_step": res["fwd_nl"], "tokens_per_s": w.B * w.T / (res["fwd_nl"] * 1e-3),
             "gain_kernel_ms": res["nl_gain"],
             "gain_roofline": {"bound": "hbm", "bytes_per_token_head": per_th, "bytes_per_launch": total,
                               "achieved": gb, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                               "frac": None if gb is None else gb / HBM_PEAK_GBS, "kernel": "nl_gain_kernel"},
-            "steps": steps, "warmup": warmup, "input_sets": 2}
+            "predicted_gains": pred_out, "steps": steps, "warmup": warmup, "input_sets": 2}
 
 
 def main():

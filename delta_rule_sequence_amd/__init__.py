@@ -65,6 +65,10 @@ def load_library() -> ctypes.CDLL:
     lib.prism_nl_gain.restype = ctypes.c_int
     lib.prism_fwd_nl.argtypes = fwd_args + [vp]
     lib.prism_fwd_nl.restype = ctypes.c_int
+    lib.prism_nl_gain_pred.argtypes = [vp, fp, vp, fp, vp, i, i, i, i, i, i, vp, vp]
+    lib.prism_nl_gain_pred.restype = ctypes.c_int
+    lib.prism_fwd_nl_pred.argtypes = fwd_args + [vp]
+    lib.prism_fwd_nl_pred.restype = ctypes.c_int
     lib.prism_fwd_nl_workspace_bytes.argtypes = [i] * 8
     lib.prism_fwd_nl_workspace_bytes.restype = sz
     lib.prism_status_string.argtypes = [ctypes.c_int]
@@ -375,4 +379,66 @@ def fwd_nl(q, k, v, g, beta, u=None, alpha=None, p=None, conv_w=None, L: int = 1
                           ctypes.c_void_p(workspace.data_ptr()), workspace.numel(), ctypes.c_void_p(s))
     if st != 0:
         raise PrismError(f"prism_fwd_nl failed: {status_string(st)}")
+    return o, S
+
+
+def nl_gain_pred(v, alpha, W_p, conv_w, L: int, conv_in=None, stream=None):
+    """gamma = nl_gain_pred(v, alpha, W_p, conv_w, L, conv_in): the chain factors of the
+    nonlinear refinement with the gains predicted from the anchor, p_l = W_p[h, l] anchor.
+    v [B,H,T,dv] bfloat16; alpha [B,H,T,L] float32; W_p [H,L-1,dv,dv] bfloat16 (out, in);
+    conv_w [H,4,dv] float32; conv_in [B,H,3,dv] optional.  None when L == 1."""
+    import torch
+    lib = load_library()
+    B, H, T, dv = v.shape
+    dev = v.device
+    if dev.type != "cuda":
+        raise PrismError("inputs must be on a GPU")
+    if L == 1:
+        return None
+    shapes = {"alpha": (B, H, T, L), "W_p": (H, L - 1, dv, dv), "conv_w": (H, 4, dv), "conv_in": (B, H, 3, dv)}
+    _check([("v", v), ("W_p", W_p)] + ([("conv_in", conv_in)] if conv_in is not None else []),
+           [("alpha", alpha), ("conv_w", conv_w)], shapes, v.dtype, dev)
+    gamma = torch.empty((B, H, T, L - 1, dv), dtype=v.dtype, device=dev)
+    s = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
+    st = lib.prism_nl_gain_pred(_ptr(v), _ptr(alpha), _ptr(W_p), _ptr(conv_w), _ptr(conv_in),
+                                B, H, T, dv, L, _dtype_code(v), _ptr(gamma), ctypes.c_void_p(s))
+    if st != 0:
+        raise PrismError(f"prism_nl_gain_pred failed: {status_string(st)}")
+    return gamma
+
+
+def fwd_nl_pred(q, k, v, g, beta, u=None, alpha=None, W_p=None, conv_w=None, L: int = 1, chunk: int = 64,
+                out: Optional[Tuple] = None, workspace=None, stream=None):
+    """o, S_final = fwd_nl_pred(q, k, v, g, beta, u, alpha, W_p, conv_w, L, chunk): the
+    nonlinear-refinement forward with gains predicted from the anchor (see nl_gain_pred)."""
+    import torch
+    lib = load_library()
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    dt = _dtype_code(q)
+    dev = q.device
+    if dev.type != "cuda":
+        raise PrismError("inputs must be on a GPU")
+    vec = [("q", q), ("k", k), ("v", v)] + ([("u", u), ("W_p", W_p)] if L > 1 else [])
+    flt = [("g", g), ("beta", beta)] + ([("alpha", alpha), ("conv_w", conv_w)] if L > 1 else [])
+    shapes = {"k": (B, H, T, dk), "v": (B, H, T, dv), "g": (B, H, T), "beta": (B, H, T),
+              "u": (B, H, T, L - 1, dk), "W_p": (H, L - 1, dv, dv), "alpha": (B, H, T, L),
+              "conv_w": (H, 4, dv)}
+    _check(vec, flt, shapes, q.dtype, dev)
+    if out is None:
+        o = torch.empty((B, H, T, dv), dtype=q.dtype, device=dev)
+        S = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    else:
+        o, S = out
+    need = max(1, lib.prism_fwd_nl_workspace_bytes(B, H, T, dk, dv, L, chunk, dt))
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    s = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
+    st = lib.prism_fwd_nl_pred(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                               _ptr(u) if L > 1 else None, _ptr(alpha) if L > 1 else None,
+                               _ptr(W_p) if L > 1 else None, _ptr(conv_w) if L > 1 else None,
+                               B, H, T, dk, dv, L, chunk, dt, _ptr(o), _ptr(S),
+                               ctypes.c_void_p(workspace.data_ptr()), workspace.numel(), ctypes.c_void_p(s))
+    if st != 0:
+        raise PrismError(f"prism_fwd_nl_pred failed: {status_string(st)}")
     return o, S

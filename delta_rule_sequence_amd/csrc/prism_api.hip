@@ -541,6 +541,53 @@ prism_status prism_fwd_nl(const void* q, const void* k, const void* v, const flo
                   ws + off, workspace_bytes - off, 0, nullptr, stream);
 }
 
+prism_status prism_nl_gain_pred(const void* v, const float* alpha, const void* W_p, const float* conv_w,
+                                const void* conv_in, int B, int H, int T, int dv, int L, prism_dtype dt,
+                                void* gamma, hipStream_t stream) {
+  if (B <= 0 || H <= 0 || T <= 0) return PRISM_ERR_INVALID_ARG;
+  if (dt != PRISM_F32 && dt != PRISM_BF16) return PRISM_ERR_INVALID_ARG;
+  if (L < 1 || L > 8) return PRISM_ERR_UNSUPPORTED;
+  if (dt != PRISM_BF16 || !(dv == 32 || dv == 64 || dv == 128)) return PRISM_ERR_UNSUPPORTED;
+  if (L == 1) return PRISM_OK;
+  if (!v || !alpha || !W_p || !conv_w || !gamma) return PRISM_ERR_INVALID_ARG;
+  size_t P, bytes;
+  if (!mul_ok((size_t)B, (size_t)H, &P) || !nl_gamma_bytes(B, H, T, dv, L, dt, &bytes)) return PRISM_ERR_INVALID_ARG;
+  if (P > 65535) return PRISM_ERR_UNSUPPORTED;
+  const dim3 grid((unsigned)(((size_t)T + 63) / 64), (unsigned)P);
+  prism::NlPredArgs a;
+  a.v = v; a.alpha = alpha; a.W_p = W_p; a.conv_w = conv_w; a.conv_in = conv_in; a.gamma = gamma;
+  a.H = H; a.T = T; a.L = L;
+  switch (dv) {
+    case 32: hipLaunchKernelGGL((prism::nl_pred_gain_kernel<32>), grid, dim3(256), 0, stream, a); break;
+    case 64: hipLaunchKernelGGL((prism::nl_pred_gain_kernel<64>), grid, dim3(256), 0, stream, a); break;
+    default: hipLaunchKernelGGL((prism::nl_pred_gain_kernel<128>), grid, dim3(256), 0, stream, a); break;
+  }
+  return hipGetLastError() == hipSuccess ? PRISM_OK : PRISM_ERR_HIP;
+}
+
+prism_status prism_fwd_nl_pred(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                               const void* u, const float* alpha, const void* W_p, const float* conv_w,
+                               int B, int H, int T, int dk, int dv, int L, int chunk, prism_dtype dt,
+                               void* o, float* S_final, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
+  Plan pl;
+  prism_status st = make_plan(B, H, T, dk, dv, L, chunk, dt, 0, &pl);
+  if (st != PRISM_OK) return st;
+  if (L > 1 && (dt != PRISM_BF16 || dv == 16)) return PRISM_ERR_UNSUPPORTED;
+  if (!q || !k || !v || !g || !beta || !o || !S_final) return PRISM_ERR_INVALID_ARG;
+  if (L > 1 && (!u || !alpha || !W_p || !conv_w)) return PRISM_ERR_INVALID_ARG;
+  size_t gb;
+  if (!nl_gamma_bytes(B, H, T, dv, L, dt, &gb)) return PRISM_ERR_INVALID_ARG;
+  const size_t off = align_up(gb);
+  if (!workspace || workspace_bytes < off + pl.total) return PRISM_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  void* gamma = L > 1 ? ws : nullptr;
+  st = prism_nl_gain_pred(v, alpha, W_p, conv_w, nullptr, B, H, T, dv, L, dt, gamma, stream);
+  if (st != PRISM_OK) return st;
+  return fwd_impl(q, k, v, g, beta, u, alpha, gamma, conv_w, B, H, T, dk, dv, L, chunk, dt, o, S_final,
+                  ws + off, workspace_bytes - off, 0, nullptr, stream);
+}
+
 const char* prism_status_string(prism_status s) {
   switch (s) {
     case PRISM_OK: return "PRISM_OK";

@@ -249,6 +249,29 @@ prism_status prism_fwd_nl(const void* q, const void* k, const void* v,
                           void* o, float* S_final,
                           void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Gains from a linear predictor on the anchor, fused with the factor pass ("PRISM" reading
+ * notes, section 2.3: predictors read the ShortConv anchor and emit each layer's gain):
+ *   p_{t,l} = W_p[h, l] anchor_t,   W_p [H, L-1, dv, dv] bfloat16 in the (out, in) layout,
+ * then the factors of prism_nl_gain from those gains.  The gains are formed on MFMA from the
+ * anchor rounded to bfloat16 (float32 sums) and never written.  Other arguments as
+ * prism_nl_gain.  Supported: dt = PRISM_BF16, dv in {32, 64, 128}, B * H <= 65535.  For
+ * L == 1 nothing is enqueued and the pointers may be NULL. */
+prism_status prism_nl_gain_pred(const void* v, const float* alpha, const void* W_p, const float* conv_w,
+                                const void* conv_in, int B, int H, int T, int dv, int L, prism_dtype dt,
+                                void* gamma, hipStream_t stream);
+
+/* The nonlinear-refinement forward with predicted gains in one call: prism_nl_gain_pred into
+ * the front of the workspace, then prism_fwd.  Arguments as prism_fwd with the predictor
+ * weights W_p in place of gamma (NULL allowed when L == 1).  Workspace:
+ * prism_fwd_nl_workspace_bytes.  Supported as prism_nl_gain_pred when L > 1. */
+prism_status prism_fwd_nl_pred(const void* q, const void* k, const void* v,
+                               const float* g, const float* beta,
+                               const void* u, const float* alpha, const void* W_p,
+                               const float* conv_w,
+                               int B, int H, int T, int dk, int dv, int L, int chunk, prism_dtype dt,
+                               void* o, float* S_final,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* A static, human-readable name of a status code. */
 const char* prism_status_string(prism_status s);
 

@@ -246,3 +246,39 @@ def test_fwd_nl_workspace(lib):
     assert _fwd_nl_call(lib, ws_bytes=need - 1) == WORKSPACE
     assert _fwd_nl_call(lib, d=48) == UNSUPPORTED
     assert _fwd_nl_call(lib, T=0) == INVALID
+
+
+def _pred_call(lib, B=1, H=1, T=64, dv=64, L=3, dt=1, null=()):
+    p = ctypes.c_void_p(1)
+    a = {n: (None if n in null else p) for n in ["v", "alpha", "W", "conv_w", "gamma"]}
+    return lib.prism_nl_gain_pred(a["v"], a["alpha"], a["W"], a["conv_w"], None, B, H, T, dv, L, dt,
+                                  a["gamma"], None)
+
+
+@pytest.mark.parametrize("name", ["v", "alpha", "W", "conv_w", "gamma"])
+def test_nl_gain_pred_null_pointer(lib, name):
+    assert _pred_call(lib, null=(name,)) == INVALID
+
+
+def test_nl_gain_pred_argument_checks(lib):
+    assert _pred_call(lib, T=0) == INVALID
+    assert _pred_call(lib, dt=0) == UNSUPPORTED       # bfloat16 only (MFMA operands)
+    assert _pred_call(lib, dv=16) == UNSUPPORTED      # the contraction is 32 deep
+    assert _pred_call(lib, L=9) == UNSUPPORTED
+    assert _pred_call(lib, dt=4) == INVALID
+    assert _pred_call(lib, L=1, null=("v", "alpha", "W", "conv_w", "gamma")) == OK
+
+
+def test_fwd_nl_pred_checks(lib):
+    p = ctypes.c_void_p(1)
+
+    def call(d=64, L=3, dt=1, null=(), ws=1 << 30):
+        a = {n: (None if n in null else p) for n in ["q", "k", "v", "g", "beta", "u", "alpha", "W", "cw", "o", "S",
+                                                     "ws"]}
+        return lib.prism_fwd_nl_pred(a["q"], a["k"], a["v"], a["g"], a["beta"], a["u"], a["alpha"], a["W"], a["cw"],
+                                     1, 1, 64, d, d, L, 64, dt, a["o"], a["S"], a["ws"], ws, None)
+    for n in ["q", "k", "v", "g", "beta", "u", "alpha", "W", "cw", "o", "S"]:
+        assert call(null=(n,)) == INVALID, n
+    assert call(dt=0) == UNSUPPORTED
+    assert call(null=("ws",)) == WORKSPACE
+    assert call(ws=lib.prism_fwd_nl_workspace_bytes(1, 1, 64, 64, 64, 3, 64, 1) - 1) == WORKSPACE

@@ -8,6 +8,8 @@
   two pieces, against one oracle pass.
 * At the 16K workload (T = 16384, H = 4, d = 64, L = 4, bf16) the factors of sampled
   token windows against the oracle, and the one-call forward against the two-call one.
+* Gains predicted from the anchor (prism_nl_gain_pred, prism_fwd_nl_pred): factors and
+  forward against the oracle fed oracle.prism_nl.predictor_gains.
 
 Tolerances (max-abs error relative to max |reference|): forward as the linear forward's
 parity tests, 1e-4 for float32 I/O and 2e-2 for bfloat16 I/O.  Factors: 1e-5 in float32
@@ -163,3 +165,58 @@ def test_nl_full_size_16k(prism):
         err = rel_err(gam[:, :, t0:t1], ref)
         assert err <= GTOL["bf16"], (t0, err)
     log("  sampled factors within tolerance; fused and two-call forwards identical")
+
+
+# ---- gains predicted from the anchor (prism_nl_gain_pred, prism_fwd_nl_pred) -------------
+PRED_CASES = {
+    "bf16_d32_L3": workloads.Workload("nlp_bf16_d32", "bf16", B=2, H=2, T=75, dk=32, dv=32, L=3, chunk=32, seed=85),
+    "bf16_d64_L4": CASES["bf16_d64_L4"],
+    "bf16_d128_L8": CASES["bf16_d128_L8"],
+}
+
+
+def _pred_inputs(w, conv_in=None):
+    x = workloads.generate(w)
+    x["W_p"] = workloads.generate_predictor(w)
+    x["p"] = onl.predictor_gains(x["v"], x["conv_w"], x["W_p"], w.L, conv_in=conv_in)
+    return x
+
+
+@pytest.mark.parametrize("hist", [False, True])
+@pytest.mark.parametrize("key", list(PRED_CASES))
+def test_pred_gain_factors(prism, key, hist):
+    """Factors from predicted gains against the oracle's (gains in float64 from the float64
+    anchor; the kernel rounds the anchor to bfloat16 for its MFMA operand)."""
+    import torch
+    w = PRED_CASES[key]
+    ci = workloads.generate_state(w)["conv_in"] if hist else None
+    x = _pred_inputs(w, ci)
+    log(f"[nl pred gain] {key} hist={hist}")
+    d = workloads.to_torch({k: x[k] for k in ("v", "alpha", "W_p", "conv_w")}, w.dtype)
+    cid = workloads.to_torch({"conv_in": ci}, w.dtype)["conv_in"] if hist else None
+    gam = prism.nl_gain_pred(d["v"], d["alpha"], d["W_p"], d["conv_w"], w.L, conv_in=cid)
+    torch.cuda.synchronize()
+    ref = onl.preconditioner(x["v"], x["alpha"], x["p"], x["conv_w"], w.L, conv_in=ci)
+    err = rel_err(gam.float().cpu().numpy(), ref)
+    log(f"  factors rel err {err:.3e} (tol {GTOL[w.dtype]:.0e})")
+    assert err <= GTOL[w.dtype]
+
+
+@pytest.mark.parametrize("key", list(PRED_CASES))
+def test_fwd_nl_pred_parity(prism, key):
+    import torch
+    w = PRED_CASES[key]
+    x = _pred_inputs(w)
+    log(f"[nl pred fwd] {key}")
+    d = workloads.to_torch({k: v for k, v in x.items() if k not in ("gamma", "p")}, w.dtype)
+    o, S = prism.fwd_nl_pred(d["q"], d["k"], d["v"], d["g"], d["beta"], d["u"], d["alpha"], d["W_p"],
+                             d["conv_w"], L=w.L, chunk=w.chunk)
+    torch.cuda.synchronize()
+    ref_o, ref_S = onl.forward_nl(x["q"], x["k"], x["v"], x["g"], x["beta"], x["u"], x["alpha"], x["p"],
+                                  x["conv_w"], w.L)
+    o = o.float().cpu().numpy()
+    S = S.cpu().numpy()
+    eo, es = rel_err(o, ref_o), rel_err(S, ref_S)
+    log(f"  rel err o {eo:.3e}  S_final {es:.3e} (tol {TOL[w.dtype]:.0e})")
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(S))
+    assert eo <= TOL[w.dtype] and es <= TOL[w.dtype]

@@ -22,7 +22,8 @@ Input recipe (seed = the workload's seed):
 * For the nonlinear-refinement variant only (generate_gain): the gains
   p ~ N(0, 1) [B, H, T, L-1, dv], tensor id 5, in the I/O dtype.  The pages give
   no statistics for the predicted gains; unit normals put p * r across the
-  GELU's curved range.
+  GELU's curved range.  For the predicted gains instead (generate_predictor): weights
+  W_p ~ N(0, 1/dv) [H, L-1, dv, dv] from default_rng(seed + 2000), in the I/O dtype.
 * Vectors (q, k, v, u, gamma) are stored in the I/O dtype: float32, or
   bfloat16 values (round to nearest even of the float32 value).  The scalars g,
   beta, alpha and the conv weights are float32 in both paths.
@@ -43,7 +44,7 @@ from typing import Dict, Optional
 import numpy as np
 from scipy.special import ndtr
 
-__all__ = ["Workload", "WORKLOADS", "workload", "generate", "generate_gain",
+__all__ = ["Workload", "WORKLOADS", "workload", "generate", "generate_gain", "generate_predictor",
            "generate_state", "to_bf16_values", "manifest"]
 
 
@@ -211,6 +212,18 @@ def generate_gain(w: Workload, seed: Optional[int] = None) -> Optional[np.ndarra
     return _fill_rows(seed, 5, (w.B, w.H, w.T, w.L - 1, w.dv), w.dtype, None)
 
 
+def generate_predictor(w: Workload, seed: Optional[int] = None) -> Optional[np.ndarray]:
+    """Weights W_p [H, L-1, dv, dv] ((out, in) layout, I/O dtype) of a linear gain predictor
+    on the anchor, N(0, 1/dv) entries (a random initialisation: the gains then have about
+    the anchor's scale).  None for L = 1."""
+    if w.L == 1:
+        return None
+    seed = (w.seed if seed is None else seed) + 2000
+    rng = np.random.default_rng(seed)
+    W = rng.standard_normal((w.H, w.L - 1, w.dv, w.dv)) / np.sqrt(w.dv)
+    return _cast_vec(W, w.dtype)
+
+
 def generate_state(w: Workload, seed: Optional[int] = None) -> Dict[str, np.ndarray]:
     """A starting point for a continued sequence of workload `w`: S0 [B,H,dk,dv] float32
     with N(0, 0.3^2) entries (the S_final layout) and conv_in [B,H,3,dv], values of the
@@ -239,7 +252,7 @@ def to_torch(inputs: Dict[str, np.ndarray], dtype: str, device="cuda"):
             out[key] = None
             continue
         t = torch.from_numpy(np.ascontiguousarray(val))
-        if key in ("q", "k", "v", "u", "gamma", "conv_in", "p"):
+        if key in ("q", "k", "v", "u", "gamma", "conv_in", "p", "W_p"):
             t = t.to(device=device).to(vt)
         else:
             t = t.to(device=device, dtype=torch.float32)
