@@ -220,3 +220,33 @@ def test_fwd_nl_pred_parity(prism, key):
     log(f"  rel err o {eo:.3e}  S_final {es:.3e} (tol {TOL[w.dtype]:.0e})")
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(S))
     assert eo <= TOL[w.dtype] and es <= TOL[w.dtype]
+
+
+@pytest.mark.parametrize("key", ["f32_d32_L3", "bf16_d64_L4"])
+def test_nl_decode_steps(prism, key):
+    """Token-by-token generation of the nonlinear variant: each token's factors from the
+    carried ShortConv window (prism_nl_gain with T = 1, conv_in = the decode window), then
+    prism_decode_step; against the oracle over the same tokens from the same start."""
+    import torch
+    w = CASES[key].replace(T=12)
+    x = _inputs(w)
+    st = workloads.generate_state(w)
+    log(f"[nl decode] {key} {w.T} steps")
+    d = _dev(x, w)
+    s = workloads.to_torch(st, w.dtype)
+    S, conv = s["S0"].clone(), s["conv_in"].clone()
+    outs = []
+    for t in range(w.T):
+        one = {k: (None if v is None else v[:, :, t:t + 1].contiguous()) for k, v in d.items() if k != "conv_w"}
+        gam = prism.nl_gain(one["v"], one["alpha"], one["p"], d["conv_w"], w.L, conv_in=conv)
+        sq = lambda t_: t_[:, :, 0].contiguous()  # noqa: E731
+        o = prism.decode_step(S, conv, sq(one["q"]), sq(one["k"]), sq(one["v"]), sq(one["g"]), sq(one["beta"]),
+                              sq(one["u"]), sq(one["alpha"]), sq(gam), d["conv_w"], L=w.L)
+        outs.append(o.float().cpu().numpy().astype(np.float64))
+    torch.cuda.synchronize()
+    ref_o, ref_S = onl.forward_nl(x["q"], x["k"], x["v"], x["g"], x["beta"], x["u"], x["alpha"], x["p"],
+                                  x["conv_w"], w.L, S0=st["S0"], conv_in=st["conv_in"])
+    o = np.stack(outs, axis=2)
+    eo, es = rel_err(o, ref_o), rel_err(S.cpu().numpy(), ref_S)
+    log(f"  rel err o {eo:.3e}  S_final {es:.3e}")
+    assert eo <= TOL[w.dtype] and es <= TOL[w.dtype]
