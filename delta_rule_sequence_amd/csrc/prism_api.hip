@@ -553,7 +553,8 @@ prism_status prism_nl_gain_pred(const void* v, const float* alpha, const void* W
   size_t P, bytes;
   if (!mul_ok((size_t)B, (size_t)H, &P) || !nl_gamma_bytes(B, H, T, dv, L, dt, &bytes)) return PRISM_ERR_INVALID_ARG;
   if (P > 65535) return PRISM_ERR_UNSUPPORTED;
-  const dim3 grid((unsigned)(((size_t)T + 63) / 64), (unsigned)P);
+  const size_t wg_tokens = dv == 64 ? 256 : 64;  // 4 waves x 16 tokens x tiles per wave
+  const dim3 grid((unsigned)(((size_t)T + wg_tokens - 1) / wg_tokens), (unsigned)P);
   prism::NlPredArgs a;
   a.v = v; a.alpha = alpha; a.W_p = W_p; a.conv_w = conv_w; a.conv_in = conv_in; a.gamma = gamma;
   a.H = H; a.T = T; a.L = L;

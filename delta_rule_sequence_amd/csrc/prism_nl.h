@@ -125,15 +125,17 @@ __global__ __launch_bounds__(256) void nl_gain_kernel(NlArgs a) {
 //   p_{t,l} = W_p[h][l] anchor_t    (W_p [H][L-1][D][D], (out, in) layout, bfloat16)
 // then the factors as in nl_gain_kernel.  The gains never touch memory: per token-head the
 // pass reads v and the step sizes and writes the factors (W_p, D x D per level and head,
-// stays in cache).  One workgroup of 4 waves per 64 tokens of a pair; wave w takes tokens
-// tw = 64 blockIdx.x + 16 w .. + 15 on its own:
-//   * its 19-row value window (3 rows of halo) is staged in LDS;
+// stays in cache).  One workgroup of 4 waves per 4 x 16 TPW tokens of a pair; wave w takes
+// 16 TPW consecutive tokens on its own:
+//   * its value window (3 rows of halo) and step sizes are staged in LDS;
 //   * the anchor of its 16 tokens, rounded to bfloat16, is the A operand of 16x16x32
 //     MFMAs (lane: token li, channels 32 kb + 8 g .. + 7, from 16-byte LDS reads); the B
 //     operand of output tile nt in lane li is row NT li + nt of W_p (one 16-byte load), so
 //     lane (li, g) ends with p for tokens 4 g + rr and the NT adjacent channels NT li ..:
 //   * the residual chain runs in that layout (r from 8-byte window reads, in the
 //     forward's order of operations) and each token's NT factors leave as one vector store.
+// Ruled out at the 16K shape: one 16-token tile per wave re-read each level's weights for
+// every 16 tokens (46-51 us, whatever the LDS layout or occupancy).
 struct NlPredArgs {
   const void* v;        // [P][T][D] bf16
   const float* alpha;   // [P][T][L]
@@ -165,23 +167,27 @@ __device__ __forceinline__ void bf_store(bf16_t* p, const bf16_t (&x)[N]) {
   *reinterpret_cast<typename BfN<N>::raw*>(p) = r;
 }
 
-// at most 168 VGPRs for d <= 64, so three waves share each SIMD to hide the memory latency
+// Wave w of a workgroup takes TPW consecutive 16-token tiles (TPW = 4 for d = 64, so each
+// level's W_p fragments are loaded once for 64 tokens: the weights' cache traffic is a
+// quarter of one tile per wave; 243 VGPRs, two waves per SIMD, no spills).
 template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 3 : 1)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 2 : 1)))
 void nl_pred_gain_kernel(NlPredArgs a) {
   static_assert(D == 32 || D == 64 || D == 128, "32-deep MFMA contraction over the channels");
-  constexpr int LDV = D + 8;  // LDS row stride (bf16)
+  constexpr int TPW = D == 64 ? 4 : 1;
+  constexpr int ROWS = 16 * TPW + 3;  // a wave's value window
+  constexpr int LDV = D + 8;          // LDS row stride (bf16)
   constexpr int KB = D / 32, NT = D / 16, PIECES = D / 8;
-  __shared__ __align__(16) bf16_t sV[4][19 * LDV];  // per wave: value rows tw-3 .. tw+15
-  __shared__ float sA[4][16 * 8];                    // per wave: step sizes [token][level]
+  __shared__ __align__(16) bf16_t sV[4][ROWS * LDV];  // per wave: value rows tw-3 .. tw+16 TPW-1
+  __shared__ float sA[4][16 * TPW * 8];               // per wave: step sizes [token][level]
   const int w = wave_id(), l = lane_id(), li = l & 15, g = l >> 4;
   const int pr = blockIdx.y, hd = pr % a.H, T = a.T, L = a.L, Lm1 = L - 1;
-  const int tw = blockIdx.x * 64 + 16 * w;
+  const int tw = (blockIdx.x * 4 + w) * 16 * TPW;
   const bf16_t* v = reinterpret_cast<const bf16_t*>(a.v) + (size_t)pr * T * D;
   const bf16_t* ci = a.conv_in != nullptr ? reinterpret_cast<const bf16_t*>(a.conv_in) + (size_t)pr * 3 * D : nullptr;
   bf16_t* sv = sV[w];
   // rows before the sequence come from the history (else zero); rows past its end are zero
-  for (int i = l; i < 19 * PIECES; i += 64) {
+  for (int i = l; i < ROWS * PIECES; i += 64) {
     const int rr = i / PIECES, cv = (i % PIECES) * 8;
     const int s = tw - 3 + rr;
     uint4 x = make_uint4(0u, 0u, 0u, 0u);
@@ -192,88 +198,91 @@ void nl_pred_gain_kernel(NlPredArgs a) {
     *reinterpret_cast<uint4*>(sv + rr * LDV + cv) = x;
   }
   const float* al = a.alpha + (size_t)pr * T * L;
-  for (int i = l; i < 16 * L; i += 64) {
+  for (int i = l; i < 16 * TPW * L; i += 64) {
     const int tok = tw + i / L;
     sA[w][i] = tok < T ? al[(size_t)tok * L + i % L] : 0.f;
   }
   __syncthreads();
   const float* cw = a.conv_w + (size_t)hd * 4 * D;
-  bf16x8 an[KB];
+  // A operands: anchor of token 16 j + li, channels 32 kb + 8 g .. + 7
+  bf16x8 an[TPW][KB];
 #pragma unroll
-  for (int kb = 0; kb < KB; ++kb) {
-    const int c0 = 32 * kb + 8 * g;
-    float s8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < TPW; ++j)
 #pragma unroll
-    for (int jt = 0; jt < 4; ++jt) {
-      float x[8];
-      bf_load<8>(sv + (li + jt) * LDV + c0, x);
-      const float4 wa = *reinterpret_cast<const float4*>(cw + jt * D + c0);
-      const float4 wb = *reinterpret_cast<const float4*>(cw + jt * D + c0 + 4);
-      const float wt[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
+    for (int kb = 0; kb < KB; ++kb) {
+      const int c0 = 32 * kb + 8 * g;
+      float s8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int j = 0; j < 8; ++j) s8[j] += wt[j] * x[j];
+      for (int jt = 0; jt < 4; ++jt) {
+        float x[8];
+        bf_load<8>(sv + (16 * j + li + jt) * LDV + c0, x);
+        const float4 wa = *reinterpret_cast<const float4*>(cw + jt * D + c0);
+        const float4 wb = *reinterpret_cast<const float4*>(cw + jt * D + c0 + 4);
+        const float wt[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
+#pragma unroll
+        for (int q = 0; q < 8; ++q) s8[q] += wt[q] * x[q];
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) an[j][kb][q] = (bf16_t)s8[q];
     }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) an[kb][j] = (bf16_t)s8[j];
-  }
-  // residuals of tokens 4 g + rr, channels NT li + nt
+  // residuals of tokens 16 j + 4 g + rr, channels NT li + nt
   const int cl = NT * li;
-  float wt[4][NT];
+  float r[TPW][4][NT];
+  {
+    float wt[4][NT];
 #pragma unroll
-  for (int jt = 0; jt < 4; ++jt)
+    for (int jt = 0; jt < 4; ++jt)
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) wt[jt][nt] = cw[jt * D + cl + nt];
-  float r[4][NT];
+      for (int nt = 0; nt < NT; ++nt) wt[jt][nt] = cw[jt * D + cl + nt];
 #pragma unroll
-  for (int rr = 0; rr < 4; ++rr) {
-    const int tok = 4 * g + rr;  // window rows tok .. tok + 3, the token itself last
-    float x0[NT], x1[NT], x2[NT], x3[NT];
-    bf_load<NT>(sv + tok * LDV + cl, x0);
-    bf_load<NT>(sv + (tok + 1) * LDV + cl, x1);
-    bf_load<NT>(sv + (tok + 2) * LDV + cl, x2);
-    bf_load<NT>(sv + (tok + 3) * LDV + cl, x3);
+    for (int j = 0; j < TPW; ++j)
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-      r[rr][nt] = x3[nt] - (wt[0][nt] * x0[nt] + wt[1][nt] * x1[nt] + wt[2][nt] * x2[nt] + wt[3][nt] * x3[nt]);
+      for (int rr = 0; rr < 4; ++rr) {
+        const int tok = 16 * j + 4 * g + rr;  // window rows tok .. tok + 3, the token itself last
+        float x0[NT], x1[NT], x2[NT], x3[NT];
+        bf_load<NT>(sv + tok * LDV + cl, x0);
+        bf_load<NT>(sv + (tok + 1) * LDV + cl, x1);
+        bf_load<NT>(sv + (tok + 2) * LDV + cl, x2);
+        bf_load<NT>(sv + (tok + 3) * LDV + cl, x3);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          r[j][rr][nt] = x3[nt] - (wt[0][nt] * x0[nt] + wt[1][nt] * x1[nt] + wt[2][nt] * x2[nt] + wt[3][nt] * x3[nt]);
+      }
   }
   const bf16_t* Wh = reinterpret_cast<const bf16_t*>(a.W_p) + (size_t)hd * Lm1 * D * D;
   bf16_t* gout = reinterpret_cast<bf16_t*>(a.gamma) + (size_t)pr * T * Lm1 * D;
-  // the gains do not depend on the residuals: level lv + 1's are formed (its weight loads
-  // and MFMAs in flight) while level lv's factors are computed
-  auto gains = [&](int lv, f32x4 (&p)[NT]) {
-    const bf16_t* W = Wh + (size_t)lv * D * D;
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      f32x4 acc = zero4();
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-        acc = mfma(an[kb], *reinterpret_cast<const bf16x8*>(W + (size_t)(cl + nt) * D + 32 * kb + 8 * g), acc);
-      p[nt] = acc;
-    }
-  };
-  f32x4 pc[NT];
-  gains(0, pc);
   for (int lv = 0; lv < Lm1; ++lv) {
-    f32x4 pn[NT];
-    gains(lv + 1 < Lm1 ? lv + 1 : lv, pn);
-    bf16_t fb[4][NT];
+    // this level's weight fragments, loaded once for the wave's TPW tiles
+    const bf16_t* W = Wh + (size_t)lv * D * D;
+    bf16x8 wf[NT][KB];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const float pv = pc[nt][rr];
-        fb[rr][nt] = (bf16_t)(pv * std_normal_cdf(pv * r[rr][nt]));
+      for (int kb = 0; kb < KB; ++kb)
+        wf[nt][kb] = *reinterpret_cast<const bf16x8*>(W + (size_t)(cl + nt) * D + 32 * kb + 8 * g);
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) {
+      bf16_t fb[4][NT];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) acc = mfma(an[j][kb], wf[nt][kb], acc);
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const float pv = acc[rr];
+          fb[rr][nt] = (bf16_t)(pv * std_normal_cdf(pv * r[j][rr][nt]));
+        }
       }
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int tok = tw + 4 * g + rr;
-      const float at = sA[w][(4 * g + rr) * L + lv];
+      for (int rr = 0; rr < 4; ++rr) {
+        const int tl = 16 * j + 4 * g + rr, tok = tw + tl;
+        const float at = sA[w][tl * L + lv];
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) r[rr][nt] = r[rr][nt] * (1.f - at * (float)fb[rr][nt]);
-      if (tok < T) bf_store<NT>(gout + ((size_t)tok * Lm1 + lv) * D + cl, fb[rr]);
+        for (int nt = 0; nt < NT; ++nt) r[j][rr][nt] = r[j][rr][nt] * (1.f - at * (float)fb[rr][nt]);
+        if (tok < T) bf_store<NT>(gout + ((size_t)tok * Lm1 + lv) * D + cl, fb[rr]);
+      }
     }
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) pc[nt] = pn[nt];
   }
 }
 
