@@ -155,16 +155,26 @@ prism_status launch(const FwdArgs& a, const Plan& pl, hipEvent_t* ev, hipStream_
   }
 }
 
-prism_status launch_fast(const FwdArgs& a, const Plan& pl, hipEvent_t* ev, hipStream_t stream) {
+prism_status launch_fast(const FwdArgs& a, const Plan& pl, hipEvent_t* ev, hipStream_t stream,
+                         bool nl_gains = false) {
   if (!record(ev, 0, stream)) return PRISM_ERR_HIP;
   // L = 1, 2, 4, 8 with the rank-L steps unrolled; other L through the runtime step loop
   const dim3 grid(pl.nseg, pl.P), block(512);
+  if (nl_gains) {  // a.gamma holds the gains of the nonlinear refinement
+    switch (a.L) {
+      case 2: hipLaunchKernelGGL((prism::seg_sweep8_nl_kernel<64, 64, 1>), grid, block, 0, stream, a); break;
+      case 4: hipLaunchKernelGGL((prism::seg_sweep8_nl_kernel<64, 64, 3>), grid, block, 0, stream, a); break;
+      case 8: hipLaunchKernelGGL((prism::seg_sweep8_nl_kernel<64, 64, 7>), grid, block, 0, stream, a); break;
+      default: hipLaunchKernelGGL((prism::seg_sweep8_nl_kernel<64, 64, -1>), grid, block, 0, stream, a); break;
+    }
+  } else {
   switch (a.L) {
     case 1: hipLaunchKernelGGL((prism::seg_sweep8_kernel<64, 64, 0>), grid, block, 0, stream, a); break;
     case 2: hipLaunchKernelGGL((prism::seg_sweep8_kernel<64, 64, 1>), grid, block, 0, stream, a); break;
     case 4: hipLaunchKernelGGL((prism::seg_sweep8_kernel<64, 64, 3>), grid, block, 0, stream, a); break;
     case 8: hipLaunchKernelGGL((prism::seg_sweep8_kernel<64, 64, 7>), grid, block, 0, stream, a); break;
     default: hipLaunchKernelGGL((prism::seg_sweep8_kernel<64, 64, -1>), grid, block, 0, stream, a); break;
+  }
   }
   if (hipGetLastError() != hipSuccess || !record(ev, 1, stream)) return PRISM_ERR_HIP;
   hipLaunchKernelGGL((prism::seg_scan_fast_kernel<64, 64>), dim3(pl.P, 64 / 2), dim3(256), 0, stream, a);
@@ -190,7 +200,8 @@ prism_status fwd_impl(const void* q, const void* k, const void* v, const float* 
                       int B, int H, int T, int dk, int dv, int L, int chunk, prism_dtype dt,
                       void* o, float* S_final, void* workspace, size_t workspace_bytes,
                       int seg_chunks, hipEvent_t* ev, hipStream_t stream,
-                      const float* S0 = nullptr, const void* conv_in = nullptr, void* conv_out = nullptr) {
+                      const float* S0 = nullptr, const void* conv_in = nullptr, void* conv_out = nullptr,
+                      bool nl_gains = false) {
   Plan pl;
   prism_status st = make_plan(B, H, T, dk, dv, L, chunk, dt, seg_chunks, &pl);
   if (st != PRISM_OK) return st;
@@ -210,8 +221,10 @@ prism_status fwd_impl(const void* q, const void* k, const void* v, const float* 
   a.Hin = reinterpret_cast<float*>(ws + pl.off_hin);
   a.B = B; a.H = H; a.T = T; a.L = L;
   a.nch = pl.nch; a.seg_chunks = pl.seg_chunks; a.nseg = pl.nseg;
-  st = dt == PRISM_BF16 ? dispatch<bf16_t>(dk, chunk, a, pl, ev, stream)
-                        : dispatch<float>(dk, chunk, a, pl, ev, stream);
+  if (nl_gains && !pl.fast) return PRISM_ERR_UNSUPPORTED;
+  st = nl_gains ? launch_fast(a, pl, ev, stream, true)
+       : dt == PRISM_BF16 ? dispatch<bf16_t>(dk, chunk, a, pl, ev, stream)
+                          : dispatch<float>(dk, chunk, a, pl, ev, stream);
   if (st != PRISM_OK || conv_out == nullptr) return st;
   // after the sweep, the only reader of conv_in, so conv_out may alias it
   if (dt == PRISM_BF16)
@@ -534,6 +547,10 @@ prism_status prism_fwd_nl(const void* q, const void* k, const void* v, const flo
   const size_t off = align_up(gb);
   if (!workspace || workspace_bytes < off + pl.total) return PRISM_ERR_WORKSPACE;
   char* ws = static_cast<char*>(workspace);
+  // the bf16 d = 64 sweep evaluates the factors in its own residual chain: no factor pass
+  if (pl.fast && L > 1)
+    return fwd_impl(q, k, v, g, beta, u, alpha, p, conv_w, B, H, T, dk, dv, L, chunk, dt, o, S_final,
+                    ws + off, workspace_bytes - off, 0, nullptr, stream, nullptr, nullptr, nullptr, true);
   void* gamma = L > 1 ? ws : nullptr;
   st = prism_nl_gain(v, alpha, p, conv_w, nullptr, B, H, T, dv, L, dt, gamma, stream);
   if (st != PRISM_OK) return st;

@@ -27,6 +27,7 @@
 //     inputs of the next step / chunk are loaded one phase ahead into registers.
 #pragma once
 #include "prism_fast.h"
+#include "prism_nl.h"
 
 namespace prism {
 
@@ -505,7 +506,9 @@ __device__ __forceinline__ void sweep8_kwave(const Sweep8Ctx& x, int wq) {
 }
 
 // ---- the Q waves ------------------------------------------------------------------------
-template <int LM1S>
+// NLG: the chain's factor slots hold gains p and each factor is p Phi(p r) of the running
+// residual, rounded to bfloat16 (the nonlinear refinement, as nl_gain_kernel computes it).
+template <int LM1S, bool NLG>
 __device__ __forceinline__ void sweep8_qwave(const Sweep8Ctx& x, int wq) {
   constexpr int LD = Sweep8Lds::LD, LDT = Sweep8Lds::LDT, C = 64;
   const Sweep8View V(x.smem);
@@ -584,7 +587,9 @@ __device__ __forceinline__ void sweep8_qwave(const Sweep8Ctx& x, int wq) {
       const bf16x4 gv = __builtin_bit_cast(bf16x4, gx[r]);
 #pragma unroll
       for (int cc = 0; cc < 4; ++cc) {
-        const float xr = rr[r][cc] * (1.f - apr[r] * (float)gv[cc]);
+        float gm = (float)gv[cc];
+        if constexpr (NLG) gm = (float)(bf16_t)(gm * std_normal_cdf(gm * rr[r][cc]));
+        const float xr = rr[r][cc] * (1.f - apr[r] * gm);
         rr[r][cc] = xr;
         R[r][cc] = awr[r] * xr;
       }
@@ -767,8 +772,8 @@ __device__ __forceinline__ void sweep8_qwave(const Sweep8Ctx& x, int wq) {
     for (int r = 0; r < 4; ++r) x.agg[(16 * kt + g4 + r) * 64 + 16 * cb + li] = A[kt][r];
 }
 
-template <int D, int C, int LM1S>
-__global__ __launch_bounds__(512, 1) void seg_sweep8_kernel(FwdArgs a) {
+template <int D, int C, int LM1S, bool NLG>
+__device__ __forceinline__ void sweep8_run(FwdArgs a) {
   static_assert(D == 64 && C == 64, "the two-wave sweep is written for head dim 64 and 64-token chunks");
   __shared__ __align__(16) unsigned char smem[Sweep8Lds::total];
   const Sweep8View V(smem);
@@ -823,7 +828,18 @@ __global__ __launch_bounds__(512, 1) void seg_sweep8_kernel(FwdArgs a) {
   // Both roles pass the same barriers in the same order: B0, B1, one per phase
   // P1 .. P_NL and one after the state phase, for every chunk of the segment.
   if (w < 4) sweep8_kwave<LM1S>(x, w);
-  else sweep8_qwave<LM1S>(x, w - 4);
+  else sweep8_qwave<LM1S, NLG>(x, w - 4);
+}
+
+template <int D, int C, int LM1S>
+__global__ __launch_bounds__(512, 1) void seg_sweep8_kernel(FwdArgs a) {
+  sweep8_run<D, C, LM1S, false>(a);
+}
+
+// the same sweep with the nonlinear refinement: a.gamma holds the gains p
+template <int D, int C, int LM1S>
+__global__ __launch_bounds__(512, 1) void seg_sweep8_nl_kernel(FwdArgs a) {
+  sweep8_run<D, C, LM1S, true>(a);
 }
 
 }  // namespace prism

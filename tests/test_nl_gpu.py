@@ -137,8 +137,9 @@ def test_nl_streaming_resume(prism, key):
 
 def test_nl_full_size_16k(prism):
     """The 16K workload: factors of sampled token windows against the oracle (each
-    window's three earlier values as its history), and the one-call forward against
-    factors + prism_fwd (the same kernels, so identical bits)."""
+    window's three earlier values as its history), and the one-call forward (whose d = 64
+    sweep evaluates the factors in its own chain) against factors + prism_fwd: the same
+    rounded factors up to float32 contraction order, so within a few bfloat16 steps."""
     import torch
     w = workloads.workload("rec16k_bf16")
     x = _inputs(w)
@@ -150,7 +151,10 @@ def test_nl_full_size_16k(prism):
     o2, S2 = prism.fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["u"], d["alpha"], gam, d["conv_w"],
                        L=w.L, chunk=w.chunk)
     torch.cuda.synchronize()
-    assert torch.equal(o, o2) and torch.equal(S, S2)
+    eo = rel_err(o.float().cpu().numpy(), o2.float().cpu().numpy().astype(np.float64))
+    es = rel_err(S.cpu().numpy(), S2.cpu().numpy().astype(np.float64))
+    log(f"  fused vs two-pass forward: rel diff o {eo:.3e}  S_final {es:.3e}")
+    assert eo <= 1e-2 and es <= 1e-2
     gam = gam.float().cpu().numpy()
     rng = np.random.default_rng(5)
     for t0 in [0, 1, 2, 3, 4095, 8191] + list(rng.integers(3, w.T - 64, 6)):
@@ -164,7 +168,7 @@ def test_nl_full_size_16k(prism):
                                  x["conv_w"], w.L, conv_in=ci)
         err = rel_err(gam[:, :, t0:t1], ref)
         assert err <= GTOL["bf16"], (t0, err)
-    log("  sampled factors within tolerance; fused and two-call forwards identical")
+    log("  sampled factors within tolerance")
 
 
 # ---- gains predicted from the anchor (prism_nl_gain_pred, prism_fwd_nl_pred) -------------
