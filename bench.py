@@ -49,7 +49,7 @@ def algorithmic_bytes(w):
 # the sources the segment-sweep kernel is compiled from, and the build flags
 SWEEP_SOURCES = ["delta_rule_sequence_amd/csrc/prism_sweep8.h", "delta_rule_sequence_amd/csrc/prism_fast.h",
                  "delta_rule_sequence_amd/csrc/prism_kernels.h", "delta_rule_sequence_amd/csrc/prism_tile.h",
-                 "delta_rule_sequence_amd/build.py"]
+                 "delta_rule_sequence_amd/csrc/prism_nl.h", "delta_rule_sequence_amd/build.py"]
 
 
 def kernel_source_hash():
