@@ -554,7 +554,7 @@ def main():
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the forward has no multi-GPU path "
               "(pairs and sequence segments would shard with no exchange but a small operator "
-              "all-gather; see DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+              "all-gather of the segment operators). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy)
