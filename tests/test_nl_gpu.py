@@ -38,6 +38,14 @@ CASES = {
     "bf16_d128_L8": workloads.Workload("nl_bf16_d128", "bf16", B=1, H=2, T=130, dk=128, dv=128, L=8, chunk=64,
                                        seed=83),
     "bf16_d64_L1": workloads.Workload("nl_bf16_L1", "bf16", B=1, H=1, T=70, dk=64, dv=64, L=1, chunk=64, seed=84),
+    # the nonlinear d = 64 sweep's other instantiations: L = 2 and 8 unrolled, L = 3 through
+    # the run-time step loop
+    "bf16_d64_L2": workloads.Workload("nl_bf16_d64_L2", "bf16", B=2, H=1, T=130, dk=64, dv=64, L=2, chunk=64,
+                                      seed=86),
+    "bf16_d64_L3": workloads.Workload("nl_bf16_d64_L3", "bf16", B=1, H=2, T=100, dk=64, dv=64, L=3, chunk=64,
+                                      seed=87),
+    "bf16_d64_L8": workloads.Workload("nl_bf16_d64_L8", "bf16", B=1, H=2, T=150, dk=64, dv=64, L=8, chunk=64,
+                                      seed=88),
 }
 
 
