@@ -307,11 +307,13 @@ def time_workload(w, steps, warmup, sets, x0=None):
 
 def l_sweep(steps, warmup):
     """The 16K bf16 shape at L = 1 (the plain gated delta rule), 2, 4 and 8: one JSON
-    line per L with whole-forward tokens/s and the sweep's HBM roofline fraction."""
+    line per L with whole-forward tokens/s and the sweep's HBM roofline fraction, and for
+    L > 1 the nonlinear-refinement forward (prism_fwd_nl) on the same shape."""
     import workloads
     base = workloads.workload("rec16k_bf16")
     for L in (1, 2, 4, 8):
         w = base.replace(L=L, name=f"rec16k_bf16_L{L}")
+        nl = time_nl(w, max(10, steps // 2), warmup) if L > 1 else None
         t = time_workload(w, steps, warmup, 0)
         in_bytes, path_bytes = algorithmic_bytes(w)
         sweep_ms = float(t["per"][:, 0].mean())
@@ -323,7 +325,9 @@ def l_sweep(steps, warmup):
                           "input_bytes_per_token_head": in_bytes,
                           "sweep_hbm_frac": sweep_bytes / (sweep_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                           "path_hbm_roofline_tokens_per_s":
-                              w.B * w.T * HBM_PEAK_GBS * 1e9 / (w.pairs * w.T * path_bytes)}), flush=True)
+                              w.B * w.T * HBM_PEAK_GBS * 1e9 / (w.pairs * w.T * path_bytes),
+                          "nl_ms_per_step": None if nl is None else nl["ms_per_step"],
+                          "nl_tokens_per_s": None if nl is None else nl["tokens_per_s"]}), flush=True)
 
 
 def decode_bench(steps, warmup, batch):
