@@ -8,15 +8,17 @@
 //
 //   alpha GELU(p r) = alpha (p Phi(p r)) r,   i.e.  gamma = p Phi(p r),
 //
-// evaluated on the chain's own residuals.  This kernel walks the chain once per token and
-// channel and writes those factors; the linear forward (any of its entry points) run with
-// them is the nonlinear forward.  Each factor is rounded to the I/O type before the chain
-// moves on with it, exactly as the forward's chain will use it, so both evaluate the same
-// residuals.
+// evaluated on the chain's own residuals.  nl_gain_kernel walks the chain once per token
+// and channel and writes those factors; the linear forward (any of its entry points) run
+// with them is the nonlinear forward.  Each factor is rounded to the I/O type before the
+// chain moves on with it, exactly as the forward's chain will use it, so both evaluate the
+// same residuals.  nl_pred_gain_kernel does the same with gains predicted from the anchor;
+// the bf16 d = 64 sweep (prism_sweep8.h) evaluates the factors in its own chain with
+// std_normal_cdf below.
 //
-// Work: one thread per (pair, token, 4 value channels), element-wise and HBM-bound: per
-// token-head it reads v (and the three earlier rows, from cache), L - 1 gain rows and L
-// step sizes, and writes L - 1 factor rows.
+// nl_gain_kernel: one thread per (pair, token, 4 value channels), element-wise and
+// HBM-bound: per token-head it reads v (and the three earlier rows, from cache), L - 1 gain
+// rows and L step sizes, and writes L - 1 factor rows.
 #pragma once
 #include "prism_kernels.h"
 
@@ -128,7 +130,7 @@ __global__ __launch_bounds__(256) void nl_gain_kernel(NlArgs a) {
 // stays in cache).  One workgroup of 4 waves per 4 x 16 TPW tokens of a pair; wave w takes
 // 16 TPW consecutive tokens on its own:
 //   * its value window (3 rows of halo) and step sizes are staged in LDS;
-//   * the anchor of its 16 tokens, rounded to bfloat16, is the A operand of 16x16x32
+//   * per 16-token tile the anchor, rounded to bfloat16, is the A operand of 16x16x32
 //     MFMAs (lane: token li, channels 32 kb + 8 g .. + 7, from 16-byte LDS reads); the B
 //     operand of output tile nt in lane li is row NT li + nt of W_p (one 16-byte load), so
 //     lane (li, g) ends with p for tokens 4 g + rr and the NT adjacent channels NT li ..:
