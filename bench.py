@@ -299,10 +299,13 @@ def time_workload(w, steps, warmup, sets, x0=None):
     torch.cuda.synchronize()
     per = np.array([[hip.elapsed_ms(evs[4 * i + j], evs[4 * i + j + 1]) for j in range(3)]
                     for i in range(steps)])
+    # each call's own duration, first event to last (the three kernels and the gaps between)
+    call_ms = np.array([hip.elapsed_ms(evs[4 * i], evs[4 * i + 3]) for i in range(steps)])
     span_ms = hip.elapsed_ms(evs[0], evs[4 * steps - 1])
     hip.destroy(evs)
     del dev_sets, o, S, ws
-    return {"ms_per_step": 1e3 * wall / steps, "per": per, "span_ms": span_ms, "nsets": nsets}
+    return {"ms_per_step": 1e3 * wall / steps, "per": per, "span_ms": span_ms, "nsets": nsets,
+            "call_ms": call_ms}
 
 
 def l_sweep(steps, warmup):
@@ -592,6 +595,7 @@ def main():
     t = time_workload(w, args.steps, args.warmup, args.sets, x0)
     import torch
 
+    import numpy as np
     in_bytes, path_bytes = algorithmic_bytes(w)
     ms_per_step, per, span_ms, nsets = t["ms_per_step"], t["per"], t["span_ms"], t["nsets"]
     tokens = w.B * w.T
@@ -617,13 +621,22 @@ def main():
         "data": "synthetic (seeded generator; random inputs of the workload's shapes and distributions)",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "dk": w.dk, "dv": w.dv, "L": w.L,
                    "chunk": w.chunk, "input_sets": nsets},
+        # the dominant kernel alone (the segment sweep): its input bytes over its own event time
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "scope": "dominant kernel (segment sweep), input bytes over its event-timed duration",
                      # the counters' HBM bytes over the same duration (null with traffic)
                      "traffic_GBs": None if traffic is None else traffic / (sweep_ms * 1e-3) / 1e9,
                      "kernel": sweep_name, "algorithmic_bytes_per_launch": sweep_bytes},
         "path": {"algorithmic_bytes_per_step": w.pairs * w.T * path_bytes,
                  "hbm_roofline_tokens_per_s": tokens * HBM_PEAK_GBS * 1e9 / (w.pairs * w.T * path_bytes),
+                 # the whole forward (all three kernels) against the same HBM roofline
+                 "hbm_frac": (tokens / (ms_per_step * 1e-3)) / (tokens * HBM_PEAK_GBS * 1e9 /
+                                                               (w.pairs * w.T * path_bytes)),
+                 # per-call durations from HIP events on the launch stream (second timed region)
+                 "event_ms_per_call": {"median": float(np.median(t["call_ms"])), "mean": float(t["call_ms"].mean()),
+                                       "min": float(t["call_ms"].min()), "calls": int(len(t["call_ms"]))},
+                 "event_median_tokens_per_s": tokens / (float(np.median(t["call_ms"])) * 1e-3),
                  "kernel_ms": {"sweep": sweep_ms, "scan": float(per[:, 1].mean()),
                                "fixup": float(per[:, 2].mean())},
                  "instrumented_ms_per_step": span_ms / args.steps},
@@ -639,7 +652,6 @@ def main():
                                          "flop_per_token_head": chunk_flop}
     # the backward on the same workload (one warm-up, two timed calls): reported beside the
     # forward metric, not part of it
-    import numpy as np
     d_o = np.random.default_rng(w.seed + 7).standard_normal((w.B, w.H, w.T, w.dv)).astype(np.float32)
     if w.dtype == "bf16":
         d_o = workloads.to_bf16_values(d_o)

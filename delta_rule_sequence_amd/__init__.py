@@ -37,6 +37,11 @@ def load_library() -> ctypes.CDLL:
     # hipErrorNoDevice once torch has brought up its own.
     import torch  # noqa: F401
     lib = ctypes.CDLL(LIB_PATH)
+    runtimes = _hip_runtimes_mapped()
+    if len(runtimes) > 1:
+        raise PrismError("two HIP runtimes are loaded in this process (" + ", ".join(runtimes) + "): "
+                         "libprism.so was opened before torch, so its kernels would run on a runtime that "
+                         "sees no device.  Import torch (or delta_rule_sequence_amd) before opening libprism.so.")
     vp, fp, i, sz = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
     fwd_args = [vp, vp, vp, fp, fp, vp, fp, vp, fp, i, i, i, i, i, i, i, i, vp, fp, vp, sz]
     lib.prism_fwd.argtypes = fwd_args + [vp]
@@ -71,12 +76,26 @@ def load_library() -> ctypes.CDLL:
     lib.prism_fwd_nl_pred.restype = ctypes.c_int
     lib.prism_fwd_nl_workspace_bytes.argtypes = [i] * 8
     lib.prism_fwd_nl_workspace_bytes.restype = sz
+    lib.prism_fwd_nl_seg.argtypes = fwd_args + [i, vp]
+    lib.prism_fwd_nl_seg.restype = ctypes.c_int
+    lib.prism_fwd_nl_seg_workspace_bytes.argtypes = [i] * 9
+    lib.prism_fwd_nl_seg_workspace_bytes.restype = sz
     lib.prism_status_string.argtypes = [ctypes.c_int]
     lib.prism_status_string.restype = ctypes.c_char_p
     lib.prism_version.argtypes = []
     lib.prism_version.restype = ctypes.c_char_p
     _lib = lib
     return lib
+
+
+def _hip_runtimes_mapped() -> list:
+    """Distinct files of the HIP runtime (libamdhip64) mapped into this process."""
+    try:
+        with open("/proc/self/maps") as f:
+            paths = {line.split()[-1] for line in f if "libamdhip64" in line}
+    except OSError:
+        return []
+    return sorted({os.path.realpath(p) for p in paths if p.startswith("/")})
 
 
 def header_functions() -> list:
@@ -129,6 +148,41 @@ def _check(named_vec, named_flt, shapes, dtype, dev):
             raise PrismError(f"{name} must be float32")
 
 
+def _outputs(out, B, H, T, dk, dv, dtype, dev):
+    """o and S_final: fresh tensors, or the caller's out=(o, S) after checking them."""
+    import torch
+    if out is None:
+        return (torch.empty((B, H, T, dv), dtype=dtype, device=dev),
+                torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev))
+    if not isinstance(out, (tuple, list)) or len(out) != 2:
+        raise PrismError("out must be a pair (o, S_final)")
+    o, S = out
+    for name, t, shape, dt in (("o", o, (B, H, T, dv), dtype), ("S_final", S, (B, H, dk, dv), torch.float32)):
+        if not isinstance(t, torch.Tensor):
+            raise PrismError(f"out {name} must be a tensor")
+        if t.device != dev or not t.is_contiguous():
+            raise PrismError(f"out {name} must be a contiguous tensor on {dev}")
+        if tuple(t.shape) != shape or t.dtype != dt:
+            raise PrismError(f"out {name} must have shape {shape} and dtype {dt}, "
+                             f"got {tuple(t.shape)} {t.dtype}")
+    return o, S
+
+
+def _workspace(workspace, need: int, dev):
+    """The caller's workspace after checking it, or a fresh one of `need` bytes."""
+    import torch
+    need = max(1, int(need))
+    if workspace is None:
+        return torch.empty(need, dtype=torch.uint8, device=dev)
+    if not isinstance(workspace, torch.Tensor) or workspace.dtype != torch.uint8:
+        raise PrismError("workspace must be a uint8 tensor")
+    if workspace.device != dev or not workspace.is_contiguous():
+        raise PrismError(f"workspace must be a contiguous tensor on {dev}")
+    if workspace.numel() < need:
+        raise PrismError(f"workspace holds {workspace.numel()} bytes, {need} needed")
+    return workspace
+
+
 def fwd_state(q, k, v, g, beta, u=None, alpha=None, gamma=None, conv_w=None, L: int = 1, chunk: int = 64,
               S0=None, conv_in=None, want_conv: bool = True, workspace=None, stream=None):
     """o, S_final, conv_out = fwd_state(..., S0, conv_in): the forward continued from a state.
@@ -156,9 +210,7 @@ def fwd_state(q, k, v, g, beta, u=None, alpha=None, gamma=None, conv_w=None, L: 
     o = torch.empty((B, H, T, dv), dtype=q.dtype, device=dev)
     S = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
     conv_out = torch.empty((B, H, 3, dv), dtype=q.dtype, device=dev) if want_conv else None
-    need = max(1, workspace_bytes(B, H, T, dk, dv, L, chunk, dt))
-    if workspace is None or workspace.numel() < need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    workspace = _workspace(workspace, workspace_bytes(B, H, T, dk, dv, L, chunk, dt), dev)
     s = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
     st = lib.prism_fwd_state(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                              _ptr(u) if L > 1 else None, _ptr(alpha) if L > 1 else None,
@@ -242,17 +294,9 @@ def fwd(q, k, v, g, beta, u=None, alpha=None, gamma=None, conv_w=None, L: int = 
     for name, t in vec + flt:
         if name in shapes and tuple(t.shape) != shapes[name]:
             raise PrismError(f"{name} has shape {tuple(t.shape)}, expected {shapes[name]}")
-    if out is None:
-        o = torch.empty((B, H, T, dv), dtype=q.dtype, device=dev)
-        S = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
-    else:
-        o, S = out
-    need = workspace_bytes(B, H, T, dk, dv, L, chunk, dt, seg_chunks)
-    if need == 0:
-        # let the library report which argument is wrong
-        need = 1
-    if workspace is None or workspace.numel() < need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    o, S = _outputs(out, B, H, T, dk, dv, q.dtype, dev)
+    # a size of 0 (invalid arguments) lets the library report which argument is wrong
+    workspace = _workspace(workspace, workspace_bytes(B, H, T, dk, dv, L, chunk, dt, seg_chunks), dev)
     s = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
     args = [_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
             _ptr(u) if L > 1 else None, _ptr(alpha) if L > 1 else None,
@@ -302,9 +346,7 @@ def bwd(q, k, v, g, beta, u=None, alpha=None, gamma=None, conv_w=None, L: int = 
         out.update({"du": torch.empty((B, H, T, L - 1, dk), **f32), "dalpha": torch.empty((B, H, T, L), **f32),
                     "dgamma": torch.empty((B, H, T, L - 1, dv), **f32), "dconv_w": torch.empty((H, 4, dv), **f32)})
     wsb = lib.prism_bwd_lowmem_workspace_bytes if low_memory else lib.prism_bwd_workspace_bytes
-    need = wsb(B, H, T, dk, dv, L, dt) or 1
-    if workspace is None or workspace.numel() < need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    workspace = _workspace(workspace, wsb(B, H, T, dk, dv, L, dt), dev)
     s = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
     fn = lib.prism_bwd_lowmem if low_memory else lib.prism_bwd
     st = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
@@ -346,9 +388,10 @@ def nl_gain(v, alpha, p, conv_w, L: int, conv_in=None, stream=None):
 
 
 def fwd_nl(q, k, v, g, beta, u=None, alpha=None, p=None, conv_w=None, L: int = 1, chunk: int = 64,
-           out: Optional[Tuple] = None, workspace=None, stream=None):
+           out: Optional[Tuple] = None, workspace=None, stream=None, seg_chunks: Optional[int] = None):
     """o, S_final = fwd_nl(q, k, v, g, beta, u, alpha, p, conv_w, L, chunk): the forward with
-    the nonlinear refinement, gains p [B,H,T,L-1,dv] in place of gamma (see fwd)."""
+    the nonlinear refinement, gains p [B,H,T,L-1,dv] in place of gamma (see fwd).
+    seg_chunks: an explicit segment length in chunks (prism_fwd_nl_seg)."""
     import torch
     lib = load_library()
     B, H, T, dk = q.shape
@@ -363,20 +406,22 @@ def fwd_nl(q, k, v, g, beta, u=None, alpha=None, p=None, conv_w=None, L: int = 1
               "u": (B, H, T, L - 1, dk), "p": (B, H, T, L - 1, dv), "alpha": (B, H, T, L),
               "conv_w": (H, 4, dv)}
     _check(vec, flt, shapes, q.dtype, dev)
-    if out is None:
-        o = torch.empty((B, H, T, dv), dtype=q.dtype, device=dev)
-        S = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    o, S = _outputs(out, B, H, T, dk, dv, q.dtype, dev)
+    if seg_chunks is None:
+        need = lib.prism_fwd_nl_workspace_bytes(B, H, T, dk, dv, L, chunk, dt)
     else:
-        o, S = out
-    need = max(1, lib.prism_fwd_nl_workspace_bytes(B, H, T, dk, dv, L, chunk, dt))
-    if workspace is None or workspace.numel() < need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        need = lib.prism_fwd_nl_seg_workspace_bytes(B, H, T, dk, dv, L, chunk, dt, seg_chunks)
+    workspace = _workspace(workspace, need, dev)
     s = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
-    st = lib.prism_fwd_nl(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-                          _ptr(u) if L > 1 else None, _ptr(alpha) if L > 1 else None,
-                          _ptr(p) if L > 1 else None, _ptr(conv_w) if L > 1 else None,
-                          B, H, T, dk, dv, L, chunk, dt, _ptr(o), _ptr(S),
-                          ctypes.c_void_p(workspace.data_ptr()), workspace.numel(), ctypes.c_void_p(s))
+    args = [_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+            _ptr(u) if L > 1 else None, _ptr(alpha) if L > 1 else None,
+            _ptr(p) if L > 1 else None, _ptr(conv_w) if L > 1 else None,
+            B, H, T, dk, dv, L, chunk, dt, _ptr(o), _ptr(S),
+            ctypes.c_void_p(workspace.data_ptr()), workspace.numel()]
+    if seg_chunks is None:
+        st = lib.prism_fwd_nl(*args, ctypes.c_void_p(s))
+    else:
+        st = lib.prism_fwd_nl_seg(*args, seg_chunks, ctypes.c_void_p(s))
     if st != 0:
         raise PrismError(f"prism_fwd_nl failed: {status_string(st)}")
     return o, S
@@ -425,14 +470,8 @@ def fwd_nl_pred(q, k, v, g, beta, u=None, alpha=None, W_p=None, conv_w=None, L: 
               "u": (B, H, T, L - 1, dk), "W_p": (H, L - 1, dv, dv), "alpha": (B, H, T, L),
               "conv_w": (H, 4, dv)}
     _check(vec, flt, shapes, q.dtype, dev)
-    if out is None:
-        o = torch.empty((B, H, T, dv), dtype=q.dtype, device=dev)
-        S = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
-    else:
-        o, S = out
-    need = max(1, lib.prism_fwd_nl_workspace_bytes(B, H, T, dk, dv, L, chunk, dt))
-    if workspace is None or workspace.numel() < need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    o, S = _outputs(out, B, H, T, dk, dv, q.dtype, dev)
+    workspace = _workspace(workspace, lib.prism_fwd_nl_workspace_bytes(B, H, T, dk, dv, L, chunk, dt), dev)
     s = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
     st = lib.prism_fwd_nl_pred(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                _ptr(u) if L > 1 else None, _ptr(alpha) if L > 1 else None,

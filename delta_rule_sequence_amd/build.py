@@ -2,20 +2,32 @@
 
     python -m delta_rule_sequence_amd.build
 
-Compiles every .hip source under csrc/ into one shared library next to this
+Compiles every .hip source under csrc/ to an object file (in parallel, one hipcc per
+source, objects under csrc/_build/) and links them into one shared library next to this
 file.  Uses hipcc from ROCm; no GPU is needed to build.
 """
 import os
 import shutil
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
+OBJ = os.path.join(CSRC, "_build")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libprism.so")
 ARCH = os.environ.get("PRISM_OFFLOAD_ARCH", "gfx950")
+
+# Device code flags of every translation unit.
+FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+         "-I", INCLUDE, "-I", CSRC,
+         # packed fp32 VALU ops are kept out of every kernel
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         # the latency-bound kernels (scan, sweep phases) gain from the ILP-first
+         # machine scheduler (measured: scan 19.0 -> 17.1 us at the 16K workload)
+         "-mllvm", "-amdgpu-sched-strategy=max-ilp"]
 
 
 def hipcc() -> str:
@@ -25,25 +37,35 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: install ROCm or put hipcc on PATH")
 
 
-def build(verbose: bool = False) -> str:
-    sources = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-           "-I", INCLUDE, "-I", CSRC,
-           # packed fp32 VALU ops are kept out of every kernel
-           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           # the latency-bound kernels (scan, sweep phases) gain from the ILP-first
-           # machine scheduler (measured: scan 19.0 -> 17.1 us at the 16K workload)
-           "-mllvm", "-amdgpu-sched-strategy=max-ilp",
-           *sources, "-o", tmp]
+def _jobs() -> int:
+    for var in ("MAX_JOBS", "CMAKE_BUILD_PARALLEL_LEVEL"):
+        if os.environ.get(var, "").isdigit():
+            return max(1, min(16, int(os.environ[var])))
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError(f"hipcc failed with exit code {res.returncode}")
-    os.replace(tmp, LIB)
-    return LIB
+        raise RuntimeError(f"hipcc failed with exit code {res.returncode}: {' '.join(cmd[-3:])}")
+
+
+def build(verbose: bool = False, extra_flags=(), lib_path: str = LIB, obj_dir: str = OBJ) -> str:
+    """Compile every csrc/*.hip and link lib_path; extra_flags go to every hipcc line."""
+    cc = hipcc()
+    sources = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
+    os.makedirs(obj_dir, exist_ok=True)
+    objs = [os.path.join(obj_dir, os.path.basename(s)[:-4] + ".o") for s in sources]
+    cmds = [[cc, *FLAGS, *extra_flags, "-c", s, "-o", o] for s, o in zip(sources, objs)]
+    with ThreadPoolExecutor(_jobs()) as ex:
+        list(ex.map(lambda c: _run(c, verbose), cmds))
+    tmp = lib_path + ".tmp"
+    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *extra_flags, *objs, "-o", tmp], verbose)
+    os.replace(tmp, lib_path)
+    return lib_path
 
 
 if __name__ == "__main__":

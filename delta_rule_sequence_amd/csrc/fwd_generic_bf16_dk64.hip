@@ -1,0 +1,5 @@
+// fwd_generic_bf16_dk64.hip - the generic forward for bf16 I/O and key width 64: every
+// value width (16, 32, 64, 128) and chunk size (16, 32, 64) whose tiles fit a CU's LDS.
+#include "prism_generic_launch.h"
+
+PRISM_DEFINE_GENERIC(launch_generic_bf16_dk64, prism::bf16_t, 64)

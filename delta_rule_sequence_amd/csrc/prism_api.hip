@@ -8,11 +8,10 @@
 #include <type_traits>
 
 #include "prism.h"
-#include "prism_fast.h"
-#include "prism_kernels.h"
-#include "prism_sweep8.h"
+#include "prism_bwd_args.h"
 #include "prism_decode.h"
-#include "prism_bwd.h"
+#include "prism_host.h"
+#include "prism_kernels.h"
 #include "prism_nl.h"
 
 namespace {
@@ -48,20 +47,27 @@ bool use_fast(int T, int dk, int dv, int L, int chunk, prism_dtype dt) {
   return dt == PRISM_BF16 && dk == 64 && dv == 64 && chunk == 64 && slice < ((size_t)1 << 31);
 }
 
-template <class E, int D, int C>
-constexpr bool fits() { return prism::SegLds<E, D, D, C>::fits; }
+template <class E, int DK, int DV>
+constexpr bool fits_c(int C) {
+  return C == 16 ? prism::SegLds<E, DK, DV, 16>::fits
+         : C == 32 ? prism::SegLds<E, DK, DV, 32>::fits : prism::SegLds<E, DK, DV, 64>::fits;
+}
 
-bool lds_fits(prism_dtype dt, int d, int C) {
-#define PRISM_FITS(E) \
-  switch (d) { \
-    case 16: return C == 16 ? fits<E, 16, 16>() : C == 32 ? fits<E, 16, 32>() : fits<E, 16, 64>(); \
-    case 32: return C == 16 ? fits<E, 32, 16>() : C == 32 ? fits<E, 32, 32>() : fits<E, 32, 64>(); \
-    case 64: return C == 16 ? fits<E, 64, 16>() : C == 32 ? fits<E, 64, 32>() : fits<E, 64, 64>(); \
-    default: return C == 16 ? fits<E, 128, 16>() : C == 32 ? fits<E, 128, 32>() : fits<E, 128, 64>(); \
-  }
-  if (dt == PRISM_BF16) { PRISM_FITS(bf16_t) }
-  PRISM_FITS(float)
-#undef PRISM_FITS
+template <class E, int DK>
+constexpr bool fits_v(int dv, int C) {
+  return dv == 16 ? fits_c<E, DK, 16>(C) : dv == 32 ? fits_c<E, DK, 32>(C)
+         : dv == 64 ? fits_c<E, DK, 64>(C) : fits_c<E, DK, 128>(C);
+}
+
+template <class E>
+constexpr bool fits_e(int dk, int dv, int C) {
+  return dk == 16 ? fits_v<E, 16>(dv, C) : dk == 32 ? fits_v<E, 32>(dv, C)
+         : dk == 64 ? fits_v<E, 64>(dv, C) : fits_v<E, 128>(dv, C);
+}
+
+// Whether the generic sweep's chunk tiles fit the 160 KB of LDS of a CU.
+bool lds_fits(prism_dtype dt, int dk, int dv, int C) {
+  return dt == PRISM_BF16 ? fits_e<bf16_t>(dk, dv, C) : fits_e<float>(dk, dv, C);
 }
 
 // Shape checks shared by the size query and the forward call.
@@ -70,9 +76,8 @@ prism_status check_shape(int B, int H, int T, int dk, int dv, int L, int chunk, 
   if (dt != PRISM_F32 && dt != PRISM_BF16) return PRISM_ERR_INVALID_ARG;
   if (L < 1 || L > 8) return PRISM_ERR_UNSUPPORTED;
   if (!valid_dim(dk) || !valid_dim(dv)) return PRISM_ERR_UNSUPPORTED;
-  if (dk != dv) return PRISM_ERR_UNSUPPORTED;
   if (chunk != 16 && chunk != 32 && chunk != 64) return PRISM_ERR_UNSUPPORTED;
-  if (!lds_fits(dt, dk, chunk)) return PRISM_ERR_UNSUPPORTED;
+  if (!lds_fits(dt, dk, dv, chunk)) return PRISM_ERR_UNSUPPORTED;
   return PRISM_OK;
 }
 
@@ -108,12 +113,15 @@ prism_status make_plan(int B, int H, int T, int dk, int dv, int L, int chunk, pr
     }
   }
   const size_t nseg = (nch + seg_chunks - 1) / seg_chunks;
+  // the generic path keeps O_loc, Qhat and H_in in float32; the fast path in bfloat16
+  const size_t wel = fast ? 2 : 4;
   size_t Tpad = nch * (size_t)chunk, a, b, c;
-  size_t sz_oloc, sz_qhat, sz_agg_a, sz_agg_b;
-  if (!mul_ok(P, Tpad, &a) || !mul_ok(a, (size_t)dv * 4, &sz_oloc)) return PRISM_ERR_INVALID_ARG;
-  if (!mul_ok(a, (size_t)dk * 4, &sz_qhat)) return PRISM_ERR_INVALID_ARG;
+  size_t sz_oloc, sz_qhat, sz_agg_a, sz_agg_b, sz_hin;
+  if (!mul_ok(P, Tpad, &a) || !mul_ok(a, (size_t)dv * wel, &sz_oloc)) return PRISM_ERR_INVALID_ARG;
+  if (!mul_ok(a, (size_t)dk * wel, &sz_qhat)) return PRISM_ERR_INVALID_ARG;
   if (!mul_ok(P, nseg, &b) || !mul_ok(b, (size_t)dk * dk * 4, &sz_agg_a)) return PRISM_ERR_INVALID_ARG;
   if (!mul_ok(b, (size_t)dk * dv * 4, &sz_agg_b)) return PRISM_ERR_INVALID_ARG;
+  sz_hin = sz_agg_b / 4 * wel;
   // inputs must be addressable too: P*T*(L-1)*max(dk,dv) elements
   if (!mul_ok(P, (size_t)T, &c) || !mul_ok(c, (size_t)L * (dk > dv ? dk : dv) * 4, &c))
     return PRISM_ERR_INVALID_ARG;
@@ -127,71 +135,28 @@ prism_status make_plan(int B, int H, int T, int dk, int dv, int L, int chunk, pr
   pl->off_aagg = align_up(pl->off_qhat + sz_qhat);
   pl->off_bagg = align_up(pl->off_aagg + sz_agg_a);
   pl->off_hin = align_up(pl->off_bagg + sz_agg_b);
-  pl->total = align_up(pl->off_hin + sz_agg_b);
+  pl->total = align_up(pl->off_hin + sz_hin);
   if (pl->total < sz_oloc) return PRISM_ERR_INVALID_ARG;
   return PRISM_OK;
 }
 
-inline bool record(hipEvent_t* ev, int i, hipStream_t stream) {
-  return ev == nullptr || hipEventRecord(ev[i], stream) == hipSuccess;
-}
-
-template <class E, int D, int C>
-prism_status launch(const FwdArgs& a, const Plan& pl, hipEvent_t* ev, hipStream_t stream) {
-  if constexpr (!prism::SegLds<E, D, D, C>::fits) {
-    return PRISM_ERR_UNSUPPORTED;
-  } else {
-    if (!record(ev, 0, stream)) return PRISM_ERR_HIP;
-    hipLaunchKernelGGL((prism::seg_local_kernel<E, D, D, C>), dim3(pl.nseg, pl.P), dim3(256), 0, stream, a);
-    if (hipGetLastError() != hipSuccess || !record(ev, 1, stream)) return PRISM_ERR_HIP;
-    hipLaunchKernelGGL((prism::seg_scan_kernel<D, D>), dim3(pl.P, D / 16), dim3(256), 0, stream, a);
-    if (hipGetLastError() != hipSuccess || !record(ev, 2, stream)) return PRISM_ERR_HIP;
-    if constexpr (std::is_same<E, bf16_t>::value && D == 128 && C == 64)
-      hipLaunchKernelGGL((prism::seg_fixup_mfma_kernel<D, C>), dim3(pl.nch, pl.P), dim3(256), 0, stream, a);
-    else
-      hipLaunchKernelGGL((prism::seg_fixup_kernel<E, D, D, C>), dim3(pl.nch, pl.P), dim3(256), 0, stream, a);
-    if (hipGetLastError() != hipSuccess || !record(ev, 3, stream)) return PRISM_ERR_HIP;
-    return PRISM_OK;
-  }
-}
-
-prism_status launch_fast(const FwdArgs& a, const Plan& pl, hipEvent_t* ev, hipStream_t stream,
-                         bool nl_gains = false) {
-  if (!record(ev, 0, stream)) return PRISM_ERR_HIP;
-  // L = 1, 2, 4, 8 with the rank-L steps unrolled; other L through the runtime step loop
-  const dim3 grid(pl.nseg, pl.P), block(512);
-  if (nl_gains) {  // a.gamma holds the gains of the nonlinear refinement
-    switch (a.L) {
-      case 2: hipLaunchKernelGGL((prism::seg_sweep8_nl_kernel<64, 64, 1>), grid, block, 0, stream, a); break;
-      case 4: hipLaunchKernelGGL((prism::seg_sweep8_nl_kernel<64, 64, 3>), grid, block, 0, stream, a); break;
-      case 8: hipLaunchKernelGGL((prism::seg_sweep8_nl_kernel<64, 64, 7>), grid, block, 0, stream, a); break;
-      default: hipLaunchKernelGGL((prism::seg_sweep8_nl_kernel<64, 64, -1>), grid, block, 0, stream, a); break;
+// The generic forward of one I/O type, by key width.
+prism_status dispatch_generic(prism_dtype dt, int dk, int dv, int C, const FwdArgs& a,
+                              const prism::host::LaunchShape& s, hipEvent_t* ev, hipStream_t st) {
+  using namespace prism::host;
+  if (dt == PRISM_BF16) {
+    switch (dk) {
+      case 16: return launch_generic_bf16_dk16(dv, C, a, s, ev, st);
+      case 32: return launch_generic_bf16_dk32(dv, C, a, s, ev, st);
+      case 64: return launch_generic_bf16_dk64(dv, C, a, s, ev, st);
+      default: return launch_generic_bf16_dk128(dv, C, a, s, ev, st);
     }
-  } else {
-  switch (a.L) {
-    case 1: hipLaunchKernelGGL((prism::seg_sweep8_kernel<64, 64, 0>), grid, block, 0, stream, a); break;
-    case 2: hipLaunchKernelGGL((prism::seg_sweep8_kernel<64, 64, 1>), grid, block, 0, stream, a); break;
-    case 4: hipLaunchKernelGGL((prism::seg_sweep8_kernel<64, 64, 3>), grid, block, 0, stream, a); break;
-    case 8: hipLaunchKernelGGL((prism::seg_sweep8_kernel<64, 64, 7>), grid, block, 0, stream, a); break;
-    default: hipLaunchKernelGGL((prism::seg_sweep8_kernel<64, 64, -1>), grid, block, 0, stream, a); break;
   }
-  }
-  if (hipGetLastError() != hipSuccess || !record(ev, 1, stream)) return PRISM_ERR_HIP;
-  hipLaunchKernelGGL((prism::seg_scan_fast_kernel<64, 64>), dim3(pl.P, 64 / 2), dim3(256), 0, stream, a);
-  if (hipGetLastError() != hipSuccess || !record(ev, 2, stream)) return PRISM_ERR_HIP;
-  hipLaunchKernelGGL((prism::seg_fixup_fast_kernel<64, 64>), dim3(pl.nseg, pl.P), dim3(256), 0, stream, a);
-  if (hipGetLastError() != hipSuccess || !record(ev, 3, stream)) return PRISM_ERR_HIP;
-  return PRISM_OK;
-}
-
-template <class E>
-prism_status dispatch(int d, int C, const FwdArgs& a, const Plan& pl, hipEvent_t* ev, hipStream_t s) {
-  if (pl.fast) return launch_fast(a, pl, ev, s);
-  switch (d) {
-    case 16: return C == 16 ? launch<E, 16, 16>(a, pl, ev, s) : C == 32 ? launch<E, 16, 32>(a, pl, ev, s) : launch<E, 16, 64>(a, pl, ev, s);
-    case 32: return C == 16 ? launch<E, 32, 16>(a, pl, ev, s) : C == 32 ? launch<E, 32, 32>(a, pl, ev, s) : launch<E, 32, 64>(a, pl, ev, s);
-    case 64: return C == 16 ? launch<E, 64, 16>(a, pl, ev, s) : C == 32 ? launch<E, 64, 32>(a, pl, ev, s) : launch<E, 64, 64>(a, pl, ev, s);
-    default: return C == 16 ? launch<E, 128, 16>(a, pl, ev, s) : C == 32 ? launch<E, 128, 32>(a, pl, ev, s) : launch<E, 128, 64>(a, pl, ev, s);
+  switch (dk) {
+    case 16: return launch_generic_f32_dk16(dv, C, a, s, ev, st);
+    case 32: return launch_generic_f32_dk32(dv, C, a, s, ev, st);
+    case 64: return launch_generic_f32_dk64(dv, C, a, s, ev, st);
+    default: return launch_generic_f32_dk128(dv, C, a, s, ev, st);
   }
 }
 
@@ -222,9 +187,9 @@ prism_status fwd_impl(const void* q, const void* k, const void* v, const float* 
   a.B = B; a.H = H; a.T = T; a.L = L;
   a.nch = pl.nch; a.seg_chunks = pl.seg_chunks; a.nseg = pl.nseg;
   if (nl_gains && !pl.fast) return PRISM_ERR_UNSUPPORTED;
-  st = nl_gains ? launch_fast(a, pl, ev, stream, true)
-       : dt == PRISM_BF16 ? dispatch<bf16_t>(dk, chunk, a, pl, ev, stream)
-                          : dispatch<float>(dk, chunk, a, pl, ev, stream);
+  const prism::host::LaunchShape shape{pl.P, pl.nch, pl.nseg};
+  st = pl.fast ? prism::host::launch_fast(a, shape, ev, stream, nl_gains)
+               : dispatch_generic(dt, dk, dv, chunk, a, shape, ev, stream);
   if (st != PRISM_OK || conv_out == nullptr) return st;
   // after the sweep, the only reader of conv_in, so conv_out may alias it
   if (dt == PRISM_BF16)
@@ -261,16 +226,6 @@ inline int bwd_rank_slots(int L) { return L == 1 ? 0 : L <= 4 ? 3 : 7; }
 // through LDS: one sequential forward sweep fewer.
 constexpr size_t kBwdAllStatesMax = (size_t)4 << 30;
 
-template <class E>
-bool bwd_staged(int d, int L) {
-  const int nr = L == 1 ? 1 : L <= 4 ? 3 : 7;
-#define PRISM_NB(D) (nr == 1 ? prism::bwd_stage_tokens<E, D, 1>() : nr == 3 ? prism::bwd_stage_tokens<E, D, 3>() \
-                                                                          : prism::bwd_stage_tokens<E, D, 7>())
-  const int nb = d == 16 ? PRISM_NB(16) : d == 32 ? PRISM_NB(32) : d == 64 ? PRISM_NB(64) : PRISM_NB(128);
-#undef PRISM_NB
-  return nb > 0;
-}
-
 prism_status make_bwd_plan(int B, int H, int T, int dk, int dv, int L, prism_dtype dt, BwdPlan* pl,
                            bool low_memory = false) {
   if (B <= 0 || H <= 0 || T <= 0) return PRISM_ERR_INVALID_ARG;
@@ -282,7 +237,7 @@ prism_status make_bwd_plan(int B, int H, int T, int dk, int dv, int L, prism_dty
   const size_t nblk = ((size_t)T + prism::kBwdBlock - 1) / prism::kBwdBlock;
   const size_t dd = (size_t)dk * dk * 4;
   size_t sz_all;
-  const bool staged = dt == PRISM_BF16 ? bwd_staged<bf16_t>(dk, L) : bwd_staged<float>(dk, L);
+  const bool staged = prism::host::bwd_staged(dt, dk, L);
   pl->all_states = !low_memory && staged && mul_ok(P, (size_t)T, &a) && mul_ok(a, dd, &sz_all) &&
                    sz_all <= kBwdAllStatesMax;
   if (pl->all_states) {
@@ -312,37 +267,6 @@ prism_status make_bwd_plan(int B, int H, int T, int dk, int dv, int L, prism_dty
   pl->total = align_up(pl->off_red + sz_red);
   if (pl->total < sz_ckpt) return PRISM_ERR_INVALID_ARG;
   return PRISM_OK;
-}
-
-// D / 16 workgroups per pair (16 state rows each); then, when that is more than one, the
-// fixed-order sum of their per-token partials (8 tokens per workgroup, 1-D grid).
-template <class E, int D, int NRK>
-void bwd_launch_d(const prism::BwdArgs& a, int P, hipStream_t stream) {
-  constexpr int NSP = D / 16;
-  hipLaunchKernelGGL((prism::bwd_pair_kernel<E, D, NRK>), dim3((unsigned)P * NSP), dim3(256), 0, stream, a);
-  if constexpr (NSP > 1) {
-    const unsigned nt8 = (unsigned)((a.T + 7) / 8);
-    hipLaunchKernelGGL((prism::bwd_part_reduce_kernel<D, NRK>), dim3((unsigned)P * nt8), dim3(256), 0, stream, a);
-  }
-}
-
-template <class E, int NRK>
-void bwd_launch(int d, const prism::BwdArgs& a, int P, hipStream_t stream) {
-  switch (d) {
-    case 16: bwd_launch_d<E, 16, NRK>(a, P, stream); break;
-    case 32: bwd_launch_d<E, 32, NRK>(a, P, stream); break;
-    case 64: bwd_launch_d<E, 64, NRK>(a, P, stream); break;
-    default: bwd_launch_d<E, 128, NRK>(a, P, stream); break;
-  }
-}
-
-// rank slots compiled in: 0 for L = 1, 3 for L <= 4, 7 for L <= 8
-template <class E>
-prism_status bwd_dispatch(int d, const prism::BwdArgs& a, int P, hipStream_t stream) {
-  if (a.L == 1) bwd_launch<E, 0>(d, a, P, stream);
-  else if (a.L <= 4) bwd_launch<E, 3>(d, a, P, stream);
-  else bwd_launch<E, 7>(d, a, P, stream);
-  return hipGetLastError() == hipSuccess ? PRISM_OK : PRISM_ERR_HIP;
 }
 
 }  // namespace
@@ -389,11 +313,7 @@ prism_status bwd_impl(const void* q, const void* k, const void* v, const float* 
   a.dconv_part = reinterpret_cast<float*>(ws + pl.off_part);
   a.part = reinterpret_cast<float*>(ws + pl.off_red);
   a.H = H; a.T = T; a.L = L; a.nblk = pl.nblk; a.all_states = pl.all_states ? 1 : 0;
-  st = dt == PRISM_BF16 ? bwd_dispatch<bf16_t>(dk, a, pl.P, stream) : bwd_dispatch<float>(dk, a, pl.P, stream);
-  if (st != PRISM_OK || L == 1) return st;
-  hipLaunchKernelGGL(prism::bwd_conv_reduce_kernel, dim3(H), dim3(256), 0, stream,
-                     static_cast<const float*>(a.dconv_part), dconv_w, B, H, dk);
-  return hipGetLastError() == hipSuccess ? PRISM_OK : PRISM_ERR_HIP;
+  return prism::host::launch_bwd(dt, dk, a, B, pl.P, dconv_w, stream);
 }
 
 }  // namespace
@@ -532,13 +452,19 @@ size_t prism_fwd_nl_workspace_bytes(int B, int H, int T, int dk, int dv, int L, 
   return align_up(gb) + pl.total;
 }
 
-prism_status prism_fwd_nl(const void* q, const void* k, const void* v, const float* g, const float* beta,
-                          const void* u, const float* alpha, const void* p, const float* conv_w,
-                          int B, int H, int T, int dk, int dv, int L, int chunk, prism_dtype dt,
-                          void* o, float* S_final, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// prism_fwd_nl with a segment length in chunks (0 = the planner's choice).
+prism_status fwd_nl_impl(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                         const void* u, const float* alpha, const void* p, const float* conv_w,
+                         int B, int H, int T, int dk, int dv, int L, int chunk, prism_dtype dt,
+                         void* o, float* S_final, void* workspace, size_t workspace_bytes, int seg_chunks,
+                         hipStream_t stream) {
   // every check before the first launch
   Plan pl;
-  prism_status st = make_plan(B, H, T, dk, dv, L, chunk, dt, 0, &pl);
+  prism_status st = make_plan(B, H, T, dk, dv, L, chunk, dt, seg_chunks, &pl);
   if (st != PRISM_OK) return st;
   if (!q || !k || !v || !g || !beta || !o || !S_final) return PRISM_ERR_INVALID_ARG;
   if (L > 1 && (!u || !alpha || !p || !conv_w)) return PRISM_ERR_INVALID_ARG;
@@ -550,12 +476,44 @@ prism_status prism_fwd_nl(const void* q, const void* k, const void* v, const flo
   // the bf16 d = 64 sweep evaluates the factors in its own residual chain: no factor pass
   if (pl.fast && L > 1)
     return fwd_impl(q, k, v, g, beta, u, alpha, p, conv_w, B, H, T, dk, dv, L, chunk, dt, o, S_final,
-                    ws + off, workspace_bytes - off, 0, nullptr, stream, nullptr, nullptr, nullptr, true);
+                    ws + off, workspace_bytes - off, seg_chunks, nullptr, stream, nullptr, nullptr, nullptr, true);
   void* gamma = L > 1 ? ws : nullptr;
   st = prism_nl_gain(v, alpha, p, conv_w, nullptr, B, H, T, dv, L, dt, gamma, stream);
   if (st != PRISM_OK) return st;
   return fwd_impl(q, k, v, g, beta, u, alpha, gamma, conv_w, B, H, T, dk, dv, L, chunk, dt, o, S_final,
-                  ws + off, workspace_bytes - off, 0, nullptr, stream);
+                  ws + off, workspace_bytes - off, seg_chunks, nullptr, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+prism_status prism_fwd_nl(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                          const void* u, const float* alpha, const void* p, const float* conv_w,
+                          int B, int H, int T, int dk, int dv, int L, int chunk, prism_dtype dt,
+                          void* o, float* S_final, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return fwd_nl_impl(q, k, v, g, beta, u, alpha, p, conv_w, B, H, T, dk, dv, L, chunk, dt, o, S_final,
+                     workspace, workspace_bytes, 0, stream);
+}
+
+size_t prism_fwd_nl_seg_workspace_bytes(int B, int H, int T, int dk, int dv, int L, int chunk, prism_dtype dt,
+                                        int seg_chunks) {
+  Plan pl;
+  size_t gb;
+  if (seg_chunks <= 0 || make_plan(B, H, T, dk, dv, L, chunk, dt, seg_chunks, &pl) != PRISM_OK ||
+      !nl_gamma_bytes(B, H, T, dv, L, dt, &gb))
+    return 0;
+  return align_up(gb) + pl.total;
+}
+
+prism_status prism_fwd_nl_seg(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                              const void* u, const float* alpha, const void* p, const float* conv_w,
+                              int B, int H, int T, int dk, int dv, int L, int chunk, prism_dtype dt,
+                              void* o, float* S_final, void* workspace, size_t workspace_bytes, int seg_chunks,
+                              hipStream_t stream) {
+  if (seg_chunks <= 0) return PRISM_ERR_INVALID_ARG;
+  return fwd_nl_impl(q, k, v, g, beta, u, alpha, p, conv_w, B, H, T, dk, dv, L, chunk, dt, o, S_final,
+                     workspace, workspace_bytes, seg_chunks, stream);
 }
 
 prism_status prism_nl_gain_pred(const void* v, const float* alpha, const void* W_p, const float* conv_w,

@@ -1,0 +1,57 @@
+// prism_host.h - host-side pieces shared by the translation units of libprism.
+//
+// The kernels are compiled in several translation units so that the library builds in
+// parallel: the generic forward per (I/O type, key width), the bfloat16 d = 64 fast path,
+// and the backward.  prism_api.hip validates arguments, plans the workspace and calls the
+// launch functions declared here; each launch function enqueues its kernels on the
+// stream and reports launch failures.
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include "prism.h"
+#include "prism_kernels.h"
+
+namespace prism {
+
+struct BwdArgs;
+
+namespace host {
+
+// Kernel launches of one forward: the segment sweep, the inter-segment scan and the
+// output correction over P pairs, nch chunks and nseg segments per sequence.  `ev`
+// (nullable) receives events before the sweep and after each of the three kernels.
+struct LaunchShape {
+  int P, nch, nseg;
+};
+
+inline bool record(hipEvent_t* ev, int i, hipStream_t stream) {
+  return ev == nullptr || hipEventRecord(ev[i], stream) == hipSuccess;
+}
+
+// Generic sweep (any supported dk, dv, chunk): one function per I/O type and key width.
+#define PRISM_DECL_GENERIC(NAME) \
+  prism_status NAME(int dv, int chunk, const FwdArgs& a, const LaunchShape& s, hipEvent_t* ev, hipStream_t stream);
+PRISM_DECL_GENERIC(launch_generic_bf16_dk16)
+PRISM_DECL_GENERIC(launch_generic_bf16_dk32)
+PRISM_DECL_GENERIC(launch_generic_bf16_dk64)
+PRISM_DECL_GENERIC(launch_generic_bf16_dk128)
+PRISM_DECL_GENERIC(launch_generic_f32_dk16)
+PRISM_DECL_GENERIC(launch_generic_f32_dk32)
+PRISM_DECL_GENERIC(launch_generic_f32_dk64)
+PRISM_DECL_GENERIC(launch_generic_f32_dk128)
+#undef PRISM_DECL_GENERIC
+
+// The bfloat16, dk = dv = 64, chunk 64 path (prism_sweep8.h, prism_fast.h); nl_gains:
+// a.gamma holds the gains of the nonlinear refinement.
+prism_status launch_fast(const FwdArgs& a, const LaunchShape& s, hipEvent_t* ev, hipStream_t stream,
+                         bool nl_gains);
+
+// The backward (prism_bwd.h).  bwd_staged: whether the adjoint sweep of this shape stages
+// its inputs through LDS (the all-states workspace needs it).  launch_bwd: the sweep, the
+// partial sums and, for L > 1, the batch sum of the conv-weight gradient into dconv_w.
+bool bwd_staged(prism_dtype dt, int d, int L);
+prism_status launch_bwd(prism_dtype dt, int d, const BwdArgs& a, int B, int P, float* dconv_w,
+                        hipStream_t stream);
+
+}  // namespace host
+}  // namespace prism

@@ -76,9 +76,10 @@ typedef enum { PRISM_F32 = 0, PRISM_BF16 = 1 } prism_dtype;
 
 /* Bytes of device workspace prism_fwd needs for these sizes; 0 when the
  * arguments are invalid or unsupported (prism_fwd then reports which).
- * Supported: B, H, T >= 1; dk == dv in {16, 32, 64, 128}; chunk in {16, 32, 64};
- * 1 <= L <= 8; with PRISM_F32 the chunk tiles must fit the 160 KB of LDS per CU
- * (dk = dv = 128 needs chunk <= 32, dk = dv = 64 needs chunk <= 64). */
+ * Supported: B, H, T >= 1; dk and dv each in {16, 32, 64, 128} (independently);
+ * chunk in {16, 32, 64}; 1 <= L <= 8; B * H <= 65535; the chunk tiles must fit the
+ * 160 KB of LDS per CU (with PRISM_F32, dk = dv = 128 needs chunk <= 32).  Shapes
+ * other than bfloat16 dk = dv = 64 with chunk 64 run the generic kernels. */
 size_t prism_fwd_workspace_bytes(int B, int H, int T, int dk, int dv, int L, int chunk,
                                  prism_dtype dt);
 
@@ -147,6 +148,20 @@ prism_status prism_fwd_seg(const void* q, const void* k, const void* v,
                            void* o, float* S_final,
                            void* workspace, size_t workspace_bytes, int seg_chunks,
                            hipStream_t stream);
+
+/* Same as prism_fwd_nl (below) with an explicit segment length in chunks (>= 1), as
+ * prism_fwd_seg is to prism_fwd; used to test that independence for the nonlinear sweep.
+ * Workspace: prism_fwd_nl_seg_workspace_bytes (0 for invalid arguments). */
+size_t prism_fwd_nl_seg_workspace_bytes(int B, int H, int T, int dk, int dv, int L, int chunk,
+                                        prism_dtype dt, int seg_chunks);
+prism_status prism_fwd_nl_seg(const void* q, const void* k, const void* v,
+                              const float* g, const float* beta,
+                              const void* u, const float* alpha, const void* p,
+                              const float* conv_w,
+                              int B, int H, int T, int dk, int dv, int L, int chunk, prism_dtype dt,
+                              void* o, float* S_final,
+                              void* workspace, size_t workspace_bytes, int seg_chunks,
+                              hipStream_t stream);
 
 /* Same as prism_fwd, and records four caller-created events on `stream` around
  * the launches: events[0] before the segment sweep kernel, events[1] after it,

@@ -42,13 +42,33 @@ def test_workspace_bytes_valid_and_invalid(lib):
     assert f(0, 1, 64, 16, 16, 1, 16, 0) == 0          # B <= 0
     assert f(1, 1, 0, 16, 16, 1, 16, 0) == 0           # T <= 0
     assert f(1, 1, 64, 48, 48, 1, 16, 0) == 0          # unsupported head dim
-    assert f(1, 1, 64, 64, 32, 1, 16, 0) == 0          # dk != dv
+    assert f(1, 1, 64, 64, 32, 1, 16, 0) > 0           # dk != dv (generic kernels)
+    assert f(1, 1, 64, 64, 48, 1, 16, 0) == 0          # unsupported value width
     assert f(1, 1, 64, 16, 16, 1, 8, 0) == 0           # chunk not in {16, 32, 64}
     assert f(1, 1, 64, 16, 16, 9, 16, 0) == 0          # L > 8
     assert f(1, 1, 64, 16, 16, 0, 16, 0) == 0          # L < 1
     assert f(1, 1, 64, 16, 16, 1, 16, 7) == 0          # unknown dtype
     assert f(1, 1, 64, 128, 128, 2, 64, 0) == 0        # fp32 tiles exceed LDS
     assert f(1 << 20, 1 << 12, 1 << 20, 128, 128, 8, 64, 1) == 0   # size overflow
+
+
+# every (dk, dv) pair of the supported widths has a kernel at some chunk size; the pairs the
+# GPU parity tests run (tests/test_parity_gpu.py, UNEQUAL) all have one
+@pytest.mark.parametrize("dt", [0, 1])
+@pytest.mark.parametrize("dk", [16, 32, 64, 128])
+@pytest.mark.parametrize("dv", [16, 32, 64, 128])
+def test_workspace_every_width_pair(lib, dt, dk, dv):
+    f = lib.prism_fwd_workspace_bytes
+    assert max(f(1, 2, 300, dk, dv, 3, c, dt) for c in (16, 32, 64)) > 0
+    assert f(1, 2, 300, dk, dv, 3, 16, dt) > 0
+
+
+def test_workspace_unequal_parity_cases(lib):
+    from tests.test_parity_gpu import UNEQUAL
+    for dt, dk, dv, chunk, L in UNEQUAL:
+        code = 1 if dt == "bf16" else 0
+        assert lib.prism_fwd_workspace_bytes(1, 2, 4 * chunk + 7, dk, dv, L, chunk, code) > 0, (dt, dk, dv, chunk)
+        assert lib.prism_fwd_seg_workspace_bytes(1, 2, 4 * chunk + 7, dk, dv, L, chunk, code, 2) > 0
 
 
 def test_workspace_grows_with_segments(lib):
@@ -240,7 +260,11 @@ def test_fwd_nl_workspace(lib):
     # the factors (64 tokens x 2 slots x 16 channels of bf16) in front of the forward's workspace
     assert f(1, 1, 64, 16, 16, 3, 16, 1) == 4096 + base
     assert f(1, 1, 64, 16, 16, 1, 16, 1) == lib.prism_fwd_workspace_bytes(1, 1, 64, 16, 16, 1, 16, 1)
-    assert f(1, 1, 64, 16, 32, 3, 16, 1) == 0
+    assert f(1, 1, 64, 16, 32, 3, 16, 1) > 0           # dk != dv: factor pass + generic forward
+    assert f(1, 1, 64, 16, 48, 3, 16, 1) == 0
+    g = lib.prism_fwd_nl_seg_workspace_bytes
+    assert g(1, 2, 600, 64, 64, 4, 64, 1, 2) > g(1, 2, 600, 64, 64, 4, 64, 1, 10) > 0
+    assert g(1, 2, 600, 64, 64, 4, 64, 1, 0) == 0
     need = f(1, 1, 64, 16, 16, 2, 16, 1)
     assert _fwd_nl_call(lib, null=("ws",)) == WORKSPACE
     assert _fwd_nl_call(lib, ws_bytes=need - 1) == WORKSPACE
@@ -282,3 +306,4 @@ def test_fwd_nl_pred_checks(lib):
     assert call(dt=0) == UNSUPPORTED
     assert call(null=("ws",)) == WORKSPACE
     assert call(ws=lib.prism_fwd_nl_workspace_bytes(1, 1, 64, 64, 64, 3, 64, 1) - 1) == WORKSPACE
+

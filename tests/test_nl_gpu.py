@@ -262,3 +262,44 @@ def test_nl_decode_steps(prism, key):
     eo, es = rel_err(o, ref_o), rel_err(S.cpu().numpy(), ref_S)
     log(f"  rel err o {eo:.3e}  S_final {es:.3e}")
     assert eo <= TOL[w.dtype] and es <= TOL[w.dtype]
+
+
+@pytest.mark.parametrize("seg", [2, 3])
+@pytest.mark.parametrize("L", [2, 3, 4, 8])
+def test_nl_sweep_multichunk_segments(prism, L, seg):
+    """The nonlinear d = 64 sweep with segments of several chunks (state, segment operator
+    and rank-input slots carried from chunk to chunk) against the token-by-token oracle."""
+    import torch
+    w = workloads.Workload("nl_seg", "bf16", B=1, H=2, T=450, dk=64, dv=64, L=L, chunk=64, seed=150 + L)
+    x = _inputs(w)
+    log(f"[nl fwd] L={L} seg={seg} T={w.T}")
+    d = _dev(x, w)
+    o, S = prism.fwd_nl(d["q"], d["k"], d["v"], d["g"], d["beta"], d["u"], d["alpha"], d["p"], d["conv_w"],
+                        L=w.L, chunk=w.chunk, seg_chunks=seg)
+    torch.cuda.synchronize()
+    ref_o, ref_S = onl.forward_nl(x["q"], x["k"], x["v"], x["g"], x["beta"], x["u"], x["alpha"], x["p"],
+                                  x["conv_w"], w.L)
+    eo, es = rel_err(o.float().cpu().numpy(), ref_o), rel_err(S.cpu().numpy(), ref_S)
+    log(f"  rel err o {eo:.3e}  S_final {es:.3e} (tol {TOL[w.dtype]:.0e})")
+    assert eo <= TOL[w.dtype] and es <= TOL[w.dtype]
+
+
+def test_nl_full_size_16k_against_oracle(prism):
+    """The fused nonlinear forward at the 16K workload (B2 H4 T16384 d64 L4, planner's
+    segments of 8 chunks) against the token-by-token oracle on head 1 (both batches)."""
+    import torch
+    w = workloads.workload("rec16k_bf16")
+    x = _inputs(w)
+    log("[nl 16k] fused forward vs oracle, head 1")
+    d = _dev(x, w)
+    o, S = prism.fwd_nl(d["q"], d["k"], d["v"], d["g"], d["beta"], d["u"], d["alpha"], d["p"], d["conv_w"],
+                        L=w.L, chunk=w.chunk)
+    torch.cuda.synchronize()
+    o = o.float().cpu().numpy()
+    S = S.cpu().numpy()
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(S))
+    ref_o, ref_S = onl.forward_nl(x["q"], x["k"], x["v"], x["g"], x["beta"], x["u"], x["alpha"], x["p"],
+                                  x["conv_w"], w.L, heads=[1])
+    eo, es = rel_err(o[:, [1]], ref_o), rel_err(S[:, [1]], ref_S)
+    log(f"  rel err o {eo:.3e}  S_final {es:.3e} (tol {TOL[w.dtype]:.0e})")
+    assert eo <= TOL[w.dtype] and es <= TOL[w.dtype]

@@ -174,3 +174,72 @@ def test_bf16_d64_generic_chunk32_matches(prism):
     w = workloads.Workload("gen32", "bf16", B=1, H=2, T=300, dk=64, dv=64, L=4, chunk=32, seed=95)
     x = workloads.generate(w)
     check(w, run_gpu(prism, w, x), run_oracle(w, x), " generic chunk=32")
+
+
+# ---- segments spanning several chunks on every path -------------------------------------
+# A segment of more than one chunk carries the state H and the segment operator A_acc from
+# chunk to chunk inside one workgroup, and (on the bf16 d = 64 sweep) prefetches the next
+# chunk at an L-dependent rank step and rotates the two rank-input slots across chunks.  The
+# planner gives small problems one chunk per segment, so these cases force longer segments.
+
+@pytest.mark.parametrize("seg", [2, 4])
+@pytest.mark.parametrize("L", [1, 2, 3, 4, 5, 8])
+def test_fast_sweep_multichunk_segments(prism, L, seg):
+    w = workloads.Workload("fastseg", "bf16", B=1, H=2, T=600, dk=64, dv=64, L=L, chunk=64, seed=100 + L)
+    x = workloads.generate(w)
+    log(f"[parity] fast sweep L={L} seg={seg} T={w.T}")
+    check(w, run_gpu(prism, w, x, seg=seg), run_oracle(w, x), f" L={L} seg={seg}")
+
+
+GENERIC_SEG = [
+    # (dtype, d, chunk, L)
+    ("f32", 16, 16, 3), ("f32", 32, 32, 4), ("f32", 64, 32, 2), ("f32", 64, 64, 5),
+    ("bf16", 16, 16, 3), ("bf16", 32, 32, 8), ("bf16", 64, 32, 4), ("bf16", 128, 64, 4),
+]
+
+
+@pytest.mark.parametrize("seg", [2, 3])
+@pytest.mark.parametrize("case", GENERIC_SEG, ids=lambda c: f"{c[0]}_d{c[1]}_c{c[2]}_L{c[3]}")
+def test_generic_multichunk_segments(prism, case, seg):
+    dt, d, chunk, L = case
+    T = 6 * chunk + chunk // 2 + 3       # ragged last chunk
+    w = workloads.Workload("genseg", dt, B=2, H=1, T=T, dk=d, dv=d, L=L, chunk=chunk, seed=110 + d + L)
+    x = workloads.generate(w)
+    log(f"[parity] generic {case} seg={seg} T={T}")
+    check(w, run_gpu(prism, w, x, seg=seg), run_oracle(w, x), f" {case} seg={seg}")
+
+
+# dk != dv (generic kernels): every key width meets every value width
+UNEQUAL = [
+    # (dtype, dk, dv, chunk, L)
+    ("bf16", 64, 128, 64, 4), ("bf16", 128, 64, 64, 3), ("bf16", 32, 64, 32, 2), ("bf16", 16, 128, 16, 5),
+    ("bf16", 128, 32, 32, 1), ("f32", 64, 32, 32, 3), ("f32", 32, 64, 64, 4), ("f32", 16, 32, 16, 2),
+    ("f32", 128, 16, 16, 3),
+]
+
+
+@pytest.mark.parametrize("case", UNEQUAL, ids=lambda c: f"{c[0]}_dk{c[1]}_dv{c[2]}_c{c[3]}_L{c[4]}")
+def test_unequal_key_value_widths(prism, case):
+    dt, dk, dv, chunk, L = case
+    T = 4 * chunk + 7
+    w = workloads.Workload("unequal", dt, B=1, H=2, T=T, dk=dk, dv=dv, L=L, chunk=chunk, seed=130 + dk + dv + L)
+    x = workloads.generate(w)
+    log(f"[parity] dk={dk} dv={dv} {dt} chunk={chunk} L={L}")
+    check(w, run_gpu(prism, w, x), run_oracle(w, x), f" dk={dk} dv={dv}")
+    check(w, run_gpu(prism, w, x, seg=2), run_oracle(w, x), f" dk={dk} dv={dv} seg=2")
+
+
+@pytest.mark.parametrize("L", [1, 2, 8])
+def test_lsweep_shape_against_oracle(prism, L):
+    """The L-sweep runs the 16K workload's shape (B2 H4 T16384 d64, chunk 64) at other L,
+    in the planner's launch configuration (32 segments of 8 chunks per pair); heads 0 and 3
+    are compared with the oracle, every head checked for finiteness."""
+    w = workloads.workload("rec16k_bf16").replace(L=L, seed=140 + L)
+    x = workloads.generate(w)
+    log(f"[parity] L-sweep shape L={L}: gpu")
+    got = run_gpu(prism, w, x)
+    assert np.all(np.isfinite(got[0])) and np.all(np.isfinite(got[1]))
+    heads = [0, 3]
+    log(f"[parity] L-sweep shape L={L}: oracle heads={heads}")
+    ref = run_oracle(w, x, heads)
+    check(w, (got[0][:, heads], got[1][:, heads]), ref, f" L={L}")
