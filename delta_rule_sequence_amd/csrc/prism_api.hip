@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "prism.h"
@@ -562,6 +563,58 @@ prism_status prism_fwd_nl_pred(const void* q, const void* k, const void* v, cons
   if (st != PRISM_OK) return st;
   return fwd_impl(q, k, v, g, beta, u, alpha, gamma, conv_w, B, H, T, dk, dv, L, chunk, dt, o, S_final,
                   ws + off, workspace_bytes - off, 0, nullptr, stream);
+}
+
+}  // extern "C"
+
+// ---- the forward without a caller workspace -------------------------------------------------
+// The workspace of prism_fwd_noalloc: a file-scope device array, one copy per GPU, held
+// until the process ends.  Host code never passes the array's name to a kernel (on the host
+// it is only a stand-in for the symbol): it uses the device address that
+// hipGetSymbolAddress returns for the current device, looked up once per device.
+static __device__ __align__(256) unsigned char scratch[PRISM_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` per device (null: not looked up)
+
+// The device address of the current device's copy of `scratch`, or null on a HIP error.
+void* scratch_ptr() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t prism_noalloc_scratch_bytes(void) { return PRISM_NOALLOC_SCRATCH_BYTES; }
+
+prism_status prism_fwd_noalloc(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                               const void* u, const float* alpha, const void* gamma, const float* conv_w,
+                               int B, int H, int T, int dk, int dv, int L, int chunk, prism_dtype dt,
+                               void* o, float* S_final, hipStream_t stream) {
+  Plan pl;
+  prism_status st = make_plan(B, H, T, dk, dv, L, chunk, dt, 0, &pl);
+  if (st != PRISM_OK) return st;
+  if (!q || !k || !v || !g || !beta || !o || !S_final) return PRISM_ERR_INVALID_ARG;
+  if (L > 1 && (!u || !alpha || !gamma || !conv_w)) return PRISM_ERR_INVALID_ARG;
+  if (pl.total > (size_t)PRISM_NOALLOC_SCRATCH_BYTES) return PRISM_ERR_WORKSPACE;
+  void* ws = scratch_ptr();
+  if (ws == nullptr) return PRISM_ERR_HIP;
+  // every region of the workspace is written before it is read within one call, so the
+  // previous call's contents need no clearing
+  return fwd_impl(q, k, v, g, beta, u, alpha, gamma, conv_w, B, H, T, dk, dv, L, chunk, dt, o, S_final,
+                  ws, (size_t)PRISM_NOALLOC_SCRATCH_BYTES, 0, nullptr, stream);
 }
 
 const char* prism_status_string(prism_status s) {

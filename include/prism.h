@@ -289,6 +289,25 @@ prism_status prism_fwd_nl_pred(const void* q, const void* k, const void* v,
                                void* o, float* S_final,
                                void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* The forward for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): prism_fwd without the
+ * workspace arguments.  Its workspace is a static device array of
+ * PRISM_NOALLOC_SCRATCH_BYTES bytes inside the library, one copy per GPU, held until the
+ * process ends; the call allocates nothing (the first call on a device looks up that
+ * device's copy).  Shapes whose prism_fwd_workspace_bytes exceed the array return
+ * PRISM_ERR_WORKSPACE before anything is enqueued (the 16K workload, B = 2, H = 4,
+ * T = 16384, d = 64, L = 4 in bfloat16, needs about 44 MB).  Every call on one GPU shares
+ * that GPU's array: calls that overlap on one GPU (other streams, other threads) race and
+ * must be serialised by the caller.  Arguments, results and other errors as prism_fwd. */
+#define PRISM_NOALLOC_SCRATCH_BYTES (64u << 20)
+size_t prism_noalloc_scratch_bytes(void);
+prism_status prism_fwd_noalloc(const void* q, const void* k, const void* v,
+                               const float* g, const float* beta,
+                               const void* u, const float* alpha, const void* gamma,
+                               const float* conv_w,
+                               int B, int H, int T, int dk, int dv, int L, int chunk, prism_dtype dt,
+                               void* o, float* S_final, hipStream_t stream);
+
 /* A static, human-readable name of a status code. */
 const char* prism_status_string(prism_status s);
 

@@ -307,3 +307,18 @@ def test_fwd_nl_pred_checks(lib):
     assert call(null=("ws",)) == WORKSPACE
     assert call(ws=lib.prism_fwd_nl_workspace_bytes(1, 1, 64, 64, 64, 3, 64, 1) - 1) == WORKSPACE
 
+
+def test_noalloc_rejects_shapes_beyond_its_array(lib):
+    """prism_fwd_noalloc checks the forward's workspace against its static array on the
+    host and returns PRISM_ERR_WORKSPACE before looking up the array or launching."""
+    cap = lib.prism_noalloc_scratch_bytes()
+    assert cap == 64 << 20
+    assert lib.prism_fwd_workspace_bytes(2, 4, 16384, 64, 64, 4, 64, 1) <= cap
+    assert lib.prism_fwd_workspace_bytes(1, 8, 65536, 128, 128, 8, 64, 1) > cap
+    f = lib.prism_fwd_noalloc
+    f.argtypes = [ctypes.c_void_p] * 9 + [ctypes.c_int] * 8 + [ctypes.c_void_p] * 3
+    f.restype = ctypes.c_int
+    p = ctypes.c_void_p(1)
+    assert f(*[p] * 9, 1, 8, 65536, 128, 128, 8, 64, 1, p, p, None) == WORKSPACE
+    assert f(*[p] * 9, 1, 8, 64, 48, 48, 8, 64, 1, p, p, None) == UNSUPPORTED
+    assert f(*[p] * 9, 0, 8, 64, 64, 64, 8, 64, 1, p, p, None) == INVALID
