@@ -10,7 +10,10 @@ and runs the residual chain one refinement step at a time.  See
 ``oracle.prism`` for the definitions and the passages each one follows,
 ``oracle.prism_grad`` for the float64 gradients of the same forward, and
 ``oracle.prism_nl`` for the nonlinear refinement variant (the GELU of the
-gain-modulated residual in the chain) and its absorbed per-channel factors.
+gain-modulated residual in the chain) and its absorbed per-channel factors, and
+``oracle.prism_delta`` for the written-correction form (each layer writes its
+GELU correction along its own key with its own gate) and the predictor front end
+(gains, keys and gates from the anchor).
 """
 from .prism import (shortconv_anchor, residual_chain, token_step, forward,
                     forward_pairs, conv_tail, decode_step)
