@@ -80,6 +80,26 @@ def load_library() -> ctypes.CDLL:
     lib.prism_fwd_nl_seg.restype = ctypes.c_int
     lib.prism_fwd_nl_seg_workspace_bytes.argtypes = [i] * 9
     lib.prism_fwd_nl_seg_workspace_bytes.restype = sz
+    lib.prism_delta_gain.argtypes = [vp, vp, fp, vp, i, i, i, i, i, i, vp, vp]
+    lib.prism_delta_gain.restype = ctypes.c_int
+    lib.prism_fwd_delta.argtypes = fwd_args + [vp]
+    lib.prism_fwd_delta.restype = ctypes.c_int
+    lib.prism_fwd_delta_seg.argtypes = fwd_args + [i, vp]
+    lib.prism_fwd_delta_seg.restype = ctypes.c_int
+    lib.prism_fwd_delta_workspace_bytes.argtypes = [i] * 8
+    lib.prism_fwd_delta_workspace_bytes.restype = sz
+    lib.prism_fwd_delta_seg_workspace_bytes.argtypes = [i] * 9
+    lib.prism_fwd_delta_seg_workspace_bytes.restype = sz
+    lib.prism_anchor_predict.argtypes = [vp, fp, vp, vp, vp, vp] + [i] * 7 + [vp, vp, fp, vp]
+    lib.prism_anchor_predict.restype = ctypes.c_int
+    lib.prism_fwd_delta_pred.argtypes = [vp, vp, vp, fp, fp, vp, vp, vp, fp] + [i] * 8 + [vp, fp, vp, sz, vp]
+    lib.prism_fwd_delta_pred.restype = ctypes.c_int
+    lib.prism_fwd_delta_pred_workspace_bytes.argtypes = [i] * 8
+    lib.prism_fwd_delta_pred_workspace_bytes.restype = sz
+    lib.prism_fwd_noalloc.argtypes = fwd_args[:19] + [vp]
+    lib.prism_fwd_noalloc.restype = ctypes.c_int
+    lib.prism_noalloc_scratch_bytes.argtypes = []
+    lib.prism_noalloc_scratch_bytes.restype = sz
     lib.prism_status_string.argtypes = [ctypes.c_int]
     lib.prism_status_string.restype = ctypes.c_char_p
     lib.prism_version.argtypes = []
@@ -480,4 +500,125 @@ def fwd_nl_pred(q, k, v, g, beta, u=None, alpha=None, W_p=None, conv_w=None, L: 
                                ctypes.c_void_p(workspace.data_ptr()), workspace.numel(), ctypes.c_void_p(s))
     if st != 0:
         raise PrismError(f"prism_fwd_nl_pred failed: {status_string(st)}")
+    return o, S
+
+
+# ---- the written-correction form (each layer writes its GELU correction) ----------------------
+def delta_gain(v, p, conv_w, L: int, conv_in=None, stream=None):
+    """f = delta_gain(v, p, conv_w, L, conv_in): the per-channel factors of the written
+    corrections, GELU(p r) = f r along the chain r <- r - f r; [B,H,T,L-1,dv] in the dtype of
+    v.  v [B,H,T,dv]; p [B,H,T,L-1,dv] (dtype of v); conv_w [H,4,dv] float32; conv_in
+    [B,H,3,dv] optional.  None when L == 1."""
+    import torch
+    lib = load_library()
+    B, H, T, dv = v.shape
+    dev = v.device
+    if dev.type != "cuda":
+        raise PrismError("inputs must be on a GPU")
+    if L == 1:
+        return None
+    shapes = {"p": (B, H, T, L - 1, dv), "conv_w": (H, 4, dv), "conv_in": (B, H, 3, dv)}
+    _check([("v", v), ("p", p)] + ([("conv_in", conv_in)] if conv_in is not None else []),
+           [("conv_w", conv_w)], shapes, v.dtype, dev)
+    fac = torch.empty((B, H, T, L - 1, dv), dtype=v.dtype, device=dev)
+    s = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
+    st = lib.prism_delta_gain(_ptr(v), _ptr(p), _ptr(conv_w), _ptr(conv_in), B, H, T, dv, L, _dtype_code(v),
+                              _ptr(fac), ctypes.c_void_p(s))
+    if st != 0:
+        raise PrismError(f"prism_delta_gain failed: {status_string(st)}")
+    return fac
+
+
+def fwd_delta(q, k, v, g, beta, u=None, alpha=None, p=None, conv_w=None, L: int = 1, chunk: int = 64,
+              out: Optional[Tuple] = None, workspace=None, stream=None, seg_chunks: Optional[int] = None):
+    """o, S_final = fwd_delta(q, k, v, g, beta, u, alpha, p, conv_w, L, chunk): the forward of the
+    written-correction form (layer l writes alpha_l GELU(p_{l-1} r_{l-1}) along u_l), gains p
+    [B,H,T,L-1,dv] in place of gamma (see fwd).  seg_chunks: explicit segment length."""
+    import torch
+    lib = load_library()
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    dt = _dtype_code(q)
+    dev = q.device
+    if dev.type != "cuda":
+        raise PrismError("inputs must be on a GPU")
+    vec = [("q", q), ("k", k), ("v", v)] + ([("u", u), ("p", p)] if L > 1 else [])
+    flt = [("g", g), ("beta", beta)] + ([("alpha", alpha), ("conv_w", conv_w)] if L > 1 else [])
+    shapes = {"k": (B, H, T, dk), "v": (B, H, T, dv), "g": (B, H, T), "beta": (B, H, T),
+              "u": (B, H, T, L - 1, dk), "p": (B, H, T, L - 1, dv), "alpha": (B, H, T, L),
+              "conv_w": (H, 4, dv)}
+    _check(vec, flt, shapes, q.dtype, dev)
+    o, S = _outputs(out, B, H, T, dk, dv, q.dtype, dev)
+    if seg_chunks is None:
+        need = lib.prism_fwd_delta_workspace_bytes(B, H, T, dk, dv, L, chunk, dt)
+    else:
+        need = lib.prism_fwd_delta_seg_workspace_bytes(B, H, T, dk, dv, L, chunk, dt, seg_chunks)
+    workspace = _workspace(workspace, need, dev)
+    s = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
+    args = [_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+            _ptr(u) if L > 1 else None, _ptr(alpha) if L > 1 else None,
+            _ptr(p) if L > 1 else None, _ptr(conv_w) if L > 1 else None,
+            B, H, T, dk, dv, L, chunk, dt, _ptr(o), _ptr(S),
+            ctypes.c_void_p(workspace.data_ptr()), workspace.numel()]
+    if seg_chunks is None:
+        st = lib.prism_fwd_delta(*args, ctypes.c_void_p(s))
+    else:
+        st = lib.prism_fwd_delta_seg(*args, seg_chunks, ctypes.c_void_p(s))
+    if st != 0:
+        raise PrismError(f"prism_fwd_delta failed: {status_string(st)}")
+    return o, S
+
+
+def anchor_predict(v, conv_w, W_p, W_k, W_b, L: int, conv_in=None, stream=None):
+    """f, u, alpha = anchor_predict(v, conv_w, W_p, W_k, W_b, L, conv_in): the predictor front end
+    of the written-correction form: correction factors [B,H,T,L-1,dv] and unit keys
+    [B,H,T,L-1,dk] (bfloat16) and gates [B,H,T,L] (float32), from the anchor through
+    W_p [H,L-1,dv,dv], W_k [H,L-1,dk,dv], W_b [H,L,dv] (bfloat16)."""
+    import torch
+    lib = load_library()
+    B, H, T, dv = v.shape
+    dk = W_k.shape[2]
+    dev = v.device
+    if dev.type != "cuda":
+        raise PrismError("inputs must be on a GPU")
+    shapes = {"W_p": (H, L - 1, dv, dv), "W_k": (H, L - 1, dk, dv), "W_b": (H, L, dv), "conv_w": (H, 4, dv),
+              "conv_in": (B, H, 3, dv)}
+    _check([("v", v), ("W_p", W_p), ("W_k", W_k), ("W_b", W_b)] +
+           ([("conv_in", conv_in)] if conv_in is not None else []), [("conv_w", conv_w)], shapes, v.dtype, dev)
+    fac = torch.empty((B, H, T, L - 1, dv), dtype=v.dtype, device=dev)
+    uk = torch.empty((B, H, T, L - 1, dk), dtype=v.dtype, device=dev)
+    al = torch.empty((B, H, T, L), dtype=torch.float32, device=dev)
+    s = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
+    st = lib.prism_anchor_predict(_ptr(v), _ptr(conv_w), _ptr(W_p), _ptr(W_k), _ptr(W_b), _ptr(conv_in),
+                                  B, H, T, dk, dv, L, _dtype_code(v), _ptr(fac), _ptr(uk), _ptr(al),
+                                  ctypes.c_void_p(s))
+    if st != 0:
+        raise PrismError(f"prism_anchor_predict failed: {status_string(st)}")
+    return fac, uk, al
+
+
+def fwd_delta_pred(q, k, v, g, beta, W_p, W_k, W_b, conv_w, L: int, chunk: int = 64,
+                   out: Optional[Tuple] = None, workspace=None, stream=None):
+    """o, S_final = fwd_delta_pred(q, k, v, g, beta, W_p, W_k, W_b, conv_w, L, chunk): the
+    written-correction forward with gains, keys and gates predicted from the anchor."""
+    import torch
+    lib = load_library()
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    dt = _dtype_code(q)
+    dev = q.device
+    if dev.type != "cuda":
+        raise PrismError("inputs must be on a GPU")
+    shapes = {"k": (B, H, T, dk), "v": (B, H, T, dv), "g": (B, H, T), "beta": (B, H, T),
+              "W_p": (H, L - 1, dv, dv), "W_k": (H, L - 1, dk, dv), "W_b": (H, L, dv), "conv_w": (H, 4, dv)}
+    _check([("q", q), ("k", k), ("v", v), ("W_p", W_p), ("W_k", W_k), ("W_b", W_b)],
+           [("g", g), ("beta", beta), ("conv_w", conv_w)], shapes, q.dtype, dev)
+    o, S = _outputs(out, B, H, T, dk, dv, q.dtype, dev)
+    workspace = _workspace(workspace, lib.prism_fwd_delta_pred_workspace_bytes(B, H, T, dk, dv, L, chunk, dt), dev)
+    s = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
+    st = lib.prism_fwd_delta_pred(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(W_p), _ptr(W_k),
+                                  _ptr(W_b), _ptr(conv_w), B, H, T, dk, dv, L, chunk, dt, _ptr(o), _ptr(S),
+                                  ctypes.c_void_p(workspace.data_ptr()), workspace.numel(), ctypes.c_void_p(s))
+    if st != 0:
+        raise PrismError(f"prism_fwd_delta_pred failed: {status_string(st)}")
     return o, S

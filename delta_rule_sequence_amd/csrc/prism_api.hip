@@ -19,6 +19,7 @@ namespace {
 
 using prism::bf16_t;
 using prism::FwdArgs;
+using prism::host::ChainForm;
 
 constexpr size_t kAlign = 256;
 constexpr size_t kCUs = 256;                // compute units of an MI355X
@@ -167,7 +168,7 @@ prism_status fwd_impl(const void* q, const void* k, const void* v, const float* 
                       void* o, float* S_final, void* workspace, size_t workspace_bytes,
                       int seg_chunks, hipEvent_t* ev, hipStream_t stream,
                       const float* S0 = nullptr, const void* conv_in = nullptr, void* conv_out = nullptr,
-                      bool nl_gains = false) {
+                      ChainForm form = ChainForm::kLinear) {
   Plan pl;
   prism_status st = make_plan(B, H, T, dk, dv, L, chunk, dt, seg_chunks, &pl);
   if (st != PRISM_OK) return st;
@@ -187,9 +188,10 @@ prism_status fwd_impl(const void* q, const void* k, const void* v, const float* 
   a.Hin = reinterpret_cast<float*>(ws + pl.off_hin);
   a.B = B; a.H = H; a.T = T; a.L = L;
   a.nch = pl.nch; a.seg_chunks = pl.seg_chunks; a.nseg = pl.nseg;
-  if (nl_gains && !pl.fast) return PRISM_ERR_UNSUPPORTED;
+  a.chain_delta = form == ChainForm::kDelta ? 1 : 0;
+  if (form == ChainForm::kGelu && !pl.fast) return PRISM_ERR_UNSUPPORTED;
   const prism::host::LaunchShape shape{pl.P, pl.nch, pl.nseg};
-  st = pl.fast ? prism::host::launch_fast(a, shape, ev, stream, nl_gains)
+  st = pl.fast ? prism::host::launch_fast(a, shape, ev, stream, L > 1 ? form : ChainForm::kLinear)
                : dispatch_generic(dt, dk, dv, chunk, a, shape, ev, stream);
   if (st != PRISM_OK || conv_out == nullptr) return st;
   // after the sweep, the only reader of conv_in, so conv_out may alias it
@@ -420,14 +422,19 @@ static bool nl_gamma_bytes(int B, int H, int T, int dv, int L, prism_dtype dt, s
   return mul_ok(pt, (size_t)(L - 1) * dv * (dt == PRISM_BF16 ? 2 : 4), out);
 }
 
-prism_status prism_nl_gain(const void* v, const float* alpha, const void* p, const float* conv_w,
-                           const void* conv_in, int B, int H, int T, int dv, int L, prism_dtype dt,
-                           void* gamma, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// The chain-factor pass: linear chain (alpha read) or written corrections (delta).
+prism_status gain_impl(const void* v, const float* alpha, const void* p, const float* conv_w,
+                       const void* conv_in, int B, int H, int T, int dv, int L, prism_dtype dt,
+                       void* gamma, bool delta, hipStream_t stream) {
   if (B <= 0 || H <= 0 || T <= 0) return PRISM_ERR_INVALID_ARG;
   if (dt != PRISM_F32 && dt != PRISM_BF16) return PRISM_ERR_INVALID_ARG;
   if (L < 1 || L > 8 || !valid_dim(dv)) return PRISM_ERR_UNSUPPORTED;
   if (L == 1) return PRISM_OK;
-  if (!v || !alpha || !p || !conv_w || !gamma) return PRISM_ERR_INVALID_ARG;
+  if (!v || (!delta && !alpha) || !p || !conv_w || !gamma) return PRISM_ERR_INVALID_ARG;
   size_t P, bytes;
   if (!mul_ok((size_t)B, (size_t)H, &P) || !nl_gamma_bytes(B, H, T, dv, L, dt, &bytes)) return PRISM_ERR_INVALID_ARG;
   if (P > 65535) return PRISM_ERR_UNSUPPORTED;  // (b, h) pairs map to grid.y, as in the forward
@@ -438,11 +445,23 @@ prism_status prism_nl_gain(const void* v, const float* alpha, const void* p, con
   prism::NlArgs a;
   a.v = v; a.alpha = alpha; a.p = p; a.conv_w = conv_w; a.conv_in = conv_in; a.gamma = gamma;
   a.H = H; a.T = T; a.L = L; a.dv = dv; a.lognc = lognc;
-  if (dt == PRISM_BF16)
-    hipLaunchKernelGGL((prism::nl_gain_kernel<bf16_t>), grid, dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL((prism::nl_gain_kernel<float>), grid, dim3(256), 0, stream, a);
-  return hipGetLastError() == hipSuccess ? PRISM_OK : PRISM_ERR_HIP;
+  return prism::host::launch_gain(a, dt, grid, delta, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+prism_status prism_nl_gain(const void* v, const float* alpha, const void* p, const float* conv_w,
+                           const void* conv_in, int B, int H, int T, int dv, int L, prism_dtype dt,
+                           void* gamma, hipStream_t stream) {
+  return gain_impl(v, alpha, p, conv_w, conv_in, B, H, T, dv, L, dt, gamma, false, stream);
+}
+
+prism_status prism_delta_gain(const void* v, const void* p, const float* conv_w, const void* conv_in,
+                              int B, int H, int T, int dv, int L, prism_dtype dt, void* gamma,
+                              hipStream_t stream) {
+  return gain_impl(v, nullptr, p, conv_w, conv_in, B, H, T, dv, L, dt, gamma, true, stream);
 }
 
 size_t prism_fwd_nl_workspace_bytes(int B, int H, int T, int dk, int dv, int L, int chunk, prism_dtype dt) {
@@ -477,7 +496,8 @@ prism_status fwd_nl_impl(const void* q, const void* k, const void* v, const floa
   // the bf16 d = 64 sweep evaluates the factors in its own residual chain: no factor pass
   if (pl.fast && L > 1)
     return fwd_impl(q, k, v, g, beta, u, alpha, p, conv_w, B, H, T, dk, dv, L, chunk, dt, o, S_final,
-                    ws + off, workspace_bytes - off, seg_chunks, nullptr, stream, nullptr, nullptr, nullptr, true);
+                    ws + off, workspace_bytes - off, seg_chunks, nullptr, stream, nullptr, nullptr, nullptr,
+                    ChainForm::kGelu);
   void* gamma = L > 1 ? ws : nullptr;
   st = prism_nl_gain(v, alpha, p, conv_w, nullptr, B, H, T, dv, L, dt, gamma, stream);
   if (st != PRISM_OK) return st;
@@ -531,15 +551,10 @@ prism_status prism_nl_gain_pred(const void* v, const float* alpha, const void* W
   if (P > 65535) return PRISM_ERR_UNSUPPORTED;
   const size_t wg_tokens = dv == 64 ? 256 : 64;  // 4 waves x 16 tokens x tiles per wave
   const dim3 grid((unsigned)(((size_t)T + wg_tokens - 1) / wg_tokens), (unsigned)P);
-  prism::NlPredArgs a;
+  prism::NlPredArgs a = {};
   a.v = v; a.alpha = alpha; a.W_p = W_p; a.conv_w = conv_w; a.conv_in = conv_in; a.gamma = gamma;
   a.H = H; a.T = T; a.L = L;
-  switch (dv) {
-    case 32: hipLaunchKernelGGL((prism::nl_pred_gain_kernel<32>), grid, dim3(256), 0, stream, a); break;
-    case 64: hipLaunchKernelGGL((prism::nl_pred_gain_kernel<64>), grid, dim3(256), 0, stream, a); break;
-    default: hipLaunchKernelGGL((prism::nl_pred_gain_kernel<128>), grid, dim3(256), 0, stream, a); break;
-  }
-  return hipGetLastError() == hipSuccess ? PRISM_OK : PRISM_ERR_HIP;
+  return prism::host::launch_pred(a, dv, grid, false, stream);
 }
 
 prism_status prism_fwd_nl_pred(const void* q, const void* k, const void* v, const float* g, const float* beta,
@@ -563,6 +578,154 @@ prism_status prism_fwd_nl_pred(const void* q, const void* k, const void* v, cons
   if (st != PRISM_OK) return st;
   return fwd_impl(q, k, v, g, beta, u, alpha, gamma, conv_w, B, H, T, dk, dv, L, chunk, dt, o, S_final,
                   ws + off, workspace_bytes - off, 0, nullptr, stream);
+}
+
+// ---- the written-correction form -------------------------------------------------------------
+
+size_t prism_fwd_delta_seg_workspace_bytes(int B, int H, int T, int dk, int dv, int L, int chunk, prism_dtype dt,
+                                           int seg_chunks) {
+  Plan pl;
+  size_t gb;
+  if (seg_chunks < 0 || make_plan(B, H, T, dk, dv, L, chunk, dt, seg_chunks, &pl) != PRISM_OK ||
+      !nl_gamma_bytes(B, H, T, dv, L, dt, &gb))
+    return 0;
+  return align_up(gb) + pl.total;
+}
+
+size_t prism_fwd_delta_workspace_bytes(int B, int H, int T, int dk, int dv, int L, int chunk, prism_dtype dt) {
+  return prism_fwd_delta_seg_workspace_bytes(B, H, T, dk, dv, L, chunk, dt, 0);
+}
+
+}  // extern "C"
+
+namespace {
+
+prism_status fwd_delta_impl(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                            const void* u, const float* alpha, const void* p, const float* conv_w,
+                            int B, int H, int T, int dk, int dv, int L, int chunk, prism_dtype dt,
+                            void* o, float* S_final, void* workspace, size_t workspace_bytes, int seg_chunks,
+                            hipStream_t stream) {
+  Plan pl;
+  prism_status st = make_plan(B, H, T, dk, dv, L, chunk, dt, seg_chunks, &pl);
+  if (st != PRISM_OK) return st;
+  if (!q || !k || !v || !g || !beta || !o || !S_final) return PRISM_ERR_INVALID_ARG;
+  if (L > 1 && (!u || !alpha || !p || !conv_w)) return PRISM_ERR_INVALID_ARG;
+  size_t gb;
+  if (!nl_gamma_bytes(B, H, T, dv, L, dt, &gb)) return PRISM_ERR_INVALID_ARG;
+  const size_t off = align_up(gb);
+  if (!workspace || workspace_bytes < off + pl.total) return PRISM_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  void* fac = L > 1 ? ws : nullptr;
+  st = prism_delta_gain(v, p, conv_w, nullptr, B, H, T, dv, L, dt, fac, stream);
+  if (st != PRISM_OK) return st;
+  return fwd_impl(q, k, v, g, beta, u, alpha, fac, conv_w, B, H, T, dk, dv, L, chunk, dt, o, S_final,
+                  ws + off, workspace_bytes - off, seg_chunks, nullptr, stream, nullptr, nullptr, nullptr,
+                  ChainForm::kDelta);
+}
+
+}  // namespace
+
+extern "C" {
+
+prism_status prism_fwd_delta(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                             const void* u, const float* alpha, const void* p, const float* conv_w,
+                             int B, int H, int T, int dk, int dv, int L, int chunk, prism_dtype dt,
+                             void* o, float* S_final, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream) {
+  return fwd_delta_impl(q, k, v, g, beta, u, alpha, p, conv_w, B, H, T, dk, dv, L, chunk, dt, o, S_final,
+                        workspace, workspace_bytes, 0, stream);
+}
+
+prism_status prism_fwd_delta_seg(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                                 const void* u, const float* alpha, const void* p, const float* conv_w,
+                                 int B, int H, int T, int dk, int dv, int L, int chunk, prism_dtype dt,
+                                 void* o, float* S_final, void* workspace, size_t workspace_bytes,
+                                 int seg_chunks, hipStream_t stream) {
+  if (seg_chunks <= 0) return PRISM_ERR_INVALID_ARG;
+  return fwd_delta_impl(q, k, v, g, beta, u, alpha, p, conv_w, B, H, T, dk, dv, L, chunk, dt, o, S_final,
+                        workspace, workspace_bytes, seg_chunks, stream);
+}
+
+prism_status prism_anchor_predict(const void* v, const float* conv_w, const void* W_p, const void* W_k,
+                                  const void* W_b, const void* conv_in, int B, int H, int T, int dk, int dv,
+                                  int L, prism_dtype dt, void* gamma, void* u, float* alpha, hipStream_t stream) {
+  if (B <= 0 || H <= 0 || T <= 0) return PRISM_ERR_INVALID_ARG;
+  if (dt != PRISM_F32 && dt != PRISM_BF16) return PRISM_ERR_INVALID_ARG;
+  if (L < 2 || L > 8) return PRISM_ERR_UNSUPPORTED;
+  if (dt != PRISM_BF16 || dk != dv || !(dv == 32 || dv == 64 || dv == 128)) return PRISM_ERR_UNSUPPORTED;
+  if (!v || !conv_w || !W_p || !W_k || !W_b || !gamma || !u || !alpha) return PRISM_ERR_INVALID_ARG;
+  size_t P, bytes;
+  if (!mul_ok((size_t)B, (size_t)H, &P) || !nl_gamma_bytes(B, H, T, dv, L, dt, &bytes)) return PRISM_ERR_INVALID_ARG;
+  if (P > 65535) return PRISM_ERR_UNSUPPORTED;
+  const size_t wg_tokens = dv == 64 ? 256 : 64;  // 4 waves x 16 tokens x tiles per wave
+  const dim3 grid((unsigned)(((size_t)T + wg_tokens - 1) / wg_tokens), (unsigned)P);
+  prism::NlPredArgs a = {};
+  a.v = v; a.W_p = W_p; a.conv_w = conv_w; a.conv_in = conv_in; a.gamma = gamma;
+  a.W_k = W_k; a.W_b = W_b; a.u = u; a.alpha_out = alpha;
+  a.H = H; a.T = T; a.L = L;
+  return prism::host::launch_pred(a, dv, grid, true, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Front-end outputs in the workspace of prism_fwd_delta_pred: factors, keys, gates, then
+// the forward's own workspace.
+struct PredLayout {
+  size_t off_u, off_alpha, off_fwd, total;
+};
+
+bool pred_layout(int B, int H, int T, int dk, int dv, int L, prism_dtype dt, size_t fwd_bytes, PredLayout* ly) {
+  size_t gb, ub, ab, P, pt;
+  if (!nl_gamma_bytes(B, H, T, dv, L, dt, &gb) || !nl_gamma_bytes(B, H, T, dk, L, dt, &ub)) return false;
+  if (!mul_ok((size_t)B, (size_t)H, &P) || !mul_ok(P, (size_t)T, &pt) || !mul_ok(pt, (size_t)L * 4, &ab))
+    return false;
+  ly->off_u = align_up(gb);
+  ly->off_alpha = align_up(ly->off_u + ub);
+  ly->off_fwd = align_up(ly->off_alpha + ab);
+  ly->total = ly->off_fwd + fwd_bytes;
+  return ly->total >= fwd_bytes;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t prism_fwd_delta_pred_workspace_bytes(int B, int H, int T, int dk, int dv, int L, int chunk, prism_dtype dt) {
+  Plan pl;
+  PredLayout ly;
+  if (L < 2 || dt != PRISM_BF16 || dk != dv || !(dv == 32 || dv == 64 || dv == 128)) return 0;
+  if (make_plan(B, H, T, dk, dv, L, chunk, dt, 0, &pl) != PRISM_OK ||
+      !pred_layout(B, H, T, dk, dv, L, dt, pl.total, &ly))
+    return 0;
+  return ly.total;
+}
+
+prism_status prism_fwd_delta_pred(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                                  const void* W_p, const void* W_k, const void* W_b, const float* conv_w,
+                                  int B, int H, int T, int dk, int dv, int L, int chunk, prism_dtype dt,
+                                  void* o, float* S_final, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream) {
+  Plan pl;
+  prism_status st = make_plan(B, H, T, dk, dv, L, chunk, dt, 0, &pl);
+  if (st != PRISM_OK) return st;
+  if (L < 2) return PRISM_ERR_UNSUPPORTED;  // nothing to predict: prism_fwd
+  if (dt != PRISM_BF16 || dk != dv || !(dv == 32 || dv == 64 || dv == 128)) return PRISM_ERR_UNSUPPORTED;
+  if (!q || !k || !v || !g || !beta || !o || !S_final || !W_p || !W_k || !W_b || !conv_w)
+    return PRISM_ERR_INVALID_ARG;
+  PredLayout ly;
+  if (!pred_layout(B, H, T, dk, dv, L, dt, pl.total, &ly)) return PRISM_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < ly.total) return PRISM_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  void* fac = ws;
+  void* uk = ws + ly.off_u;
+  float* gates = reinterpret_cast<float*>(ws + ly.off_alpha);
+  st = prism_anchor_predict(v, conv_w, W_p, W_k, W_b, nullptr, B, H, T, dk, dv, L, dt, fac, uk, gates, stream);
+  if (st != PRISM_OK) return st;
+  return fwd_impl(q, k, v, g, beta, uk, gates, fac, conv_w, B, H, T, dk, dv, L, chunk, dt, o, S_final,
+                  ws + ly.off_fwd, workspace_bytes - ly.off_fwd, 0, nullptr, stream, nullptr, nullptr, nullptr,
+                  ChainForm::kDelta);
 }
 
 }  // extern "C"

@@ -14,6 +14,8 @@
 namespace prism {
 
 struct BwdArgs;
+struct NlArgs;
+struct NlPredArgs;
 
 namespace host {
 
@@ -41,10 +43,19 @@ PRISM_DECL_GENERIC(launch_generic_f32_dk64)
 PRISM_DECL_GENERIC(launch_generic_f32_dk128)
 #undef PRISM_DECL_GENERIC
 
-// The bfloat16, dk = dv = 64, chunk 64 path (prism_sweep8.h, prism_fast.h); nl_gains:
-// a.gamma holds the gains of the nonlinear refinement.
+// The residual chain a forward runs.  kLinear: factors gamma, r <- r (1 - alpha gamma),
+// written alpha r.  kGelu: gains in gamma's place, each factor p Phi(p r) formed on the way
+// (d = 64 sweep only).  kDelta: factors of the written corrections, d = gamma r,
+// r <- r - d, written alpha d (FwdArgs::chain_delta = 1).
+enum class ChainForm { kLinear, kGelu, kDelta };
+
+// The bfloat16, dk = dv = 64, chunk 64 path (prism_sweep8.h, prism_fast.h): the segment
+// sweep of the chain form (fwd_fast_*.hip), the scan and the output correction.
 prism_status launch_fast(const FwdArgs& a, const LaunchShape& s, hipEvent_t* ev, hipStream_t stream,
-                         bool nl_gains);
+                         ChainForm form);
+void launch_sweep8_linear(const FwdArgs& a, dim3 grid, hipStream_t stream);
+void launch_sweep8_nl(const FwdArgs& a, dim3 grid, hipStream_t stream);
+void launch_sweep8_delta(const FwdArgs& a, dim3 grid, hipStream_t stream);
 
 // The backward (prism_bwd.h).  bwd_staged: whether the adjoint sweep of this shape stages
 // its inputs through LDS (the all-states workspace needs it).  launch_bwd: the sweep, the
@@ -52,6 +63,13 @@ prism_status launch_fast(const FwdArgs& a, const LaunchShape& s, hipEvent_t* ev,
 bool bwd_staged(prism_dtype dt, int d, int L);
 prism_status launch_bwd(prism_dtype dt, int d, const BwdArgs& a, int B, int P, float* dconv_w,
                         hipStream_t stream);
+
+// Nonlinear refinement (prism_nl.h, nl.hip).  launch_gain: the chain factors from given
+// gains, for the linear chain or (delta) the written corrections.  launch_pred: the factors
+// from gains predicted on the anchor (linear chain), or with front the written-correction
+// front end (factors, unit keys and gates).
+prism_status launch_gain(const NlArgs& a, prism_dtype dt, dim3 grid, bool delta, hipStream_t stream);
+prism_status launch_pred(const NlPredArgs& a, int dv, dim3 grid, bool front, hipStream_t stream);
 
 }  // namespace host
 }  // namespace prism

@@ -54,6 +54,10 @@ struct FwdArgs {
   int nch;          // chunks per sequence
   int seg_chunks;   // chunks per segment
   int nseg;         // segments per sequence
+  // residual chain: 0 = r_l = r_{l-1} (1 - alpha_{l-1} gamma_{l-1}), written alpha_l r_l;
+  // 1 = written corrections: d_l = gamma_{l-1} r_{l-1}, r_l = r_{l-1} - d_l, written
+  // alpha_l d_l (gamma then holds per-channel factors of the corrections)
+  int chain_delta;
 };
 
 // LDS plan of seg_local (bytes).  Row strides are padded by 16 bytes.
@@ -279,9 +283,15 @@ __global__ __launch_bounds__(256, 1) void seg_local_kernel(FwdArgs a) {
               const int t = 16 * mt + g4 + r;
               if (t < nvalid) {
                 const float gm = to_f(gam[((size_t)(t0 + t) * Lm1 + (lr - 1)) * DV + col]);
-                const float x = Rr[jv][mt][r] * (1.f - sAlpha[t * 8 + lr - 1] * gm);
-                Rr[jv][mt][r] = x;
-                rv[r] = sAlpha[t * 8 + lr] * x;
+                if (a.chain_delta) {  // the correction itself is written and subtracted
+                  const float d = gm * Rr[jv][mt][r];
+                  Rr[jv][mt][r] -= d;
+                  rv[r] = sAlpha[t * 8 + lr] * d;
+                } else {
+                  const float x = Rr[jv][mt][r] * (1.f - sAlpha[t * 8 + lr - 1] * gm);
+                  Rr[jv][mt][r] = x;
+                  rv[r] = sAlpha[t * 8 + lr] * x;
+                }
               }
             }
           }

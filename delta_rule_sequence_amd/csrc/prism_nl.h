@@ -69,8 +69,10 @@ template <> struct Vec4<bf16_t> {
 
 __device__ __forceinline__ float f4get(const float4& x, int i) { return i == 0 ? x.x : i == 1 ? x.y : i == 2 ? x.z : x.w; }
 
-// grid (ceil(T * dv / 4 / 256), P): 32-bit indexing inside a pair, no division
-template <class E>
+// grid (ceil(T * dv / 4 / 256), P): 32-bit indexing inside a pair, no division.
+// DLT: the written-correction chain (notes, section 2.3: the correction GELU(p r) is
+// subtracted as it is and written): r <- r - f r with the rounded factor f, alpha unread.
+template <class E, bool DLT>
 __global__ __launch_bounds__(256) void nl_gain_kernel(NlArgs a) {
   const unsigned j = blockIdx.x * 256u + threadIdx.x;
   const int L = a.L, Lm1 = L - 1, dv = a.dv;
@@ -103,12 +105,12 @@ __global__ __launch_bounds__(256) void nl_gain_kernel(NlArgs a) {
   for (int c = 0; c < 4; ++c)
     r[c] = f4get(x[3], c) - (f4get(w0, c) * f4get(x[0], c) + f4get(w1, c) * f4get(x[1], c) +
                              f4get(w2, c) * f4get(x[2], c) + f4get(w3, c) * f4get(x[3], c));
-  const float* al = a.alpha + (size_t)pt * L;
+  const float* al = DLT ? nullptr : a.alpha + (size_t)pt * L;
   const E* pg = reinterpret_cast<const E*>(a.p) + (size_t)pt * Lm1 * dv + c4;
   E* gm = reinterpret_cast<E*>(a.gamma) + (size_t)pt * Lm1 * dv + c4;
   for (int l = 0; l < Lm1; ++l) {
     const float4 pv = Vec4<E>::load(pg + (size_t)l * dv);
-    const float at = al[l];
+    const float at = DLT ? 1.f : al[l];
     float f[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
@@ -118,7 +120,14 @@ __global__ __launch_bounds__(256) void nl_gain_kernel(NlArgs a) {
     Vec4<E>::store(gm + (size_t)l * dv, make_float4(f[0], f[1], f[2], f[3]));
     // move on with the stored (rounded) factor, as the forward's chain will
 #pragma unroll
-    for (int c = 0; c < 4; ++c) r[c] = r[c] * (1.f - at * to_f(from_f<E>(f[c])));
+    for (int c = 0; c < 4; ++c) {
+      if constexpr (DLT) {
+        const float d = to_f(from_f<E>(f[c])) * r[c];
+        r[c] -= d;
+      } else {
+        r[c] = r[c] * (1.f - at * to_f(from_f<E>(f[c])));
+      }
+    }
   }
 }
 
@@ -140,11 +149,16 @@ __global__ __launch_bounds__(256) void nl_gain_kernel(NlArgs a) {
 // every 16 tokens (46-51 us, whatever the LDS layout or occupancy).
 struct NlPredArgs {
   const void* v;        // [P][T][D] bf16
-  const float* alpha;   // [P][T][L]
+  const float* alpha;   // [P][T][L] (the linear chain's step sizes; unread by the front end)
   const void* W_p;      // [H][L-1][D][D] bf16
   const float* conv_w;  // [H][4][D]
   const void* conv_in;  // [P][3][D] bf16, or null
   void* gamma;          // out [P][T][L-1][D] bf16
+  // the front end only: key and gate predictors and their outputs
+  const void* W_k;      // [H][L-1][D][D] bf16 ((out, in): key channel, anchor channel)
+  const void* W_b;      // [H][L][D] bf16
+  void* u;              // out [P][T][L-1][D] bf16: unit keys
+  float* alpha_out;     // out [P][T][L]: gates
   int H, T, L;
 };
 
@@ -172,10 +186,17 @@ __device__ __forceinline__ void bf_store(bf16_t* p, const bf16_t (&x)[N]) {
 // Wave w of a workgroup takes TPW consecutive 16-token tiles (TPW = 4 for d = 64, so each
 // level's W_p fragments are loaded once for 64 tokens: the weights' cache traffic is a
 // quarter of one tile per wave; 243 VGPRs, two waves per SIMD, no spills).
-template <int D>
+//
+// DLT: the written-correction chain, r <- r - f r (notes, section 2.3: greedy residual
+// subtraction without a step size).  FRONT (with DLT): the whole predictor front end of
+// the notes' Phase 1 from the same anchor operands: per level the keys W_k[h, l] anchor,
+// normalised over their channels (a 16-lane sum of squares), and once per tile the gates
+// sigmoid(W_b[h, l] . anchor) for l < L as one more MFMA tile (output column l = gate l).
+template <int D, bool DLT, bool FRONT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 2 : 1)))
 void nl_pred_gain_kernel(NlPredArgs a) {
   static_assert(D == 32 || D == 64 || D == 128, "32-deep MFMA contraction over the channels");
+  static_assert(!FRONT || DLT, "the front end feeds the written-correction chain");
   constexpr int TPW = D == 64 ? 4 : 1;
   constexpr int ROWS = 16 * TPW + 3;  // a wave's value window
   constexpr int LDV = D + 8;          // LDS row stride (bf16)
@@ -199,10 +220,12 @@ void nl_pred_gain_kernel(NlPredArgs a) {
       x = *reinterpret_cast<const uint4*>(ci + (size_t)(s + 3) * D + cv);
     *reinterpret_cast<uint4*>(sv + rr * LDV + cv) = x;
   }
-  const float* al = a.alpha + (size_t)pr * T * L;
-  for (int i = l; i < 16 * TPW * L; i += 64) {
-    const int tok = tw + i / L;
-    sA[w][i] = tok < T ? al[(size_t)tok * L + i % L] : 0.f;
+  if constexpr (!DLT) {
+    const float* al = a.alpha + (size_t)pr * T * L;
+    for (int i = l; i < 16 * TPW * L; i += 64) {
+      const int tok = tw + i / L;
+      sA[w][i] = tok < T ? al[(size_t)tok * L + i % L] : 0.f;
+    }
   }
   __syncthreads();
   const float* cw = a.conv_w + (size_t)hd * 4 * D;
@@ -279,10 +302,83 @@ void nl_pred_gain_kernel(NlPredArgs a) {
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const int tl = 16 * j + 4 * g + rr, tok = tw + tl;
-        const float at = sA[w][tl * L + lv];
+        if constexpr (DLT) {
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) r[j][rr][nt] = r[j][rr][nt] * (1.f - at * (float)fb[rr][nt]);
+          for (int nt = 0; nt < NT; ++nt) {
+            const float d = (float)fb[rr][nt] * r[j][rr][nt];
+            r[j][rr][nt] -= d;
+          }
+        } else {
+          const float at = sA[w][tl * L + lv];
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) r[j][rr][nt] = r[j][rr][nt] * (1.f - at * (float)fb[rr][nt]);
+        }
         if (tok < T) bf_store<NT>(gout + ((size_t)tok * Lm1 + lv) * D + cl, fb[rr]);
+      }
+    }
+    if constexpr (FRONT) {
+      // keys u_{t, lv+1} = W_k[h, lv] anchor_t / |W_k[h, lv] anchor_t|, tokens 16 j + 4 g + rr,
+      // channels NT li ..: the weight fragments take wf's registers
+      const bf16_t* Wkl = reinterpret_cast<const bf16_t*>(a.W_k) + ((size_t)hd * Lm1 + lv) * D * D;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+          wf[nt][kb] = *reinterpret_cast<const bf16x8*>(Wkl + (size_t)(cl + nt) * D + 32 * kb + 8 * g);
+      bf16_t* uout = reinterpret_cast<bf16_t*>(a.u) + (size_t)pr * T * Lm1 * D;
+#pragma unroll
+      for (int j = 0; j < TPW; ++j) {
+        float kv[4][NT], ss[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          f32x4 acc = zero4();
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb) acc = mfma(an[j][kb], wf[nt][kb], acc);
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            kv[rr][nt] = acc[rr];
+            ss[rr] += acc[rr] * acc[rr];
+          }
+        }
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          // a token's channels sit in the 16 lanes of its lane group g
+#pragma unroll
+          for (int m = 1; m < 16; m <<= 1) ss[rr] += __shfl_xor(ss[rr], m, 16);
+          const float inv = 1.f / sqrtf(ss[rr]);
+          const int tok = tw + 16 * j + 4 * g + rr;
+          bf16_t kb16[NT];
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) kb16[nt] = (bf16_t)(kv[rr][nt] * inv);
+          if (tok < T) bf_store<NT>(uout + ((size_t)tok * Lm1 + lv) * D + cl, kb16);
+        }
+      }
+    }
+  }
+  if constexpr (FRONT) {
+    // gates alpha_{t, l} = sigmoid(W_b[h, l] . anchor_t): B operand row li = W_b[h, li]
+    // (zero for li >= L), so lane (li, g) ends with gate li of tokens 16 j + 4 g + rr
+    const bf16_t* Wb = reinterpret_cast<const bf16_t*>(a.W_b) + (size_t)hd * L * D;
+    bf16x8 bfr[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      if (li < L) {
+        bfr[kb] = *reinterpret_cast<const bf16x8*>(Wb + (size_t)li * D + 32 * kb + 8 * g);
+      } else {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) bfr[kb][q] = (bf16_t)0.f;
+      }
+    }
+    float* aout = a.alpha_out + (size_t)pr * T * L;
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) {
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) acc = mfma(an[j][kb], bfr[kb], acc);
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int tok = tw + 16 * j + 4 * g + rr;
+        if (li < L && tok < T) aout[(size_t)tok * L + li] = 1.f / (1.f + __expf(-acc[rr]));
       }
     }
   }

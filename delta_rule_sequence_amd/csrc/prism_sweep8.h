@@ -508,7 +508,9 @@ __device__ __forceinline__ void sweep8_kwave(const Sweep8Ctx& x, int wq) {
 // ---- the Q waves ------------------------------------------------------------------------
 // NLG: the chain's factor slots hold gains p and each factor is p Phi(p r) of the running
 // residual, rounded to bfloat16 (the nonlinear refinement, as nl_gain_kernel computes it).
-template <int LM1S, bool NLG>
+// DLT: the written-correction chain (d = gamma r, r <- r - d, written alpha d; the factor
+// slots hold the corrections' per-channel factors) in place of r <- r (1 - alpha gamma).
+template <int LM1S, bool NLG, bool DLT>
 __device__ __forceinline__ void sweep8_qwave(const Sweep8Ctx& x, int wq) {
   constexpr int LD = Sweep8Lds::LD, LDT = Sweep8Lds::LDT, C = 64;
   const Sweep8View V(x.smem);
@@ -589,9 +591,15 @@ __device__ __forceinline__ void sweep8_qwave(const Sweep8Ctx& x, int wq) {
       for (int cc = 0; cc < 4; ++cc) {
         float gm = (float)gv[cc];
         if constexpr (NLG) gm = (float)(bf16_t)(gm * std_normal_cdf(gm * rr[r][cc]));
-        const float xr = rr[r][cc] * (1.f - apr[r] * gm);
-        rr[r][cc] = xr;
-        R[r][cc] = awr[r] * xr;
+        if constexpr (DLT) {
+          const float d = gm * rr[r][cc];
+          rr[r][cc] -= d;
+          R[r][cc] = awr[r] * d;
+        } else {
+          const float xr = rr[r][cc] * (1.f - apr[r] * gm);
+          rr[r][cc] = xr;
+          R[r][cc] = awr[r] * xr;
+        }
       }
     }
     bf16_t* dst = V.slotRt(s);
@@ -772,7 +780,7 @@ __device__ __forceinline__ void sweep8_qwave(const Sweep8Ctx& x, int wq) {
     for (int r = 0; r < 4; ++r) x.agg[(16 * kt + g4 + r) * 64 + 16 * cb + li] = A[kt][r];
 }
 
-template <int D, int C, int LM1S, bool NLG>
+template <int D, int C, int LM1S, bool NLG, bool DLT>
 __device__ __forceinline__ void sweep8_run(FwdArgs a) {
   static_assert(D == 64 && C == 64, "the two-wave sweep is written for head dim 64 and 64-token chunks");
   __shared__ __align__(16) unsigned char smem[Sweep8Lds::total];
@@ -828,18 +836,24 @@ __device__ __forceinline__ void sweep8_run(FwdArgs a) {
   // Both roles pass the same barriers in the same order: B0, B1, one per phase
   // P1 .. P_NL and one after the state phase, for every chunk of the segment.
   if (w < 4) sweep8_kwave<LM1S>(x, w);
-  else sweep8_qwave<LM1S, NLG>(x, w - 4);
+  else sweep8_qwave<LM1S, NLG, DLT>(x, w - 4);
 }
 
 template <int D, int C, int LM1S>
 __global__ __launch_bounds__(512, 1) void seg_sweep8_kernel(FwdArgs a) {
-  sweep8_run<D, C, LM1S, false>(a);
+  sweep8_run<D, C, LM1S, false, false>(a);
 }
 
 // the same sweep with the nonlinear refinement: a.gamma holds the gains p
 template <int D, int C, int LM1S>
 __global__ __launch_bounds__(512, 1) void seg_sweep8_nl_kernel(FwdArgs a) {
-  sweep8_run<D, C, LM1S, true>(a);
+  sweep8_run<D, C, LM1S, true, false>(a);
+}
+
+// the same sweep with the written-correction chain: a.gamma holds the corrections' factors
+template <int D, int C, int LM1S>
+__global__ __launch_bounds__(512, 1) void seg_sweep8_delta_kernel(FwdArgs a) {
+  sweep8_run<D, C, LM1S, false, true>(a);
 }
 
 }  // namespace prism

@@ -289,6 +289,79 @@ prism_status prism_fwd_nl_pred(const void* q, const void* k, const void* v,
                                void* o, float* S_final,
                                void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* The written-correction form of the refinement ("PRISM" reading notes, section 2.2: rank
+ * accumulation, every refinement layer adds its correction along its own basis with its own
+ * gate; section 2.3: greedy residual subtraction, the correction is a GELU of the
+ * gain-modulated residual and is subtracted from the residual as it is).  With the GDN
+ * forgetting and the GDN write of prism_fwd as the first component:
+ *   r_{t,0}     = v_t - anchor_t
+ *   delta_{t,l} = GELU(p_{t,l-1} * r_{t,l-1}),   r_{t,l} = r_{t,l-1} - delta_{t,l},  l = 1..L-1
+ *   B_t         = beta_t v_t k_t^T + sum_{l=1}^{L-1} alpha_{t,l} delta_{t,l} u_{t,l}^T
+ * alpha_{t,l} is layer l's gate (alpha_{t,0} is not read); p [B, H, T, L-1, dv] (dtype dt,
+ * slot j holds p_{t,j}) takes gamma's place.  The exact erf GELU, as prism_nl_gain.
+ *
+ * prism_delta_gain writes the corrections' per-channel factors f = p Phi(p r) along this
+ * chain (delta = f r), gamma's layout, each rounded to dt before the chain continues with it
+ * (r <- r - f r); no alpha.  conv_in as prism_nl_gain.  For L == 1 nothing is enqueued.
+ *
+ * prism_fwd_delta runs that factor pass into the front of the workspace, then the forward
+ * with the written-correction chain (on the bfloat16 d = 64, chunk 64 path its own sweep
+ * instantiation).  Arguments as prism_fwd with p in gamma's place; workspace
+ * prism_fwd_delta_workspace_bytes.  prism_fwd_delta_seg: the same with an explicit segment
+ * length in chunks (as prism_fwd_seg).  Supported shapes as prism_fwd. */
+prism_status prism_delta_gain(const void* v, const void* p, const float* conv_w, const void* conv_in,
+                              int B, int H, int T, int dv, int L, prism_dtype dt, void* gamma,
+                              hipStream_t stream);
+size_t prism_fwd_delta_workspace_bytes(int B, int H, int T, int dk, int dv, int L, int chunk,
+                                       prism_dtype dt);
+prism_status prism_fwd_delta(const void* q, const void* k, const void* v,
+                             const float* g, const float* beta,
+                             const void* u, const float* alpha, const void* p,
+                             const float* conv_w,
+                             int B, int H, int T, int dk, int dv, int L, int chunk, prism_dtype dt,
+                             void* o, float* S_final,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+size_t prism_fwd_delta_seg_workspace_bytes(int B, int H, int T, int dk, int dv, int L, int chunk,
+                                           prism_dtype dt, int seg_chunks);
+prism_status prism_fwd_delta_seg(const void* q, const void* k, const void* v,
+                                 const float* g, const float* beta,
+                                 const void* u, const float* alpha, const void* p,
+                                 const float* conv_w,
+                                 int B, int H, int T, int dk, int dv, int L, int chunk, prism_dtype dt,
+                                 void* o, float* S_final,
+                                 void* workspace, size_t workspace_bytes, int seg_chunks,
+                                 hipStream_t stream);
+
+/* The predictor front end of the written-correction form ("PRISM" reading notes, section
+ * 2.3, Phase 1: predictors on the ShortConv anchor emit each layer's gain, basis and gate):
+ *   p_{t,l}     = W_p[h, l] anchor_t                            l = 0..L-2 (never written)
+ *   u_{t,l+1}   = W_k[h, l] anchor_t / |W_k[h, l] anchor_t|     l = 0..L-2 (unit keys)
+ *   alpha_{t,l} = sigmoid(W_b[h, l] . anchor_t)                 l = 0..L-1 (gates)
+ * and the correction factors of prism_delta_gain from those gains, in one pass on MFMA
+ * (the anchor rounded to bfloat16 as the A operand, float32 sums).
+ *   W_p [H, L-1, dv, dv], W_k [H, L-1, dk, dv] ((out, in) layouts), W_b [H, L, dv]: bfloat16
+ *   outputs gamma [B, H, T, L-1, dv] and u [B, H, T, L-1, dk] bfloat16, alpha [B, H, T, L]
+ *   float32 (the layouts prism_fwd reads).
+ * Supported: dt = PRISM_BF16, dk == dv in {32, 64, 128}, 2 <= L <= 8, B * H <= 65535.
+ *
+ * prism_fwd_delta_pred: the front end into the workspace, then the written-correction
+ * forward with the predicted keys, gates and factors; q, k, v, g, beta and conv_w as
+ * prism_fwd.  Workspace: prism_fwd_delta_pred_workspace_bytes.  Supported as
+ * prism_anchor_predict. */
+prism_status prism_anchor_predict(const void* v, const float* conv_w, const void* W_p, const void* W_k,
+                                  const void* W_b, const void* conv_in,
+                                  int B, int H, int T, int dk, int dv, int L, prism_dtype dt,
+                                  void* gamma, void* u, float* alpha, hipStream_t stream);
+size_t prism_fwd_delta_pred_workspace_bytes(int B, int H, int T, int dk, int dv, int L, int chunk,
+                                            prism_dtype dt);
+prism_status prism_fwd_delta_pred(const void* q, const void* k, const void* v,
+                                  const float* g, const float* beta,
+                                  const void* W_p, const void* W_k, const void* W_b,
+                                  const float* conv_w,
+                                  int B, int H, int T, int dk, int dv, int L, int chunk, prism_dtype dt,
+                                  void* o, float* S_final,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* The forward for callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): prism_fwd without the
  * workspace arguments.  Its workspace is a static device array of

@@ -107,12 +107,16 @@ def forward_delta(q, k, v, g, beta, u, alpha, p, conv_w, L: int,
             np.ascontiguousarray(S.transpose(0, 2, 1)).reshape(B, Hs, dk, dv))
 
 
-def delta_factors(v, p, conv_w, L: int, conv_in=None) -> np.ndarray:
+def delta_factors(v, p, conv_w, L: int, conv_in=None, rounding=None) -> np.ndarray:
     """Per-channel factors f with f_{t,l} * r_{t,l} = delta_{t,l+1} = GELU(p_{t,l} * r_{t,l})
     along the chain (the GELU absorbed into scaling coefficients, as the Tencent Ads
     article, section 03-三, does for the linear chain), so that the chain becomes
     r <- r - f * r with written values alpha * f * r.  Where r is exactly zero the limit
-    p / 2.  Returns [B, H, T, L-1, dv], float64."""
+    p / 2.  Returns [B, H, T, L-1, dv], float64.
+
+    rounding: optional element-wise map applied to each factor before the chain continues
+    with it (a storage type's rounding: factors handed to a forward in that type are
+    defined on the residuals that forward will see)."""
     v = np.asarray(v, F64)
     B, H, T, dv = v.shape
     p = np.asarray(p, F64)
@@ -125,8 +129,11 @@ def delta_factors(v, p, conv_w, L: int, conv_in=None) -> np.ndarray:
         for l in range(1, L):
             z = gelu(p[:, :, t, l - 1] * r)
             safe = np.where(r == 0.0, 1.0, r)
-            fac[:, :, t, l - 1] = np.where(r == 0.0, 0.5 * p[:, :, t, l - 1], z / safe)
-            r = r - z
+            f = np.where(r == 0.0, 0.5 * p[:, :, t, l - 1], z / safe)
+            if rounding is not None:
+                f = np.asarray(rounding(f), F64)
+            fac[:, :, t, l - 1] = f
+            r = r - f * r
     return fac
 
 
@@ -166,12 +173,14 @@ def forward_delta_factors(q, k, v, g, beta, u, alpha, fac, conv_w, L: int, heads
             np.ascontiguousarray(S.transpose(0, 2, 1)).reshape(B, Hs, dk, dv))
 
 
-def anchor_predict(v, conv_w, W_p, W_k, W_b, L: int, conv_in=None):
+def anchor_predict(v, conv_w, W_p, W_k, W_b, L: int, conv_in=None, anchor_rounding=None):
     """The predictor front end ([Notes §2.3]): gains, unit keys and gates from the anchor.
 
     v: [B, H, T, dv]; conv_w: [H, 4, dv]; W_p: [H, L-1, dv, dv]; W_k: [H, L-1, dk, dv];
     W_b: [H, L, dv]; conv_in: optional [B, H, 3, dv].
     Returns p [B, H, T, L-1, dv], u [B, H, T, L-1, dk], alpha [B, H, T, L], float64.
+    anchor_rounding: optional element-wise map applied to the anchor before the
+    projections (a storage type for the projections' operand).
     """
     v = np.asarray(v, F64)
     B, H, T, dv = v.shape
@@ -185,6 +194,8 @@ def anchor_predict(v, conv_w, W_p, W_k, W_b, L: int, conv_in=None):
     alpha = np.zeros((B, H, T, L), F64)
     for t in range(T):
         anc = shortconv_anchor(v_ext, w[None], t + 3)                  # [B, H, dv]
+        if anchor_rounding is not None:
+            anc = np.asarray(anchor_rounding(anc), F64)
         for l in range(L - 1):
             p[:, :, t, l] = np.einsum("hoi,bhi->bho", Wp[:, l], anc)
             key = np.einsum("hoi,bhi->bho", Wk[:, l], anc)

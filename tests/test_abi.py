@@ -322,3 +322,34 @@ def test_noalloc_rejects_shapes_beyond_its_array(lib):
     assert f(*[p] * 9, 1, 8, 65536, 128, 128, 8, 64, 1, p, p, None) == WORKSPACE
     assert f(*[p] * 9, 1, 8, 64, 48, 48, 8, 64, 1, p, p, None) == UNSUPPORTED
     assert f(*[p] * 9, 0, 8, 64, 64, 64, 8, 64, 1, p, p, None) == INVALID
+
+
+def test_delta_form_workspace_and_checks(lib):
+    f = lib.prism_fwd_delta_workspace_bytes
+    assert f(1, 1, 64, 16, 16, 3, 16, 1) == lib.prism_fwd_nl_workspace_bytes(1, 1, 64, 16, 16, 3, 16, 1)
+    assert f(1, 1, 64, 16, 48, 3, 16, 1) == 0
+    g = lib.prism_fwd_delta_seg_workspace_bytes
+    assert g(1, 2, 600, 64, 64, 4, 64, 1, 2) > g(1, 2, 600, 64, 64, 4, 64, 1, 10) > 0
+    p = lib.prism_fwd_delta_pred_workspace_bytes
+    assert p(2, 4, 16384, 64, 64, 4, 64, 1) > f(2, 4, 16384, 64, 64, 4, 64, 1)
+    assert p(1, 1, 64, 64, 64, 1, 64, 1) == 0          # L = 1: nothing to predict
+    assert p(1, 1, 64, 64, 64, 4, 64, 0) == 0          # float32: no MFMA front end
+    assert p(1, 1, 64, 64, 32, 4, 64, 1) == 0          # dk != dv
+    assert p(1, 1, 64, 16, 16, 4, 16, 1) == 0          # d = 16
+    v = ctypes.c_void_p(1)
+    fwd = lambda **kw: lib.prism_fwd_delta(*[kw.get(n, v) for n in ("q", "k", "v", "g", "beta", "u", "alpha", "p",
+                                                                     "w")],
+                                           1, 1, 64, 16, 16, 3, 16, 1, v, v, kw.get("ws", v), 1 << 30, None)
+    assert fwd(p=None) == INVALID
+    assert fwd(alpha=None) == INVALID
+    assert fwd(ws=None) == WORKSPACE
+    ap = lib.prism_anchor_predict
+    assert ap(v, v, v, v, v, None, 1, 1, 64, 64, 64, 3, 0, v, v, v, None) == UNSUPPORTED   # float32
+    assert ap(v, v, v, v, v, None, 1, 1, 64, 64, 64, 1, 1, v, v, v, None) == UNSUPPORTED   # L = 1
+    assert ap(v, v, v, v, v, None, 1, 1, 64, 64, 32, 3, 1, v, v, v, None) == UNSUPPORTED   # dk != dv
+    assert ap(v, v, None, v, v, None, 1, 1, 64, 64, 64, 3, 1, v, v, v, None) == INVALID
+    assert ap(v, v, v, v, v, None, 0, 1, 64, 64, 64, 3, 1, v, v, v, None) == INVALID
+    dg = lib.prism_delta_gain
+    assert dg(v, None, v, None, 1, 1, 64, 16, 3, 1, v, None) == INVALID
+    assert dg(v, v, v, None, 1, 1, 64, 24, 3, 1, v, None) == UNSUPPORTED
+    assert dg(None, None, None, None, 1, 1, 64, 16, 1, 1, None, None) == OK   # L = 1: nothing to do

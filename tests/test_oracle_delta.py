@@ -144,6 +144,19 @@ def test_factor_limit_at_zero_residual():
     np.testing.assert_allclose(fac, 0.5 * np.asarray(x["p"], np.float64), atol=0, rtol=0)
 
 
+def test_factor_rounding_is_the_chain_the_forward_sees():
+    """With each factor rounded before the chain continues, the factor form run with those
+    factors is still exact: the rounding only moves the residuals the next levels see."""
+    w, x = _inputs(L=5, T=10)
+    rnd = lambda f: np.round(f * 64.0) / 64.0  # noqa: E731  (a coarse grid: visible effect)
+    fr = odl.delta_factors(x["v"], x["p"], x["conv_w"], 5, rounding=rnd)
+    assert np.all(fr * 64.0 == np.round(fr * 64.0))
+    assert np.max(np.abs(fr - odl.delta_factors(x["v"], x["p"], x["conv_w"], 5))) > 1e-3
+    # level 0 sees the exact residual r_0 either way
+    f0 = odl.delta_factors(x["v"], x["p"], x["conv_w"], 5)[..., 0, :]
+    np.testing.assert_array_equal(fr[..., 0, :], rnd(f0))
+
+
 def test_greedy_subtraction_shrinks_residual():
     rng = np.random.default_rng(3)
     r0 = rng.standard_normal((50, 16))

@@ -45,7 +45,7 @@ import numpy as np
 from scipy.special import ndtr
 
 __all__ = ["Workload", "WORKLOADS", "workload", "generate", "generate_gain", "generate_predictor",
-           "generate_state", "to_bf16_values", "manifest"]
+           "generate_front", "generate_state", "to_bf16_values", "manifest"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -224,6 +224,22 @@ def generate_predictor(w: Workload, seed: Optional[int] = None) -> Optional[np.n
     return _cast_vec(W, w.dtype)
 
 
+def generate_front(w: Workload, seed: Optional[int] = None) -> Optional[Dict[str, np.ndarray]]:
+    """Weights of the predictor front end of the written-correction form: W_p [H, L-1, dv, dv],
+    W_k [H, L-1, dk, dv] ((out, in) layouts) and W_b [H, L, dv], N(0, 1/dv) entries from
+    default_rng(seed + 3000) in that order (a random initialisation: gains of about the
+    anchor's scale, gate logits of about unit scale), in the I/O dtype.  None for L = 1."""
+    if w.L == 1:
+        return None
+    seed = (w.seed if seed is None else seed) + 3000
+    rng = np.random.default_rng(seed)
+    sc = 1.0 / np.sqrt(w.dv)
+    Wp = rng.standard_normal((w.H, w.L - 1, w.dv, w.dv)) * sc
+    Wk = rng.standard_normal((w.H, w.L - 1, w.dk, w.dv)) * sc
+    Wb = rng.standard_normal((w.H, w.L, w.dv)) * sc
+    return {"W_p": _cast_vec(Wp, w.dtype), "W_k": _cast_vec(Wk, w.dtype), "W_b": _cast_vec(Wb, w.dtype)}
+
+
 def generate_state(w: Workload, seed: Optional[int] = None) -> Dict[str, np.ndarray]:
     """A starting point for a continued sequence of workload `w`: S0 [B,H,dk,dv] float32
     with N(0, 0.3^2) entries (the S_final layout) and conv_in [B,H,3,dv], values of the
@@ -252,7 +268,7 @@ def to_torch(inputs: Dict[str, np.ndarray], dtype: str, device="cuda"):
             out[key] = None
             continue
         t = torch.from_numpy(np.ascontiguousarray(val))
-        if key in ("q", "k", "v", "u", "gamma", "conv_in", "p", "W_p"):
+        if key in ("q", "k", "v", "u", "gamma", "conv_in", "p", "W_p", "W_k", "W_b"):
             t = t.to(device=device).to(vt)
         else:
             t = t.to(device=device, dtype=torch.float32)
