@@ -14,10 +14,14 @@ prism_status launch_generic(const FwdArgs& a, const LaunchShape& s, hipEvent_t* 
   if constexpr (!SegLds<E, DK, DV, C>::fits) {
     return PRISM_ERR_UNSUPPORTED;
   } else {
+    // eight waves when a tile side is 128 wide (one value and one key column block per
+    // wave, two waves per SIMD), four otherwise
+    constexpr int NW = (DK >= 128 || DV >= 128) ? 8 : 4;
     if (!record(ev, 0, stream)) return PRISM_ERR_HIP;
-    hipLaunchKernelGGL((seg_local_kernel<E, DK, DV, C>), dim3(s.nseg, s.P), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((seg_local_kernel<E, DK, DV, C, NW>), dim3(s.nseg, s.P), dim3(64 * NW), 0, stream, a);
     if (hipGetLastError() != hipSuccess || !record(ev, 1, stream)) return PRISM_ERR_HIP;
-    hipLaunchKernelGGL((seg_scan_kernel<DK, DV>), dim3(s.P, DV / 16), dim3(256), 0, stream, a);
+    constexpr int NQ = DK >= 128 ? 8 : 4;  // state columns per scan workgroup
+    hipLaunchKernelGGL((seg_scan_kernel<DK, DV>), dim3(s.P, DV / NQ), dim3(NQ * DK), 0, stream, a);
     if (hipGetLastError() != hipSuccess || !record(ev, 2, stream)) return PRISM_ERR_HIP;
     if constexpr (std::is_same<E, bf16_t>::value && DK == 128 && DV == 128 && C == 64)
       hipLaunchKernelGGL((seg_fixup_mfma_kernel<DK, C>), dim3(s.nch, s.P), dim3(256), 0, stream, a);

@@ -84,13 +84,14 @@ struct SegLds {
   static constexpr bool fits = total <= 160 * 1024;
 };
 
-template <class E, int DK, int DV, int C>
-__global__ __launch_bounds__(256, 1) void seg_local_kernel(FwdArgs a) {
+template <class E, int DK, int DV, int C, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void seg_local_kernel(FwdArgs a) {
   using Ly = SegLds<E, DK, DV, C>;
   constexpr int LDK = Ly::LDK, LDC = Ly::LDC, LDF = Ly::LDF;
   constexpr int MT = C / 16, KT = DK / 16, VT = DV / 16;
-  constexpr int NVW = (VT + 3) / 4;  // value column blocks per wave
-  constexpr int NKW = (KT + 3) / 4;  // key column blocks per wave
+  constexpr int NVW = (VT + NW - 1) / NW;  // value column blocks per wave
+  constexpr int NKW = (KT + NW - 1) / NW;  // key column blocks per wave
+  constexpr int NT = 64 * NW;              // threads
   __shared__ __align__(16) unsigned char smem[Ly::total];
   E* sQ = reinterpret_cast<E*>(smem + Ly::oQ);
   E* sK = reinterpret_cast<E*>(smem + Ly::oK);
@@ -130,8 +131,8 @@ __global__ __launch_bounds__(256, 1) void seg_local_kernel(FwdArgs a) {
   const float* al = L > 1 ? a.alpha + (size_t)pr * T * L : nullptr;
   const float* cw = L > 1 ? a.conv_w + (size_t)hd * 4 * DV : nullptr;
 
-  // State tiles owned by this wave: value column blocks vt = w + 4*jv, key
-  // column blocks kt' = w + 4*jk.
+  // State tiles owned by this wave: value column blocks vt = w + NW*jv, key
+  // column blocks kt' = w + NW*jk.
   f32x4 Hs[NVW][KT];   // H(kt, vt)
   f32x4 As[NKW][KT];   // A_acc(kt, kt')
 #pragma unroll
@@ -142,7 +143,7 @@ __global__ __launch_bounds__(256, 1) void seg_local_kernel(FwdArgs a) {
   for (int jk = 0; jk < NKW; ++jk)
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt) {
-      const int kc = w + 4 * jk;
+      const int kc = w + NW * jk;
       f32x4 t = zero4();
       if (kc == kt) {
 #pragma unroll
@@ -158,7 +159,7 @@ __global__ __launch_bounds__(256, 1) void seg_local_kernel(FwdArgs a) {
     // ---- stage 0: state operand (H^T) into LDS, Q / K rows, gates --------------
 #pragma unroll
     for (int jv = 0; jv < NVW; ++jv) {
-      const int vt = w + 4 * jv;
+      const int vt = w + NW * jv;
       if (vt < VT) {
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt)
@@ -170,7 +171,7 @@ __global__ __launch_bounds__(256, 1) void seg_local_kernel(FwdArgs a) {
     {
       constexpr int VEC = 16 / sizeof(E);
       constexpr int PER_ROW = DK / VEC;
-      for (int idx = tid; idx < C * PER_ROW; idx += 256) {
+      for (int idx = tid; idx < C * PER_ROW; idx += NT) {
         const int row = idx / PER_ROW, cv = (idx % PER_ROW) * VEC;
         uint4 qv = make_uint4(0, 0, 0, 0), kv = make_uint4(0, 0, 0, 0);
         if (row < nvalid) {
@@ -204,12 +205,18 @@ __global__ __launch_bounds__(256, 1) void seg_local_kernel(FwdArgs a) {
     __syncthreads();
 
     // ---- prologue: V' init, anchor and initial residual, in tile layout ------
-    f32x4 Vp[NVW][MT], Oc[NVW][MT], Rr[NVW][MT], HB[NVW][KT];
+    // The state's operand copy in LDS (stage 0) is all the chunk reads of the old H; the
+    // registers now take the decayed state G_C H, and the chunk's write terms accumulate
+    // into them (H' = G_C H + sum_l U_l^T D R_l + K^T D E).
+    f32x4 Vp[NVW][MT], Oc[NVW][MT], Rr[NVW][MT];
 #pragma unroll
     for (int jv = 0; jv < NVW; ++jv) {
-      const int vt = w + 4 * jv;
+      const int vt = w + NW * jv;
+      const float GC0 = sG[C - 1];
 #pragma unroll
-      for (int kt = 0; kt < KT; ++kt) HB[jv][kt] = zero4();
+      for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Hs[jv][kt][r] *= GC0;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         Oc[jv][mt] = zero4();
@@ -243,7 +250,7 @@ __global__ __launch_bounds__(256, 1) void seg_local_kernel(FwdArgs a) {
     }
 
     // ---- P = lower(Gam * Q K^T) -----------------------------------------------
-    for (int tI = w; tI < MT * MT; tI += 4) {
+    for (int tI = w; tI < MT * MT; tI += NW) {
       const int mt = tI / MT, jt = tI % MT;
       f32x4 acc = zero4();
       if (jt <= mt) mm_ll<E>(acc, sQ, LDK, 16 * mt, sK, LDK, 16 * jt, DK);
@@ -260,7 +267,7 @@ __global__ __launch_bounds__(256, 1) void seg_local_kernel(FwdArgs a) {
       {  // U_l rows into LDS
         constexpr int VEC = 16 / sizeof(E);
         constexpr int PER_ROW = DK / VEC;
-        for (int idx = tid; idx < C * PER_ROW; idx += 256) {
+        for (int idx = tid; idx < C * PER_ROW; idx += NT) {
           const int row = idx / PER_ROW, cv = (idx % PER_ROW) * VEC;
           uint4 uv = make_uint4(0, 0, 0, 0);
           if (row < nvalid)
@@ -272,7 +279,7 @@ __global__ __launch_bounds__(256, 1) void seg_local_kernel(FwdArgs a) {
       f32x4 R[NVW][MT];
 #pragma unroll
       for (int jv = 0; jv < NVW; ++jv) {
-        const int vt = w + 4 * jv;
+        const int vt = w + NW * jv;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
           f32x4 rv = zero4();
@@ -300,7 +307,7 @@ __global__ __launch_bounds__(256, 1) void seg_local_kernel(FwdArgs a) {
       }
       __syncthreads();
       // X1 = -strict(Gam * K U^T), X2 = lower(Gam * Q U^T)
-      for (int tI = w; tI < 2 * MT * MT; tI += 4) {
+      for (int tI = w; tI < 2 * MT * MT; tI += NW) {
         const int which = tI / (MT * MT), t2 = tI % (MT * MT);
         const int mt = t2 / MT, jt = t2 % MT;
         f32x4 acc = zero4();
@@ -317,21 +324,21 @@ __global__ __launch_bounds__(256, 1) void seg_local_kernel(FwdArgs a) {
       __syncthreads();
 #pragma unroll
       for (int jv = 0; jv < NVW; ++jv) {
-        if (w + 4 * jv < VT) {
+        if (w + NW * jv < VT) {
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt) {
             mm_lt<E, MT>(Vp[jv][mt], sX1, LDC, 16 * mt, R[jv], nullptr, C);
             mm_lt<E, MT>(Oc[jv][mt], sX2, LDC, 16 * mt, R[jv], nullptr, C);
           }
 #pragma unroll
-          for (int kt = 0; kt < KT; ++kt) mm_tt<E, MT>(HB[jv][kt], sU, LDK, 16 * kt, sD, R[jv], C);
+          for (int kt = 0; kt < KT; ++kt) mm_tt<E, MT>(Hs[jv][kt], sU, LDK, 16 * kt, sD, R[jv], C);
         }
       }
       __syncthreads();
     }
 
     // ---- UT transform: T = (I + strict(diag(beta) Gam * K K^T))^-1 -------------
-    for (int tI = w; tI < MT * MT; tI += 4) {
+    for (int tI = w; tI < MT * MT; tI += NW) {
       const int mt = tI / MT, jt = tI % MT;
       f32x4 acc = zero4();
       if (jt <= mt) mm_ll<E>(acc, sK, LDK, 16 * mt, sK, LDK, 16 * jt, DK);
@@ -360,15 +367,17 @@ __global__ __launch_bounds__(256, 1) void seg_local_kernel(FwdArgs a) {
     }
     __syncthreads();
     for (int d = 1; d < MT; ++d) {  // off-diagonal blocks, T_ij = -T_ii sum_k M_ik T_kj
-      const int r = tid >> 4, cc = tid & 15;
-      for (int bi = d; bi < MT; ++bi) {
+      // thread (r, cc) of each group of 256 threads takes element (r, cc) of every
+      // (NW / 4)-th block of the diagonal d
+      const int r = (tid >> 4) & 15, cc = tid & 15, grp = tid >> 8;
+      for (int bi = d + grp; bi < MT; bi += NW / 4) {
         const int bj = bi - d;
         float s = 0.f;
         for (int kk = 16 * bj; kk < 16 * bi; ++kk) s += sMf[(16 * bi + r) * LDF + kk] * sTf[kk * LDF + 16 * bj + cc];
         sTmp[(bi - d) * 272 + r * 17 + cc] = s;
       }
       __syncthreads();
-      for (int bi = d; bi < MT; ++bi) {
+      for (int bi = d + grp; bi < MT; bi += NW / 4) {
         const int bj = bi - d;
         float s = 0.f;
 #pragma unroll
@@ -377,7 +386,7 @@ __global__ __launch_bounds__(256, 1) void seg_local_kernel(FwdArgs a) {
       }
       __syncthreads();
     }
-    for (int idx = tid; idx < C * C; idx += 256) {
+    for (int idx = tid; idx < C * C; idx += NT) {
       const int i = idx / C, j = idx % C;
       sT[i * LDC + j] = from_f<E>(j <= i ? sTf[i * LDF + j] : 0.f);
     }
@@ -391,14 +400,14 @@ __global__ __launch_bounds__(256, 1) void seg_local_kernel(FwdArgs a) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         Uc[mt] = zero4();
-        if (w + 4 * jv < VT) mm_lt<E, MT>(Uc[mt], sT, LDC, 16 * mt, Vp[jv], sBeta, C);
+        if (w + NW * jv < VT) mm_lt<E, MT>(Uc[mt], sT, LDC, 16 * mt, Vp[jv], sBeta, C);
       }
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) Vp[jv][mt] = Uc[mt];
     }
 #pragma unroll
     for (int jk = 0; jk < NKW; ++jk) {
-      const int kc = w + 4 * jk;
+      const int kc = w + NW * jk;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         f32x4 acc = zero4();
@@ -416,7 +425,7 @@ __global__ __launch_bounds__(256, 1) void seg_local_kernel(FwdArgs a) {
     float* oloc = a.Oloc + ((size_t)pr * Tpad + t0) * DV;
 #pragma unroll
     for (int jv = 0; jv < NVW; ++jv) {
-      const int vt = w + 4 * jv;
+      const int vt = w + NW * jv;
       if (vt >= VT) continue;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
@@ -435,21 +444,14 @@ __global__ __launch_bounds__(256, 1) void seg_local_kernel(FwdArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) oloc[(size_t)(16 * mt + g4 + r) * DV + 16 * vt + li] = Oc[jv][mt][r];
       }
-      const float GC = sG[C - 1];
 #pragma unroll
-      for (int kt = 0; kt < KT; ++kt) {
-        f32x4 acc = HB[jv][kt];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[r] += GC * Hs[jv][kt][r];
-        mm_tt<E, MT>(acc, sK, LDK, 16 * kt, sD, Vp[jv], C);
-        Hs[jv][kt] = acc;
-      }
+      for (int kt = 0; kt < KT; ++kt) mm_tt<E, MT>(Hs[jv][kt], sK, LDK, 16 * kt, sD, Vp[jv], C);
     }
     __syncthreads();
     // A_acc^T into the state-operand buffer
 #pragma unroll
     for (int jk = 0; jk < NKW; ++jk) {
-      const int kc = w + 4 * jk;
+      const int kc = w + NW * jk;
       if (kc < KT) {
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt)
@@ -465,7 +467,7 @@ __global__ __launch_bounds__(256, 1) void seg_local_kernel(FwdArgs a) {
       const float GC = sG[C - 1];
 #pragma unroll
       for (int jk = 0; jk < NKW; ++jk) {
-        const int kc = w + 4 * jk;
+        const int kc = w + NW * jk;
         if (kc >= KT) continue;
         f32x4 WA[MT];
 #pragma unroll
@@ -493,7 +495,7 @@ __global__ __launch_bounds__(256, 1) void seg_local_kernel(FwdArgs a) {
     // ---- Qhat = Qtilde A_acc (A_acc before this chunk) --------------------------
     {
       float* qhat = a.Qhat + ((size_t)pr * Tpad + t0) * DK;
-      for (int tI = w; tI < MT * KT; tI += 4) {
+      for (int tI = w; tI < MT * KT; tI += NW) {
         const int mt = tI / KT, kc = tI % KT;
         f32x4 acc = zero4();
         mm_ll<E>(acc, sQt, LDK, 16 * mt, sS, LDK, 16 * kc, DK);
@@ -509,7 +511,7 @@ __global__ __launch_bounds__(256, 1) void seg_local_kernel(FwdArgs a) {
   float* Bg = a.Bagg + ((size_t)pr * a.nseg + seg) * DK * DV;
 #pragma unroll
   for (int jk = 0; jk < NKW; ++jk) {
-    const int kc = w + 4 * jk;
+    const int kc = w + NW * jk;
     if (kc >= KT) continue;
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt)
@@ -518,7 +520,7 @@ __global__ __launch_bounds__(256, 1) void seg_local_kernel(FwdArgs a) {
   }
 #pragma unroll
   for (int jv = 0; jv < NVW; ++jv) {
-    const int vt = w + 4 * jv;
+    const int vt = w + NW * jv;
     if (vt >= VT) continue;
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt)
@@ -527,36 +529,105 @@ __global__ __launch_bounds__(256, 1) void seg_local_kernel(FwdArgs a) {
   }
 }
 
-// Inter-segment recurrence for 16 state columns of one pair (float32 VALU).
+// x from the lane the DPP control CTRL names (within a row of 16 lanes)
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+// Inter-segment recurrence H_in(s+1) = A_s H_in(s) + B_s (float32) for NQ state columns of
+// one pair (NQ = 8 at DK = 128, else 4).  Thread (i, q) = (tid / NQ, tid % NQ) takes row i of
+// A_s over the contraction slice k = q DK/NQ .. + DK/NQ - 1, kept in registers and loaded
+// DEPTH steps ahead (so a step waits on LDS only); it forms partial sums for the NQ columns
+// from the LDS copy of H_in(s) (row r at r + r / (DK/NQ): the slices' rows fall on different
+// banks), and DPP exchanges inside the group of NQ lanes leave lane q with column c0 + q:
+// partner 7 - q (bit 2) for NQ = 8, then 3 - q (bit 1), then q ^ 1 (bit 0).  One barrier
+// per step.  Eight columns per workgroup at DK = 128 halve the workgroups that read each
+// A_s, against four.
 template <int DK, int DV>
-__global__ __launch_bounds__(256) void seg_scan_kernel(FwdArgs a) {
-  __shared__ float sA[DK * DK];
-  __shared__ float sH[2][DK * 16];
-  const int tid = threadIdx.x, pr = blockIdx.x, c0 = 16 * blockIdx.y;
-  const int j = tid & 15;
-  const float* S0 = a.S0 != nullptr ? a.S0 + (size_t)pr * DK * DV : nullptr;
-  for (int idx = tid; idx < DK * 16; idx += 256)
-    sH[0][idx] = S0 != nullptr ? S0[(idx >> 4) * DV + c0 + (idx & 15)] : 0.f;
+__global__ __launch_bounds__(DK >= 128 ? 8 * DK : 4 * DK) void seg_scan_kernel(FwdArgs a) {
+  constexpr int NQ = DK >= 128 ? 8 : 4;       // contraction slices = columns per workgroup
+  static_assert(DV % NQ == 0, "NQ state columns per workgroup");
+  constexpr int KQ = DK / NQ;                 // contraction entries per thread
+  constexpr int NF = KQ / 4;                  // float4 loads per step
+  constexpr int NH = NQ / 4;                  // float4 per LDS row
+  constexpr int DEPTH = NQ == 8 ? 4 : 8;      // steps loaded ahead (1024 threads: 128 VGPRs)
+  constexpr int HS = DK + NQ;                 // skewed rows of the LDS copy
+  __shared__ __align__(16) float4 sH[2][HS][NH];
+  const int tid = threadIdx.x, i = tid / NQ, q = tid % NQ;
+  const int pr = blockIdx.x, c0 = NQ * blockIdx.y, col = c0 + q;
+  const int nseg = a.nseg;
+  const float* A0 = a.Aagg + (size_t)pr * nseg * DK * DK + (size_t)i * DK + q * KQ;
+  const float* B0 = a.Bagg + (size_t)pr * nseg * DK * DV + (size_t)i * DV + col;
+  float* H0 = a.Hin + (size_t)pr * nseg * DK * DV + (size_t)i * DV + col;
+  auto hrow = [](int r) { return r + r / KQ; };
+  float h = a.S0 != nullptr ? a.S0[(size_t)pr * DK * DV + (size_t)i * DV + col] : 0.f;
+  reinterpret_cast<float*>(&sH[0][hrow(i)][0])[q] = h;
+  float4 ra[DEPTH][NF];
+  float rb[DEPTH];
+  auto fetch = [&](float4 (&x)[NF], float& b, int s) {
+    const size_t sn = (size_t)(s < nseg ? s : nseg - 1);  // unconditional: waits stay exact
+    const float4* src = reinterpret_cast<const float4*>(A0 + sn * DK * DK);
+#pragma unroll
+    for (int f = 0; f < NF; ++f) x[f] = src[f];
+    b = B0[sn * DK * DV];
+  };
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d) fetch(ra[d], rb[d], d);
   __syncthreads();
   int cur = 0;
-  for (int s = 0; s < a.nseg; ++s) {
-    const float* As = a.Aagg + ((size_t)pr * a.nseg + s) * DK * DK;
-    const float* Bs = a.Bagg + ((size_t)pr * a.nseg + s) * DK * DV;
-    float* Hi = a.Hin + ((size_t)pr * a.nseg + s) * DK * DV;
-    for (int idx = tid; idx < DK * 16; idx += 256) Hi[(idx >> 4) * DV + c0 + (idx & 15)] = sH[cur][idx];
-    for (int idx = tid; idx < DK * DK / 4; idx += 256)
-      reinterpret_cast<float4*>(sA)[idx] = reinterpret_cast<const float4*>(As)[idx];
-    __syncthreads();
-    for (int i = tid >> 4; i < DK; i += 16) {
-      float acc = Bs[i * DV + c0 + j];
-      for (int kk = 0; kk < DK; ++kk) acc += sA[i * DK + kk] * sH[cur][kk * 16 + j];
-      sH[cur ^ 1][i * 16 + j] = acc;
+  for (int s0 = 0; s0 < nseg; s0 += DEPTH) {
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) {
+      const int s = s0 + d;
+      if (s < nseg) {
+        H0[(size_t)s * DK * DV] = h;
+        float v[NQ];
+#pragma unroll
+        for (int c = 0; c < NQ; ++c) v[c] = 0.f;
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+          const float am[4] = {ra[d][f].x, ra[d][f].y, ra[d][f].z, ra[d][f].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+#pragma unroll
+            for (int hh = 0; hh < NH; ++hh) {
+              const float4 hv = sH[cur][hrow(q * KQ + 4 * f + e)][hh];
+              v[4 * hh + 0] += am[e] * hv.x;
+              v[4 * hh + 1] += am[e] * hv.y;
+              v[4 * hh + 2] += am[e] * hv.z;
+              v[4 * hh + 3] += am[e] * hv.w;
+            }
+          }
+        }
+        const float bv = rb[d];
+        fetch(ra[d], rb[d], s + DEPTH);
+        // reduce-scatter over the NQ lanes: keep the half, then the pair, then the column
+        float n4[4];
+        if constexpr (NQ == 8) {
+          const bool up = (q & 4) != 0;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) n4[j] = (up ? v[4 + j] : v[j]) + dpp_mov<0x141>(up ? v[j] : v[4 + j]);  // 7 - q
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) n4[j] = v[j];
+        }
+        const bool hi2 = (q & 2) != 0, hi1 = (q & 1) != 0;
+        float n2[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          // 3 - q for NQ = 8 (bits 1 and 0 both flip; bit 1 decides), q ^ 2 for NQ = 4
+          const float recv = dpp_mov<NQ == 8 ? 0x1B : 0x4E>(hi2 ? n4[j] : n4[2 + j]);
+          n2[j] = (hi2 ? n4[2 + j] : n4[j]) + recv;
+        }
+        h = (hi1 ? n2[1] : n2[0]) + dpp_mov<0xB1>(hi1 ? n2[0] : n2[1]) + bv;  // q ^ 1
+        reinterpret_cast<float*>(&sH[cur ^ 1][hrow(i)][0])[q] = h;
+        cur ^= 1;
+        __syncthreads();
+      }
     }
-    __syncthreads();
-    cur ^= 1;
   }
-  float* Sf = a.S_final + (size_t)pr * DK * DV;
-  for (int idx = tid; idx < DK * 16; idx += 256) Sf[(idx >> 4) * DV + c0 + (idx & 15)] = sH[cur][idx];
+  a.S_final[(size_t)pr * DK * DV + (size_t)i * DV + col] = h;
 }
 
 // o = O_loc + Qhat H_in(segment) for one chunk of one pair (float32 VALU).
