@@ -13,7 +13,8 @@ import re
 from typing import Optional, Tuple
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libprism.so")
+# PRISM_LIB selects another build of the same library (the host-sanitized one of the ABI tests)
+LIB_PATH = os.environ.get("PRISM_LIB") or os.path.join(HERE, "libprism.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "prism.h")
 
 PRISM_F32, PRISM_BF16 = 0, 1

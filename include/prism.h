@@ -72,7 +72,15 @@ typedef enum {
   PRISM_ERR_HIP = -4            /* a HIP launch or runtime call failed */
 } prism_status;
 
-typedef enum { PRISM_F32 = 0, PRISM_BF16 = 1 } prism_dtype;
+/* The last two enumerators are not types: they make every int a value of prism_dtype, so an
+ * unknown code can be passed across the ABI and is rejected (PRISM_ERR_INVALID_ARG or
+ * PRISM_ERR_UNSUPPORTED) instead of being undefined behaviour to read. */
+typedef enum {
+  PRISM_F32 = 0,
+  PRISM_BF16 = 1,
+  PRISM_DTYPE_RANGE_MIN_ = -2147483647 - 1,
+  PRISM_DTYPE_RANGE_MAX_ = 2147483647
+} prism_dtype;
 
 /* Bytes of device workspace prism_fwd needs for these sizes; 0 when the
  * arguments are invalid or unsupported (prism_fwd then reports which).
