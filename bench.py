@@ -49,7 +49,8 @@ def algorithmic_bytes(w):
 # the sources the segment-sweep kernel is compiled from, and the build flags
 SWEEP_SOURCES = ["delta_rule_sequence_amd/csrc/prism_sweep8.h", "delta_rule_sequence_amd/csrc/prism_fast.h",
                  "delta_rule_sequence_amd/csrc/prism_kernels.h", "delta_rule_sequence_amd/csrc/prism_tile.h",
-                 "delta_rule_sequence_amd/csrc/prism_nl.h", "delta_rule_sequence_amd/build.py"]
+                 "delta_rule_sequence_amd/csrc/prism_nl.h", "delta_rule_sequence_amd/csrc/prism_generic_launch.h",
+                 "delta_rule_sequence_amd/csrc/fwd_fast_linear.hip", "delta_rule_sequence_amd/build.py"]
 
 
 def kernel_source_hash():
@@ -556,6 +557,9 @@ def main():
                     help="time the backward (prism_bwd) on --workload instead")
     ap.add_argument("--nl", action="store_true",
                     help="time the nonlinear-refinement forward (prism_fwd_nl) on --workload instead")
+    ap.add_argument("--forward-only", action="store_true",
+                    help="the forward's line only: skip the backward, nonlinear, copy and GEMM legs "
+                         "(for profiler runs)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -650,6 +654,9 @@ def main():
     out["roofline"]["mfma_secondary"] = {"achieved": mfma_achieved, "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                                          "frac": mfma_achieved / MFMA_PEAK_TFLOPS,
                                          "flop_per_token_head": chunk_flop}
+    if args.forward_only:
+        print(json.dumps(out))
+        return
     # the backward on the same workload (one warm-up, two timed calls): reported beside the
     # forward metric, not part of it
     d_o = np.random.default_rng(w.seed + 7).standard_normal((w.B, w.H, w.T, w.dv)).astype(np.float32)
