@@ -60,6 +60,10 @@ def load_library() -> ctypes.CDLL:
     lib.prism_bwd_workspace_bytes.argtypes = [i] * 7
     lib.prism_bwd_workspace_bytes.restype = sz
     lib.prism_bwd_lowmem.argtypes = lib.prism_bwd.argtypes
+    lib.prism_bwd_seg.argtypes = fwd_args[:9] + [i] * 7 + [vp, fp] + [fp] * 9 + [i, vp, sz, vp]
+    lib.prism_bwd_seg.restype = ctypes.c_int
+    lib.prism_bwd_seg_workspace_bytes.argtypes = [i] * 8
+    lib.prism_bwd_seg_workspace_bytes.restype = sz
     lib.prism_bwd_lowmem.restype = ctypes.c_int
     lib.prism_bwd_lowmem_workspace_bytes.argtypes = [i] * 7
     lib.prism_bwd_lowmem_workspace_bytes.restype = sz
@@ -334,11 +338,13 @@ def fwd(q, k, v, g, beta, u=None, alpha=None, gamma=None, conv_w=None, L: int = 
 
 
 def bwd(q, k, v, g, beta, u=None, alpha=None, gamma=None, conv_w=None, L: int = 1, d_o=None,
-        dS_final=None, workspace=None, stream=None, low_memory: bool = False):
+        dS_final=None, workspace=None, stream=None, low_memory: bool = False, seg_len=None):
     """Gradients of sum <d_o, o> + <dS_final, S_final> for fwd(q, ..., conv_w, L) (zero start).
 
     Inputs as fwd(); d_o [B,H,T,dv] in the input dtype; dS_final [B,H,dk,dv] float32 or None.
-    low_memory: use prism_bwd_lowmem (states every 64 tokens only).
+    low_memory: use prism_bwd_lowmem (the sequential form, states every 64 tokens only).
+    seg_len: segment length of the segment-parallel form (prism_bwd_seg; a multiple of 8,
+    at least 16); None: prism_bwd, which picks it.
     Returns a dict of float32 tensors dq, dk, dv, dg, dbeta and, when L > 1, du, dalpha,
     dgamma, dconv_w (the shapes of the corresponding inputs; dconv_w summed over the batch).
     """
@@ -366,20 +372,29 @@ def bwd(q, k, v, g, beta, u=None, alpha=None, gamma=None, conv_w=None, L: int = 
     if L > 1:
         out.update({"du": torch.empty((B, H, T, L - 1, dk), **f32), "dalpha": torch.empty((B, H, T, L), **f32),
                     "dgamma": torch.empty((B, H, T, L - 1, dv), **f32), "dconv_w": torch.empty((H, 4, dv), **f32)})
-    wsb = lib.prism_bwd_lowmem_workspace_bytes if low_memory else lib.prism_bwd_workspace_bytes
-    workspace = _workspace(workspace, wsb(B, H, T, dk, dv, L, dt), dev)
+    if low_memory and seg_len is not None:
+        raise PrismError("low_memory and seg_len select different forms")
+    if low_memory:
+        name, need = "prism_bwd_lowmem", lib.prism_bwd_lowmem_workspace_bytes(B, H, T, dk, dv, L, dt)
+    elif seg_len is not None:
+        name, need = "prism_bwd_seg", lib.prism_bwd_seg_workspace_bytes(B, H, T, dk, dv, L, dt, seg_len)
+    else:
+        name, need = "prism_bwd", lib.prism_bwd_workspace_bytes(B, H, T, dk, dv, L, dt)
+    if need == 0:
+        raise PrismError(f"{name}: shape not supported")
+    workspace = _workspace(workspace, need, dev)
     s = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
-    fn = lib.prism_bwd_lowmem if low_memory else lib.prism_bwd
-    st = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-                       _ptr(u) if L > 1 else None, _ptr(alpha) if L > 1 else None,
-                       _ptr(gamma) if L > 1 else None, _ptr(conv_w) if L > 1 else None,
-                       B, H, T, dk, dv, L, dt, _ptr(d_o), _ptr(dS_final),
-                       _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]), _ptr(out["dbeta"]),
-                       _ptr(out.get("du")), _ptr(out.get("dalpha")), _ptr(out.get("dgamma")),
-                       _ptr(out.get("dconv_w")),
-                       ctypes.c_void_p(workspace.data_ptr()), workspace.numel(), ctypes.c_void_p(s))
+    args = [_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+            _ptr(u) if L > 1 else None, _ptr(alpha) if L > 1 else None,
+            _ptr(gamma) if L > 1 else None, _ptr(conv_w) if L > 1 else None,
+            B, H, T, dk, dv, L, dt, _ptr(d_o), _ptr(dS_final),
+            _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]), _ptr(out["dbeta"]),
+            _ptr(out.get("du")), _ptr(out.get("dalpha")), _ptr(out.get("dgamma")), _ptr(out.get("dconv_w"))]
+    if seg_len is not None:
+        args.append(seg_len)
+    st = getattr(lib, name)(*args, ctypes.c_void_p(workspace.data_ptr()), workspace.numel(), ctypes.c_void_p(s))
     if st != 0:
-        raise PrismError(f"{'prism_bwd_lowmem' if low_memory else 'prism_bwd'} failed: {status_string(st)}")
+        raise PrismError(f"{name} failed: {status_string(st)}")
     return out
 
 

@@ -1,5 +1,6 @@
-// bwd.hip - launches of the backward (prism_bwd.h): the per-pair adjoint sweep, the
-// fixed-order sum of its per-workgroup partials and the batch sum of dconv_w.
+// bwd.hip - launches of the backward (prism_bwd.h): the sequential per-pair adjoint sweep
+// and the segment-parallel passes, the fixed-order sum of per-workgroup partials and the
+// batch sum of dconv_w.
 #include "prism_bwd.h"
 #include "prism_host.h"
 
@@ -8,60 +9,80 @@ namespace host {
 
 namespace {
 
-template <class E>
-bool bwd_staged_e(int d, int L) {
-  const int nr = L == 1 ? 1 : L <= 4 ? 3 : 7;
-#define PRISM_NB(D) (nr == 1 ? bwd_stage_tokens<E, D, 1>() : nr == 3 ? bwd_stage_tokens<E, D, 3>() \
-                                                                      : bwd_stage_tokens<E, D, 7>())
-  const int nb = d == 16 ? PRISM_NB(16) : d == 32 ? PRISM_NB(32) : d == 64 ? PRISM_NB(64) : PRISM_NB(128);
-#undef PRISM_NB
-  return nb > 0;
-}
-
-// D / 16 workgroups per pair (16 state rows each); then, when that is more than one, the
-// fixed-order sum of their per-token partials (8 tokens per workgroup, 1-D grid).
+// Sequential: D / 16 workgroups per pair (16 state rows each); then, when that is more than
+// one, the fixed-order sum of their per-token partials (8 tokens per workgroup, 1-D grid).
 template <class E, int D, int NRK>
 void bwd_launch_d(const BwdArgs& a, int P, hipStream_t stream) {
-  constexpr int NSP = D / 16;
+  constexpr int NSP = BwdShape<D, NRK>::NSP;
   hipLaunchKernelGGL((bwd_pair_kernel<E, D, NRK>), dim3((unsigned)P * NSP), dim3(256), 0, stream, a);
   if constexpr (NSP > 1) {
     const unsigned nt8 = (unsigned)((a.T + 7) / 8);
-    hipLaunchKernelGGL((bwd_part_reduce_kernel<D, NRK>), dim3((unsigned)P * nt8), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((bwd_part_reduce_kernel<D, NRK, 1>), dim3((unsigned)P * nt8), dim3(256), 0, stream, a);
   }
 }
 
-template <class E, int NRK>
-void bwd_launch(int d, const BwdArgs& a, int P, hipStream_t stream) {
-  switch (d) {
-    case 16: bwd_launch_d<E, 16, NRK>(a, P, stream); break;
-    case 32: bwd_launch_d<E, 32, NRK>(a, P, stream); break;
-    case 64: bwd_launch_d<E, 64, NRK>(a, P, stream); break;
-    default: bwd_launch_d<E, 128, NRK>(a, P, stream); break;
+// Segment-parallel: segment states, operators and local adjoints; the two scans; the
+// token steps of every segment; partial sums (NSP > 1); the anchor terms across segment
+// starts.
+template <class E, int D, int NRK>
+void bwd_seg_launch_d(const BwdArgs& a, int P, hipStream_t stream) {
+  constexpr int RW = bwd_seg_rows<D>(), NSP = BwdShape<D, NRK, RW>::NSP;
+  const unsigned nwg = (unsigned)P * (unsigned)a.nseg * NSP;
+  hipLaunchKernelGGL((bwd_seg_local_kernel<E, D, NRK, RW>), dim3(nwg), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((bwd_seg_scan_kernel<D>), dim3((unsigned)P, D / 4, 2), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((bwd_seg_kernel<E, D, NRK, RW>), dim3(nwg), dim3(256), 0, stream, a);
+  if constexpr (NSP > 1) {
+    const unsigned nt8 = (unsigned)((a.T + 7) / 8);
+    hipLaunchKernelGGL((bwd_part_reduce_kernel<D, NRK, RW>), dim3((unsigned)P * nt8), dim3(256), 0, stream, a);
   }
+  if (a.L > 1 && a.nseg > 1)
+    hipLaunchKernelGGL(bwd_seg_carry_kernel, dim3((unsigned)P * (unsigned)a.nseg), dim3(256), 0, stream, a, D);
+}
+
+template <class E, int NRK, bool SEG>
+void bwd_launch(int d, const BwdArgs& a, int P, hipStream_t stream) {
+#define PRISM_BWD_D(D) (SEG ? bwd_seg_launch_d<E, D, NRK>(a, P, stream) : bwd_launch_d<E, D, NRK>(a, P, stream))
+  switch (d) {
+    case 16: PRISM_BWD_D(16); break;
+    case 32: PRISM_BWD_D(32); break;
+    case 64: PRISM_BWD_D(64); break;
+    default: PRISM_BWD_D(128); break;
+  }
+#undef PRISM_BWD_D
 }
 
 // rank slots compiled in: 0 for L = 1, 3 for L <= 4, 7 for L <= 8
-template <class E>
+template <class E, bool SEG>
 void bwd_dispatch(int d, const BwdArgs& a, int P, hipStream_t stream) {
-  if (a.L == 1) bwd_launch<E, 0>(d, a, P, stream);
-  else if (a.L <= 4) bwd_launch<E, 3>(d, a, P, stream);
-  else bwd_launch<E, 7>(d, a, P, stream);
+  if (a.L == 1) bwd_launch<E, 0, SEG>(d, a, P, stream);
+  else if (a.L <= 4) bwd_launch<E, 3, SEG>(d, a, P, stream);
+  else bwd_launch<E, 7, SEG>(d, a, P, stream);
 }
 
 }  // namespace
 
-bool bwd_staged(prism_dtype dt, int d, int L) {
-  return dt == PRISM_BF16 ? bwd_staged_e<bf16_t>(d, L) : bwd_staged_e<float>(d, L);
+int bwd_seg_slices(int d) {
+  switch (d) {
+    case 16: return 16 / (16 * bwd_seg_rows<16>());
+    case 32: return 32 / (16 * bwd_seg_rows<32>());
+    case 64: return 64 / (16 * bwd_seg_rows<64>());
+    default: return 128 / (16 * bwd_seg_rows<128>());
+  }
 }
 
-prism_status launch_bwd(prism_dtype dt, int d, const BwdArgs& a, int B, int P, float* dconv_w,
+prism_status launch_bwd(prism_dtype dt, int d, const BwdArgs& a, int B, int P, float* dconv_w, bool segments,
                         hipStream_t stream) {
-  if (dt == PRISM_BF16) bwd_dispatch<bf16_t>(d, a, P, stream);
-  else bwd_dispatch<float>(d, a, P, stream);
+  if (segments) {
+    if (dt == PRISM_BF16) bwd_dispatch<bf16_t, true>(d, a, P, stream);
+    else bwd_dispatch<float, true>(d, a, P, stream);
+  } else {
+    if (dt == PRISM_BF16) bwd_dispatch<bf16_t, false>(d, a, P, stream);
+    else bwd_dispatch<float, false>(d, a, P, stream);
+  }
   if (hipGetLastError() != hipSuccess) return PRISM_ERR_HIP;
   if (a.L == 1) return PRISM_OK;
   hipLaunchKernelGGL(bwd_conv_reduce_kernel, dim3(a.H), dim3(256), 0, stream,
-                     static_cast<const float*>(a.dconv_part), dconv_w, B, a.H, d);
+                     static_cast<const float*>(a.dconv_part), dconv_w, B, a.H, d, segments ? a.nseg : 1);
   return hipGetLastError() == hipSuccess ? PRISM_OK : PRISM_ERR_HIP;
 }
 

@@ -213,63 +213,91 @@ prism_status decode_dispatch(int d, const prism::DecodeArgs& a, int P, hipStream
   return hipGetLastError() == hipSuccess ? PRISM_OK : PRISM_ERR_HIP;
 }
 
-// Workspace of the backward: checkpoints [P][nblk][D*D], block states [P][64][D*D] and
-// per-pair dconv_w shares [P][4][D], all float32, 256-byte aligned regions.
+// Workspace of the backward, float32 regions aligned to 256 bytes.
+//   sequential: checkpoints [P][NSP][nblk][D*D/NSP], block states [P][NSP][64][D*D/NSP],
+//     dconv_w shares [P][4][D] and, with NSP = D/16 > 1 workgroups per pair, their per-token
+//     column sums [P][NSP][T][RED];
+//   segment-parallel: B, Phi, ell, S_in, Lambda [P][nseg][D][D] each, sub-block checkpoints
+//     [P][nseg][seg_len/8][D][D], sub-block states [P][nseg][8][D][D], dconv_w shares
+//     [P][nseg][4][D], anchor carries [P][nseg][3][D] and, with NSP > 1 workgroups per
+//     state, the column sums [P][NSP][T][RED].
 struct BwdPlan {
-  int P, nblk;
-  bool all_states;
-  size_t off_ckpt, off_scr, off_part, off_red, total;
+  int P, nblk, nseg, seg_len;
+  bool segments;
+  size_t off_ckpt, off_scr, off_part, off_red, off_seg, off_carry, total;
 };
 
 // rank slots compiled in for L (0 for L = 1, 3 for L <= 4, 7 for L <= 8)
 inline int bwd_rank_slots(int L) { return L == 1 ? 0 : L <= 4 ? 3 : 7; }
 
-// Keep the state after every token (instead of one per 64 tokens and a re-run of each
-// block) when those states take at most this much memory and the kernel stages its inputs
-// through LDS: one sequential forward sweep fewer.
-constexpr size_t kBwdAllStatesMax = (size_t)4 << 30;
+// Segment length of the segment-parallel backward when the caller does not give one: the
+// longest of 128, 64, 32 tokens that still makes at least 2048 workgroups (several per
+// CU, so that their token steps hide one another's latency), else 16.
+int bwd_default_seg_len(size_t P, int T, int d) {
+  const size_t nsp = (size_t)prism::host::bwd_seg_slices(d);
+  for (int len = 128; len >= 32; len /= 2)
+    if (P * (((size_t)T + len - 1) / len) * nsp >= 2048) return len;
+  return 16;
+}
 
-prism_status make_bwd_plan(int B, int H, int T, int dk, int dv, int L, prism_dtype dt, BwdPlan* pl,
-                           bool low_memory = false) {
+// seg_len: 0 for the sequential form, else the segment length (a multiple of 8, >= 16).
+prism_status make_bwd_plan(int B, int H, int T, int dk, int dv, int L, prism_dtype dt, int seg_len, BwdPlan* pl) {
   if (B <= 0 || H <= 0 || T <= 0) return PRISM_ERR_INVALID_ARG;
   if (dt != PRISM_F32 && dt != PRISM_BF16) return PRISM_ERR_INVALID_ARG;
   if (L < 1 || L > 8) return PRISM_ERR_UNSUPPORTED;
   if (!valid_dim(dk) || dk != dv) return PRISM_ERR_UNSUPPORTED;
-  size_t P, a, b, c, sz_ckpt, sz_scr, sz_part;
+  if (seg_len != 0 && (seg_len < 16 || seg_len % prism::kBwdSegSub != 0)) return PRISM_ERR_INVALID_ARG;
+  size_t P, a, c, sz_ckpt, sz_scr, sz_part, sz_seg = 0, sz_carry = 0;
   if (!mul_ok((size_t)B, (size_t)H, &P) || P > (size_t)INT32_MAX) return PRISM_ERR_INVALID_ARG;
-  const size_t nblk = ((size_t)T + prism::kBwdBlock - 1) / prism::kBwdBlock;
+  // inputs must be addressable: P*T*L*dk elements
+  if (!mul_ok(P, (size_t)T, &c) || !mul_ok(c, (size_t)L * dk * 4, &c)) return PRISM_ERR_INVALID_ARG;
   const size_t dd = (size_t)dk * dk * 4;
-  size_t sz_all;
-  const bool staged = prism::host::bwd_staged(dt, dk, L);
-  pl->all_states = !low_memory && staged && mul_ok(P, (size_t)T, &a) && mul_ok(a, dd, &sz_all) &&
-                   sz_all <= kBwdAllStatesMax;
-  if (pl->all_states) {
-    sz_ckpt = sz_all;
-    sz_scr = 0;
+  const bool seg = seg_len != 0;
+  const size_t nseg = seg ? ((size_t)T + seg_len - 1) / seg_len : 1;
+  const size_t nblk = ((size_t)T + prism::kBwdBlock - 1) / prism::kBwdBlock;
+  int nsp = dk / 16;
+  if (seg) {
+    nsp = prism::host::bwd_seg_slices(dk);
+    size_t ps;
+    if (!mul_ok(P, nseg, &ps) || ps * nsp > (size_t)INT32_MAX) return PRISM_ERR_INVALID_ARG;
+    if (!mul_ok(ps, dd, &a) || !mul_ok(a, 5, &sz_seg)) return PRISM_ERR_INVALID_ARG;
+    if (!mul_ok(a, (size_t)seg_len / prism::kBwdSegSub, &sz_ckpt)) return PRISM_ERR_INVALID_ARG;
+    if (!mul_ok(a, (size_t)prism::kBwdSegSub, &sz_scr)) return PRISM_ERR_INVALID_ARG;
+    if (!mul_ok(ps, (size_t)4 * dk * 4, &sz_part) || !mul_ok(ps, (size_t)3 * dk * 4, &sz_carry))
+      return PRISM_ERR_INVALID_ARG;
   } else {
     if (!mul_ok(P, nblk, &a) || !mul_ok(a, dd, &sz_ckpt)) return PRISM_ERR_INVALID_ARG;
-    if (!mul_ok(P, (size_t)prism::kBwdBlock, &b) || !mul_ok(b, dd, &sz_scr)) return PRISM_ERR_INVALID_ARG;
+    if (!mul_ok(P, (size_t)prism::kBwdBlock, &a) || !mul_ok(a, dd, &sz_scr)) return PRISM_ERR_INVALID_ARG;
+    if (!mul_ok(P, (size_t)4 * dk * 4, &sz_part)) return PRISM_ERR_INVALID_ARG;
   }
-  if (!mul_ok(P, (size_t)4 * dk * 4, &sz_part)) return PRISM_ERR_INVALID_ARG;
-  // per-workgroup column sums and scalars when a pair's rows span dk / 16 > 1 workgroups
+  // per-workgroup column sums when a state's rows span more than one workgroup
   size_t sz_red = 0;
-  const int nsp = dk / 16, nr = bwd_rank_slots(L) > 0 ? bwd_rank_slots(L) : 1;
+  const int nr = bwd_rank_slots(L) > 0 ? bwd_rank_slots(L) : 1;
   if (nsp > 1) {
     const size_t red = (size_t)(2 + nr) * dk + 3 + nr;
     size_t x;
     if (!mul_ok(P, (size_t)nsp * T, &x) || !mul_ok(x, red * 4, &sz_red)) return PRISM_ERR_INVALID_ARG;
   }
-  // inputs must be addressable: P*T*(L-1)*dk elements
-  if (!mul_ok(P, (size_t)T, &c) || !mul_ok(c, (size_t)L * dk * 4, &c)) return PRISM_ERR_INVALID_ARG;
   pl->P = (int)P;
   pl->nblk = (int)nblk;
+  pl->nseg = (int)nseg;
+  pl->seg_len = seg_len;
+  pl->segments = seg;
   pl->off_ckpt = 0;
   pl->off_scr = align_up(sz_ckpt);
   pl->off_part = align_up(pl->off_scr + sz_scr);
   pl->off_red = align_up(pl->off_part + sz_part);
-  pl->total = align_up(pl->off_red + sz_red);
-  if (pl->total < sz_ckpt) return PRISM_ERR_INVALID_ARG;
+  pl->off_seg = align_up(pl->off_red + sz_red);
+  pl->off_carry = align_up(pl->off_seg + sz_seg);
+  pl->total = align_up(pl->off_carry + sz_carry);
+  if (pl->total < sz_ckpt + sz_scr + sz_red + sz_seg) return PRISM_ERR_INVALID_ARG;
   return PRISM_OK;
+}
+
+// the default segment length for the shape (0 when the shape is refused)
+int bwd_seg_len_for(int B, int H, int T, int dk) {
+  if (B <= 0 || H <= 0 || T <= 0 || !valid_dim(dk)) return 0;
+  return bwd_default_seg_len((size_t)B * (size_t)H, T, dk);
 }
 
 }  // namespace
@@ -278,12 +306,18 @@ extern "C" {
 
 size_t prism_bwd_workspace_bytes(int B, int H, int T, int dk, int dv, int L, prism_dtype dt) {
   BwdPlan pl;
-  return make_bwd_plan(B, H, T, dk, dv, L, dt, &pl) == PRISM_OK ? pl.total : 0;
+  const int len = bwd_seg_len_for(B, H, T, dk);
+  return len > 0 && make_bwd_plan(B, H, T, dk, dv, L, dt, len, &pl) == PRISM_OK ? pl.total : 0;
+}
+
+size_t prism_bwd_seg_workspace_bytes(int B, int H, int T, int dk, int dv, int L, prism_dtype dt, int seg_len) {
+  BwdPlan pl;
+  return seg_len > 0 && make_bwd_plan(B, H, T, dk, dv, L, dt, seg_len, &pl) == PRISM_OK ? pl.total : 0;
 }
 
 size_t prism_bwd_lowmem_workspace_bytes(int B, int H, int T, int dk, int dv, int L, prism_dtype dt) {
   BwdPlan pl;
-  return make_bwd_plan(B, H, T, dk, dv, L, dt, &pl, true) == PRISM_OK ? pl.total : 0;
+  return make_bwd_plan(B, H, T, dk, dv, L, dt, 0, &pl) == PRISM_OK ? pl.total : 0;
 }
 
 }  // extern "C"
@@ -296,9 +330,9 @@ prism_status bwd_impl(const void* q, const void* k, const void* v, const float* 
                       const void* d_o, const float* dS_final,
                       float* dq, float* dk_out, float* dv_out, float* dg, float* dbeta,
                       float* du, float* dalpha, float* dgamma, float* dconv_w,
-                      void* workspace, size_t workspace_bytes, hipStream_t stream, bool low_memory) {
+                      void* workspace, size_t workspace_bytes, hipStream_t stream, int seg_len) {
   BwdPlan pl;
-  prism_status st = make_bwd_plan(B, H, T, dk, dv, L, dt, &pl, low_memory);
+  prism_status st = make_bwd_plan(B, H, T, dk, dv, L, dt, seg_len, &pl);
   if (st != PRISM_OK) return st;
   if (!q || !k || !v || !g || !beta || !d_o || !dq || !dk_out || !dv_out || !dg || !dbeta)
     return PRISM_ERR_INVALID_ARG;
@@ -315,8 +349,17 @@ prism_status bwd_impl(const void* q, const void* k, const void* v, const float* 
   a.scratch = reinterpret_cast<float*>(ws + pl.off_scr);
   a.dconv_part = reinterpret_cast<float*>(ws + pl.off_part);
   a.part = reinterpret_cast<float*>(ws + pl.off_red);
-  a.H = H; a.T = T; a.L = L; a.nblk = pl.nblk; a.all_states = pl.all_states ? 1 : 0;
-  return prism::host::launch_bwd(dt, dk, a, B, pl.P, dconv_w, stream);
+  const size_t sq = (size_t)pl.P * pl.nseg * dk * dk;
+  float* sg = reinterpret_cast<float*>(ws + pl.off_seg);
+  a.seg_B = pl.segments ? sg : nullptr;
+  a.seg_Phi = pl.segments ? sg + sq : nullptr;
+  a.seg_ell = pl.segments ? sg + 2 * sq : nullptr;
+  a.seg_Sin = pl.segments ? sg + 3 * sq : nullptr;
+  a.seg_Lam = pl.segments ? sg + 4 * sq : nullptr;
+  a.carry = pl.segments ? reinterpret_cast<float*>(ws + pl.off_carry) : nullptr;
+  a.H = H; a.T = T; a.L = L; a.nblk = pl.nblk;
+  a.nseg = pl.nseg; a.seg_len = pl.seg_len;
+  return prism::host::launch_bwd(dt, dk, a, B, pl.P, dconv_w, pl.segments, stream);
 }
 
 }  // namespace
@@ -330,8 +373,22 @@ prism_status prism_bwd(const void* q, const void* k, const void* v, const float*
                        float* dq, float* dk_out, float* dv_out, float* dg, float* dbeta,
                        float* du, float* dalpha, float* dgamma, float* dconv_w,
                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const int len = bwd_seg_len_for(B, H, T, dk);
+  if (len == 0) return B <= 0 || H <= 0 || T <= 0 ? PRISM_ERR_INVALID_ARG : PRISM_ERR_UNSUPPORTED;
   return bwd_impl(q, k, v, g, beta, u, alpha, gamma, conv_w, B, H, T, dk, dv, L, dt, d_o, dS_final, dq, dk_out,
-                  dv_out, dg, dbeta, du, dalpha, dgamma, dconv_w, workspace, workspace_bytes, stream, false);
+                  dv_out, dg, dbeta, du, dalpha, dgamma, dconv_w, workspace, workspace_bytes, stream, len);
+}
+
+prism_status prism_bwd_seg(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                           const void* u, const float* alpha, const void* gamma, const float* conv_w,
+                           int B, int H, int T, int dk, int dv, int L, prism_dtype dt,
+                           const void* d_o, const float* dS_final,
+                           float* dq, float* dk_out, float* dv_out, float* dg, float* dbeta,
+                           float* du, float* dalpha, float* dgamma, float* dconv_w, int seg_len,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (seg_len <= 0) return PRISM_ERR_INVALID_ARG;
+  return bwd_impl(q, k, v, g, beta, u, alpha, gamma, conv_w, B, H, T, dk, dv, L, dt, d_o, dS_final, dq, dk_out,
+                  dv_out, dg, dbeta, du, dalpha, dgamma, dconv_w, workspace, workspace_bytes, stream, seg_len);
 }
 
 prism_status prism_bwd_lowmem(const void* q, const void* k, const void* v, const float* g, const float* beta,
@@ -342,7 +399,7 @@ prism_status prism_bwd_lowmem(const void* q, const void* k, const void* v, const
                               float* du, float* dalpha, float* dgamma, float* dconv_w,
                               void* workspace, size_t workspace_bytes, hipStream_t stream) {
   return bwd_impl(q, k, v, g, beta, u, alpha, gamma, conv_w, B, H, T, dk, dv, L, dt, d_o, dS_final, dq, dk_out,
-                  dv_out, dg, dbeta, du, dalpha, dgamma, dconv_w, workspace, workspace_bytes, stream, true);
+                  dv_out, dg, dbeta, du, dalpha, dgamma, dconv_w, workspace, workspace_bytes, stream, 0);
 }
 
 

@@ -14,24 +14,35 @@
 //   dv_t = beta e + (1 - w_3) dr_0 + later tokens' anchor terms;  du_{t,l} = dS_t^T W_{t,l}
 //   dg_t = <dS_t, S_{t-1}> - beta p.e;  dbeta_t = e.(v_t - g p)
 //   dW_{t,l} = dS_t u_{t,l}, then back through the residual chain to alpha, gamma, v, w
-//   dS_{t-1} = g (dS_t - beta e k_t^T)
+//   dS_{t-1} = g (dS_t - beta e k_t^T) = dS_t A_t      (A_t = g (I - beta k k^T) is symmetric)
 //
 // The rows of S and dS evolve independently (the recurrence acts on the right), so a
-// pair's D rows are split over D / 16 workgroups of 256 threads; thread (rb, cb) =
-// (tid / 16, tid % 16) of workgroup sp owns row 16 sp + rb and columns cb R .. (R = D / 16).
-// Sums over a row run through the 16 lanes of the thread's row group (DPP butterfly); sums
-// over a column through an LDS table with one slot per token of a group of KR tokens,
-// indexed by row block and reduced once per group (two barriers per group), then over the
-// workgroups of the pair in bwd_part_reduce_kernel.  Pass 1 runs the forward and keeps the state
-// entering every block of kBwdBlock tokens; pass 2 walks the blocks backwards, re-runs
-// each block's forward into a per-pair scratch (every thread reads back only what it
-// wrote itself) and then the adjoint steps of the block in reverse order.
+// state's D rows are split over NSP workgroups of 256 threads; thread (rb, cb) =
+// (tid / 16, tid % 16) of workgroup sp owns rows RW (16 sp + rb) .. + RW - 1 and columns
+// cb R .. (R = D / 16).  Sums over a row run through the 16 lanes of the thread's row
+// group (DPP butterfly); sums over a column through an LDS table with one slot per token
+// of a group of KR tokens, indexed by row block and reduced once per group (two barriers
+// per group), then, with NSP > 1, over the workgroups in bwd_part_reduce_kernel.
+//
+// Two organisations of the same per-token steps:
+//   * sequential (bwd_pair_kernel, the low-memory form): one state per pair walks the
+//     whole sequence; pass 1 keeps the state entering every block of kBwdBlock tokens,
+//     pass 2 walks the blocks backwards, re-runs each block's forward into a scratch and
+//     then the adjoint steps of the block in reverse order;
+//   * segment-parallel (bwd_seg_*): the sequence is cut into segments of seg_len tokens.
+//     Because both recurrences are affine in their carried matrix,
+//        S_end = S_in Phi_s + B_s,   Lambda_{s-1} = Lambda_s Phi_s^T + ell_s,
+//     with Phi_s = A_{t0} .. A_{t1-1} the segment operator (associativity of the
+//     recurrence: reading notes section 2.1; article section 01-二), one parallel pass
+//     forms (B_s, Phi_s, ell_s) per segment, two short scans give every segment its
+//     entering state S_in and the adjoint Lambda arriving at its last state, and a second
+//     parallel pass runs the token steps of every segment from those, exactly as the
+//     sequential form does; anchor terms that cross a segment start are added afterwards.
 #pragma once
 #include "prism_bwd_args.h"
 #include "prism_tile.h"
 
 namespace prism {
-
 
 // One token's inputs as seen by thread (rb, cb): key-side entries of its columns,
 // value-side entries of its rows (NR rank slots).
@@ -40,6 +51,13 @@ struct BwdTok {
   float k[R], q[R], u[NR][R];
   float v[RW], dO[RW], gm[NR][RW], vh[3][RW];  // vh: v_{t-3}, v_{t-2}, v_{t-1}
   float g, beta, al[NR + 1];
+};
+
+// The inputs of the adjoint's own recurrence: q, k of the thread's columns, d_o of its rows.
+template <int R, int RW>
+struct BwdAdjTok {
+  float k[R], q[R], dO[RW];
+  float g, beta;
 };
 
 // Sum over the 16 lanes of a row (DPP butterfly): swap neighbours, swap pairs, mirror
@@ -95,15 +113,53 @@ __device__ __forceinline__ void load_block(float (&M)[RW][R], const float* src) 
   }
 }
 
+// A thread's entries (rows row0 .., columns c0 ..) of a row-major D x D matrix.
+template <int D, int RW, int R>
+__device__ __forceinline__ void store_entries(float* dst, int row0, int c0, const float (&M)[RW][R]) {
+#pragma unroll
+  for (int r = 0; r < RW; ++r) {
+    float* p = dst + (size_t)(row0 + r) * D + c0;
+    if constexpr (R % 4 == 0) {
+#pragma unroll
+      for (int c = 0; c < R; c += 4) *reinterpret_cast<float4*>(p + c) = make_float4(M[r][c], M[r][c + 1], M[r][c + 2], M[r][c + 3]);
+    } else {
+#pragma unroll
+      for (int c = 0; c < R; ++c) p[c] = M[r][c];
+    }
+  }
+}
+
+template <int D, int RW, int R>
+__device__ __forceinline__ void load_entries(float (&M)[RW][R], const float* src, int row0, int c0) {
+#pragma unroll
+  for (int r = 0; r < RW; ++r) {
+    const float* p = src + (size_t)(row0 + r) * D + c0;
+    if constexpr (R % 4 == 0) {
+#pragma unroll
+      for (int c = 0; c < R; c += 4) {
+        const float4 x = *reinterpret_cast<const float4*>(p + c);
+        M[r][c] = x.x;
+        M[r][c + 1] = x.y;
+        M[r][c + 2] = x.z;
+        M[r][c + 3] = x.w;
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < R; ++c) M[r][c] = p[c];
+    }
+  }
+}
+
 // Sizes shared by the backward kernels: NR rank slots compiled in, NV column vectors
-// (dq, dk, du_l) and NS scalars (dg, dbeta, dalpha_l) per token; a pair's state rows are
-// split over NSP workgroups of 16 rows each.
-template <int D, int NRK>
+// (dq, dk, du_l) and NS scalars (dg, dbeta, dalpha_l) per token; a state's rows are split
+// over NSP workgroups of 16 RW rows each.
+template <int D, int NRK, int RW = 1>
 struct BwdShape {
   static constexpr int NR = NRK > 0 ? NRK : 1;
   static constexpr int NV = 2 + NR, NS = 3 + NR;
   static constexpr int RED = NV * D + NS;
-  static constexpr int NSP = D / 16;
+  static constexpr int NSP = D / (16 * RW);
+  static_assert(NSP >= 1 && NSP * 16 * RW == D, "rows per thread must divide the state");
 };
 
 // Writes one of a token's summed column entries / scalars (idx < RED) to its gradient.
@@ -175,40 +231,74 @@ constexpr int bwd_stage_tokens() {
   return 0;
 }
 
-// NRK: rank slots compiled in (0 for L = 1, 3 for L <= 4, 7 for L <= 8).  Every loop
-// over the token sequence is software-pipelined: the next token's inputs (and, in the
-// adjoint, its previous state) are loaded while the current token is processed, into
-// the other of two register buffers.
-template <class E, int D, int NRK>
-__global__ __launch_bounds__(256) void bwd_pair_kernel(BwdArgs a) {
-  using Sh = BwdShape<D, NRK>;
-  constexpr int R = D / 16, RW = 1, CK = kBwdBlock, NR = Sh::NR, NV = Sh::NV, NS = Sh::NS, RED = Sh::RED;
-  constexpr int NSP = Sh::NSP, SD = D * D / NSP;  // workgroups per pair, floats of a state slice
+// The segment-parallel kernels keep their LDS small, so that several workgroups share a
+// CU: the reduction table alone, two tokens per group when that stays within 48 KB.
+template <int D, int NR>
+constexpr int bwd_seg_red_group() { return 2 * bwd_red_slot_bytes<D, NR>() <= 48 * 1024 ? 2 : 1; }
+
+// Rows per thread of the segment-parallel kernels: one state per workgroup up to D = 64
+// (no cross-workgroup sums), two workgroups of four rows per thread at D = 128.
+template <int D>
+constexpr int bwd_seg_rows() { return 1; }
+
+// A thread's view of the backward: its rows and columns, the per-token steps (inputs,
+// residual chain, forward step, adjoint step) and the adjoint-side registers they carry.
+// NRK: rank slots compiled in (0 for L = 1, 3 for L <= 4, 7 for L <= 8).
+template <class E, int D, int NRK, int RW, int KR>
+struct BwdCore {
+  using Sh = BwdShape<D, NRK, RW>;
+  static constexpr int R = D / 16, NR = Sh::NR, NV = Sh::NV, NS = Sh::NS, RED = Sh::RED, NSP = Sh::NSP;
+  static constexpr int SD = D * D / NSP;  // floats of a workgroup's slice of a state
   using Tok = BwdTok<R, NR, RW>;
-  constexpr int KR = bwd_red_group<E, D, NR>();
-  __shared__ float red[KR][16][RED];  // [token of the group][row block][column sums, scalars]
-  const int tid = threadIdx.x;
-  const int rb = tid >> 4, cb = tid & 15;
-  const int pr = blockIdx.x / NSP, sp = blockIdx.x % NSP, hd = pr % a.H;
-  const int row0 = 16 * sp + rb;  // this thread's state row
-  const int T = a.T, L = a.L, Lm1 = L - 1;
-  const E* Q = reinterpret_cast<const E*>(a.q);
-  const E* K = reinterpret_cast<const E*>(a.k);
-  const E* V = reinterpret_cast<const E*>(a.v);
-  const E* U = reinterpret_cast<const E*>(a.u);
-  const E* GM = reinterpret_cast<const E*>(a.gamma);
-  const E* DO = reinterpret_cast<const E*>(a.d_o);
-  const float *Gg = a.g, *Gb = a.beta, *Ga = a.alpha;
-  float* ckpt = a.ckpt + ((size_t)pr * NSP + sp) * (a.all_states ? T : a.nblk) * SD;
-  float* scr = a.scratch + ((size_t)pr * NSP + sp) * CK * SD;
+  using AdjTok = BwdAdjTok<R, RW>;
 
-  float tw[4][RW];  // conv taps of this thread's rows
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-#pragma unroll
-    for (int r = 0; r < RW; ++r) tw[j][r] = L > 1 ? a.conv_w[((size_t)hd * 4 + j) * D + row0 + r] : 0.f;
+  const BwdArgs& a;
+  float (*red)[16][RED];  // the LDS reduction table, [KR][row block][column sums, scalars]
+  int tid, rb, cb, pr, sp, hd, row0, T, L, Lm1;
+  const E *Q, *K, *V, *U, *GM, *DO;
+  float tw[4][RW];               // conv taps of this thread's rows
+  float dS[RW][R], St[RW][R];    // dL/dS_t (carried backwards), S_t
+  float pend[3][RW], dw[4][RW];  // anchor terms owed to tokens t-1, t-2, t-3; dconv_w share
+  int ng, gfirst;  // tokens written into the reduction table, the group's first (last in time)
 
-  auto load_tok = [&](int t, Tok& x) __attribute__((always_inline)) {
+  __device__ __forceinline__ BwdCore(const BwdArgs& args, float (*table)[16][RED], int pair, int slice)
+      : a(args), red(table) {
+    tid = threadIdx.x;
+    rb = tid >> 4;
+    cb = tid & 15;
+    pr = pair;
+    sp = slice;
+    hd = pair % args.H;
+    row0 = RW * (16 * slice + rb);
+    T = args.T;
+    L = args.L;
+    Lm1 = L - 1;
+    Q = reinterpret_cast<const E*>(args.q);
+    K = reinterpret_cast<const E*>(args.k);
+    V = reinterpret_cast<const E*>(args.v);
+    U = reinterpret_cast<const E*>(args.u);
+    GM = reinterpret_cast<const E*>(args.gamma);
+    DO = reinterpret_cast<const E*>(args.d_o);
+#pragma unroll
+    for (int r = 0; r < RW; ++r) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        tw[j][r] = L > 1 ? args.conv_w[((size_t)hd * 4 + j) * D + row0 + r] : 0.f;
+        dw[j][r] = 0.f;
+      }
+#pragma unroll
+      for (int j = 0; j < 3; ++j) pend[j][r] = 0.f;
+#pragma unroll
+      for (int c = 0; c < R; ++c) {
+        dS[r][c] = 0.f;
+        St[r][c] = 0.f;
+      }
+    }
+    ng = 0;
+    gfirst = 0;
+  }
+
+  __device__ __forceinline__ void load_tok(int t, Tok& x) const {
     const size_t tr = (size_t)pr * T + t;
 #pragma unroll
     for (int c = 0; c < R; ++c) {
@@ -235,9 +325,23 @@ __global__ __launch_bounds__(256) void bwd_pair_kernel(BwdArgs a) {
     }
 #pragma unroll
     for (int l = 0; l <= NR; ++l) x.al[l] = (L > 1 && l < L) ? a.alpha[tr * L + l] : 0.f;
-  };
+  }
+
+  __device__ __forceinline__ void load_adj(int t, AdjTok& x) const {
+    const size_t tr = (size_t)pr * T + t;
+#pragma unroll
+    for (int c = 0; c < R; ++c) {
+      x.k[c] = (float)K[tr * D + cb * R + c];
+      x.q[c] = (float)Q[tr * D + cb * R + c];
+    }
+#pragma unroll
+    for (int r = 0; r < RW; ++r) x.dO[r] = (float)DO[tr * D + row0 + r];
+    x.g = a.g[tr];
+    x.beta = a.beta[tr];
+  }
+
   // residuals r_{t,0..L-1} and written values W_{t,1..L-1} of this thread's rows
-  auto chain = [&](const Tok& x, float (&rr)[NR + 1][RW], float (&W)[NR][RW]) __attribute__((always_inline)) {
+  __device__ __forceinline__ void chain(const Tok& x, float (&rr)[NR + 1][RW], float (&W)[NR][RW]) const {
 #pragma unroll
     for (int r = 0; r < RW; ++r)
       rr[0][r] = x.v[r] - (tw[0][r] * x.vh[0][r] + tw[1][r] * x.vh[1][r] + tw[2][r] * x.vh[2][r] + tw[3][r] * x.v[r]);
@@ -251,9 +355,10 @@ __global__ __launch_bounds__(256) void bwd_pair_kernel(BwdArgs a) {
         }
       }
     }
-  };
+  }
+
   // S_t from S_{t-1} (in place)
-  auto fwd_step = [&](float (&M)[RW][R], const Tok& x) __attribute__((always_inline)) {
+  __device__ __forceinline__ void fwd_step(float (&M)[RW][R], const Tok& x) const {
     float rr[NR + 1][RW], W[NR][RW];
     chain(x, rr, W);
     float p[RW];
@@ -274,15 +379,29 @@ __global__ __launch_bounds__(256) void bwd_pair_kernel(BwdArgs a) {
           if (l < Lm1) s += W[l][r] * x.u[l][c];
         M[r][c] = s;
       }
-  };
+  }
 
-  float dS[RW][R], St[RW][R];                   // dL/dS_t (carried backwards), S_t
-  float pend[3][RW], dw[4][RW];                 // anchor terms owed to tokens t, t-1, t-2; dconv_w share
-  int ng = 0, gfirst = 0;  // tokens written into the reduction table, the group's first (last in time)
-  // one adjoint step at token t from its inputs x and the state before it, Mp = S_{t-1}
+  // X <- X A_t = g (X - beta (X k) k^T): the step of a carried matrix with no write (the
+  // segment operator forwards, the adjoint backwards)
+  template <class X>
+  __device__ __forceinline__ void transition(float (&M)[RW][R], const X& x) const {
+    float p[RW];
+#pragma unroll
+    for (int r = 0; r < RW; ++r) {
+      p[r] = 0.f;
+#pragma unroll
+      for (int c = 0; c < R; ++c) p[r] += M[r][c] * x.k[c];
+    }
+    sum_row_group(p);
+#pragma unroll
+    for (int r = 0; r < RW; ++r)
+#pragma unroll
+      for (int c = 0; c < R; ++c) M[r][c] = x.g * (M[r][c] - x.beta * p[r] * x.k[c]);
+  }
+
   // the group's column sums and scalars, summed over the row blocks (tokens gfirst,
-  // gfirst - 1, ..), to the gradients or, with several workgroups per pair, to the partials
-  auto flush = [&]() __attribute__((always_inline)) {
+  // gfirst - 1, ..), to the gradients or, with several workgroups per state, to the partials
+  __device__ __forceinline__ void flush() {
     __syncthreads();
     for (int idx = tid; idx < ng * RED; idx += 256) {
       const int gi = idx / RED, e = idx - gi * RED, t = gfirst - gi;
@@ -294,8 +413,11 @@ __global__ __launch_bounds__(256) void bwd_pair_kernel(BwdArgs a) {
     }
     __syncthreads();
     ng = 0;
-  };
-  auto rev_step = [&](int t, const Tok& x, const float (&Mp)[RW][R]) __attribute__((always_inline)) {
+  }
+
+  // one adjoint step at token t from its inputs x and the state before it, Mp = S_{t-1};
+  // on entry dS holds the adjoint of S_t from the tokens after t and St holds S_t
+  __device__ __forceinline__ void rev_step(int t, const Tok& x, const float (&Mp)[RW][R]) {
     const size_t tr = (size_t)pr * T + t;
     float rr[NR + 1][RW], W[NR][RW];
     chain(x, rr, W);
@@ -417,22 +539,100 @@ __global__ __launch_bounds__(256) void bwd_pair_kernel(BwdArgs a) {
         St[r][c] = Mp[r][c];
       }
     if (++ng == KR) flush();
-  };
+  }
 
-  float Ma[RW][R], Mb[RW][R];
+  // The adjoint steps of tokens b1 - 1 down to b0, the states S_b0 .. S_{b1-2} read back
+  // from scr (S_t at scr + (t - b0) SD) and S_{b0-1} from cp; each thread reads back only
+  // what it wrote itself.  St must hold S_{b1-1}.  PIPE: software-pipelined (the next
+  // token's inputs and previous state are loaded while the current token is processed,
+  // into the other of two register buffers); otherwise one buffer, for kernels that rely
+  // on other resident waves to cover the loads.
+  template <bool PIPE>
+  __device__ __forceinline__ void rev_block(int b0, int b1, const float* scr, const float* cp) {
+    auto prev_state = [&](int t) __attribute__((always_inline)) { return t > b0 ? scr + (size_t)(t - 1 - b0) * SD : cp; };
+    if constexpr (PIPE) {
+      float Ma[RW][R], Mb[RW][R];
+      Tok xa, xb;
+      load_tok(b1 - 1, xa);
+      load_block(Ma, prev_state(b1 - 1));
+      for (int t = b1 - 1; t >= b0; t -= 2) {  // tokens t (buffers a) and t - 1 (buffers b)
+        if (t - 1 >= b0) {
+          load_tok(t - 1, xb);
+          load_block(Mb, prev_state(t - 1));
+        }
+        rev_step(t, xa, Ma);
+        if (t - 1 >= b0) {
+          if (t - 2 >= b0) {
+            load_tok(t - 2, xa);
+            load_block(Ma, prev_state(t - 2));
+          }
+          rev_step(t - 1, xb, Mb);
+        }
+      }
+    } else {
+      for (int t = b1 - 1; t >= b0; --t) {
+        float Mp[RW][R];
+        Tok x;
+        load_tok(t, x);
+        load_block(Mp, prev_state(t));
+        rev_step(t, x, Mp);
+      }
+    }
+    if (ng > 0) flush();
+  }
+
+  // The forward over tokens b0 .. b1 - 1 from M, each S_t stored at scr + (t - b0) SD
+  // (scr == nullptr: not stored); on return M = S_{b1-1}.  PIPE as for rev_block.
+  template <bool PIPE>
+  __device__ __forceinline__ void fwd_block(float (&M)[RW][R], int b0, int b1, float* scr) const {
+    if constexpr (PIPE) {
+      Tok xa, xb;
+      load_tok(b0, xa);
+      for (int t = b0; t < b1; t += 2) {  // tokens t (buffer a) and t + 1 (buffer b)
+        if (t + 1 < b1) load_tok(t + 1, xb);
+        fwd_step(M, xa);
+        if (scr) store_block(scr + (size_t)(t - b0) * SD, M);
+        if (t + 1 < b1) {
+          if (t + 2 < b1) load_tok(t + 2, xa);
+          fwd_step(M, xb);
+          if (scr) store_block(scr + (size_t)(t + 1 - b0) * SD, M);
+        }
+      }
+    } else {
+      for (int t = b0; t < b1; ++t) {
+        Tok x;
+        load_tok(t, x);
+        fwd_step(M, x);
+        if (scr) store_block(scr + (size_t)(t - b0) * SD, M);
+      }
+    }
+  }
+};
+
+// ======================= sequential form (one state per pair) ===========================
+// D / 16 workgroups per pair.  Every loop over the token sequence is software-pipelined.
+template <class E, int D, int NRK>
+__global__ __launch_bounds__(256) void bwd_pair_kernel(BwdArgs a) {
+  constexpr int NR = BwdShape<D, NRK>::NR;
+  constexpr int KR = bwd_red_group<E, D, NR>();
+  using Core = BwdCore<E, D, NRK, 1, KR>;
+  using Tok = typename Core::Tok;
+  constexpr int R = Core::R, RW = 1, CK = kBwdBlock, RED = Core::RED, NSP = Core::NSP, SD = Core::SD;
+  __shared__ float red[KR][16][RED];  // [token of the group][row block][column sums, scalars]
+  const int pr = blockIdx.x / NSP, sp = blockIdx.x % NSP;
+  Core c(a, red, pr, sp);
+  const int tid = c.tid, T = c.T, L = c.L, Lm1 = c.Lm1, row0 = c.row0, cb = c.cb;
+  float* ckpt = a.ckpt + ((size_t)pr * NSP + sp) * a.nblk * SD;
+  float* scr = a.scratch + ((size_t)pr * NSP + sp) * CK * SD;
+
   float M[RW][R];
 #pragma unroll
-  for (int r = 0; r < RW; ++r) {
+  for (int r = 0; r < RW; ++r)
 #pragma unroll
-    for (int c = 0; c < R; ++c) {
-      M[r][c] = 0.f;
-      dS[r][c] = a.dS_final != nullptr ? a.dS_final[(size_t)pr * D * D + (size_t)(cb * R + c) * D + row0 + r] : 0.f;
+    for (int cc = 0; cc < R; ++cc) {
+      M[r][cc] = 0.f;
+      c.dS[r][cc] = a.dS_final != nullptr ? a.dS_final[(size_t)pr * D * D + (size_t)(cb * R + cc) * D + row0 + r] : 0.f;
     }
-#pragma unroll
-    for (int j = 0; j < 3; ++j) pend[j][r] = 0.f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) dw[j][r] = 0.f;
-  }
   constexpr int NB = bwd_stage_tokens<E, D, NR>();
   if constexpr (NB > 0) {
     // ---- inputs staged through LDS, NB tokens at a time ---------------------------------
@@ -453,24 +653,24 @@ __global__ __launch_bounds__(256) void bwd_pair_kernel(BwdArgs a) {
     float pres = 0.f;
     // one array per loop (no pointer is chosen at run time)
     auto fetch = [&](int s0) __attribute__((always_inline)) {
-      const size_t row0 = (size_t)pr * T + s0;
-      stage_fetch_seg(pq, Q + row0 * D, nq, VEC, D, s0, T);
-      stage_fetch_seg(pk, K + row0 * D, nq, VEC, D, s0, T);
-      stage_fetch_seg(po, DO + row0 * D, nq, VEC, D, s0, T);
-      stage_fetch_seg(pv, V + row0 * D - 3 * D, nv, VEC, D, s0 - 3, T);
+      const size_t rw0 = (size_t)pr * T + s0;
+      stage_fetch_seg(pq, c.Q + rw0 * D, nq, VEC, D, s0, T);
+      stage_fetch_seg(pk, c.K + rw0 * D, nq, VEC, D, s0, T);
+      stage_fetch_seg(po, c.DO + rw0 * D, nq, VEC, D, s0, T);
+      stage_fetch_seg(pv, c.V + rw0 * D - 3 * D, nv, VEC, D, s0 - 3, T);
       if (Lm1 > 0) {
-        stage_fetch_seg(pu, U + row0 * Lm1 * D, nu, VEC, Lm1 * D, s0, T);
-        stage_fetch_seg(pg, GM + row0 * Lm1 * D, nu, VEC, Lm1 * D, s0, T);
+        stage_fetch_seg(pu, c.U + rw0 * Lm1 * D, nu, VEC, Lm1 * D, s0, T);
+        stage_fetch_seg(pg, c.GM + rw0 * Lm1 * D, nu, VEC, Lm1 * D, s0, T);
       }
       // scalars: g, beta (NB each), then alpha (NB x L)
       pres = 0.f;
       if (tid < NB * (2 + (L > 1 ? L : 0))) {
         const int tl = tid < 2 * NB ? tid % NB : (tid - 2 * NB) / L;
-        const size_t tr = row0 + tl;
+        const size_t tr = rw0 + tl;
         if (s0 + tl < T) {
-          if (tid < NB) pres = Gg[tr];
-          else if (tid < 2 * NB) pres = Gb[tr];
-          else pres = Ga[tr * L + (tid - 2 * NB) % L];
+          if (tid < NB) pres = a.g[tr];
+          else if (tid < 2 * NB) pres = a.beta[tr];
+          else pres = a.alpha[tr * L + (tid - 2 * NB) % L];
         }
       }
     };
@@ -490,9 +690,9 @@ __global__ __launch_bounds__(256) void bwd_pair_kernel(BwdArgs a) {
     auto load_tok_s = [&](int bs, int tl, Tok& x) __attribute__((always_inline)) {
       const E* b = stv[bs];
 #pragma unroll
-      for (int c = 0; c < R; ++c) {
-        x.q[c] = (float)b[tl * D + cb * R + c];
-        x.k[c] = (float)b[(NB + tl) * D + cb * R + c];
+      for (int cc = 0; cc < R; ++cc) {
+        x.q[cc] = (float)b[tl * D + cb * R + cc];
+        x.k[cc] = (float)b[(NB + tl) * D + cb * R + cc];
       }
 #pragma unroll
       for (int r = 0; r < RW; ++r) {
@@ -505,7 +705,7 @@ __global__ __launch_bounds__(256) void bwd_pair_kernel(BwdArgs a) {
       for (int l = 0; l < NR; ++l) {
         if (l < Lm1) {
 #pragma unroll
-          for (int c = 0; c < R; ++c) x.u[l][c] = (float)b[oU + (tl * Lm1 + l) * D + cb * R + c];
+          for (int cc = 0; cc < R; ++cc) x.u[l][cc] = (float)b[oU + (tl * Lm1 + l) * D + cb * R + cc];
 #pragma unroll
           for (int r = 0; r < RW; ++r) x.gm[l][r] = (float)b[oG + (tl * Lm1 + l) * D + row0 + r];
         }
@@ -516,10 +716,8 @@ __global__ __launch_bounds__(256) void bwd_pair_kernel(BwdArgs a) {
       for (int l = 0; l <= NR; ++l) x.al[l] = (L > 1 && l < L) ? sts[bs][2 * NB + tl * L + l] : 0.f;
     };
 
-    // ---- pass 1: the forward, keeping the state entering every block (or, with
-    // all_states, the state after every token) ----------------------------------------------
+    // ---- pass 1: the forward, keeping the state entering every block -------------------
     const int nst = (T + NB - 1) / NB;
-    const bool all = a.all_states != 0;
     int cur = 0;
     fetch(0);
     commit(0);
@@ -528,58 +726,15 @@ __global__ __launch_bounds__(256) void bwd_pair_kernel(BwdArgs a) {
       const int s0 = st * NB;
       if (st + 1 < nst) fetch(s0 + NB);
       for (int t = s0; t < min(T, s0 + NB); ++t) {
-        if (!all && t % CK == 0) store_block(ckpt + (size_t)(t / CK) * SD, M);
+        if (t % CK == 0) store_block(ckpt + (size_t)(t / CK) * SD, M);
         Tok x;
         load_tok_s(cur, t - s0, x);
-        fwd_step(M, x);
-        if (all) store_block(ckpt + (size_t)t * SD, M);
+        c.fwd_step(M, x);
       }
       if (st + 1 < nst) commit(cur ^ 1);
       __syncthreads();
       cur ^= 1;
     }
-    if (all) {
-      // ---- pass 2 with every S_t kept: the adjoint steps over the stages, last first -----
-#pragma unroll
-      for (int r = 0; r < RW; ++r)
-#pragma unroll
-        for (int c = 0; c < R; ++c) St[r][c] = M[r][c];
-      // S_{t-1}: the kept state, zero before the first token
-      auto prev_state = [&](float (&Mx)[RW][R], int t) __attribute__((always_inline)) {
-        if (t > 0) {
-          load_block(Mx, ckpt + (size_t)(t - 1) * SD);
-        } else {
-#pragma unroll
-          for (int r = 0; r < RW; ++r)
-#pragma unroll
-            for (int c = 0; c < R; ++c) Mx[r][c] = 0.f;
-        }
-      };
-      fetch((nst - 1) * NB);
-      commit(cur);
-      __syncthreads();
-      for (int st = nst - 1; st >= 0; --st) {
-        const int s0 = st * NB, s1 = min(T, s0 + NB);
-        if (st > 0) fetch(s0 - NB);
-        prev_state(Ma, s1 - 1);
-        for (int t = s1 - 1; t >= s0; t -= 2) {  // tokens t (Ma) and t - 1 (Mb)
-          if (t - 1 >= s0) prev_state(Mb, t - 1);
-          Tok x;
-          load_tok_s(cur, t - s0, x);
-          rev_step(t, x, Ma);
-          if (t - 1 >= s0) {
-            if (t - 2 >= s0) prev_state(Ma, t - 2);
-            Tok y;
-            load_tok_s(cur, t - 1 - s0, y);
-            rev_step(t - 1, y, Mb);
-          }
-        }
-        if (ng > 0) flush();
-        if (st > 0) commit(cur ^ 1);
-        __syncthreads();
-        cur ^= 1;
-      }
-    } else {
 
     // ---- pass 2: per block (last first) its stages ascending (the block's forward again,
     // keeping every S_t), then descending (the adjoint steps, last token first) -------------
@@ -589,6 +744,7 @@ __global__ __launch_bounds__(256) void bwd_pair_kernel(BwdArgs a) {
     fetch(blk * CK);
     commit(cur);
     __syncthreads();
+    float Ma[RW][R], Mb[RW][R];
     while (blk >= 0) {
       const int t0 = blk * CK, t1 = min(T, t0 + CK), s0 = t0 + j * NB, s1 = min(t1, s0 + NB);
       // the visit after this one
@@ -608,14 +764,14 @@ __global__ __launch_bounds__(256) void bwd_pair_kernel(BwdArgs a) {
         for (int t = s0; t < s1; ++t) {
           Tok x;
           load_tok_s(cur, t - s0, x);
-          fwd_step(M, x);
+          c.fwd_step(M, x);
           store_block(scr + (size_t)(t - t0) * SD, M);
         }
         if (s1 == t1) {
 #pragma unroll
           for (int r = 0; r < RW; ++r)
 #pragma unroll
-            for (int c = 0; c < R; ++c) St[r][c] = M[r][c];
+            for (int cc = 0; cc < R; ++cc) c.St[r][cc] = M[r][cc];
         }
       } else {
         const float* cp = ckpt + (size_t)blk * SD;
@@ -625,15 +781,15 @@ __global__ __launch_bounds__(256) void bwd_pair_kernel(BwdArgs a) {
           if (t - 1 >= s0) load_block(Mb, prev_state(t - 1));
           Tok x;
           load_tok_s(cur, t - s0, x);
-          rev_step(t, x, Ma);
+          c.rev_step(t, x, Ma);
           if (t - 1 >= s0) {
             if (t - 2 >= s0) load_block(Ma, prev_state(t - 2));
             Tok y;
             load_tok_s(cur, t - 1 - s0, y);
-            rev_step(t - 1, y, Mb);
+            c.rev_step(t - 1, y, Mb);
           }
         }
-        if (ng > 0) flush();
+        if (c.ng > 0) c.flush();
       }
       if (more) commit(cur ^ 1);
       __syncthreads();
@@ -642,79 +798,237 @@ __global__ __launch_bounds__(256) void bwd_pair_kernel(BwdArgs a) {
       j = nj;
       rev = nrev;
     }
-    }
   } else {
     // ---- inputs read straight from memory (shapes whose stages do not fit in LDS) ------
     // ---- pass 1: the forward, keeping the state entering every block -------------------
-    Tok xa, xb;
-    load_tok(0, xa);
-    for (int t = 0; t < T; t += 2) {  // tokens t (buffer a) and t + 1 (buffer b)
-      if (t % CK == 0) store_block(ckpt + (size_t)(t / CK) * SD, M);
-      if (t + 1 < T) load_tok(t + 1, xb);
-      fwd_step(M, xa);
-      if (t + 1 < T) {
-        if ((t + 1) % CK == 0) store_block(ckpt + (size_t)((t + 1) / CK) * SD, M);
-        if (t + 2 < T) load_tok(t + 2, xa);
-        fwd_step(M, xb);
-      }
+    for (int blk = 0; blk < a.nblk; ++blk) {
+      store_block(ckpt + (size_t)blk * SD, M);
+      if (blk + 1 < a.nblk) c.template fwd_block<true>(M, blk * CK, blk * CK + CK, nullptr);
     }
-
-    // ---- pass 2: blocks in reverse -------------------------------------------------------
+    // ---- pass 2: blocks in reverse: the block's forward again, keeping every S_t, then
+    // the adjoint steps, last token first ---------------------------------------------------
     for (int blk = a.nblk - 1; blk >= 0; --blk) {
       const int t0 = blk * CK, t1 = min(T, t0 + CK);
       const float* cp = ckpt + (size_t)blk * SD;
-      // the block's forward again, keeping every S_t
       load_block(M, cp);
-      load_tok(t0, xa);
-      for (int t = t0; t < t1; t += 2) {
-        if (t + 1 < t1) load_tok(t + 1, xb);
-        fwd_step(M, xa);
-        store_block(scr + (size_t)(t - t0) * SD, M);
-        if (t + 1 < t1) {
-          if (t + 2 < t1) load_tok(t + 2, xa);
-          fwd_step(M, xb);
-          store_block(scr + (size_t)(t + 1 - t0) * SD, M);
-        }
-      }
+      c.template fwd_block<true>(M, t0, t1, scr);
 #pragma unroll
       for (int r = 0; r < RW; ++r)
 #pragma unroll
-        for (int c = 0; c < R; ++c) St[r][c] = M[r][c];
-      // the adjoint steps, last token first (S_{t-1} is the block state t - 1 - t0, or the
-      // checkpoint for the first token)
-      auto prev_state = [&](int t) __attribute__((always_inline)) { return t > t0 ? scr + (size_t)(t - 1 - t0) * SD : cp; };
-      load_tok(t1 - 1, xa);
-      load_block(Ma, prev_state(t1 - 1));
-      for (int t = t1 - 1; t >= t0; t -= 2) {  // tokens t (buffers a) and t - 1 (buffers b)
-        if (t - 1 >= t0) {
-          load_tok(t - 1, xb);
-          load_block(Mb, prev_state(t - 1));
-        }
-        rev_step(t, xa, Ma);
-        if (t - 1 >= t0) {
-          if (t - 2 >= t0) {
-            load_tok(t - 2, xa);
-            load_block(Ma, prev_state(t - 2));
-          }
-          rev_step(t - 1, xb, Mb);
-        }
-      }
-      if (ng > 0) flush();
+        for (int cc = 0; cc < R; ++cc) c.St[r][cc] = M[r][cc];
+      c.template rev_block<true>(t0, t1, scr, cp);
     }
   }
   if (cb == 0 && L > 1) {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int r = 0; r < RW; ++r) a.dconv_part[((size_t)pr * 4 + j) * D + row0 + r] = dw[j][r];
+      for (int r = 0; r < RW; ++r) a.dconv_part[((size_t)pr * 4 + j) * D + row0 + r] = c.dw[j][r];
   }
 }
 
-// Column sums and scalars of a pair whose rows were split over NSP workgroups: the
+// ======================= segment-parallel form ==========================================
+// Workgroup wg of a segment launch: slice wg % NSP of segment (wg / NSP) % nseg of pair
+// wg / (NSP nseg).
+
+// Pass 1: per segment, from a zero state, the state at its end (B_s), the segment operator
+// Phi_s = A_{t0} .. A_{t1-1} (its rows evolve like the state's, with no write), and,
+// walking the segment backwards with a zero adjoint at its end, the adjoint ell_s at its
+// start (dS += d_o q^T, then dS <- dS A_t).  Only row sums are needed: no LDS.
+template <class E, int D, int NRK, int RW>
+__global__ __launch_bounds__(256) void bwd_seg_local_kernel(BwdArgs a) {
+  using Core = BwdCore<E, D, NRK, RW, 1>;
+  using Tok = typename Core::Tok;
+  using AdjTok = typename Core::AdjTok;
+  constexpr int R = Core::R, NSP = Core::NSP;
+  const int wg = blockIdx.x, sp = wg % NSP, seg = (wg / NSP) % a.nseg, pr = wg / (NSP * a.nseg);
+  Core c(a, nullptr, pr, sp);
+  const int t0 = seg * a.seg_len, t1 = min(c.T, t0 + a.seg_len), c0 = c.cb * R;
+  const size_t so = ((size_t)pr * a.nseg + seg) * D * D;
+  float M[RW][R], F[RW][R];
+#pragma unroll
+  for (int r = 0; r < RW; ++r)
+#pragma unroll
+    for (int cc = 0; cc < R; ++cc) {
+      M[r][cc] = 0.f;
+      F[r][cc] = c.row0 + r == c0 + cc ? 1.f : 0.f;
+    }
+  {
+    Tok xa, xb;
+    c.load_tok(t0, xa);
+    for (int t = t0; t < t1; t += 2) {  // tokens t (buffer a) and t + 1 (buffer b)
+      if (t + 1 < t1) c.load_tok(t + 1, xb);
+      c.transition(F, xa);
+      c.fwd_step(M, xa);
+      if (t + 1 < t1) {
+        if (t + 2 < t1) c.load_tok(t + 2, xa);
+        c.transition(F, xb);
+        c.fwd_step(M, xb);
+      }
+    }
+  }
+  store_entries<D>(a.seg_B + so, c.row0, c0, M);
+  store_entries<D>(a.seg_Phi + so, c.row0, c0, F);
+  // the local adjoint (M reused as dS)
+#pragma unroll
+  for (int r = 0; r < RW; ++r)
+#pragma unroll
+    for (int cc = 0; cc < R; ++cc) M[r][cc] = 0.f;
+  AdjTok ya, yb;
+  auto adj = [&](const AdjTok& y) __attribute__((always_inline)) {
+#pragma unroll
+    for (int r = 0; r < RW; ++r)
+#pragma unroll
+      for (int cc = 0; cc < R; ++cc) M[r][cc] += y.dO[r] * y.q[cc];
+    c.transition(M, y);
+  };
+  c.load_adj(t1 - 1, ya);
+  for (int t = t1 - 1; t >= t0; t -= 2) {  // tokens t (buffer a) and t - 1 (buffer b)
+    if (t - 1 >= t0) c.load_adj(t - 1, yb);
+    adj(ya);
+    if (t - 1 >= t0) {
+      if (t - 2 >= t0) c.load_adj(t - 2, ya);
+      adj(yb);
+    }
+  }
+  store_entries<D>(a.seg_ell + so, c.row0, c0, M);
+}
+
+// Pass 2: the two scans over a pair's segments, on rows r0 .. r0 + 3 of the carried matrix
+// (blockIdx.y), forwards (blockIdx.z = 0):
+//     S_in(0) = 0,  S_in(s + 1) = S_in(s) Phi_s + B_s
+// and backwards (blockIdx.z = 1):
+//     Lambda_{nseg-1} = dS_final (in S layout; zero if absent),  Lambda_{s-1} = Lambda_s Phi_s^T + ell_s.
+// Thread (j, ks) forms the partial products of output column j over the contraction slice
+// ks KD .. with its slice of Phi_s in registers (loaded one step ahead); the KS partials
+// meet in LDS.  Two barriers per step.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_seg_scan_kernel(BwdArgs a) {
+  constexpr int NROW = 4, KS = 256 / D, KD = D / KS;
+  __shared__ float sx[NROW][D];
+  __shared__ float spart[KS][NROW][D];
+  const int tid = threadIdx.x, j = tid % D, ks = tid / D;
+  const int pr = blockIdx.x, r0 = NROW * blockIdx.y;
+  const bool rev = blockIdx.z == 1;
+  const int nseg = a.nseg;
+  const size_t DD = (size_t)D * D, base = (size_t)pr * nseg * DD;
+  float* out = rev ? a.seg_Lam : a.seg_Sin;
+  const float* add = rev ? a.seg_ell : a.seg_B;
+  for (int e = tid; e < NROW * D; e += 256) {
+    const int r = e / D, jj = e % D;
+    sx[r][jj] = rev && a.dS_final != nullptr ? a.dS_final[(size_t)pr * DD + (size_t)jj * D + r0 + r] : 0.f;
+  }
+  float ph[2][KD];
+  auto load_phi = [&](int i, float (&dst)[KD]) __attribute__((always_inline)) {
+    const int s = rev ? nseg - 1 - i : i;
+    const float* P = a.seg_Phi + base + (size_t)s * DD;
+#pragma unroll
+    for (int m = 0; m < KD; ++m) {
+      const int k = ks * KD + m;
+      dst[m] = rev ? P[(size_t)j * D + k] : P[(size_t)k * D + j];
+    }
+  };
+  auto step = [&](int i, const float (&phi)[KD]) __attribute__((always_inline)) {
+    const int s = rev ? nseg - 1 - i : i;
+    for (int e = tid; e < NROW * D; e += 256) out[base + s * DD + (size_t)(r0 + e / D) * D + e % D] = sx[e / D][e % D];
+    float acc[NROW];
+#pragma unroll
+    for (int r = 0; r < NROW; ++r) {
+      acc[r] = 0.f;
+#pragma unroll
+      for (int m = 0; m < KD; ++m) acc[r] += sx[r][ks * KD + m] * phi[m];
+      spart[ks][r][j] = acc[r];
+    }
+    __syncthreads();
+    for (int e = tid; e < NROW * D; e += 256) {
+      const int r = e / D, jj = e % D;
+      float v = add[base + s * DD + (size_t)(r0 + r) * D + jj];
+#pragma unroll
+      for (int q = 0; q < KS; ++q) v += spart[q][r][jj];
+      sx[r][jj] = v;
+    }
+    __syncthreads();
+  };
+  __syncthreads();
+  if (nseg > 0) load_phi(0, ph[0]);
+  int i = 0;
+  for (; i + 2 <= nseg; i += 2) {
+    load_phi(i + 1, ph[1]);
+    step(i, ph[0]);
+    if (i + 2 < nseg) load_phi(i + 2, ph[0]);
+    step(i + 1, ph[1]);
+  }
+  if (i < nseg) step(i, ph[0]);
+}
+
+// Pass 3: the token steps of every segment, from its entering state S_in and the adjoint
+// Lambda of its last state: a forward over the segment keeping the state every kBwdSegSub
+// tokens, then per sub-block (last first) the sub-block's forward again into a per-workgroup
+// scratch and its adjoint steps.  The anchor terms the segment owes the three tokens before
+// it, and its dconv_w share, go to the workspace.
+template <class E, int D, int NRK, int RW>
+__global__ __launch_bounds__(256) void bwd_seg_kernel(BwdArgs a) {
+  constexpr int NR = BwdShape<D, NRK, RW>::NR;
+  constexpr int KR = bwd_seg_red_group<D, NR>();
+  using Core = BwdCore<E, D, NRK, RW, KR>;
+  constexpr int R = Core::R, NSP = Core::NSP, SD = Core::SD, RED = Core::RED, CK = kBwdSegSub;
+  __shared__ float red[KR][16][RED];
+  const int wg = blockIdx.x, sp = wg % NSP, seg = (wg / NSP) % a.nseg, pr = wg / (NSP * a.nseg);
+  Core c(a, red, pr, sp);
+  const int t0 = seg * a.seg_len, t1 = min(c.T, t0 + a.seg_len), c0 = c.cb * R;
+  const int nsub = (t1 - t0 + CK - 1) / CK;
+  float* ckpt = a.ckpt + (size_t)wg * (a.seg_len / CK) * SD;
+  float* scr = a.scratch + (size_t)wg * CK * SD;
+  const size_t so = ((size_t)pr * a.nseg + seg) * D * D;
+  float M[RW][R];
+  load_entries<D>(M, a.seg_Sin + so, c.row0, c0);
+  load_entries<D>(c.dS, a.seg_Lam + so, c.row0, c0);
+  // the states entering sub-blocks 0 .. nsub - 1
+  for (int b = 0; b < nsub; ++b) {
+    store_block(ckpt + (size_t)b * SD, M);
+    if (b + 1 < nsub) c.template fwd_block<false>(M, t0 + b * CK, t0 + b * CK + CK, nullptr);
+  }
+  for (int b = nsub - 1; b >= 0; --b) {
+    const int b0 = t0 + b * CK, b1 = min(t1, b0 + CK);
+    const float* cp = ckpt + (size_t)b * SD;
+    load_block(M, cp);
+    c.template fwd_block<false>(M, b0, b1, scr);
+#pragma unroll
+    for (int r = 0; r < RW; ++r)
+#pragma unroll
+      for (int cc = 0; cc < R; ++cc) c.St[r][cc] = M[r][cc];
+    c.template rev_block<false>(b0, b1, scr, cp);
+  }
+  if (c.cb == 0 && c.L > 1) {
+    const size_t ps = (size_t)pr * a.nseg + seg;
+#pragma unroll
+    for (int r = 0; r < RW; ++r) {
+#pragma unroll
+      for (int j = 0; j < 3; ++j) a.carry[(ps * 3 + j) * D + c.row0 + r] = c.pend[j][r];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) a.dconv_part[(ps * 4 + j) * D + c.row0 + r] = c.dw[j][r];
+    }
+  }
+}
+
+// Pass 4: the anchor terms that cross a segment start: segment s (s >= 1) owes tokens
+// t0 - 1, t0 - 2, t0 - 3 (all in earlier segments, which are at least 16 tokens long).
+__global__ __launch_bounds__(256) void bwd_seg_carry_kernel(BwdArgs a, int D) {
+  const int pr = blockIdx.x / a.nseg, seg = blockIdx.x % a.nseg;
+  if (seg == 0) return;
+  const int t0 = seg * a.seg_len;
+  const size_t ps = (size_t)pr * a.nseg + seg;
+  for (int e = threadIdx.x; e < 3 * D; e += 256) {
+    const int j = e / D, i = e % D, t = t0 - 1 - j;
+    a.dv[((size_t)pr * a.T + t) * D + i] += a.carry[(ps * 3 + j) * D + i];
+  }
+}
+
+// Column sums and scalars of a state whose rows were split over NSP workgroups: the
 // partials added in a fixed order (deterministic); 8 tokens per workgroup.
-template <int D, int NRK>
+template <int D, int NRK, int RW>
 __global__ __launch_bounds__(256) void bwd_part_reduce_kernel(BwdArgs a) {
-  using Sh = BwdShape<D, NRK>;
+  using Sh = BwdShape<D, NRK, RW>;
   const int T = a.T, nt8 = (T + 7) / 8;
   const int pr = blockIdx.x / nt8, t8 = blockIdx.x % nt8;
   for (int tl = 0; tl < 8; ++tl) {
@@ -728,12 +1042,15 @@ __global__ __launch_bounds__(256) void bwd_part_reduce_kernel(BwdArgs a) {
   }
 }
 
-// dconv_w[h] = sum over the batch of the pairs' shares (fixed order: deterministic).
-__global__ __launch_bounds__(256) void bwd_conv_reduce_kernel(const float* part, float* dconv_w, int B, int H, int D) {
+// dconv_w[h] = sum over the batch and the nseg shares of each pair (fixed order:
+// deterministic); shares laid out [B][H][nseg][4][D].
+__global__ __launch_bounds__(256) void bwd_conv_reduce_kernel(const float* part, float* dconv_w, int B, int H, int D,
+                                                              int nseg) {
   const int h = blockIdx.x;
   for (int i = threadIdx.x; i < 4 * D; i += 256) {
     float s = 0.f;
-    for (int b = 0; b < B; ++b) s += part[((size_t)b * H + h) * 4 * D + i];
+    for (int b = 0; b < B; ++b)
+      for (int sg = 0; sg < nseg; ++sg) s += part[(((size_t)b * H + h) * nseg + sg) * 4 * D + i];
     dconv_w[(size_t)h * 4 * D + i] = s;
   }
 }

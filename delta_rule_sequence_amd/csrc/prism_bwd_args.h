@@ -4,19 +4,27 @@
 
 namespace prism {
 
-constexpr int kBwdBlock = 64;  // tokens between state checkpoints
+constexpr int kBwdBlock = 64;   // tokens between state checkpoints of the sequential backward
+constexpr int kBwdSegSub = 8;   // tokens between state checkpoints inside a segment
 
 struct BwdArgs {
   const void *q, *k, *v, *u, *gamma, *d_o;
   const float *g, *beta, *alpha, *conv_w, *dS_final;
   float *dq, *dk, *dv, *dg, *dbeta, *du, *dalpha, *dgamma;
-  float* dconv_part;  // [P][4][D] this pair's share of dconv_w
-  float* ckpt;        // [P][nblk][D * D] state entering each block (thread-block order), or
-                      // with all_states: [P][T][D * D] the state after every token
-  float* scratch;     // [P][kBwdBlock][D * D] states S_t of the block being reversed
+  float* dconv_part;  // [P][nseg][4][D] dconv_w shares (nseg = 1 for the sequential kernel)
+  float* ckpt;        // sequential: [P][NSP][nblk][D * D / NSP] state entering each block;
+                      // segments: [P][nseg][NSP][seg_len / kBwdSegSub][..] per sub-block
+  float* scratch;     // [..][block tokens][D * D / NSP] states S_t of the block being reversed
   float* part;        // [P][NSP][T][RED] per-workgroup column sums and scalars (NSP > 1)
+  // segment-parallel form only, float32 [P][nseg][D][D] in S layout (row = value index):
+  float* seg_B;    // state at the segment end from a zero start
+  float* seg_Phi;  // segment operator A_{t0} .. A_{t1-1}
+  float* seg_ell;  // adjoint at the segment start from the segment's own outputs
+  float* seg_Sin;  // state entering the segment
+  float* seg_Lam;  // adjoint of the segment's last state from the tokens after it
+  float* carry;    // [P][nseg][3][D] anchor terms a segment owes the three tokens before it
   int H, T, L, nblk;
-  int all_states;  // 1: keep every S_t (one forward sweep fewer); only with LDS staging
+  int nseg, seg_len;
 };
 
 }  // namespace prism

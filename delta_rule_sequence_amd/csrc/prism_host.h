@@ -57,11 +57,12 @@ void launch_sweep8_linear(const FwdArgs& a, dim3 grid, hipStream_t stream);
 void launch_sweep8_nl(const FwdArgs& a, dim3 grid, hipStream_t stream);
 void launch_sweep8_delta(const FwdArgs& a, dim3 grid, hipStream_t stream);
 
-// The backward (prism_bwd.h).  bwd_staged: whether the adjoint sweep of this shape stages
-// its inputs through LDS (the all-states workspace needs it).  launch_bwd: the sweep, the
+// The backward (prism_bwd.h).  launch_bwd: with segments the segment-parallel passes
+// (a.nseg segments of a.seg_len tokens), otherwise the sequential per-pair sweep; then the
 // partial sums and, for L > 1, the batch sum of the conv-weight gradient into dconv_w.
-bool bwd_staged(prism_dtype dt, int d, int L);
-prism_status launch_bwd(prism_dtype dt, int d, const BwdArgs& a, int B, int P, float* dconv_w,
+// bwd_seg_slices: workgroups per state of the segment-parallel passes at head dim d.
+int bwd_seg_slices(int d);
+prism_status launch_bwd(prism_dtype dt, int d, const BwdArgs& a, int B, int P, float* dconv_w, bool segments,
                         hipStream_t stream);
 
 // Nonlinear refinement (prism_nl.h, nl.hip).  launch_gain: the chain factors from given

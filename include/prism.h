@@ -187,9 +187,13 @@ prism_status prism_fwd_timed(const void* q, const void* k, const void* v,
 /* The backward pass: gradients of  sum_t <d_o_t, o_t> + <dS_final, S_final>  with respect
  * to every input of prism_fwd (S_0 = 0, no ShortConv history), i.e. the reverse-mode
  * derivative that end-to-end training of the layer needs (the pages quote training
- * throughput: "PRISM" reading notes, section 3.3).  Token by token in float32, dk / 16
- * workgroups per (b, h) pair (16 state rows each): the forward is re-run keeping its
- * states, then the adjoint steps run last token first.
+ * throughput: "PRISM" reading notes, section 3.3).  Float32 throughout.  Segment-parallel:
+ * the sequence is cut into segments; since the state and its adjoint are affine in what
+ * they carry (the associativity of the recurrence, reading notes section 2.1, Tencent /
+ * PKU article section 01-二), one pass forms each segment's end state from zero, its
+ * operator A_{t0} .. A_{t1-1} and its own adjoint contribution, two scans give every
+ * segment its entering state and the adjoint arriving at its end, and a second pass runs
+ * the token-by-token adjoint of all segments at once.
  *   inputs    q .. conv_w, B, H, T, dk, dv, L, dt exactly as prism_fwd
  *   d_o       [B, H, T, dv] dtype dt: gradient of o
  *   dS_final  [B, H, dk, dv] float32: gradient of S_final; NULL = zero
@@ -199,13 +203,12 @@ prism_status prism_fwd_timed(const void* q, const void* k, const void* v,
  *   dconv_w [H, 4, dv] (summed over the batch)
  * The four rank-L gradients are not written when L == 1 (they may be NULL then) and
  * are required otherwise.  Supported: dk == dv in {16, 32, 64, 128}, 1 <= L <= 8,
- * B * H <= 2^31 - 1.  Workspace: prism_bwd_workspace_bytes.  When every per-token state
- * fits in 4 GiB (B*H*T*dk*dv*4 bytes) the workspace keeps all of them and the forward is
- * re-run once; otherwise it keeps the state every 64 tokens plus a 64-token buffer per pair
- * and re-runs each 64-token block (one more forward sweep).  With dk > 16 it also holds
- * each workgroup's per-token column sums, B*H * (dk/16) * T * ((2+R)*dk + 3 + R) floats
- * (R = 1, 3 or 7 rank slots for L = 1, L <= 4, L <= 8), added in a fixed order by a second
- * kernel.  Ownership, stream and errors as prism_fwd. */
+ * B * H <= 2^31 - 1.  Results are deterministic (fixed summation orders).  Workspace:
+ * prism_bwd_workspace_bytes; it holds five float32 dk x dk matrices per segment, the
+ * state every 8 tokens plus an 8-token state buffer per segment, per-segment dconv_w and
+ * anchor shares, and, with dk = 128 (two workgroups per state), their per-token column
+ * sums.  The segment length is chosen from the shape (16 to 128 tokens).  Ownership,
+ * stream and errors as prism_fwd. */
 size_t prism_bwd_workspace_bytes(int B, int H, int T, int dk, int dv, int L, prism_dtype dt);
 prism_status prism_bwd(const void* q, const void* k, const void* v,
                        const float* g, const float* beta,
@@ -217,10 +220,30 @@ prism_status prism_bwd(const void* q, const void* k, const void* v,
                        float* du, float* dalpha, float* dgamma, float* dconv_w,
                        void* workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* The same gradients with the low-memory workspace whatever the size: the state every 64
- * tokens plus a 64-token buffer per pair (O(T / 64) states instead of O(T)), at the cost
- * of one more sequential forward sweep.  For callers with little free device memory.
- * Arguments, layouts and errors as prism_bwd; workspace: prism_bwd_lowmem_workspace_bytes. */
+/* prism_bwd with the segment length given: seg_len tokens per segment (a multiple of 8,
+ * at least 16; the last segment may be shorter), else PRISM_ERR_INVALID_ARG.  The
+ * gradients do not depend on it beyond float32 rounding; for callers that tune it and for
+ * tests that reach every segment case.  Workspace: prism_bwd_seg_workspace_bytes (0 for a
+ * refused shape or length). */
+size_t prism_bwd_seg_workspace_bytes(int B, int H, int T, int dk, int dv, int L, prism_dtype dt, int seg_len);
+prism_status prism_bwd_seg(const void* q, const void* k, const void* v,
+                           const float* g, const float* beta,
+                           const void* u, const float* alpha, const void* gamma,
+                           const float* conv_w,
+                           int B, int H, int T, int dk, int dv, int L, prism_dtype dt,
+                           const void* d_o, const float* dS_final,
+                           float* dq, float* dk_out, float* dv_out, float* dg, float* dbeta,
+                           float* du, float* dalpha, float* dgamma, float* dconv_w, int seg_len,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* The same gradients with a workspace of O(T / 64) states per pair: one pair's state walks
+ * the whole sequence on dk / 16 workgroups (the forward once keeping the state every 64
+ * tokens, then per 64-token block, last first, the block's forward again and its adjoint
+ * steps).  Much slower than prism_bwd on long sequences; for callers with little free
+ * device memory.  With dk > 16 the workspace also holds each workgroup's per-token column
+ * sums, B*H * (dk/16) * T * ((2+R)*dk + 3 + R) floats (R = 1, 3 or 7 rank slots for
+ * L = 1, L <= 4, L <= 8).  Arguments, layouts and errors as prism_bwd; workspace:
+ * prism_bwd_lowmem_workspace_bytes. */
 size_t prism_bwd_lowmem_workspace_bytes(int B, int H, int T, int dk, int dv, int L, prism_dtype dt);
 prism_status prism_bwd_lowmem(const void* q, const void* k, const void* v,
                               const float* g, const float* beta,

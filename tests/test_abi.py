@@ -214,9 +214,35 @@ def test_bwd_argument_checks(lib):
     # the low-memory form keeps one state per 64 tokens: one more once T passes a multiple of 64
     low = lib.prism_bwd_lowmem_workspace_bytes(1, 1, 64, 16, 16, 2, 1)
     assert 0 < low and lib.prism_bwd_lowmem_workspace_bytes(1, 1, 65, 16, 16, 2, 1) > low
-    # the default keeps every per-token state while they fit: it grows with T
+    # the segment-parallel default holds per-segment matrices: one more segment once T
+    # passes a multiple of the segment length (16 tokens at this size)
     assert lib.prism_bwd_workspace_bytes(1, 1, 65, 16, 16, 2, 1) > need
     assert lib.prism_bwd_workspace_bytes(1, 1, 4096, 64, 64, 4, 1) > lib.prism_bwd_lowmem_workspace_bytes(1, 1, 4096, 64, 64, 4, 1)
+
+
+def _bwd_seg_call(lib, seg_len, T=64, d=16, L=2, ws_bytes=1 << 30):
+    p = ctypes.c_void_p(1)
+    return lib.prism_bwd_seg(p, p, p, p, p, p, p, p, p, 1, 1, T, d, d, L, 1, p, None,
+                             p, p, p, p, p, p, p, p, p, seg_len, p, ws_bytes, None)
+
+
+@pytest.mark.parametrize("seg_len", [0, -8, 8, 12, 20, 33])
+def test_bwd_seg_refuses_bad_segment_length(lib, seg_len):
+    """Segments are a multiple of the 8-token checkpoint spacing and at least 16 tokens (so
+    that the anchor terms a segment owes reach only the segment before it)."""
+    assert lib.prism_bwd_seg_workspace_bytes(1, 1, 64, 16, 16, 2, 1, seg_len) == 0
+    assert _bwd_seg_call(lib, seg_len) == INVALID
+
+
+def test_bwd_seg_workspace(lib):
+    a = lib.prism_bwd_seg_workspace_bytes(1, 1, 64, 16, 16, 2, 1, 16)
+    b = lib.prism_bwd_seg_workspace_bytes(1, 1, 64, 16, 16, 2, 1, 32)
+    assert a > 0 and b > 0
+    # five 16 x 16 float32 matrices per segment: four segments against two
+    assert a - b >= 2 * 5 * 16 * 16 * 4
+    assert _bwd_seg_call(lib, 16, ws_bytes=a - 1) == WORKSPACE
+    assert lib.prism_bwd_seg_workspace_bytes(1, 1, 64, 16, 32, 2, 1, 16) == 0
+    assert lib.prism_bwd_seg_workspace_bytes(1, 1, 64, 48, 48, 2, 1, 16) == 0
 
 
 def _nl_gain_call(lib, B=1, H=1, T=64, dv=16, L=3, dt=1, null=()):

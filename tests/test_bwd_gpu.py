@@ -2,9 +2,12 @@
 gradient oracle (oracle/prism_grad.py: autograd through the token recurrence, pinned
 by finite differences of the numpy forward).
 
-Every gradient is compared as max |x - x_ref| / max |x_ref| <= 1e-4: the kernel
-computes in float32 from the same (bf16-rounded, for bf16 inputs) input values the
-oracle reads, so the float32 bar applies to both input dtypes.
+Every gradient is compared as max |x - x_ref| / max |x_ref| <= 1e-4: the kernels
+compute in float32 from the same (bf16-rounded, for bf16 inputs) input values the
+oracle reads, so the float32 bar applies to both input dtypes.  Both organisations are
+covered: the segment-parallel default (prism_bwd; with prism_bwd_seg for chosen segment
+lengths, ragged last segments and segments that span several 8-token sub-blocks) and the
+sequential low-memory form (prism_bwd_lowmem).
 """
 import numpy as np
 import pytest
@@ -41,23 +44,33 @@ def _setup(dtype, B, H, T, d, L, with_dS, seed):
     return w, x, d_o, dS
 
 
-@pytest.mark.parametrize("low_memory", [False, True], ids=["all_states", "lowmem"])
-@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
-def test_bwd_matches_oracle(case, low_memory):
-    if not gpu_available():
-        pytest.skip("no GPU")
+# segment-parallel cases with a chosen segment length: name, dtype, B, H, T, d, L, with
+# dS_final, seg_len (several segments, a ragged last one, segments of 2-16 sub-blocks,
+# rows split over workgroups at d = 128)
+SEG_CASES = [
+    ("bf16_d64_L4_T200_s16", "bf16", 1, 2, 200, 64, 4, True, 16),
+    ("f32_d32_L3_T130_s24", "f32", 2, 2, 130, 32, 3, False, 24),
+    ("f32_d16_L8_T97_s16", "f32", 1, 1, 97, 16, 8, True, 16),
+    ("f32_d64_L1_T100_s32", "f32", 1, 2, 100, 64, 1, True, 32),
+    ("bf16_d128_L8_T70_s16", "bf16", 1, 1, 70, 128, 8, True, 16),
+    ("bf16_d128_L2_T300_s64", "bf16", 1, 1, 300, 128, 2, False, 64),
+    ("bf16_d64_L4_T1000_s128", "bf16", 1, 1, 1000, 64, 4, True, 128),
+    ("f32_d32_L5_T40_s40", "f32", 1, 1, 40, 32, 5, True, 40),
+]
+
+
+def _check_against_oracle(name, dtype, B, H, T, d, L, with_dS, **kw):
     import torch
     import delta_rule_sequence_amd as prism
     import workloads
     from oracle import prism_grad
-    name, dtype, B, H, T, d, L, with_dS = case
-    print(f"[bwd] {name} low_memory={low_memory}", flush=True)
+    print(f"[bwd] {name} {kw}", flush=True)
     w, x, d_o, dS = _setup(dtype, B, H, T, d, L, with_dS, seed=len(name) + T)
     dev = workloads.to_torch(x, dtype, "cuda")
     vt = torch.bfloat16 if dtype == "bf16" else torch.float32
     got = prism.bwd(dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], dev["u"], dev["alpha"], dev["gamma"],
                     dev["conv_w"], L=L, d_o=torch.tensor(d_o, device="cuda").to(vt),
-                    dS_final=None if dS is None else torch.tensor(dS, device="cuda"), low_memory=low_memory)
+                    dS_final=None if dS is None else torch.tensor(dS, device="cuda"), **kw)
     torch.cuda.synchronize()
     ref = prism_grad.backward(x["q"], x["k"], x["v"], x["g"], x["beta"], x["u"], x["alpha"], x["gamma"],
                               x["conv_w"], L, d_o, dS)
@@ -72,6 +85,21 @@ def test_bwd_matches_oracle(case, low_memory):
     print(f"[bwd] {name} rel errors " + " ".join(f"{n}={e:.1e}" for n, e in errs.items()), flush=True)
     bad = {n: e for n, e in errs.items() if not e <= TOL}
     assert not bad, bad
+
+
+@pytest.mark.parametrize("low_memory", [False, True], ids=["segments", "lowmem"])
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_bwd_matches_oracle(case, low_memory):
+    if not gpu_available():
+        pytest.skip("no GPU")
+    _check_against_oracle(*case, low_memory=low_memory)
+
+
+@pytest.mark.parametrize("case", SEG_CASES, ids=[c[0] for c in SEG_CASES])
+def test_bwd_seg_matches_oracle(case):
+    if not gpu_available():
+        pytest.skip("no GPU")
+    _check_against_oracle(*case[:-1], seg_len=case[-1])
 
 
 def test_bwd_deterministic():
