@@ -236,10 +236,12 @@ constexpr int bwd_stage_tokens() {
 template <int D, int NR>
 constexpr int bwd_seg_red_group() { return 2 * bwd_red_slot_bytes<D, NR>() <= 48 * 1024 ? 2 : 1; }
 
-// Rows per thread of the segment-parallel kernels: one state per workgroup up to D = 64
-// (no cross-workgroup sums), two workgroups of four rows per thread at D = 128.
+// Rows per thread of the segment-parallel kernels: two from D = 32 up (the per-token
+// loads, column-side products and reductions of a thread then serve two rows; measured at
+// the 16K workload, d = 64: 7.7 -> 5.5 ms per backward against one row; four rows exceed
+// 256 VGPRs), so D / 32 workgroups per state.
 template <int D>
-constexpr int bwd_seg_rows() { return 1; }
+constexpr int bwd_seg_rows() { return D >= 32 ? 2 : 1; }
 
 // A thread's view of the backward: its rows and columns, the per-token steps (inputs,
 // residual chain, forward step, adjoint step) and the adjoint-side registers they carry.
@@ -524,8 +526,9 @@ struct BwdCore {
     for (int n = 0; n < NV; ++n)
 #pragma unroll
       for (int c = 0; c < R; ++c) red[ng][rb][n * D + cb * R + c] = y[n][c];
-#pragma unroll
-    for (int s = 0; s < NS; ++s) sc[s] = row16_sum(sc[s]);
+    // sc[0] has a share in every lane of the row; the others are per-row terms that only
+    // lane cb = 0 formed
+    sc[0] = row16_sum(sc[0]);
     if (cb == 0) {
 #pragma unroll
       for (int s = 0; s < NS; ++s) red[ng][rb][NV * D + s] = sc[s];

@@ -206,7 +206,7 @@ prism_status prism_fwd_timed(const void* q, const void* k, const void* v,
  * B * H <= 2^31 - 1.  Results are deterministic (fixed summation orders).  Workspace:
  * prism_bwd_workspace_bytes; it holds five float32 dk x dk matrices per segment, the
  * state every 8 tokens plus an 8-token state buffer per segment, per-segment dconv_w and
- * anchor shares, and, with dk = 128 (two workgroups per state), their per-token column
+ * anchor shares, and, with dk >= 64 (dk / 32 workgroups per state), their per-token column
  * sums.  The segment length is chosen from the shape (16 to 128 tokens).  Ownership,
  * stream and errors as prism_fwd. */
 size_t prism_bwd_workspace_bytes(int B, int H, int T, int dk, int dv, int L, prism_dtype dt);
