@@ -453,7 +453,8 @@ def time_bwd(w, x, d_o, steps, warmup):
     return {"ms_per_step": ms, "tokens_per_s": w.B * w.T / (ms * 1e-3),
             "roofline": {"bound": "hbm", "bytes_per_token_head": per_th, "bytes_per_call": total,
                          "achieved": total / (ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": total / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "kernel": "bwd_pair_kernel"}}
+                         "frac": total / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                         "scope": "whole prism_bwd call (segment-parallel: local pass, scans, token steps, sums)"}}
 
 
 def time_nl(w, steps, warmup, x0=None):

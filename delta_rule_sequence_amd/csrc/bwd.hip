@@ -81,7 +81,7 @@ prism_status launch_bwd(prism_dtype dt, int d, const BwdArgs& a, int B, int P, f
   }
   if (hipGetLastError() != hipSuccess) return PRISM_ERR_HIP;
   if (a.L == 1) return PRISM_OK;
-  hipLaunchKernelGGL(bwd_conv_reduce_kernel, dim3(a.H), dim3(256), 0, stream,
+  hipLaunchKernelGGL(bwd_conv_reduce_kernel, dim3(a.H, (4 * d + 63) / 64), dim3(256), 0, stream,
                      static_cast<const float*>(a.dconv_part), dconv_w, B, a.H, d, segments ? a.nseg : 1);
   return hipGetLastError() == hipSuccess ? PRISM_OK : PRISM_ERR_HIP;
 }

@@ -903,11 +903,12 @@ __global__ __launch_bounds__(256) void bwd_seg_local_kernel(BwdArgs a) {
 // and backwards (blockIdx.z = 1):
 //     Lambda_{nseg-1} = dS_final (in S layout; zero if absent),  Lambda_{s-1} = Lambda_s Phi_s^T + ell_s.
 // Thread (j, ks) forms the partial products of output column j over the contraction slice
-// ks KD .. with its slice of Phi_s in registers (loaded one step ahead); the KS partials
-// meet in LDS.  Two barriers per step.
+// ks KD .. with its slice of Phi_s in registers; the KS partials meet in LDS.  The operator
+// slice and the added term of the next step are loaded while the current step runs, so a
+// step waits on no memory.  Two barriers per step.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_seg_scan_kernel(BwdArgs a) {
-  constexpr int NROW = 4, KS = 256 / D, KD = D / KS;
+  constexpr int NROW = 4, KS = 256 / D, KD = D / KS, NE = (NROW * D + 255) / 256;
   __shared__ float sx[NROW][D];
   __shared__ float spart[KS][NROW][D];
   const int tid = threadIdx.x, j = tid % D, ks = tid / D;
@@ -921,8 +922,9 @@ __global__ __launch_bounds__(256) void bwd_seg_scan_kernel(BwdArgs a) {
     const int r = e / D, jj = e % D;
     sx[r][jj] = rev && a.dS_final != nullptr ? a.dS_final[(size_t)pr * DD + (size_t)jj * D + r0 + r] : 0.f;
   }
-  float ph[2][KD];
-  auto load_phi = [&](int i, float (&dst)[KD]) __attribute__((always_inline)) {
+  float ph[2][KD], ad[2][NE];
+  // step i's operator slice and added entries (element e = tid + 256 n of the 4 x D rows)
+  auto fetch = [&](int i, float (&dst)[KD], float (&da)[NE]) __attribute__((always_inline)) {
     const int s = rev ? nseg - 1 - i : i;
     const float* P = a.seg_Phi + base + (size_t)s * DD;
 #pragma unroll
@@ -930,38 +932,50 @@ __global__ __launch_bounds__(256) void bwd_seg_scan_kernel(BwdArgs a) {
       const int k = ks * KD + m;
       dst[m] = rev ? P[(size_t)j * D + k] : P[(size_t)k * D + j];
     }
+#pragma unroll
+    for (int n = 0; n < NE; ++n) {
+      const int e = tid + 256 * n;
+      da[n] = e < NROW * D ? add[base + (size_t)s * DD + (size_t)(r0 + e / D) * D + e % D] : 0.f;
+    }
   };
-  auto step = [&](int i, const float (&phi)[KD]) __attribute__((always_inline)) {
+  auto step = [&](int i, const float (&phi)[KD], const float (&da)[NE]) __attribute__((always_inline)) {
     const int s = rev ? nseg - 1 - i : i;
-    for (int e = tid; e < NROW * D; e += 256) out[base + s * DD + (size_t)(r0 + e / D) * D + e % D] = sx[e / D][e % D];
-    float acc[NROW];
+#pragma unroll
+    for (int n = 0; n < NE; ++n) {
+      const int e = tid + 256 * n;
+      if (e < NROW * D) out[base + (size_t)s * DD + (size_t)(r0 + e / D) * D + e % D] = sx[e / D][e % D];
+    }
 #pragma unroll
     for (int r = 0; r < NROW; ++r) {
-      acc[r] = 0.f;
+      float acc = 0.f;
 #pragma unroll
-      for (int m = 0; m < KD; ++m) acc[r] += sx[r][ks * KD + m] * phi[m];
-      spart[ks][r][j] = acc[r];
+      for (int m = 0; m < KD; ++m) acc += sx[r][ks * KD + m] * phi[m];
+      spart[ks][r][j] = acc;
     }
     __syncthreads();
-    for (int e = tid; e < NROW * D; e += 256) {
-      const int r = e / D, jj = e % D;
-      float v = add[base + s * DD + (size_t)(r0 + r) * D + jj];
 #pragma unroll
-      for (int q = 0; q < KS; ++q) v += spart[q][r][jj];
-      sx[r][jj] = v;
+    for (int n = 0; n < NE; ++n) {
+      const int e = tid + 256 * n;
+      if (e < NROW * D) {
+        const int r = e / D, jj = e % D;
+        float v = da[n];
+#pragma unroll
+        for (int q = 0; q < KS; ++q) v += spart[q][r][jj];
+        sx[r][jj] = v;
+      }
     }
     __syncthreads();
   };
   __syncthreads();
-  if (nseg > 0) load_phi(0, ph[0]);
+  if (nseg > 0) fetch(0, ph[0], ad[0]);
   int i = 0;
   for (; i + 2 <= nseg; i += 2) {
-    load_phi(i + 1, ph[1]);
-    step(i, ph[0]);
-    if (i + 2 < nseg) load_phi(i + 2, ph[0]);
-    step(i + 1, ph[1]);
+    fetch(i + 1, ph[1], ad[1]);
+    step(i, ph[0], ad[0]);
+    if (i + 2 < nseg) fetch(i + 2, ph[0], ad[0]);
+    step(i + 1, ph[1], ad[1]);
   }
-  if (i < nseg) step(i, ph[0]);
+  if (i < nseg) step(i, ph[0], ad[0]);
 }
 
 // Pass 3: the token steps of every segment, from its entering state S_in and the adjoint
@@ -1045,17 +1059,25 @@ __global__ __launch_bounds__(256) void bwd_part_reduce_kernel(BwdArgs a) {
   }
 }
 
-// dconv_w[h] = sum over the batch and the nseg shares of each pair (fixed order:
-// deterministic); shares laid out [B][H][nseg][4][D].
+// dconv_w[h] = sum over the batch and the nseg shares of each pair, shares laid out
+// [B][H][nseg][4][D]: workgroup (h, block of 64 entries); thread (entry, quarter) sums every
+// fourth share in order, then the four quarter sums are added in order (deterministic).
 __global__ __launch_bounds__(256) void bwd_conv_reduce_kernel(const float* part, float* dconv_w, int B, int H, int D,
                                                               int nseg) {
-  const int h = blockIdx.x;
-  for (int i = threadIdx.x; i < 4 * D; i += 256) {
-    float s = 0.f;
-    for (int b = 0; b < B; ++b)
-      for (int sg = 0; sg < nseg; ++sg) s += part[(((size_t)b * H + h) * nseg + sg) * 4 * D + i];
-    dconv_w[(size_t)h * 4 * D + i] = s;
+  __shared__ float q4[4][64];
+  const int h = blockIdx.x, i = 64 * blockIdx.y + (threadIdx.x & 63), qt = threadIdx.x >> 6;
+  const int n = B * nseg;
+  float s = 0.f;
+  if (i < 4 * D) {
+    for (int x = qt; x < n; x += 4) {
+      const int b = x / nseg, sg = x % nseg;
+      s += part[(((size_t)b * H + h) * nseg + sg) * 4 * D + i];
+    }
   }
+  q4[qt][threadIdx.x & 63] = s;
+  __syncthreads();
+  if (qt == 0 && i < 4 * D)
+    dconv_w[(size_t)h * 4 * D + i] = (q4[0][threadIdx.x] + q4[1][threadIdx.x]) + (q4[2][threadIdx.x] + q4[3][threadIdx.x]);
 }
 
 }  // namespace prism
