@@ -136,37 +136,40 @@ __device__ __forceinline__ void mm_lt(f32x4& acc, const E* A, int lda, int m0,
   }
 }
 
-// acc += A * Bt with A(m, k) = ascale[k] * S[k * lds + m0 + m] read element-wise
-// from a row-major LDS array S whose rows are indexed by k (a scaled transpose).
+// acc += A * Bt with A(m, k) = ascale[k] * S[k * lds + m0 + m]: a scaled transpose of a
+// row-major LDS array S whose rows are indexed by k.  bfloat16: the A operand comes from
+// gfx950's transposing LDS read (ds_read_b64_tr_b16: in each group of 16 lanes, lane
+// 4 r + c supplies row r, columns 4 c .. 4 c + 3 of a 4 x 16 block and lane j receives its
+// column j), two reads per 32-deep block; the scale moves onto the B operand's k rows
+// (ascale[k] multiplies the same products).  float32: element-wise.
 template <class E, int NKT>
 __device__ __forceinline__ void mm_tt(f32x4& acc, const E* S, int lds, int m0, const float* ascale,
                                       const f32x4 (&Bt)[NKT], int K) {
   const int l = lane_id(), g = l >> 4, i = l & 15;
-  const E* s = S + m0 + i;
   if constexpr (std::is_same<E, bf16_t>::value) {
+    typedef short s16x4_t __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
+    const E* s = S + (i >> 2) * lds + m0 + 4 * (i & 3);
 #pragma unroll
     for (int kb = 0; kb < (NKT + 1) / 2; ++kb) {
       const int k0 = kb * 32;
       if (k0 >= K) break;
       const bool hi = (2 * kb + 1 < NKT) && (k0 + 16 < K);
-      bf16x8 fa, fb;
+      const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4*)(const_cast<E*>(s + (k0 + 4 * g) * lds)));
+      s16x4_t up = {0, 0, 0, 0};
+      if (hi) up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(const_cast<E*>(s + (k0 + 16 + 4 * g) * lds)));
+      const bf16x8 fa = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
+      bf16x8 fb;
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
-        const int ka = k0 + 4 * g + p;
-        fa[p] = (bf16_t)(to_f(s[ka * lds]) * ascale[ka]);
-        fb[p] = (bf16_t)Bt[2 * kb][p];
-        if (hi) {
-          const int kc = ka + 16;
-          fa[4 + p] = (bf16_t)(to_f(s[kc * lds]) * ascale[kc]);
-          fb[4 + p] = (bf16_t)Bt[2 * kb + 1][p];
-        } else {
-          fa[4 + p] = (bf16_t)0.f;
-          fb[4 + p] = (bf16_t)0.f;
-        }
+        fb[p] = (bf16_t)(Bt[2 * kb][p] * ascale[k0 + 4 * g + p]);
+        fb[4 + p] = hi ? (bf16_t)(Bt[2 * kb + 1][p] * ascale[k0 + 16 + 4 * g + p]) : (bf16_t)0.f;
       }
       acc = mfma(fa, fb, acc);
     }
   } else {
+    const E* s = S + m0 + i;
 #pragma unroll
     for (int kt = 0; kt < NKT; ++kt) {
       const int k0 = kt * 16;
