@@ -115,15 +115,16 @@ prism_status make_plan(int B, int H, int T, int dk, int dv, int L, int chunk, pr
     }
   }
   const size_t nseg = (nch + seg_chunks - 1) / seg_chunks;
-  // the generic path keeps O_loc, Qhat and H_in in float32; the fast path in bfloat16
-  const size_t wel = fast ? 2 : 4;
+  // O_loc and Qhat in the I/O type (the fast path's in fragment order); H_in in bfloat16 on
+  // the fast path (the correction's MFMA operand), float32 on the generic path
+  const size_t wel = dt == PRISM_BF16 ? 2 : 4, hel = fast ? 2 : 4;
   size_t Tpad = nch * (size_t)chunk, a, b, c;
   size_t sz_oloc, sz_qhat, sz_agg_a, sz_agg_b, sz_hin;
   if (!mul_ok(P, Tpad, &a) || !mul_ok(a, (size_t)dv * wel, &sz_oloc)) return PRISM_ERR_INVALID_ARG;
   if (!mul_ok(a, (size_t)dk * wel, &sz_qhat)) return PRISM_ERR_INVALID_ARG;
   if (!mul_ok(P, nseg, &b) || !mul_ok(b, (size_t)dk * dk * 4, &sz_agg_a)) return PRISM_ERR_INVALID_ARG;
   if (!mul_ok(b, (size_t)dk * dv * 4, &sz_agg_b)) return PRISM_ERR_INVALID_ARG;
-  sz_hin = sz_agg_b / 4 * wel;
+  sz_hin = sz_agg_b / 4 * hel;
   // inputs must be addressable too: P*T*(L-1)*max(dk,dv) elements
   if (!mul_ok(P, (size_t)T, &c) || !mul_ok(c, (size_t)L * (dk > dv ? dk : dv) * 4, &c))
     return PRISM_ERR_INVALID_ARG;

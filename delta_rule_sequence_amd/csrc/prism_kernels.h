@@ -45,8 +45,8 @@ struct FwdArgs {
   const float* S0;       // [P][dk][dv] starting state (the S_final layout), or null for zero
   const void* conv_in;   // [P][3][dv] values of the 3 tokens before the sequence, or null
   void* conv_out;        // [P][3][dv] values of the last 3 tokens of [conv_in; v], or null
-  float* Oloc;   // [P][Tpad][dv]
-  float* Qhat;   // [P][Tpad][dk]
+  float* Oloc;   // [P][Tpad][dv], I/O type (bf16 fast path: fragment order)
+  float* Qhat;   // [P][Tpad][dk], I/O type (bf16 fast path: fragment order)
   float* Aagg;   // [P][nseg][dk][dk]
   float* Bagg;   // [P][nseg][dk][dv]
   float* Hin;    // [P][nseg][dk][dv]
@@ -422,7 +422,7 @@ __global__ __launch_bounds__(64 * NW, 1) void seg_local_kernel(FwdArgs a) {
     __syncthreads();
 
     // ---- E = Uc - Wc H;  O_loc;  H update ---------------------------------------
-    float* oloc = a.Oloc + ((size_t)pr * Tpad + t0) * DV;
+    E* oloc = reinterpret_cast<E*>(a.Oloc) + ((size_t)pr * Tpad + t0) * DV;
 #pragma unroll
     for (int jv = 0; jv < NVW; ++jv) {
       const int vt = w + NW * jv;
@@ -442,7 +442,7 @@ __global__ __launch_bounds__(64 * NW, 1) void seg_local_kernel(FwdArgs a) {
       for (int mt = 0; mt < MT; ++mt) {
         mm_lt<E, MT>(Oc[jv][mt], sP, LDC, 16 * mt, Vp[jv], nullptr, C);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) oloc[(size_t)(16 * mt + g4 + r) * DV + 16 * vt + li] = Oc[jv][mt][r];
+        for (int r = 0; r < 4; ++r) oloc[(size_t)(16 * mt + g4 + r) * DV + 16 * vt + li] = from_f<E>(Oc[jv][mt][r]);
       }
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt) mm_tt<E, MT>(Hs[jv][kt], sK, LDK, 16 * kt, sD, Vp[jv], C);
@@ -494,13 +494,13 @@ __global__ __launch_bounds__(64 * NW, 1) void seg_local_kernel(FwdArgs a) {
     __syncthreads();
     // ---- Qhat = Qtilde A_acc (A_acc before this chunk) --------------------------
     {
-      float* qhat = a.Qhat + ((size_t)pr * Tpad + t0) * DK;
+      E* qhat = reinterpret_cast<E*>(a.Qhat) + ((size_t)pr * Tpad + t0) * DK;
       for (int tI = w; tI < MT * KT; tI += NW) {
         const int mt = tI / KT, kc = tI % KT;
         f32x4 acc = zero4();
         mm_ll<E>(acc, sQt, LDK, 16 * mt, sS, LDK, 16 * kc, DK);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) qhat[(size_t)(16 * mt + g4 + r) * DK + 16 * kc + li] = acc[r];
+        for (int r = 0; r < 4; ++r) qhat[(size_t)(16 * mt + g4 + r) * DK + 16 * kc + li] = from_f<E>(acc[r]);
       }
     }
     __syncthreads();
@@ -640,24 +640,24 @@ __global__ __launch_bounds__(256) void seg_fixup_kernel(FwdArgs a) {
   const int t0 = c * C, nvalid = min(C, a.T - t0);
   const int Tpad = a.nch * C;
   const float* Hi = a.Hin + ((size_t)pr * a.nseg + seg) * DK * DV;
-  const float* qh = a.Qhat + ((size_t)pr * Tpad + t0) * DK;
-  const float* ol = a.Oloc + ((size_t)pr * Tpad + t0) * DV;
+  const E* qh = reinterpret_cast<const E*>(a.Qhat) + ((size_t)pr * Tpad + t0) * DK;
+  const E* ol = reinterpret_cast<const E*>(a.Oloc) + ((size_t)pr * Tpad + t0) * DV;
   E* o = reinterpret_cast<E*>(a.o) + ((size_t)pr * a.T + t0) * DV;
   for (int idx = tid; idx < DK * DV / 4; idx += 256)
     reinterpret_cast<float4*>(sH)[idx] = reinterpret_cast<const float4*>(Hi)[idx];
-  for (int idx = tid; idx < C * DK; idx += 256) sQh[(idx / DK) * (DK + 1) + idx % DK] = qh[idx];
+  for (int idx = tid; idx < C * DK; idx += 256) sQh[(idx / DK) * (DK + 1) + idx % DK] = to_f(qh[idx]);
   __syncthreads();
   for (int idx = tid; idx < nvalid * DV; idx += 256) {
     const int t = idx / DV, jj = idx % DV;
-    float acc = ol[(size_t)t * DV + jj];
+    float acc = to_f(ol[(size_t)t * DV + jj]);
     for (int kk = 0; kk < DK; ++kk) acc += sQh[t * (DK + 1) + kk] * sH[kk * DV + jj];
     o[(size_t)t * DV + jj] = from_f<E>(acc);
   }
 }
 
 // o = O_loc + Qhat H_in(segment) for one chunk of one pair on MFMA, for bfloat16 I/O at
-// d = 128 and 64-token chunks: bfloat16 operands (Qhat and H_in rounded once, as the
-// output itself is), float32 accumulation started from O_loc.  H_in^T of the chunk's
+// d = 128 and 64-token chunks: bfloat16 operands (Qhat as stored, H_in rounded once, as
+// the output itself is), float32 accumulation started from O_loc (stored in bfloat16).  H_in^T of the chunk's
 // segment is staged in LDS with the contraction index permuted inside each 32-block
 // (k = 32 kb + 16 h + 4 q + e at 32 kb + 8 q + 4 h + e), so a lane's 8-value operand
 // (k0 + 4 q .. + 3 and k0 + 16 + 4 q .. + 3) is one 16-byte read; wave w takes token rows
@@ -680,23 +680,21 @@ __global__ __launch_bounds__(256) void seg_fixup_mfma_kernel(FwdArgs a) {
   }
   // this wave's Qhat rows as A operands (4 blocks of 32 along k)
   const int row = 16 * w + li;
-  const float* qh = a.Qhat + ((size_t)pr * Tpad + t0 + row) * D;
+  const bf16_t* qh = reinterpret_cast<const bf16_t*>(a.Qhat) + ((size_t)pr * Tpad + t0 + row) * D;
   bf16x8 af[D / 32];
 #pragma unroll
   for (int kb = 0; kb < D / 32; ++kb) {
-    const float4 x0 = *reinterpret_cast<const float4*>(qh + 32 * kb + 4 * q);
-    const float4 x1 = *reinterpret_cast<const float4*>(qh + 32 * kb + 16 + 4 * q);
-    const float v8[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) af[kb][e] = (bf16_t)v8[e];
+    const bf16x4 x0 = *reinterpret_cast<const bf16x4*>(qh + 32 * kb + 4 * q);
+    const bf16x4 x1 = *reinterpret_cast<const bf16x4*>(qh + 32 * kb + 16 + 4 * q);
+    af[kb] = __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
   }
   // accumulators from O_loc: lane (li, q) of tile vt holds rows 16 w + 4 q + r, column 16 vt + li
-  const float* ol = a.Oloc + ((size_t)pr * Tpad + t0 + 16 * w + 4 * q) * D;
+  const bf16_t* ol = reinterpret_cast<const bf16_t*>(a.Oloc) + ((size_t)pr * Tpad + t0 + 16 * w + 4 * q) * D;
   f32x4 acc[D / 16];
 #pragma unroll
   for (int vt = 0; vt < D / 16; ++vt)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) acc[vt][r] = ol[(size_t)r * D + 16 * vt + li];
+    for (int r = 0; r < 4; ++r) acc[vt][r] = (float)ol[(size_t)r * D + 16 * vt + li];
   __syncthreads();
 #pragma unroll
   for (int vt = 0; vt < D / 16; ++vt)
