@@ -938,13 +938,17 @@ __global__ __launch_bounds__(256) void bwd_seg_scan_kernel(BwdArgs a) {
       da[n] = e < NROW * D ? add[base + (size_t)s * DD + (size_t)(r0 + e / D) * D + e % D] : 0.f;
     }
   };
-  auto step = [&](int i, const float (&phi)[KD], const float (&da)[NE]) __attribute__((always_inline)) {
+  // the carried rows of step i, stored where the step's segment reads them
+  auto put = [&](int i) __attribute__((always_inline)) {
     const int s = rev ? nseg - 1 - i : i;
 #pragma unroll
     for (int n = 0; n < NE; ++n) {
       const int e = tid + 256 * n;
       if (e < NROW * D) out[base + (size_t)s * DD + (size_t)(r0 + e / D) * D + e % D] = sx[e / D][e % D];
     }
+  };
+  // step i: x <- x Phi' + added term; then the new rows are stored for step i + 1
+  auto step = [&](int i, const float (&phi)[KD], const float (&da)[NE]) __attribute__((always_inline)) {
 #pragma unroll
     for (int r = 0; r < NROW; ++r) {
       float acc = 0.f;
@@ -953,6 +957,7 @@ __global__ __launch_bounds__(256) void bwd_seg_scan_kernel(BwdArgs a) {
       spart[ks][r][j] = acc;
     }
     __syncthreads();
+    const int sn = rev ? nseg - 2 - i : i + 1;  // the segment the new rows enter
 #pragma unroll
     for (int n = 0; n < NE; ++n) {
       const int e = tid + 256 * n;
@@ -962,20 +967,27 @@ __global__ __launch_bounds__(256) void bwd_seg_scan_kernel(BwdArgs a) {
 #pragma unroll
         for (int q = 0; q < KS; ++q) v += spart[q][r][jj];
         sx[r][jj] = v;
+        if (i + 1 < nseg) out[base + (size_t)sn * DD + (size_t)(r0 + r) * D + jj] = v;
       }
     }
     __syncthreads();
   };
   __syncthreads();
-  if (nseg > 0) fetch(0, ph[0], ad[0]);
-  int i = 0;
-  for (; i + 2 <= nseg; i += 2) {
-    fetch(i + 1, ph[1], ad[1]);
-    step(i, ph[0], ad[0]);
-    if (i + 2 < nseg) fetch(i + 2, ph[0], ad[0]);
-    step(i + 1, ph[1], ad[1]);
+  if (nseg > 0) {
+    put(0);
+    // operands loaded a step ahead, unconditionally (the index clamps at the last
+    // segment), so the loop body is straight-line code and no step waits on a load issued
+    // after its own operands
+    fetch(0, ph[0], ad[0]);
+    int i = 0;
+    for (; i + 2 <= nseg; i += 2) {
+      fetch(min(i + 1, nseg - 1), ph[1], ad[1]);
+      step(i, ph[0], ad[0]);
+      fetch(min(i + 2, nseg - 1), ph[0], ad[0]);
+      step(i + 1, ph[1], ad[1]);
+    }
+    if (i < nseg) step(i, ph[0], ad[0]);
   }
-  if (i < nseg) step(i, ph[0], ad[0]);
 }
 
 // Pass 3: the token steps of every segment, from its entering state S_in and the adjoint
