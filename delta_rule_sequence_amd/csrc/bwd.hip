@@ -24,13 +24,18 @@ void bwd_launch_d(const BwdArgs& a, int P, hipStream_t stream) {
 // Segment-parallel: segment states, operators and local adjoints; the two scans; the
 // token steps of every segment; partial sums (NSP > 1); the anchor terms across segment
 // starts.
+// (the token-step kernels are compiled with L fixed when L - 1 fills the rank slots: L = 1,
+// 4 and 8, so that their rank loops carry no run-time test)
 template <class E, int D, int NRK>
 void bwd_seg_launch_d(const BwdArgs& a, int P, hipStream_t stream) {
   constexpr int RW = bwd_seg_rows<D>(), NSP = BwdShape<D, NRK, RW>::NSP;
   const unsigned nwg = (unsigned)P * (unsigned)a.nseg * NSP;
-  hipLaunchKernelGGL((bwd_seg_local_kernel<E, D, NRK, RW>), dim3(nwg), dim3(256), 0, stream, a);
+  const bool exact = a.L - 1 == NRK;
+  if (exact) hipLaunchKernelGGL((bwd_seg_local_kernel<E, D, NRK, RW, NRK>), dim3(nwg), dim3(256), 0, stream, a);
+  else hipLaunchKernelGGL((bwd_seg_local_kernel<E, D, NRK, RW, -1>), dim3(nwg), dim3(256), 0, stream, a);
   hipLaunchKernelGGL((bwd_seg_scan_kernel<D>), dim3((unsigned)P, D / 4, 2), dim3(256), 0, stream, a);
-  hipLaunchKernelGGL((bwd_seg_kernel<E, D, NRK, RW>), dim3(nwg), dim3(256), 0, stream, a);
+  if (exact) hipLaunchKernelGGL((bwd_seg_kernel<E, D, NRK, RW, NRK>), dim3(nwg), dim3(256), 0, stream, a);
+  else hipLaunchKernelGGL((bwd_seg_kernel<E, D, NRK, RW, -1>), dim3(nwg), dim3(256), 0, stream, a);
   if constexpr (NSP > 1) {
     const unsigned nt8 = (unsigned)((a.T + 7) / 8);
     hipLaunchKernelGGL((bwd_part_reduce_kernel<D, NRK, RW>), dim3((unsigned)P * nt8), dim3(256), 0, stream, a);

@@ -245,8 +245,10 @@ constexpr int bwd_seg_rows() { return D >= 32 ? 2 : 1; }
 
 // A thread's view of the backward: its rows and columns, the per-token steps (inputs,
 // residual chain, forward step, adjoint step) and the adjoint-side registers they carry.
-// NRK: rank slots compiled in (0 for L = 1, 3 for L <= 4, 7 for L <= 8).
-template <class E, int D, int NRK, int RW, int KR>
+// NRK: rank slots compiled in (0 for L = 1, 3 for L <= 4, 7 for L <= 8); LX: L - 1 when
+// it is known at compile time (it equals NRK), else -1 (the rank loops then test L at run
+// time, which splits them into short basic blocks).
+template <class E, int D, int NRK, int RW, int KR, int LX = -1>
 struct BwdCore {
   using Sh = BwdShape<D, NRK, RW>;
   static constexpr int R = D / 16, NR = Sh::NR, NV = Sh::NV, NS = Sh::NS, RED = Sh::RED, NSP = Sh::NSP;
@@ -273,8 +275,8 @@ struct BwdCore {
     hd = pair % args.H;
     row0 = RW * (16 * slice + rb);
     T = args.T;
-    L = args.L;
-    Lm1 = L - 1;
+    L = LX >= 0 ? LX + 1 : args.L;
+    Lm1 = LX >= 0 ? LX : L - 1;
     Q = reinterpret_cast<const E*>(args.q);
     K = reinterpret_cast<const E*>(args.k);
     V = reinterpret_cast<const E*>(args.v);
@@ -838,9 +840,9 @@ __global__ __launch_bounds__(256) void bwd_pair_kernel(BwdArgs a) {
 // Phi_s = A_{t0} .. A_{t1-1} (its rows evolve like the state's, with no write), and,
 // walking the segment backwards with a zero adjoint at its end, the adjoint ell_s at its
 // start (dS += d_o q^T, then dS <- dS A_t).  Only row sums are needed: no LDS.
-template <class E, int D, int NRK, int RW>
+template <class E, int D, int NRK, int RW, int LX>
 __global__ __launch_bounds__(256) void bwd_seg_local_kernel(BwdArgs a) {
-  using Core = BwdCore<E, D, NRK, RW, 1>;
+  using Core = BwdCore<E, D, NRK, RW, 1, LX>;
   using Tok = typename Core::Tok;
   using AdjTok = typename Core::AdjTok;
   constexpr int R = Core::R, NSP = Core::NSP;
@@ -995,11 +997,11 @@ __global__ __launch_bounds__(256) void bwd_seg_scan_kernel(BwdArgs a) {
 // tokens, then per sub-block (last first) the sub-block's forward again into a per-workgroup
 // scratch and its adjoint steps.  The anchor terms the segment owes the three tokens before
 // it, and its dconv_w share, go to the workspace.
-template <class E, int D, int NRK, int RW>
+template <class E, int D, int NRK, int RW, int LX>
 __global__ __launch_bounds__(256) void bwd_seg_kernel(BwdArgs a) {
   constexpr int NR = BwdShape<D, NRK, RW>::NR;
   constexpr int KR = bwd_seg_red_group<D, NR>();
-  using Core = BwdCore<E, D, NRK, RW, KR>;
+  using Core = BwdCore<E, D, NRK, RW, KR, LX>;
   constexpr int R = Core::R, NSP = Core::NSP, SD = Core::SD, RED = Core::RED, CK = kBwdSegSub;
   __shared__ float red[KR][16][RED];
   const int wg = blockIdx.x, sp = wg % NSP, seg = (wg / NSP) % a.nseg, pr = wg / (NSP * a.nseg);
