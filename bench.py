@@ -50,7 +50,8 @@ def algorithmic_bytes(w):
 SWEEP_SOURCES = ["delta_rule_sequence_amd/csrc/prism_sweep8.h", "delta_rule_sequence_amd/csrc/prism_fast.h",
                  "delta_rule_sequence_amd/csrc/prism_kernels.h", "delta_rule_sequence_amd/csrc/prism_tile.h",
                  "delta_rule_sequence_amd/csrc/prism_nl.h", "delta_rule_sequence_amd/csrc/prism_generic_launch.h",
-                 "delta_rule_sequence_amd/csrc/fwd_fast_linear.hip", "delta_rule_sequence_amd/build.py"]
+                 "delta_rule_sequence_amd/csrc/fwd_fast_linear.hip", "delta_rule_sequence_amd/csrc/prism_sweep128.h",
+                 "delta_rule_sequence_amd/csrc/fwd_fast128_linear.hip", "delta_rule_sequence_amd/build.py"]
 
 
 def kernel_source_hash():
@@ -609,7 +610,8 @@ def main():
     achieved = sweep_bytes / (sweep_ms * 1e-3) / 1e9
     traffic = load_traffic(w.name)
     fast = w.dtype == "bf16" and w.dk == 64 and w.dv == 64 and w.chunk == 64
-    sweep_name = "seg_sweep8_kernel" if fast else "seg_local_kernel"
+    fast128 = w.dtype == "bf16" and w.dk == 128 and w.dv == 128 and w.chunk == 64
+    sweep_name = "seg_sweep8_kernel" if fast else "seg_sweep128_kernel" if fast128 else "seg_local_kernel"
 
     out = {
         "metric": "fwd tokens/sec at T=16K,H=4,d=64,L=4 bf16; % of HBM/MFMA roofline",

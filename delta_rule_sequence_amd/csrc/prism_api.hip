@@ -35,7 +35,8 @@ inline bool mul_ok(size_t a, size_t b, size_t* out) {
 }
 
 struct Plan {
-  bool fast;
+  bool fast;     // the bfloat16 d = 64 sweep
+  bool fast128;  // the bfloat16 d = 128 half-split sweep
   int P, nch, seg_chunks, nseg;
   size_t off_oloc, off_qhat, off_aagg, off_bagg, off_hin, total;
 };
@@ -47,6 +48,13 @@ bool valid_dim(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 bool use_fast(int T, int dk, int dv, int L, int chunk, prism_dtype dt) {
   const size_t slice = (size_t)T * (size_t)(L > 1 ? L - 1 : 1) * 64 * 2;
   return dt == PRISM_BF16 && dk == 64 && dv == 64 && chunk == 64 && slice < ((size_t)1 << 31);
+}
+
+// The half-split sweep (prism_sweep128.h): bfloat16, head dim 128, chunk 64, the same
+// 32-bit addressing of one pair's u / gamma slice.
+bool use_fast128(int T, int dk, int dv, int L, int chunk, prism_dtype dt) {
+  const size_t slice = (size_t)T * (size_t)(L > 1 ? L - 1 : 1) * 128 * 2;
+  return dt == PRISM_BF16 && dk == 128 && dv == 128 && chunk == 64 && slice < ((size_t)1 << 31);
 }
 
 template <class E, int DK, int DV>
@@ -93,21 +101,25 @@ prism_status make_plan(int B, int H, int T, int dk, int dv, int L, int chunk, pr
   if (P > 65535) return PRISM_ERR_UNSUPPORTED;  // (b, h) pairs map to grid.y
   const size_t nch = ((size_t)T + chunk - 1) / chunk;
   const bool fast = use_fast(T, dk, dv, L, chunk, dt);
+  const bool fast128 = use_fast128(T, dk, dv, L, chunk, dt);
   if (seg_chunks == 0 && fast) {
     size_t nseg_target = kTargetWorkgroupsFast / P;
     if (nseg_target < 1) nseg_target = 1;
     seg_chunks = (int)((nch + nseg_target - 1) / nseg_target);
     if (seg_chunks < 1) seg_chunks = 1;
   } else if (seg_chunks == 0) {
-    // the generic sweep runs one workgroup per CU: the sweep takes about (rounds of
-    // kCUs workgroups) x (chunks per segment) chunk times, and every segment adds one
-    // step of the inter-segment scan (~0.1 of a chunk at d = 128, measured)
+    // the generic and the half-split sweeps run one workgroup per CU (two per segment for
+    // the half-split one): the sweep takes about (rounds of kCUs workgroups) x (chunks per
+    // segment) chunk times, and every segment adds one step of the inter-segment scan
+    // (~0.1 of a generic chunk at d = 128, ~0.15 of a half-split one, measured)
+    const size_t per_seg = fast128 ? 2 : 1;
+    const double scan_cost = fast128 ? 0.15 : 0.1;
     double best = 0.0;
     const size_t smax = nch < 1024 ? nch : 1024;
     for (size_t sc = 1; sc <= smax; ++sc) {
       const size_t ns = (nch + sc - 1) / sc;
-      const size_t rounds = (P * ns + kCUs - 1) / kCUs;
-      const double cost = (double)rounds * (double)sc + 0.1 * (double)ns;
+      const size_t rounds = (P * ns * per_seg + kCUs - 1) / kCUs;
+      const double cost = (double)rounds * (double)sc + scan_cost * (double)ns;
       if (sc == 1 || cost < best) {
         best = cost;
         seg_chunks = (int)sc;
@@ -129,6 +141,7 @@ prism_status make_plan(int B, int H, int T, int dk, int dv, int L, int chunk, pr
   if (!mul_ok(P, (size_t)T, &c) || !mul_ok(c, (size_t)L * (dk > dv ? dk : dv) * 4, &c))
     return PRISM_ERR_INVALID_ARG;
   pl->fast = fast;
+  pl->fast128 = fast128;
   pl->P = (int)P;
   pl->nch = (int)nch;
   pl->seg_chunks = seg_chunks;
@@ -192,8 +205,12 @@ prism_status fwd_impl(const void* q, const void* k, const void* v, const float* 
   a.chain_delta = form == ChainForm::kDelta ? 1 : 0;
   if (form == ChainForm::kGelu && !pl.fast) return PRISM_ERR_UNSUPPORTED;
   const prism::host::LaunchShape shape{pl.P, pl.nch, pl.nseg};
-  st = pl.fast ? prism::host::launch_fast(a, shape, ev, stream, L > 1 ? form : ChainForm::kLinear)
-               : dispatch_generic(dt, dk, dv, chunk, a, shape, ev, stream);
+  if (pl.fast)
+    st = prism::host::launch_fast(a, shape, ev, stream, L > 1 ? form : ChainForm::kLinear);
+  else if (pl.fast128)
+    st = prism::host::launch_fast128(a, shape, ev, stream, L > 1 ? form : ChainForm::kLinear);
+  else
+    st = dispatch_generic(dt, dk, dv, chunk, a, shape, ev, stream);
   if (st != PRISM_OK || conv_out == nullptr) return st;
   // after the sweep, the only reader of conv_in, so conv_out may alias it
   if (dt == PRISM_BF16)

@@ -9,6 +9,20 @@
 namespace prism {
 namespace host {
 
+// The scan and the output correction after a sweep (events 2 and 3).
+template <class E, int DK, int DV, int C>
+prism_status launch_generic_tail(const FwdArgs& a, const LaunchShape& s, hipEvent_t* ev, hipStream_t stream) {
+  constexpr int NQ = DK >= 128 ? 8 : 4;  // state columns per scan workgroup
+  hipLaunchKernelGGL((seg_scan_kernel<DK, DV>), dim3(s.P, DV / NQ), dim3(NQ * DK), 0, stream, a);
+  if (hipGetLastError() != hipSuccess || !record(ev, 2, stream)) return PRISM_ERR_HIP;
+  if constexpr (std::is_same<E, bf16_t>::value && DK == 128 && DV == 128 && C == 64)
+    hipLaunchKernelGGL((seg_fixup_mfma_kernel<DK, C>), dim3(s.nch, s.P), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((seg_fixup_kernel<E, DK, DV, C>), dim3(s.nch, s.P), dim3(256), 0, stream, a);
+  if (hipGetLastError() != hipSuccess || !record(ev, 3, stream)) return PRISM_ERR_HIP;
+  return PRISM_OK;
+}
+
 template <class E, int DK, int DV, int C>
 prism_status launch_generic(const FwdArgs& a, const LaunchShape& s, hipEvent_t* ev, hipStream_t stream) {
   if constexpr (!SegLds<E, DK, DV, C>::fits) {
@@ -20,15 +34,7 @@ prism_status launch_generic(const FwdArgs& a, const LaunchShape& s, hipEvent_t* 
     if (!record(ev, 0, stream)) return PRISM_ERR_HIP;
     hipLaunchKernelGGL((seg_local_kernel<E, DK, DV, C, NW>), dim3(s.nseg, s.P), dim3(64 * NW), 0, stream, a);
     if (hipGetLastError() != hipSuccess || !record(ev, 1, stream)) return PRISM_ERR_HIP;
-    constexpr int NQ = DK >= 128 ? 8 : 4;  // state columns per scan workgroup
-    hipLaunchKernelGGL((seg_scan_kernel<DK, DV>), dim3(s.P, DV / NQ), dim3(NQ * DK), 0, stream, a);
-    if (hipGetLastError() != hipSuccess || !record(ev, 2, stream)) return PRISM_ERR_HIP;
-    if constexpr (std::is_same<E, bf16_t>::value && DK == 128 && DV == 128 && C == 64)
-      hipLaunchKernelGGL((seg_fixup_mfma_kernel<DK, C>), dim3(s.nch, s.P), dim3(256), 0, stream, a);
-    else
-      hipLaunchKernelGGL((seg_fixup_kernel<E, DK, DV, C>), dim3(s.nch, s.P), dim3(256), 0, stream, a);
-    if (hipGetLastError() != hipSuccess || !record(ev, 3, stream)) return PRISM_ERR_HIP;
-    return PRISM_OK;
+    return launch_generic_tail<E, DK, DV, C>(a, s, ev, stream);
   }
 }
 

@@ -57,6 +57,15 @@ void launch_sweep8_linear(const FwdArgs& a, dim3 grid, hipStream_t stream);
 void launch_sweep8_nl(const FwdArgs& a, dim3 grid, hipStream_t stream);
 void launch_sweep8_delta(const FwdArgs& a, dim3 grid, hipStream_t stream);
 
+// The bfloat16, dk = dv = 128, chunk 64 path: the half-split segment sweep
+// (prism_sweep128.h, grid (nseg, P, 2)) of the chain form, then the d = 128 scan and
+// MFMA output correction of the generic path (launch_tail_bf16_d128).
+prism_status launch_fast128(const FwdArgs& a, const LaunchShape& s, hipEvent_t* ev, hipStream_t stream,
+                            ChainForm form);
+void launch_sweep128_linear(const FwdArgs& a, dim3 grid, hipStream_t stream);
+void launch_sweep128_delta(const FwdArgs& a, dim3 grid, hipStream_t stream);
+prism_status launch_tail_bf16_d128(const FwdArgs& a, const LaunchShape& s, hipEvent_t* ev, hipStream_t stream);
+
 // The backward (prism_bwd.h).  launch_bwd: with segments the segment-parallel passes
 // (a.nseg segments of a.seg_len tokens), otherwise the sequential per-pair sweep; then the
 // partial sums and, for L > 1, the batch sum of the conv-weight gradient into dconv_w.
