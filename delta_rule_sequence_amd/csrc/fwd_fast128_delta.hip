@@ -1,18 +1,23 @@
 // fwd_fast128_delta.hip - the d = 128 half-split segment sweep with the written-correction
-// chain (a.gamma holds the corrections' per-channel factors).  L >= 2.
+// chain (a.gamma holds the corrections' per-channel factors), one instantiation per
+// L = 2 .. 8.
 #include "prism_host.h"
 #include "prism_sweep128.h"
 
 namespace prism {
 namespace host {
 
-void launch_sweep128_delta(const FwdArgs& a, dim3 grid, hipStream_t stream) {
+bool launch_sweep128_delta(const FwdArgs& a, dim3 grid, hipStream_t stream) {
   const dim3 block(512);
   switch (a.L) {
-    case 2: hipLaunchKernelGGL((seg_sweep128_delta_kernel<1>), grid, block, 0, stream, a); break;
-    case 4: hipLaunchKernelGGL((seg_sweep128_delta_kernel<3>), grid, block, 0, stream, a); break;
-    case 8: hipLaunchKernelGGL((seg_sweep128_delta_kernel<7>), grid, block, 0, stream, a); break;
-    default: hipLaunchKernelGGL((seg_sweep128_delta_kernel<-1>), grid, block, 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((seg_sweep128_delta_kernel<1>), grid, block, 0, stream, a); return true;
+    case 3: hipLaunchKernelGGL((seg_sweep128_delta_kernel<2>), grid, block, 0, stream, a); return true;
+    case 4: hipLaunchKernelGGL((seg_sweep128_delta_kernel<3>), grid, block, 0, stream, a); return true;
+    case 5: hipLaunchKernelGGL((seg_sweep128_delta_kernel<4>), grid, block, 0, stream, a); return true;
+    case 6: hipLaunchKernelGGL((seg_sweep128_delta_kernel<5>), grid, block, 0, stream, a); return true;
+    case 7: hipLaunchKernelGGL((seg_sweep128_delta_kernel<6>), grid, block, 0, stream, a); return true;
+    case 8: hipLaunchKernelGGL((seg_sweep128_delta_kernel<7>), grid, block, 0, stream, a); return true;
+    default: return false;
   }
 }
 

@@ -543,8 +543,9 @@ __device__ __forceinline__ float dpp_mov(float x) {
 // banks), and DPP exchanges inside the group of NQ lanes leave lane q with column c0 + q:
 // partner 7 - q (bit 2) for NQ = 8, then 3 - q (bit 1), then q ^ 1 (bit 0).  One barrier
 // per step.  Eight columns per workgroup at DK = 128 halve the workgroups that read each
-// A_s, against four.
-template <int DK, int DV>
+// A_s, against four.  FEW (nseg <= DEPTH): every step's operands come with the first loads,
+// each segment's once.
+template <int DK, int DV, bool FEW = false>
 __global__ __launch_bounds__(DK >= 128 ? 8 * DK : 4 * DK) void seg_scan_kernel(FwdArgs a) {
   constexpr int NQ = DK >= 128 ? 8 : 4;       // contraction slices = columns per workgroup
   static_assert(DV % NQ == 0, "NQ state columns per workgroup");
@@ -573,7 +574,8 @@ __global__ __launch_bounds__(DK >= 128 ? 8 * DK : 4 * DK) void seg_scan_kernel(F
     b = B0[sn * DK * DV];
   };
 #pragma unroll
-  for (int d = 0; d < DEPTH; ++d) fetch(ra[d], rb[d], d);
+  for (int d = 0; d < DEPTH; ++d)
+    if (!FEW || d < nseg) fetch(ra[d], rb[d], d);
   __syncthreads();
   int cur = 0;
   for (int s0 = 0; s0 < nseg; s0 += DEPTH) {
@@ -601,7 +603,7 @@ __global__ __launch_bounds__(DK >= 128 ? 8 * DK : 4 * DK) void seg_scan_kernel(F
           }
         }
         const float bv = rb[d];
-        fetch(ra[d], rb[d], s + DEPTH);
+        if constexpr (!FEW) fetch(ra[d], rb[d], s + DEPTH);
         // reduce-scatter over the NQ lanes: keep the half, then the pair, then the column
         float n4[4];
         if constexpr (NQ == 8) {
@@ -655,59 +657,75 @@ __global__ __launch_bounds__(256) void seg_fixup_kernel(FwdArgs a) {
   }
 }
 
-// o = O_loc + Qhat H_in(segment) for one chunk of one pair on MFMA, for bfloat16 I/O at
-// d = 128 and 64-token chunks: bfloat16 operands (Qhat as stored, H_in rounded once, as
-// the output itself is), float32 accumulation started from O_loc (stored in bfloat16).  H_in^T of the chunk's
-// segment is staged in LDS with the contraction index permuted inside each 32-block
-// (k = 32 kb + 16 h + 4 q + e at 32 kb + 8 q + 4 h + e), so a lane's 8-value operand
-// (k0 + 4 q .. + 3 and k0 + 16 + 4 q .. + 3) is one 16-byte read; wave w takes token rows
-// 16 w .. 16 w + 15 and all 128 value columns.
+// o = O_loc + Qhat H_in(segment) on MFMA, for bfloat16 I/O at d = 128 and 64-token
+// chunks: bfloat16 operands (Qhat as stored, H_in rounded once, as the output itself is),
+// float32 accumulation started from O_loc (stored in bfloat16).  One workgroup takes
+// kFixupChunks consecutive chunks of a pair and stages H_in^T of their segment in LDS once
+// (again only where a segment starts among them), with the contraction index permuted
+// inside each 32-block (k = 32 kb + 16 h + 4 q + e at 32 kb + 8 q + 4 h + e) so a lane's
+// 8-value operand (k0 + 4 q .. + 3 and k0 + 16 + 4 q .. + 3) is one 16-byte read.  Wave w
+// takes token rows 16 w .. 16 w + 15 of each chunk and forms o^T = H_in^T Qhat^T + O_loc^T:
+// lane (li, q) of tile vt holds value columns 16 vt + 4 q .. + 3 of token 16 w + li, so
+// O_loc is read and o written 8 bytes at a time.
+constexpr int kFixupChunks = 4;
+
 template <int D, int C>
 __global__ __launch_bounds__(256) void seg_fixup_mfma_kernel(FwdArgs a) {
   static_assert(D == 128 && C == 64, "written for d = 128 and 64-token chunks");
   constexpr int LH = D + 8;  // row stride of the staged H_in^T (bfloat16 elements)
   __shared__ __align__(16) bf16_t sHt[D * LH];
   const int tid = threadIdx.x, w = wave_id(), l = lane_id(), q = l >> 4, li = l & 15;
-  const int c = blockIdx.x, pr = blockIdx.y;
-  const int seg = c / a.seg_chunks;
-  const int t0 = c * C, nvalid = min(C, a.T - t0);
+  const int pr = blockIdx.y;
+  const int c_lo = blockIdx.x * kFixupChunks, c_hi = min(a.nch, c_lo + kFixupChunks);
   const int Tpad = a.nch * C;
-  const float* Hi = a.Hin + ((size_t)pr * a.nseg + seg) * D * D;  // [k][col]
-  for (int idx = tid; idx < D * D; idx += 256) {
-    const int k = idx / D, col = idx % D;
-    const int kp = (k & ~31) | ((k & 12) << 1) | ((k & 16) >> 2) | (k & 3);
-    sHt[col * LH + kp] = (bf16_t)Hi[idx];
-  }
-  // this wave's Qhat rows as A operands (4 blocks of 32 along k)
-  const int row = 16 * w + li;
-  const bf16_t* qh = reinterpret_cast<const bf16_t*>(a.Qhat) + ((size_t)pr * Tpad + t0 + row) * D;
-  bf16x8 af[D / 32];
+  int staged = -1;
+  for (int c = c_lo; c < c_hi; ++c) {
+    const int seg = c / a.seg_chunks;  // the same for every thread of the workgroup
+    const int t0 = c * C, nvalid = min(C, a.T - t0);
+    if (seg != staged) {
+      if (staged >= 0) __syncthreads();  // every read of the previous segment's H_in is done
+      const float* Hi = a.Hin + ((size_t)pr * a.nseg + seg) * D * D;  // [k][col]
+      for (int idx = tid; idx < D * D; idx += 256) {
+        const int k = idx / D, col = idx % D;
+        const int kp = (k & ~31) | ((k & 12) << 1) | ((k & 16) >> 2) | (k & 3);
+        sHt[col * LH + kp] = (bf16_t)Hi[idx];
+      }
+      __syncthreads();
+      staged = seg;
+    }
+    // this wave's Qhat rows as B operands (4 blocks of 32 along k)
+    const int row = 16 * w + li;
+    const bf16_t* qh = reinterpret_cast<const bf16_t*>(a.Qhat) + ((size_t)pr * Tpad + t0 + row) * D;
+    bf16x8 bq[D / 32];
 #pragma unroll
-  for (int kb = 0; kb < D / 32; ++kb) {
-    const bf16x4 x0 = *reinterpret_cast<const bf16x4*>(qh + 32 * kb + 4 * q);
-    const bf16x4 x1 = *reinterpret_cast<const bf16x4*>(qh + 32 * kb + 16 + 4 * q);
-    af[kb] = __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
-  }
-  // accumulators from O_loc: lane (li, q) of tile vt holds rows 16 w + 4 q + r, column 16 vt + li
-  const bf16_t* ol = reinterpret_cast<const bf16_t*>(a.Oloc) + ((size_t)pr * Tpad + t0 + 16 * w + 4 * q) * D;
-  f32x4 acc[D / 16];
+    for (int kb = 0; kb < D / 32; ++kb) {
+      const bf16x4 x0 = *reinterpret_cast<const bf16x4*>(qh + 32 * kb + 4 * q);
+      const bf16x4 x1 = *reinterpret_cast<const bf16x4*>(qh + 32 * kb + 16 + 4 * q);
+      bq[kb] = __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+    const size_t rowoff = ((size_t)pr * Tpad + t0 + row) * D;
+    const bf16_t* ol = reinterpret_cast<const bf16_t*>(a.Oloc) + rowoff;
+    f32x4 acc[D / 16];
 #pragma unroll
-  for (int vt = 0; vt < D / 16; ++vt)
+    for (int vt = 0; vt < D / 16; ++vt) {
+      const bf16x4 x = *reinterpret_cast<const bf16x4*>(ol + 16 * vt + 4 * q);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) acc[vt][r] = (float)ol[(size_t)r * D + 16 * vt + li];
-  __syncthreads();
+      for (int r = 0; r < 4; ++r) acc[vt][r] = (float)x[r];
+    }
 #pragma unroll
-  for (int vt = 0; vt < D / 16; ++vt)
+    for (int vt = 0; vt < D / 16; ++vt)
 #pragma unroll
-    for (int kb = 0; kb < D / 32; ++kb)
-      acc[vt] = mfma(af[kb], *reinterpret_cast<const bf16x8*>(&sHt[(16 * vt + li) * LH + 32 * kb + 8 * q]), acc[vt]);
-  bf16_t* o = reinterpret_cast<bf16_t*>(a.o) + ((size_t)pr * a.T + t0) * D;
+      for (int kb = 0; kb < D / 32; ++kb)
+        acc[vt] = mfma(*reinterpret_cast<const bf16x8*>(&sHt[(16 * vt + li) * LH + 32 * kb + 8 * q]), bq[kb], acc[vt]);
+    if (row < nvalid) {
+      bf16_t* o = reinterpret_cast<bf16_t*>(a.o) + ((size_t)pr * a.T + t0 + row) * D;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int t = 16 * w + 4 * q + r;
-    if (t < nvalid) {
+      for (int vt = 0; vt < D / 16; ++vt) {
+        bf16x4 y;
 #pragma unroll
-      for (int vt = 0; vt < D / 16; ++vt) o[(size_t)t * D + 16 * vt + li] = (bf16_t)acc[vt][r];
+        for (int r = 0; r < 4; ++r) y[r] = (bf16_t)acc[vt][r];
+        *reinterpret_cast<bf16x4*>(o + 16 * vt + 4 * q) = y;
+      }
     }
   }
 }

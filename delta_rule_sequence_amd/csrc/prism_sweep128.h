@@ -358,7 +358,7 @@ __device__ __forceinline__ void sweep128_kwave(const Sweep128Ctx& x, int wq) {
           }
         }
       }
-      if (lv == 3) {  // WH = Wc H(:, cb), Wc from phase 2
+      if (lv == NL) {  // WH = Wc H(:, cb), Wc from phase 2 (formed last: fewer live registers)
         bf16x8 hf[4];
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) hf[kb] = pair8(H[2 * kb], H[2 * kb + 1]);
@@ -376,8 +376,8 @@ __device__ __forceinline__ void sweep128_kwave(const Sweep128Ctx& x, int wq) {
         row_store(lpf, V.slotU(s ^ 1), tq);
         if (lv + 2 <= Lm1) row_fetch(lpf, x.ru_, tq, t0, x.urow, (lv + 1) * 256);
       }
-      // next chunk's inputs, once this chunk's last rank-L prefetch is consumed
-      if (lv == (Lm1 >= 2 ? Lm1 - 1 : 1)) fetch_chunk(cn);
+      // next chunk's inputs in the last level phase (fewer live registers before it)
+      if (lv == NL) fetch_chunk(cn);
       if (lv == NL) {  // (beta V')^T rows rb for the per-column solve
         const float4 be = *reinterpret_cast<const float4*>(V.sBeta + 16 * rb + g4);
 #pragma unroll
@@ -449,7 +449,7 @@ __device__ __forceinline__ void sweep128_qwave(const Sweep128Ctx& x, int wq) {
   const int NL = Lm1 > 3 ? Lm1 : 3, L = Lm1 + 1;
   const int vcol = 128 * x.h + 2 * c4;  // byte offset of this thread's 4 value columns
 
-  f32x4 A[8], O[4], WA[4];
+  f32x4 A[8], O[4], WA[4];  // O^T tiles: [value 16 vt ..][token 16 rb ..]
   float rr[4][4];  // residual r_l of this lane's 4x4 block [row][col]
   float dec[4][4];
   bf16x8 Pa[2];
@@ -565,7 +565,7 @@ __device__ __forceinline__ void sweep128_qwave(const Sweep128Ctx& x, int wq) {
     if (Lm1 >= 2) quad_fetch<4>(lpf, x.rg_, (t0 + 4 * rq) * x.urow + 256 + vcol, x.urow);  // gamma_1
     __syncthreads();  // B1
 
-    // ---- P1 .. P_NL: rank-L steps; M^-1 (P1), WA, Qhat (P3) ---------------------------------
+    // ---- P1 .. P_NL: rank-L steps; M^-1 (P1), WA and Qhat (P_NL) -----------------------------
     auto level_phase = [&](const int lv) {
       const int s = (lv - 1) & 1;
       if (lv <= Lm1) {  // O += lower(Gam * Q U_l^T) R_l
@@ -575,8 +575,8 @@ __device__ __forceinline__ void sweep128_qwave(const Sweep128Ctx& x, int wq) {
         gram_rows128(xa, sU, V.sQ, rb, dec, 1.f);
 #pragma unroll
         for (int vt = 0; vt < 4; ++vt) {
-          O[vt] = mfma(xa[0], lfragL<LC>(sRt, 16 * vt, 0), O[vt]);
-          if (rb >= 2) O[vt] = mfma(xa[1], lfragL<LC>(sRt, 16 * vt, 32), O[vt]);
+          O[vt] = mfma(lfragL<LC>(sRt, 16 * vt, 0), xa[0], O[vt]);
+          if (rb >= 2) O[vt] = mfma(lfragL<LC>(sRt, 16 * vt, 32), xa[1], O[vt]);
         }
       }
       if (lv == 1) {
@@ -612,7 +612,8 @@ __device__ __forceinline__ void sweep128_qwave(const Sweep128Ctx& x, int wq) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) V.sMinv[(16 * i + g4 + r) * LC + pcol(16 * cb + li)] = xv[r];
         }
-      } else if (lv == 3) {
+      }
+      if (lv == NL) {
         // WA = Wc A_acc(:, cb)
         bf16x8 af[4];
 #pragma unroll
@@ -662,7 +663,7 @@ __device__ __forceinline__ void sweep128_qwave(const Sweep128Ctx& x, int wq) {
         if (lv + 2 <= Lm1)
           quad_fetch<4>(lpf, x.rg_, (t0 + 4 * rq) * x.urow + (lv + 1) * 256 + vcol, x.urow);
       }
-      if (lv == (Lm1 >= 2 ? Lm1 - 1 : 1)) fetch_chunk(cn);
+      if (lv == NL) fetch_chunk(cn);
       __syncthreads();
     };
     if constexpr (LM1S >= 0) {
@@ -675,19 +676,18 @@ __device__ __forceinline__ void sweep128_qwave(const Sweep128Ctx& x, int wq) {
     // ---- P_S: O += diag(G) Q H;  A_acc(:, cb) = G_C A_acc - K^T D WA ---------------------------
     {
       const float GC = V.sG[C - 1];
-      const float4 G4 = *reinterpret_cast<const float4*>(V.sG + 16 * rb + g4);
-      const float Gr[4] = {G4.x, G4.y, G4.z, G4.w};
+      const float Gi = V.sG[16 * rb + li];
       bf16x8 qf[4];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) qf[kb] = lfragL<LK>(V.sQ, 16 * rb, 32 * kb);
 #pragma unroll
-      for (int vt = 0; vt < 4; ++vt) {
-        f32x4 qh = mfma(qf[0], lfragL<LK>(V.sHt, 16 * vt, 0), zero4());
-        f32x4 qh2 = mfma(qf[2], lfragL<LK>(V.sHt, 16 * vt, 64), zero4());
-        qh = mfma(qf[1], lfragL<LK>(V.sHt, 16 * vt, 32), qh);
-        qh2 = mfma(qf[3], lfragL<LK>(V.sHt, 16 * vt, 96), qh2);
+      for (int vt = 0; vt < 4; ++vt) {  // O^T += H^T Q^T diag(G)
+        f32x4 qh = mfma(lfragL<LK>(V.sHt, 16 * vt, 0), qf[0], zero4());
+        f32x4 qh2 = mfma(lfragL<LK>(V.sHt, 16 * vt, 64), qf[2], zero4());
+        qh = mfma(lfragL<LK>(V.sHt, 16 * vt, 32), qf[1], qh);
+        qh2 = mfma(lfragL<LK>(V.sHt, 16 * vt, 96), qf[3], qh2);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) O[vt][r] += Gr[r] * (qh[r] + qh2[r]);
+        for (int r = 0; r < 4; ++r) O[vt][r] += Gi * (qh[r] + qh2[r]);
       }
       const bf16x8 w0 = scaled_pair(WA[0], WA[1], V.sD, 0), w1 = scaled_pair(WA[2], WA[3], V.sD, 32);
 #pragma unroll
@@ -703,13 +703,14 @@ __device__ __forceinline__ void sweep128_qwave(const Sweep128Ctx& x, int wq) {
 
     // ---- P_O: O += P E, write O_loc; next chunk's Q, V^T and residual --------------------------
     {
-      bf16_t* orow = x.oloc + (size_t)(t0 + 16 * rb + g4) * 128 + 64 * x.h + li;
+      // lane (li, g) holds O^T[16 vt + g4 + r][16 rb + li]: four adjacent values of token
+      // 16 rb + li, one 8-byte store per tile
+      bf16_t* orow = x.oloc + (size_t)(t0 + 16 * rb + li) * 128 + 64 * x.h + g4;
 #pragma unroll
       for (int vt = 0; vt < 4; ++vt) {
-        O[vt] = mfma(Pa[0], lfragL<LC>(V.sEt, 16 * vt, 0), O[vt]);
-        if (rb >= 2) O[vt] = mfma(Pa[1], lfragL<LC>(V.sEt, 16 * vt, 32), O[vt]);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) orow[(size_t)r * 128 + 16 * vt] = (bf16_t)O[vt][r];
+        O[vt] = mfma(lfragL<LC>(V.sEt, 16 * vt, 0), Pa[0], O[vt]);
+        if (rb >= 2) O[vt] = mfma(lfragL<LC>(V.sEt, 16 * vt, 32), Pa[1], O[vt]);
+        *reinterpret_cast<bf16x4*>(orow + 16 * vt) = to_bf16x4(O[vt]);
       }
     }
     if (c + 1 < x.c_end) store_chunk();
