@@ -3,6 +3,8 @@
 // Host side only: argument validation, workspace layout, segment sizing and the
 // three kernel launches.  Every check runs before anything is enqueued.
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
 #include <stdint.h>
 
 #include <mutex>
@@ -110,16 +112,18 @@ prism_status make_plan(int B, int H, int T, int dk, int dv, int L, int chunk, pr
   } else if (seg_chunks == 0) {
     // the generic and the half-split sweeps run one workgroup per CU (two per segment for
     // the half-split one): the sweep takes about (rounds of kCUs workgroups) x (chunks per
-    // segment) chunk times, and every segment adds one step of the inter-segment scan
-    // (~0.1 of a generic chunk at d = 128, ~0.15 of a half-split one, measured)
+    // segment) chunk times.  The inter-segment scan adds, in chunk times, ~0.1 per segment
+    // after a generic sweep; after the half-split one the larger of its chain (~0.19 per
+    // segment) and its total work over the GPU (~0.016 per pair and segment), measured at
+    // the 130M-layer and 64K-sequence shapes.
     const size_t per_seg = fast128 ? 2 : 1;
-    const double scan_cost = fast128 ? 0.15 : 0.1;
     double best = 0.0;
     const size_t smax = nch < 1024 ? nch : 1024;
     for (size_t sc = 1; sc <= smax; ++sc) {
       const size_t ns = (nch + sc - 1) / sc;
       const size_t rounds = (P * ns * per_seg + kCUs - 1) / kCUs;
-      const double cost = (double)rounds * (double)sc + scan_cost * (double)ns;
+      const double scan = fast128 ? std::max(0.19 * (double)ns, 0.016 * (double)(P * ns)) : 0.1 * (double)ns;
+      const double cost = (double)rounds * (double)sc + scan;
       if (sc == 1 || cost < best) {
         best = cost;
         seg_chunks = (int)sc;
