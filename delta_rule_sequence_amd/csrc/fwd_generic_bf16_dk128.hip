@@ -10,7 +10,7 @@ namespace host {
 
 // the scan and the output correction of the d = 128 half-split sweep (fwd_fast128_*.hip)
 prism_status launch_tail_bf16_d128(const FwdArgs& a, const LaunchShape& s, hipEvent_t* ev, hipStream_t stream) {
-  return launch_generic_tail<bf16_t, 128, 128, 64>(a, s, ev, stream);
+  return launch_generic_tail<bf16_t, 128, 128, 64, true>(a, s, ev, stream);
 }
 
 }  // namespace host

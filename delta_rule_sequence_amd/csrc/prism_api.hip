@@ -131,9 +131,9 @@ prism_status make_plan(int B, int H, int T, int dk, int dv, int L, int chunk, pr
     }
   }
   const size_t nseg = (nch + seg_chunks - 1) / seg_chunks;
-  // O_loc and Qhat in the I/O type (the fast path's in fragment order); H_in in bfloat16 on
-  // the fast path (the correction's MFMA operand), float32 on the generic path
-  const size_t wel = dt == PRISM_BF16 ? 2 : 4, hel = fast ? 2 : 4;
+  // O_loc and Qhat in the I/O type (the d = 64 fast path's in fragment order); H_in in
+  // bfloat16 on the fast paths (the corrections' MFMA operand), float32 on the generic path
+  const size_t wel = dt == PRISM_BF16 ? 2 : 4, hel = fast || fast128 ? 2 : 4;
   size_t Tpad = nch * (size_t)chunk, a, b, c;
   size_t sz_oloc, sz_qhat, sz_agg_a, sz_agg_b, sz_hin;
   if (!mul_ok(P, Tpad, &a) || !mul_ok(a, (size_t)dv * wel, &sz_oloc)) return PRISM_ERR_INVALID_ARG;

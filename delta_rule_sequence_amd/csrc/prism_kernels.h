@@ -544,8 +544,9 @@ __device__ __forceinline__ float dpp_mov(float x) {
 // partner 7 - q (bit 2) for NQ = 8, then 3 - q (bit 1), then q ^ 1 (bit 0).  One barrier
 // per step.  Eight columns per workgroup at DK = 128 halve the workgroups that read each
 // A_s, against four.  FEW (nseg <= DEPTH): every step's operands come with the first loads,
-// each segment's once.
-template <int DK, int DV, bool FEW = false>
+// each segment's once.  HB16: H_in is stored in bfloat16 in the layout the d = 128 MFMA
+// output correction stages (see seg_fixup_mfma_kernel), else float32 [k][col].
+template <int DK, int DV, bool FEW = false, bool HB16 = false>
 __global__ __launch_bounds__(DK >= 128 ? 8 * DK : 4 * DK) void seg_scan_kernel(FwdArgs a) {
   constexpr int NQ = DK >= 128 ? 8 : 4;       // contraction slices = columns per workgroup
   static_assert(DV % NQ == 0, "NQ state columns per workgroup");
@@ -561,6 +562,9 @@ __global__ __launch_bounds__(DK >= 128 ? 8 * DK : 4 * DK) void seg_scan_kernel(F
   const float* A0 = a.Aagg + (size_t)pr * nseg * DK * DK + (size_t)i * DK + q * KQ;
   const float* B0 = a.Bagg + (size_t)pr * nseg * DK * DV + (size_t)i * DV + col;
   float* H0 = a.Hin + (size_t)pr * nseg * DK * DV + (size_t)i * DV + col;
+  // bfloat16 H_in^T [col][k'] with k' = k permuted inside each 32-block
+  const int ip = (i & ~31) | ((i & 12) << 1) | ((i & 16) >> 2) | (i & 3);
+  bf16_t* Hb = reinterpret_cast<bf16_t*>(a.Hin) + (size_t)pr * nseg * DK * DV + (size_t)col * DK + ip;
   auto hrow = [](int r) { return r + r / KQ; };
   float h = a.S0 != nullptr ? a.S0[(size_t)pr * DK * DV + (size_t)i * DV + col] : 0.f;
   reinterpret_cast<float*>(&sH[0][hrow(i)][0])[q] = h;
@@ -583,7 +587,8 @@ __global__ __launch_bounds__(DK >= 128 ? 8 * DK : 4 * DK) void seg_scan_kernel(F
     for (int d = 0; d < DEPTH; ++d) {
       const int s = s0 + d;
       if (s < nseg) {
-        H0[(size_t)s * DK * DV] = h;
+        if constexpr (HB16) Hb[(size_t)s * DK * DV] = (bf16_t)h;
+        else H0[(size_t)s * DK * DV] = h;
         float v[NQ];
 #pragma unroll
         for (int c = 0; c < NQ; ++c) v[c] = 0.f;
@@ -669,7 +674,7 @@ __global__ __launch_bounds__(256) void seg_fixup_kernel(FwdArgs a) {
 // O_loc is read and o written 8 bytes at a time.
 constexpr int kFixupChunks = 4;
 
-template <int D, int C>
+template <int D, int C, bool HB16 = false>
 __global__ __launch_bounds__(256) void seg_fixup_mfma_kernel(FwdArgs a) {
   static_assert(D == 128 && C == 64, "written for d = 128 and 64-token chunks");
   constexpr int LH = D + 8;  // row stride of the staged H_in^T (bfloat16 elements)
@@ -684,11 +689,18 @@ __global__ __launch_bounds__(256) void seg_fixup_mfma_kernel(FwdArgs a) {
     const int t0 = c * C, nvalid = min(C, a.T - t0);
     if (seg != staged) {
       if (staged >= 0) __syncthreads();  // every read of the previous segment's H_in is done
-      const float* Hi = a.Hin + ((size_t)pr * a.nseg + seg) * D * D;  // [k][col]
-      for (int idx = tid; idx < D * D; idx += 256) {
-        const int k = idx / D, col = idx % D;
-        const int kp = (k & ~31) | ((k & 12) << 1) | ((k & 16) >> 2) | (k & 3);
-        sHt[col * LH + kp] = (bf16_t)Hi[idx];
+      if constexpr (HB16) {  // already bfloat16 [col][k'] (the scan's layout): 16-byte copies
+        const uint4* Hb = reinterpret_cast<const uint4*>(reinterpret_cast<const bf16_t*>(a.Hin) +
+                                                         ((size_t)pr * a.nseg + seg) * D * D);
+        for (int idx = tid; idx < D * D / 8; idx += 256)
+          *reinterpret_cast<uint4*>(&sHt[(idx >> 4) * LH + 8 * (idx & 15)]) = Hb[idx];
+      } else {
+        const float* Hi = a.Hin + ((size_t)pr * a.nseg + seg) * D * D;  // [k][col]
+        for (int idx = tid; idx < D * D; idx += 256) {
+          const int k = idx / D, col = idx % D;
+          const int kp = (k & ~31) | ((k & 12) << 1) | ((k & 16) >> 2) | (k & 3);
+          sHt[col * LH + kp] = (bf16_t)Hi[idx];
+        }
       }
       __syncthreads();
       staged = seg;
