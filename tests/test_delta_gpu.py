@@ -149,6 +149,20 @@ def test_fwd_delta_multichunk_segments(prism, L, seg):
     _check_fwd(w, o, S, _oracle(w, x), f"L={L} seg={seg}")
 
 
+@pytest.mark.parametrize("L", [2, 3, 5, 8])
+def test_fwd_delta_half_split_segments(prism, L):
+    """The d = 128 written-correction half-split sweep with segments of three chunks."""
+    import torch
+    w = W("dl_seg128", "bf16", B=2, H=1, T=5 * 64 + 21, dk=128, dv=128, L=L, chunk=64, seed=200 + L)
+    x = _inputs(w)
+    log(f"[delta fwd] d=128 L={L} seg=3 T={w.T}")
+    d = _dev(x, w)
+    o, S = prism.fwd_delta(d["q"], d["k"], d["v"], d["g"], d["beta"], d["u"], d["alpha"], d["p"], d["conv_w"],
+                           L=w.L, chunk=w.chunk, seg_chunks=3)
+    torch.cuda.synchronize()
+    _check_fwd(w, o, S, _oracle(w, x), f"d128 L={L} seg=3")
+
+
 def test_fwd_delta_generic_multichunk_segments(prism):
     import torch
     w = W("dl_gseg", "f32", B=1, H=2, T=7 * 32 + 5, dk=32, dv=32, L=4, chunk=32, seed=189)

@@ -191,6 +191,18 @@ def test_fast_sweep_multichunk_segments(prism, L, seg):
     check(w, run_gpu(prism, w, x, seg=seg), run_oracle(w, x), f" L={L} seg={seg}")
 
 
+# The bf16 d = 128 half-split sweep (two workgroups per segment, one per value half): every
+# L it is instantiated for, with segments of several chunks and a ragged last chunk.
+@pytest.mark.parametrize("seg", [2, 3])
+@pytest.mark.parametrize("L", [1, 2, 3, 4, 5, 6, 7, 8])
+def test_half_split_sweep_multichunk_segments(prism, L, seg):
+    w = workloads.Workload("d128seg", "bf16", B=2, H=1, T=6 * 64 + 35, dk=128, dv=128, L=L, chunk=64,
+                           seed=140 + L)
+    x = workloads.generate(w)
+    log(f"[parity] d=128 half-split sweep L={L} seg={seg} T={w.T}")
+    check(w, run_gpu(prism, w, x, seg=seg), run_oracle(w, x), f" d128 L={L} seg={seg}")
+
+
 GENERIC_SEG = [
     # (dtype, d, chunk, L)
     ("f32", 16, 16, 3), ("f32", 32, 32, 4), ("f32", 64, 32, 2), ("f32", 64, 64, 5),
