@@ -26,8 +26,9 @@ prism_status launch_fast128(const FwdArgs& a, const LaunchShape& s, hipEvent_t* 
                             ChainForm form) {
   if (!record(ev, 0, stream)) return PRISM_ERR_HIP;
   const dim3 grid(s.nseg, s.P, 2);
-  const bool ok = form == ChainForm::kDelta ? launch_sweep128_delta(a, grid, stream)
-                                            : launch_sweep128_linear(a, grid, stream);
+  const bool ok = form == ChainForm::kDelta  ? launch_sweep128_delta(a, grid, stream)
+                  : form == ChainForm::kGelu ? launch_sweep128_nl(a, grid, stream)
+                                             : launch_sweep128_linear(a, grid, stream);
   if (!ok) return PRISM_ERR_UNSUPPORTED;
   if (hipGetLastError() != hipSuccess || !record(ev, 1, stream)) return PRISM_ERR_HIP;
   return launch_tail_bf16_d128(a, s, ev, stream);

@@ -207,7 +207,7 @@ prism_status fwd_impl(const void* q, const void* k, const void* v, const float* 
   a.B = B; a.H = H; a.T = T; a.L = L;
   a.nch = pl.nch; a.seg_chunks = pl.seg_chunks; a.nseg = pl.nseg;
   a.chain_delta = form == ChainForm::kDelta ? 1 : 0;
-  if (form == ChainForm::kGelu && !pl.fast) return PRISM_ERR_UNSUPPORTED;
+  if (form == ChainForm::kGelu && !pl.fast && !pl.fast128) return PRISM_ERR_UNSUPPORTED;
   const prism::host::LaunchShape shape{pl.P, pl.nch, pl.nseg};
   if (pl.fast)
     st = prism::host::launch_fast(a, shape, ev, stream, L > 1 ? form : ChainForm::kLinear);
@@ -572,8 +572,9 @@ prism_status fwd_nl_impl(const void* q, const void* k, const void* v, const floa
   const size_t off = align_up(gb);
   if (!workspace || workspace_bytes < off + pl.total) return PRISM_ERR_WORKSPACE;
   char* ws = static_cast<char*>(workspace);
-  // the bf16 d = 64 sweep evaluates the factors in its own residual chain: no factor pass
-  if (pl.fast && L > 1)
+  // the bf16 d = 64 and d = 128 sweeps evaluate the factors in their own residual chain:
+  // no factor pass
+  if ((pl.fast || pl.fast128) && L > 1)
     return fwd_impl(q, k, v, g, beta, u, alpha, p, conv_w, B, H, T, dk, dv, L, chunk, dt, o, S_final,
                     ws + off, workspace_bytes - off, seg_chunks, nullptr, stream, nullptr, nullptr, nullptr,
                     ChainForm::kGelu);

@@ -65,6 +65,7 @@ prism_status launch_fast128(const FwdArgs& a, const LaunchShape& s, hipEvent_t* 
 // (false: no instantiation for a.L)
 bool launch_sweep128_linear(const FwdArgs& a, dim3 grid, hipStream_t stream);
 bool launch_sweep128_delta(const FwdArgs& a, dim3 grid, hipStream_t stream);
+bool launch_sweep128_nl(const FwdArgs& a, dim3 grid, hipStream_t stream);
 prism_status launch_tail_bf16_d128(const FwdArgs& a, const LaunchShape& s, hipEvent_t* ev, hipStream_t stream);
 
 // The backward (prism_bwd.h).  launch_bwd: with segments the segment-parallel passes

@@ -282,9 +282,9 @@ prism_status prism_nl_gain(const void* v, const float* alpha, const void* p, con
                            void* gamma, hipStream_t stream);
 
 /* The nonlinear-refinement forward in one call: prism_nl_gain into the front of the
- * workspace, then prism_fwd with those factors.  On the bfloat16 dk = dv = 64, chunk 64
- * path the sweep evaluates the same rounded factors in its own residual chain instead
- * (no factor pass; identical results).  Arguments as prism_fwd with the gains p in place
+ * workspace, then prism_fwd with those factors.  On the bfloat16 dk = dv = 64 and
+ * dk = dv = 128, chunk 64 paths the sweep evaluates the same rounded factors in its own
+ * residual chain instead (no factor pass; identical results).  Arguments as prism_fwd with the gains p in place
  * of gamma (p may be NULL when L == 1).  Workspace: prism_fwd_nl_workspace_bytes (room for
  * the factors, 256-byte aligned, plus prism_fwd_workspace_bytes). */
 size_t prism_fwd_nl_workspace_bytes(int B, int H, int T, int dk, int dv, int L, int chunk,

@@ -284,6 +284,26 @@ def test_nl_sweep_multichunk_segments(prism, L, seg):
     assert eo <= TOL[w.dtype] and es <= TOL[w.dtype]
 
 
+@pytest.mark.parametrize("L", [2, 5, 8])
+def test_nl_half_split_sweep_segments(prism, L):
+    """The nonlinear d = 128 half-split sweep (factors formed in its chain) with segments of
+    three chunks and a ragged tail, against the token-by-token oracle."""
+    import torch
+    w = workloads.Workload("nl_seg128", "bf16", B=2, H=1, T=5 * 64 + 29, dk=128, dv=128, L=L, chunk=64,
+                           seed=160 + L)
+    x = _inputs(w)
+    log(f"[nl fwd] d=128 L={L} seg=3 T={w.T}")
+    d = _dev(x, w)
+    o, S = prism.fwd_nl(d["q"], d["k"], d["v"], d["g"], d["beta"], d["u"], d["alpha"], d["p"], d["conv_w"],
+                        L=w.L, chunk=w.chunk, seg_chunks=3)
+    torch.cuda.synchronize()
+    ref_o, ref_S = onl.forward_nl(x["q"], x["k"], x["v"], x["g"], x["beta"], x["u"], x["alpha"], x["p"],
+                                  x["conv_w"], w.L)
+    eo, es = rel_err(o.float().cpu().numpy(), ref_o), rel_err(S.cpu().numpy(), ref_S)
+    log(f"  rel err o {eo:.3e}  S_final {es:.3e} (tol {TOL[w.dtype]:.0e})")
+    assert eo <= TOL[w.dtype] and es <= TOL[w.dtype]
+
+
 def test_nl_full_size_16k_against_oracle(prism):
     """The fused nonlinear forward at the 16K workload (B2 H4 T16384 d64 L4, planner's
     segments of 8 chunks) against the token-by-token oracle on head 1 (both batches)."""
