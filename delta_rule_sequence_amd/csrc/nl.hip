@@ -21,6 +21,7 @@ prism_status launch_gain(const NlArgs& a, prism_dtype dt, dim3 grid, bool delta,
 template <int D>
 void launch_pred_d(const NlPredArgs& a, dim3 grid, bool front, hipStream_t stream) {
   if (front) hipLaunchKernelGGL((nl_pred_gain_kernel<D, true, true>), grid, dim3(256), 0, stream, a);
+  else if constexpr (D == 128) hipLaunchKernelGGL((nl_pred_gain_lds_kernel<D>), grid, dim3(256), 0, stream, a);
   else hipLaunchKernelGGL((nl_pred_gain_kernel<D, false, false>), grid, dim3(256), 0, stream, a);
 }
 

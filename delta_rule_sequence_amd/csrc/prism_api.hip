@@ -629,7 +629,8 @@ prism_status prism_nl_gain_pred(const void* v, const float* alpha, const void* W
   size_t P, bytes;
   if (!mul_ok((size_t)B, (size_t)H, &P) || !nl_gamma_bytes(B, H, T, dv, L, dt, &bytes)) return PRISM_ERR_INVALID_ARG;
   if (P > 65535) return PRISM_ERR_UNSUPPORTED;
-  const size_t wg_tokens = dv == 64 ? 256 : 64;  // 4 waves x 16 tokens x tiles per wave
+  // tokens per workgroup: 4 waves x 4 tiles of 16 at dv = 64, x 2 tiles at 128, else x 1
+  const size_t wg_tokens = dv == 64 ? 256 : dv == 128 ? 128 : 64;
   const dim3 grid((unsigned)(((size_t)T + wg_tokens - 1) / wg_tokens), (unsigned)P);
   prism::NlPredArgs a = {};
   a.v = v; a.alpha = alpha; a.W_p = W_p; a.conv_w = conv_w; a.conv_in = conv_in; a.gamma = gamma;

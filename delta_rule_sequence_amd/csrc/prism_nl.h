@@ -384,4 +384,153 @@ void nl_pred_gain_kernel(NlPredArgs a) {
   }
 }
 
+// The d = 128 gains-only pass (linear chain) with the weights shared through LDS: a
+// workgroup of 4 waves (one per SIMD, the registers of two) takes 128 consecutive tokens
+// (wave w: two 16-token tiles, its value window and step sizes in LDS as above), and each
+// level's W_p[h, l] (32 KB) is copied from memory into LDS once per workgroup, the next
+// level's while the current one is used (two buffers, one barrier per level);
+// nl_pred_gain_kernel at d = 128 reads a level's weights once per 16-token tile and wave.
+// The anchors, residuals, products and chain are those of nl_pred_gain_kernel<128, false,
+// false>.
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void nl_pred_gain_lds_kernel(NlPredArgs a) {
+  static_assert(D == 128, "the weights of one level fill 32 KB of LDS at d = 128");
+  constexpr int NW = 4, TPW = 2, ROWS = 16 * TPW + 3, LDV = D + 8, LDW = D + 8;
+  constexpr int KB = D / 32, NT = D / 16, PIECES = D / 8;
+  __shared__ __align__(16) bf16_t sV[NW][ROWS * LDV];  // per wave: value rows tw-3 .. tw+31
+  __shared__ float sA[NW][16 * TPW * 8];               // per wave: step sizes [token][level]
+  __shared__ __align__(16) bf16_t sW[2][D * LDW];     // the current and the next level's W_p
+  const int w = wave_id(), l = lane_id(), li = l & 15, g = l >> 4, tid = threadIdx.x;
+  const int pr = blockIdx.y, hd = pr % a.H, T = a.T, L = a.L, Lm1 = L - 1;
+  const int tw = (blockIdx.x * NW + w) * 16 * TPW;
+  const bf16_t* v = reinterpret_cast<const bf16_t*>(a.v) + (size_t)pr * T * D;
+  const bf16_t* ci = a.conv_in != nullptr ? reinterpret_cast<const bf16_t*>(a.conv_in) + (size_t)pr * 3 * D : nullptr;
+  const bf16_t* Wh = reinterpret_cast<const bf16_t*>(a.W_p) + (size_t)hd * Lm1 * D * D;
+  bf16_t* sv = sV[w];
+  // rows before the sequence come from the history (else zero); rows past its end are zero
+  for (int i = l; i < ROWS * PIECES; i += 64) {
+    const int rr = i / PIECES, cv = (i % PIECES) * 8;
+    const int s = tw - 3 + rr;
+    uint4 x = make_uint4(0u, 0u, 0u, 0u);
+    if (s >= 0 && s < T)
+      x = *reinterpret_cast<const uint4*>(v + (size_t)s * D + cv);
+    else if (s < 0 && ci != nullptr)
+      x = *reinterpret_cast<const uint4*>(ci + (size_t)(s + 3) * D + cv);
+    *reinterpret_cast<uint4*>(sv + rr * LDV + cv) = x;
+  }
+  {
+    const float* al = a.alpha + (size_t)pr * T * L;
+    for (int i = l; i < 16 * TPW * L; i += 64) {
+      const int tok = tw + i / L;
+      sA[w][i] = tok < T ? al[(size_t)tok * L + i % L] : 0.f;
+    }
+  }
+  // level 0's weights: 2048 16-byte pieces, eight per thread
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int i = tid + 64 * NW * q, row = i / PIECES, c8 = (i % PIECES) * 8;
+    *reinterpret_cast<uint4*>(sW[0] + row * LDW + c8) = *reinterpret_cast<const uint4*>(Wh + (size_t)row * D + c8);
+  }
+  __syncthreads();
+  const float* cw = a.conv_w + (size_t)hd * 4 * D;
+  // A operands: anchor of token 16 j + li, channels 32 kb + 8 g .. + 7
+  bf16x8 an[TPW][KB];
+#pragma unroll
+  for (int j = 0; j < TPW; ++j)
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      const int c0 = 32 * kb + 8 * g;
+      float s8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt) {
+        float x[8];
+        bf_load<8>(sv + (16 * j + li + jt) * LDV + c0, x);
+        const float4 wa = *reinterpret_cast<const float4*>(cw + jt * D + c0);
+        const float4 wb = *reinterpret_cast<const float4*>(cw + jt * D + c0 + 4);
+        const float wt[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
+#pragma unroll
+        for (int q = 0; q < 8; ++q) s8[q] += wt[q] * x[q];
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) an[j][kb][q] = (bf16_t)s8[q];
+    }
+  // residuals of tokens 16 j + 4 g + rr, channels NT li + nt
+  const int cl = NT * li;
+  float r[TPW][4][NT];
+  {
+    float wt[4][NT];
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) wt[jt][nt] = cw[jt * D + cl + nt];
+#pragma unroll
+    for (int j = 0; j < TPW; ++j)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int tok = 16 * j + 4 * g + rr;  // window rows tok .. tok + 3, the token itself last
+        float x0[NT], x1[NT], x2[NT], x3[NT];
+        bf_load<NT>(sv + tok * LDV + cl, x0);
+        bf_load<NT>(sv + (tok + 1) * LDV + cl, x1);
+        bf_load<NT>(sv + (tok + 2) * LDV + cl, x2);
+        bf_load<NT>(sv + (tok + 3) * LDV + cl, x3);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          r[j][rr][nt] = x3[nt] - (wt[0][nt] * x0[nt] + wt[1][nt] * x1[nt] + wt[2][nt] * x2[nt] + wt[3][nt] * x3[nt]);
+      }
+  }
+  bf16_t* gout = reinterpret_cast<bf16_t*>(a.gamma) + (size_t)pr * T * Lm1 * D;
+  for (int lv = 0; lv < Lm1; ++lv) {
+    // the next level's weights into registers while this level's are used
+    const bool more = lv + 1 < Lm1;
+    uint4 wn[8];
+    if (more) {
+      const bf16_t* Wn = Wh + (size_t)(lv + 1) * D * D;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int i = tid + 64 * NW * q;
+        wn[q] = *reinterpret_cast<const uint4*>(Wn + (size_t)(i / PIECES) * D + (i % PIECES) * 8);
+      }
+    }
+    const bf16_t* sw = sW[lv & 1];
+    bf16_t fb[TPW][4][NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      // B operand of output tile nt: row NT li + nt of W_p, so lane (li, g) ends with p for
+      // tokens 4 g + rr and the NT adjacent channels NT li ..
+      bf16x8 wf[KB];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) wf[kb] = *reinterpret_cast<const bf16x8*>(sw + (cl + nt) * LDW + 32 * kb + 8 * g);
+#pragma unroll
+      for (int j = 0; j < TPW; ++j) {
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) acc = mfma(an[j][kb], wf[kb], acc);
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const float pv = acc[rr];
+          fb[j][rr][nt] = (bf16_t)(pv * std_normal_cdf(pv * r[j][rr][nt]));
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < TPW; ++j)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int tl = 16 * j + 4 * g + rr, tok = tw + tl;
+        const float at = sA[w][tl * L + lv];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) r[j][rr][nt] = r[j][rr][nt] * (1.f - at * (float)fb[j][rr][nt]);
+        if (tok < T) bf_store<NT>(gout + ((size_t)tok * Lm1 + lv) * D + cl, fb[j][rr]);
+      }
+    if (more) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int i = tid + 64 * NW * q;
+        *reinterpret_cast<uint4*>(sW[(lv + 1) & 1] + (i / PIECES) * LDW + (i % PIECES) * 8) = wn[q];
+      }
+    }
+    __syncthreads();
+  }
+}
+
 }  // namespace prism
