@@ -33,3 +33,27 @@ def test_blocked_inverse():
         M = np.eye(C) + np.tril(rng.standard_normal((C, C)) * 0.1, -1)
         T = cm.unit_lower_inverse_blocked(M)
         assert np.max(np.abs(T @ M - np.eye(C))) < 1e-12
+
+
+@pytest.mark.parametrize("T,chunk,L,d,with_dS", [(150, 32, 3, 16, True), (64, 16, 1, 8, False),
+                                                 (100, 64, 4, 16, True), (37, 16, 2, 8, True),
+                                                 (70, 16, 8, 8, False)])
+def test_backward_mirror_matches_gradient_oracle(T, chunk, L, d, with_dS):
+    """The chunked adjoint (per chunk: the readout, end-state, UT-transform and decay
+    terms; across chunks: dH = Qt^T dO + Acc^T dH') against autograd through the token
+    recurrence, every gradient at 1e-11."""
+    from oracle import prism_grad
+    rng = np.random.default_rng(7 + T + L)
+    x = _inputs(rng, B=1, H=1, T=T, dk=d, dv=d, L=L, g_range=(0.9, 1.0))
+    d_o = rng.standard_normal((1, 1, T, d))
+    dS = rng.standard_normal((1, 1, d, d)) if with_dS else None
+    ref = prism_grad.backward(x["q"], x["k"], x["v"], x["g"], x["beta"], x["u"], x["alpha"], x["gamma"],
+                              x["conv_w"], L, d_o, dS)
+    got = cm.backward_chunked(x["q"][0, 0], x["k"][0, 0], x["v"][0, 0], x["g"][0, 0], x["beta"][0, 0],
+                              x["u"][0, 0] if L > 1 else None, x["alpha"][0, 0] if L > 1 else None,
+                              x["gamma"][0, 0] if L > 1 else None, x["conv_w"][0], L, chunk, d_o[0, 0],
+                              None if dS is None else dS[0, 0])
+    names = ["dq", "dk", "dv", "dg", "dbeta"] + (["du", "dalpha", "dgamma", "dconv_w"] if L > 1 else [])
+    for n in names:
+        r = ref[n][0] if n == "dconv_w" else ref[n][0, 0]
+        assert _rel(got[n], r) < 1e-11, n
