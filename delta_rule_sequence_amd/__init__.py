@@ -66,6 +66,10 @@ def load_library() -> ctypes.CDLL:
     lib.prism_bwd_seg_workspace_bytes.restype = sz
     lib.prism_bwd_lowmem.restype = ctypes.c_int
     lib.prism_bwd_lowmem_workspace_bytes.argtypes = [i] * 7
+    lib.prism_bwd_chunked.argtypes = lib.prism_bwd.argtypes
+    lib.prism_bwd_chunked.restype = ctypes.c_int
+    lib.prism_bwd_chunked_workspace_bytes.argtypes = [i] * 7
+    lib.prism_bwd_chunked_workspace_bytes.restype = sz
     lib.prism_bwd_lowmem_workspace_bytes.restype = sz
     lib.prism_fwd_workspace_bytes.argtypes = [i] * 8
     lib.prism_fwd_workspace_bytes.restype = sz
@@ -338,13 +342,15 @@ def fwd(q, k, v, g, beta, u=None, alpha=None, gamma=None, conv_w=None, L: int = 
 
 
 def bwd(q, k, v, g, beta, u=None, alpha=None, gamma=None, conv_w=None, L: int = 1, d_o=None,
-        dS_final=None, workspace=None, stream=None, low_memory: bool = False, seg_len=None):
+        dS_final=None, workspace=None, stream=None, low_memory: bool = False, seg_len=None,
+        chunked: bool = False):
     """Gradients of sum <d_o, o> + <dS_final, S_final> for fwd(q, ..., conv_w, L) (zero start).
 
     Inputs as fwd(); d_o [B,H,T,dv] in the input dtype; dS_final [B,H,dk,dv] float32 or None.
     low_memory: use prism_bwd_lowmem (the sequential form, states every 64 tokens only).
     seg_len: segment length of the segment-parallel form (prism_bwd_seg; a multiple of 8,
     at least 16); None: prism_bwd, which picks it.
+    chunked: use prism_bwd_chunked (chunked form on MFMA; bfloat16, dk = dv = 64).
     Returns a dict of float32 tensors dq, dk, dv, dg, dbeta and, when L > 1, du, dalpha,
     dgamma, dconv_w (the shapes of the corresponding inputs; dconv_w summed over the batch).
     """
@@ -372,9 +378,11 @@ def bwd(q, k, v, g, beta, u=None, alpha=None, gamma=None, conv_w=None, L: int = 
     if L > 1:
         out.update({"du": torch.empty((B, H, T, L - 1, dk), **f32), "dalpha": torch.empty((B, H, T, L), **f32),
                     "dgamma": torch.empty((B, H, T, L - 1, dv), **f32), "dconv_w": torch.empty((H, 4, dv), **f32)})
-    if low_memory and seg_len is not None:
-        raise PrismError("low_memory and seg_len select different forms")
-    if low_memory:
+    if int(low_memory) + int(seg_len is not None) + int(chunked) > 1:
+        raise PrismError("low_memory, seg_len and chunked select different forms")
+    if chunked:
+        name, need = "prism_bwd_chunked", lib.prism_bwd_chunked_workspace_bytes(B, H, T, dk, dv, L, dt)
+    elif low_memory:
         name, need = "prism_bwd_lowmem", lib.prism_bwd_lowmem_workspace_bytes(B, H, T, dk, dv, L, dt)
     elif seg_len is not None:
         name, need = "prism_bwd_seg", lib.prism_bwd_seg_workspace_bytes(B, H, T, dk, dv, L, dt, seg_len)

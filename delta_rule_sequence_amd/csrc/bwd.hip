@@ -1,7 +1,9 @@
 // bwd.hip - launches of the backward (prism_bwd.h): the sequential per-pair adjoint sweep
 // and the segment-parallel passes, the fixed-order sum of per-workgroup partials and the
-// batch sum of dconv_w.
+// batch sum of dconv_w; and the chunked MFMA form (prism_bwd_chunk.h), which shares the
+// segment scans, the anchor carry and the dconv_w sum with the segment-parallel form.
 #include "prism_bwd.h"
+#include "prism_bwd_chunk.h"
 #include "prism_host.h"
 
 namespace prism {
@@ -88,6 +90,21 @@ prism_status launch_bwd(prism_dtype dt, int d, const BwdArgs& a, int B, int P, f
   if (a.L == 1) return PRISM_OK;
   hipLaunchKernelGGL(bwd_conv_reduce_kernel, dim3(a.H, (4 * d + 63) / 64), dim3(256), 0, stream,
                      static_cast<const float*>(a.dconv_part), dconv_w, B, a.H, d, segments ? a.nseg : 1);
+  return hipGetLastError() == hipSuccess ? PRISM_OK : PRISM_ERR_HIP;
+}
+
+// Chunked form: segments of one chunk (a.nseg chunks per pair, a.seg_len = 64).
+prism_status launch_bwd_chunked(const BwdArgs& a, int B, int P, float* dconv_w, hipStream_t stream) {
+  const dim3 grid((unsigned)a.nseg, (unsigned)P);
+  hipLaunchKernelGGL(bwdc::bwdc_local_kernel, grid, dim3(bwdc::NT), 0, stream, a);
+  hipLaunchKernelGGL((bwd_seg_scan_kernel<64>), dim3((unsigned)P, 64 / 4, 2), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(bwdc::bwdc_grad_kernel, grid, dim3(bwdc::NT), 0, stream, a);
+  if (hipGetLastError() != hipSuccess) return PRISM_ERR_HIP;
+  if (a.L == 1) return PRISM_OK;
+  if (a.nseg > 1)
+    hipLaunchKernelGGL(bwd_seg_carry_kernel, dim3((unsigned)P * (unsigned)a.nseg), dim3(256), 0, stream, a, 64);
+  hipLaunchKernelGGL(bwd_conv_reduce_kernel, dim3(a.H, 4), dim3(256), 0, stream,
+                     static_cast<const float*>(a.dconv_part), dconv_w, B, a.H, 64, a.nseg);
   return hipGetLastError() == hipSuccess ? PRISM_OK : PRISM_ERR_HIP;
 }
 

@@ -424,6 +424,84 @@ prism_status prism_bwd_lowmem(const void* q, const void* k, const void* v, const
                   dv_out, dg, dbeta, du, dalpha, dgamma, dconv_w, workspace, workspace_bytes, stream, 0);
 }
 
+}  // extern "C"
+
+namespace {
+
+// Workspace of the chunked backward: per 64-token chunk five float32 64 x 64 matrices
+// (operator, end state from zero, local adjoint, entering state, arriving adjoint), its
+// anchor carry [3][64] and dconv_w share [4][64].
+struct BwdChunkPlan {
+  int P, nch;
+  size_t off_seg, off_carry, off_part, total;
+};
+
+prism_status make_bwd_chunk_plan(int B, int H, int T, int dk, int dv, int L, prism_dtype dt, BwdChunkPlan* pl) {
+  if (B <= 0 || H <= 0 || T <= 0) return PRISM_ERR_INVALID_ARG;
+  if (dt != PRISM_F32 && dt != PRISM_BF16) return PRISM_ERR_INVALID_ARG;
+  if (L < 1 || L > 8) return PRISM_ERR_UNSUPPORTED;
+  if (dt != PRISM_BF16 || dk != 64 || dv != 64) return PRISM_ERR_UNSUPPORTED;
+  size_t P, c, nseg_all, sz_seg, sz_carry, sz_part;
+  if (!mul_ok((size_t)B, (size_t)H, &P) || P > 65535) return PRISM_ERR_INVALID_ARG;
+  if (!mul_ok(P, (size_t)T, &c) || !mul_ok(c, (size_t)L * dk * 4, &c)) return PRISM_ERR_INVALID_ARG;
+  const size_t nch = ((size_t)T + 63) / 64;
+  if (!mul_ok(P, nch, &nseg_all) || nseg_all > (size_t)INT32_MAX) return PRISM_ERR_INVALID_ARG;
+  if (!mul_ok(nseg_all, (size_t)5 * 64 * 64 * 4, &sz_seg) || !mul_ok(nseg_all, (size_t)3 * 64 * 4, &sz_carry) ||
+      !mul_ok(nseg_all, (size_t)4 * 64 * 4, &sz_part))
+    return PRISM_ERR_INVALID_ARG;
+  pl->P = (int)P;
+  pl->nch = (int)nch;
+  pl->off_seg = 0;
+  pl->off_carry = align_up(sz_seg);
+  pl->off_part = align_up(pl->off_carry + sz_carry);
+  pl->total = align_up(pl->off_part + sz_part);
+  return PRISM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t prism_bwd_chunked_workspace_bytes(int B, int H, int T, int dk, int dv, int L, prism_dtype dt) {
+  BwdChunkPlan pl;
+  return make_bwd_chunk_plan(B, H, T, dk, dv, L, dt, &pl) == PRISM_OK ? pl.total : 0;
+}
+
+prism_status prism_bwd_chunked(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                               const void* u, const float* alpha, const void* gamma, const float* conv_w,
+                               int B, int H, int T, int dk, int dv, int L, prism_dtype dt,
+                               const void* d_o, const float* dS_final,
+                               float* dq, float* dk_out, float* dv_out, float* dg, float* dbeta,
+                               float* du, float* dalpha, float* dgamma, float* dconv_w,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  BwdChunkPlan pl;
+  prism_status st = make_bwd_chunk_plan(B, H, T, dk, dv, L, dt, &pl);
+  if (st != PRISM_OK) return st;
+  if (!q || !k || !v || !g || !beta || !d_o || !dq || !dk_out || !dv_out || !dg || !dbeta)
+    return PRISM_ERR_INVALID_ARG;
+  if (L > 1 && (!u || !alpha || !gamma || !conv_w || !du || !dalpha || !dgamma || !dconv_w))
+    return PRISM_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < pl.total) return PRISM_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  prism::BwdArgs a = {};
+  a.q = q; a.k = k; a.v = v; a.u = u; a.gamma = gamma; a.d_o = d_o;
+  a.g = g; a.beta = beta; a.alpha = alpha; a.conv_w = conv_w; a.dS_final = dS_final;
+  a.dq = dq; a.dk = dk_out; a.dv = dv_out; a.dg = dg; a.dbeta = dbeta;
+  a.du = du; a.dalpha = dalpha; a.dgamma = dgamma;
+  const size_t sq = (size_t)pl.P * pl.nch * 64 * 64;
+  float* sg = reinterpret_cast<float*>(ws + pl.off_seg);
+  a.seg_B = sg;
+  a.seg_Phi = sg + sq;
+  a.seg_ell = sg + 2 * sq;
+  a.seg_Sin = sg + 3 * sq;
+  a.seg_Lam = sg + 4 * sq;
+  a.carry = reinterpret_cast<float*>(ws + pl.off_carry);
+  a.dconv_part = reinterpret_cast<float*>(ws + pl.off_part);
+  a.H = H; a.T = T; a.L = L; a.nblk = 0;
+  a.nseg = pl.nch; a.seg_len = 64;
+  return prism::host::launch_bwd_chunked(a, B, pl.P, dconv_w, stream);
+}
+
 
 size_t prism_fwd_workspace_bytes(int B, int H, int T, int dk, int dv, int L, int chunk, prism_dtype dt) {
   Plan pl;

@@ -1,0 +1,873 @@
+// prism_bwd_chunk.h - the backward in chunked (UT / WY) form on MFMA: bfloat16 inputs,
+// dk = dv = 64, chunks of 64 tokens (gfx950).
+//
+// The forward per chunk, with H = S^T (dk x dv) its start state, b = cumsum(log g),
+// G = exp(b), D_j = exp(b_C - b_j), Gam_ij = exp(b_i - b_j) (j <= i), T = (I + A)^-1 with
+// A = strict(diag(beta) (Gam * K K^T)), N_l = strict(Gam * K U_l^T), P = lower(Gam * Q K^T),
+// PU_l = lower(Gam * Q U_l^T), R_l = alpha_l r_l the written values of the residual chain:
+//   V' = V - sum_l N_l R_l,  Uc = T diag(beta) V',  Wc = T diag(beta G) K,  E = Uc - Wc H
+//   O  = diag(G) Q H + P E + sum_l PU_l R_l
+//   H' = G_C H + K^T diag(D) E + sum_l U_l^T diag(D) R_l
+// (the UT transform of the delta rule's chunked form with PRISM's rank-L writes: PRISM
+// reading notes, sections 2.1-2.3; Tencent / PKU article, sections 01-三 and 03-三).  Every
+// step is a matrix product, so its adjoint is a handful of products too.  Given d_o and the
+// adjoint dH' of the chunk's end state:
+//   dE  = P^T dO + diag(D) K dH'             dX1 = T^T dE,  dVp = diag(beta) dX1
+//   dWc = -dE H^T,  dX2 = T^T dWc            dA  = strict(-T^T (dE Uc^T + dWc Wc^T))
+//   dQ  = diag(G) dO H^T + (Gam*dP) K + sum_l (Gam*dPU_l) U_l,  dP = lower(dO E^T), dPU_l = lower(dO R_l^T)
+//   dK  = diag(D) E dH'^T + (Gam*dP)^T Q + diag(beta G) dX2 + Z K + Z^T K + sum_l (Gam*dN_l) U_l
+//         with Z = diag(beta) Gam * dA and dN_l = strict(-dVp R_l^T)
+//   dU_l = diag(D) R_l dH'^T + (Gam*dPU_l)^T Q + (Gam*dN_l)^T K
+//   dR_l = diag(D) U_l dH' + PU_l^T dO - N_l^T dVp   (then back through the residual chain)
+//   dbeta = rowsum(V' * dX1) + G rowsum(K * dX2) + rowsum(dA * Gam * K K^T)
+//   d log g = reverse cumsum of  dG G - dD D + rowsum(dlG) - colsum(dlG)  (+ the G_C, D terms
+//         at the last token), dlG the elementwise sum of dX * X over the decayed matrices
+// and the adjoint of the start state is dH = Qt^T dO + Acc^T dH' with Qt = diag(G) Q - P Wc,
+// Acc = G_C I - K^T diag(D) Wc.  Two kernels:
+//   * bwdc_local_kernel: per chunk, in the segment form's S layout (S = H^T), the operator
+//     Phi = Acc^T, the end state from zero B = (K^T D Uc + sum U_l^T D R_l)^T and the local
+//     adjoint ell = dO^T Qt (the segment scans then give each chunk its start state and
+//     the adjoint of its end state);
+//   * bwdc_grad_kernel: per chunk, from those, every gradient.
+// One workgroup of 8 waves per chunk.  Every 64 x 64 product is 16 output tiles of
+// v_mfma_f32_16x16x32_bf16; wave w computes the tiles (w / 2, 2 (w % 2) + {0, 1}) of each,
+// its operands read from LDS (16-byte row reads, or gfx950's transposing reads for a
+// transposed operand), accumulating in float32.  Lane (i, g) = (lane % 16, lane / 16) holds
+// out[m0 + i][n0 + 4 g + r], r = 0..3 (the product's operands are passed to the MFMA
+// swapped, which yields the transposed tile): a lane's four values are consecutive columns
+// of one row.  The unit lower triangular inverse is a float32 forward substitution.
+#pragma once
+#include "prism_bwd_args.h"
+#include "prism_tile.h"
+
+namespace prism {
+namespace bwdc {
+
+constexpr int C = 64;        // tokens per chunk
+constexpr int D = 64;        // dk = dv
+constexpr int LDM = 72;      // bf16 row stride of an LDS matrix (144 bytes, rows 16-byte aligned)
+constexpr int MB = C * LDM;  // bf16 elements per LDS matrix
+constexpr int LDF = 68;      // float32 row stride of an LDS matrix
+constexpr int NT = 512;      // threads per workgroup
+constexpr int kMaxL = 8;
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
+
+// LDS plan (bytes): sixteen bf16 64 x 64 matrices M0 .. M15, then per-token float32
+// arrays.  The float32 matrices overlay pairs of bf16 ones (a 64 x 68 float32 matrix
+// takes 17 408 of their 18 432 bytes).
+struct Lds {
+  static constexpr int kMat = MB * 2;  // 9216 bytes
+  static constexpr int oM = 0;
+  static constexpr int oTok = 16 * kMat;          // per-token arrays
+  // per-token float32 arrays (64 each)
+  static constexpr int nTok = 5 + kMaxL + 12;     // b, G, D, beta, g, alpha[8], partials
+  static constexpr int total = oTok + nTok * 64 * 4 + 4 * 64 * 4;  // + dlG column partials [4][64]
+};
+static_assert(Lds::total <= 163840, "LDS plan exceeds 160 KiB");
+
+// Per-token arrays, offsets in floats from Lds::oTok.
+enum : int {
+  kB = 0, kG = 64, kDd = 128, kBeta = 192, kGg = 256, kAl = 320,       // alpha: [l][64], l < 8
+  kRowBeta = 320 + 512,       // dbeta partials [2 halves][64]
+  kRowGv = kRowBeta + 128,    // dG partials
+  kRowDd = kRowGv + 128,      // dD partials
+  kRowLg = kRowDd + 128,      // row sums of dlG
+  kMisc = kRowLg + 128,       // [0..15]: dG_C partials of the 8 waves etc.
+  kColLg = kMisc + 128,       // column sums of dlG, [4 row blocks][64]
+};
+
+__device__ __forceinline__ bf16x8 rfrag(const bf16_t* X, int r0, int k0) {
+  const int l = lane_id();
+  return *reinterpret_cast<const bf16x8*>(X + (r0 + (l & 15)) * LDM + k0 + 8 * (l >> 4));
+}
+
+// The operand slots of column m0 + lane % 16 of a row-major matrix X, rows k0 + 8 g .. +7:
+// two transposing reads.  In each 16-lane group, lane 4 a + b names row k0 + 8 g + a (+4),
+// columns m0 + 4 b .. +3, and receives column m0 + lane % 16 of the 4 rows.
+__device__ __forceinline__ bf16x8 tfrag(const bf16_t* X, int m0, int k0) {
+  const int l = lane_id(), g = l >> 4, i = l & 15;
+  const bf16_t* s = X + (k0 + 8 * g + (i >> 2)) * LDM + m0 + 4 * (i & 3);
+  const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(const_cast<bf16_t*>(s)));
+  const s16x4_t up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(const_cast<bf16_t*>(s + 4 * LDM)));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// operand slots k0 + 8 g + p scaled by sc[k0 + 8 g + p]
+__device__ __forceinline__ bf16x8 scale8(const bf16x8& x, const float* sc, int k0) {
+  const int g8 = 8 * (lane_id() >> 4);
+  const float4 a = *reinterpret_cast<const float4*>(sc + k0 + g8);
+  const float4 b = *reinterpret_cast<const float4*>(sc + k0 + g8 + 4);
+  bf16x8 r;
+  r[0] = (bf16_t)((float)x[0] * a.x);
+  r[1] = (bf16_t)((float)x[1] * a.y);
+  r[2] = (bf16_t)((float)x[2] * a.z);
+  r[3] = (bf16_t)((float)x[3] * a.w);
+  r[4] = (bf16_t)((float)x[4] * b.x);
+  r[5] = (bf16_t)((float)x[5] * b.y);
+  r[6] = (bf16_t)((float)x[6] * b.z);
+  r[7] = (bf16_t)((float)x[7] * b.w);
+  return r;
+}
+
+// acc += A B over k = 0 .. 63 for the output tile (m0, n0).  TA: A(m, k) = XA[k][m], else
+// XA[m][k]; TB: B(k, n) = XB[k][n], else XB[n][k].  bsc (optional): B's row k scaled by bsc[k].
+template <bool TA, bool TB>
+__device__ __forceinline__ f32x4 mm(f32x4 acc, const bf16_t* XA, const bf16_t* XB, int m0, int n0,
+                                    const float* bsc = nullptr) {
+#pragma unroll
+  for (int k0 = 0; k0 < 64; k0 += 32) {
+    const bf16x8 a = TA ? tfrag(XA, m0, k0) : rfrag(XA, m0, k0);
+    bf16x8 b = TB ? tfrag(XB, n0, k0) : rfrag(XB, n0, k0);
+    if (bsc != nullptr) b = scale8(b, bsc, k0);
+    acc = mfma(b, a, acc);
+  }
+  return acc;
+}
+
+__device__ __forceinline__ void put_bf16(bf16_t* X, int row, int col, const f32x4& v) {
+  bf16x4 y;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) y[r] = (bf16_t)v[r];
+  *reinterpret_cast<bf16x4*>(X + row * LDM + col) = y;
+}
+
+__device__ __forceinline__ f32x4 get_bf16(const bf16_t* X, int row, int col) {
+  const bf16x4 y = *reinterpret_cast<const bf16x4*>(X + row * LDM + col);
+  f32x4 v;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) v[r] = (float)y[r];
+  return v;
+}
+
+// Sum over the 8 consecutive lanes of a group (every lane ends with the total).
+__device__ __forceinline__ float sum8(float x) {
+  x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x141, 0xF, 0xF, false));
+  return x;
+}
+
+// Sum over the four lane groups g of a wave (lanes i, i + 16, i + 32, i + 48).
+__device__ __forceinline__ float sum_groups(float x) {
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
+
+// Sum over the 16 lanes i of a lane group (every lane ends with the total).
+__device__ __forceinline__ float sum16(float x) {
+  x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x141, 0xF, 0xF, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x140, 0xF, 0xF, false));
+  return x;
+}
+
+// The chunk's view: pointers into LDS and the global inputs of pair pr, chunk c.
+struct Chunk {
+  const BwdArgs* a;
+  int pr, c, t0, nt;  // nt: tokens of the chunk inside the sequence
+  int L;
+  char* lds;
+  float* tok;
+  __device__ bf16_t* m(int i) const { return reinterpret_cast<bf16_t*>(lds + i * Lds::kMat); }
+  __device__ float* mf(int i) const { return reinterpret_cast<float*>(lds + i * Lds::kMat); }
+};
+
+// Matrix slots.
+enum : int { mQ = 0, mK = 1, mdO = 2, mT = 3, mU = 4, mR = 5, mN = 6, mX1 = 7, mX2 = 8, mUc = 9, mWc = 10,
+             mS = 11, mLam = 12, m13 = 13, m14 = 14, m15 = 15 };
+
+// 64 rows x 64 bf16 of a token-major global array (row stride rs elements, rows >= nt zero)
+// into LDS matrix X: 16 bytes per thread.
+__device__ __forceinline__ void load_rows(bf16_t* X, const bf16_t* src, size_t rs, int nt) {
+  const int tid = threadIdx.x, row = tid >> 3, col = 8 * (tid & 7);
+  uint4 v = {0u, 0u, 0u, 0u};
+  if (row < nt) v = *reinterpret_cast<const uint4*>(src + (size_t)row * rs + col);
+  *reinterpret_cast<uint4*>(X + row * LDM + col) = v;
+}
+
+// A float32 64 x 64 matrix of the segment form ([v][k], row-major) into LDS as bf16;
+// returns this thread's share of <X, Y> when y is given.
+__device__ __forceinline__ float load_state(bf16_t* X, const float* src, const float* other) {
+  const int tid = threadIdx.x, row = tid >> 3, col = 8 * (tid & 7);
+  const float4 a = *reinterpret_cast<const float4*>(src + row * D + col);
+  const float4 b = *reinterpret_cast<const float4*>(src + row * D + col + 4);
+  bf16x8 y;
+  y[0] = (bf16_t)a.x; y[1] = (bf16_t)a.y; y[2] = (bf16_t)a.z; y[3] = (bf16_t)a.w;
+  y[4] = (bf16_t)b.x; y[5] = (bf16_t)b.y; y[6] = (bf16_t)b.z; y[7] = (bf16_t)b.w;
+  *reinterpret_cast<bf16x8*>(X + row * LDM + col) = y;
+  float s = 0.f;
+  if (other != nullptr) {
+    const float4 c = *reinterpret_cast<const float4*>(other + row * D + col);
+    const float4 d = *reinterpret_cast<const float4*>(other + row * D + col + 4);
+    s = a.x * c.x + a.y * c.y + a.z * c.z + a.w * c.w + b.x * d.x + b.y * d.y + b.z * d.z + b.w * d.w;
+  }
+  return s;
+}
+
+// Token scalars: b = cumsum(log g) (wave 0, one token per lane), G, D, beta, g, alpha.
+__device__ __forceinline__ void load_scalars(const Chunk& x) {
+  const BwdArgs& a = *x.a;
+  const int tid = threadIdx.x;
+  float* tk = x.tok;
+  if (tid < 64) {
+    const size_t gi = (size_t)x.pr * a.T + x.t0 + tid;
+    const bool in = tid < x.nt;
+    const float gv = in ? a.g[gi] : 1.f;
+    float s = __logf(gv);
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const float y = __shfl_up(s, o);
+      if (tid >= o) s += y;
+    }
+    const float bl = __shfl(s, 63);
+    tk[kB + tid] = s;
+    tk[kG + tid] = __expf(s);
+    tk[kDd + tid] = __expf(bl - s);
+    tk[kBeta + tid] = in ? a.beta[gi] : 0.f;
+    tk[kGg + tid] = gv;
+  }
+  if (x.L > 1) {
+    for (int e = tid; e < 64 * x.L; e += NT) {
+      const int t = e / x.L, l = e % x.L;
+      tk[kAl + l * 64 + t] = t < x.nt ? a.alpha[((size_t)x.pr * a.T + x.t0 + t) * x.L + l] : 0.f;
+    }
+  }
+}
+
+// The residual chain of thread (t, 8 channels ch0 ..): r_0 = v - anchor for its channels.
+struct ChainLane {
+  int t, ch0;
+  float r0[8];
+};
+
+__device__ __forceinline__ void load_bf16x8(float (&y)[8], const bf16_t* p) {
+  const bf16x8 v = *reinterpret_cast<const bf16x8*>(p);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) y[e] = (float)v[e];
+}
+
+__device__ __forceinline__ void chain_start(const Chunk& x, ChainLane& cl) {
+  const BwdArgs& a = *x.a;
+  cl.t = threadIdx.x >> 3;
+  cl.ch0 = 8 * (threadIdx.x & 7);
+  const bf16_t* v = static_cast<const bf16_t*>(a.v) + (size_t)x.pr * a.T * D;
+  const float* w = a.conv_w + (size_t)(x.pr % a.H) * 4 * D + cl.ch0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) cl.r0[e] = 0.f;
+  if (cl.t >= x.nt) return;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int tg = x.t0 + cl.t - 3 + j;
+    if (tg < 0) continue;
+    float y[8];
+    load_bf16x8(y, v + (size_t)tg * D + cl.ch0);
+    const float4 w0 = *reinterpret_cast<const float4*>(w + j * D);
+    const float4 w1 = *reinterpret_cast<const float4*>(w + j * D + 4);
+    const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) cl.r0[e] += (j == 3 ? y[e] : 0.f) - wv[e] * y[e];
+  }
+}
+
+// factor 1 - alpha_{t,l} gamma_{t,l} of the thread's channels (gamma slot l)
+__device__ __forceinline__ void chain_factor(const Chunk& x, const ChainLane& cl, int l, float (&f)[8]) {
+  const BwdArgs& a = *x.a;
+  if (cl.t >= x.nt) {  // past the sequence end: alpha is zero, nothing is read
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = 1.f;
+    return;
+  }
+  float gm[8];
+  load_bf16x8(gm, static_cast<const bf16_t*>(a.gamma) +
+                      (((size_t)x.pr * a.T + x.t0 + cl.t) * (x.L - 1) + l) * D + cl.ch0);
+  const float al = x.tok[kAl + l * 64 + cl.t];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f[e] = 1.f - al * gm[e];
+}
+
+// R_l = alpha_l r_l into X (bf16 rows t)
+__device__ __forceinline__ void put_written(const Chunk& x, const ChainLane& cl, bf16_t* X, int l, const float (&r)[8]) {
+  const float al = x.tok[kAl + l * 64 + cl.t];
+  bf16x8 y;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) y[e] = (bf16_t)(al * r[e]);
+  *reinterpret_cast<bf16x8*>(X + cl.t * LDM + cl.ch0) = y;
+}
+
+// T = (I + A)^-1 for A strictly lower triangular, in float32: thread (c, p) = (tid / 8,
+// tid % 8) owns T[8 m + p][c], m = 0..7; row r of the substitution is
+// T[r][c] = -sum_{j < r} A[r][j] T[j][c] (r > c), its 64 terms summed over the 8 lanes p.
+// Ap: A with row r's entry j at r * 64 + 8 (j % 8) + j / 8.  Result: bf16 row-major in X.
+__device__ __forceinline__ void unit_lower_inverse(const float* Ap, bf16_t* X) {
+  const int c = threadIdx.x >> 3, p = threadIdx.x & 7;
+  float t[8];
+#pragma unroll
+  for (int m = 0; m < 8; ++m) t[m] = (8 * m + p == c) ? 1.f : 0.f;
+#pragma unroll
+  for (int r = 1; r < 64; ++r) {
+    const float4 a0 = *reinterpret_cast<const float4*>(Ap + r * 64 + 8 * p);
+    const float4 a1 = *reinterpret_cast<const float4*>(Ap + r * 64 + 8 * p + 4);
+    const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+    float s = 0.f;
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+      if (8 * m < r) s += av[m] * t[m];
+    s = sum8(s);
+    if (p == (r & 7) && r > c) t[r >> 3] = -s;
+  }
+#pragma unroll
+  for (int m = 0; m < 8; ++m) X[(8 * m + p) * LDM + c] = (bf16_t)t[m];
+}
+
+// The state-independent part of a chunk, shared by both kernels.  On return (after a
+// barrier): sT, sUc, sWc filled; kk = K K^T tiles and gm = lower(Gam) tiles of the wave,
+// vp = V' tiles (float32).  With HB, hb accumulates sum_l R_l^T diag(D) U_l (S layout).
+struct Fwd {
+  f32x4 kk[2], gm[2], vp[2], uc[2];
+};
+
+template <bool HB>
+__device__ __forceinline__ void chunk_forward(const Chunk& x, ChainLane& cl, Fwd& f, f32x4 (&hb)[2]) {
+  const BwdArgs& a = *x.a;
+  const int w = wave_id(), l = lane_id(), i = l & 15, g = l >> 4;
+  const int mt = w >> 1, nt0 = 2 * (w & 1), row = 16 * mt + i;
+  const float* tk = x.tok;
+  bf16_t *sK = x.m(mK), *sT = x.m(mT), *sU = x.m(mU), *sR = x.m(mR), *sN = x.m(mN);
+  bf16_t *sX1 = x.m(mX1), *sX2 = x.m(mX2), *sUc = x.m(mUc), *sWc = x.m(mWc);
+  float* sAp = x.mf(m13);
+  const float beta_i = tk[kBeta + row], G_i = tk[kG + row], b_i = tk[kB + row];
+  // F1: K K^T, the decay tile, A (float32, permuted for the substitution)
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int n0 = 16 * (nt0 + h), col = n0 + 4 * g;
+    f.kk[h] = mm<false, false>(zero4(), sK, sK, 16 * mt, n0);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int j = col + r;
+      f.gm[h][r] = j <= row ? __expf(b_i - tk[kB + j]) : 0.f;
+      const float av = j < row ? beta_i * f.gm[h][r] * f.kk[h][r] : 0.f;
+      sAp[row * 64 + 8 * (j & 7) + (j >> 3)] = av;
+    }
+  }
+  __syncthreads();
+  unit_lower_inverse(sAp, sT);
+  // V' = V - sum_l N_l R_l: V's tiles straight from memory
+  const bf16_t* vg = static_cast<const bf16_t*>(a.v) + ((size_t)x.pr * a.T + x.t0) * D;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int col = 16 * (nt0 + h) + 4 * g;
+    f.vp[h] = zero4();
+    if (row < x.nt) {
+      const bf16x4 y = *reinterpret_cast<const bf16x4*>(vg + (size_t)row * D + col);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) f.vp[h][r] = (float)y[r];
+    }
+  }
+  // F3: rank slots, ascending
+  float rc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) rc[e] = cl.r0[e];
+  for (int lv = 1; lv < x.L; ++lv) {
+    // (the previous slot's products are done: barrier at the loop end, or the one above)
+    load_rows(sU, static_cast<const bf16_t*>(a.u) + (((size_t)x.pr * a.T + x.t0) * (x.L - 1) + lv - 1) * D,
+              (size_t)(x.L - 1) * D, x.nt);
+    {
+      float fct[8];
+      chain_factor(x, cl, lv - 1, fct);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) rc[e] *= fct[e];
+      put_written(x, cl, sR, lv, rc);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int n0 = 16 * (nt0 + h), col = n0 + 4 * g;
+      f32x4 nr = mm<false, false>(zero4(), sK, sU, 16 * mt, n0);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) nr[r] = col + r < row ? f.gm[h][r] * nr[r] : 0.f;
+      put_bf16(sN, row, col, nr);
+      if constexpr (HB) hb[h] = mm<true, true>(hb[h], sR, sU, 16 * mt, n0, tk + kDd);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const f32x4 t = mm<false, true>(zero4(), sN, sR, 16 * mt, 16 * (nt0 + h));
+#pragma unroll
+      for (int r = 0; r < 4; ++r) f.vp[h][r] -= t[r];
+    }
+    __syncthreads();
+  }
+  // F4: X1 = diag(beta) V', X2 = diag(beta G) K; Uc = T X1, Wc = T X2
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int col = 16 * (nt0 + h) + 4 * g;
+    f32x4 x1, x2 = get_bf16(sK, row, col);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      x1[r] = beta_i * f.vp[h][r];
+      x2[r] *= beta_i * G_i;
+    }
+    put_bf16(sX1, row, col, x1);
+    put_bf16(sX2, row, col, x2);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int n0 = 16 * (nt0 + h), col = n0 + 4 * g;
+    f.uc[h] = mm<false, true>(zero4(), sT, sX1, 16 * mt, n0);
+    const f32x4 wc = mm<false, true>(zero4(), sT, sX2, 16 * mt, n0);
+    put_bf16(sUc, row, col, f.uc[h]);
+    put_bf16(sWc, row, col, wc);
+  }
+  __syncthreads();
+}
+
+__device__ __forceinline__ void load_chunk_inputs(const Chunk& x) {
+  const BwdArgs& a = *x.a;
+  const size_t r0 = ((size_t)x.pr * a.T + x.t0) * D;
+  load_rows(x.m(mQ), static_cast<const bf16_t*>(a.q) + r0, D, x.nt);
+  load_rows(x.m(mK), static_cast<const bf16_t*>(a.k) + r0, D, x.nt);
+  load_rows(x.m(mdO), static_cast<const bf16_t*>(a.d_o) + r0, D, x.nt);
+  load_scalars(x);
+}
+
+// Segment-form operands of each chunk (segments of one chunk: a.nseg == chunks per pair).
+__global__ __launch_bounds__(NT) void bwdc_local_kernel(BwdArgs a) {
+  __shared__ __align__(16) char lds[Lds::total];
+  Chunk x;
+  x.a = &a;
+  x.c = blockIdx.x;
+  x.pr = blockIdx.y;
+  x.t0 = x.c * C;
+  x.nt = min(C, a.T - x.t0);
+  x.L = a.L;
+  x.lds = lds;
+  x.tok = reinterpret_cast<float*>(lds + Lds::oTok);
+  const int w = wave_id(), l = lane_id(), i = l & 15, g = l >> 4;
+  const int mt = w >> 1, nt0 = 2 * (w & 1), row = 16 * mt + i;
+  load_chunk_inputs(x);
+  ChainLane cl;
+  if (a.L > 1) chain_start(x, cl);
+  __syncthreads();
+  Fwd f;
+  f32x4 hb[2] = {zero4(), zero4()};
+  chunk_forward<true>(x, cl, f, hb);
+  const float* tk = x.tok;
+  bf16_t *sQ = x.m(mQ), *sK = x.m(mK), *sdO = x.m(mdO), *sUc = x.m(mUc), *sWc = x.m(mWc);
+  bf16_t *sP = x.m(mX1), *sQt = x.m(mX2);
+  // P = lower(Gam * Q K^T)
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int n0 = 16 * (nt0 + h);
+    f32x4 p = mm<false, false>(zero4(), sQ, sK, 16 * mt, n0);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) p[r] *= f.gm[h][r];
+    put_bf16(sP, row, n0 + 4 * g, p);
+  }
+  __syncthreads();
+  // Qt = diag(G) Q - P Wc; Phi = G_C I - Wc^T D K; B = hb + Uc^T D K
+  const float GC = tk[kG + 63];
+  const size_t so = ((size_t)x.pr * a.nseg + x.c) * D * D;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int n0 = 16 * (nt0 + h), col = n0 + 4 * g;
+    f32x4 qt = get_bf16(sQ, row, col);
+    const f32x4 pw = mm<false, true>(zero4(), sP, sWc, 16 * mt, n0);
+    const float G_i = tk[kG + row];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) qt[r] = G_i * qt[r] - pw[r];
+    put_bf16(sQt, row, col, qt);
+    f32x4 ph = mm<true, true>(zero4(), sWc, sK, 16 * mt, n0, tk + kDd);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) ph[r] = (col + r == row ? GC : 0.f) - ph[r];
+    *reinterpret_cast<f32x4*>(a.seg_Phi + so + (size_t)row * D + col) = ph;
+    const f32x4 bb = mm<true, true>(hb[h], sUc, sK, 16 * mt, n0, tk + kDd);
+    *reinterpret_cast<f32x4*>(a.seg_B + so + (size_t)row * D + col) = bb;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int n0 = 16 * (nt0 + h), col = n0 + 4 * g;
+    const f32x4 el = mm<true, true>(zero4(), sdO, sQt, 16 * mt, n0);
+    *reinterpret_cast<f32x4*>(a.seg_ell + so + (size_t)row * D + col) = el;
+  }
+}
+
+// Every gradient of chunk (blockIdx.x, pair blockIdx.y) from its start state (seg_Sin) and
+// the adjoint of its end state (seg_Lam).
+__global__ __launch_bounds__(NT) void bwdc_grad_kernel(BwdArgs a) {
+  __shared__ __align__(16) char lds[Lds::total];
+  Chunk x;
+  x.a = &a;
+  x.c = blockIdx.x;
+  x.pr = blockIdx.y;
+  x.t0 = x.c * C;
+  x.nt = min(C, a.T - x.t0);
+  x.L = a.L;
+  x.lds = lds;
+  x.tok = reinterpret_cast<float*>(lds + Lds::oTok);
+  float* tk = x.tok;
+  const int tid = threadIdx.x, w = wave_id(), l = lane_id(), i = l & 15, g = l >> 4;
+  const int mt = w >> 1, nt0 = 2 * (w & 1), row = 16 * mt + i, half = w & 1;
+  const size_t so = ((size_t)x.pr * a.nseg + x.c) * D * D;
+  load_chunk_inputs(x);
+  const float gc_part = load_state(x.m(mS), a.seg_Sin + so, a.seg_Lam + so);
+  load_state(x.m(mLam), a.seg_Lam + so, nullptr);
+  {
+    const float s = sum8(gc_part);  // 8 lanes: one row of 64 entries
+    // rows of the wave: 8; partials of the wave's 8 rows summed in order below
+    if ((tid & 7) == 0) tk[kRowLg + (tid >> 3)] = s;  // borrowed: rewritten before kRowLg is used
+  }
+  ChainLane cl;
+  if (a.L > 1) chain_start(x, cl);
+  __syncthreads();
+  float dGC = 0.f;
+  if (tid == 0) {
+    for (int r = 0; r < 64; ++r) dGC += tk[kRowLg + r];
+    tk[kMisc] = dGC;
+  }
+  Fwd f;
+  f32x4 hb_unused[2];
+  chunk_forward<false>(x, cl, f, hb_unused);
+  bf16_t *sQ = x.m(mQ), *sK = x.m(mK), *sdO = x.m(mdO), *sT = x.m(mT), *sU = x.m(mU), *sR = x.m(mR);
+  bf16_t *sS = x.m(mS), *sLam = x.m(mLam), *sUc = x.m(mUc), *sWc = x.m(mWc);
+  bf16_t *sE = x.m(mX1), *sP = x.m(mX2), *sZ = x.m(mN), *sdE = x.m(m13), *sdVp = x.m(m14), *sdWc = x.m(m15);
+  const float beta_i = tk[kBeta + row], G_i = tk[kG + row], D_i = tk[kDd + row];
+  const bool in_i = row < x.nt;
+  const size_t grow = (size_t)x.pr * a.T + x.t0 + row;  // global token row of this lane
+  f32x4 dq[2], dk[2], dlg[2], p[2];
+  float rb_beta = 0.f, rb_gv = 0.f, rb_dd = 0.f;  // this lane's row partials (4 columns x 2 tiles)
+  // B0: E = Uc - Wc H; P = lower(Gam * Q K^T)
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int n0 = 16 * (nt0 + h), col = n0 + 4 * g;
+    f32x4 e = mm<false, false>(zero4(), sWc, sS, 16 * mt, n0);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) e[r] = f.uc[h][r] - e[r];
+    put_bf16(sE, row, col, e);
+    p[h] = mm<false, false>(zero4(), sQ, sK, 16 * mt, n0);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) p[h][r] *= f.gm[h][r];
+    put_bf16(sP, row, col, p[h]);
+    dlg[h] = zero4();
+  }
+  __syncthreads();
+  // B1: dE = P^T dO + D (K dH'); dP = lower(dO E^T) -> Zp = Gam * dP; dG from Q H;
+  //     dQ = G dO H^T; E dH'^T -> dK, dD
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int n0 = 16 * (nt0 + h), col = n0 + 4 * g;
+    const f32x4 a1 = mm<true, true>(zero4(), sP, sdO, 16 * mt, n0);
+    const f32x4 a2 = mm<false, false>(zero4(), sK, sLam, 16 * mt, n0);
+    f32x4 de;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) de[r] = a1[r] + D_i * a2[r];
+    put_bf16(sdE, row, col, de);
+    f32x4 dp = mm<false, false>(zero4(), sdO, sE, 16 * mt, n0);
+    f32x4 zp;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      dp[r] = col + r <= row ? dp[r] : 0.f;
+      dlg[h][r] += dp[r] * p[h][r];
+      zp[r] = f.gm[h][r] * dp[r];
+    }
+    put_bf16(sZ, row, col, zp);
+    const f32x4 qh = mm<false, false>(zero4(), sQ, sS, 16 * mt, n0);
+    const f32x4 dov = get_bf16(sdO, row, col);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) rb_gv += dov[r] * qh[r];
+    dq[h] = mm<false, true>(zero4(), sdO, sS, 16 * mt, n0);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) dq[h][r] *= G_i;
+    const f32x4 edh = mm<false, true>(zero4(), sE, sLam, 16 * mt, n0);
+    const f32x4 kv = get_bf16(sK, row, col);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      dk[h][r] = D_i * edh[r];
+      rb_dd += kv[r] * edh[r];
+    }
+  }
+  __syncthreads();
+  // B2: dX1 = T^T dE -> dVp (LDS, and dv's direct part), dbeta; dWc = -dE H^T;
+  //     dQ += Zp K; dK += Zp^T Q
+  float* dvg = a.dv + grow * D;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int n0 = 16 * (nt0 + h), col = n0 + 4 * g;
+    const f32x4 dx1 = mm<true, true>(zero4(), sT, sdE, 16 * mt, n0);
+    f32x4 dvp;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      dvp[r] = beta_i * dx1[r];
+      rb_beta += f.vp[h][r] * dx1[r];
+    }
+    put_bf16(sdVp, row, col, dvp);
+    if (in_i) *reinterpret_cast<f32x4*>(dvg + col) = dvp;
+    f32x4 dwc = mm<false, true>(zero4(), sdE, sS, 16 * mt, n0);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) dwc[r] = -dwc[r];
+    put_bf16(sdWc, row, col, dwc);
+    dq[h] = mm<false, true>(dq[h], sZ, sK, 16 * mt, n0);
+    dk[h] = mm<true, true>(dk[h], sZ, sQ, 16 * mt, n0);
+  }
+  __syncthreads();
+  // B3: dX2 = T^T dWc -> dK, dbeta, dG; Y = dE Uc^T + dWc Wc^T (into E's slot)
+  bf16_t* sY = sE;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int n0 = 16 * (nt0 + h), col = n0 + 4 * g;
+    const f32x4 dx2 = mm<true, true>(zero4(), sT, sdWc, 16 * mt, n0);
+    const f32x4 kv = get_bf16(sK, row, col);
+    float rk = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      rk += kv[r] * dx2[r];
+      dk[h][r] += beta_i * G_i * dx2[r];
+    }
+    rb_beta += G_i * rk;
+    rb_gv += beta_i * rk;
+    f32x4 y = mm<false, false>(zero4(), sdE, sUc, 16 * mt, n0);
+    y = mm<false, false>(y, sdWc, sWc, 16 * mt, n0);
+    put_bf16(sY, row, col, y);
+  }
+  __syncthreads();
+  // B4: dA = strict(-T^T Y) -> dbeta, dlG, Z = diag(beta) Gam * dA (into P's slot)
+  bf16_t* sZ2 = sP;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int n0 = 16 * (nt0 + h), col = n0 + 4 * g;
+    const f32x4 t = mm<true, true>(zero4(), sT, sY, 16 * mt, n0);
+    f32x4 z;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float da = col + r < row ? -t[r] : 0.f;
+      const float gk = f.gm[h][r] * f.kk[h][r];
+      rb_beta += da * gk;
+      dlg[h][r] += da * beta_i * gk;
+      z[r] = beta_i * f.gm[h][r] * da;
+    }
+    put_bf16(sZ2, row, col, z);
+  }
+  __syncthreads();
+  // B5: dK += Z K + Z^T K
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int n0 = 16 * (nt0 + h);
+    dk[h] = mm<false, true>(dk[h], sZ2, sK, 16 * mt, n0);
+    dk[h] = mm<true, true>(dk[h], sZ2, sK, 16 * mt, n0);
+  }
+  // B6: rank slots, descending
+  bf16_t *sN = x.m(mN), *sPU = x.m(mT), *sZpu = x.m(mX1), *sZn = x.m(mX2);
+  float* sdR = x.mf(mUc);
+  float dr[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) dr[e] = 0.f;
+  float da_carry = 0.f;
+  const bool in_t = a.L > 1 && cl.t < x.nt;
+  const size_t tg = (size_t)x.pr * a.T + x.t0 + (a.L > 1 ? cl.t : 0);
+  for (int lv = x.L - 1; lv >= 1; --lv) {
+    load_rows(sU, static_cast<const bf16_t*>(a.u) + (((size_t)x.pr * a.T + x.t0) * (x.L - 1) + lv - 1) * D,
+              (size_t)(x.L - 1) * D, x.nt);
+    // r_{l-1} and r_l of the thread's channels
+    float rp[8], rl[8], fl[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) rp[e] = cl.r0[e];
+    for (int m = 0; m < lv - 1; ++m) {
+      float fm[8];
+      chain_factor(x, cl, m, fm);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) rp[e] *= fm[e];
+    }
+    chain_factor(x, cl, lv - 1, fl);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) rl[e] = rp[e] * fl[e];
+    put_written(x, cl, sR, lv, rl);
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int n0 = 16 * (nt0 + h), col = n0 + 4 * g;
+      f32x4 n = mm<false, false>(zero4(), sK, sU, 16 * mt, n0);
+      f32x4 pu = mm<false, false>(zero4(), sQ, sU, 16 * mt, n0);
+      f32x4 dpu = mm<false, false>(zero4(), sdO, sR, 16 * mt, n0);
+      f32x4 dn = mm<false, false>(zero4(), sdVp, sR, 16 * mt, n0);
+      f32x4 zpu, zn;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const bool lo = col + r <= row, st = col + r < row;
+        n[r] = st ? f.gm[h][r] * n[r] : 0.f;
+        pu[r] = f.gm[h][r] * pu[r];
+        dpu[r] = lo ? dpu[r] : 0.f;
+        dn[r] = st ? -dn[r] : 0.f;
+        dlg[h][r] += dpu[r] * pu[r] + dn[r] * n[r];
+        zpu[r] = f.gm[h][r] * dpu[r];
+        zn[r] = f.gm[h][r] * dn[r];
+      }
+      put_bf16(sN, row, col, n);
+      put_bf16(sPU, row, col, pu);
+      put_bf16(sZpu, row, col, zpu);
+      put_bf16(sZn, row, col, zn);
+    }
+    __syncthreads();
+    float* dug = a.du + (grow * (a.L - 1) + lv - 1) * D;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int n0 = 16 * (nt0 + h), col = n0 + 4 * g;
+      const f32x4 udh = mm<false, false>(zero4(), sU, sLam, 16 * mt, n0);
+      f32x4 drt = mm<true, true>(zero4(), sPU, sdO, 16 * mt, n0);
+      const f32x4 ndv = mm<true, true>(zero4(), sN, sdVp, 16 * mt, n0);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) drt[r] += D_i * udh[r] - ndv[r];
+      *reinterpret_cast<f32x4*>(sdR + row * LDF + col) = drt;
+      const f32x4 rdh = mm<false, true>(zero4(), sR, sLam, 16 * mt, n0);
+      const f32x4 uv = get_bf16(sU, row, col);
+      f32x4 du = mm<true, true>(zero4(), sZpu, sQ, 16 * mt, n0);
+      du = mm<true, true>(du, sZn, sK, 16 * mt, n0);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        rb_dd += uv[r] * rdh[r];
+        du[r] += D_i * rdh[r];
+      }
+      if (in_i) *reinterpret_cast<f32x4*>(dug + col) = du;
+      dq[h] = mm<false, true>(dq[h], sZpu, sU, 16 * mt, n0);
+      dk[h] = mm<false, true>(dk[h], sZn, sU, 16 * mt, n0);
+    }
+    __syncthreads();
+    // the chain's adjoint for slot lv
+    {
+      const float4 d0 = *reinterpret_cast<const float4*>(sdR + cl.t * LDF + cl.ch0);
+      const float4 d1 = *reinterpret_cast<const float4*>(sdR + cl.t * LDF + cl.ch0 + 4);
+      const float dR[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+      const float al = tk[kAl + lv * 64 + cl.t], alm = tk[kAl + (lv - 1) * 64 + cl.t];
+      float s = 0.f, s2 = 0.f;
+      float gmv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      if (in_t) load_bf16x8(gmv, static_cast<const bf16_t*>(a.gamma) + (tg * (a.L - 1) + lv - 1) * D + cl.ch0);
+      float dgm[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        s += dR[e] * rl[e];
+        dr[e] += al * dR[e];
+        s2 += dr[e] * gmv[e] * rp[e];
+        dgm[e] = -dr[e] * alm * rp[e];
+        dr[e] *= fl[e];
+      }
+      s = sum8(s) + da_carry;
+      da_carry = -sum8(s2);
+      if (in_t) {
+        if ((tid & 7) == 0) a.dalpha[tg * a.L + lv] = s;
+        float* dgp = a.dgamma + (tg * (a.L - 1) + lv - 1) * D + cl.ch0;
+        *reinterpret_cast<float4*>(dgp) = make_float4(dgm[0], dgm[1], dgm[2], dgm[3]);
+        *reinterpret_cast<float4*>(dgp + 4) = make_float4(dgm[4], dgm[5], dgm[6], dgm[7]);
+      }
+    }
+  }
+  // dq, dk
+  float* dqg = a.dq + grow * D;
+  float* dkg = a.dk + grow * D;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int col = 16 * (nt0 + h) + 4 * g;
+    if (in_i) {
+      *reinterpret_cast<f32x4*>(dqg + col) = dq[h];
+      *reinterpret_cast<f32x4*>(dkg + col) = dk[h];
+    }
+  }
+  // row partials of this lane's row over the wave's 32 columns; column sums of dlG
+  {
+    float rlg = 0.f;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) rlg += dlg[h][r];
+    const float s_beta = sum_groups(rb_beta), s_gv = sum_groups(rb_gv), s_dd = sum_groups(rb_dd),
+                s_lg = sum_groups(rlg);
+    if (g == 0) {
+      tk[kRowBeta + half * 64 + row] = s_beta;
+      tk[kRowGv + half * 64 + row] = s_gv;
+      tk[kRowDd + half * 64 + row] = s_dd;
+      tk[kRowLg + half * 64 + row] = s_lg;
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float cs = sum16(dlg[h][r]);
+        if (i == 0) tk[kColLg + mt * 64 + 16 * (nt0 + h) + 4 * g + r] = cs;
+      }
+  }
+  if (a.L > 1) {
+    // d r_0 of the chain, then the anchor's terms
+#pragma unroll
+    for (int e = 0; e < 8; e += 4)
+      *reinterpret_cast<float4*>(sdR + cl.t * LDF + cl.ch0 + e) = make_float4(dr[e], dr[e + 1], dr[e + 2], dr[e + 3]);
+    if ((tid & 7) == 0 && in_t) a.dalpha[tg * a.L] = da_carry;
+  }
+  __syncthreads();
+  if (tid < 64) {
+    // db, then d log g = reverse cumsum, dg = d log g / g; dbeta (wave 0, one token per lane)
+    const int t = tid;
+    const float Gt = tk[kG + t], Dt = tk[kDd + t];
+    const float dD = tk[kRowDd + t] + tk[kRowDd + 64 + t];
+    const float dGv = tk[kRowGv + t] + tk[kRowGv + 64 + t];
+    const float cs = (tk[kColLg + t] + tk[kColLg + 64 + t]) + (tk[kColLg + 128 + t] + tk[kColLg + 192 + t]);
+    float db = dGv * Gt - dD * Dt + (tk[kRowLg + t] + tk[kRowLg + 64 + t]) - cs;
+    float tot = dD * Dt;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) tot += __shfl_xor(tot, o);
+    if (t == 63) db += tot + tk[kMisc] * Gt;
+    // suffix sum over lanes t .. 63
+    float sfx = db;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const float y = __shfl_down(sfx, o);
+      if (t + o < 64) sfx += y;
+    }
+    if (t < x.nt) {
+      const size_t gi = (size_t)x.pr * a.T + x.t0 + t;
+      a.dg[gi] = sfx / tk[kGg + t];
+      a.dbeta[gi] = tk[kRowBeta + t] + tk[kRowBeta + 64 + t];
+    }
+  }
+  if (a.L > 1) {
+    const size_t ps = (size_t)x.pr * a.nseg + x.c;
+    const float* w = a.conv_w + (size_t)(x.pr % a.H) * 4 * D;
+    // dv += d r_0 - sum_j w_j d r_0(t + 3 - j) over the chunk's anchors that read v_t
+    if (in_t) {
+      float* dvp = a.dv + tg * D + cl.ch0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int ch = cl.ch0 + e;
+        float s = dvp[e] + sdR[cl.t * LDF + ch];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int ta = cl.t + 3 - j;
+          if (ta < C) s -= w[j * D + ch] * sdR[ta * LDF + ch];
+        }
+        dvp[e] = s;
+      }
+    }
+    if (tid < 3 * D) {
+      // the terms owed to tokens t0 - 1 - jj of the previous chunk
+      const int jj = tid / D, ch = tid % D;
+      float s = 0.f;
+      for (int t = 0; t <= 2 - jj; ++t) s -= w[(2 - jj - t) * D + ch] * sdR[t * LDF + ch];
+      a.carry[(ps * 3 + jj) * D + ch] = s;
+    } else if (tid >= 256) {
+      // dconv_w share: dw_j = -sum_t d r_0(t) v_{t-3+j}
+      const int j = (tid - 256) / D, ch = (tid - 256) % D;
+      const bf16_t* v = static_cast<const bf16_t*>(a.v) + (size_t)x.pr * a.T * D;
+      float s = 0.f;
+      for (int t = 0; t < x.nt; ++t) {
+        const int tv = x.t0 + t - 3 + j;
+        if (tv >= 0) s -= sdR[t * LDF + ch] * (float)v[(size_t)tv * D + ch];
+      }
+      a.dconv_part[(ps * 4 + j) * D + ch] = s;
+    }
+  }
+}
+
+}  // namespace bwdc
+}  // namespace prism

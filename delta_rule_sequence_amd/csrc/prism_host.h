@@ -75,6 +75,10 @@ prism_status launch_tail_bf16_d128(const FwdArgs& a, const LaunchShape& s, hipEv
 int bwd_seg_slices(int d);
 prism_status launch_bwd(prism_dtype dt, int d, const BwdArgs& a, int B, int P, float* dconv_w, bool segments,
                         hipStream_t stream);
+// The chunked backward (prism_bwd_chunk.h): bfloat16, dk = dv = 64, one segment per 64-token
+// chunk (a.nseg chunks per pair): chunk operators, the segment scans, chunk gradients, the
+// anchor carry and the batch sum of dconv_w.
+prism_status launch_bwd_chunked(const BwdArgs& a, int B, int P, float* dconv_w, hipStream_t stream);
 
 // Nonlinear refinement (prism_nl.h, nl.hip).  launch_gain: the chain factors from given
 // gains, for the linear chain or (delta) the written corrections.  launch_pred: the factors

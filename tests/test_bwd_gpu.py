@@ -120,8 +120,9 @@ def test_bwd_deterministic():
         assert torch.equal(a[n], b[n]), n
 
 
+@pytest.mark.parametrize("chunked", [False, True], ids=["segments", "chunked"])
 @pytest.mark.parametrize("which", ["v", "q"])
-def test_bwd_full_size_linear_directions(which):
+def test_bwd_full_size_linear_directions(which, chunked):
     """At the full 16K bf16 workload (B=2, H=4, T=16384, d=64, L=4): o and S_final are linear
     in v (A_t does not depend on v; B_t, the anchor and the residual chain are linear in it)
     and o is linear in q (S does not depend on q), so for any direction e
@@ -130,14 +131,15 @@ def test_bwd_full_size_linear_directions(which):
     depend on x).  Both sides carry bf16 rounding of their operands (a relative error of a
     few 2^-9 per element, with random signs), so the bound is 2^-6 sqrt(sum (d_o o)^2):
     about 23 here, against sums of a few hundred to a thousand that a wrong gradient would
-    miss by their own size."""
+    miss by their own size.  Run for the segment-parallel form and the chunked MFMA form
+    (prism_bwd_chunked), whose gradients carry bf16 rounding of the same order."""
     if not gpu_available():
         pytest.skip("no GPU")
     import torch
     import delta_rule_sequence_amd as prism
     import workloads
     w = workloads.workload("rec16k_bf16")
-    print(f"[bwd] full-size linear direction {which} on {w.name}", flush=True)
+    print(f"[bwd] full-size linear direction {which} on {w.name} chunked={chunked}", flush=True)
     x = workloads.generate(w)
     dev = workloads.to_torch(x, w.dtype, "cuda")
     gen = torch.Generator(device="cuda").manual_seed(17)
@@ -147,7 +149,7 @@ def test_bwd_full_size_linear_directions(which):
     if which == "q":
         e = e / e.float().norm(dim=-1, keepdim=True).to(torch.bfloat16)
     grads = prism.bwd(dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], dev["u"], dev["alpha"], dev["gamma"],
-                      dev["conv_w"], L=w.L, d_o=d_o, dS_final=dS)
+                      dev["conv_w"], L=w.L, d_o=d_o, dS_final=dS, chunked=chunked)
     args = dict(dev)
     args[which] = e
     o, S = prism.fwd(args["q"], args["k"], args["v"], args["g"], args["beta"], args["u"], args["alpha"],
