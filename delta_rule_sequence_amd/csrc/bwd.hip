@@ -1,7 +1,7 @@
 // bwd.hip - launches of the backward (prism_bwd.h): the sequential per-pair adjoint sweep
 // and the segment-parallel passes, the fixed-order sum of per-workgroup partials and the
 // batch sum of dconv_w; and the chunked MFMA form (prism_bwd_chunk.h), which shares the
-// segment scans, the anchor carry and the dconv_w sum with the segment-parallel form.
+// anchor carry and the dconv_w sum with the segment-parallel form.
 #include "prism_bwd.h"
 #include "prism_bwd_chunk.h"
 #include "prism_host.h"
@@ -94,11 +94,28 @@ prism_status launch_bwd(prism_dtype dt, int d, const BwdArgs& a, int B, int P, f
 }
 
 // Chunked form: segments of one chunk (a.nseg chunks per pair, a.seg_len = 64).
-prism_status launch_bwd_chunked(const BwdArgs& a, int B, int P, float* dconv_w, hipStream_t stream) {
+namespace {
+template <int NL>
+void bwdc_launch(const BwdArgs& a, int P, hipStream_t stream) {
   const dim3 grid((unsigned)a.nseg, (unsigned)P);
-  hipLaunchKernelGGL(bwdc::bwdc_local_kernel, grid, dim3(bwdc::NT), 0, stream, a);
-  hipLaunchKernelGGL((bwd_seg_scan_kernel<64>), dim3((unsigned)P, 64 / 4, 2), dim3(256), 0, stream, a);
-  hipLaunchKernelGGL(bwdc::bwdc_grad_kernel, grid, dim3(bwdc::NT), 0, stream, a);
+  hipLaunchKernelGGL((bwdc::bwdc_local_kernel<NL>), grid, dim3(bwdc::NT), 0, stream, a);
+  hipLaunchKernelGGL(bwdc::bwdc_scan_kernel, dim3((unsigned)P, 64 / 2, 2), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((bwdc::bwdc_grad_kernel<NL>), grid, dim3(bwdc::NT), 0, stream, a);
+}
+}  // namespace
+
+prism_status launch_bwd_chunked(const BwdArgs& a, int B, int P, float* dconv_w, hipStream_t stream) {
+  switch (a.L) {
+    case 1: bwdc_launch<0>(a, P, stream); break;
+    case 2: bwdc_launch<1>(a, P, stream); break;
+    case 3: bwdc_launch<2>(a, P, stream); break;
+    case 4: bwdc_launch<3>(a, P, stream); break;
+    case 5: bwdc_launch<4>(a, P, stream); break;
+    case 6: bwdc_launch<5>(a, P, stream); break;
+    case 7: bwdc_launch<6>(a, P, stream); break;
+    case 8: bwdc_launch<7>(a, P, stream); break;
+    default: return PRISM_ERR_UNSUPPORTED;
+  }
   if (hipGetLastError() != hipSuccess) return PRISM_ERR_HIP;
   if (a.L == 1) return PRISM_OK;
   if (a.nseg > 1)

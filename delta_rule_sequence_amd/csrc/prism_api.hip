@@ -362,7 +362,7 @@ prism_status bwd_impl(const void* q, const void* k, const void* v, const float* 
     return PRISM_ERR_INVALID_ARG;
   if (!workspace || workspace_bytes < pl.total) return PRISM_ERR_WORKSPACE;
   char* ws = static_cast<char*>(workspace);
-  prism::BwdArgs a;
+  prism::BwdArgs a = {};
   a.q = q; a.k = k; a.v = v; a.u = u; a.gamma = gamma; a.d_o = d_o;
   a.g = g; a.beta = beta; a.alpha = alpha; a.conv_w = conv_w; a.dS_final = dS_final;
   a.dq = dq; a.dk = dk_out; a.dv = dv_out; a.dg = dg; a.dbeta = dbeta;
@@ -428,9 +428,9 @@ prism_status prism_bwd_lowmem(const void* q, const void* k, const void* v, const
 
 namespace {
 
-// Workspace of the chunked backward: per 64-token chunk five float32 64 x 64 matrices
-// (operator, end state from zero, local adjoint, entering state, arriving adjoint), its
-// anchor carry [3][64] and dconv_w share [4][64].
+// Workspace of the chunked backward: per 64-token chunk six float32 64 x 64 matrices
+// (operator and its transpose, end state from zero, local adjoint, entering state,
+// arriving adjoint), its anchor carry [3][64] and dconv_w share [4][64].
 struct BwdChunkPlan {
   int P, nch;
   size_t off_seg, off_carry, off_part, total;
@@ -446,7 +446,7 @@ prism_status make_bwd_chunk_plan(int B, int H, int T, int dk, int dv, int L, pri
   if (!mul_ok(P, (size_t)T, &c) || !mul_ok(c, (size_t)L * dk * 4, &c)) return PRISM_ERR_INVALID_ARG;
   const size_t nch = ((size_t)T + 63) / 64;
   if (!mul_ok(P, nch, &nseg_all) || nseg_all > (size_t)INT32_MAX) return PRISM_ERR_INVALID_ARG;
-  if (!mul_ok(nseg_all, (size_t)5 * 64 * 64 * 4, &sz_seg) || !mul_ok(nseg_all, (size_t)3 * 64 * 4, &sz_carry) ||
+  if (!mul_ok(nseg_all, (size_t)6 * 64 * 64 * 4, &sz_seg) || !mul_ok(nseg_all, (size_t)3 * 64 * 4, &sz_carry) ||
       !mul_ok(nseg_all, (size_t)4 * 64 * 4, &sz_part))
     return PRISM_ERR_INVALID_ARG;
   pl->P = (int)P;
@@ -495,6 +495,7 @@ prism_status prism_bwd_chunked(const void* q, const void* k, const void* v, cons
   a.seg_ell = sg + 2 * sq;
   a.seg_Sin = sg + 3 * sq;
   a.seg_Lam = sg + 4 * sq;
+  a.seg_Acc = sg + 5 * sq;
   a.carry = reinterpret_cast<float*>(ws + pl.off_carry);
   a.dconv_part = reinterpret_cast<float*>(ws + pl.off_part);
   a.H = H; a.T = T; a.L = L; a.nblk = 0;

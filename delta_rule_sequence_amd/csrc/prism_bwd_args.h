@@ -16,13 +16,15 @@ struct BwdArgs {
                       // segments: [P][nseg][NSP][seg_len / kBwdSegSub][..] per sub-block
   float* scratch;     // [..][block tokens][D * D / NSP] states S_t of the block being reversed
   float* part;        // [P][NSP][T][RED] per-workgroup column sums and scalars (NSP > 1)
-  // segment-parallel form only, float32 [P][nseg][D][D] in S layout (row = value index):
+  // segment-parallel and chunked forms only, float32 [P][nseg][D][D] in S layout (row =
+  // value index; the chunked form keeps seg_B and seg_ell in H layout, H = S^T):
   float* seg_B;    // state at the segment end from a zero start
   float* seg_Phi;  // segment operator A_{t0} .. A_{t1-1}
   float* seg_ell;  // adjoint at the segment start from the segment's own outputs
   float* seg_Sin;  // state entering the segment
   float* seg_Lam;  // adjoint of the segment's last state from the tokens after it
   float* carry;    // [P][nseg][3][D] anchor terms a segment owes the three tokens before it
+  float* seg_Acc;  // chunked form only: the chunk operator in H layout (H = S^T), Phi^T
   int H, T, L, nblk;
   int nseg, seg_len;
 };

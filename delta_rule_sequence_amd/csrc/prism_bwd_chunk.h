@@ -24,10 +24,10 @@
 //         at the last token), dlG the elementwise sum of dX * X over the decayed matrices
 // and the adjoint of the start state is dH = Qt^T dO + Acc^T dH' with Qt = diag(G) Q - P Wc,
 // Acc = G_C I - K^T diag(D) Wc.  Two kernels:
-//   * bwdc_local_kernel: per chunk, in the segment form's S layout (S = H^T), the operator
-//     Phi = Acc^T, the end state from zero B = (K^T D Uc + sum U_l^T D R_l)^T and the local
-//     adjoint ell = dO^T Qt (the segment scans then give each chunk its start state and
-//     the adjoint of its end state);
+//   * bwdc_local_kernel: per chunk, the operator Acc and its transpose, the end state from
+//     zero HB = K^T D Uc + sum U_l^T D R_l and the local adjoint ell = Qt^T dO (H layout);
+//   * bwdc_scan_kernel: the two scans over a pair's chunks, giving each chunk its start
+//     state and the adjoint of its end state (stored in the S layout, S = H^T);
 //   * bwdc_grad_kernel: per chunk, from those, every gradient.
 // One workgroup of 8 waves per chunk.  Every 64 x 64 product is 16 output tiles of
 // v_mfma_f32_16x16x32_bf16; wave w computes the tiles (w / 2, 2 (w % 2) + {0, 1}) of each,
@@ -298,36 +298,79 @@ __device__ __forceinline__ void put_written(const Chunk& x, const ChainLane& cl,
   *reinterpret_cast<bf16x8*>(X + cl.t * LDM + cl.ch0) = y;
 }
 
-// T = (I + A)^-1 for A strictly lower triangular, in float32: thread (c, p) = (tid / 8,
-// tid % 8) owns T[8 m + p][c], m = 0..7; row r of the substitution is
-// T[r][c] = -sum_{j < r} A[r][j] T[j][c] (r > c), its 64 terms summed over the 8 lanes p.
-// Ap: A with row r's entry j at r * 64 + 8 (j % 8) + j / 8.  Result: bf16 row-major in X.
-__device__ __forceinline__ void unit_lower_inverse(const float* Ap, bf16_t* X) {
-  const int c = threadIdx.x >> 3, p = threadIdx.x & 7;
-  float t[8];
+// T = (I + A)^-1 for A strictly lower triangular (float32 A, row-major, stride LDF), in
+// float32 by 16 x 16 blocks.  Diagonal blocks: wave 0, lane 16 b + c walks column c of
+// block b down its rows (right-looking substitution, x_r -= A_rj x_j).  Off-diagonal
+// blocks by block distance d = 1, 2, 3 (block (j + d, j) on wave j):
+//   T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj
+// two float32 MFMA products (v_mfma_f32_16x16x4_f32), the sum's tile fed straight back as
+// the B operand of the second.  Tf (float32, stride LDF) is scratch; the result goes to Tb
+// in bfloat16 (zero above the diagonal blocks).  Every thread calls it (four barriers).
+__device__ __forceinline__ void block_inverse(const float* A, float* Tf, bf16_t* Tb) {
+  const int w = wave_id(), l = lane_id(), i = l & 15, g = l >> 4;
+  if (w == 0) {
+    const int o = 16 * g, c = i;
+    float x[16];
 #pragma unroll
-  for (int m = 0; m < 8; ++m) t[m] = (8 * m + p == c) ? 1.f : 0.f;
+    for (int r = 0; r < 16; ++r) x[r] = r == c ? 1.f : 0.f;
 #pragma unroll
-  for (int r = 1; r < 64; ++r) {
-    const float4 a0 = *reinterpret_cast<const float4*>(Ap + r * 64 + 8 * p);
-    const float4 a1 = *reinterpret_cast<const float4*>(Ap + r * 64 + 8 * p + 4);
-    const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-    float s = 0.f;
+    for (int j = 0; j < 15; ++j) {
 #pragma unroll
-    for (int m = 0; m < 8; ++m)
-      if (8 * m < r) s += av[m] * t[m];
-    s = sum8(s);
-    if (p == (r & 7) && r > c) t[r >> 3] = -s;
+      for (int r = j + 1; r < 16; ++r) x[r] -= A[(o + r) * LDF + o + j] * x[j];
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) Tf[(o + r) * LDF + o + c] = x[r];
   }
+  __syncthreads();
 #pragma unroll
-  for (int m = 0; m < 8; ++m) X[(8 * m + p) * LDM + c] = (bf16_t)t[m];
+  for (int d = 1; d < 4; ++d) {
+    if (w < 4 - d) {
+      const int bj = w, bi = w + d;
+      f32x4 xs = zero4();
+      for (int bk = bj; bk < bi; ++bk) {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+          xs = mfma(A[(16 * bi + i) * LDF + 16 * bk + 4 * kb + g], Tf[(16 * bk + 4 * kb + g) * LDF + 16 * bj + i], xs);
+      }
+      // xs[r] = X[4 g + r][i]; the next product contracts over k = 4 g + r
+      f32x4 t = zero4();
+#pragma unroll
+      for (int r = 0; r < 4; ++r) t = mfma(Tf[(16 * bi + i) * LDF + 16 * bi + 4 * g + r], xs[r], t);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Tf[(16 * bi + 4 * g + r) * LDF + 16 * bj + i] = -t[r];
+    }
+    __syncthreads();
+  }
+  for (int e = threadIdx.x; e < 64 * 16; e += NT) {
+    const int row = e >> 4, c4 = 4 * (e & 15);
+    const bool keep = (c4 >> 4) <= (row >> 4);
+    const float4 v = *reinterpret_cast<const float4*>(Tf + row * LDF + c4);
+    bf16x4 y;
+    y[0] = keep ? (bf16_t)v.x : (bf16_t)0.f;
+    y[1] = keep ? (bf16_t)v.y : (bf16_t)0.f;
+    y[2] = keep ? (bf16_t)v.z : (bf16_t)0.f;
+    y[3] = keep ? (bf16_t)v.w : (bf16_t)0.f;
+    *reinterpret_cast<bf16x4*>(Tb + row * LDM + c4) = y;
+  }
+}
+
+// lower(Gam) at the lane's four entries (row, col .. col + 3) of a 64 x 64 tile.
+__device__ __forceinline__ f32x4 gam_tile(const float* tk, int row, int col) {
+  const float b_i = tk[kB + row];
+  const float4 bj = *reinterpret_cast<const float4*>(tk + kB + col);
+  f32x4 gm;
+  gm[0] = col + 0 <= row ? __expf(b_i - bj.x) : 0.f;
+  gm[1] = col + 1 <= row ? __expf(b_i - bj.y) : 0.f;
+  gm[2] = col + 2 <= row ? __expf(b_i - bj.z) : 0.f;
+  gm[3] = col + 3 <= row ? __expf(b_i - bj.w) : 0.f;
+  return gm;
 }
 
 // The state-independent part of a chunk, shared by both kernels.  On return (after a
-// barrier): sT, sUc, sWc filled; kk = K K^T tiles and gm = lower(Gam) tiles of the wave,
-// vp = V' tiles (float32).  With HB, hb accumulates sum_l R_l^T diag(D) U_l (S layout).
+// barrier): sT, sUc, sWc filled; vp = V' tiles and uc = Uc tiles of the wave (float32).
+// With HB, hb accumulates sum_l U_l^T diag(D) R_l (H layout).
 struct Fwd {
-  f32x4 kk[2], gm[2], vp[2], uc[2];
+  f32x4 vp[2], uc[2];
 };
 
 template <bool HB>
@@ -338,23 +381,21 @@ __device__ __forceinline__ void chunk_forward(const Chunk& x, ChainLane& cl, Fwd
   const float* tk = x.tok;
   bf16_t *sK = x.m(mK), *sT = x.m(mT), *sU = x.m(mU), *sR = x.m(mR), *sN = x.m(mN);
   bf16_t *sX1 = x.m(mX1), *sX2 = x.m(mX2), *sUc = x.m(mUc), *sWc = x.m(mWc);
-  float* sAp = x.mf(m13);
-  const float beta_i = tk[kBeta + row], G_i = tk[kG + row], b_i = tk[kB + row];
-  // F1: K K^T, the decay tile, A (float32, permuted for the substitution)
+  float* sAf = x.mf(m13);
+  const float beta_i = tk[kBeta + row], G_i = tk[kG + row];
+  // F1: A = strict(diag(beta) Gam * K K^T) (float32)
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int n0 = 16 * (nt0 + h), col = n0 + 4 * g;
-    f.kk[h] = mm<false, false>(zero4(), sK, sK, 16 * mt, n0);
+    const f32x4 kk = mm<false, false>(zero4(), sK, sK, 16 * mt, n0);
+    const f32x4 gm = gam_tile(tk, row, col);
+    f32x4 av;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int j = col + r;
-      f.gm[h][r] = j <= row ? __expf(b_i - tk[kB + j]) : 0.f;
-      const float av = j < row ? beta_i * f.gm[h][r] * f.kk[h][r] : 0.f;
-      sAp[row * 64 + 8 * (j & 7) + (j >> 3)] = av;
-    }
+    for (int r = 0; r < 4; ++r) av[r] = col + r < row ? beta_i * gm[r] * kk[r] : 0.f;
+    *reinterpret_cast<f32x4*>(sAf + row * LDF + col) = av;
   }
   __syncthreads();
-  unit_lower_inverse(sAp, sT);
+  block_inverse(sAf, x.mf(mUc), sT);
   // V' = V - sum_l N_l R_l: V's tiles straight from memory
   const bf16_t* vg = static_cast<const bf16_t*>(a.v) + ((size_t)x.pr * a.T + x.t0) * D;
 #pragma unroll
@@ -371,6 +412,7 @@ __device__ __forceinline__ void chunk_forward(const Chunk& x, ChainLane& cl, Fwd
   float rc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) rc[e] = cl.r0[e];
+#pragma unroll
   for (int lv = 1; lv < x.L; ++lv) {
     // (the previous slot's products are done: barrier at the loop end, or the one above)
     load_rows(sU, static_cast<const bf16_t*>(a.u) + (((size_t)x.pr * a.T + x.t0) * (x.L - 1) + lv - 1) * D,
@@ -387,10 +429,11 @@ __device__ __forceinline__ void chunk_forward(const Chunk& x, ChainLane& cl, Fwd
     for (int h = 0; h < 2; ++h) {
       const int n0 = 16 * (nt0 + h), col = n0 + 4 * g;
       f32x4 nr = mm<false, false>(zero4(), sK, sU, 16 * mt, n0);
+      const f32x4 gm = gam_tile(tk, row, col);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) nr[r] = col + r < row ? f.gm[h][r] * nr[r] : 0.f;
+      for (int r = 0; r < 4; ++r) nr[r] = col + r < row ? gm[r] * nr[r] : 0.f;
       put_bf16(sN, row, col, nr);
-      if constexpr (HB) hb[h] = mm<true, true>(hb[h], sR, sU, 16 * mt, n0, tk + kDd);
+      if constexpr (HB) hb[h] = mm<true, true>(hb[h], sU, sR, 16 * mt, n0, tk + kDd);
     }
     __syncthreads();
 #pragma unroll
@@ -436,6 +479,8 @@ __device__ __forceinline__ void load_chunk_inputs(const Chunk& x) {
 }
 
 // Segment-form operands of each chunk (segments of one chunk: a.nseg == chunks per pair).
+// NL = L - 1 rank slots, fixed at compile time so that the rank loops unroll.
+template <int NL>
 __global__ __launch_bounds__(NT) void bwdc_local_kernel(BwdArgs a) {
   __shared__ __align__(16) char lds[Lds::total];
   Chunk x;
@@ -444,14 +489,14 @@ __global__ __launch_bounds__(NT) void bwdc_local_kernel(BwdArgs a) {
   x.pr = blockIdx.y;
   x.t0 = x.c * C;
   x.nt = min(C, a.T - x.t0);
-  x.L = a.L;
+  x.L = NL + 1;
   x.lds = lds;
   x.tok = reinterpret_cast<float*>(lds + Lds::oTok);
   const int w = wave_id(), l = lane_id(), i = l & 15, g = l >> 4;
   const int mt = w >> 1, nt0 = 2 * (w & 1), row = 16 * mt + i;
   load_chunk_inputs(x);
   ChainLane cl;
-  if (a.L > 1) chain_start(x, cl);
+  if (x.L > 1) chain_start(x, cl);
   __syncthreads();
   Fwd f;
   f32x4 hb[2] = {zero4(), zero4()};
@@ -464,12 +509,13 @@ __global__ __launch_bounds__(NT) void bwdc_local_kernel(BwdArgs a) {
   for (int h = 0; h < 2; ++h) {
     const int n0 = 16 * (nt0 + h);
     f32x4 p = mm<false, false>(zero4(), sQ, sK, 16 * mt, n0);
+    const f32x4 gm = gam_tile(tk, row, n0 + 4 * g);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) p[r] *= f.gm[h][r];
+    for (int r = 0; r < 4; ++r) p[r] *= gm[r];
     put_bf16(sP, row, n0 + 4 * g, p);
   }
   __syncthreads();
-  // Qt = diag(G) Q - P Wc; Phi = G_C I - Wc^T D K; B = hb + Uc^T D K
+  // Qt = diag(G) Q - P Wc; Acc = G_C I - K^T D Wc and its transpose Phi; HB = hb + K^T D Uc
   const float GC = tk[kG + 63];
   const size_t so = ((size_t)x.pr * a.nseg + x.c) * D * D;
 #pragma unroll
@@ -482,23 +528,132 @@ __global__ __launch_bounds__(NT) void bwdc_local_kernel(BwdArgs a) {
     for (int r = 0; r < 4; ++r) qt[r] = G_i * qt[r] - pw[r];
     put_bf16(sQt, row, col, qt);
     f32x4 ph = mm<true, true>(zero4(), sWc, sK, 16 * mt, n0, tk + kDd);
+    f32x4 ac = mm<true, true>(zero4(), sK, sWc, 16 * mt, n0, tk + kDd);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) ph[r] = (col + r == row ? GC : 0.f) - ph[r];
+    for (int r = 0; r < 4; ++r) {
+      ph[r] = (col + r == row ? GC : 0.f) - ph[r];
+      ac[r] = (col + r == row ? GC : 0.f) - ac[r];
+    }
     *reinterpret_cast<f32x4*>(a.seg_Phi + so + (size_t)row * D + col) = ph;
-    const f32x4 bb = mm<true, true>(hb[h], sUc, sK, 16 * mt, n0, tk + kDd);
+    *reinterpret_cast<f32x4*>(a.seg_Acc + so + (size_t)row * D + col) = ac;
+    const f32x4 bb = mm<true, true>(hb[h], sK, sUc, 16 * mt, n0, tk + kDd);
     *reinterpret_cast<f32x4*>(a.seg_B + so + (size_t)row * D + col) = bb;
   }
   __syncthreads();
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int n0 = 16 * (nt0 + h), col = n0 + 4 * g;
-    const f32x4 el = mm<true, true>(zero4(), sdO, sQt, 16 * mt, n0);
+    const f32x4 el = mm<true, true>(zero4(), sQt, sdO, 16 * mt, n0);
     *reinterpret_cast<f32x4*>(a.seg_ell + so + (size_t)row * D + col) = el;
   }
 }
 
+// The two chunk scans, on columns c0, c0 + 1 of the carried 64 x 64 matrix (H layout):
+// forwards (blockIdx.z = 0) X_0 = 0, X_{c+1} = Acc_c X_c + HB_c, storing S_in(c) = X_c^T;
+// backwards (blockIdx.z = 1) X_{nch-1} = dS_final (zero if absent), X_{c-1} = Acc_c^T X_c +
+// ell_c, storing Lambda_c = X_c^T.  Thread t takes rows i0 = 2 (t / 8), i0 + 1 and the
+// contraction slice k = 8 q .. 8 q + 7 (q = t % 8): it keeps those 16 entries of the step's
+// operator in registers (loaded DEPTH steps ahead, so a step never waits on memory), reads
+// rows 8 q .. 8 q + 7 of the two carried columns from LDS (skewed so the eight slices of a
+// wave hit distinct banks) and forms 2 x 2 partial sums; three DPP exchange rounds within
+// the 8 lanes of the row pair leave lanes q and q ^ 1 with X_new[i0 + q / 4][c0 + (q / 2) % 2].
+// One barrier per step.
+__device__ __forceinline__ float dpp_mirror8(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x141, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float dpp_rev4(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x1B, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float dpp_swap2(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
+}
+
+__global__ __launch_bounds__(256) void bwdc_scan_kernel(BwdArgs a) {
+  constexpr int DEPTH = 8;
+  constexpr int HS = D + D / 8;  // carried rows with a one-row skew every 8 rows
+  __shared__ __align__(16) float2 sH[2][HS];
+  const int tid = threadIdx.x, i0 = 2 * (tid >> 3), q = tid & 7;
+  const int pr = blockIdx.x, c0 = 2 * blockIdx.y;
+  const bool rev = blockIdx.z == 1;
+  const int n = a.nseg;
+  const int orow = i0 + (q >> 2), ocol = c0 + ((q >> 1) & 1);  // the output this lane ends with (lanes q, q ^ 1)
+  const size_t base = (size_t)pr * n * D * D;
+  const float* A0 = (rev ? a.seg_Phi : a.seg_Acc) + base + (size_t)i0 * D + 8 * q;
+  const float* B0 = (rev ? a.seg_ell : a.seg_B) + base + (size_t)orow * D + ocol;
+  float* O0 = (rev ? a.seg_Lam : a.seg_Sin) + base + (size_t)ocol * D + orow;
+  const bool wr = (q & 1) == 0;
+  auto hrow = [](int r) { return r + (r >> 3); };
+  auto chunk_of = [&](int s) { return rev ? n - 1 - s : s; };
+#define PRISM_DECL(D_) float4 R##D_##_0, R##D_##_1, R##D_##_2, R##D_##_3; float R##D_##_b;
+#define PRISM_FETCH(D_, S)                                                                    \
+  {                                                                                           \
+    const size_t cn_ = (size_t)chunk_of((S) < n ? (S) : n - 1);                               \
+    const float4* src_ = reinterpret_cast<const float4*>(A0 + cn_ * D * D);                  \
+    R##D_##_0 = src_[0];                                                                      \
+    R##D_##_1 = src_[1];                                                                      \
+    R##D_##_2 = src_[D / 4];                                                                  \
+    R##D_##_3 = src_[D / 4 + 1];                                                              \
+    R##D_##_b = B0[cn_ * D * D];                                                              \
+  }
+  PRISM_DECL(0) PRISM_DECL(1) PRISM_DECL(2) PRISM_DECL(3)
+  PRISM_DECL(4) PRISM_DECL(5) PRISM_DECL(6) PRISM_DECL(7)
+  PRISM_FETCH(0, 0) PRISM_FETCH(1, 1) PRISM_FETCH(2, 2) PRISM_FETCH(3, 3)
+  PRISM_FETCH(4, 4) PRISM_FETCH(5, 5) PRISM_FETCH(6, 6) PRISM_FETCH(7, 7)
+  const float* X0 = rev ? a.dS_final : nullptr;
+  float h = X0 != nullptr ? X0[(size_t)pr * D * D + (size_t)orow * D + ocol] : 0.f;
+  if (tid < D)
+    sH[0][hrow(tid)] = X0 != nullptr ? *reinterpret_cast<const float2*>(X0 + (size_t)pr * D * D + (size_t)tid * D + c0)
+                                     : make_float2(0.f, 0.f);
+  __syncthreads();
+  const bool lo4 = q < 4, lo2 = (q & 2) == 0;
+  int cur = 0;
+#define PRISM_SCAN_STEP(D_, PREFETCH)                                                         \
+  {                                                                                           \
+    const int s = s0 + (D_);                                                                  \
+    if (wr) O0[(size_t)chunk_of(s) * D * D] = h;                                              \
+    const float ar0[8] = {R##D_##_0.x, R##D_##_0.y, R##D_##_0.z, R##D_##_0.w,                 \
+                          R##D_##_1.x, R##D_##_1.y, R##D_##_1.z, R##D_##_1.w};                \
+    const float ar1[8] = {R##D_##_2.x, R##D_##_2.y, R##D_##_2.z, R##D_##_2.w,                 \
+                          R##D_##_3.x, R##D_##_3.y, R##D_##_3.z, R##D_##_3.w};                \
+    const float bv = R##D_##_b;                                                               \
+    float v[4] = {0.f, 0.f, 0.f, 0.f}; /* [row][col] */                                       \
+    _Pragma("unroll") for (int m = 0; m < 8; ++m) {                                           \
+      const float2 hv = sH[cur][hrow(8 * q + m)];                                             \
+      v[0] += ar0[m] * hv.x;                                                                  \
+      v[1] += ar0[m] * hv.y;                                                                  \
+      v[2] += ar1[m] * hv.x;                                                                  \
+      v[3] += ar1[m] * hv.y;                                                                  \
+    }                                                                                         \
+    if (PREFETCH) PRISM_FETCH(D_, s + DEPTH)                                                  \
+    float n2[2];                                                                              \
+    _Pragma("unroll") for (int j = 0; j < 2; ++j)                                             \
+      n2[j] = (lo4 ? v[j] : v[2 + j]) + dpp_mirror8(lo4 ? v[2 + j] : v[j]);                   \
+    const float n1 = (lo2 ? n2[0] : n2[1]) + dpp_rev4(lo2 ? n2[1] : n2[0]);                   \
+    h = n1 + dpp_swap2(n1) + bv;                                                              \
+    reinterpret_cast<float*>(&sH[cur ^ 1][hrow(orow)])[(q >> 1) & 1] = h;                     \
+    cur ^= 1;                                                                                 \
+    __syncthreads();                                                                          \
+  }
+  int s0 = 0;
+  for (; s0 + DEPTH <= n; s0 += DEPTH) {
+    PRISM_SCAN_STEP(0, true) PRISM_SCAN_STEP(1, true) PRISM_SCAN_STEP(2, true) PRISM_SCAN_STEP(3, true)
+    PRISM_SCAN_STEP(4, true) PRISM_SCAN_STEP(5, true) PRISM_SCAN_STEP(6, true) PRISM_SCAN_STEP(7, true)
+  }
+  if (s0 + 0 < n) PRISM_SCAN_STEP(0, false)
+  if (s0 + 1 < n) PRISM_SCAN_STEP(1, false)
+  if (s0 + 2 < n) PRISM_SCAN_STEP(2, false)
+  if (s0 + 3 < n) PRISM_SCAN_STEP(3, false)
+  if (s0 + 4 < n) PRISM_SCAN_STEP(4, false)
+  if (s0 + 5 < n) PRISM_SCAN_STEP(5, false)
+  if (s0 + 6 < n) PRISM_SCAN_STEP(6, false)
+#undef PRISM_SCAN_STEP
+#undef PRISM_FETCH
+#undef PRISM_DECL
+}
+
 // Every gradient of chunk (blockIdx.x, pair blockIdx.y) from its start state (seg_Sin) and
-// the adjoint of its end state (seg_Lam).
+// the adjoint of its end state (seg_Lam).  NL = L - 1 rank slots, fixed at compile time.
+template <int NL>
 __global__ __launch_bounds__(NT) void bwdc_grad_kernel(BwdArgs a) {
   __shared__ __align__(16) char lds[Lds::total];
   Chunk x;
@@ -507,7 +662,7 @@ __global__ __launch_bounds__(NT) void bwdc_grad_kernel(BwdArgs a) {
   x.pr = blockIdx.y;
   x.t0 = x.c * C;
   x.nt = min(C, a.T - x.t0);
-  x.L = a.L;
+  x.L = NL + 1;
   x.lds = lds;
   x.tok = reinterpret_cast<float*>(lds + Lds::oTok);
   float* tk = x.tok;
@@ -515,21 +670,17 @@ __global__ __launch_bounds__(NT) void bwdc_grad_kernel(BwdArgs a) {
   const int mt = w >> 1, nt0 = 2 * (w & 1), row = 16 * mt + i, half = w & 1;
   const size_t so = ((size_t)x.pr * a.nseg + x.c) * D * D;
   load_chunk_inputs(x);
-  const float gc_part = load_state(x.m(mS), a.seg_Sin + so, a.seg_Lam + so);
-  load_state(x.m(mLam), a.seg_Lam + so, nullptr);
   {
-    const float s = sum8(gc_part);  // 8 lanes: one row of 64 entries
-    // rows of the wave: 8; partials of the wave's 8 rows summed in order below
-    if ((tid & 7) == 0) tk[kRowLg + (tid >> 3)] = s;  // borrowed: rewritten before kRowLg is used
+    // <dH', H> (the end state's factor G_C): this thread's 8 entries, then the wave's sum
+    float gc = load_state(x.m(mS), a.seg_Sin + so, a.seg_Lam + so);
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) gc += __shfl_xor(gc, o);
+    if (l == 0) tk[kMisc + w] = gc;
   }
+  load_state(x.m(mLam), a.seg_Lam + so, nullptr);
   ChainLane cl;
-  if (a.L > 1) chain_start(x, cl);
+  if (x.L > 1) chain_start(x, cl);
   __syncthreads();
-  float dGC = 0.f;
-  if (tid == 0) {
-    for (int r = 0; r < 64; ++r) dGC += tk[kRowLg + r];
-    tk[kMisc] = dGC;
-  }
   Fwd f;
   f32x4 hb_unused[2];
   chunk_forward<false>(x, cl, f, hb_unused);
@@ -550,8 +701,9 @@ __global__ __launch_bounds__(NT) void bwdc_grad_kernel(BwdArgs a) {
     for (int r = 0; r < 4; ++r) e[r] = f.uc[h][r] - e[r];
     put_bf16(sE, row, col, e);
     p[h] = mm<false, false>(zero4(), sQ, sK, 16 * mt, n0);
+    const f32x4 gm = gam_tile(tk, row, col);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) p[h][r] *= f.gm[h][r];
+    for (int r = 0; r < 4; ++r) p[h][r] *= gm[r];
     put_bf16(sP, row, col, p[h]);
     dlg[h] = zero4();
   }
@@ -568,12 +720,13 @@ __global__ __launch_bounds__(NT) void bwdc_grad_kernel(BwdArgs a) {
     for (int r = 0; r < 4; ++r) de[r] = a1[r] + D_i * a2[r];
     put_bf16(sdE, row, col, de);
     f32x4 dp = mm<false, false>(zero4(), sdO, sE, 16 * mt, n0);
+    const f32x4 gm = gam_tile(tk, row, col);
     f32x4 zp;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       dp[r] = col + r <= row ? dp[r] : 0.f;
       dlg[h][r] += dp[r] * p[h][r];
-      zp[r] = f.gm[h][r] * dp[r];
+      zp[r] = gm[r] * dp[r];
     }
     put_bf16(sZ, row, col, zp);
     const f32x4 qh = mm<false, false>(zero4(), sQ, sS, 16 * mt, n0);
@@ -641,14 +794,16 @@ __global__ __launch_bounds__(NT) void bwdc_grad_kernel(BwdArgs a) {
   for (int h = 0; h < 2; ++h) {
     const int n0 = 16 * (nt0 + h), col = n0 + 4 * g;
     const f32x4 t = mm<true, true>(zero4(), sT, sY, 16 * mt, n0);
+    const f32x4 kk = mm<false, false>(zero4(), sK, sK, 16 * mt, n0);
+    const f32x4 gm = gam_tile(tk, row, col);
     f32x4 z;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float da = col + r < row ? -t[r] : 0.f;
-      const float gk = f.gm[h][r] * f.kk[h][r];
+      const float gk = gm[r] * kk[r];
       rb_beta += da * gk;
       dlg[h][r] += da * beta_i * gk;
-      z[r] = beta_i * f.gm[h][r] * da;
+      z[r] = beta_i * gm[r] * da;
     }
     put_bf16(sZ2, row, col, z);
   }
@@ -667,8 +822,9 @@ __global__ __launch_bounds__(NT) void bwdc_grad_kernel(BwdArgs a) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) dr[e] = 0.f;
   float da_carry = 0.f;
-  const bool in_t = a.L > 1 && cl.t < x.nt;
-  const size_t tg = (size_t)x.pr * a.T + x.t0 + (a.L > 1 ? cl.t : 0);
+  const bool in_t = x.L > 1 && cl.t < x.nt;
+  const size_t tg = (size_t)x.pr * a.T + x.t0 + (x.L > 1 ? cl.t : 0);
+#pragma unroll 1
   for (int lv = x.L - 1; lv >= 1; --lv) {
     load_rows(sU, static_cast<const bf16_t*>(a.u) + (((size_t)x.pr * a.T + x.t0) * (x.L - 1) + lv - 1) * D,
               (size_t)(x.L - 1) * D, x.nt);
@@ -694,17 +850,18 @@ __global__ __launch_bounds__(NT) void bwdc_grad_kernel(BwdArgs a) {
       f32x4 pu = mm<false, false>(zero4(), sQ, sU, 16 * mt, n0);
       f32x4 dpu = mm<false, false>(zero4(), sdO, sR, 16 * mt, n0);
       f32x4 dn = mm<false, false>(zero4(), sdVp, sR, 16 * mt, n0);
+      const f32x4 gm = gam_tile(tk, row, col);
       f32x4 zpu, zn;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const bool lo = col + r <= row, st = col + r < row;
-        n[r] = st ? f.gm[h][r] * n[r] : 0.f;
-        pu[r] = f.gm[h][r] * pu[r];
+        n[r] = st ? gm[r] * n[r] : 0.f;
+        pu[r] = gm[r] * pu[r];
         dpu[r] = lo ? dpu[r] : 0.f;
         dn[r] = st ? -dn[r] : 0.f;
         dlg[h][r] += dpu[r] * pu[r] + dn[r] * n[r];
-        zpu[r] = f.gm[h][r] * dpu[r];
-        zn[r] = f.gm[h][r] * dn[r];
+        zpu[r] = gm[r] * dpu[r];
+        zn[r] = gm[r] * dn[r];
       }
       put_bf16(sN, row, col, n);
       put_bf16(sPU, row, col, pu);
@@ -712,7 +869,7 @@ __global__ __launch_bounds__(NT) void bwdc_grad_kernel(BwdArgs a) {
       put_bf16(sZn, row, col, zn);
     }
     __syncthreads();
-    float* dug = a.du + (grow * (a.L - 1) + lv - 1) * D;
+    float* dug = a.du + (grow * (x.L - 1) + lv - 1) * D;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int n0 = 16 * (nt0 + h), col = n0 + 4 * g;
@@ -744,7 +901,7 @@ __global__ __launch_bounds__(NT) void bwdc_grad_kernel(BwdArgs a) {
       const float al = tk[kAl + lv * 64 + cl.t], alm = tk[kAl + (lv - 1) * 64 + cl.t];
       float s = 0.f, s2 = 0.f;
       float gmv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      if (in_t) load_bf16x8(gmv, static_cast<const bf16_t*>(a.gamma) + (tg * (a.L - 1) + lv - 1) * D + cl.ch0);
+      if (in_t) load_bf16x8(gmv, static_cast<const bf16_t*>(a.gamma) + (tg * (x.L - 1) + lv - 1) * D + cl.ch0);
       float dgm[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -757,8 +914,8 @@ __global__ __launch_bounds__(NT) void bwdc_grad_kernel(BwdArgs a) {
       s = sum8(s) + da_carry;
       da_carry = -sum8(s2);
       if (in_t) {
-        if ((tid & 7) == 0) a.dalpha[tg * a.L + lv] = s;
-        float* dgp = a.dgamma + (tg * (a.L - 1) + lv - 1) * D + cl.ch0;
+        if ((tid & 7) == 0) a.dalpha[tg * x.L + lv] = s;
+        float* dgp = a.dgamma + (tg * (x.L - 1) + lv - 1) * D + cl.ch0;
         *reinterpret_cast<float4*>(dgp) = make_float4(dgm[0], dgm[1], dgm[2], dgm[3]);
         *reinterpret_cast<float4*>(dgp + 4) = make_float4(dgm[4], dgm[5], dgm[6], dgm[7]);
       }
@@ -798,12 +955,27 @@ __global__ __launch_bounds__(NT) void bwdc_grad_kernel(BwdArgs a) {
         if (i == 0) tk[kColLg + mt * 64 + 16 * (nt0 + h) + 4 * g + r] = cs;
       }
   }
-  if (a.L > 1) {
-    // d r_0 of the chain, then the anchor's terms
+  float dvd[8];
+  bf16_t* sVx = x.m(mQ);  // value rows t0 - 3 .. t0 + 63 (67 rows: slot Q and the start of K's)
+  if (x.L > 1) {
+    // d r_0 of the chain, then the anchor's terms: this thread's direct dv, the value rows
 #pragma unroll
     for (int e = 0; e < 8; e += 4)
       *reinterpret_cast<float4*>(sdR + cl.t * LDF + cl.ch0 + e) = make_float4(dr[e], dr[e + 1], dr[e + 2], dr[e + 3]);
-    if ((tid & 7) == 0 && in_t) a.dalpha[tg * a.L] = da_carry;
+    if ((tid & 7) == 0 && in_t) a.dalpha[tg * x.L] = da_carry;
+    if (in_t) {
+      const float4 d0 = *reinterpret_cast<const float4*>(a.dv + tg * D + cl.ch0);
+      const float4 d1 = *reinterpret_cast<const float4*>(a.dv + tg * D + cl.ch0 + 4);
+      dvd[0] = d0.x; dvd[1] = d0.y; dvd[2] = d0.z; dvd[3] = d0.w;
+      dvd[4] = d1.x; dvd[5] = d1.y; dvd[6] = d1.z; dvd[7] = d1.w;
+    }
+    const bf16_t* vg = static_cast<const bf16_t*>(a.v) + (size_t)x.pr * a.T * D;
+    for (int e = tid; e < 67 * 8; e += NT) {
+      const int r = e >> 3, c8 = 8 * (e & 7), tv = x.t0 - 3 + r;
+      uint4 y = {0u, 0u, 0u, 0u};
+      if (tv >= 0 && tv < a.T) y = *reinterpret_cast<const uint4*>(vg + (size_t)tv * D + c8);
+      *reinterpret_cast<uint4*>(sVx + r * LDM + c8) = y;
+    }
   }
   __syncthreads();
   if (tid < 64) {
@@ -817,7 +989,12 @@ __global__ __launch_bounds__(NT) void bwdc_grad_kernel(BwdArgs a) {
     float tot = dD * Dt;
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) tot += __shfl_xor(tot, o);
-    if (t == 63) db += tot + tk[kMisc] * Gt;
+    if (t == 63) {
+      float dGC = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < 8; ++ww) dGC += tk[kMisc + ww];
+      db += tot + dGC * Gt;
+    }
     // suffix sum over lanes t .. 63
     float sfx = db;
 #pragma unroll
@@ -831,23 +1008,26 @@ __global__ __launch_bounds__(NT) void bwdc_grad_kernel(BwdArgs a) {
       a.dbeta[gi] = tk[kRowBeta + t] + tk[kRowBeta + 64 + t];
     }
   }
-  if (a.L > 1) {
+  if (x.L > 1) {
     const size_t ps = (size_t)x.pr * a.nseg + x.c;
     const float* w = a.conv_w + (size_t)(x.pr % a.H) * 4 * D;
     // dv += d r_0 - sum_j w_j d r_0(t + 3 - j) over the chunk's anchors that read v_t
     if (in_t) {
-      float* dvp = a.dv + tg * D + cl.ch0;
+      float out[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int ch = cl.ch0 + e;
-        float s = dvp[e] + sdR[cl.t * LDF + ch];
+        float s = dvd[e] + sdR[cl.t * LDF + ch];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int ta = cl.t + 3 - j;
           if (ta < C) s -= w[j * D + ch] * sdR[ta * LDF + ch];
         }
-        dvp[e] = s;
+        out[e] = s;
       }
+      float* dvp = a.dv + tg * D + cl.ch0;
+      *reinterpret_cast<float4*>(dvp) = make_float4(out[0], out[1], out[2], out[3]);
+      *reinterpret_cast<float4*>(dvp + 4) = make_float4(out[4], out[5], out[6], out[7]);
     }
     if (tid < 3 * D) {
       // the terms owed to tokens t0 - 1 - jj of the previous chunk
@@ -858,12 +1038,8 @@ __global__ __launch_bounds__(NT) void bwdc_grad_kernel(BwdArgs a) {
     } else if (tid >= 256) {
       // dconv_w share: dw_j = -sum_t d r_0(t) v_{t-3+j}
       const int j = (tid - 256) / D, ch = (tid - 256) % D;
-      const bf16_t* v = static_cast<const bf16_t*>(a.v) + (size_t)x.pr * a.T * D;
       float s = 0.f;
-      for (int t = 0; t < x.nt; ++t) {
-        const int tv = x.t0 + t - 3 + j;
-        if (tv >= 0) s -= sdR[t * LDF + ch] * (float)v[(size_t)tv * D + ch];
-      }
+      for (int t = 0; t < x.nt; ++t) s -= sdR[t * LDF + ch] * (float)sVx[(t + j) * LDM + ch];
       a.dconv_part[(ps * 4 + j) * D + ch] = s;
     }
   }

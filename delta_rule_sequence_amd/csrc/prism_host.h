@@ -76,7 +76,7 @@ int bwd_seg_slices(int d);
 prism_status launch_bwd(prism_dtype dt, int d, const BwdArgs& a, int B, int P, float* dconv_w, bool segments,
                         hipStream_t stream);
 // The chunked backward (prism_bwd_chunk.h): bfloat16, dk = dv = 64, one segment per 64-token
-// chunk (a.nseg chunks per pair): chunk operators, the segment scans, chunk gradients, the
+// chunk (a.nseg chunks per pair): chunk operators, the chunk scans, chunk gradients, the
 // anchor carry and the batch sum of dconv_w.
 prism_status launch_bwd_chunked(const BwdArgs& a, int B, int P, float* dconv_w, hipStream_t stream);
 

@@ -259,15 +259,15 @@ prism_status prism_bwd_lowmem(const void* q, const void* k, const void* v,
  * the delta rule's UT / WY chunk form (Tencent / PKU article, section 01-三: each chunk
  * processed as blocks of matrix products; PRISM reading notes, sections 2.1-2.3 for the
  * rank-L writes) differentiated chunk by chunk.  Per 64-token chunk one workgroup forms the
- * chunk's operator, its end state from zero and its own adjoint contribution; the segment
- * scans give every chunk its entering state and the adjoint arriving at its end; a second
+ * chunk's operator, its end state from zero and its own adjoint contribution; two scans
+ * over the chunks give every chunk its entering state and the adjoint arriving at its end; a second
  * workgroup per chunk forms every gradient from those with bfloat16 MFMA products (float32
  * sums; the unit lower triangular inverse in float32).  The operands are rounded to
  * bfloat16 like the forward's, so the gradients carry the forward's bfloat16 error
  * (a few 1e-3 of each gradient's largest entry), not prism_bwd's float32 one.  Arguments,
  * layouts and outputs as prism_bwd; dt must be PRISM_BF16 and dk = dv = 64 (else
  * PRISM_ERR_UNSUPPORTED), B * H <= 65535.  Deterministic.  Workspace:
- * prism_bwd_chunked_workspace_bytes (per chunk five float32 64 x 64 matrices plus 1.75 KiB);
+ * prism_bwd_chunked_workspace_bytes (per chunk six float32 64 x 64 matrices plus 1.75 KiB);
  * ownership, stream and errors as prism_fwd. */
 size_t prism_bwd_chunked_workspace_bytes(int B, int H, int T, int dk, int dv, int L, prism_dtype dt);
 prism_status prism_bwd_chunked(const void* q, const void* k, const void* v,
