@@ -98,8 +98,11 @@ namespace {
 template <int NL>
 void bwdc_launch(const BwdArgs& a, int P, hipStream_t stream) {
   const dim3 grid((unsigned)a.nseg, (unsigned)P);
+  const dim3 ggrid((unsigned)a.ngrp, (unsigned)P);
   hipLaunchKernelGGL((bwdc::bwdc_local_kernel<NL>), grid, dim3(bwdc::NT), 0, stream, a);
-  hipLaunchKernelGGL(bwdc::bwdc_scan_kernel, dim3((unsigned)P, 64 / 2, 2), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(bwdc::bwdc_compose_kernel, ggrid, dim3(bwdc::NT), 0, stream, a);
+  hipLaunchKernelGGL(bwdc::bwdc_scan_kernel, dim3((unsigned)P, 64 / bwdc::kScanCols, 2), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(bwdc::bwdc_expand_kernel, dim3((unsigned)a.ngrp, (unsigned)P, 2), dim3(bwdc::NT), 0, stream, a);
   hipLaunchKernelGGL((bwdc::bwdc_grad_kernel<NL>), grid, dim3(bwdc::NT), 0, stream, a);
 }
 }  // namespace

@@ -430,10 +430,12 @@ namespace {
 
 // Workspace of the chunked backward: per 64-token chunk six float32 64 x 64 matrices
 // (operator and its transpose, end state from zero, local adjoint, entering state,
-// arriving adjoint), its anchor carry [3][64] and dconv_w share [4][64].
+// arriving adjoint), its anchor carry [3][64] and dconv_w share [4][64], and four bf16
+// 64 x 64 matrices (T, Uc, Wc, V') that the local pass hands to the gradient pass; per
+// group of four chunks the same six float32 matrices for the two-level scan.
 struct BwdChunkPlan {
-  int P, nch;
-  size_t off_seg, off_carry, off_part, total;
+  int P, nch, ngrp;
+  size_t off_seg, off_carry, off_part, off_mats, off_grp, total;
 };
 
 prism_status make_bwd_chunk_plan(int B, int H, int T, int dk, int dv, int L, prism_dtype dt, BwdChunkPlan* pl) {
@@ -441,20 +443,25 @@ prism_status make_bwd_chunk_plan(int B, int H, int T, int dk, int dv, int L, pri
   if (dt != PRISM_F32 && dt != PRISM_BF16) return PRISM_ERR_INVALID_ARG;
   if (L < 1 || L > 8) return PRISM_ERR_UNSUPPORTED;
   if (dt != PRISM_BF16 || dk != 64 || dv != 64) return PRISM_ERR_UNSUPPORTED;
-  size_t P, c, nseg_all, sz_seg, sz_carry, sz_part;
+  size_t P, c, nseg_all, sz_seg, sz_carry, sz_part, sz_mats, sz_grp;
   if (!mul_ok((size_t)B, (size_t)H, &P) || P > 65535) return PRISM_ERR_INVALID_ARG;
   if (!mul_ok(P, (size_t)T, &c) || !mul_ok(c, (size_t)L * dk * 4, &c)) return PRISM_ERR_INVALID_ARG;
   const size_t nch = ((size_t)T + 63) / 64;
   if (!mul_ok(P, nch, &nseg_all) || nseg_all > (size_t)INT32_MAX) return PRISM_ERR_INVALID_ARG;
   if (!mul_ok(nseg_all, (size_t)6 * 64 * 64 * 4, &sz_seg) || !mul_ok(nseg_all, (size_t)3 * 64 * 4, &sz_carry) ||
-      !mul_ok(nseg_all, (size_t)4 * 64 * 4, &sz_part))
+      !mul_ok(nseg_all, (size_t)4 * 64 * 4, &sz_part) || !mul_ok(nseg_all, (size_t)4 * 64 * 64 * 2, &sz_mats))
     return PRISM_ERR_INVALID_ARG;
+  const size_t ngrp = (nch + prism::kBwdGroup - 1) / prism::kBwdGroup;
+  if (!mul_ok(P * ngrp, (size_t)6 * 64 * 64 * 4, &sz_grp)) return PRISM_ERR_INVALID_ARG;
   pl->P = (int)P;
   pl->nch = (int)nch;
   pl->off_seg = 0;
   pl->off_carry = align_up(sz_seg);
   pl->off_part = align_up(pl->off_carry + sz_carry);
-  pl->total = align_up(pl->off_part + sz_part);
+  pl->off_mats = align_up(pl->off_part + sz_part);
+  pl->off_grp = align_up(pl->off_mats + sz_mats);
+  pl->total = align_up(pl->off_grp + sz_grp);
+  pl->ngrp = (int)ngrp;
   return PRISM_OK;
 }
 
@@ -498,6 +505,16 @@ prism_status prism_bwd_chunked(const void* q, const void* k, const void* v, cons
   a.seg_Acc = sg + 5 * sq;
   a.carry = reinterpret_cast<float*>(ws + pl.off_carry);
   a.dconv_part = reinterpret_cast<float*>(ws + pl.off_part);
+  a.chunk_mats = ws + pl.off_mats;
+  const size_t gq = (size_t)pl.P * pl.ngrp * 64 * 64;
+  float* gs = reinterpret_cast<float*>(ws + pl.off_grp);
+  a.grp_Acc = gs;
+  a.grp_Phi = gs + gq;
+  a.grp_B = gs + 2 * gq;
+  a.grp_ell = gs + 3 * gq;
+  a.grp_Sin = gs + 4 * gq;
+  a.grp_Lam = gs + 5 * gq;
+  a.ngrp = pl.ngrp;
   a.H = H; a.T = T; a.L = L; a.nblk = 0;
   a.nseg = pl.nch; a.seg_len = 64;
   return prism::host::launch_bwd_chunked(a, B, pl.P, dconv_w, stream);

@@ -6,6 +6,7 @@ namespace prism {
 
 constexpr int kBwdBlock = 64;   // tokens between state checkpoints of the sequential backward
 constexpr int kBwdSegSub = 8;   // tokens between state checkpoints inside a segment
+constexpr int kBwdGroup = 4;    // chunks per group of the chunked form's two-level scan
 
 struct BwdArgs {
   const void *q, *k, *v, *u, *gamma, *d_o;
@@ -25,6 +26,12 @@ struct BwdArgs {
   float* seg_Lam;  // adjoint of the segment's last state from the tokens after it
   float* carry;    // [P][nseg][3][D] anchor terms a segment owes the three tokens before it
   float* seg_Acc;  // chunked form only: the chunk operator in H layout (H = S^T), Phi^T
+  void* chunk_mats;  // chunked form only: bf16 [P][nseg][4][64][64] T, Uc, Wc, V' of each chunk
+  // chunked form only, float32 [P][ngrp][64][64], groups of kBwdGroup chunks: the group
+  // operator (H layout) and its transpose, its end state from zero and local adjoint (H
+  // layout), its entering state and arriving adjoint (S layout)
+  float *grp_Acc, *grp_Phi, *grp_B, *grp_ell, *grp_Sin, *grp_Lam;
+  int ngrp;
   int H, T, L, nblk;
   int nseg, seg_len;
 };

@@ -25,10 +25,12 @@
 // and the adjoint of the start state is dH = Qt^T dO + Acc^T dH' with Qt = diag(G) Q - P Wc,
 // Acc = G_C I - K^T diag(D) Wc.  Two kernels:
 //   * bwdc_local_kernel: per chunk, the operator Acc and its transpose, the end state from
-//     zero HB = K^T D Uc + sum U_l^T D R_l and the local adjoint ell = Qt^T dO (H layout);
+//     zero HB = K^T D Uc + sum U_l^T D R_l and the local adjoint ell = Qt^T dO (H layout),
+//     and T, Uc, Wc, V' for the gradient pass (bfloat16);
 //   * bwdc_scan_kernel: the two scans over a pair's chunks, giving each chunk its start
 //     state and the adjoint of its end state (stored in the S layout, S = H^T);
-//   * bwdc_grad_kernel: per chunk, from those, every gradient.
+//   * bwdc_grad_kernel: per chunk, from those, every gradient (the state-independent part
+//     of the chunk is not formed again).
 // One workgroup of 8 waves per chunk.  Every 64 x 64 product is 16 output tiles of
 // v_mfma_f32_16x16x32_bf16; wave w computes the tiles (w / 2, 2 (w % 2) + {0, 1}) of each,
 // its operands read from LDS (16-byte row reads, or gfx950's transposing reads for a
@@ -63,7 +65,8 @@ struct Lds {
   static constexpr int oTok = 16 * kMat;          // per-token arrays
   // per-token float32 arrays (64 each)
   static constexpr int nTok = 5 + kMaxL + 12;     // b, G, D, beta, g, alpha[8], partials
-  static constexpr int total = oTok + nTok * 64 * 4 + 4 * 64 * 4;  // + dlG column partials [4][64]
+  static constexpr int oVx = oTok + nTok * 64 * 4 + 4 * 64 * 4;  // after the dlG column partials [4][64]
+  static constexpr int total = oVx + 67 * 64 * 2;  // value rows t0 - 3 .. t0 + 63, bf16, unpadded
 };
 static_assert(Lds::total <= 163840, "LDS plan exceeds 160 KiB");
 
@@ -273,20 +276,27 @@ __device__ __forceinline__ void chain_start(const Chunk& x, ChainLane& cl) {
   }
 }
 
-// factor 1 - alpha_{t,l} gamma_{t,l} of the thread's channels (gamma slot l)
-__device__ __forceinline__ void chain_factor(const Chunk& x, const ChainLane& cl, int l, float (&f)[8]) {
+// factor 1 - alpha_{t,l} gamma_{t,l} of the thread's channels (gamma slot l), and gamma itself
+__device__ __forceinline__ void chain_factor(const Chunk& x, const ChainLane& cl, int l, float (&f)[8],
+                                             float (&gm)[8]) {
   const BwdArgs& a = *x.a;
   if (cl.t >= x.nt) {  // past the sequence end: alpha is zero, nothing is read
 #pragma unroll
-    for (int e = 0; e < 8; ++e) f[e] = 1.f;
+    for (int e = 0; e < 8; ++e) {
+      f[e] = 1.f;
+      gm[e] = 0.f;
+    }
     return;
   }
-  float gm[8];
   load_bf16x8(gm, static_cast<const bf16_t*>(a.gamma) +
                       (((size_t)x.pr * a.T + x.t0 + cl.t) * (x.L - 1) + l) * D + cl.ch0);
   const float al = x.tok[kAl + l * 64 + cl.t];
 #pragma unroll
   for (int e = 0; e < 8; ++e) f[e] = 1.f - al * gm[e];
+}
+__device__ __forceinline__ void chain_factor(const Chunk& x, const ChainLane& cl, int l, float (&f)[8]) {
+  float gm[8];
+  chain_factor(x, cl, l, f, gm);
 }
 
 // R_l = alpha_l r_l into X (bf16 rows t)
@@ -504,6 +514,21 @@ __global__ __launch_bounds__(NT) void bwdc_local_kernel(BwdArgs a) {
   const float* tk = x.tok;
   bf16_t *sQ = x.m(mQ), *sK = x.m(mK), *sdO = x.m(mdO), *sUc = x.m(mUc), *sWc = x.m(mWc);
   bf16_t *sP = x.m(mX1), *sQt = x.m(mX2);
+  {
+    // T, Uc, Wc and V' for the gradient pass (bf16, row-major 64 x 64 each)
+    bf16_t* cm = static_cast<bf16_t*>(a.chunk_mats) + ((size_t)x.pr * a.nseg + x.c) * 4 * 4096;
+    const int tid = threadIdx.x, r = tid >> 3, c8 = 8 * (tid & 7);
+    *reinterpret_cast<uint4*>(cm + r * 64 + c8) = *reinterpret_cast<const uint4*>(x.m(mT) + r * LDM + c8);
+    *reinterpret_cast<uint4*>(cm + 4096 + r * 64 + c8) = *reinterpret_cast<const uint4*>(sUc + r * LDM + c8);
+    *reinterpret_cast<uint4*>(cm + 8192 + r * 64 + c8) = *reinterpret_cast<const uint4*>(sWc + r * LDM + c8);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      bf16x4 y;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) y[q] = (bf16_t)f.vp[h][q];
+      *reinterpret_cast<bf16x4*>(cm + 12288 + row * 64 + 16 * (nt0 + h) + 4 * g) = y;
+    }
+  }
   // P = lower(Gam * Q K^T)
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
@@ -548,16 +573,17 @@ __global__ __launch_bounds__(NT) void bwdc_local_kernel(BwdArgs a) {
   }
 }
 
-// The two chunk scans, on columns c0, c0 + 1 of the carried 64 x 64 matrix (H layout):
-// forwards (blockIdx.z = 0) X_0 = 0, X_{c+1} = Acc_c X_c + HB_c, storing S_in(c) = X_c^T;
-// backwards (blockIdx.z = 1) X_{nch-1} = dS_final (zero if absent), X_{c-1} = Acc_c^T X_c +
-// ell_c, storing Lambda_c = X_c^T.  Thread t takes rows i0 = 2 (t / 8), i0 + 1 and the
+// The two scans over a pair's groups of chunks, on columns c0 .. c0 + 7 of the carried
+// 64 x 64 matrix (H layout): forwards (blockIdx.z = 0) X_0 = 0, X_{g+1} = Acc_g X_g + HB_g,
+// storing S_in(g) = X_g^T; backwards (blockIdx.z = 1) X_{ngrp-1} = dS_final (zero if
+// absent), X_{g-1} = Acc_g^T X_g + ell_g, storing Lambda_g = X_g^T.  Thread t takes rows i0 = 2 (t / 8), i0 + 1 and the
 // contraction slice k = 8 q .. 8 q + 7 (q = t % 8): it keeps those 16 entries of the step's
 // operator in registers (loaded DEPTH steps ahead, so a step never waits on memory), reads
-// rows 8 q .. 8 q + 7 of the two carried columns from LDS (skewed so the eight slices of a
-// wave hit distinct banks) and forms 2 x 2 partial sums; three DPP exchange rounds within
-// the 8 lanes of the row pair leave lanes q and q ^ 1 with X_new[i0 + q / 4][c0 + (q / 2) % 2].
-// One barrier per step.
+// rows 8 q .. 8 q + 7 of the eight carried columns from LDS (rows skewed so the eight slices
+// hit distinct banks) and forms 2 x 8 partial sums; three DPP exchange rounds within the 8
+// lanes of the row pair (halves of the columns, then quarters, then single columns) leave
+// lane q with X_new[i0][c0 + q] and X_new[i0 + 1][c0 + q].  Eight columns per workgroup:
+// each step's operator is read by 8 workgroups per pair and direction.  One barrier per step.
 __device__ __forceinline__ float dpp_mirror8(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x141, 0xF, 0xF, false));
 }
@@ -568,23 +594,22 @@ __device__ __forceinline__ float dpp_swap2(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
 }
 
+constexpr int kScanCols = 8;
+__device__ __forceinline__ int scan_row(int r) { return 8 * r + 4 * (r >> 3); }  // float offset of carried row r
+
 __global__ __launch_bounds__(256) void bwdc_scan_kernel(BwdArgs a) {
   constexpr int DEPTH = 8;
-  constexpr int HS = D + D / 8;  // carried rows with a one-row skew every 8 rows
-  __shared__ __align__(16) float2 sH[2][HS];
+  __shared__ __align__(16) float sH[2][64 * 8 + 8 * 4];
   const int tid = threadIdx.x, i0 = 2 * (tid >> 3), q = tid & 7;
-  const int pr = blockIdx.x, c0 = 2 * blockIdx.y;
+  const int pr = blockIdx.x, c0 = kScanCols * blockIdx.y;
   const bool rev = blockIdx.z == 1;
-  const int n = a.nseg;
-  const int orow = i0 + (q >> 2), ocol = c0 + ((q >> 1) & 1);  // the output this lane ends with (lanes q, q ^ 1)
+  const int n = a.ngrp;
   const size_t base = (size_t)pr * n * D * D;
-  const float* A0 = (rev ? a.seg_Phi : a.seg_Acc) + base + (size_t)i0 * D + 8 * q;
-  const float* B0 = (rev ? a.seg_ell : a.seg_B) + base + (size_t)orow * D + ocol;
-  float* O0 = (rev ? a.seg_Lam : a.seg_Sin) + base + (size_t)ocol * D + orow;
-  const bool wr = (q & 1) == 0;
-  auto hrow = [](int r) { return r + (r >> 3); };
+  const float* A0 = (rev ? a.grp_Phi : a.grp_Acc) + base + (size_t)i0 * D + 8 * q;
+  const float* B0 = (rev ? a.grp_ell : a.grp_B) + base + (size_t)i0 * D + c0 + q;
+  float* O0 = (rev ? a.grp_Lam : a.grp_Sin) + base + (size_t)(c0 + q) * D + i0;
   auto chunk_of = [&](int s) { return rev ? n - 1 - s : s; };
-#define PRISM_DECL(D_) float4 R##D_##_0, R##D_##_1, R##D_##_2, R##D_##_3; float R##D_##_b;
+#define PRISM_DECL(D_) float4 R##D_##_0, R##D_##_1, R##D_##_2, R##D_##_3; float R##D_##_b0, R##D_##_b1;
 #define PRISM_FETCH(D_, S)                                                                    \
   {                                                                                           \
     const size_t cn_ = (size_t)chunk_of((S) < n ? (S) : n - 1);                               \
@@ -593,44 +618,62 @@ __global__ __launch_bounds__(256) void bwdc_scan_kernel(BwdArgs a) {
     R##D_##_1 = src_[1];                                                                      \
     R##D_##_2 = src_[D / 4];                                                                  \
     R##D_##_3 = src_[D / 4 + 1];                                                              \
-    R##D_##_b = B0[cn_ * D * D];                                                              \
+    R##D_##_b0 = B0[cn_ * D * D];                                                             \
+    R##D_##_b1 = B0[cn_ * D * D + D];                                                         \
   }
   PRISM_DECL(0) PRISM_DECL(1) PRISM_DECL(2) PRISM_DECL(3)
   PRISM_DECL(4) PRISM_DECL(5) PRISM_DECL(6) PRISM_DECL(7)
   PRISM_FETCH(0, 0) PRISM_FETCH(1, 1) PRISM_FETCH(2, 2) PRISM_FETCH(3, 3)
   PRISM_FETCH(4, 4) PRISM_FETCH(5, 5) PRISM_FETCH(6, 6) PRISM_FETCH(7, 7)
   const float* X0 = rev ? a.dS_final : nullptr;
-  float h = X0 != nullptr ? X0[(size_t)pr * D * D + (size_t)orow * D + ocol] : 0.f;
-  if (tid < D)
-    sH[0][hrow(tid)] = X0 != nullptr ? *reinterpret_cast<const float2*>(X0 + (size_t)pr * D * D + (size_t)tid * D + c0)
-                                     : make_float2(0.f, 0.f);
+  const float* xs = X0 != nullptr ? X0 + (size_t)pr * D * D : nullptr;
+  float h0 = xs != nullptr ? xs[(size_t)i0 * D + c0 + q] : 0.f;
+  float h1 = xs != nullptr ? xs[(size_t)(i0 + 1) * D + c0 + q] : 0.f;
+  if (tid < 128) {
+    const int r = tid >> 1, hf = 4 * (tid & 1);
+    *reinterpret_cast<float4*>(&sH[0][scan_row(r) + hf]) =
+        xs != nullptr ? *reinterpret_cast<const float4*>(xs + (size_t)r * D + c0 + hf) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
   __syncthreads();
-  const bool lo4 = q < 4, lo2 = (q & 2) == 0;
+  const bool lo4 = q < 4, lo2 = (q & 2) == 0, lo1 = (q & 1) == 0;
   int cur = 0;
 #define PRISM_SCAN_STEP(D_, PREFETCH)                                                         \
   {                                                                                           \
     const int s = s0 + (D_);                                                                  \
-    if (wr) O0[(size_t)chunk_of(s) * D * D] = h;                                              \
+    *reinterpret_cast<float2*>(O0 + (size_t)chunk_of(s) * D * D) = make_float2(h0, h1);      \
     const float ar0[8] = {R##D_##_0.x, R##D_##_0.y, R##D_##_0.z, R##D_##_0.w,                 \
                           R##D_##_1.x, R##D_##_1.y, R##D_##_1.z, R##D_##_1.w};                \
     const float ar1[8] = {R##D_##_2.x, R##D_##_2.y, R##D_##_2.z, R##D_##_2.w,                 \
                           R##D_##_3.x, R##D_##_3.y, R##D_##_3.z, R##D_##_3.w};                \
-    const float bv = R##D_##_b;                                                               \
-    float v[4] = {0.f, 0.f, 0.f, 0.f}; /* [row][col] */                                       \
+    const float bv0 = R##D_##_b0, bv1 = R##D_##_b1;                                           \
+    float v0[8], v1[8]; /* rows i0, i0 + 1; columns c0 .. c0 + 7 */                          \
+    _Pragma("unroll") for (int c = 0; c < 8; ++c) { v0[c] = 0.f; v1[c] = 0.f; }              \
     _Pragma("unroll") for (int m = 0; m < 8; ++m) {                                           \
-      const float2 hv = sH[cur][hrow(8 * q + m)];                                             \
-      v[0] += ar0[m] * hv.x;                                                                  \
-      v[1] += ar0[m] * hv.y;                                                                  \
-      v[2] += ar1[m] * hv.x;                                                                  \
-      v[3] += ar1[m] * hv.y;                                                                  \
+      const float* xr = &sH[cur][scan_row(8 * q + m)];                                        \
+      const float4 xa = *reinterpret_cast<const float4*>(xr);                                 \
+      const float4 xb = *reinterpret_cast<const float4*>(xr + 4);                             \
+      const float xv[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};                   \
+      _Pragma("unroll") for (int c = 0; c < 8; ++c) {                                         \
+        v0[c] += ar0[m] * xv[c];                                                              \
+        v1[c] += ar1[m] * xv[c];                                                              \
+      }                                                                                       \
     }                                                                                         \
     if (PREFETCH) PRISM_FETCH(D_, s + DEPTH)                                                  \
-    float n2[2];                                                                              \
-    _Pragma("unroll") for (int j = 0; j < 2; ++j)                                             \
-      n2[j] = (lo4 ? v[j] : v[2 + j]) + dpp_mirror8(lo4 ? v[2 + j] : v[j]);                   \
-    const float n1 = (lo2 ? n2[0] : n2[1]) + dpp_rev4(lo2 ? n2[1] : n2[0]);                   \
-    h = n1 + dpp_swap2(n1) + bv;                                                              \
-    reinterpret_cast<float*>(&sH[cur ^ 1][hrow(orow)])[(q >> 1) & 1] = h;                     \
+    /* halves of the columns, then quarters, then single columns */                           \
+    float k0[4], k1[4];                                                                       \
+    _Pragma("unroll") for (int c = 0; c < 4; ++c) {                                           \
+      k0[c] = (lo4 ? v0[c] : v0[4 + c]) + dpp_mirror8(lo4 ? v0[4 + c] : v0[c]);              \
+      k1[c] = (lo4 ? v1[c] : v1[4 + c]) + dpp_mirror8(lo4 ? v1[4 + c] : v1[c]);              \
+    }                                                                                         \
+    float j0[2], j1[2];                                                                       \
+    _Pragma("unroll") for (int c = 0; c < 2; ++c) {                                           \
+      j0[c] = (lo2 ? k0[c] : k0[2 + c]) + dpp_rev4(lo2 ? k0[2 + c] : k0[c]);                  \
+      j1[c] = (lo2 ? k1[c] : k1[2 + c]) + dpp_rev4(lo2 ? k1[2 + c] : k1[c]);                  \
+    }                                                                                         \
+    h0 = (lo1 ? j0[0] : j0[1]) + dpp_swap2(lo1 ? j0[1] : j0[0]) + bv0;                        \
+    h1 = (lo1 ? j1[0] : j1[1]) + dpp_swap2(lo1 ? j1[1] : j1[0]) + bv1;                        \
+    sH[cur ^ 1][scan_row(i0) + q] = h0;                                                       \
+    sH[cur ^ 1][scan_row(i0 + 1) + q] = h1;                                                   \
     cur ^= 1;                                                                                 \
     __syncthreads();                                                                          \
   }
@@ -649,6 +692,126 @@ __global__ __launch_bounds__(256) void bwdc_scan_kernel(BwdArgs a) {
 #undef PRISM_SCAN_STEP
 #undef PRISM_FETCH
 #undef PRISM_DECL
+}
+
+// A float32 64 x 64 matrix (row-major) into LDS as bf16, 16 bytes per thread.
+__device__ __forceinline__ void load_f32_bf16(bf16_t* X, const float* src) {
+  const int tid = threadIdx.x, row = tid >> 3, col = 8 * (tid & 7);
+  const float4 u = *reinterpret_cast<const float4*>(src + row * D + col);
+  const float4 v = *reinterpret_cast<const float4*>(src + row * D + col + 4);
+  bf16x8 y;
+  y[0] = (bf16_t)u.x; y[1] = (bf16_t)u.y; y[2] = (bf16_t)u.z; y[3] = (bf16_t)u.w;
+  y[4] = (bf16_t)v.x; y[5] = (bf16_t)v.y; y[6] = (bf16_t)v.z; y[7] = (bf16_t)v.w;
+  *reinterpret_cast<bf16x8*>(X + row * LDM + col) = y;
+}
+
+// A row-lane tile (lane: out[row][col .. col + 3]) stored transposed into a float32 matrix.
+__device__ __forceinline__ void store_tile_t(float* dst, int row, int col, const f32x4& v) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) dst[(size_t)(col + r) * D + row] = v[r];
+}
+
+// Group operators of the two-level scan, one workgroup per group of up to kBwdGroup chunks
+// (c0 .. c0 + G - 1): with Pre_i = Acc_{c0+i-1} .. Acc_{c0} (Pre_0 = I),
+//   Acc_g = Pre_G,  HB_g = sum_i Acc_{c0+G-1} .. Acc_{c0+i+1} HB_{c0+i},  ell_g = sum_i Pre_i^T ell_{c0+i}
+// (the state after the group from a zero start, and the adjoint at its start from its own
+// outputs), formed one chunk at a time: ell_g += M^T ell_i, M <- Acc_i M, HB_g <- Acc_i HB_g +
+// HB_i.  Products on bf16 MFMA operands (the running matrices kept in float32).
+__global__ __launch_bounds__(NT) void bwdc_compose_kernel(BwdArgs a) {
+  __shared__ __align__(16) bf16_t sm[4][MB];
+  bf16_t *sA = sm[0], *sE = sm[1], *sM = sm[2], *sHg = sm[3];
+  const int w = wave_id(), l = lane_id(), i = l & 15, g = l >> 4;
+  const int mt = w >> 1, nt0 = 2 * (w & 1), row = 16 * mt + i;
+  const int grp = blockIdx.x, pr = blockIdx.y;
+  const int c0 = grp * kBwdGroup, G = min(kBwdGroup, a.nseg - c0);
+  f32x4 M[2], Hg[2], Eg[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int col = 16 * (nt0 + h) + 4 * g;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) M[h][r] = col + r == row ? 1.f : 0.f;
+    Hg[h] = zero4();
+    Eg[h] = zero4();
+  }
+  for (int it = 0; it < G; ++it) {
+    const size_t so = ((size_t)pr * a.nseg + c0 + it) * D * D;
+    load_f32_bf16(sA, a.seg_Acc + so);
+    load_f32_bf16(sE, a.seg_ell + so);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int col = 16 * (nt0 + h) + 4 * g;
+      put_bf16(sM, row, col, M[h]);
+      put_bf16(sHg, row, col, Hg[h]);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int n0 = 16 * (nt0 + h), col = n0 + 4 * g;
+      Eg[h] = mm<true, true>(Eg[h], sM, sE, 16 * mt, n0);
+      M[h] = mm<false, true>(zero4(), sA, sM, 16 * mt, n0);
+      const f32x4 hb = *reinterpret_cast<const f32x4*>(a.seg_B + so + (size_t)row * D + col);
+      Hg[h] = mm<false, true>(hb, sA, sHg, 16 * mt, n0);
+    }
+    __syncthreads();
+  }
+  const size_t go = ((size_t)pr * a.ngrp + grp) * D * D;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int col = 16 * (nt0 + h) + 4 * g;
+    *reinterpret_cast<f32x4*>(a.grp_Acc + go + (size_t)row * D + col) = M[h];
+    store_tile_t(a.grp_Phi + go, row, col, M[h]);
+    *reinterpret_cast<f32x4*>(a.grp_B + go + (size_t)row * D + col) = Hg[h];
+    *reinterpret_cast<f32x4*>(a.grp_ell + go + (size_t)row * D + col) = Eg[h];
+  }
+}
+
+// Each chunk's entering state and arriving adjoint from its group's (S layout): forwards
+// (blockIdx.z = 0) X_{c0} = X_g, X_{c+1} = Acc_c X_c + HB_c; backwards (blockIdx.z = 1)
+// Y_{c0+G-1} = Y_g, Y_{c-1} = Acc_c^T Y_c + ell_c.  The carried matrix is the B operand of
+// the next product in its S layout (B(k, n) = X[k][n] = S[n][k]); bf16 operands, float32 sums.
+__global__ __launch_bounds__(NT) void bwdc_expand_kernel(BwdArgs a) {
+  __shared__ __align__(16) bf16_t sm[2][MB];
+  bf16_t *sA = sm[0], *sS = sm[1];
+  const int tid = threadIdx.x, w = wave_id(), l = lane_id(), i = l & 15, g = l >> 4;
+  const int mt = w >> 1, nt0 = 2 * (w & 1), row = 16 * mt + i;
+  const int grp = blockIdx.x, pr = blockIdx.y;
+  const bool rev = blockIdx.z == 1;
+  const int c0 = grp * kBwdGroup, G = min(kBwdGroup, a.nseg - c0);
+  const size_t go = ((size_t)pr * a.ngrp + grp) * D * D;
+  const float* xg = (rev ? a.grp_Lam : a.grp_Sin) + go;
+  float* outb = rev ? a.seg_Lam : a.seg_Sin;
+  // the group's own entry: copied (float32, S layout) and staged for the first product
+  {
+    const int c = rev ? c0 + G - 1 : c0;
+    float* dst = outb + ((size_t)pr * a.nseg + c) * D * D;
+    const int r = tid >> 3, c8 = 8 * (tid & 7);
+    *reinterpret_cast<float4*>(dst + r * D + c8) = *reinterpret_cast<const float4*>(xg + r * D + c8);
+    *reinterpret_cast<float4*>(dst + r * D + c8 + 4) = *reinterpret_cast<const float4*>(xg + r * D + c8 + 4);
+    load_f32_bf16(sS, xg);
+  }
+  for (int it = 1; it < G; ++it) {
+    const int cs = rev ? c0 + G - it : c0 + it - 1;   // the chunk whose operator applies
+    const int cd = rev ? cs - 1 : cs + 1;             // the chunk that receives the result
+    const size_t so = ((size_t)pr * a.nseg + cs) * D * D;
+    load_f32_bf16(sA, a.seg_Acc + so);
+    __syncthreads();
+    f32x4 x[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int n0 = 16 * (nt0 + h), col = n0 + 4 * g;
+      const f32x4 add = *reinterpret_cast<const f32x4*>((rev ? a.seg_ell : a.seg_B) + so + (size_t)row * D + col);
+      x[h] = rev ? mm<true, false>(add, sA, sS, 16 * mt, n0) : mm<false, false>(add, sA, sS, 16 * mt, n0);
+    }
+    __syncthreads();
+    float* dst = outb + ((size_t)pr * a.nseg + cd) * D * D;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int col = 16 * (nt0 + h) + 4 * g;
+      store_tile_t(dst, row, col, x[h]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sS[(col + r) * LDM + row] = (bf16_t)x[h][r];
+    }
+  }
 }
 
 // Every gradient of chunk (blockIdx.x, pair blockIdx.y) from its start state (seg_Sin) and
@@ -678,12 +841,31 @@ __global__ __launch_bounds__(NT) void bwdc_grad_kernel(BwdArgs a) {
     if (l == 0) tk[kMisc + w] = gc;
   }
   load_state(x.m(mLam), a.seg_Lam + so, nullptr);
+  // T, Uc, Wc (LDS) and V' (this lane's tiles) as the chunk's local pass formed them
+  const bf16_t* cm = static_cast<const bf16_t*>(a.chunk_mats) + ((size_t)x.pr * a.nseg + x.c) * 4 * 4096;
+  load_rows(x.m(mT), cm, 64, 64);
+  load_rows(x.m(mUc), cm + 4096, 64, 64);
+  load_rows(x.m(mWc), cm + 8192, 64, 64);
+  f32x4 vp[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const bf16x4 y = *reinterpret_cast<const bf16x4*>(cm + 12288 + row * 64 + 16 * (nt0 + h) + 4 * g);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) vp[h][q] = (float)y[q];
+  }
   ChainLane cl;
-  if (x.L > 1) chain_start(x, cl);
+  bf16_t* sVx = reinterpret_cast<bf16_t*>(lds + Lds::oVx);  // value rows t0 - 3 .. t0 + 63
+  if (x.L > 1) {
+    chain_start(x, cl);
+    const bf16_t* vg = static_cast<const bf16_t*>(a.v) + (size_t)x.pr * a.T * D;
+    for (int e = tid; e < 67 * 8; e += NT) {
+      const int r = e >> 3, c8 = 8 * (e & 7), tv = x.t0 - 3 + r;
+      uint4 y = {0u, 0u, 0u, 0u};
+      if (tv >= 0 && tv < a.T) y = *reinterpret_cast<const uint4*>(vg + (size_t)tv * D + c8);
+      *reinterpret_cast<uint4*>(sVx + r * 64 + c8) = y;
+    }
+  }
   __syncthreads();
-  Fwd f;
-  f32x4 hb_unused[2];
-  chunk_forward<false>(x, cl, f, hb_unused);
   bf16_t *sQ = x.m(mQ), *sK = x.m(mK), *sdO = x.m(mdO), *sT = x.m(mT), *sU = x.m(mU), *sR = x.m(mR);
   bf16_t *sS = x.m(mS), *sLam = x.m(mLam), *sUc = x.m(mUc), *sWc = x.m(mWc);
   bf16_t *sE = x.m(mX1), *sP = x.m(mX2), *sZ = x.m(mN), *sdE = x.m(m13), *sdVp = x.m(m14), *sdWc = x.m(m15);
@@ -697,8 +879,9 @@ __global__ __launch_bounds__(NT) void bwdc_grad_kernel(BwdArgs a) {
   for (int h = 0; h < 2; ++h) {
     const int n0 = 16 * (nt0 + h), col = n0 + 4 * g;
     f32x4 e = mm<false, false>(zero4(), sWc, sS, 16 * mt, n0);
+    const f32x4 ucv = get_bf16(sUc, row, col);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) e[r] = f.uc[h][r] - e[r];
+    for (int r = 0; r < 4; ++r) e[r] = ucv[r] - e[r];
     put_bf16(sE, row, col, e);
     p[h] = mm<false, false>(zero4(), sQ, sK, 16 * mt, n0);
     const f32x4 gm = gam_tile(tk, row, col);
@@ -756,7 +939,7 @@ __global__ __launch_bounds__(NT) void bwdc_grad_kernel(BwdArgs a) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       dvp[r] = beta_i * dx1[r];
-      rb_beta += f.vp[h][r] * dx1[r];
+      rb_beta += vp[h][r] * dx1[r];
     }
     put_bf16(sdVp, row, col, dvp);
     if (in_i) *reinterpret_cast<f32x4*>(dvg + col) = dvp;
@@ -829,7 +1012,7 @@ __global__ __launch_bounds__(NT) void bwdc_grad_kernel(BwdArgs a) {
     load_rows(sU, static_cast<const bf16_t*>(a.u) + (((size_t)x.pr * a.T + x.t0) * (x.L - 1) + lv - 1) * D,
               (size_t)(x.L - 1) * D, x.nt);
     // r_{l-1} and r_l of the thread's channels
-    float rp[8], rl[8], fl[8];
+    float rp[8], rl[8], fl[8], gmv[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) rp[e] = cl.r0[e];
     for (int m = 0; m < lv - 1; ++m) {
@@ -838,7 +1021,7 @@ __global__ __launch_bounds__(NT) void bwdc_grad_kernel(BwdArgs a) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) rp[e] *= fm[e];
     }
-    chain_factor(x, cl, lv - 1, fl);
+    chain_factor(x, cl, lv - 1, fl, gmv);
 #pragma unroll
     for (int e = 0; e < 8; ++e) rl[e] = rp[e] * fl[e];
     put_written(x, cl, sR, lv, rl);
@@ -867,6 +1050,7 @@ __global__ __launch_bounds__(NT) void bwdc_grad_kernel(BwdArgs a) {
       put_bf16(sPU, row, col, pu);
       put_bf16(sZpu, row, col, zpu);
       put_bf16(sZn, row, col, zn);
+      __builtin_amdgcn_sched_barrier(0);
     }
     __syncthreads();
     float* dug = a.du + (grow * (x.L - 1) + lv - 1) * D;
@@ -891,6 +1075,7 @@ __global__ __launch_bounds__(NT) void bwdc_grad_kernel(BwdArgs a) {
       if (in_i) *reinterpret_cast<f32x4*>(dug + col) = du;
       dq[h] = mm<false, true>(dq[h], sZpu, sU, 16 * mt, n0);
       dk[h] = mm<false, true>(dk[h], sZn, sU, 16 * mt, n0);
+      __builtin_amdgcn_sched_barrier(0);  // one tile's temporaries at a time (register budget)
     }
     __syncthreads();
     // the chain's adjoint for slot lv
@@ -900,8 +1085,6 @@ __global__ __launch_bounds__(NT) void bwdc_grad_kernel(BwdArgs a) {
       const float dR[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
       const float al = tk[kAl + lv * 64 + cl.t], alm = tk[kAl + (lv - 1) * 64 + cl.t];
       float s = 0.f, s2 = 0.f;
-      float gmv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      if (in_t) load_bf16x8(gmv, static_cast<const bf16_t*>(a.gamma) + (tg * (x.L - 1) + lv - 1) * D + cl.ch0);
       float dgm[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -921,16 +1104,13 @@ __global__ __launch_bounds__(NT) void bwdc_grad_kernel(BwdArgs a) {
       }
     }
   }
-  // dq, dk
-  float* dqg = a.dq + grow * D;
-  float* dkg = a.dk + grow * D;
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int col = 16 * (nt0 + h) + 4 * g;
-    if (in_i) {
-      *reinterpret_cast<f32x4*>(dqg + col) = dq[h];
-      *reinterpret_cast<f32x4*>(dkg + col) = dk[h];
-    }
+  // the direct part of dv (stored by this workgroup in B2), for the anchor terms at the end
+  float dvd[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (in_t) {
+    const float4 d0 = *reinterpret_cast<const float4*>(a.dv + tg * D + cl.ch0);
+    const float4 d1 = *reinterpret_cast<const float4*>(a.dv + tg * D + cl.ch0 + 4);
+    dvd[0] = d0.x; dvd[1] = d0.y; dvd[2] = d0.z; dvd[3] = d0.w;
+    dvd[4] = d1.x; dvd[5] = d1.y; dvd[6] = d1.z; dvd[7] = d1.w;
   }
   // row partials of this lane's row over the wave's 32 columns; column sums of dlG
   {
@@ -955,29 +1135,28 @@ __global__ __launch_bounds__(NT) void bwdc_grad_kernel(BwdArgs a) {
         if (i == 0) tk[kColLg + mt * 64 + 16 * (nt0 + h) + 4 * g + r] = cs;
       }
   }
-  float dvd[8];
-  bf16_t* sVx = x.m(mQ);  // value rows t0 - 3 .. t0 + 63 (67 rows: slot Q and the start of K's)
+  float* sW = x.mf(mT);  // the head's conv taps [4][64] (slot T is free after the rank loop)
   if (x.L > 1) {
-    // d r_0 of the chain, then the anchor's terms: this thread's direct dv, the value rows
+    // d r_0 of the chain, for the anchor's terms
 #pragma unroll
     for (int e = 0; e < 8; e += 4)
       *reinterpret_cast<float4*>(sdR + cl.t * LDF + cl.ch0 + e) = make_float4(dr[e], dr[e + 1], dr[e + 2], dr[e + 3]);
     if ((tid & 7) == 0 && in_t) a.dalpha[tg * x.L] = da_carry;
-    if (in_t) {
-      const float4 d0 = *reinterpret_cast<const float4*>(a.dv + tg * D + cl.ch0);
-      const float4 d1 = *reinterpret_cast<const float4*>(a.dv + tg * D + cl.ch0 + 4);
-      dvd[0] = d0.x; dvd[1] = d0.y; dvd[2] = d0.z; dvd[3] = d0.w;
-      dvd[4] = d1.x; dvd[5] = d1.y; dvd[6] = d1.z; dvd[7] = d1.w;
-    }
-    const bf16_t* vg = static_cast<const bf16_t*>(a.v) + (size_t)x.pr * a.T * D;
-    for (int e = tid; e < 67 * 8; e += NT) {
-      const int r = e >> 3, c8 = 8 * (e & 7), tv = x.t0 - 3 + r;
-      uint4 y = {0u, 0u, 0u, 0u};
-      if (tv >= 0 && tv < a.T) y = *reinterpret_cast<const uint4*>(vg + (size_t)tv * D + c8);
-      *reinterpret_cast<uint4*>(sVx + r * LDM + c8) = y;
-    }
+    if (tid < 4 * D) sW[tid] = a.conv_w[(size_t)(x.pr % a.H) * 4 * D + tid];
   }
   __syncthreads();
+  {
+    float* dqg = a.dq + grow * D;
+    float* dkg = a.dk + grow * D;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int col = 16 * (nt0 + h) + 4 * g;
+      if (in_i) {
+        *reinterpret_cast<f32x4*>(dqg + col) = dq[h];
+        *reinterpret_cast<f32x4*>(dkg + col) = dk[h];
+      }
+    }
+  }
   if (tid < 64) {
     // db, then d log g = reverse cumsum, dg = d log g / g; dbeta (wave 0, one token per lane)
     const int t = tid;
@@ -1010,7 +1189,7 @@ __global__ __launch_bounds__(NT) void bwdc_grad_kernel(BwdArgs a) {
   }
   if (x.L > 1) {
     const size_t ps = (size_t)x.pr * a.nseg + x.c;
-    const float* w = a.conv_w + (size_t)(x.pr % a.H) * 4 * D;
+    const float* w = sW;
     // dv += d r_0 - sum_j w_j d r_0(t + 3 - j) over the chunk's anchors that read v_t
     if (in_t) {
       float out[8];
@@ -1037,10 +1216,12 @@ __global__ __launch_bounds__(NT) void bwdc_grad_kernel(BwdArgs a) {
       a.carry[(ps * 3 + jj) * D + ch] = s;
     } else if (tid >= 256) {
       // dconv_w share: dw_j = -sum_t d r_0(t) v_{t-3+j}
+      // four independent partial sums (tokens t = 4 m + q), added in a fixed order
       const int j = (tid - 256) / D, ch = (tid - 256) % D;
-      float s = 0.f;
-      for (int t = 0; t < x.nt; ++t) s -= sdR[t * LDF + ch] * (float)sVx[(t + j) * LDM + ch];
-      a.dconv_part[(ps * 4 + j) * D + ch] = s;
+      float s4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+      for (int t = 0; t < C; ++t) s4[t & 3] -= sdR[t * LDF + ch] * (float)sVx[(t + j) * 64 + ch];
+      a.dconv_part[(ps * 4 + j) * D + ch] = (s4[0] + s4[1]) + (s4[2] + s4[3]);
     }
   }
 }
