@@ -10,8 +10,9 @@ the launch stream around each kernel (the dominant kernel's duration, hence its
 achieved HBM bandwidth against the 8 TB/s peak).  Prints one JSON line, with the
 float64 oracle timed on the host cores on a bounded sample.
 
-    python bench.py --bwd [--workload NAME] [--steps K]
-times the backward pass (prism_bwd) instead and prints its own JSON line.
+    python bench.py --bwd [--workload NAME] [--steps K] [--bwd-form auto|chunked|float32]
+times the backward pass instead (the chunked MFMA form where it applies, else prism_bwd)
+and prints its own JSON line.
 
     python bench.py --nl [--workload NAME] [--steps K]
 times the forward with the nonlinear refinement (prism_fwd_nl) and its factor kernel.
@@ -381,8 +382,9 @@ def decode_bench(steps, warmup, batch):
                       "frac": step_bytes / dt / 1e9 / HBM_PEAK_GBS}), flush=True)
 
 
-def bwd_bench(steps, warmup, workload_name, cpu=True):
-    """The backward (prism_bwd) on one workload: whole calls timed with HIP events on the
+def bwd_bench(steps, warmup, workload_name, cpu=True, form="auto"):
+    """The backward on one workload (form: "chunked" prism_bwd_chunked, "float32" prism_bwd,
+    "auto" the chunked form where it applies): whole calls timed with HIP events on the
     launch stream.  One JSON line: tokens/s and the call's algorithmic bytes (inputs and
     d_o read once, every gradient written once in float32) against the HBM peak, beside
     the float64 gradient oracle timed on a bounded sample (one pair, 512 tokens)."""
@@ -407,18 +409,25 @@ def bwd_bench(steps, warmup, workload_name, cpu=True):
         dt_cpu = time.perf_counter() - t0
         cpu_out = {"value": Ts / dt_cpu, "unit": "tokens/s (per head)", "cores": torch.get_num_threads(),
                    "kind": "oracle", "sample": f"one (b, h) pair, {Ts} tokens, float64 autograd, {dt_cpu:.1f} s"}
-    res = time_bwd(w, x, d_o, steps, warmup)
-    print(json.dumps({"metric": "bwd tokens/sec (prism_bwd)", "workload": w.name, "dtype": w.dtype,
+    chunked = form == "chunked" or (form == "auto" and bwd_chunked_supported(w))
+    res = time_bwd(w, x, d_o, steps, warmup, chunked=chunked)
+    name = "prism_bwd_chunked" if chunked else "prism_bwd"
+    print(json.dumps({"metric": f"bwd tokens/sec ({name})", "workload": w.name, "dtype": w.dtype,
                       "config": {"B": w.B, "H": w.H, "T": w.T, "dk": w.dk, "dv": w.dv, "L": w.L},
                       "steps": steps, "warmup": warmup, "ms_per_step": res["ms_per_step"],
                       "tokens_per_s": res["tokens_per_s"], "roofline": res["roofline"],
                       "cpu_baseline": cpu_out}), flush=True)
 
 
-def time_bwd(w, x, d_o, steps, warmup):
-    """prism_bwd on workload w (inputs x, output gradient d_o): whole calls timed with HIP
-    events on the launch stream; returns ms per call, tokens/s and the HBM roofline of the
-    call's algorithmic bytes."""
+def bwd_chunked_supported(w):
+    """prism_bwd_chunked covers bfloat16 inputs at dk = dv = 64."""
+    return w.dtype == "bf16" and w.dk == 64 and w.dv == 64
+
+
+def time_bwd(w, x, d_o, steps, warmup, chunked=False):
+    """prism_bwd (or, chunked, prism_bwd_chunked) on workload w (inputs x, output gradient
+    d_o): whole calls timed with HIP events on the launch stream; returns ms per call,
+    tokens/s and the HBM roofline of the call's algorithmic bytes."""
     import torch
     import delta_rule_sequence_amd as prism
     import workloads
@@ -427,11 +436,12 @@ def time_bwd(w, x, d_o, steps, warmup):
     do_t = torch.tensor(d_o, device="cuda").to(vt)
     args = (dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], dev["u"], dev["alpha"], dev["gamma"],
             dev["conv_w"])
-    need = prism.load_library().prism_bwd_workspace_bytes(w.B, w.H, w.T, w.dk, w.dv, w.L,
-                                                          prism.PRISM_BF16 if w.dtype == "bf16" else prism.PRISM_F32)
+    lib = prism.load_library()
+    sizer = lib.prism_bwd_chunked_workspace_bytes if chunked else lib.prism_bwd_workspace_bytes
+    need = sizer(w.B, w.H, w.T, w.dk, w.dv, w.L, prism.PRISM_BF16 if w.dtype == "bf16" else prism.PRISM_F32)
     ws = torch.empty(need, dtype=torch.uint8, device="cuda")
     for _ in range(warmup):
-        prism.bwd(*args, L=w.L, d_o=do_t, workspace=ws)
+        prism.bwd(*args, L=w.L, d_o=do_t, workspace=ws, chunked=chunked)
     torch.cuda.synchronize()
     hip = Hip()
     ev = hip.events(2)
@@ -440,7 +450,7 @@ def time_bwd(w, x, d_o, steps, warmup):
     rec.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
     rec(ev[0], ctypes.c_void_p(stream.cuda_stream))
     for _ in range(steps):
-        prism.bwd(*args, L=w.L, d_o=do_t, workspace=ws)
+        prism.bwd(*args, L=w.L, d_o=do_t, workspace=ws, chunked=chunked)
     rec(ev[1], ctypes.c_void_p(stream.cuda_stream))
     torch.cuda.synchronize()
     ms = hip.elapsed_ms(ev[0], ev[1]) / steps
@@ -455,7 +465,10 @@ def time_bwd(w, x, d_o, steps, warmup):
             "roofline": {"bound": "hbm", "bytes_per_token_head": per_th, "bytes_per_call": total,
                          "achieved": total / (ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": total / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                         "scope": "whole prism_bwd call (segment-parallel: local pass, scans, token steps, sums)"}}
+                         "scope": ("whole prism_bwd_chunked call (chunk operators, compose, group scans, "
+                                   "expand, chunk gradients, sums)" if chunked else
+                                   "whole prism_bwd call (segment-parallel: local pass, scans, token steps, sums)")},
+            "form": "prism_bwd_chunked (bf16 MFMA)" if chunked else "prism_bwd (float32)"}
 
 
 def time_nl(w, steps, warmup, x0=None):
@@ -556,7 +569,10 @@ def main():
     ap.add_argument("--decode", type=int, default=0, metavar="BATCH",
                     help="time one-token decode steps for BATCH sequences instead")
     ap.add_argument("--bwd", action="store_true",
-                    help="time the backward (prism_bwd) on --workload instead")
+                    help="time the backward on --workload instead")
+    ap.add_argument("--bwd-form", default="auto", choices=["auto", "chunked", "float32"],
+                    help="--bwd: prism_bwd_chunked (bf16 MFMA, dk = dv = 64), prism_bwd (float32), or "
+                         "auto (the chunked form where it applies)")
     ap.add_argument("--nl", action="store_true",
                     help="time the nonlinear-refinement forward (prism_fwd_nl) on --workload instead")
     ap.add_argument("--forward-only", action="store_true",
@@ -579,7 +595,7 @@ def main():
         decode_bench(args.steps, args.warmup, args.decode)
         return
     if args.bwd:
-        bwd_bench(args.steps, args.warmup, args.workload, cpu=not args.no_cpu_baseline)
+        bwd_bench(args.steps, args.warmup, args.workload, cpu=not args.no_cpu_baseline, form=args.bwd_form)
         return
     if args.nl:
         import workloads
@@ -665,7 +681,11 @@ def main():
     d_o = np.random.default_rng(w.seed + 7).standard_normal((w.B, w.H, w.T, w.dv)).astype(np.float32)
     if w.dtype == "bf16":
         d_o = workloads.to_bf16_values(d_o)
-    out["bwd"] = dict(time_bwd(w, x0, d_o, 2, 1), steps=2, warmup=1)
+    if bwd_chunked_supported(w):
+        out["bwd"] = dict(time_bwd(w, x0, d_o, 5, 2, chunked=True), steps=5, warmup=2)
+        out["bwd_float32"] = dict(time_bwd(w, x0, d_o, 2, 1), steps=2, warmup=1)
+    else:
+        out["bwd"] = dict(time_bwd(w, x0, d_o, 2, 1), steps=2, warmup=1)
     # the nonlinear-refinement forward on the same shape (its own gains), reported beside it
     out["nl"] = time_nl(w, 10, 2, x0)
     out["roofline"]["measured_copy"] = copy_bandwidth(torch)

@@ -430,9 +430,10 @@ namespace {
 
 // Workspace of the chunked backward: per 64-token chunk six float32 64 x 64 matrices
 // (operator and its transpose, end state from zero, local adjoint, entering state,
-// arriving adjoint), its anchor carry [3][64] and dconv_w share [4][64], and four bf16
-// 64 x 64 matrices (T, Uc, Wc, V') that the local pass hands to the gradient pass; per
-// group of four chunks the same six float32 matrices for the two-level scan.
+// arriving adjoint), its anchor carry [3][64] and dconv_w share [4][64], and 3 + L bf16
+// 64 x 64 matrices (T, Uc, Wc, V' and the chain residuals r_0 .. r_{L-2}) that the local
+// pass hands to the gradient pass; per group of four chunks the same six float32 matrices
+// for the two-level scan.
 struct BwdChunkPlan {
   int P, nch, ngrp;
   size_t off_seg, off_carry, off_part, off_mats, off_grp, total;
@@ -449,7 +450,7 @@ prism_status make_bwd_chunk_plan(int B, int H, int T, int dk, int dv, int L, pri
   const size_t nch = ((size_t)T + 63) / 64;
   if (!mul_ok(P, nch, &nseg_all) || nseg_all > (size_t)INT32_MAX) return PRISM_ERR_INVALID_ARG;
   if (!mul_ok(nseg_all, (size_t)6 * 64 * 64 * 4, &sz_seg) || !mul_ok(nseg_all, (size_t)3 * 64 * 4, &sz_carry) ||
-      !mul_ok(nseg_all, (size_t)4 * 64 * 4, &sz_part) || !mul_ok(nseg_all, (size_t)4 * 64 * 64 * 2, &sz_mats))
+      !mul_ok(nseg_all, (size_t)4 * 64 * 4, &sz_part) || !mul_ok(nseg_all, (size_t)(3 + L) * 64 * 64 * 2, &sz_mats))
     return PRISM_ERR_INVALID_ARG;
   const size_t ngrp = (nch + prism::kBwdGroup - 1) / prism::kBwdGroup;
   if (!mul_ok(P * ngrp, (size_t)6 * 64 * 64 * 4, &sz_grp)) return PRISM_ERR_INVALID_ARG;

@@ -418,41 +418,64 @@ __device__ __forceinline__ void chunk_forward(const Chunk& x, ChainLane& cl, Fwd
       for (int r = 0; r < 4; ++r) f.vp[h][r] = (float)y[r];
     }
   }
-  // F3: rank slots, ascending
+  // F3: rank slots, ascending.  U_l and R_l alternate between two LDS slots, so the next
+  // slot's rows are written while the current slot's last product runs (two barriers per
+  // slot); its u rows and gamma are loaded from memory one slot ahead.  r_{l-1} goes to the
+  // chunk's matrices (bf16) for the gradient pass.
+  bf16_t* sUb[2] = {sU, x.m(m13)};
+  bf16_t* sRb[2] = {sR, x.m(m14)};
+  const int tid = threadIdx.x, trow = tid >> 3, tc8 = 8 * (tid & 7);
+  const bool tin = trow < x.nt;
+  const bf16_t* ug = static_cast<const bf16_t*>(a.u) + ((size_t)x.pr * a.T + x.t0) * (x.L - 1) * D;
+  const bf16_t* gg = static_cast<const bf16_t*>(a.gamma) + ((size_t)x.pr * a.T + x.t0) * (x.L - 1) * D;
+  bf16_t* rout = static_cast<bf16_t*>(a.chunk_mats) + ((size_t)x.pr * a.nseg + x.c) * (4 + x.L - 1) * 4096 +
+                 4 * 4096;
+  uint4 pu = {0u, 0u, 0u, 0u}, pg = {0u, 0u, 0u, 0u};
+  if (x.L > 1 && tin) {
+    pu = *reinterpret_cast<const uint4*>(ug + (size_t)trow * (x.L - 1) * D + tc8);
+    pg = *reinterpret_cast<const uint4*>(gg + (size_t)trow * (x.L - 1) * D + tc8);
+  }
   float rc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) rc[e] = cl.r0[e];
 #pragma unroll
   for (int lv = 1; lv < x.L; ++lv) {
-    // (the previous slot's products are done: barrier at the loop end, or the one above)
-    load_rows(sU, static_cast<const bf16_t*>(a.u) + (((size_t)x.pr * a.T + x.t0) * (x.L - 1) + lv - 1) * D,
-              (size_t)(x.L - 1) * D, x.nt);
+    const int b = (lv - 1) & 1;
     {
-      float fct[8];
-      chain_factor(x, cl, lv - 1, fct);
+      // slot lv: u rows, r_{lv-1} handed on, r_lv = r_{lv-1} (1 - alpha_{lv-1} gamma_{lv-1}), R_lv
+      *reinterpret_cast<uint4*>(sUb[b] + trow * LDM + tc8) = pu;
+      bf16x8 rb;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) rc[e] *= fct[e];
-      put_written(x, cl, sR, lv, rc);
+      for (int e = 0; e < 8; ++e) rb[e] = (bf16_t)rc[e];
+      *reinterpret_cast<bf16x8*>(rout + (size_t)(lv - 1) * 4096 + trow * 64 + tc8) = rb;
+      const bf16x8 gv = __builtin_bit_cast(bf16x8, pg);
+      const float al = tk[kAl + (lv - 1) * 64 + trow];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) rc[e] *= 1.f - al * (float)gv[e];
+      put_written(x, cl, sRb[b], lv, rc);
     }
     __syncthreads();
+    if (lv + 1 < x.L && tin) {
+      pu = *reinterpret_cast<const uint4*>(ug + (size_t)trow * (x.L - 1) * D + (size_t)lv * D + tc8);
+      pg = *reinterpret_cast<const uint4*>(gg + (size_t)trow * (x.L - 1) * D + (size_t)lv * D + tc8);
+    }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int n0 = 16 * (nt0 + h), col = n0 + 4 * g;
-      f32x4 nr = mm<false, false>(zero4(), sK, sU, 16 * mt, n0);
+      f32x4 nr = mm<false, false>(zero4(), sK, sUb[b], 16 * mt, n0);
       const f32x4 gm = gam_tile(tk, row, col);
 #pragma unroll
       for (int r = 0; r < 4; ++r) nr[r] = col + r < row ? gm[r] * nr[r] : 0.f;
       put_bf16(sN, row, col, nr);
-      if constexpr (HB) hb[h] = mm<true, true>(hb[h], sU, sR, 16 * mt, n0, tk + kDd);
+      if constexpr (HB) hb[h] = mm<true, true>(hb[h], sUb[b], sRb[b], 16 * mt, n0, tk + kDd);
     }
     __syncthreads();
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const f32x4 t = mm<false, true>(zero4(), sN, sR, 16 * mt, 16 * (nt0 + h));
+      const f32x4 t = mm<false, true>(zero4(), sN, sRb[b], 16 * mt, 16 * (nt0 + h));
 #pragma unroll
       for (int r = 0; r < 4; ++r) f.vp[h][r] -= t[r];
     }
-    __syncthreads();
   }
   // F4: X1 = diag(beta) V', X2 = diag(beta G) K; Uc = T X1, Wc = T X2
 #pragma unroll
@@ -516,7 +539,7 @@ __global__ __launch_bounds__(NT) void bwdc_local_kernel(BwdArgs a) {
   bf16_t *sP = x.m(mX1), *sQt = x.m(mX2);
   {
     // T, Uc, Wc and V' for the gradient pass (bf16, row-major 64 x 64 each)
-    bf16_t* cm = static_cast<bf16_t*>(a.chunk_mats) + ((size_t)x.pr * a.nseg + x.c) * 4 * 4096;
+    bf16_t* cm = static_cast<bf16_t*>(a.chunk_mats) + ((size_t)x.pr * a.nseg + x.c) * (4 + x.L - 1) * 4096;
     const int tid = threadIdx.x, r = tid >> 3, c8 = 8 * (tid & 7);
     *reinterpret_cast<uint4*>(cm + r * 64 + c8) = *reinterpret_cast<const uint4*>(x.m(mT) + r * LDM + c8);
     *reinterpret_cast<uint4*>(cm + 4096 + r * 64 + c8) = *reinterpret_cast<const uint4*>(sUc + r * LDM + c8);
@@ -842,7 +865,7 @@ __global__ __launch_bounds__(NT) void bwdc_grad_kernel(BwdArgs a) {
   }
   load_state(x.m(mLam), a.seg_Lam + so, nullptr);
   // T, Uc, Wc (LDS) and V' (this lane's tiles) as the chunk's local pass formed them
-  const bf16_t* cm = static_cast<const bf16_t*>(a.chunk_mats) + ((size_t)x.pr * a.nseg + x.c) * 4 * 4096;
+  const bf16_t* cm = static_cast<const bf16_t*>(a.chunk_mats) + ((size_t)x.pr * a.nseg + x.c) * (4 + x.L - 1) * 4096;
   load_rows(x.m(mT), cm, 64, 64);
   load_rows(x.m(mUc), cm + 4096, 64, 64);
   load_rows(x.m(mWc), cm + 8192, 64, 64);
@@ -853,10 +876,8 @@ __global__ __launch_bounds__(NT) void bwdc_grad_kernel(BwdArgs a) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) vp[h][q] = (float)y[q];
   }
-  ChainLane cl;
   bf16_t* sVx = reinterpret_cast<bf16_t*>(lds + Lds::oVx);  // value rows t0 - 3 .. t0 + 63
   if (x.L > 1) {
-    chain_start(x, cl);
     const bf16_t* vg = static_cast<const bf16_t*>(a.v) + (size_t)x.pr * a.T * D;
     for (int e = tid; e < 67 * 8; e += NT) {
       const int r = e >> 3, c8 = 8 * (e & 7), tv = x.t0 - 3 + r;
@@ -1005,27 +1026,43 @@ __global__ __launch_bounds__(NT) void bwdc_grad_kernel(BwdArgs a) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) dr[e] = 0.f;
   float da_carry = 0.f;
-  const bool in_t = x.L > 1 && cl.t < x.nt;
-  const size_t tg = (size_t)x.pr * a.T + x.t0 + (x.L > 1 ? cl.t : 0);
+  // thread (ct, 8 channels cc ..) of the chain: u rows, r_{l-1} (as the local pass formed it)
+  // and gamma_{l-1} of the next slot are loaded one slot ahead
+  const int ct = tid >> 3, cc = 8 * (tid & 7);
+  const bool in_t = x.L > 1 && ct < x.nt;
+  const size_t tg = (size_t)x.pr * a.T + x.t0 + ct;
+  const bf16_t* ug = static_cast<const bf16_t*>(a.u) + ((size_t)x.pr * a.T + x.t0) * (x.L - 1) * D;
+  const bf16_t* gg = static_cast<const bf16_t*>(a.gamma) + ((size_t)x.pr * a.T + x.t0) * (x.L - 1) * D;
+  const bf16_t* rin = cm + 4 * 4096;
+  uint4 pu = {0u, 0u, 0u, 0u}, pr_ = {0u, 0u, 0u, 0u}, pg = {0u, 0u, 0u, 0u};
+  if (x.L > 1) {
+    if (in_t) {
+      pu = *reinterpret_cast<const uint4*>(ug + (size_t)ct * (x.L - 1) * D + (size_t)(x.L - 2) * D + cc);
+      pg = *reinterpret_cast<const uint4*>(gg + (size_t)ct * (x.L - 1) * D + (size_t)(x.L - 2) * D + cc);
+    }
+    pr_ = *reinterpret_cast<const uint4*>(rin + (size_t)(x.L - 2) * 4096 + ct * 64 + cc);
+  }
 #pragma unroll 1
   for (int lv = x.L - 1; lv >= 1; --lv) {
-    load_rows(sU, static_cast<const bf16_t*>(a.u) + (((size_t)x.pr * a.T + x.t0) * (x.L - 1) + lv - 1) * D,
-              (size_t)(x.L - 1) * D, x.nt);
-    // r_{l-1} and r_l of the thread's channels
-    float rp[8], rl[8], fl[8], gmv[8];
+    // slot lv: U_lv, R_lv = alpha_lv r_lv with r_lv = r_{lv-1} (1 - alpha_{lv-1} gamma_{lv-1})
+    *reinterpret_cast<uint4*>(sU + ct * LDM + cc) = pu;
+    const uint4 cr = pr_, cgv = pg;  // this slot's r_{lv-1} and gamma_{lv-1}, kept packed
+    {
+      const bf16x8 rv = __builtin_bit_cast(bf16x8, cr), gv = __builtin_bit_cast(bf16x8, cgv);
+      const float alm = tk[kAl + (lv - 1) * 64 + ct], al = tk[kAl + lv * 64 + ct];
+      bf16x8 y;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) rp[e] = cl.r0[e];
-    for (int m = 0; m < lv - 1; ++m) {
-      float fm[8];
-      chain_factor(x, cl, m, fm);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) rp[e] *= fm[e];
+      for (int e = 0; e < 8; ++e) y[e] = (bf16_t)(al * ((float)rv[e] * (1.f - alm * (float)gv[e])));
+      *reinterpret_cast<bf16x8*>(sR + ct * LDM + cc) = y;
     }
-    chain_factor(x, cl, lv - 1, fl, gmv);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) rl[e] = rp[e] * fl[e];
-    put_written(x, cl, sR, lv, rl);
     __syncthreads();
+    if (lv > 1) {
+      if (in_t) {
+        pu = *reinterpret_cast<const uint4*>(ug + (size_t)ct * (x.L - 1) * D + (size_t)(lv - 2) * D + cc);
+        pg = *reinterpret_cast<const uint4*>(gg + (size_t)ct * (x.L - 1) * D + (size_t)(lv - 2) * D + cc);
+      }
+      pr_ = *reinterpret_cast<const uint4*>(rin + (size_t)(lv - 2) * 4096 + ct * 64 + cc);
+    }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int n0 = 16 * (nt0 + h), col = n0 + 4 * g;
@@ -1080,25 +1117,27 @@ __global__ __launch_bounds__(NT) void bwdc_grad_kernel(BwdArgs a) {
     __syncthreads();
     // the chain's adjoint for slot lv
     {
-      const float4 d0 = *reinterpret_cast<const float4*>(sdR + cl.t * LDF + cl.ch0);
-      const float4 d1 = *reinterpret_cast<const float4*>(sdR + cl.t * LDF + cl.ch0 + 4);
+      const float4 d0 = *reinterpret_cast<const float4*>(sdR + ct * LDF + cc);
+      const float4 d1 = *reinterpret_cast<const float4*>(sdR + ct * LDF + cc + 4);
       const float dR[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
-      const float al = tk[kAl + lv * 64 + cl.t], alm = tk[kAl + (lv - 1) * 64 + cl.t];
+      const bf16x8 rv = __builtin_bit_cast(bf16x8, cr), gv = __builtin_bit_cast(bf16x8, cgv);
+      const float al = tk[kAl + lv * 64 + ct], alm = tk[kAl + (lv - 1) * 64 + ct];
       float s = 0.f, s2 = 0.f;
       float dgm[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        s += dR[e] * rl[e];
+        const float rp = (float)rv[e], gm = (float)gv[e], fl = 1.f - alm * gm;
+        s += dR[e] * (rp * fl);
         dr[e] += al * dR[e];
-        s2 += dr[e] * gmv[e] * rp[e];
-        dgm[e] = -dr[e] * alm * rp[e];
-        dr[e] *= fl[e];
+        s2 += dr[e] * gm * rp;
+        dgm[e] = -dr[e] * alm * rp;
+        dr[e] *= fl;
       }
       s = sum8(s) + da_carry;
       da_carry = -sum8(s2);
       if (in_t) {
         if ((tid & 7) == 0) a.dalpha[tg * x.L + lv] = s;
-        float* dgp = a.dgamma + (tg * (x.L - 1) + lv - 1) * D + cl.ch0;
+        float* dgp = a.dgamma + (tg * (x.L - 1) + lv - 1) * D + cc;
         *reinterpret_cast<float4*>(dgp) = make_float4(dgm[0], dgm[1], dgm[2], dgm[3]);
         *reinterpret_cast<float4*>(dgp + 4) = make_float4(dgm[4], dgm[5], dgm[6], dgm[7]);
       }
@@ -1107,8 +1146,8 @@ __global__ __launch_bounds__(NT) void bwdc_grad_kernel(BwdArgs a) {
   // the direct part of dv (stored by this workgroup in B2), for the anchor terms at the end
   float dvd[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   if (in_t) {
-    const float4 d0 = *reinterpret_cast<const float4*>(a.dv + tg * D + cl.ch0);
-    const float4 d1 = *reinterpret_cast<const float4*>(a.dv + tg * D + cl.ch0 + 4);
+    const float4 d0 = *reinterpret_cast<const float4*>(a.dv + tg * D + cc);
+    const float4 d1 = *reinterpret_cast<const float4*>(a.dv + tg * D + cc + 4);
     dvd[0] = d0.x; dvd[1] = d0.y; dvd[2] = d0.z; dvd[3] = d0.w;
     dvd[4] = d1.x; dvd[5] = d1.y; dvd[6] = d1.z; dvd[7] = d1.w;
   }
@@ -1140,7 +1179,7 @@ __global__ __launch_bounds__(NT) void bwdc_grad_kernel(BwdArgs a) {
     // d r_0 of the chain, for the anchor's terms
 #pragma unroll
     for (int e = 0; e < 8; e += 4)
-      *reinterpret_cast<float4*>(sdR + cl.t * LDF + cl.ch0 + e) = make_float4(dr[e], dr[e + 1], dr[e + 2], dr[e + 3]);
+      *reinterpret_cast<float4*>(sdR + ct * LDF + cc + e) = make_float4(dr[e], dr[e + 1], dr[e + 2], dr[e + 3]);
     if ((tid & 7) == 0 && in_t) a.dalpha[tg * x.L] = da_carry;
     if (tid < 4 * D) sW[tid] = a.conv_w[(size_t)(x.pr % a.H) * 4 * D + tid];
   }
@@ -1195,16 +1234,16 @@ __global__ __launch_bounds__(NT) void bwdc_grad_kernel(BwdArgs a) {
       float out[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int ch = cl.ch0 + e;
-        float s = dvd[e] + sdR[cl.t * LDF + ch];
+        const int ch = cc + e;
+        float s = dvd[e] + sdR[ct * LDF + ch];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int ta = cl.t + 3 - j;
+          const int ta = ct + 3 - j;
           if (ta < C) s -= w[j * D + ch] * sdR[ta * LDF + ch];
         }
         out[e] = s;
       }
-      float* dvp = a.dv + tg * D + cl.ch0;
+      float* dvp = a.dv + tg * D + cc;
       *reinterpret_cast<float4*>(dvp) = make_float4(out[0], out[1], out[2], out[3]);
       *reinterpret_cast<float4*>(dvp + 4) = make_float4(out[4], out[5], out[6], out[7]);
     }
