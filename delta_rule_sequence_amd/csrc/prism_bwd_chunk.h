@@ -129,6 +129,20 @@ __device__ __forceinline__ f32x4 mm(f32x4 acc, const bf16_t* XA, const bf16_t* X
   return acc;
 }
 
+// Both of a wave's output tiles (m0, n0) and (m0, n0 + 16) of one product, the A operand
+// read once per k block.
+template <bool TA, bool TB>
+__device__ __forceinline__ void mm2(f32x4 (&acc)[2], const bf16_t* XA, const bf16_t* XB, int m0, int n0) {
+#pragma unroll
+  for (int k0 = 0; k0 < 64; k0 += 32) {
+    const bf16x8 a = TA ? tfrag(XA, m0, k0) : rfrag(XA, m0, k0);
+    const bf16x8 b0 = TB ? tfrag(XB, n0, k0) : rfrag(XB, n0, k0);
+    const bf16x8 b1 = TB ? tfrag(XB, n0 + 16, k0) : rfrag(XB, n0 + 16, k0);
+    acc[0] = mfma(b0, a, acc[0]);
+    acc[1] = mfma(b1, a, acc[1]);
+  }
+}
+
 __device__ __forceinline__ void put_bf16(bf16_t* X, int row, int col, const f32x4& v) {
   bf16x4 y;
 #pragma unroll
@@ -895,130 +909,162 @@ __global__ __launch_bounds__(NT) void bwdc_grad_kernel(BwdArgs a) {
   const size_t grow = (size_t)x.pr * a.T + x.t0 + row;  // global token row of this lane
   f32x4 dq[2], dk[2], dlg[2], p[2];
   float rb_beta = 0.f, rb_gv = 0.f, rb_dd = 0.f;  // this lane's row partials (4 columns x 2 tiles)
+  const int n0w = 16 * nt0;  // the wave's first output column
   // B0: E = Uc - Wc H; P = lower(Gam * Q K^T)
+  {
+    f32x4 e[2] = {zero4(), zero4()};
+    p[0] = zero4();
+    p[1] = zero4();
+    mm2<false, false>(e, sWc, sS, 16 * mt, n0w);
+    mm2<false, false>(p, sQ, sK, 16 * mt, n0w);
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int n0 = 16 * (nt0 + h), col = n0 + 4 * g;
-    f32x4 e = mm<false, false>(zero4(), sWc, sS, 16 * mt, n0);
-    const f32x4 ucv = get_bf16(sUc, row, col);
+    for (int h = 0; h < 2; ++h) {
+      const int col = n0w + 16 * h + 4 * g;
+      const f32x4 ucv = get_bf16(sUc, row, col);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) e[r] = ucv[r] - e[r];
-    put_bf16(sE, row, col, e);
-    p[h] = mm<false, false>(zero4(), sQ, sK, 16 * mt, n0);
-    const f32x4 gm = gam_tile(tk, row, col);
+      for (int r = 0; r < 4; ++r) e[h][r] = ucv[r] - e[h][r];
+      put_bf16(sE, row, col, e[h]);
+      const f32x4 gm = gam_tile(tk, row, col);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) p[h][r] *= gm[r];
-    put_bf16(sP, row, col, p[h]);
-    dlg[h] = zero4();
+      for (int r = 0; r < 4; ++r) p[h][r] *= gm[r];
+      put_bf16(sP, row, col, p[h]);
+      dlg[h] = zero4();
+    }
   }
   __syncthreads();
   // B1: dE = P^T dO + D (K dH'); dP = lower(dO E^T) -> Zp = Gam * dP; dG from Q H;
   //     dQ = G dO H^T; E dH'^T -> dK, dD
+  {
+    f32x4 a1[2] = {zero4(), zero4()}, a2[2] = {zero4(), zero4()};
+    mm2<true, true>(a1, sP, sdO, 16 * mt, n0w);
+    mm2<false, false>(a2, sK, sLam, 16 * mt, n0w);
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int n0 = 16 * (nt0 + h), col = n0 + 4 * g;
-    const f32x4 a1 = mm<true, true>(zero4(), sP, sdO, 16 * mt, n0);
-    const f32x4 a2 = mm<false, false>(zero4(), sK, sLam, 16 * mt, n0);
-    f32x4 de;
+    for (int h = 0; h < 2; ++h) {
+      f32x4 de;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) de[r] = a1[r] + D_i * a2[r];
-    put_bf16(sdE, row, col, de);
-    f32x4 dp = mm<false, false>(zero4(), sdO, sE, 16 * mt, n0);
-    const f32x4 gm = gam_tile(tk, row, col);
-    f32x4 zp;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      dp[r] = col + r <= row ? dp[r] : 0.f;
-      dlg[h][r] += dp[r] * p[h][r];
-      zp[r] = gm[r] * dp[r];
+      for (int r = 0; r < 4; ++r) de[r] = a1[h][r] + D_i * a2[h][r];
+      put_bf16(sdE, row, n0w + 16 * h + 4 * g, de);
     }
-    put_bf16(sZ, row, col, zp);
-    const f32x4 qh = mm<false, false>(zero4(), sQ, sS, 16 * mt, n0);
-    const f32x4 dov = get_bf16(sdO, row, col);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  {
+    f32x4 dp[2] = {zero4(), zero4()}, qh[2] = {zero4(), zero4()};
+    mm2<false, false>(dp, sdO, sE, 16 * mt, n0w);
+    mm2<false, false>(qh, sQ, sS, 16 * mt, n0w);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) rb_gv += dov[r] * qh[r];
-    dq[h] = mm<false, true>(zero4(), sdO, sS, 16 * mt, n0);
+    for (int h = 0; h < 2; ++h) {
+      const int col = n0w + 16 * h + 4 * g;
+      const f32x4 gm = gam_tile(tk, row, col);
+      const f32x4 dov = get_bf16(sdO, row, col);
+      f32x4 zp;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) dq[h][r] *= G_i;
-    const f32x4 edh = mm<false, true>(zero4(), sE, sLam, 16 * mt, n0);
-    const f32x4 kv = get_bf16(sK, row, col);
+      for (int r = 0; r < 4; ++r) {
+        const float d = col + r <= row ? dp[h][r] : 0.f;
+        dlg[h][r] += d * p[h][r];
+        zp[r] = gm[r] * d;
+        rb_gv += dov[r] * qh[h][r];
+      }
+      put_bf16(sZ, row, col, zp);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  {
+    dq[0] = zero4();
+    dq[1] = zero4();
+    mm2<false, true>(dq, sdO, sS, 16 * mt, n0w);
+    f32x4 edh[2] = {zero4(), zero4()};
+    mm2<false, true>(edh, sE, sLam, 16 * mt, n0w);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      dk[h][r] = D_i * edh[r];
-      rb_dd += kv[r] * edh[r];
+    for (int h = 0; h < 2; ++h) {
+      const f32x4 kv = get_bf16(sK, row, n0w + 16 * h + 4 * g);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        dq[h][r] *= G_i;
+        dk[h][r] = D_i * edh[h][r];
+        rb_dd += kv[r] * edh[h][r];
+      }
     }
   }
   __syncthreads();
   // B2: dX1 = T^T dE -> dVp (LDS, and dv's direct part), dbeta; dWc = -dE H^T;
   //     dQ += Zp K; dK += Zp^T Q
   float* dvg = a.dv + grow * D;
+  {
+    f32x4 dx1[2] = {zero4(), zero4()}, dwc[2] = {zero4(), zero4()};
+    mm2<true, true>(dx1, sT, sdE, 16 * mt, n0w);
+    mm2<false, true>(dwc, sdE, sS, 16 * mt, n0w);
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int n0 = 16 * (nt0 + h), col = n0 + 4 * g;
-    const f32x4 dx1 = mm<true, true>(zero4(), sT, sdE, 16 * mt, n0);
-    f32x4 dvp;
+    for (int h = 0; h < 2; ++h) {
+      const int col = n0w + 16 * h + 4 * g;
+      f32x4 dvp;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      dvp[r] = beta_i * dx1[r];
-      rb_beta += vp[h][r] * dx1[r];
+      for (int r = 0; r < 4; ++r) {
+        dvp[r] = beta_i * dx1[h][r];
+        rb_beta += vp[h][r] * dx1[h][r];
+        dwc[h][r] = -dwc[h][r];
+      }
+      put_bf16(sdVp, row, col, dvp);
+      if (in_i) *reinterpret_cast<f32x4*>(dvg + col) = dvp;
+      put_bf16(sdWc, row, col, dwc[h]);
     }
-    put_bf16(sdVp, row, col, dvp);
-    if (in_i) *reinterpret_cast<f32x4*>(dvg + col) = dvp;
-    f32x4 dwc = mm<false, true>(zero4(), sdE, sS, 16 * mt, n0);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) dwc[r] = -dwc[r];
-    put_bf16(sdWc, row, col, dwc);
-    dq[h] = mm<false, true>(dq[h], sZ, sK, 16 * mt, n0);
-    dk[h] = mm<true, true>(dk[h], sZ, sQ, 16 * mt, n0);
   }
+  __builtin_amdgcn_sched_barrier(0);
+  mm2<false, true>(dq, sZ, sK, 16 * mt, n0w);
+  mm2<true, true>(dk, sZ, sQ, 16 * mt, n0w);
   __syncthreads();
   // B3: dX2 = T^T dWc -> dK, dbeta, dG; Y = dE Uc^T + dWc Wc^T (into E's slot)
   bf16_t* sY = sE;
+  {
+    f32x4 dx2[2] = {zero4(), zero4()};
+    mm2<true, true>(dx2, sT, sdWc, 16 * mt, n0w);
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int n0 = 16 * (nt0 + h), col = n0 + 4 * g;
-    const f32x4 dx2 = mm<true, true>(zero4(), sT, sdWc, 16 * mt, n0);
-    const f32x4 kv = get_bf16(sK, row, col);
-    float rk = 0.f;
+    for (int h = 0; h < 2; ++h) {
+      const f32x4 kv = get_bf16(sK, row, n0w + 16 * h + 4 * g);
+      float rk = 0.f;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      rk += kv[r] * dx2[r];
-      dk[h][r] += beta_i * G_i * dx2[r];
+      for (int r = 0; r < 4; ++r) {
+        rk += kv[r] * dx2[h][r];
+        dk[h][r] += beta_i * G_i * dx2[h][r];
+      }
+      rb_beta += G_i * rk;
+      rb_gv += beta_i * rk;
     }
-    rb_beta += G_i * rk;
-    rb_gv += beta_i * rk;
-    f32x4 y = mm<false, false>(zero4(), sdE, sUc, 16 * mt, n0);
-    y = mm<false, false>(y, sdWc, sWc, 16 * mt, n0);
-    put_bf16(sY, row, col, y);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  {
+    f32x4 y[2] = {zero4(), zero4()};
+    mm2<false, false>(y, sdE, sUc, 16 * mt, n0w);
+    mm2<false, false>(y, sdWc, sWc, 16 * mt, n0w);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) put_bf16(sY, row, n0w + 16 * h + 4 * g, y[h]);
   }
   __syncthreads();
   // B4: dA = strict(-T^T Y) -> dbeta, dlG, Z = diag(beta) Gam * dA (into P's slot)
   bf16_t* sZ2 = sP;
+  {
+    f32x4 t[2] = {zero4(), zero4()}, kk[2] = {zero4(), zero4()};
+    mm2<true, true>(t, sT, sY, 16 * mt, n0w);
+    mm2<false, false>(kk, sK, sK, 16 * mt, n0w);
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int n0 = 16 * (nt0 + h), col = n0 + 4 * g;
-    const f32x4 t = mm<true, true>(zero4(), sT, sY, 16 * mt, n0);
-    const f32x4 kk = mm<false, false>(zero4(), sK, sK, 16 * mt, n0);
-    const f32x4 gm = gam_tile(tk, row, col);
-    f32x4 z;
+    for (int h = 0; h < 2; ++h) {
+      const int col = n0w + 16 * h + 4 * g;
+      const f32x4 gm = gam_tile(tk, row, col);
+      f32x4 z;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float da = col + r < row ? -t[r] : 0.f;
-      const float gk = gm[r] * kk[r];
-      rb_beta += da * gk;
-      dlg[h][r] += da * beta_i * gk;
-      z[r] = beta_i * gm[r] * da;
+      for (int r = 0; r < 4; ++r) {
+        const float da = col + r < row ? -t[h][r] : 0.f;
+        const float gk = gm[r] * kk[h][r];
+        rb_beta += da * gk;
+        dlg[h][r] += da * beta_i * gk;
+        z[r] = beta_i * gm[r] * da;
+      }
+      put_bf16(sZ2, row, col, z);
     }
-    put_bf16(sZ2, row, col, z);
   }
   __syncthreads();
   // B5: dK += Z K + Z^T K
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int n0 = 16 * (nt0 + h);
-    dk[h] = mm<false, true>(dk[h], sZ2, sK, 16 * mt, n0);
-    dk[h] = mm<true, true>(dk[h], sZ2, sK, 16 * mt, n0);
-  }
+  mm2<false, true>(dk, sZ2, sK, 16 * mt, n0w);
+  mm2<true, true>(dk, sZ2, sK, 16 * mt, n0w);
   // B6: rank slots, descending
   bf16_t *sN = x.m(mN), *sPU = x.m(mT), *sZpu = x.m(mX1), *sZn = x.m(mX2);
   float* sdR = x.mf(mUc);
@@ -1063,56 +1109,88 @@ __global__ __launch_bounds__(NT) void bwdc_grad_kernel(BwdArgs a) {
       }
       pr_ = *reinterpret_cast<const uint4*>(rin + (size_t)(lv - 2) * 4096 + ct * 64 + cc);
     }
+    {
+      const int n0 = 16 * nt0;
+      f32x4 n[2] = {zero4(), zero4()}, pu[2] = {zero4(), zero4()};
+      mm2<false, false>(n, sK, sU, 16 * mt, n0);
+      mm2<false, false>(pu, sQ, sU, 16 * mt, n0);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int n0 = 16 * (nt0 + h), col = n0 + 4 * g;
-      f32x4 n = mm<false, false>(zero4(), sK, sU, 16 * mt, n0);
-      f32x4 pu = mm<false, false>(zero4(), sQ, sU, 16 * mt, n0);
-      f32x4 dpu = mm<false, false>(zero4(), sdO, sR, 16 * mt, n0);
-      f32x4 dn = mm<false, false>(zero4(), sdVp, sR, 16 * mt, n0);
-      const f32x4 gm = gam_tile(tk, row, col);
-      f32x4 zpu, zn;
+      for (int h = 0; h < 2; ++h) {
+        const int col = n0 + 16 * h + 4 * g;
+        const f32x4 gm = gam_tile(tk, row, col);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const bool lo = col + r <= row, st = col + r < row;
-        n[r] = st ? gm[r] * n[r] : 0.f;
-        pu[r] = gm[r] * pu[r];
-        dpu[r] = lo ? dpu[r] : 0.f;
-        dn[r] = st ? -dn[r] : 0.f;
-        dlg[h][r] += dpu[r] * pu[r] + dn[r] * n[r];
-        zpu[r] = gm[r] * dpu[r];
-        zn[r] = gm[r] * dn[r];
+        for (int r = 0; r < 4; ++r) {
+          n[h][r] = col + r < row ? gm[r] * n[h][r] : 0.f;
+          pu[h][r] = gm[r] * pu[h][r];
+        }
+        put_bf16(sN, row, col, n[h]);
+        put_bf16(sPU, row, col, pu[h]);
       }
-      put_bf16(sN, row, col, n);
-      put_bf16(sPU, row, col, pu);
-      put_bf16(sZpu, row, col, zpu);
-      put_bf16(sZn, row, col, zn);
       __builtin_amdgcn_sched_barrier(0);
+      f32x4 dpu[2] = {zero4(), zero4()}, dn[2] = {zero4(), zero4()};
+      mm2<false, false>(dpu, sdO, sR, 16 * mt, n0);
+      mm2<false, false>(dn, sdVp, sR, 16 * mt, n0);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int col = n0 + 16 * h + 4 * g;
+        const f32x4 gm = gam_tile(tk, row, col);
+        f32x4 zpu, zn;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const bool lo = col + r <= row, st = col + r < row;
+          const float dp = lo ? dpu[h][r] : 0.f, dq_ = st ? -dn[h][r] : 0.f;
+          dlg[h][r] += dp * pu[h][r] + dq_ * n[h][r];
+          zpu[r] = gm[r] * dp;
+          zn[r] = gm[r] * dq_;
+        }
+        put_bf16(sZpu, row, col, zpu);
+        put_bf16(sZn, row, col, zn);
+      }
     }
     __syncthreads();
     float* dug = a.du + (grow * (x.L - 1) + lv - 1) * D;
+    {
+      // groups of products sharing their A operand across the wave's two tiles, fenced so
+      // that one group's temporaries are live at a time (register budget)
+      const int n0 = 16 * nt0;
+      {
+        f32x4 udh[2] = {zero4(), zero4()}, drt[2] = {zero4(), zero4()};
+        mm2<false, false>(udh, sU, sLam, 16 * mt, n0);
+        mm2<true, true>(drt, sPU, sdO, 16 * mt, n0);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int n0 = 16 * (nt0 + h), col = n0 + 4 * g;
-      const f32x4 udh = mm<false, false>(zero4(), sU, sLam, 16 * mt, n0);
-      f32x4 drt = mm<true, true>(zero4(), sPU, sdO, 16 * mt, n0);
-      const f32x4 ndv = mm<true, true>(zero4(), sN, sdVp, 16 * mt, n0);
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) drt[r] += D_i * udh[r] - ndv[r];
-      *reinterpret_cast<f32x4*>(sdR + row * LDF + col) = drt;
-      const f32x4 rdh = mm<false, true>(zero4(), sR, sLam, 16 * mt, n0);
-      const f32x4 uv = get_bf16(sU, row, col);
-      f32x4 du = mm<true, true>(zero4(), sZpu, sQ, 16 * mt, n0);
-      du = mm<true, true>(du, sZn, sK, 16 * mt, n0);
+          for (int r = 0; r < 4; ++r) drt[h][r] += D_i * udh[h][r];
+        f32x4 ndv[2] = {zero4(), zero4()};
+        mm2<true, true>(ndv, sN, sdVp, 16 * mt, n0);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        rb_dd += uv[r] * rdh[r];
-        du[r] += D_i * rdh[r];
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) drt[h][r] -= ndv[h][r];
+          *reinterpret_cast<f32x4*>(sdR + row * LDF + n0 + 16 * h + 4 * g) = drt[h];
+        }
       }
-      if (in_i) *reinterpret_cast<f32x4*>(dug + col) = du;
-      dq[h] = mm<false, true>(dq[h], sZpu, sU, 16 * mt, n0);
-      dk[h] = mm<false, true>(dk[h], sZn, sU, 16 * mt, n0);
-      __builtin_amdgcn_sched_barrier(0);  // one tile's temporaries at a time (register budget)
+      __builtin_amdgcn_sched_barrier(0);
+      {
+        f32x4 rdh[2] = {zero4(), zero4()}, du[2] = {zero4(), zero4()};
+        mm2<false, true>(rdh, sR, sLam, 16 * mt, n0);
+        mm2<true, true>(du, sZpu, sQ, 16 * mt, n0);
+        mm2<true, true>(du, sZn, sK, 16 * mt, n0);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int col = n0 + 16 * h + 4 * g;
+          const f32x4 uv = get_bf16(sU, row, col);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            rb_dd += uv[r] * rdh[h][r];
+            du[h][r] += D_i * rdh[h][r];
+          }
+          if (in_i) *reinterpret_cast<f32x4*>(dug + col) = du[h];
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      mm2<false, true>(dq, sZpu, sU, 16 * mt, n0);
+      mm2<false, true>(dk, sZn, sU, 16 * mt, n0);
     }
     __syncthreads();
     // the chain's adjoint for slot lv
