@@ -731,14 +731,20 @@ __global__ __launch_bounds__(256) void bwdc_scan_kernel(BwdArgs a) {
 #undef PRISM_DECL
 }
 
-// A float32 64 x 64 matrix (row-major) into LDS as bf16, 16 bytes per thread.
-__device__ __forceinline__ void load_f32_bf16(bf16_t* X, const float* src) {
+// A float32 64 x 64 matrix (row-major) in two steps: this thread's 8 entries from memory,
+// then into LDS as bf16.
+struct F32Row8 {
+  float4 u, v;
+};
+__device__ __forceinline__ F32Row8 fetch8(const float* src) {
   const int tid = threadIdx.x, row = tid >> 3, col = 8 * (tid & 7);
-  const float4 u = *reinterpret_cast<const float4*>(src + row * D + col);
-  const float4 v = *reinterpret_cast<const float4*>(src + row * D + col + 4);
+  return {*reinterpret_cast<const float4*>(src + row * D + col), *reinterpret_cast<const float4*>(src + row * D + col + 4)};
+}
+__device__ __forceinline__ void put8(bf16_t* X, const F32Row8& f) {
+  const int tid = threadIdx.x, row = tid >> 3, col = 8 * (tid & 7);
   bf16x8 y;
-  y[0] = (bf16_t)u.x; y[1] = (bf16_t)u.y; y[2] = (bf16_t)u.z; y[3] = (bf16_t)u.w;
-  y[4] = (bf16_t)v.x; y[5] = (bf16_t)v.y; y[6] = (bf16_t)v.z; y[7] = (bf16_t)v.w;
+  y[0] = (bf16_t)f.u.x; y[1] = (bf16_t)f.u.y; y[2] = (bf16_t)f.u.z; y[3] = (bf16_t)f.u.w;
+  y[4] = (bf16_t)f.v.x; y[5] = (bf16_t)f.v.y; y[6] = (bf16_t)f.v.z; y[7] = (bf16_t)f.v.w;
   *reinterpret_cast<bf16x8*>(X + row * LDM + col) = y;
 }
 
@@ -753,7 +759,8 @@ __device__ __forceinline__ void store_tile_t(float* dst, int row, int col, const
 //   Acc_g = Pre_G,  HB_g = sum_i Acc_{c0+G-1} .. Acc_{c0+i+1} HB_{c0+i},  ell_g = sum_i Pre_i^T ell_{c0+i}
 // (the state after the group from a zero start, and the adjoint at its start from its own
 // outputs), formed one chunk at a time: ell_g += M^T ell_i, M <- Acc_i M, HB_g <- Acc_i HB_g +
-// HB_i.  Products on bf16 MFMA operands (the running matrices kept in float32).
+// HB_i.  Products on bf16 MFMA operands (the running matrices kept in float32); the next
+// chunk's operands are loaded while the current chunk's products run.
 __global__ __launch_bounds__(NT) void bwdc_compose_kernel(BwdArgs a) {
   __shared__ __align__(16) bf16_t sm[4][MB];
   bf16_t *sA = sm[0], *sE = sm[1], *sM = sm[2], *sHg = sm[3];
@@ -770,10 +777,15 @@ __global__ __launch_bounds__(NT) void bwdc_compose_kernel(BwdArgs a) {
     Hg[h] = zero4();
     Eg[h] = zero4();
   }
+  auto so_of = [&](int it) { return ((size_t)pr * a.nseg + c0 + it) * D * D; };
+  F32Row8 fa = fetch8(a.seg_Acc + so_of(0)), fe = fetch8(a.seg_ell + so_of(0));
+  f32x4 hb[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+    hb[h] = *reinterpret_cast<const f32x4*>(a.seg_B + so_of(0) + (size_t)row * D + 16 * (nt0 + h) + 4 * g);
   for (int it = 0; it < G; ++it) {
-    const size_t so = ((size_t)pr * a.nseg + c0 + it) * D * D;
-    load_f32_bf16(sA, a.seg_Acc + so);
-    load_f32_bf16(sE, a.seg_ell + so);
+    put8(sA, fa);
+    put8(sE, fe);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int col = 16 * (nt0 + h) + 4 * g;
@@ -781,14 +793,21 @@ __global__ __launch_bounds__(NT) void bwdc_compose_kernel(BwdArgs a) {
       put_bf16(sHg, row, col, Hg[h]);
     }
     __syncthreads();
+    const f32x4 hc[2] = {hb[0], hb[1]};
+    if (it + 1 < G) {
+      fa = fetch8(a.seg_Acc + so_of(it + 1));
+      fe = fetch8(a.seg_ell + so_of(it + 1));
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int n0 = 16 * (nt0 + h), col = n0 + 4 * g;
-      Eg[h] = mm<true, true>(Eg[h], sM, sE, 16 * mt, n0);
-      M[h] = mm<false, true>(zero4(), sA, sM, 16 * mt, n0);
-      const f32x4 hb = *reinterpret_cast<const f32x4*>(a.seg_B + so + (size_t)row * D + col);
-      Hg[h] = mm<false, true>(hb, sA, sHg, 16 * mt, n0);
+      for (int h = 0; h < 2; ++h)
+        hb[h] = *reinterpret_cast<const f32x4*>(a.seg_B + so_of(it + 1) + (size_t)row * D + 16 * (nt0 + h) + 4 * g);
     }
+    mm2<true, true>(Eg, sM, sE, 16 * mt, 16 * nt0);
+    M[0] = zero4();
+    M[1] = zero4();
+    mm2<false, true>(M, sA, sM, 16 * mt, 16 * nt0);
+    Hg[0] = hc[0];
+    Hg[1] = hc[1];
+    mm2<false, true>(Hg, sA, sHg, 16 * mt, 16 * nt0);
     __syncthreads();
   }
   const size_t go = ((size_t)pr * a.ngrp + grp) * D * D;
@@ -805,7 +824,8 @@ __global__ __launch_bounds__(NT) void bwdc_compose_kernel(BwdArgs a) {
 // Each chunk's entering state and arriving adjoint from its group's (S layout): forwards
 // (blockIdx.z = 0) X_{c0} = X_g, X_{c+1} = Acc_c X_c + HB_c; backwards (blockIdx.z = 1)
 // Y_{c0+G-1} = Y_g, Y_{c-1} = Acc_c^T Y_c + ell_c.  The carried matrix is the B operand of
-// the next product in its S layout (B(k, n) = X[k][n] = S[n][k]); bf16 operands, float32 sums.
+// the next product in its S layout (B(k, n) = X[k][n] = S[n][k]); bf16 operands, float32
+// sums; the next step's operator is loaded while the current step's product runs.
 __global__ __launch_bounds__(NT) void bwdc_expand_kernel(BwdArgs a) {
   __shared__ __align__(16) bf16_t sm[2][MB];
   bf16_t *sA = sm[0], *sS = sm[1];
@@ -817,30 +837,42 @@ __global__ __launch_bounds__(NT) void bwdc_expand_kernel(BwdArgs a) {
   const size_t go = ((size_t)pr * a.ngrp + grp) * D * D;
   const float* xg = (rev ? a.grp_Lam : a.grp_Sin) + go;
   float* outb = rev ? a.seg_Lam : a.seg_Sin;
+  const float* addb = rev ? a.seg_ell : a.seg_B;
+  auto src_of = [&](int it) { return rev ? c0 + G - it : c0 + it - 1; };  // the chunk whose operator applies
+  auto so_of = [&](int c) { return ((size_t)pr * a.nseg + c) * D * D; };
+  F32Row8 fa = {};
+  f32x4 ad[2] = {zero4(), zero4()};
+  if (G > 1) {
+    fa = fetch8(a.seg_Acc + so_of(src_of(1)));
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      ad[h] = *reinterpret_cast<const f32x4*>(addb + so_of(src_of(1)) + (size_t)row * D + 16 * (nt0 + h) + 4 * g);
+  }
   // the group's own entry: copied (float32, S layout) and staged for the first product
   {
     const int c = rev ? c0 + G - 1 : c0;
-    float* dst = outb + ((size_t)pr * a.nseg + c) * D * D;
+    float* dst = outb + so_of(c);
+    const F32Row8 x0 = fetch8(xg);
     const int r = tid >> 3, c8 = 8 * (tid & 7);
-    *reinterpret_cast<float4*>(dst + r * D + c8) = *reinterpret_cast<const float4*>(xg + r * D + c8);
-    *reinterpret_cast<float4*>(dst + r * D + c8 + 4) = *reinterpret_cast<const float4*>(xg + r * D + c8 + 4);
-    load_f32_bf16(sS, xg);
+    *reinterpret_cast<float4*>(dst + r * D + c8) = x0.u;
+    *reinterpret_cast<float4*>(dst + r * D + c8 + 4) = x0.v;
+    put8(sS, x0);
   }
   for (int it = 1; it < G; ++it) {
-    const int cs = rev ? c0 + G - it : c0 + it - 1;   // the chunk whose operator applies
-    const int cd = rev ? cs - 1 : cs + 1;             // the chunk that receives the result
-    const size_t so = ((size_t)pr * a.nseg + cs) * D * D;
-    load_f32_bf16(sA, a.seg_Acc + so);
+    const int cd = rev ? src_of(it) - 1 : src_of(it) + 1;  // the chunk that receives the result
+    put8(sA, fa);
     __syncthreads();
-    f32x4 x[2];
+    f32x4 x[2] = {ad[0], ad[1]};
+    if (it + 1 < G) {
+      fa = fetch8(a.seg_Acc + so_of(src_of(it + 1)));
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int n0 = 16 * (nt0 + h), col = n0 + 4 * g;
-      const f32x4 add = *reinterpret_cast<const f32x4*>((rev ? a.seg_ell : a.seg_B) + so + (size_t)row * D + col);
-      x[h] = rev ? mm<true, false>(add, sA, sS, 16 * mt, n0) : mm<false, false>(add, sA, sS, 16 * mt, n0);
+      for (int h = 0; h < 2; ++h)
+        ad[h] = *reinterpret_cast<const f32x4*>(addb + so_of(src_of(it + 1)) + (size_t)row * D + 16 * (nt0 + h) + 4 * g);
     }
+    if (rev) mm2<true, false>(x, sA, sS, 16 * mt, 16 * nt0);
+    else mm2<false, false>(x, sA, sS, 16 * mt, 16 * nt0);
     __syncthreads();
-    float* dst = outb + ((size_t)pr * a.nseg + cd) * D * D;
+    float* dst = outb + so_of(cd);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int col = 16 * (nt0 + h) + 4 * g;
@@ -1331,15 +1363,19 @@ __global__ __launch_bounds__(NT) void bwdc_grad_kernel(BwdArgs a) {
       float s = 0.f;
       for (int t = 0; t <= 2 - jj; ++t) s -= w[(2 - jj - t) * D + ch] * sdR[t * LDF + ch];
       a.carry[(ps * 3 + jj) * D + ch] = s;
-    } else if (tid >= 256) {
-      // dconv_w share: dw_j = -sum_t d r_0(t) v_{t-3+j}
-      // four independent partial sums (tokens t = 4 m + q), added in a fixed order
-      const int j = (tid - 256) / D, ch = (tid - 256) % D;
-      float s4[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-      for (int t = 0; t < C; ++t) s4[t & 3] -= sdR[t * LDF + ch] * (float)sVx[(t + j) * 64 + ch];
-      a.dconv_part[(ps * 4 + j) * D + ch] = (s4[0] + s4[1]) + (s4[2] + s4[3]);
     }
+    // dconv_w share: dw_j = -sum_t d r_0(t) v_{t-3+j}, each (tap, channel) over two halves of
+    // the tokens (threads tid and tid + 256), four independent partial sums per half
+    float* sPart = x.mf(mU);  // [2][256] (slot U is free after the rank loop)
+    {
+      const int hf = tid >> 8, j = (tid & 255) >> 6, ch = tid & 63;
+      float s4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+      for (int t = 32 * hf; t < 32 * hf + 32; ++t) s4[t & 3] -= sdR[t * LDF + ch] * (float)sVx[(t + j) * 64 + ch];
+      sPart[tid] = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+    }
+    __syncthreads();
+    if (tid < 256) a.dconv_part[ps * 4 * D + tid] = sPart[tid] + sPart[256 + tid];
   }
 }
 
