@@ -635,7 +635,7 @@ constexpr int kScanCols = 8;
 __device__ __forceinline__ int scan_row(int r) { return 8 * r + 4 * (r >> 3); }  // float offset of carried row r
 
 __global__ __launch_bounds__(256) void bwdc_scan_kernel(BwdArgs a) {
-  constexpr int DEPTH = 8;
+  constexpr int DEPTH = 4;
   __shared__ __align__(16) float sH[2][64 * 8 + 8 * 4];
   const int tid = threadIdx.x, i0 = 2 * (tid >> 3), q = tid & 7;
   const int pr = blockIdx.x, c0 = kScanCols * blockIdx.y;
@@ -659,9 +659,7 @@ __global__ __launch_bounds__(256) void bwdc_scan_kernel(BwdArgs a) {
     R##D_##_b1 = B0[cn_ * D * D + D];                                                         \
   }
   PRISM_DECL(0) PRISM_DECL(1) PRISM_DECL(2) PRISM_DECL(3)
-  PRISM_DECL(4) PRISM_DECL(5) PRISM_DECL(6) PRISM_DECL(7)
   PRISM_FETCH(0, 0) PRISM_FETCH(1, 1) PRISM_FETCH(2, 2) PRISM_FETCH(3, 3)
-  PRISM_FETCH(4, 4) PRISM_FETCH(5, 5) PRISM_FETCH(6, 6) PRISM_FETCH(7, 7)
   const float* X0 = rev ? a.dS_final : nullptr;
   const float* xs = X0 != nullptr ? X0 + (size_t)pr * D * D : nullptr;
   float h0 = xs != nullptr ? xs[(size_t)i0 * D + c0 + q] : 0.f;
@@ -717,15 +715,10 @@ __global__ __launch_bounds__(256) void bwdc_scan_kernel(BwdArgs a) {
   int s0 = 0;
   for (; s0 + DEPTH <= n; s0 += DEPTH) {
     PRISM_SCAN_STEP(0, true) PRISM_SCAN_STEP(1, true) PRISM_SCAN_STEP(2, true) PRISM_SCAN_STEP(3, true)
-    PRISM_SCAN_STEP(4, true) PRISM_SCAN_STEP(5, true) PRISM_SCAN_STEP(6, true) PRISM_SCAN_STEP(7, true)
   }
   if (s0 + 0 < n) PRISM_SCAN_STEP(0, false)
   if (s0 + 1 < n) PRISM_SCAN_STEP(1, false)
   if (s0 + 2 < n) PRISM_SCAN_STEP(2, false)
-  if (s0 + 3 < n) PRISM_SCAN_STEP(3, false)
-  if (s0 + 4 < n) PRISM_SCAN_STEP(4, false)
-  if (s0 + 5 < n) PRISM_SCAN_STEP(5, false)
-  if (s0 + 6 < n) PRISM_SCAN_STEP(6, false)
 #undef PRISM_SCAN_STEP
 #undef PRISM_FETCH
 #undef PRISM_DECL
