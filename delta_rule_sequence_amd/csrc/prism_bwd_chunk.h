@@ -323,31 +323,34 @@ __device__ __forceinline__ void put_written(const Chunk& x, const ChainLane& cl,
 }
 
 // T = (I + A)^-1 for A strictly lower triangular (float32 A, row-major, stride LDF), in
-// float32 by 16 x 16 blocks.  Diagonal blocks: wave 0, lane 16 b + c walks column c of
-// block b down its rows (right-looking substitution, x_r -= A_rj x_j).  Off-diagonal
-// blocks by block distance d = 1, 2, 3 (block (j + d, j) on wave j):
-//   T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj
-// two float32 MFMA products (v_mfma_f32_16x16x4_f32), the sum's tile fed straight back as
-// the B operand of the second.  Tf (float32, stride LDF) is scratch; the result goes to Tb
-// in bfloat16 (zero above the diagonal blocks).  Every thread calls it (four barriers).
-__device__ __forceinline__ void block_inverse(const float* A, float* Tf, bf16_t* Tb) {
+// float32 by 16 x 16 blocks, as five steps each followed by a barrier (the caller's, so that
+// other work shares the intervals):
+//   step 0: diagonal blocks: wave 0, lane 16 b + c walks column c of block b down its rows
+//           (right-looking substitution, x_r -= A_rj x_j);
+//   steps 1..3: off-diagonal blocks at block distance d = step (block (j + d, j) on wave j):
+//           T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj, two float32 MFMA products
+//           (v_mfma_f32_16x16x4_f32), the sum's tile fed straight back as the B operand of
+//           the second;
+//   step 4: the result into Tb in bf16 (zero above the diagonal blocks), every thread.
+// Tf (float32, stride LDF) is scratch.
+__device__ __forceinline__ void inverse_step(int step, const float* A, float* Tf, bf16_t* Tb) {
   const int w = wave_id(), l = lane_id(), i = l & 15, g = l >> 4;
-  if (w == 0) {
-    const int o = 16 * g, c = i;
-    float x[16];
+  if (step == 0) {
+    if (w == 0) {
+      const int o = 16 * g, c = i;
+      float x[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) x[r] = r == c ? 1.f : 0.f;
+      for (int r = 0; r < 16; ++r) x[r] = r == c ? 1.f : 0.f;
 #pragma unroll
-    for (int j = 0; j < 15; ++j) {
+      for (int j = 0; j < 15; ++j) {
 #pragma unroll
-      for (int r = j + 1; r < 16; ++r) x[r] -= A[(o + r) * LDF + o + j] * x[j];
+        for (int r = j + 1; r < 16; ++r) x[r] -= A[(o + r) * LDF + o + j] * x[j];
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) Tf[(o + r) * LDF + o + c] = x[r];
     }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) Tf[(o + r) * LDF + o + c] = x[r];
-  }
-  __syncthreads();
-#pragma unroll
-  for (int d = 1; d < 4; ++d) {
+  } else if (step < 4) {
+    const int d = step;
     if (w < 4 - d) {
       const int bj = w, bi = w + d;
       f32x4 xs = zero4();
@@ -363,18 +366,18 @@ __device__ __forceinline__ void block_inverse(const float* A, float* Tf, bf16_t*
 #pragma unroll
       for (int r = 0; r < 4; ++r) Tf[(16 * bi + 4 * g + r) * LDF + 16 * bj + i] = -t[r];
     }
-    __syncthreads();
-  }
-  for (int e = threadIdx.x; e < 64 * 16; e += NT) {
-    const int row = e >> 4, c4 = 4 * (e & 15);
-    const bool keep = (c4 >> 4) <= (row >> 4);
-    const float4 v = *reinterpret_cast<const float4*>(Tf + row * LDF + c4);
-    bf16x4 y;
-    y[0] = keep ? (bf16_t)v.x : (bf16_t)0.f;
-    y[1] = keep ? (bf16_t)v.y : (bf16_t)0.f;
-    y[2] = keep ? (bf16_t)v.z : (bf16_t)0.f;
-    y[3] = keep ? (bf16_t)v.w : (bf16_t)0.f;
-    *reinterpret_cast<bf16x4*>(Tb + row * LDM + c4) = y;
+  } else {
+    for (int e = threadIdx.x; e < 64 * 16; e += NT) {
+      const int row = e >> 4, c4 = 4 * (e & 15);
+      const bool keep = (c4 >> 4) <= (row >> 4);
+      const float4 v = *reinterpret_cast<const float4*>(Tf + row * LDF + c4);
+      bf16x4 y;
+      y[0] = keep ? (bf16_t)v.x : (bf16_t)0.f;
+      y[1] = keep ? (bf16_t)v.y : (bf16_t)0.f;
+      y[2] = keep ? (bf16_t)v.z : (bf16_t)0.f;
+      y[3] = keep ? (bf16_t)v.w : (bf16_t)0.f;
+      *reinterpret_cast<bf16x4*>(Tb + row * LDM + c4) = y;
+    }
   }
 }
 
@@ -419,7 +422,6 @@ __device__ __forceinline__ void chunk_forward(const Chunk& x, ChainLane& cl, Fwd
     *reinterpret_cast<f32x4*>(sAf + row * LDF + col) = av;
   }
   __syncthreads();
-  block_inverse(sAf, x.mf(mUc), sT);
   // V' = V - sum_l N_l R_l: V's tiles straight from memory
   const bf16_t* vg = static_cast<const bf16_t*>(a.v) + ((size_t)x.pr * a.T + x.t0) * D;
 #pragma unroll
@@ -432,12 +434,15 @@ __device__ __forceinline__ void chunk_forward(const Chunk& x, ChainLane& cl, Fwd
       for (int r = 0; r < 4; ++r) f.vp[h][r] = (float)y[r];
     }
   }
-  // F3: rank slots, ascending.  U_l and R_l alternate between two LDS slots, so the next
-  // slot's rows are written while the current slot's last product runs (two barriers per
-  // slot); its u rows and gamma are loaded from memory one slot ahead.  r_{l-1} goes to the
-  // chunk's matrices (bf16) for the gradient pass.
-  bf16_t* sUb[2] = {sU, x.m(m13)};
-  bf16_t* sRb[2] = {sR, x.m(m14)};
+  // The inverse (five steps, T not needed before F4) and the rank slots (F3, ascending) share
+  // barrier intervals.  Slot l's phases: A_l writes U_l and R_l (alternating between two LDS
+  // slot pairs, the u rows and gamma loaded one slot ahead; r_{l-1} goes to the chunk's
+  // matrices for the gradient pass), B_l forms N_l = strict(Gam * K U_l^T) (and hb), C_l
+  // subtracts N_l R_l from V'.  Interval k holds inverse step k (k < 5) and, for k = 2 m, C_m
+  // and A_{m+1}, for k = 2 m + 1, B_{m+1}.
+  bf16_t* sUb[2] = {sU, x.m(mS)};
+  bf16_t* sRb[2] = {sR, x.m(mLam)};
+  float* sTf = x.mf(mUc);
   const int tid = threadIdx.x, trow = tid >> 3, tc8 = 8 * (tid & 7);
   const bool tin = trow < x.nt;
   const bf16_t* ug = static_cast<const bf16_t*>(a.u) + ((size_t)x.pr * a.T + x.t0) * (x.L - 1) * D;
@@ -452,44 +457,56 @@ __device__ __forceinline__ void chunk_forward(const Chunk& x, ChainLane& cl, Fwd
   float rc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) rc[e] = cl.r0[e];
+  constexpr int kSteps = 5;
+  const int nk = (2 * (x.L - 1) + 1 > kSteps) ? 2 * (x.L - 1) + 1 : kSteps;
 #pragma unroll
-  for (int lv = 1; lv < x.L; ++lv) {
-    const int b = (lv - 1) & 1;
-    {
-      // slot lv: u rows, r_{lv-1} handed on, r_lv = r_{lv-1} (1 - alpha_{lv-1} gamma_{lv-1}), R_lv
-      *reinterpret_cast<uint4*>(sUb[b] + trow * LDM + tc8) = pu;
-      bf16x8 rb;
+  for (int k = 0; k < nk; ++k) {
+    if (k < kSteps) inverse_step(k, sAf, sTf, sT);
+    const int m = k >> 1;
+    if ((k & 1) == 0) {
+      if (m >= 1 && m <= x.L - 1) {
+        // C_m: V' -= N_m R_m
+        const int b = (m - 1) & 1;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) rb[e] = (bf16_t)rc[e];
-      *reinterpret_cast<bf16x8*>(rout + (size_t)(lv - 1) * 4096 + trow * 64 + tc8) = rb;
-      const bf16x8 gv = __builtin_bit_cast(bf16x8, pg);
-      const float al = tk[kAl + (lv - 1) * 64 + trow];
+        for (int h = 0; h < 2; ++h) {
+          const f32x4 t = mm<false, true>(zero4(), sN, sRb[b], 16 * mt, 16 * (nt0 + h));
 #pragma unroll
-      for (int e = 0; e < 8; ++e) rc[e] *= 1.f - al * (float)gv[e];
-      put_written(x, cl, sRb[b], lv, rc);
+          for (int r = 0; r < 4; ++r) f.vp[h][r] -= t[r];
+        }
+      }
+      if (m + 1 <= x.L - 1) {
+        // A_{m+1}: U and R of slot lv = m + 1
+        const int lv = m + 1, b = (lv - 1) & 1;
+        *reinterpret_cast<uint4*>(sUb[b] + trow * LDM + tc8) = pu;
+        bf16x8 rb;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) rb[e] = (bf16_t)rc[e];
+        *reinterpret_cast<bf16x8*>(rout + (size_t)(lv - 1) * 4096 + trow * 64 + tc8) = rb;
+        const bf16x8 gv = __builtin_bit_cast(bf16x8, pg);
+        const float al = tk[kAl + (lv - 1) * 64 + trow];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) rc[e] *= 1.f - al * (float)gv[e];
+        put_written(x, cl, sRb[b], lv, rc);
+      }
+    } else if (m + 1 <= x.L - 1) {
+      // B_{m+1}: N_{m+1} (and hb); the next slot's u rows and gamma from memory
+      const int lv = m + 1, b = (lv - 1) & 1;
+      if (lv + 1 < x.L && tin) {
+        pu = *reinterpret_cast<const uint4*>(ug + (size_t)trow * (x.L - 1) * D + (size_t)lv * D + tc8);
+        pg = *reinterpret_cast<const uint4*>(gg + (size_t)trow * (x.L - 1) * D + (size_t)lv * D + tc8);
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int n0 = 16 * (nt0 + h), col = n0 + 4 * g;
+        f32x4 nr = mm<false, false>(zero4(), sK, sUb[b], 16 * mt, n0);
+        const f32x4 gm = gam_tile(tk, row, col);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) nr[r] = col + r < row ? gm[r] * nr[r] : 0.f;
+        put_bf16(sN, row, col, nr);
+        if constexpr (HB) hb[h] = mm<true, true>(hb[h], sUb[b], sRb[b], 16 * mt, n0, tk + kDd);
+      }
     }
-    __syncthreads();
-    if (lv + 1 < x.L && tin) {
-      pu = *reinterpret_cast<const uint4*>(ug + (size_t)trow * (x.L - 1) * D + (size_t)lv * D + tc8);
-      pg = *reinterpret_cast<const uint4*>(gg + (size_t)trow * (x.L - 1) * D + (size_t)lv * D + tc8);
-    }
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int n0 = 16 * (nt0 + h), col = n0 + 4 * g;
-      f32x4 nr = mm<false, false>(zero4(), sK, sUb[b], 16 * mt, n0);
-      const f32x4 gm = gam_tile(tk, row, col);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) nr[r] = col + r < row ? gm[r] * nr[r] : 0.f;
-      put_bf16(sN, row, col, nr);
-      if constexpr (HB) hb[h] = mm<true, true>(hb[h], sUb[b], sRb[b], 16 * mt, n0, tk + kDd);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const f32x4 t = mm<false, true>(zero4(), sN, sRb[b], 16 * mt, 16 * (nt0 + h));
-#pragma unroll
-      for (int r = 0; r < 4; ++r) f.vp[h][r] -= t[r];
-    }
+    if (k + 1 < nk) __syncthreads();
   }
   // F4: X1 = diag(beta) V', X2 = diag(beta G) K; Uc = T X1, Wc = T X2
 #pragma unroll
