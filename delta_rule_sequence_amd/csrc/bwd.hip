@@ -123,8 +123,8 @@ prism_status launch_bwd_chunked(const BwdArgs& a, int B, int P, float* dconv_w, 
   if (a.L == 1) return PRISM_OK;
   if (a.nseg > 1)
     hipLaunchKernelGGL(bwd_seg_carry_kernel, dim3((unsigned)P * (unsigned)a.nseg), dim3(256), 0, stream, a, 64);
-  hipLaunchKernelGGL(bwd_conv_reduce_kernel, dim3(a.H, 4), dim3(256), 0, stream,
-                     static_cast<const float*>(a.dconv_part), dconv_w, B, a.H, 64, a.nseg);
+  hipLaunchKernelGGL(bwdc::bwdc_conv_reduce_kernel, dim3(a.H, 4), dim3(1024), 0, stream,
+                     static_cast<const float*>(a.dconv_part), dconv_w, B, a.H, a.nseg);
   return hipGetLastError() == hipSuccess ? PRISM_OK : PRISM_ERR_HIP;
 }
 

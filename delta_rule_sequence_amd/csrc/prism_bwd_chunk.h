@@ -893,6 +893,31 @@ __global__ __launch_bounds__(NT) void bwdc_expand_kernel(BwdArgs a) {
   }
 }
 
+// dconv_w[h] = sum over the batch and the chunks of the per-chunk shares [B][H][nch][4][64]:
+// workgroup (h, block of 64 entries) of 1024 threads; thread (q, e) sums the shares
+// x = q, q + 16, .. of entry e with four accumulators, then the 16 partial sums are added in
+// a fixed order (deterministic).
+__global__ __launch_bounds__(1024) void bwdc_conv_reduce_kernel(const float* part, float* dconv_w, int B, int H,
+                                                                int nch) {
+  __shared__ float ps[16][64];
+  const int h = blockIdx.x, q = threadIdx.x >> 6, e = threadIdx.x & 63, idx = 64 * blockIdx.y + e;
+  const int n = B * nch;
+  float s4[4] = {0.f, 0.f, 0.f, 0.f};
+  int m = 0;
+  for (int x = q; x < n; x += 16, ++m) {
+    const int b = x / nch, c = x % nch;
+    s4[m & 3] += part[(((size_t)b * H + h) * nch + c) * 4 * D + idx];
+  }
+  ps[q][e] = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+  __syncthreads();
+  if (q == 0) {
+    float t = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) t += ps[r][e];
+    dconv_w[(size_t)h * 4 * D + idx] = t;
+  }
+}
+
 // Every gradient of chunk (blockIdx.x, pair blockIdx.y) from its start state (seg_Sin) and
 // the adjoint of its end state (seg_Lam).  NL = L - 1 rank slots, fixed at compile time.
 template <int NL>
