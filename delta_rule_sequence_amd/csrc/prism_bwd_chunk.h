@@ -381,6 +381,12 @@ __device__ __forceinline__ void inverse_step(int step, const float* A, float* Tf
   }
 }
 
+// A row-lane tile (lane: out[row][col .. col + 3]) stored transposed into a float32 matrix.
+__device__ __forceinline__ void store_tile_t(float* dst, int row, int col, const f32x4& v) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) dst[(size_t)(col + r) * D + row] = v[r];
+}
+
 // lower(Gam) at the lane's four entries (row, col .. col + 3) of a 64 x 64 tile.
 __device__ __forceinline__ f32x4 gam_tile(const float* tk, int row, int col) {
   const float b_i = tk[kB + row];
@@ -410,7 +416,8 @@ __device__ __forceinline__ void chunk_forward(const Chunk& x, ChainLane& cl, Fwd
   bf16_t *sX1 = x.m(mX1), *sX2 = x.m(mX2), *sUc = x.m(mUc), *sWc = x.m(mWc);
   float* sAf = x.mf(m13);
   const float beta_i = tk[kBeta + row], G_i = tk[kG + row];
-  // F1: A = strict(diag(beta) Gam * K K^T) (float32)
+  // F1: A = strict(diag(beta) Gam * K K^T) (float32); with HB also P = lower(Gam * Q K^T)
+  // into slot 15 for the local pass's Qt
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int n0 = 16 * (nt0 + h), col = n0 + 4 * g;
@@ -420,6 +427,12 @@ __device__ __forceinline__ void chunk_forward(const Chunk& x, ChainLane& cl, Fwd
 #pragma unroll
     for (int r = 0; r < 4; ++r) av[r] = col + r < row ? beta_i * gm[r] * kk[r] : 0.f;
     *reinterpret_cast<f32x4*>(sAf + row * LDF + col) = av;
+    if constexpr (HB) {
+      f32x4 p = mm<false, false>(zero4(), x.m(mQ), sK, 16 * mt, n0);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) p[r] *= gm[r];
+      put_bf16(x.m(m15), row, col, p);
+    }
   }
   __syncthreads();
   // V' = V - sum_l N_l R_l: V's tiles straight from memory
@@ -567,7 +580,7 @@ __global__ __launch_bounds__(NT) void bwdc_local_kernel(BwdArgs a) {
   chunk_forward<true>(x, cl, f, hb);
   const float* tk = x.tok;
   bf16_t *sQ = x.m(mQ), *sK = x.m(mK), *sdO = x.m(mdO), *sUc = x.m(mUc), *sWc = x.m(mWc);
-  bf16_t *sP = x.m(mX1), *sQt = x.m(mX2);
+  bf16_t *sP = x.m(m15), *sQt = x.m(mX2);
   {
     // T, Uc, Wc and V' for the gradient pass (bf16, row-major 64 x 64 each)
     bf16_t* cm = static_cast<bf16_t*>(a.chunk_mats) + ((size_t)x.pr * a.nseg + x.c) * (4 + x.L - 1) * 4096;
@@ -583,18 +596,8 @@ __global__ __launch_bounds__(NT) void bwdc_local_kernel(BwdArgs a) {
       *reinterpret_cast<bf16x4*>(cm + 12288 + row * 64 + 16 * (nt0 + h) + 4 * g) = y;
     }
   }
-  // P = lower(Gam * Q K^T)
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int n0 = 16 * (nt0 + h);
-    f32x4 p = mm<false, false>(zero4(), sQ, sK, 16 * mt, n0);
-    const f32x4 gm = gam_tile(tk, row, n0 + 4 * g);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) p[r] *= gm[r];
-    put_bf16(sP, row, n0 + 4 * g, p);
-  }
-  __syncthreads();
-  // Qt = diag(G) Q - P Wc; Acc = G_C I - K^T D Wc and its transpose Phi; HB = hb + K^T D Uc
+  // Qt = diag(G) Q - P Wc (P formed in F1); Acc = G_C I - K^T D Wc and its transpose Phi;
+  // HB = hb + K^T D Uc
   const float GC = tk[kG + 63];
   const size_t so = ((size_t)x.pr * a.nseg + x.c) * D * D;
 #pragma unroll
@@ -606,15 +609,11 @@ __global__ __launch_bounds__(NT) void bwdc_local_kernel(BwdArgs a) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) qt[r] = G_i * qt[r] - pw[r];
     put_bf16(sQt, row, col, qt);
-    f32x4 ph = mm<true, true>(zero4(), sWc, sK, 16 * mt, n0, tk + kDd);
     f32x4 ac = mm<true, true>(zero4(), sK, sWc, 16 * mt, n0, tk + kDd);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      ph[r] = (col + r == row ? GC : 0.f) - ph[r];
-      ac[r] = (col + r == row ? GC : 0.f) - ac[r];
-    }
-    *reinterpret_cast<f32x4*>(a.seg_Phi + so + (size_t)row * D + col) = ph;
+    for (int r = 0; r < 4; ++r) ac[r] = (col + r == row ? GC : 0.f) - ac[r];
     *reinterpret_cast<f32x4*>(a.seg_Acc + so + (size_t)row * D + col) = ac;
+    store_tile_t(a.seg_Phi + so, row, col, ac);
     const f32x4 bb = mm<true, true>(hb[h], sK, sUc, 16 * mt, n0, tk + kDd);
     *reinterpret_cast<f32x4*>(a.seg_B + so + (size_t)row * D + col) = bb;
   }
@@ -756,12 +755,6 @@ __device__ __forceinline__ void put8(bf16_t* X, const F32Row8& f) {
   y[0] = (bf16_t)f.u.x; y[1] = (bf16_t)f.u.y; y[2] = (bf16_t)f.u.z; y[3] = (bf16_t)f.u.w;
   y[4] = (bf16_t)f.v.x; y[5] = (bf16_t)f.v.y; y[6] = (bf16_t)f.v.z; y[7] = (bf16_t)f.v.w;
   *reinterpret_cast<bf16x8*>(X + row * LDM + col) = y;
-}
-
-// A row-lane tile (lane: out[row][col .. col + 3]) stored transposed into a float32 matrix.
-__device__ __forceinline__ void store_tile_t(float* dst, int row, int col, const f32x4& v) {
-#pragma unroll
-  for (int r = 0; r < 4; ++r) dst[(size_t)(col + r) * D + row] = v[r];
 }
 
 // Group operators of the two-level scan, one workgroup per group of up to kBwdGroup chunks
