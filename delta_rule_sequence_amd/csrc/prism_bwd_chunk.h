@@ -143,6 +143,24 @@ __device__ __forceinline__ void mm2(f32x4 (&acc)[2], const bf16_t* XA, const bf1
   }
 }
 
+// Two products with the same B operand, XA1 B and XA2 B, on both of a wave's tiles: each
+// operand fragment read once per k block.
+template <bool TA, bool TB>
+__device__ __forceinline__ void mm2b(f32x4 (&acc1)[2], f32x4 (&acc2)[2], const bf16_t* XA1, const bf16_t* XA2,
+                                     const bf16_t* XB, int m0, int n0) {
+#pragma unroll
+  for (int k0 = 0; k0 < 64; k0 += 32) {
+    const bf16x8 a1 = TA ? tfrag(XA1, m0, k0) : rfrag(XA1, m0, k0);
+    const bf16x8 a2 = TA ? tfrag(XA2, m0, k0) : rfrag(XA2, m0, k0);
+    const bf16x8 b0 = TB ? tfrag(XB, n0, k0) : rfrag(XB, n0, k0);
+    const bf16x8 b1 = TB ? tfrag(XB, n0 + 16, k0) : rfrag(XB, n0 + 16, k0);
+    acc1[0] = mfma(b0, a1, acc1[0]);
+    acc1[1] = mfma(b1, a1, acc1[1]);
+    acc2[0] = mfma(b0, a2, acc2[0]);
+    acc2[1] = mfma(b1, a2, acc2[1]);
+  }
+}
+
 __device__ __forceinline__ void put_bf16(bf16_t* X, int row, int col, const f32x4& v) {
   bf16x4 y;
 #pragma unroll
@@ -888,20 +906,26 @@ __global__ __launch_bounds__(NT) void bwdc_expand_kernel(BwdArgs a) {
 
 // dconv_w[h] = sum over the batch and the chunks of the per-chunk shares [B][H][nch][4][64]:
 // workgroup (h, block of 64 entries) of 1024 threads; thread (q, e) sums the shares
-// x = q, q + 16, .. of entry e with four accumulators, then the 16 partial sums are added in
-// a fixed order (deterministic).
+// x = q, q + 16, .. of entry e (eight loads in flight, eight accumulators), then the 16
+// partial sums are added in a fixed order (deterministic).
 __global__ __launch_bounds__(1024) void bwdc_conv_reduce_kernel(const float* part, float* dconv_w, int B, int H,
                                                                 int nch) {
   __shared__ float ps[16][64];
   const int h = blockIdx.x, q = threadIdx.x >> 6, e = threadIdx.x & 63, idx = 64 * blockIdx.y + e;
   const int n = B * nch;
-  float s4[4] = {0.f, 0.f, 0.f, 0.f};
-  int m = 0;
-  for (int x = q; x < n; x += 16, ++m) {
-    const int b = x / nch, c = x % nch;
-    s4[m & 3] += part[(((size_t)b * H + h) * nch + c) * 4 * D + idx];
+  // eight shares in flight per round (independent loads), eight accumulators
+  float s8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int x0 = q; x0 < n; x0 += 16 * 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int x = x0 + 16 * u;
+      v[u] = x < n ? part[(((size_t)(x / nch) * H + h) * nch + x % nch) * 4 * D + idx] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s8[u] += v[u];
   }
-  ps[q][e] = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+  ps[q][e] = ((s8[0] + s8[1]) + (s8[2] + s8[3])) + ((s8[4] + s8[5]) + (s8[6] + s8[7]));
   __syncthreads();
   if (q == 0) {
     float t = 0.f;
@@ -1172,8 +1196,7 @@ __global__ __launch_bounds__(NT) void bwdc_grad_kernel(BwdArgs a) {
     {
       const int n0 = 16 * nt0;
       f32x4 n[2] = {zero4(), zero4()}, pu[2] = {zero4(), zero4()};
-      mm2<false, false>(n, sK, sU, 16 * mt, n0);
-      mm2<false, false>(pu, sQ, sU, 16 * mt, n0);
+      mm2b<false, false>(n, pu, sK, sQ, sU, 16 * mt, n0);
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int col = n0 + 16 * h + 4 * g;
@@ -1188,8 +1211,7 @@ __global__ __launch_bounds__(NT) void bwdc_grad_kernel(BwdArgs a) {
       }
       __builtin_amdgcn_sched_barrier(0);
       f32x4 dpu[2] = {zero4(), zero4()}, dn[2] = {zero4(), zero4()};
-      mm2<false, false>(dpu, sdO, sR, 16 * mt, n0);
-      mm2<false, false>(dn, sdVp, sR, 16 * mt, n0);
+      mm2b<false, false>(dpu, dn, sdO, sdVp, sR, 16 * mt, n0);
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int col = n0 + 16 * h + 4 * g;
@@ -1249,8 +1271,7 @@ __global__ __launch_bounds__(NT) void bwdc_grad_kernel(BwdArgs a) {
         }
       }
       __builtin_amdgcn_sched_barrier(0);
-      mm2<false, true>(dq, sZpu, sU, 16 * mt, n0);
-      mm2<false, true>(dk, sZn, sU, 16 * mt, n0);
+      mm2b<false, true>(dq, dk, sZpu, sZn, sU, 16 * mt, n0);
     }
     __syncthreads();
     // the chain's adjoint for slot lv
