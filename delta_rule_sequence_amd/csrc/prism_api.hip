@@ -428,12 +428,12 @@ prism_status prism_bwd_lowmem(const void* q, const void* k, const void* v, const
 
 namespace {
 
-// Workspace of the chunked backward: per 64-token chunk six float32 64 x 64 matrices
-// (operator and its transpose, end state from zero, local adjoint, entering state,
-// arriving adjoint), its anchor carry [3][64] and dconv_w share [4][64], and 3 + L bf16
-// 64 x 64 matrices (T, Uc, Wc, V' and the chain residuals r_0 .. r_{L-2}) that the local
-// pass hands to the gradient pass; per group of four chunks the same six float32 matrices
-// for the two-level scan.
+// Workspace of the chunked backward: per 64-token chunk two float32 64 x 64 matrices (end
+// state from zero, local adjoint) and three bf16 ones (operator, entering state, arriving
+// adjoint), its anchor carry [3][64] and dconv_w share [4][64], and 3 + L bf16 64 x 64
+// matrices (T, Uc, Wc, V' and the chain residuals r_0 .. r_{L-2}) that the local pass hands
+// to the gradient pass; per group of four chunks six float32 64 x 64 matrices for the
+// two-level scan.
 struct BwdChunkPlan {
   int P, nch, ngrp;
   size_t off_seg, off_carry, off_part, off_mats, off_grp, total;
@@ -449,7 +449,7 @@ prism_status make_bwd_chunk_plan(int B, int H, int T, int dk, int dv, int L, pri
   if (!mul_ok(P, (size_t)T, &c) || !mul_ok(c, (size_t)L * dk * 4, &c)) return PRISM_ERR_INVALID_ARG;
   const size_t nch = ((size_t)T + 63) / 64;
   if (!mul_ok(P, nch, &nseg_all) || nseg_all > (size_t)INT32_MAX) return PRISM_ERR_INVALID_ARG;
-  if (!mul_ok(nseg_all, (size_t)6 * 64 * 64 * 4, &sz_seg) || !mul_ok(nseg_all, (size_t)3 * 64 * 4, &sz_carry) ||
+  if (!mul_ok(nseg_all, (size_t)(2 * 4 + 3 * 2) * 64 * 64, &sz_seg) || !mul_ok(nseg_all, (size_t)3 * 64 * 4, &sz_carry) ||
       !mul_ok(nseg_all, (size_t)4 * 64 * 4, &sz_part) || !mul_ok(nseg_all, (size_t)(3 + L) * 64 * 64 * 2, &sz_mats))
     return PRISM_ERR_INVALID_ARG;
   const size_t ngrp = (nch + prism::kBwdGroup - 1) / prism::kBwdGroup;
@@ -499,11 +499,11 @@ prism_status prism_bwd_chunked(const void* q, const void* k, const void* v, cons
   const size_t sq = (size_t)pl.P * pl.nch * 64 * 64;
   float* sg = reinterpret_cast<float*>(ws + pl.off_seg);
   a.seg_B = sg;
-  a.seg_Phi = sg + sq;
-  a.seg_ell = sg + 2 * sq;
-  a.seg_Sin = sg + 3 * sq;
-  a.seg_Lam = sg + 4 * sq;
-  a.seg_Acc = sg + 5 * sq;
+  a.seg_ell = sg + sq;
+  bf16_t* sb = reinterpret_cast<bf16_t*>(sg + 2 * sq);
+  a.c_Acc = sb;
+  a.c_Sin = sb + sq;
+  a.c_Lam = sb + 2 * sq;
   a.carry = reinterpret_cast<float*>(ws + pl.off_carry);
   a.dconv_part = reinterpret_cast<float*>(ws + pl.off_part);
   a.chunk_mats = ws + pl.off_mats;

@@ -25,7 +25,9 @@ struct BwdArgs {
   float* seg_Sin;  // state entering the segment
   float* seg_Lam;  // adjoint of the segment's last state from the tokens after it
   float* carry;    // [P][nseg][3][D] anchor terms a segment owes the three tokens before it
-  float* seg_Acc;  // chunked form only: the chunk operator in H layout (H = S^T), Phi^T
+  // chunked form only, bf16 [P][nseg][64][64]: the chunk operator in H layout (H = S^T),
+  // the chunk's entering state and the adjoint arriving at its end (S layout)
+  void *c_Acc, *c_Sin, *c_Lam;
   void* chunk_mats;  // chunked form only: bf16 [P][nseg][3 + L][64][64] T, Uc, Wc, V' and the
                      // residuals r_0 .. r_{L-2} of each chunk
   // chunked form only, float32 [P][ngrp][64][64], groups of kBwdGroup chunks: the group

@@ -224,25 +224,6 @@ __device__ __forceinline__ void load_rows(bf16_t* X, const bf16_t* src, size_t r
   *reinterpret_cast<uint4*>(X + row * LDM + col) = v;
 }
 
-// A float32 64 x 64 matrix of the segment form ([v][k], row-major) into LDS as bf16;
-// returns this thread's share of <X, Y> when y is given.
-__device__ __forceinline__ float load_state(bf16_t* X, const float* src, const float* other) {
-  const int tid = threadIdx.x, row = tid >> 3, col = 8 * (tid & 7);
-  const float4 a = *reinterpret_cast<const float4*>(src + row * D + col);
-  const float4 b = *reinterpret_cast<const float4*>(src + row * D + col + 4);
-  bf16x8 y;
-  y[0] = (bf16_t)a.x; y[1] = (bf16_t)a.y; y[2] = (bf16_t)a.z; y[3] = (bf16_t)a.w;
-  y[4] = (bf16_t)b.x; y[5] = (bf16_t)b.y; y[6] = (bf16_t)b.z; y[7] = (bf16_t)b.w;
-  *reinterpret_cast<bf16x8*>(X + row * LDM + col) = y;
-  float s = 0.f;
-  if (other != nullptr) {
-    const float4 c = *reinterpret_cast<const float4*>(other + row * D + col);
-    const float4 d = *reinterpret_cast<const float4*>(other + row * D + col + 4);
-    s = a.x * c.x + a.y * c.y + a.z * c.z + a.w * c.w + b.x * d.x + b.y * d.y + b.z * d.z + b.w * d.w;
-  }
-  return s;
-}
-
 // Token scalars: b = cumsum(log g) (wave 0, one token per lane), G, D, beta, g, alpha.
 __device__ __forceinline__ void load_scalars(const Chunk& x) {
   const BwdArgs& a = *x.a;
@@ -614,8 +595,8 @@ __global__ __launch_bounds__(NT) void bwdc_local_kernel(BwdArgs a) {
       *reinterpret_cast<bf16x4*>(cm + 12288 + row * 64 + 16 * (nt0 + h) + 4 * g) = y;
     }
   }
-  // Qt = diag(G) Q - P Wc (P formed in F1); Acc = G_C I - K^T D Wc and its transpose Phi;
-  // HB = hb + K^T D Uc
+  // Qt = diag(G) Q - P Wc (P formed in F1); Acc = G_C I - K^T D Wc (bf16: it is only ever
+  // an MFMA operand); HB = hb + K^T D Uc
   const float GC = tk[kG + 63];
   const size_t so = ((size_t)x.pr * a.nseg + x.c) * D * D;
 #pragma unroll
@@ -630,8 +611,12 @@ __global__ __launch_bounds__(NT) void bwdc_local_kernel(BwdArgs a) {
     f32x4 ac = mm<true, true>(zero4(), sK, sWc, 16 * mt, n0, tk + kDd);
 #pragma unroll
     for (int r = 0; r < 4; ++r) ac[r] = (col + r == row ? GC : 0.f) - ac[r];
-    *reinterpret_cast<f32x4*>(a.seg_Acc + so + (size_t)row * D + col) = ac;
-    store_tile_t(a.seg_Phi + so, row, col, ac);
+    {
+      bf16x4 y;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) y[r] = (bf16_t)ac[r];
+      *reinterpret_cast<bf16x4*>(static_cast<bf16_t*>(a.c_Acc) + so + (size_t)row * D + col) = y;
+    }
     const f32x4 bb = mm<true, true>(hb[h], sK, sUc, 16 * mt, n0, tk + kDd);
     *reinterpret_cast<f32x4*>(a.seg_B + so + (size_t)row * D + col) = bb;
   }
@@ -758,6 +743,17 @@ __global__ __launch_bounds__(256) void bwdc_scan_kernel(BwdArgs a) {
 #undef PRISM_DECL
 }
 
+// A bf16 64 x 64 matrix (row-major, unpadded) in two steps: this thread's 8 entries from
+// memory, then into an LDS matrix.
+__device__ __forceinline__ uint4 fetch8b(const bf16_t* src) {
+  const int tid = threadIdx.x;
+  return *reinterpret_cast<const uint4*>(src + (tid >> 3) * D + 8 * (tid & 7));
+}
+__device__ __forceinline__ void put8b(bf16_t* X, const uint4& v) {
+  const int tid = threadIdx.x;
+  *reinterpret_cast<uint4*>(X + (tid >> 3) * LDM + 8 * (tid & 7)) = v;
+}
+
 // A float32 64 x 64 matrix (row-major) in two steps: this thread's 8 entries from memory,
 // then into LDS as bf16.
 struct F32Row8 {
@@ -799,13 +795,15 @@ __global__ __launch_bounds__(NT) void bwdc_compose_kernel(BwdArgs a) {
     Eg[h] = zero4();
   }
   auto so_of = [&](int it) { return ((size_t)pr * a.nseg + c0 + it) * D * D; };
-  F32Row8 fa = fetch8(a.seg_Acc + so_of(0)), fe = fetch8(a.seg_ell + so_of(0));
+  const bf16_t* cacc = static_cast<const bf16_t*>(a.c_Acc);
+  uint4 fa = fetch8b(cacc + so_of(0));
+  F32Row8 fe = fetch8(a.seg_ell + so_of(0));
   f32x4 hb[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h)
     hb[h] = *reinterpret_cast<const f32x4*>(a.seg_B + so_of(0) + (size_t)row * D + 16 * (nt0 + h) + 4 * g);
   for (int it = 0; it < G; ++it) {
-    put8(sA, fa);
+    put8b(sA, fa);
     put8(sE, fe);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -816,7 +814,7 @@ __global__ __launch_bounds__(NT) void bwdc_compose_kernel(BwdArgs a) {
     __syncthreads();
     const f32x4 hc[2] = {hb[0], hb[1]};
     if (it + 1 < G) {
-      fa = fetch8(a.seg_Acc + so_of(it + 1));
+      fa = fetch8b(cacc + so_of(it + 1));
       fe = fetch8(a.seg_ell + so_of(it + 1));
 #pragma unroll
       for (int h = 0; h < 2; ++h)
@@ -842,11 +840,12 @@ __global__ __launch_bounds__(NT) void bwdc_compose_kernel(BwdArgs a) {
   }
 }
 
-// Each chunk's entering state and arriving adjoint from its group's (S layout): forwards
-// (blockIdx.z = 0) X_{c0} = X_g, X_{c+1} = Acc_c X_c + HB_c; backwards (blockIdx.z = 1)
-// Y_{c0+G-1} = Y_g, Y_{c-1} = Acc_c^T Y_c + ell_c.  The carried matrix is the B operand of
-// the next product in its S layout (B(k, n) = X[k][n] = S[n][k]); bf16 operands, float32
-// sums; the next step's operator is loaded while the current step's product runs.
+// Each chunk's entering state and arriving adjoint from its group's (S layout, stored in
+// bf16, the gradient pass's operand type): forwards (blockIdx.z = 0) X_{c0} = X_g,
+// X_{c+1} = Acc_c X_c + HB_c; backwards (blockIdx.z = 1) Y_{c0+G-1} = Y_g, Y_{c-1} =
+// Acc_c^T Y_c + ell_c.  The carried matrix is the B operand of the next product in its S
+// layout (B(k, n) = X[k][n] = S[n][k]); bf16 operands, float32 sums; the next step's
+// operator is loaded while the current step's product runs.
 __global__ __launch_bounds__(NT) void bwdc_expand_kernel(BwdArgs a) {
   __shared__ __align__(16) bf16_t sm[2][MB];
   bf16_t *sA = sm[0], *sS = sm[1];
@@ -857,35 +856,34 @@ __global__ __launch_bounds__(NT) void bwdc_expand_kernel(BwdArgs a) {
   const int c0 = grp * kBwdGroup, G = min(kBwdGroup, a.nseg - c0);
   const size_t go = ((size_t)pr * a.ngrp + grp) * D * D;
   const float* xg = (rev ? a.grp_Lam : a.grp_Sin) + go;
-  float* outb = rev ? a.seg_Lam : a.seg_Sin;
+  bf16_t* outb = static_cast<bf16_t*>(rev ? a.c_Lam : a.c_Sin);
+  const bf16_t* cacc = static_cast<const bf16_t*>(a.c_Acc);
   const float* addb = rev ? a.seg_ell : a.seg_B;
   auto src_of = [&](int it) { return rev ? c0 + G - it : c0 + it - 1; };  // the chunk whose operator applies
   auto so_of = [&](int c) { return ((size_t)pr * a.nseg + c) * D * D; };
-  F32Row8 fa = {};
+  const int r8 = tid >> 3, c8 = 8 * (tid & 7);
+  uint4 fa = {0u, 0u, 0u, 0u};
   f32x4 ad[2] = {zero4(), zero4()};
   if (G > 1) {
-    fa = fetch8(a.seg_Acc + so_of(src_of(1)));
+    fa = fetch8b(cacc + so_of(src_of(1)));
 #pragma unroll
     for (int h = 0; h < 2; ++h)
       ad[h] = *reinterpret_cast<const f32x4*>(addb + so_of(src_of(1)) + (size_t)row * D + 16 * (nt0 + h) + 4 * g);
   }
-  // the group's own entry: copied (float32, S layout) and staged for the first product
+  // the group's own entry: into bf16, staged for the first product and stored for its chunk
   {
     const int c = rev ? c0 + G - 1 : c0;
-    float* dst = outb + so_of(c);
-    const F32Row8 x0 = fetch8(xg);
-    const int r = tid >> 3, c8 = 8 * (tid & 7);
-    *reinterpret_cast<float4*>(dst + r * D + c8) = x0.u;
-    *reinterpret_cast<float4*>(dst + r * D + c8 + 4) = x0.v;
-    put8(sS, x0);
+    put8(sS, fetch8(xg));
+    __syncthreads();
+    *reinterpret_cast<uint4*>(outb + so_of(c) + r8 * D + c8) = *reinterpret_cast<const uint4*>(sS + r8 * LDM + c8);
   }
   for (int it = 1; it < G; ++it) {
     const int cd = rev ? src_of(it) - 1 : src_of(it) + 1;  // the chunk that receives the result
-    put8(sA, fa);
+    put8b(sA, fa);
     __syncthreads();
     f32x4 x[2] = {ad[0], ad[1]};
     if (it + 1 < G) {
-      fa = fetch8(a.seg_Acc + so_of(src_of(it + 1)));
+      fa = fetch8b(cacc + so_of(src_of(it + 1)));
 #pragma unroll
       for (int h = 0; h < 2; ++h)
         ad[h] = *reinterpret_cast<const f32x4*>(addb + so_of(src_of(it + 1)) + (size_t)row * D + 16 * (nt0 + h) + 4 * g);
@@ -893,14 +891,14 @@ __global__ __launch_bounds__(NT) void bwdc_expand_kernel(BwdArgs a) {
     if (rev) mm2<true, false>(x, sA, sS, 16 * mt, 16 * nt0);
     else mm2<false, false>(x, sA, sS, 16 * mt, 16 * nt0);
     __syncthreads();
-    float* dst = outb + so_of(cd);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int col = 16 * (nt0 + h) + 4 * g;
-      store_tile_t(dst, row, col, x[h]);
 #pragma unroll
       for (int r = 0; r < 4; ++r) sS[(col + r) * LDM + row] = (bf16_t)x[h][r];
     }
+    __syncthreads();
+    *reinterpret_cast<uint4*>(outb + so_of(cd) + r8 * D + c8) = *reinterpret_cast<const uint4*>(sS + r8 * LDM + c8);
   }
 }
 
@@ -935,8 +933,8 @@ __global__ __launch_bounds__(1024) void bwdc_conv_reduce_kernel(const float* par
   }
 }
 
-// Every gradient of chunk (blockIdx.x, pair blockIdx.y) from its start state (seg_Sin) and
-// the adjoint of its end state (seg_Lam).  NL = L - 1 rank slots, fixed at compile time.
+// Every gradient of chunk (blockIdx.x, pair blockIdx.y) from its start state (c_Sin) and
+// the adjoint of its end state (c_Lam).  NL = L - 1 rank slots, fixed at compile time.
 template <int NL>
 __global__ __launch_bounds__(NT) void bwdc_grad_kernel(BwdArgs a) {
   __shared__ __align__(16) char lds[Lds::total];
@@ -955,13 +953,20 @@ __global__ __launch_bounds__(NT) void bwdc_grad_kernel(BwdArgs a) {
   const size_t so = ((size_t)x.pr * a.nseg + x.c) * D * D;
   load_chunk_inputs(x);
   {
-    // <dH', H> (the end state's factor G_C): this thread's 8 entries, then the wave's sum
-    float gc = load_state(x.m(mS), a.seg_Sin + so, a.seg_Lam + so);
+    // the entering state and the arriving adjoint (bf16, S layout); <dH', H> (the end
+    // state's factor G_C): this thread's 8 entries, then the wave's sum
+    const uint4 su = fetch8b(static_cast<const bf16_t*>(a.c_Sin) + so);
+    const uint4 lu = fetch8b(static_cast<const bf16_t*>(a.c_Lam) + so);
+    put8b(x.m(mS), su);
+    put8b(x.m(mLam), lu);
+    const bf16x8 sv = __builtin_bit_cast(bf16x8, su), lv8 = __builtin_bit_cast(bf16x8, lu);
+    float gc = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) gc += (float)sv[e] * (float)lv8[e];
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) gc += __shfl_xor(gc, o);
     if (l == 0) tk[kMisc + w] = gc;
   }
-  load_state(x.m(mLam), a.seg_Lam + so, nullptr);
   // T, Uc, Wc (LDS) and V' (this lane's tiles) as the chunk's local pass formed them
   const bf16_t* cm = static_cast<const bf16_t*>(a.chunk_mats) + ((size_t)x.pr * a.nseg + x.c) * (4 + x.L - 1) * 4096;
   load_rows(x.m(mT), cm, 64, 64);

@@ -267,7 +267,7 @@ prism_status prism_bwd_lowmem(const void* q, const void* k, const void* v,
  * (a few 1e-3 of each gradient's largest entry), not prism_bwd's float32 one.  Arguments,
  * layouts and outputs as prism_bwd; dt must be PRISM_BF16 and dk = dv = 64 (else
  * PRISM_ERR_UNSUPPORTED), B * H <= 65535.  Deterministic.  Workspace:
- * prism_bwd_chunked_workspace_bytes (per chunk six float32 and 3 + L bfloat16 64 x 64
+ * prism_bwd_chunked_workspace_bytes (per chunk two float32 and 6 + L bfloat16 64 x 64
  * matrices plus 1.75 KiB, per group of four chunks six float32 64 x 64 matrices);
  * ownership, stream and errors as prism_fwd. */
 size_t prism_bwd_chunked_workspace_bytes(int B, int H, int T, int dk, int dv, int L, prism_dtype dt);
