@@ -88,3 +88,48 @@ def test_bwd_chunked_deterministic():
     torch.cuda.synchronize()
     for n in a:
         assert torch.equal(a[n], b[n]), n
+
+
+LONG_T, LONG_L = 4096, 4
+
+
+@pytest.fixture(scope="module")
+def long_pair():
+    """One (b, h) pair of 4096 tokens (64 chunks, 16 groups of the two-level scan) and its
+    float64 oracle gradients (~25 s on the host), shared by both forms' checks."""
+    if not gpu_available():
+        pytest.skip("no GPU")
+    import time
+    from oracle import prism_grad
+    w, x, d_o, dS = _setup("bf16", 1, 1, LONG_T, 64, LONG_L, True, seed=31)
+    t0 = time.perf_counter()
+    ref = prism_grad.backward(x["q"], x["k"], x["v"], x["g"], x["beta"], x["u"], x["alpha"], x["gamma"],
+                              x["conv_w"], LONG_L, d_o, dS)
+    print(f"[bwd] long pair oracle {time.perf_counter() - t0:.1f} s", flush=True)
+    return x, d_o, dS, ref
+
+
+@pytest.mark.parametrize("chunked", [True, False], ids=["chunked", "float32"])
+def test_bwd_long_pair(long_pair, chunked):
+    """Every gradient of the 4096-token pair against the oracle: the chunked form at its 2e-2
+    bar, the float32 form at 1e-4 (the state and adjoint carried across 64 chunks)."""
+    import torch
+    import delta_rule_sequence_amd as prism
+    import workloads
+    x, d_o, dS, ref = long_pair
+    print(f"[bwd] long pair chunked={chunked}", flush=True)
+    dev = workloads.to_torch(x, "bf16", "cuda")
+    got = prism.bwd(dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], dev["u"], dev["alpha"], dev["gamma"],
+                    dev["conv_w"], L=LONG_L, d_o=torch.tensor(d_o, device="cuda").to(torch.bfloat16),
+                    dS_final=torch.tensor(dS, device="cuda"), chunked=chunked)
+    torch.cuda.synchronize()
+    tol = TOL if chunked else 1e-4
+    errs = {}
+    for n in ["dq", "dk", "dv", "dg", "dbeta", "du", "dalpha", "dgamma", "dconv_w"]:
+        g = got[n].cpu().numpy()
+        r = ref[n]
+        assert np.all(np.isfinite(g)), n
+        errs[n] = float(np.max(np.abs(g - r)) / np.max(np.abs(r)))
+    print("[bwd] long pair rel errors " + " ".join(f"{n}={e:.1e}" for n, e in errs.items()), flush=True)
+    bad = {n: e for n, e in errs.items() if not e <= tol}
+    assert not bad, bad
