@@ -9,20 +9,19 @@
 namespace prism {
 namespace host {
 
-// The scan and the output correction after a sweep (events 2 and 3).  HB16: H_in passes
-// between them in bfloat16 (the d = 128 MFMA correction's operand layout).
-template <class E, int DK, int DV, int C, bool HB16 = false>
+// The scan and the output correction after a generic sweep (events 2 and 3).
+template <class E, int DK, int DV, int C>
 prism_status launch_generic_tail(const FwdArgs& a, const LaunchShape& s, hipEvent_t* ev, hipStream_t stream) {
   constexpr int NQ = DK >= 128 ? 8 : 4;      // state columns per scan workgroup
   constexpr int DEPTH = NQ == 8 ? 4 : 8;     // the scan's steps loaded ahead
   const dim3 sgrid(s.P, DV / NQ), sblock(NQ * DK);
   if (s.nseg <= DEPTH)
-    hipLaunchKernelGGL((seg_scan_kernel<DK, DV, true, HB16>), sgrid, sblock, 0, stream, a);
+    hipLaunchKernelGGL((seg_scan_kernel<DK, DV, true>), sgrid, sblock, 0, stream, a);
   else
-    hipLaunchKernelGGL((seg_scan_kernel<DK, DV, false, HB16>), sgrid, sblock, 0, stream, a);
+    hipLaunchKernelGGL((seg_scan_kernel<DK, DV, false>), sgrid, sblock, 0, stream, a);
   if (hipGetLastError() != hipSuccess || !record(ev, 2, stream)) return PRISM_ERR_HIP;
   if constexpr (std::is_same<E, bf16_t>::value && DK == 128 && DV == 128 && C == 64)
-    hipLaunchKernelGGL((seg_fixup_mfma_kernel<DK, C, HB16>), dim3((s.nch + kFixupChunks - 1) / kFixupChunks, s.P),
+    hipLaunchKernelGGL((seg_fixup_mfma_kernel<DK, C, false>), dim3((s.nch + kFixupChunks - 1) / kFixupChunks, s.P),
                        dim3(256), 0, stream, a);
   else
     hipLaunchKernelGGL((seg_fixup_kernel<E, DK, DV, C>), dim3(s.nch, s.P), dim3(256), 0, stream, a);

@@ -544,9 +544,8 @@ __device__ __forceinline__ float dpp_mov(float x) {
 // partner 7 - q (bit 2) for NQ = 8, then 3 - q (bit 1), then q ^ 1 (bit 0).  One barrier
 // per step.  Eight columns per workgroup at DK = 128 halve the workgroups that read each
 // A_s, against four.  FEW (nseg <= DEPTH): every step's operands come with the first loads,
-// each segment's once.  HB16: H_in is stored in bfloat16 in the layout the d = 128 MFMA
-// output correction stages (see seg_fixup_mfma_kernel), else float32 [k][col].
-template <int DK, int DV, bool FEW = false, bool HB16 = false>
+// each segment's once.  H_in is stored in float32 [k][col].
+template <int DK, int DV, bool FEW = false>
 __global__ __launch_bounds__(DK >= 128 ? 8 * DK : 4 * DK) void seg_scan_kernel(FwdArgs a) {
   constexpr int NQ = DK >= 128 ? 8 : 4;       // contraction slices = columns per workgroup
   static_assert(DV % NQ == 0, "NQ state columns per workgroup");
@@ -562,9 +561,6 @@ __global__ __launch_bounds__(DK >= 128 ? 8 * DK : 4 * DK) void seg_scan_kernel(F
   const float* A0 = a.Aagg + (size_t)pr * nseg * DK * DK + (size_t)i * DK + q * KQ;
   const float* B0 = a.Bagg + (size_t)pr * nseg * DK * DV + (size_t)i * DV + col;
   float* H0 = a.Hin + (size_t)pr * nseg * DK * DV + (size_t)i * DV + col;
-  // bfloat16 H_in^T [col][k'] with k' = k permuted inside each 32-block
-  const int ip = (i & ~31) | ((i & 12) << 1) | ((i & 16) >> 2) | (i & 3);
-  bf16_t* Hb = reinterpret_cast<bf16_t*>(a.Hin) + (size_t)pr * nseg * DK * DV + (size_t)col * DK + ip;
   auto hrow = [](int r) { return r + r / KQ; };
   float h = a.S0 != nullptr ? a.S0[(size_t)pr * DK * DV + (size_t)i * DV + col] : 0.f;
   reinterpret_cast<float*>(&sH[0][hrow(i)][0])[q] = h;
@@ -587,8 +583,7 @@ __global__ __launch_bounds__(DK >= 128 ? 8 * DK : 4 * DK) void seg_scan_kernel(F
     for (int d = 0; d < DEPTH; ++d) {
       const int s = s0 + d;
       if (s < nseg) {
-        if constexpr (HB16) Hb[(size_t)s * DK * DV] = (bf16_t)h;
-        else H0[(size_t)s * DK * DV] = h;
+        H0[(size_t)s * DK * DV] = h;
         float v[NQ];
 #pragma unroll
         for (int c = 0; c < NQ; ++c) v[c] = 0.f;

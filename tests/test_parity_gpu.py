@@ -203,6 +203,18 @@ def test_half_split_sweep_multichunk_segments(prism, L, seg):
     check(w, run_gpu(prism, w, x, seg=seg), run_oracle(w, x), f" d128 L={L} seg={seg}")
 
 
+# The d = 128 path in the planner's launch configuration at 48 pairs (the 130M layer's pair
+# count, several segments per pair): every pair against the oracle, which covers the
+# inter-segment scan's 32-column workgroups (more pairs than 256 / 8 of 16-column ones).
+@pytest.mark.parametrize("L", [2, 4])
+def test_half_split_planned_48_pairs(prism, L):
+    w = workloads.Workload("d128plan", "bf16", B=8, H=6, T=7 * 64 + 20, dk=128, dv=128, L=L, chunk=64,
+                           seed=170 + L)
+    x = workloads.generate(w)
+    log(f"[parity] d=128 planned launch L={L} T={w.T} pairs={w.B * w.H}")
+    check(w, run_gpu(prism, w, x), run_oracle(w, x), f" d128 planned L={L}")
+
+
 GENERIC_SEG = [
     # (dtype, d, chunk, L)
     ("f32", 16, 16, 3), ("f32", 32, 32, 4), ("f32", 64, 32, 2), ("f32", 64, 64, 5),
