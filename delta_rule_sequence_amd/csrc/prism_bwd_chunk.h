@@ -629,17 +629,19 @@ __global__ __launch_bounds__(NT) void bwdc_local_kernel(BwdArgs a) {
   }
 }
 
-// The two scans over a pair's groups of chunks, on columns c0 .. c0 + 7 of the carried
+// The two scans over a pair's groups of chunks, on columns c0 .. c0 + 3 of the carried
 // 64 x 64 matrix (H layout): forwards (blockIdx.z = 0) X_0 = 0, X_{g+1} = Acc_g X_g + HB_g,
 // storing S_in(g) = X_g^T; backwards (blockIdx.z = 1) X_{ngrp-1} = dS_final (zero if
-// absent), X_{g-1} = Acc_g^T X_g + ell_g, storing Lambda_g = X_g^T.  Thread t takes rows i0 = 2 (t / 8), i0 + 1 and the
-// contraction slice k = 8 q .. 8 q + 7 (q = t % 8): it keeps those 16 entries of the step's
-// operator in registers (loaded DEPTH steps ahead, so a step never waits on memory), reads
-// rows 8 q .. 8 q + 7 of the eight carried columns from LDS (rows skewed so the eight slices
-// hit distinct banks) and forms 2 x 8 partial sums; three DPP exchange rounds within the 8
-// lanes of the row pair (halves of the columns, then quarters, then single columns) leave
-// lane q with X_new[i0][c0 + q] and X_new[i0 + 1][c0 + q].  Eight columns per workgroup:
-// each step's operator is read by 8 workgroups per pair and direction.  One barrier per step.
+// absent), X_{g-1} = Acc_g^T X_g + ell_g, storing Lambda_g = X_g^T.  Thread t takes rows
+// i0 = 2 (t / 8), i0 + 1 and the contraction slice k = 8 q .. 8 q + 7 (q = t % 8): it keeps
+// those 16 entries of the step's operator in registers (loaded DEPTH steps ahead, so a step
+// never waits on memory), reads rows 8 q .. 8 q + 7 of the four carried columns from LDS
+// (one 16-byte read each, rows skewed so the eight slices hit distinct banks) and forms
+// 2 x 4 partial sums; three DPP exchange rounds within the 8 lanes of the row pair (the
+// rows, then halves of the columns, then single columns) leave lane q with
+// X_new[i0 + q / 4][c0 + q % 4].  Four columns per workgroup (16 per pair and direction,
+// 256 workgroups at 8 pairs) keep each step's chain to 64 multiply-adds per thread.  One
+// barrier per step.
 __device__ __forceinline__ float dpp_mirror8(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x141, 0xF, 0xF, false));
 }
@@ -650,22 +652,23 @@ __device__ __forceinline__ float dpp_swap2(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
 }
 
-constexpr int kScanCols = 8;
-__device__ __forceinline__ int scan_row(int r) { return 8 * r + 4 * (r >> 3); }  // float offset of carried row r
+constexpr int kScanCols = 4;
+__device__ __forceinline__ int scan_row(int r) { return 4 * r + 4 * (r >> 3); }  // float offset of carried row r
 
 __global__ __launch_bounds__(256) void bwdc_scan_kernel(BwdArgs a) {
   constexpr int DEPTH = 4;
-  __shared__ __align__(16) float sH[2][64 * 8 + 8 * 4];
+  __shared__ __align__(16) float sH[2][64 * 4 + 8 * 4];
   const int tid = threadIdx.x, i0 = 2 * (tid >> 3), q = tid & 7;
   const int pr = blockIdx.x, c0 = kScanCols * blockIdx.y;
   const bool rev = blockIdx.z == 1;
   const int n = a.ngrp;
+  const int orow = i0 + (q >> 2), ocol = c0 + (q & 3);  // the entry this lane ends with
   const size_t base = (size_t)pr * n * D * D;
   const float* A0 = (rev ? a.grp_Phi : a.grp_Acc) + base + (size_t)i0 * D + 8 * q;
-  const float* B0 = (rev ? a.grp_ell : a.grp_B) + base + (size_t)i0 * D + c0 + q;
-  float* O0 = (rev ? a.grp_Lam : a.grp_Sin) + base + (size_t)(c0 + q) * D + i0;
+  const float* B0 = (rev ? a.grp_ell : a.grp_B) + base + (size_t)orow * D + ocol;
+  float* O0 = (rev ? a.grp_Lam : a.grp_Sin) + base + (size_t)ocol * D + orow;
   auto chunk_of = [&](int s) { return rev ? n - 1 - s : s; };
-#define PRISM_DECL(D_) float4 R##D_##_0, R##D_##_1, R##D_##_2, R##D_##_3; float R##D_##_b0, R##D_##_b1;
+#define PRISM_DECL(D_) float4 R##D_##_0, R##D_##_1, R##D_##_2, R##D_##_3; float R##D_##_b;
 #define PRISM_FETCH(D_, S)                                                                    \
   {                                                                                           \
     const size_t cn_ = (size_t)chunk_of((S) < n ? (S) : n - 1);                               \
@@ -674,60 +677,48 @@ __global__ __launch_bounds__(256) void bwdc_scan_kernel(BwdArgs a) {
     R##D_##_1 = src_[1];                                                                      \
     R##D_##_2 = src_[D / 4];                                                                  \
     R##D_##_3 = src_[D / 4 + 1];                                                              \
-    R##D_##_b0 = B0[cn_ * D * D];                                                             \
-    R##D_##_b1 = B0[cn_ * D * D + D];                                                         \
+    R##D_##_b = B0[cn_ * D * D];                                                              \
   }
   PRISM_DECL(0) PRISM_DECL(1) PRISM_DECL(2) PRISM_DECL(3)
   PRISM_FETCH(0, 0) PRISM_FETCH(1, 1) PRISM_FETCH(2, 2) PRISM_FETCH(3, 3)
   const float* X0 = rev ? a.dS_final : nullptr;
   const float* xs = X0 != nullptr ? X0 + (size_t)pr * D * D : nullptr;
-  float h0 = xs != nullptr ? xs[(size_t)i0 * D + c0 + q] : 0.f;
-  float h1 = xs != nullptr ? xs[(size_t)(i0 + 1) * D + c0 + q] : 0.f;
-  if (tid < 128) {
-    const int r = tid >> 1, hf = 4 * (tid & 1);
-    *reinterpret_cast<float4*>(&sH[0][scan_row(r) + hf]) =
-        xs != nullptr ? *reinterpret_cast<const float4*>(xs + (size_t)r * D + c0 + hf) : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
+  float h = xs != nullptr ? xs[(size_t)orow * D + ocol] : 0.f;
+  if (tid < 64)
+    *reinterpret_cast<float4*>(&sH[0][scan_row(tid)]) =
+        xs != nullptr ? *reinterpret_cast<const float4*>(xs + (size_t)tid * D + c0) : make_float4(0.f, 0.f, 0.f, 0.f);
   __syncthreads();
   const bool lo4 = q < 4, lo2 = (q & 2) == 0, lo1 = (q & 1) == 0;
   int cur = 0;
 #define PRISM_SCAN_STEP(D_, PREFETCH)                                                         \
   {                                                                                           \
     const int s = s0 + (D_);                                                                  \
-    *reinterpret_cast<float2*>(O0 + (size_t)chunk_of(s) * D * D) = make_float2(h0, h1);      \
+    O0[(size_t)chunk_of(s) * D * D] = h;                                                      \
     const float ar0[8] = {R##D_##_0.x, R##D_##_0.y, R##D_##_0.z, R##D_##_0.w,                 \
                           R##D_##_1.x, R##D_##_1.y, R##D_##_1.z, R##D_##_1.w};                \
     const float ar1[8] = {R##D_##_2.x, R##D_##_2.y, R##D_##_2.z, R##D_##_2.w,                 \
                           R##D_##_3.x, R##D_##_3.y, R##D_##_3.z, R##D_##_3.w};                \
-    const float bv0 = R##D_##_b0, bv1 = R##D_##_b1;                                           \
-    float v0[8], v1[8]; /* rows i0, i0 + 1; columns c0 .. c0 + 7 */                          \
-    _Pragma("unroll") for (int c = 0; c < 8; ++c) { v0[c] = 0.f; v1[c] = 0.f; }              \
+    const float bv = R##D_##_b;                                                               \
+    float v0[4], v1[4]; /* rows i0, i0 + 1; columns c0 .. c0 + 3 */                          \
+    _Pragma("unroll") for (int c = 0; c < 4; ++c) { v0[c] = 0.f; v1[c] = 0.f; }              \
     _Pragma("unroll") for (int m = 0; m < 8; ++m) {                                           \
-      const float* xr = &sH[cur][scan_row(8 * q + m)];                                        \
-      const float4 xa = *reinterpret_cast<const float4*>(xr);                                 \
-      const float4 xb = *reinterpret_cast<const float4*>(xr + 4);                             \
-      const float xv[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};                   \
-      _Pragma("unroll") for (int c = 0; c < 8; ++c) {                                         \
+      const float4 xa = *reinterpret_cast<const float4*>(&sH[cur][scan_row(8 * q + m)]);      \
+      const float xv[4] = {xa.x, xa.y, xa.z, xa.w};                                           \
+      _Pragma("unroll") for (int c = 0; c < 4; ++c) {                                         \
         v0[c] += ar0[m] * xv[c];                                                              \
         v1[c] += ar1[m] * xv[c];                                                              \
       }                                                                                       \
     }                                                                                         \
     if (PREFETCH) PRISM_FETCH(D_, s + DEPTH)                                                  \
-    /* halves of the columns, then quarters, then single columns */                           \
-    float k0[4], k1[4];                                                                       \
-    _Pragma("unroll") for (int c = 0; c < 4; ++c) {                                           \
-      k0[c] = (lo4 ? v0[c] : v0[4 + c]) + dpp_mirror8(lo4 ? v0[4 + c] : v0[c]);              \
-      k1[c] = (lo4 ? v1[c] : v1[4 + c]) + dpp_mirror8(lo4 ? v1[4 + c] : v1[c]);              \
-    }                                                                                         \
-    float j0[2], j1[2];                                                                       \
-    _Pragma("unroll") for (int c = 0; c < 2; ++c) {                                           \
-      j0[c] = (lo2 ? k0[c] : k0[2 + c]) + dpp_rev4(lo2 ? k0[2 + c] : k0[c]);                  \
-      j1[c] = (lo2 ? k1[c] : k1[2 + c]) + dpp_rev4(lo2 ? k1[2 + c] : k1[c]);                  \
-    }                                                                                         \
-    h0 = (lo1 ? j0[0] : j0[1]) + dpp_swap2(lo1 ? j0[1] : j0[0]) + bv0;                        \
-    h1 = (lo1 ? j1[0] : j1[1]) + dpp_swap2(lo1 ? j1[1] : j1[0]) + bv1;                        \
-    sH[cur ^ 1][scan_row(i0) + q] = h0;                                                       \
-    sH[cur ^ 1][scan_row(i0 + 1) + q] = h1;                                                   \
+    /* the rows, then halves of the columns, then single columns */                          \
+    float k[4];                                                                               \
+    _Pragma("unroll") for (int c = 0; c < 4; ++c)                                             \
+      k[c] = (lo4 ? v0[c] : v1[c]) + dpp_mirror8(lo4 ? v1[c] : v0[c]);                        \
+    float j[2];                                                                               \
+    _Pragma("unroll") for (int c = 0; c < 2; ++c)                                             \
+      j[c] = (lo2 ? k[c] : k[2 + c]) + dpp_rev4(lo2 ? k[2 + c] : k[c]);                        \
+    h = (lo1 ? j[0] : j[1]) + dpp_swap2(lo1 ? j[1] : j[0]) + bv;                              \
+    sH[cur ^ 1][scan_row(orow) + (q & 3)] = h;                                                \
     cur ^= 1;                                                                                 \
     __syncthreads();                                                                          \
   }
