@@ -29,6 +29,8 @@ CASES = [
     ("L4_T3", 2, 1, 3, 4, False),
     ("L6_T256_dS", 1, 1, 256, 6, True),
     ("L7_T321", 1, 1, 321, 7, False),
+    # twelve pairs: every pass indexes its workspace by pair (chunks, groups, conv shares)
+    ("L4_T300_P12_dS", 4, 3, 300, 4, True),
 ]
 
 
