@@ -76,9 +76,9 @@ enum : int {
   kRowBeta = 320 + 512,       // dbeta partials [2 halves][64]
   kRowGv = kRowBeta + 128,    // dG partials
   kRowDd = kRowGv + 128,      // dD partials
-  kRowLg = kRowDd + 128,      // row sums of dlG
+  kRowLg = kRowDd + 128,      // (unused)
   kMisc = kRowLg + 128,       // [0..15]: dG_C partials of the 8 waves etc.
-  kColLg = kMisc + 128,       // column sums of dlG, [4 row blocks][64]
+  kColLg = kMisc + 128,       // [64]: sum_{i >= s > j} dlG[i][j] for each token s
 };
 
 __device__ __forceinline__ bf16x8 rfrag(const bf16_t* X, int r0, int k0) {
@@ -1306,28 +1306,19 @@ __global__ __launch_bounds__(NT) void bwdc_grad_kernel(BwdArgs a) {
     dvd[0] = d0.x; dvd[1] = d0.y; dvd[2] = d0.z; dvd[3] = d0.w;
     dvd[4] = d1.x; dvd[5] = d1.y; dvd[6] = d1.z; dvd[7] = d1.w;
   }
-  // row partials of this lane's row over the wave's 32 columns; column sums of dlG
+  // row partials of this lane's row over the wave's 32 columns; the decay-weighted adjoint
+  // W = dlG (W_ij = Gam_ij dL/dGam_ij, lower triangular) into LDS for its rectangle sums
+  float* sWl = x.mf(mQ);  // float32 [64][LDF] over slots Q and K (free after the rank loop)
   {
-    float rlg = 0.f;
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) rlg += dlg[h][r];
-    const float s_beta = sum_groups(rb_beta), s_gv = sum_groups(rb_gv), s_dd = sum_groups(rb_dd),
-                s_lg = sum_groups(rlg);
+    const float s_beta = sum_groups(rb_beta), s_gv = sum_groups(rb_gv), s_dd = sum_groups(rb_dd);
     if (g == 0) {
       tk[kRowBeta + half * 64 + row] = s_beta;
       tk[kRowGv + half * 64 + row] = s_gv;
       tk[kRowDd + half * 64 + row] = s_dd;
-      tk[kRowLg + half * 64 + row] = s_lg;
     }
+    __syncthreads();  // every product that read slots Q and K is done
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float cs = sum16(dlg[h][r]);
-        if (i == 0) tk[kColLg + mt * 64 + 16 * (nt0 + h) + 4 * g + r] = cs;
-      }
+    for (int h = 0; h < 2; ++h) *reinterpret_cast<f32x4*>(sWl + row * LDF + 16 * (nt0 + h) + 4 * g) = dlg[h];
   }
   float* sW = x.mf(mT);  // the head's conv taps [4][64] (slot T is free after the rank loop)
   if (x.L > 1) {
@@ -1337,6 +1328,49 @@ __global__ __launch_bounds__(NT) void bwdc_grad_kernel(BwdArgs a) {
       *reinterpret_cast<float4*>(sdR + ct * LDF + cc + e) = make_float4(dr[e], dr[e + 1], dr[e + 2], dr[e + 3]);
     if ((tid & 7) == 0 && in_t) a.dalpha[tg * x.L] = da_carry;
     if (tid < 4 * D) sW[tid] = a.conv_w[(size_t)(x.pr % a.H) * 4 * D + tid];
+  }
+  __syncthreads();
+  {
+    // E[i][s] = sum_{j < s} W[i][j], in place: eight threads per row, eight columns each
+    const int ri = tid >> 3, seg = tid & 7;
+    float* wr = sWl + ri * LDF + 8 * seg;
+    const float4 w0 = *reinterpret_cast<const float4*>(wr), w1 = *reinterpret_cast<const float4*>(wr + 4);
+    const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+    float tot = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) tot += wv[e];
+    // the totals of the row's earlier column blocks (lanes seg' < seg of the same 8)
+    float off = 0.f;
+#pragma unroll
+    for (int o = 1; o < 8; ++o) {
+      const float y = __shfl(tot, (lane_id() & ~7) + ((seg - o) & 7));
+      if (seg - o >= 0) off += y;
+    }
+    float ex[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      ex[e] = off;
+      off += wv[e];
+    }
+    *reinterpret_cast<float4*>(wr) = make_float4(ex[0], ex[1], ex[2], ex[3]);
+    *reinterpret_cast<float4*>(wr + 4) = make_float4(ex[4], ex[5], ex[6], ex[7]);
+  }
+  __syncthreads();
+  {
+    // C(s) = sum_{i >= s} E[i][s] = sum_{i >= s > j} W[i][j]: eight threads per s, rows
+    // part, part + 8, ...; only entries whose decay spans token s enter, so a token with a
+    // tiny gate gets a tiny sum instead of a difference of two large ones
+    const int sc = tid >> 3, part = tid & 7;
+    float cs = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int ri = part + 8 * k;
+      if (ri >= sc) cs += sWl[ri * LDF + sc];
+    }
+    cs += __shfl_xor(cs, 1);
+    cs += __shfl_xor(cs, 2);
+    cs += __shfl_xor(cs, 4);
+    if (part == 0) tk[kColLg + sc] = cs;
   }
   __syncthreads();
   {
@@ -1352,32 +1386,39 @@ __global__ __launch_bounds__(NT) void bwdc_grad_kernel(BwdArgs a) {
     }
   }
   if (tid < 64) {
-    // db, then d log g = reverse cumsum, dg = d log g / g; dbeta (wave 0, one token per lane)
+    // d log g_s = sum_{t >= s} G_t dL/dG_t (+ G_C dL/dG_C) + sum_{t < s} D_t dL/dD_t
+    // + C(s), each a sum of terms that carry g_s (G_t = prod_{u <= t} g_u, D_t =
+    // prod_{u > t} g_u); dg = d log g / g.  dbeta (wave 0, one token per lane).
     const int t = tid;
     const float Gt = tk[kG + t], Dt = tk[kDd + t];
     const float dD = tk[kRowDd + t] + tk[kRowDd + 64 + t];
     const float dGv = tk[kRowGv + t] + tk[kRowGv + 64 + t];
-    const float cs = (tk[kColLg + t] + tk[kColLg + 64 + t]) + (tk[kColLg + 128 + t] + tk[kColLg + 192 + t]);
-    float db = dGv * Gt - dD * Dt + (tk[kRowLg + t] + tk[kRowLg + 64 + t]) - cs;
-    float tot = dD * Dt;
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) tot += __shfl_xor(tot, o);
+    float gsum = dGv * Gt;
     if (t == 63) {
       float dGC = 0.f;
 #pragma unroll
       for (int ww = 0; ww < 8; ++ww) dGC += tk[kMisc + ww];
-      db += tot + dGC * Gt;
+      gsum += dGC * Gt;
     }
-    // suffix sum over lanes t .. 63
-    float sfx = db;
+    // suffix sum of the G terms over lanes t .. 63
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
-      const float y = __shfl_down(sfx, o);
-      if (t + o < 64) sfx += y;
+      const float y = __shfl_down(gsum, o);
+      if (t + o < 64) gsum += y;
     }
+    // exclusive prefix sum of the D terms over lanes 0 .. t - 1
+    const float dterm = dD * Dt;
+    float dsum = __shfl_up(dterm, 1);
+    if (t == 0) dsum = 0.f;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const float y = __shfl_up(dsum, o);
+      if (t >= o) dsum += y;
+    }
+    const float dlog = gsum + dsum + tk[kColLg + t];
     if (t < x.nt) {
       const size_t gi = (size_t)x.pr * a.T + x.t0 + t;
-      a.dg[gi] = sfx / tk[kGg + t];
+      a.dg[gi] = dlog / tk[kGg + t];
       a.dbeta[gi] = tk[kRowBeta + t] + tk[kRowBeta + 64 + t];
     }
   }
