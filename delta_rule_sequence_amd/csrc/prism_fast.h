@@ -36,6 +36,33 @@ __device__ __forceinline__ f32x4 mm16_bf16(const f32x4& At, const f32x4& Bt) {
   return mfma16(to_bf16x4(At), to_bf16x4(Bt), zero4());
 }
 
+// T = (I + M)^-1 of a strictly lower triangular 16 x 16 block M by forward substitution in
+// float32.  The 16 lanes c of each lane group g take column c, rows 4 g .. 4 g + 3, and the
+// lane holding x_j hands it to the others of its column (one shuffle per step), so a lane
+// keeps four unknowns; it returns T[4 g + r][c], r = 0..3.  Mt is M^T in the wave's own LDS
+// ([16][kMtLd] floats, Mt[j][r] = M[r][j], zero where r <= j), written by the caller, who
+// has also waited for its own stores.  Stable whatever the size of M's entries, where the
+// product form (I + Y)(I + Y^2)(I + Y^4)(I + Y^8) with Y = -M sums powers that grow like
+// binomial coefficients when |M| is near 1 (one key repeated over the block with beta near
+// 1) and cancel to a bounded inverse only in exact arithmetic.
+constexpr int kMtLd = 20;  // row stride of Mt (floats)
+__device__ __forceinline__ f32x4 diag_inverse_subst(const float* Mt) {
+  const int l = lane_id(), c = l & 15, g = l >> 4;
+  f32x4 x;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) x[e] = 4 * g + e == c ? 1.f : 0.f;
+#pragma unroll
+  for (int j = 0; j < 15; ++j) {
+    const float xj = __shfl(x[j & 3], c + 16 * (j >> 2));  // x_j, final after step j - 1
+    const float4 m = *reinterpret_cast<const float4*>(Mt + j * kMtLd + 4 * g);
+    const float mv[4] = {m.x, m.y, m.z, m.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (4 * g + e > j) x[e] -= mv[e] * xj;
+  }
+  return x;
+}
+
 __device__ __forceinline__ bf16x8 cat8(const bf16x4& a, const bf16x4& b) {
   return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }

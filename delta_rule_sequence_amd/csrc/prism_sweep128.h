@@ -41,6 +41,7 @@ struct Sweep128Lds {
   static constexpr size_t oWc = oAt + szK;    // Wc [token][dk]; before it M and the blocks
   static constexpr size_t oM = oWc;           // M strict lower [i][j]
   static constexpr size_t oTd = oWc + szC;    // diagonal inverse blocks [4][16][LDT]
+  static constexpr size_t oMt = oTd + (size_t)4 * 16 * LDT * 2;  // the K waves' float32 M^T blocks
   static constexpr size_t oVt = oWc + szK;    // V^T, later (beta V')^T [value][token]
   static constexpr size_t oMinv = oVt + szC;  // (I + M)^-1 [i][j]
   static constexpr size_t oGate = oMinv + szC;
@@ -51,7 +52,7 @@ struct Sweep128Lds {
   static constexpr size_t oSlot = oGate + nGate * 4;
   static constexpr size_t szSlot = szK + szC;
   static constexpr size_t total = oSlot + 2 * szSlot;
-  static_assert(oTd + (size_t)4 * 16 * LDT * 2 <= oVt, "M and the diagonal blocks fit in Wc's space");
+  static_assert(oMt + (size_t)4 * 16 * kMtLd * 4 <= oVt, "M, the diagonal blocks and M^T fit in Wc's space");
   static_assert(total <= 160 * 1024, "LDS plan exceeds the 160 KB of a CU");
 };
 
@@ -296,12 +297,25 @@ __device__ __forceinline__ void sweep128_kwave(const Sweep128Ctx& x, int wq) {
       }
       const f32x4 Y2 = mm16_bf16(Yt, Y), Y2t = mm16_bf16(Y, Yt);
       const f32x4 Y4 = mm16_bf16(Y2t, Y2), Y4t = mm16_bf16(Y2, Y2t);
-      const f32x4 Y8 = mm16_bf16(Y4t, Y4);
-      f32x4 Pt = plus_identity(Yt);
-      Pt = mm16_bf16(plus_identity(Y2), Pt);
-      Pt = mm16_bf16(plus_identity(Y4), Pt);
-      Pt = mm16_bf16(plus_identity(Y8), Pt);  // Pt = T^T: T[li][g4 + r] = Pt[r]
-      *reinterpret_cast<bf16x4*>(V.sTd + (16 * rb + li) * LDT + g4) = to_bf16x4(Pt);
+      // a power of Y past 1: the product cancels large terms, so float32 substitution
+      float grow = 0.f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) grow = fmaxf(grow, fmaxf(fabsf(Y2[r]), fabsf(Y4[r])));
+      if (!__any(grow > 1.f)) {
+        const f32x4 Y8 = mm16_bf16(Y4t, Y4);
+        f32x4 Pt = plus_identity(Yt);
+        Pt = mm16_bf16(plus_identity(Y2), Pt);
+        Pt = mm16_bf16(plus_identity(Y4), Pt);
+        Pt = mm16_bf16(plus_identity(Y8), Pt);  // Pt = T^T: T[li][g4 + r] = Pt[r]
+        *reinterpret_cast<bf16x4*>(V.sTd + (16 * rb + li) * LDT + g4) = to_bf16x4(Pt);
+      } else {
+        float* Mt = reinterpret_cast<float*>(x.smem + Sweep128Lds::oMt) + wq * 16 * kMtLd;
+        *reinterpret_cast<float4*>(Mt + li * kMtLd + g4) = make_float4(-Y[0], -Y[1], -Y[2], -Y[3]);
+        __builtin_amdgcn_wave_barrier();  // the wave's LDS stores land before its reads (in order)
+        const f32x4 tc = diag_inverse_subst(Mt);  // T[g4 + r][li]
+#pragma unroll
+        for (int r = 0; r < 4; ++r) V.sTd[(16 * rb + g4 + r) * LDT + li] = (bf16_t)tc[r];
+      }
     }
 #pragma unroll
     for (int vt = 0; vt < 4; ++vt) {  // V' starts as V (rows rb)

@@ -20,9 +20,10 @@
 //     triangular Gram work is the same on every SIMD;
 //   * (I + M)^-1 is built explicitly: the 16x16 diagonal blocks by the product
 //     (I + Y)(I + Y^2)(I + Y^4)(I + Y^8) (Y = -M_ii is nilpotent; bfloat16 products
-//     with float32 accumulation, the factors rounded as the stored inverse is), the
-//     rest by block forward substitution on identity columns, overlapped with
-//     the rank-L steps, so the solve that depends on V' is one product;
+//     with float32 accumulation), or, when a power of Y grows past 1 (the product then
+//     cancels large terms: one key repeated with beta near 1), by float32 forward
+//     substitution; the rest by block forward substitution on identity columns,
+//     overlapped with the rank-L steps, so the solve that depends on V' is one product;
 //   * one barrier per rank-L step plus four per chunk (L + 3 for L >= 4); the
 //     inputs of the next step / chunk are loaded one phase ahead into registers.
 #pragma once
@@ -54,9 +55,11 @@ struct Sweep8Lds {
   static constexpr size_t oGate = oTd + (size_t)4 * 16 * LDT * 2;
   // b, G, D, beta, beta*G [C]; alpha^T [8][C]; conv taps [4][D]
   static constexpr size_t nGate = 5 * C + 8 * C + 4 * D;
+  // each key-side wave's float32 copy of its diagonal block M^T, for the substitution
+  static constexpr size_t oMt = oGate + nGate * 4;
   // two slots of (U_l [token][d], U_l^T [d][token], R_l^T [dv][token]); slot 1 holds
   // E^T between the state phase and the output phase
-  static constexpr size_t oSlot = oGate + nGate * 4;
+  static constexpr size_t oSlot = oMt + (size_t)4 * 16 * kMtLd * 4;
   static constexpr size_t szSlot = 3 * szA;
   static constexpr size_t total = oSlot + 2 * szSlot;
   static_assert(total <= 160 * 1024, "LDS plan exceeds the 160 KB of a CU");
@@ -177,7 +180,7 @@ struct Sweep8Ctx {
 // LDS views.
 struct Sweep8View {
   bf16_t *sQ, *sK, *sKt, *sVt, *sHt, *sAt, *sM, *sWc, *sMinv, *sWct, *sTd, *sEt;
-  float *sB, *sG, *sD, *sBeta, *sBG, *sAlphaT, *sTaps;
+  float *sB, *sG, *sD, *sBeta, *sBG, *sAlphaT, *sTaps, *sMt;
   unsigned char* slot0;
   __device__ __forceinline__ explicit Sweep8View(unsigned char* smem) {
     using Ly = Sweep8Lds;
@@ -199,6 +202,7 @@ struct Sweep8View {
     sBG = sBeta + 64;
     sAlphaT = sBG + 64;  // [8][64]
     sTaps = sAlphaT + 8 * 64;  // [4][64]
+    sMt = reinterpret_cast<float*>(smem + Ly::oMt);  // [4 waves][16][kMtLd]
     slot0 = smem + Ly::oSlot;
     sEt = slotU(1);
   }
@@ -365,7 +369,10 @@ __device__ __forceinline__ void sweep8_kwave(const Sweep8Ctx& x, int wq) {
           *reinterpret_cast<bf16x4*>(V.sM + (16 * rb + li) * LD + pcol(16 * jt + g4)) = mv;
         }
       }
-      // T_rb = (I + M_rb,rb)^-1 = (I + Y)(I + Y^2)(I + Y^4)(I + Y^8), Y = -M_rb,rb
+      // T_rb = (I + M_rb,rb)^-1 = (I + Y)(I + Y^2)(I + Y^4)(I + Y^8), Y = -M_rb,rb (bf16
+      // products, float32 sums), unless a power of Y grows past 1: the product then
+      // cancels large terms to a bounded inverse, which bf16 cannot resolve, and the wave
+      // takes float32 forward substitution instead (one key repeated with beta near 1)
       const float4 bi4 = *reinterpret_cast<const float4*>(V.sB + 16 * rb + g4);
       const float4 be4 = *reinterpret_cast<const float4*>(V.sBeta + 16 * rb + g4);
       const float bir[4] = {bi4.x, bi4.y, bi4.z, bi4.w};
@@ -380,12 +387,24 @@ __device__ __forceinline__ void sweep8_kwave(const Sweep8Ctx& x, int wq) {
       }
       const f32x4 Y2 = mm16_bf16(Yt, Y), Y2t = mm16_bf16(Y, Yt);
       const f32x4 Y4 = mm16_bf16(Y2t, Y2), Y4t = mm16_bf16(Y2, Y2t);
-      const f32x4 Y8 = mm16_bf16(Y4t, Y4);
-      f32x4 Pt = plus_identity(Yt);
-      Pt = mm16_bf16(plus_identity(Y2), Pt);
-      Pt = mm16_bf16(plus_identity(Y4), Pt);
-      Pt = mm16_bf16(plus_identity(Y8), Pt);  // Pt = T^T: T[li][g4 + r] = Pt[r]
-      *reinterpret_cast<bf16x4*>(V.sTd + (16 * rb + li) * LDT + g4) = to_bf16x4(Pt);
+      float grow = 0.f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) grow = fmaxf(grow, fmaxf(fabsf(Y2[r]), fabsf(Y4[r])));
+      if (!__any(grow > 1.f)) {
+        const f32x4 Y8 = mm16_bf16(Y4t, Y4);
+        f32x4 Pt = plus_identity(Yt);
+        Pt = mm16_bf16(plus_identity(Y2), Pt);
+        Pt = mm16_bf16(plus_identity(Y4), Pt);
+        Pt = mm16_bf16(plus_identity(Y8), Pt);  // Pt = T^T: T[li][g4 + r] = Pt[r]
+        *reinterpret_cast<bf16x4*>(V.sTd + (16 * rb + li) * LDT + g4) = to_bf16x4(Pt);
+      } else {
+        float* Mt = V.sMt + wq * 16 * kMtLd;  // this wave's M^T: Mt[li][g4 + r] = M[g4 + r][li]
+        *reinterpret_cast<float4*>(Mt + li * kMtLd + g4) = make_float4(-Y[0], -Y[1], -Y[2], -Y[3]);
+        __builtin_amdgcn_wave_barrier();  // the wave's LDS stores land before its reads (in order)
+        const f32x4 tc = diag_inverse_subst(Mt);  // T[g4 + r][li]
+#pragma unroll
+        for (int r = 0; r < 4; ++r) V.sTd[(16 * rb + g4 + r) * LDT + li] = (bf16_t)tc[r];
+      }
     }
 #pragma unroll
     for (int vt = 0; vt < 4; ++vt) {  // V' starts as V (rows rb); the rank-L state term at zero
