@@ -1,4 +1,5 @@
-"""Degenerate inputs of the method on the bf16 d = 64 and d = 128 forwards and both backward forms,
+"""Degenerate inputs of the method on every forward path (the bf16 d = 64 and d = 128 sweeps,
+the generic sweep in float32 and bf16) and both backward forms,
 against the float64 oracle (forward) and gradient oracle (backward):
 
 * beta = 1 everywhere: each write fully replaces the value read along k (the delta rule's
@@ -9,7 +10,8 @@ against the float64 oracle (forward) and gradient oracle (backward):
   ill-conditioned as unit keys allow (M_ij = Gam_ij for all j < i), and each token erases
   the previous one's write.
 
-Tolerances as elsewhere: 2e-2 (bf16 forward and chunked backward), 1e-4 (float32 backward),
+Tolerances as elsewhere: 2e-2 (bf16 forward and chunked backward), 1e-4 (float32 forward
+and backward),
 max-abs error relative to max |reference| per output or gradient; where a reference is
 identically zero (du, dgamma and dconv_w at alpha = 0: nothing is written along u), the
 largest entry over all gradients is the scale.
@@ -55,21 +57,27 @@ def rel(a, b, scale=None):
     return float(np.max(np.abs(np.asarray(a, np.float64) - b)) / max(1e-30, s))
 
 
-@pytest.mark.parametrize("d", [64, 128])
+# (dtype, d, chunk): the bf16 d = 64 and d = 128 sweeps and the generic sweep
+FWD_PATHS = [("bf16", 64, 64), ("bf16", 128, 64), ("f32", 32, 32), ("bf16", 32, 16)]
+
+
+@pytest.mark.parametrize("path", FWD_PATHS, ids=lambda p: f"{p[0]}_d{p[1]}_c{p[2]}")
 @pytest.mark.parametrize("kind", KINDS)
-def test_forward_degenerate(prism, kind, d):
+def test_forward_degenerate(prism, kind, path):
     import torch
-    w = workloads.Workload("degen", "bf16", B=1, H=2, T=300, dk=d, dv=d, L=4, chunk=64, seed=500)
+    dt, d, chunk = path
+    w = workloads.Workload("degen", dt, B=1, H=2, T=300, dk=d, dv=d, L=4, chunk=chunk, seed=500)
     y = degenerate(kind, workloads.generate(w))
     ref = oracle.forward(y["q"], y["k"], y["v"], y["g"], y["beta"], y["u"], y["alpha"], y["gamma"], y["conv_w"], w.L)
-    t = workloads.to_torch(y, "bf16")
+    t = workloads.to_torch(y, dt)
+    tol = 2e-2 if dt == "bf16" else 1e-4
     for sc in (None, 2):
         o, S = prism.fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], t["u"], t["alpha"], t["gamma"], t["conv_w"],
-                         L=w.L, seg_chunks=sc)
+                         L=w.L, chunk=chunk, seg_chunks=sc)
         torch.cuda.synchronize()
         eo, es = rel(o.float().cpu().numpy(), ref[0]), rel(S.cpu().numpy(), ref[1])
-        print(f"[degenerate] fwd {kind} d={d} seg={sc}: o {eo:.2e} S_final {es:.2e}", flush=True)
-        assert eo <= 2e-2 and es <= 2e-2
+        print(f"[degenerate] fwd {kind} {path} seg={sc}: o {eo:.2e} S_final {es:.2e}", flush=True)
+        assert eo <= tol and es <= tol
 
 
 @pytest.mark.parametrize("chunked", [True, False], ids=["chunked", "float32"])
