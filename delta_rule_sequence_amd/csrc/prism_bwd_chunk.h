@@ -20,8 +20,11 @@
 //   dU_l = diag(D) R_l dH'^T + (Gam*dPU_l)^T Q + (Gam*dN_l)^T K
 //   dR_l = diag(D) U_l dH' + PU_l^T dO - N_l^T dVp   (then back through the residual chain)
 //   dbeta = rowsum(V' * dX1) + G rowsum(K * dX2) + rowsum(dA * Gam * K K^T)
-//   d log g = reverse cumsum of  dG G - dD D + rowsum(dlG) - colsum(dlG)  (+ the G_C, D terms
-//         at the last token), dlG the elementwise sum of dX * X over the decayed matrices
+//   d log g_s = sum_{t >= s} dG_t G_t (+ dG_C G_C) + sum_{t < s} dD_t D_t
+//         + sum_{i >= s > j} dlG_ij, dlG the elementwise sum of dX * X over the decayed
+//         matrices: every term carries g_s, so a token with a tiny gate gets a tiny sum (the
+//         same quantity as a reverse cumsum of dG G - dD D + rowsum(dlG) - colsum(dlG), which
+//         cancels large terms there before the division by g)
 // and the adjoint of the start state is dH = Qt^T dO + Acc^T dH' with Qt = diag(G) Q - P Wc,
 // Acc = G_C I - K^T diag(D) Wc.  Two kernels:
 //   * bwdc_local_kernel: per chunk, the operator Acc and its transpose, the end state from
