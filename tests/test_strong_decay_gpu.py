@@ -75,13 +75,14 @@ def test_forward_strong_decay(prism, case):
         assert eo <= TOL[dt] and es <= TOL[dt]
 
 
+@pytest.mark.parametrize("L", [1, 4, 8])
 @pytest.mark.parametrize("chunked", [True, False], ids=["chunked", "float32"])
-def test_backward_strong_decay(prism, chunked):
+def test_backward_strong_decay(prism, chunked, L):
     import torch
     from oracle import prism_grad
     from tests.test_bwd_gpu import _setup
     dt = "bf16" if chunked else "f32"
-    L, T = 4, 200
+    T = 200
     w, x, d_o, dS = _setup(dt, 1, 2, T, 64, L, True, seed=410)
     x["g"] = strong_gates(w, 411)
     dv = workloads.to_torch(x, dt)
@@ -93,11 +94,11 @@ def test_backward_strong_decay(prism, chunked):
     ref = prism_grad.backward(x["q"], x["k"], x["v"], x["g"], x["beta"], x["u"], x["alpha"], x["gamma"],
                               x["conv_w"], L, d_o, dS)
     errs = {}
-    for n in ["dq", "dk", "dv", "dg", "dbeta", "du", "dalpha", "dgamma", "dconv_w"]:
+    for n in ["dq", "dk", "dv", "dg", "dbeta"] + (["du", "dalpha", "dgamma", "dconv_w"] if L > 1 else []):
         g = got[n].cpu().numpy()
         assert np.all(np.isfinite(g)), n
         errs[n] = rel(g, ref[n])
-    print(f"[decay] bwd chunked={chunked}: " + " ".join(f"{n}={e:.1e}" for n, e in errs.items()), flush=True)
+    print(f"[decay] bwd chunked={chunked} L={L}: " + " ".join(f"{n}={e:.1e}" for n, e in errs.items()), flush=True)
     tol = 2e-2 if chunked else 1e-4
     bad = {n: e for n, e in errs.items() if not e <= tol}
     assert not bad, bad
