@@ -10,7 +10,9 @@ be captured into a HIP graph and replayed.
   with eager calls and synchronisations between the replays.  Every replay must be
   bit-identical to an eager call on the same inputs (the same kernels and plan run), and the
   first replay is also compared with the float64 oracle at the parity tolerances (2e-2
-  bf16, 1e-4 float32; max-abs error relative to max |reference|).
+  bf16, 1e-4 float32; max-abs error relative to max |reference|);
+* serving loop: several decode steps (state and ShortConv window updated in place) captured
+  as one graph and replayed from a reset start, checked the same way.
 """
 import numpy as np
 import pytest
@@ -170,3 +172,68 @@ def test_chunked_backward_side_stream_and_graph(prism):
             errs = {n: rel(gs[n].cpu().numpy(), ref[n]) for n in GRADS}
             log("[graph] chunked bwd replay 0 vs oracle: " + " ".join(f"{n}={e:.1e}" for n, e in errs.items()))
             assert all(e <= 2e-2 for e in errs.values()), errs
+
+
+# (dtype, d, L, steps): decode steps of the serving loop, one token for every pair per step
+DECODE = [("bf16", 64, 4, 6), ("bf16", 128, 8, 5), ("f32", 32, 3, 6)]
+
+
+@pytest.mark.parametrize("case", DECODE, ids=lambda c: f"{c[0]}_d{c[1]}_L{c[2]}")
+def test_decode_loop_graph_replay(prism, case):
+    """A loop of decode steps captured as one graph (the state and the ShortConv window
+    updated in place, step after step), replayed from a reset start on fresh tokens: every
+    replay bit-identical to the same steps run eagerly, the first against the oracle over
+    those tokens from the same start."""
+    import torch
+    dt, d, L, n = case
+    seq = ["q", "k", "v", "g", "beta"] + (["u", "alpha", "gamma"] if L > 1 else [])
+
+    def inputs(seed):
+        w = workloads.Workload("decode_graph", dt, B=2, H=2, T=n, dk=d, dv=d, L=L, chunk=64, seed=seed)
+        x = workloads.generate(w)
+        st = workloads.generate_state(w)
+        t = workloads.to_torch(x, dt)
+        s = workloads.to_torch(st, dt)
+        toks = [{m: t[m][:, :, i].contiguous() for m in seq} for i in range(n)]
+        return w, x, st, toks, t["conv_w"], s["S0"], s["conv_in"]
+
+    def steps(S, conv, toks, conv_w):
+        return [prism.decode_step(S, conv, *(tk[m] for m in ["q", "k", "v", "g", "beta"]),
+                                  tk.get("u"), tk.get("alpha"), tk.get("gamma"),
+                                  conv_w if L > 1 else None, L=L) for tk in toks]
+
+    w, x, st, toks, conv_w, S0, c0 = inputs(650)
+    S, conv = S0.clone(), c0.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up before capture
+        steps(S, conv, toks, conv_w)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        outs = steps(S, conv, toks, conv_w)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        w2, x2, st2, toks2, conv_w2, S02, c02 = inputs(660 + rep)
+        for tk, tk2 in zip(toks, toks2):
+            for m in seq:
+                tk[m].copy_(tk2[m])
+        conv_w.copy_(conv_w2)
+        S.copy_(S02)
+        conv.copy_(c02)
+        graph.replay()
+        torch.cuda.synchronize()
+        Se, ce = S02.clone(), c02.clone()
+        oe = steps(Se, ce, toks2, conv_w2)
+        torch.cuda.synchronize()
+        same = (all(torch.equal(a, b) for a, b in zip(outs, oe)) and torch.equal(S, Se) and torch.equal(conv, ce))
+        log(f"[graph] decode {case} replay {rep}: bit-identical to eager {same}")
+        assert same
+        if rep == 0:
+            ro, rS = oracle.forward(*(x2[m] for m in NAMES), L, S0=st2["S0"], conv_in=st2["conv_in"])[:2]
+            o = np.stack([a.float().cpu().numpy() for a in outs], axis=2)
+            eo, es = rel(o, ro), rel(S.cpu().numpy(), rS)
+            log(f"[graph] decode {case} replay 0 vs oracle: o {eo:.2e} S_final {es:.2e}")
+            assert eo <= TOL[dt] and es <= TOL[dt]
+            assert np.array_equal(conv.float().cpu().numpy(), x2["v"][:, :, n - 3:])
