@@ -666,7 +666,8 @@ __global__ __launch_bounds__(256) void seg_fixup_kernel(FwdArgs a) {
 // 8-value operand (k0 + 4 q .. + 3 and k0 + 16 + 4 q .. + 3) is one 16-byte read.  Wave w
 // takes token rows 16 w .. 16 w + 15 of each chunk and forms o^T = H_in^T Qhat^T + O_loc^T:
 // lane (li, q) of tile vt holds value columns 16 vt + 4 q .. + 3 of token 16 w + li, so
-// O_loc is read and o written 8 bytes at a time.
+// O_loc is read and o written 8 bytes at a time.  The next chunk's Qhat and O_loc
+// fragments are loaded into a second register set while the current chunk is finished.
 constexpr int kFixupChunks = 4;
 
 template <int D, int C, bool HB16 = false>
@@ -678,60 +679,73 @@ __global__ __launch_bounds__(256) void seg_fixup_mfma_kernel(FwdArgs a) {
   const int pr = blockIdx.y;
   const int c_lo = blockIdx.x * kFixupChunks, c_hi = min(a.nch, c_lo + kFixupChunks);
   const int Tpad = a.nch * C;
-  int staged = -1;
-  for (int c = c_lo; c < c_hi; ++c) {
-    const int seg = c / a.seg_chunks;  // the same for every thread of the workgroup
-    const int t0 = c * C, nvalid = min(C, a.T - t0);
-    if (seg != staged) {
-      if (staged >= 0) __syncthreads();  // every read of the previous segment's H_in is done
-      if constexpr (HB16) {  // already bfloat16 [col][k'] (the scan's layout): 16-byte copies
-        const uint4* Hb = reinterpret_cast<const uint4*>(reinterpret_cast<const bf16_t*>(a.Hin) +
-                                                         ((size_t)pr * a.nseg + seg) * D * D);
-        for (int idx = tid; idx < D * D / 8; idx += 256)
-          *reinterpret_cast<uint4*>(&sHt[(idx >> 4) * LH + 8 * (idx & 15)]) = Hb[idx];
-      } else {
-        const float* Hi = a.Hin + ((size_t)pr * a.nseg + seg) * D * D;  // [k][col]
-        for (int idx = tid; idx < D * D; idx += 256) {
-          const int k = idx / D, col = idx % D;
-          const int kp = (k & ~31) | ((k & 12) << 1) | ((k & 16) >> 2) | (k & 3);
-          sHt[col * LH + kp] = (bf16_t)Hi[idx];
-        }
-      }
-      __syncthreads();
-      staged = seg;
-    }
-    // this wave's Qhat rows as B operands (4 blocks of 32 along k)
-    const int row = 16 * w + li;
-    const bf16_t* qh = reinterpret_cast<const bf16_t*>(a.Qhat) + ((size_t)pr * Tpad + t0 + row) * D;
-    bf16x8 bq[D / 32];
+  const int row = 16 * w + li;
+  // this wave's Qhat rows (B operands, 4 blocks of 32 along k) and O_loc entries of one
+  // chunk, in two register sets: the next chunk's are loaded while the current one is
+  // finished.  Chunk indices are clamped to the last (padded) chunk, so every load is in
+  // bounds and none is conditional.
+  const bf16_t* Qb = reinterpret_cast<const bf16_t*>(a.Qhat) + ((size_t)pr * Tpad + row) * D;
+  const bf16_t* Ob = reinterpret_cast<const bf16_t*>(a.Oloc) + ((size_t)pr * Tpad + row) * D;
+  bf16x4 qx[2][D / 32][2], ox[2][D / 16];
+  auto fetch = [&](int set, int c) {
+    const size_t off = (size_t)min(c, a.nch - 1) * C * D;
 #pragma unroll
     for (int kb = 0; kb < D / 32; ++kb) {
-      const bf16x4 x0 = *reinterpret_cast<const bf16x4*>(qh + 32 * kb + 4 * q);
-      const bf16x4 x1 = *reinterpret_cast<const bf16x4*>(qh + 32 * kb + 16 + 4 * q);
-      bq[kb] = __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
-    }
-    const size_t rowoff = ((size_t)pr * Tpad + t0 + row) * D;
-    const bf16_t* ol = reinterpret_cast<const bf16_t*>(a.Oloc) + rowoff;
-    f32x4 acc[D / 16];
-#pragma unroll
-    for (int vt = 0; vt < D / 16; ++vt) {
-      const bf16x4 x = *reinterpret_cast<const bf16x4*>(ol + 16 * vt + 4 * q);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) acc[vt][r] = (float)x[r];
+      qx[set][kb][0] = *reinterpret_cast<const bf16x4*>(Qb + off + 32 * kb + 4 * q);
+      qx[set][kb][1] = *reinterpret_cast<const bf16x4*>(Qb + off + 32 * kb + 16 + 4 * q);
     }
 #pragma unroll
-    for (int vt = 0; vt < D / 16; ++vt)
+    for (int vt = 0; vt < D / 16; ++vt) ox[set][vt] = *reinterpret_cast<const bf16x4*>(Ob + off + 16 * vt + 4 * q);
+  };
+  fetch(0, c_lo);
+  int staged = -1;
 #pragma unroll
-      for (int kb = 0; kb < D / 32; ++kb)
-        acc[vt] = mfma(*reinterpret_cast<const bf16x8*>(&sHt[(16 * vt + li) * LH + 32 * kb + 8 * q]), bq[kb], acc[vt]);
-    if (row < nvalid) {
-      bf16_t* o = reinterpret_cast<bf16_t*>(a.o) + ((size_t)pr * a.T + t0 + row) * D;
+  for (int i = 0; i < kFixupChunks; ++i) {
+    const int c = c_lo + i, cur = i & 1;
+    if (c < c_hi) {
+      const int seg = c / a.seg_chunks;  // the same for every thread of the workgroup
+      const int t0 = c * C, nvalid = min(C, a.T - t0);
+      if (seg != staged) {
+        if (staged >= 0) __syncthreads();  // every read of the previous segment's H_in is done
+        if constexpr (HB16) {  // already bfloat16 [col][k'] (the scan's layout): 16-byte copies
+          const uint4* Hb = reinterpret_cast<const uint4*>(reinterpret_cast<const bf16_t*>(a.Hin) +
+                                                           ((size_t)pr * a.nseg + seg) * D * D);
+          for (int idx = tid; idx < D * D / 8; idx += 256)
+            *reinterpret_cast<uint4*>(&sHt[(idx >> 4) * LH + 8 * (idx & 15)]) = Hb[idx];
+        } else {
+          const float* Hi = a.Hin + ((size_t)pr * a.nseg + seg) * D * D;  // [k][col]
+          for (int idx = tid; idx < D * D; idx += 256) {
+            const int k = idx / D, col = idx % D;
+            const int kp = (k & ~31) | ((k & 12) << 1) | ((k & 16) >> 2) | (k & 3);
+            sHt[col * LH + kp] = (bf16_t)Hi[idx];
+          }
+        }
+        __syncthreads();
+        staged = seg;
+      }
+      // after the staging, whose wait would otherwise also drain these loads
+      if (i + 1 < kFixupChunks) fetch(cur ^ 1, c + 1);
+      f32x4 acc[D / 16];
 #pragma unroll
-      for (int vt = 0; vt < D / 16; ++vt) {
-        bf16x4 y;
+      for (int vt = 0; vt < D / 16; ++vt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) y[r] = (bf16_t)acc[vt][r];
-        *reinterpret_cast<bf16x4*>(o + 16 * vt + 4 * q) = y;
+        for (int r = 0; r < 4; ++r) acc[vt][r] = (float)ox[cur][vt][r];
+#pragma unroll
+      for (int kb = 0; kb < D / 32; ++kb) {
+        const bf16x8 bq = __builtin_shufflevector(qx[cur][kb][0], qx[cur][kb][1], 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+        for (int vt = 0; vt < D / 16; ++vt)
+          acc[vt] = mfma(*reinterpret_cast<const bf16x8*>(&sHt[(16 * vt + li) * LH + 32 * kb + 8 * q]), bq, acc[vt]);
+      }
+      if (row < nvalid) {
+        bf16_t* o = reinterpret_cast<bf16_t*>(a.o) + ((size_t)pr * a.T + t0 + row) * D;
+#pragma unroll
+        for (int vt = 0; vt < D / 16; ++vt) {
+          bf16x4 y;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) y[r] = (bf16_t)acc[vt][r];
+          *reinterpret_cast<bf16x4*>(o + 16 * vt + 4 * q) = y;
+        }
       }
     }
   }
